@@ -1,0 +1,367 @@
+/*
+ * fp64 CPU oracle for the attention hot path.  TEST INFRASTRUCTURE ONLY: nothing in the product path
+ * (the HIP library and its Python binding) may include, link, load or call this file; only the tests,
+ * the smoke check and the CPU-baseline leg of the benchmark use it.  It shares no code, header, table or
+ * constant with the HIP kernels.
+ *
+ * What it computes (the pages' subject is FlashAttention-style attention; the plain definition that the
+ * tiled kernels reach up to rounding is mask-based softmax attention, "SkyRL: Add cuDNN flash attention",
+ * Summary and Changes, which keeps mask-based attention as the reference path):
+ *
+ *   s_j  = scale * sum_d q_d k_jd                       over the keys j the row may see
+ *   p_j  = exp(s_j - m) / sum_j' exp(s_j' - m),  m = max_j s_j
+ *   o    = sum_j p_j v_j,   lse = m + log(sum_j exp(s_j - m))
+ *   a row that sees no key gives o = 0 and lse = -inf
+ *
+ * Three modes per row:
+ *   MODE_DENSE  the definition above, no tiles.
+ *   MODE_SKIP   skip-softmax ("TensorRT-LLM: Skip Softmax Attention", Description; "Model-Optimizer:
+ *               Add split-k decode kernel for skip softmax", What does this PR do): key tiles of `tile`
+ *               keys aligned to key 0 are visited in ascending order with online softmax; a tile whose
+ *               max logit tmax satisfies exp(tmax - m) < thr, m the running max before the tile, is
+ *               skipped whole (no exp, no P.V, no rescale).  The first visited tile is never skipped
+ *               (m = -inf), and thr = 0 never skips.  A replay map may impose the decisions instead.
+ *               Map codes: 0 processed, 1 skipped, 2 not visited (no visible key in the tile).
+ *   MODE_SPLIT  split-K ("Model-Optimizer: Add split-k decode kernel for skip softmax", the 32-split,
+ *               128-token schedule): ntiles = ceil(n / tile), c = ceil(ntiles / S); split s takes tiles
+ *               [s c, (s+1) c) and is attended densely to (o_s, lse_s); then
+ *               lse = log sum_{finite} exp(lse_s) and o = sum_s exp(lse_s - lse) o_s.
+ *
+ * Inputs are read as the exact bytes the GPU reads (fp32, or bf16 widened exactly to fp64); all
+ * arithmetic is in fp64.
+ *
+ * Paged layout: k_cache / v_cache are [num_pages, Hkv, page, D]; key j of batch row b lives in page
+ * block_table[b * max_pages + j / page], slot j % page.  GQA: query head h reads KV head h / (Hq / Hkv).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+enum { ORC_F32 = 0, ORC_BF16 = 1 };
+enum { MODE_DENSE = 0, MODE_SKIP = 1, MODE_SPLIT = 2 };
+enum { MAP_DONE = 0, MAP_SKIPPED = 1, MAP_UNVISITED = 2 };
+
+static double widen(const void *base, int dtype, size_t idx)
+{
+    if (dtype == ORC_F32)
+        return (double)((const float *)base)[idx];
+    uint32_t u = (uint32_t)((const uint16_t *)base)[idx] << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+static double dot(const double *a, const double *b, int D)
+{
+    double s = 0.0;
+    for (int d = 0; d < D; ++d)
+        s += a[d] * b[d];
+    return s;
+}
+
+/* The plain definition.  K, V: n rows of D.  p (nullable) receives the n probabilities. */
+static void dense_row(const double *q, const double *K, const double *V, int n, int D, double scale,
+                      double *o, double *lse, double *p)
+{
+    for (int d = 0; d < D; ++d)
+        o[d] = 0.0;
+    if (n == 0) {
+        *lse = -INFINITY;
+        return;
+    }
+    double *s = malloc(sizeof(double) * (size_t)n);
+    double m = -INFINITY;
+    for (int j = 0; j < n; ++j) {
+        s[j] = scale * dot(q, K + (size_t)j * D, D);
+        if (s[j] > m)
+            m = s[j];
+    }
+    double sum = 0.0;
+    for (int j = 0; j < n; ++j)
+        sum += exp(s[j] - m);
+    for (int j = 0; j < n; ++j) {
+        double pj = exp(s[j] - m) / sum;
+        if (p)
+            p[j] = pj;
+        for (int d = 0; d < D; ++d)
+            o[d] += pj * V[(size_t)j * D + d];
+    }
+    *lse = m + log(sum);
+    free(s);
+}
+
+/* Skip-softmax over `tile`-key tiles in ascending order.  map: one code per tile slot (width stride);
+ * replay (nullable): decisions to impose, 1 = skip, 0 = process.  Returns 0, or -1 on a bad replay. */
+static int skip_row(const double *q, const double *K, const double *V, int n, int D, double scale,
+                    int tile, double thr, const uint8_t *replay, int stride, double *o, double *lse,
+                    uint8_t *map)
+{
+    int ntiles = (n + tile - 1) / tile;
+    if (ntiles > stride)
+        return -1;
+    if (map)
+        for (int t = 0; t < stride; ++t)
+            map[t] = MAP_UNVISITED;
+    double m = -INFINITY, l = 0.0;
+    double *acc = calloc((size_t)D, sizeof(double));
+    double *s = malloc(sizeof(double) * (size_t)tile);
+    int rc = 0;
+    for (int t = 0; t < ntiles; ++t) {
+        int j0 = t * tile, j1 = j0 + tile < n ? j0 + tile : n;
+        double tmax = -INFINITY;
+        for (int j = j0; j < j1; ++j) {
+            s[j - j0] = scale * dot(q, K + (size_t)j * D, D);
+            if (s[j - j0] > tmax)
+                tmax = s[j - j0];
+        }
+        int skip;
+        if (replay) {
+            if (replay[t] > 1) {
+                rc = -1;
+                break;
+            }
+            skip = replay[t] == 1;
+        } else {
+            skip = thr > 0.0 && m > -INFINITY && exp(tmax - m) < thr;
+        }
+        if (map)
+            map[t] = skip ? MAP_SKIPPED : MAP_DONE;
+        if (skip)
+            continue;
+        double m_new = tmax > m ? tmax : m;
+        double alpha = m == -INFINITY ? 0.0 : exp(m - m_new);
+        l *= alpha;
+        for (int d = 0; d < D; ++d)
+            acc[d] *= alpha;
+        for (int j = j0; j < j1; ++j) {
+            double e = exp(s[j - j0] - m_new);
+            l += e;
+            for (int d = 0; d < D; ++d)
+                acc[d] += e * V[(size_t)j * D + d];
+        }
+        m = m_new;
+    }
+    if (rc == 0) {
+        for (int d = 0; d < D; ++d)
+            o[d] = l > 0.0 ? acc[d] / l : 0.0;
+        *lse = l > 0.0 ? m + log(l) : -INFINITY;
+    }
+    free(acc);
+    free(s);
+    return rc;
+}
+
+/* Split-K: dense attention per contiguous chunk of tiles, then the log-sum-exp merge. */
+static void split_row(const double *q, const double *K, const double *V, int n, int D, double scale,
+                      int tile, int S, double *o, double *lse)
+{
+    int ntiles = (n + tile - 1) / tile;
+    int c = (ntiles + S - 1) / S;
+    double *os = malloc(sizeof(double) * (size_t)S * D);
+    double *ls = malloc(sizeof(double) * (size_t)S);
+    for (int sp = 0; sp < S; ++sp) {
+        long j0 = (long)sp * c * tile, j1 = (long)(sp + 1) * c * tile;
+        if (j0 > n)
+            j0 = n;
+        if (j1 > n)
+            j1 = n;
+        dense_row(q, K + j0 * D, V + j0 * D, (int)(j1 - j0), D, scale, os + (size_t)sp * D, ls + sp, NULL);
+    }
+    double mx = -INFINITY;
+    for (int sp = 0; sp < S; ++sp)
+        if (ls[sp] > mx)
+            mx = ls[sp];
+    for (int d = 0; d < D; ++d)
+        o[d] = 0.0;
+    if (mx == -INFINITY) {
+        *lse = -INFINITY;
+    } else {
+        double sum = 0.0;
+        for (int sp = 0; sp < S; ++sp)
+            if (ls[sp] > -INFINITY)
+                sum += exp(ls[sp] - mx);
+        *lse = mx + log(sum);
+        for (int sp = 0; sp < S; ++sp) {
+            if (ls[sp] == -INFINITY)
+                continue;
+            double w = exp(ls[sp] - *lse);
+            for (int d = 0; d < D; ++d)
+                o[d] += w * os[(size_t)sp * D + d];
+        }
+    }
+    free(os);
+    free(ls);
+}
+
+static int run_mode(int mode, const double *q, const double *K, const double *V, int n, int D,
+                    double scale, int tile, double thr, int splits, const uint8_t *replay, int stride,
+                    double *o, double *lse, uint8_t *map)
+{
+    switch (mode) {
+    case MODE_DENSE:
+        dense_row(q, K, V, n, D, scale, o, lse, NULL);
+        return 0;
+    case MODE_SKIP:
+        return skip_row(q, K, V, n, D, scale, tile, thr, replay, stride, o, lse, map);
+    case MODE_SPLIT:
+        if (splits < 1)
+            return -1;
+        split_row(q, K, V, n, D, scale, tile, splits, o, lse);
+        return 0;
+    }
+    return -1;
+}
+
+/*
+ * Varlen (THD) attention, "Model-Optimizer: Add Triton unified attention kernel" (variable-length
+ * batching, GQA, causal and non-causal) with sequences packed by cu_seqlens ("ROCm TransformerEngine:
+ * Integrate CK varlen cross attention", THD with cu_seqlens).
+ * q [tq, Hq, D], k/v [tk, Hkv, D]; rows: n_rows pairs (token, head).  Query row i of sequence b sees keys
+ * j < Lk when non-causal and j <= i + (Lk - Lq) when causal (bottom-right aligned).
+ * Outputs per requested row: o [n_rows, D], lse [n_rows], map [n_rows, stride] (MODE_SKIP, nullable).
+ */
+int orc_prefill_rows(int dtype, const void *q, const void *k, const void *v, const int32_t *cu_q,
+                     const int32_t *cu_k, int B, int Hq, int Hkv, int D, double scale, int causal,
+                     int mode, double thr, int tile, int splits, const int32_t *rows, int n_rows,
+                     const uint8_t *replay, int stride, double *o, double *lse, uint8_t *map)
+{
+    if (B < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv || D <= 0 || (mode != MODE_DENSE && tile <= 0))
+        return -1;
+    int G = Hq / Hkv, bad = 0;
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : bad)
+    for (int r = 0; r < n_rows; ++r) {
+        int t = rows[2 * r], h = rows[2 * r + 1];
+        int b = -1;
+        for (int bb = 0; bb < B; ++bb)
+            if (cu_q[bb] <= t && t < cu_q[bb + 1]) {
+                b = bb;
+                break;
+            }
+        if (b < 0 || h < 0 || h >= Hq) {
+            bad = 1;
+            continue;
+        }
+        int Lq = cu_q[b + 1] - cu_q[b], Lk = cu_k[b + 1] - cu_k[b], i = t - cu_q[b], g = h / G;
+        int n = Lk;
+        if (causal) {
+            n = i + 1 + (Lk - Lq);
+            if (n < 0)
+                n = 0;
+            if (n > Lk)
+                n = Lk;
+        }
+        double *qd = malloc(sizeof(double) * D);
+        double *K = malloc(sizeof(double) * ((size_t)n * D + 1));
+        double *V = malloc(sizeof(double) * ((size_t)n * D + 1));
+        for (int d = 0; d < D; ++d)
+            qd[d] = widen(q, dtype, ((size_t)t * Hq + h) * D + d);
+        for (int j = 0; j < n; ++j)
+            for (int d = 0; d < D; ++d) {
+                size_t src = ((size_t)(cu_k[b] + j) * Hkv + g) * D + d;
+                K[(size_t)j * D + d] = widen(k, dtype, src);
+                V[(size_t)j * D + d] = widen(v, dtype, src);
+            }
+        if (run_mode(mode, qd, K, V, n, D, scale, tile, thr, splits, replay ? replay + (size_t)r * stride : NULL,
+                     stride, o + (size_t)r * D, lse + r, map ? map + (size_t)r * stride : NULL))
+            bad = 1;
+        free(qd);
+        free(K);
+        free(V);
+    }
+    return bad ? -1 : 0;
+}
+
+/*
+ * One-token paged decode, "Model-Optimizer: Add split-k decode kernel for skip softmax", Usage
+ * (query, key_cache, value_cache, block_table, sequence_lengths): the single query token of batch row b
+ * sees all seq_lens[b] cached keys.  q [B, Hq, D] bf16; caches [num_pages, Hkv, page, D] bf16.
+ * rows: n_rows pairs (b, head).  Outputs as for orc_prefill_rows.
+ */
+int orc_decode_rows(const void *q, const void *kc, const void *vc, const int32_t *block_table,
+                    const int32_t *seq_lens, int B, int Hq, int Hkv, int D, int page, int max_pages,
+                    double scale, int mode, double thr, int tile, int splits, const int32_t *rows,
+                    int n_rows, const uint8_t *replay, int stride, double *o, double *lse, uint8_t *map)
+{
+    if (B < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv || D <= 0 || page <= 0 || (mode != MODE_DENSE && tile <= 0))
+        return -1;
+    int G = Hq / Hkv, bad = 0;
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : bad)
+    for (int r = 0; r < n_rows; ++r) {
+        int b = rows[2 * r], h = rows[2 * r + 1];
+        if (b < 0 || b >= B || h < 0 || h >= Hq || seq_lens[b] < 0 || seq_lens[b] > max_pages * page) {
+            bad = 1;
+            continue;
+        }
+        int n = seq_lens[b], g = h / G;
+        double *qd = malloc(sizeof(double) * D);
+        double *K = malloc(sizeof(double) * ((size_t)n * D + 1));
+        double *V = malloc(sizeof(double) * ((size_t)n * D + 1));
+        for (int d = 0; d < D; ++d)
+            qd[d] = widen(q, ORC_BF16, ((size_t)b * Hq + h) * D + d);
+        for (int j = 0; j < n; ++j) {
+            int pg = block_table[(size_t)b * max_pages + j / page];
+            for (int d = 0; d < D; ++d) {
+                size_t src = (((size_t)pg * Hkv + g) * page + j % page) * D + d;
+                K[(size_t)j * D + d] = widen(kc, ORC_BF16, src);
+                V[(size_t)j * D + d] = widen(vc, ORC_BF16, src);
+            }
+        }
+        if (run_mode(mode, qd, K, V, n, D, scale, tile, thr, splits, replay ? replay + (size_t)r * stride : NULL,
+                     stride, o + (size_t)r * D, lse + r, map ? map + (size_t)r * stride : NULL))
+            bad = 1;
+        free(qd);
+        free(K);
+        free(V);
+    }
+    return bad ? -1 : 0;
+}
+
+/*
+ * Small-seq cross-attention, "ROCm TransformerEngine: Integrate CK varlen cross attention for small-seq
+ * (s_q=1, s_kv<=16)": one query token per sequence, s_kv = cu_kv[b+1] - cu_kv[b] keys, non-causal,
+ * H query heads = H KV heads.  Besides o it returns the attention weights w[b, h, 0, j] = p_j for
+ * j < s_kv and 0 for s_kv <= j < max_s.  q [B, H, D], k/v [total_kv, H, D] (dtype).
+ * rows: n_rows pairs (b, head); o [n_rows, D], w [n_rows, max_s].
+ */
+int orc_smallseq_rows(int dtype, const void *q, const void *k, const void *v, const int32_t *cu_kv, int B,
+                      int H, int D, int max_s, double scale, const int32_t *rows, int n_rows, double *o,
+                      double *w)
+{
+    if (B < 0 || H <= 0 || D <= 0 || max_s < 0)
+        return -1;
+    int bad = 0;
+#pragma omp parallel for schedule(dynamic, 16) reduction(| : bad)
+    for (int r = 0; r < n_rows; ++r) {
+        int b = rows[2 * r], h = rows[2 * r + 1];
+        if (b < 0 || b >= B || h < 0 || h >= H) {
+            bad = 1;
+            continue;
+        }
+        int n = cu_kv[b + 1] - cu_kv[b];
+        if (n < 0 || n > max_s) {
+            bad = 1;
+            continue;
+        }
+        double *qd = malloc(sizeof(double) * D);
+        double *K = malloc(sizeof(double) * ((size_t)n * D + 1));
+        double *V = malloc(sizeof(double) * ((size_t)n * D + 1));
+        double *p = malloc(sizeof(double) * ((size_t)n + 1)), lse;
+        for (int d = 0; d < D; ++d)
+            qd[d] = widen(q, dtype, ((size_t)b * H + h) * D + d);
+        for (int j = 0; j < n; ++j)
+            for (int d = 0; d < D; ++d) {
+                size_t src = ((size_t)(cu_kv[b] + j) * H + h) * D + d;
+                K[(size_t)j * D + d] = widen(k, dtype, src);
+                V[(size_t)j * D + d] = widen(v, dtype, src);
+            }
+        dense_row(qd, K, V, n, D, scale, o + (size_t)r * D, &lse, p);
+        for (int j = 0; j < max_s; ++j)
+            w[(size_t)r * max_s + j] = j < n ? p[j] : 0.0;
+        free(qd);
+        free(K);
+        free(V);
+        free(p);
+    }
+    return bad ? -1 : 0;
+}

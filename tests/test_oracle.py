@@ -1,0 +1,365 @@
+"""Pins for the fp64 oracle: brute force, a library special case, closed forms and invariants.
+
+Each test checks the oracle against something other than itself, so that a dropped term, a wrong sign,
+a wrong index or a transposed operand in oracle/oracle.c fails at least one of them.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import brute
+import oracle
+from paged_skip_softmax_amd import workloads as W
+
+TOL = 1e-12
+
+
+def _f64(x):
+    return x.detach().cpu().double().numpy() if isinstance(x, torch.Tensor) else np.asarray(x, np.float64)
+
+
+# ---------------------------------------------------------------- brute force, tiny inputs
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_prefill_dense_matches_brute_force(causal, dtype):
+    lens = [5, 1, 17, 33]
+    x = W.varlen_prefill(seed=7, lengths=lens, Hq=4, Hkv=2, D=8, dtype=dtype)
+    o, lse, _ = oracle.prefill(x.q, x.k, x.v, x.cu_q, x.cu_k, 4, 2, 0.37, causal)
+    q, k, v = _f64(x.q), _f64(x.k), _f64(x.v)
+    start = 0
+    for L in lens:
+        for i in range(L):
+            for h in range(4):
+                g = h // 2
+                nvis = i + 1 if causal else L
+                keys = [list(k[start + j, g]) for j in range(nvis)]
+                vals = [list(v[start + j, g]) for j in range(nvis)]
+                ob, lb, _ = brute.softmax_attend(brute.scores(list(q[start + i, h]), keys, 0.37), vals)
+                assert np.max(np.abs(o[start + i, h] - ob)) < TOL
+                assert abs(lse[start + i, h] - lb) < TOL
+        start += L
+
+
+def test_decode_dense_matches_brute_force():
+    x = W.paged_decode(seed=3, B=3, Hq=4, Hkv=2, D=8, page=4, pool=64, lengths=[1, 6, 13], lmax=16)
+    o, lse, _ = oracle.decode(x.q, x.k_cache, x.v_cache, x.block_table, x.seq_lens, 0.5)
+    q, kc, vc = _f64(x.q), _f64(x.k_cache), _f64(x.v_cache)
+    bt = x.block_table.numpy()
+    for b, L in enumerate([1, 6, 13]):
+        for h in range(4):
+            keys = [list(kc[bt[b, j // 4], h // 2, j % 4]) for j in range(L)]
+            vals = [list(vc[bt[b, j // 4], h // 2, j % 4]) for j in range(L)]
+            ob, lb, _ = brute.softmax_attend(brute.scores(list(q[b, h]), keys, 0.5), vals)
+            assert np.max(np.abs(o[b, h] - ob)) < TOL and abs(lse[b, h] - lb) < TOL
+
+
+@pytest.mark.parametrize("thr", [0.0, 0.05, 0.3, 0.9])
+@pytest.mark.parametrize("tile", [4, 7])
+def test_skip_matches_brute_force(thr, tile):
+    # a few large-logit keys make skipping common
+    lens = [3, 29, 40]
+    x = W.varlen_prefill(seed=11, lengths=lens, Hq=2, Hkv=1, D=6, dtype=torch.float32)
+    kk = x.k.clone()
+    kk[10:13] += 3.0 * x.q[10:13, :1].sign()
+    o, lse, mp = oracle.prefill(x.q, kk, x.v, x.cu_q, x.cu_k, 2, 1, 0.8, True, mode="skip", thr=thr,
+                                tile=tile)
+    q, k, v = _f64(x.q), _f64(kk), _f64(x.v)
+    start = 0
+    for L in lens:
+        for i in range(L):
+            for h in range(2):
+                keys = [list(k[start + j, 0]) for j in range(i + 1)]
+                vals = [list(v[start + j, 0]) for j in range(i + 1)]
+                ob, lb, dec = brute.skip_attend(brute.scores(list(q[start + i, h]), keys, 0.8), vals, tile, thr)
+                assert np.max(np.abs(o[start + i, h] - ob)) < TOL and abs(lse[start + i, h] - lb) < TOL
+                got = list(mp[start + i, h, :len(dec)])
+                assert got == dec
+                assert all(c == 2 for c in mp[start + i, h, len(dec):])
+        start += L
+
+
+def test_skip_replay_imposes_decisions():
+    x = W.varlen_prefill(seed=12, lengths=[64], Hq=1, Hkv=1, D=4, dtype=torch.float32)
+    o0, _, m0 = oracle.prefill(x.q, x.k, x.v, x.cu_q, x.cu_k, 1, 1, 0.5, False, mode="skip", thr=0.0, tile=8)
+    rng = np.random.default_rng(0)
+    rep = (rng.random(m0.shape) < 0.4).astype(np.uint8)
+    rep[..., 0] = 0
+    o1, lse1, m1 = oracle.prefill(x.q, x.k, x.v, x.cu_q, x.cu_k, 1, 1, 0.5, False, mode="skip", tile=8,
+                                  replay=rep.reshape(64, -1), stride=m0.shape[-1])
+    assert np.array_equal(m1, rep)
+    q, k, v = _f64(x.q), _f64(x.k), _f64(x.v)
+    for i in range(64):
+        keep = [j for j in range(64) if rep[i, 0, j // 8] == 0]
+        ob, lb, _ = brute.softmax_attend(brute.scores(list(q[i, 0]), [list(k[j, 0]) for j in keep], 0.5),
+                                         [list(v[j, 0]) for j in keep])
+        assert np.max(np.abs(o1[i, 0] - ob)) < TOL and abs(lse1[i, 0] - lb) < TOL
+
+
+def test_smallseq_matches_brute_force():
+    x = W.smallseq_cross(seed=5, B=6, H=3, D=8)
+    o, w = oracle.smallseq(x.q, x.k, x.v, x.cu_kv, x.max_s, 0.3)
+    q, k, v = _f64(x.q), _f64(x.k), _f64(x.v)
+    cu = x.cu_kv.numpy()
+    for b in range(6):
+        for h in range(3):
+            keys = [list(k[j, h]) for j in range(cu[b], cu[b + 1])]
+            vals = [list(v[j, h]) for j in range(cu[b], cu[b + 1])]
+            ob, _, p = brute.softmax_attend(brute.scores(list(q[b, h]), keys, 0.3), vals)
+            assert np.max(np.abs(o[b, h] - ob)) < TOL
+            assert np.max(np.abs(w[b, h, 0, :len(p)] - p)) < TOL
+            assert np.all(w[b, h, 0, len(p):] == 0)
+
+
+# ---------------------------------------------------------------- library special case
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_prefill_matches_torch_sdpa_fp64(causal, dtype):
+    lens = [37, 128, 64]
+    x = W.varlen_prefill(seed=21, lengths=lens, Hq=8, Hkv=2, D=32, dtype=dtype)
+    o, lse, _ = oracle.prefill(x.q, x.k, x.v, x.cu_q, x.cu_k, 8, 2, x.scale, causal)
+    cu = x.cu_q.tolist()
+    for b in range(3):
+        q = x.q[cu[b]:cu[b + 1]].double().transpose(0, 1)
+        k = x.k[cu[b]:cu[b + 1]].double().transpose(0, 1).repeat_interleave(4, 0)
+        v = x.v[cu[b]:cu[b + 1]].double().transpose(0, 1).repeat_interleave(4, 0)
+        ref = torch.nn.functional.scaled_dot_product_attention(q, k, v, is_causal=causal, scale=x.scale)
+        assert np.max(np.abs(o[cu[b]:cu[b + 1]] - ref.transpose(0, 1).numpy())) < TOL
+
+
+# ---------------------------------------------------------------- closed forms
+
+def test_closed_forms():
+    # worked by hand: q=(1,0), keys e1,e2, values e1,e2, scale 1 -> p = (e, 1)/(e+1)
+    q = torch.tensor([[[1.0, 0.0]]])
+    k = torch.tensor([[[1.0, 0.0]], [[0.0, 1.0]]])
+    cu_q, cu_k = torch.tensor([0, 1], dtype=torch.int32), torch.tensor([0, 2], dtype=torch.int32)
+    o, lse, _ = oracle.prefill(q, k, k.clone(), cu_q, cu_k, 1, 1, 1.0, False)
+    e = math.e
+    assert np.allclose(o[0, 0], [e / (e + 1), 1 / (e + 1)], atol=TOL, rtol=0)
+    assert abs(lse[0, 0] - math.log(e + 1)) < TOL
+
+    x = W.varlen_prefill(seed=2, lengths=[9], Hq=2, Hkv=1, D=5, dtype=torch.float32)
+    v = x.v
+    # identical keys -> mean of V
+    kk = x.k[:1].expand(9, 1, 5).contiguous()
+    o, lse, _ = oracle.prefill(x.q, kk, v, x.cu_q, x.cu_k, 2, 1, 0.7, False)
+    assert np.max(np.abs(o - _f64(v).mean(0)[None, 0:1])) < TOL
+    # q = 0 -> mean of V and lse = log n
+    o, lse, _ = oracle.prefill(torch.zeros_like(x.q), x.k, v, x.cu_q, x.cu_k, 2, 1, 0.7, False)
+    assert np.max(np.abs(o - _f64(v).mean(0)[None, 0:1])) < TOL
+    assert np.max(np.abs(lse - math.log(9))) < TOL
+    # constant V -> that constant
+    o, _, _ = oracle.prefill(x.q, x.k, torch.full_like(v, 1.25), x.cu_q, x.cu_k, 2, 1, 0.7, True)
+    assert np.max(np.abs(o - 1.25)) < TOL
+    # a single visible key (causal row 0) -> that key's value, lse = its logit
+    o, lse, _ = oracle.prefill(x.q, x.k, v, x.cu_q, x.cu_k, 2, 1, 0.7, True)
+    assert np.max(np.abs(o[0] - _f64(v)[0, 0])) < TOL
+    s00 = 0.7 * float(_f64(x.q)[0, 0] @ _f64(x.k)[0, 0])
+    assert abs(lse[0, 0] - s00) < TOL
+
+
+def test_probabilities_sum_to_one_and_lse_normalises():
+    x = W.varlen_prefill(seed=4, lengths=[50], Hq=2, Hkv=2, D=16, dtype=torch.bfloat16)
+    o, lse, _ = oracle.prefill(x.q, x.k, x.v, x.cu_q, x.cu_k, 2, 2, 0.25, False)
+    s = 0.25 * np.einsum("ihd,jhd->hij", _f64(x.q), _f64(x.k))
+    tot = np.exp(s - lse.T[:, :, None]).sum(-1)
+    assert np.max(np.abs(tot - 1)) < TOL
+    # o is the probability-weighted sum of V
+    p = np.exp(s - lse.T[:, :, None])
+    assert np.max(np.abs(np.einsum("hij,jhd->ihd", p, _f64(x.v)) - o)) < 1e-10
+    xs = W.smallseq_cross(seed=9, B=40, H=2, D=16)
+    _, w = oracle.smallseq(xs.q, xs.k, xs.v, xs.cu_kv, xs.max_s, xs.scale)
+    assert np.max(np.abs(w.sum(-1) - 1)) < TOL
+
+
+# ---------------------------------------------------------------- invariants
+
+def test_varlen_equals_per_sequence_and_empty_sequences():
+    lens_q, lens_k = [3, 0, 6, 2], [5, 4, 0, 2]
+    Hq, Hkv, D = 4, 2, 8
+    gq = torch.Generator().manual_seed(1)
+    q = torch.randn(sum(lens_q), Hq, D, generator=gq)
+    k = torch.randn(sum(lens_k), Hkv, D, generator=gq)
+    v = torch.randn(sum(lens_k), Hkv, D, generator=gq)
+    cu_q = torch.tensor([0, 3, 3, 9, 11], dtype=torch.int32)
+    cu_k = torch.tensor([0, 5, 9, 9, 11], dtype=torch.int32)
+    for causal in (False, True):
+        o, lse, _ = oracle.prefill(q, k, v, cu_q, cu_k, Hq, Hkv, 0.3, causal)
+        for b in range(4):
+            sq, sk = slice(int(cu_q[b]), int(cu_q[b + 1])), slice(int(cu_k[b]), int(cu_k[b + 1]))
+            one = torch.tensor([0, lens_q[b]], dtype=torch.int32)
+            onek = torch.tensor([0, lens_k[b]], dtype=torch.int32)
+            ob, lb, _ = oracle.prefill(q[sq], k[sk], v[sk], one, onek, Hq, Hkv, 0.3, causal)
+            assert np.array_equal(o[sq], ob) and np.array_equal(lse[sq], lb)
+        # the sequence with no keys gives zeros and lse = -inf
+        assert np.all(o[cu_q[2]:cu_q[3]] == 0) and np.all(np.isneginf(lse[cu_q[2]:cu_q[3]]))
+    # causal with Lq < Lk is bottom-right aligned: the last query row sees every key
+    o, _, _ = oracle.prefill(q, k, v, cu_q, cu_k, Hq, Hkv, 0.3, True)
+    on, _, _ = oracle.prefill(q, k, v, cu_q, cu_k, Hq, Hkv, 0.3, False)
+    assert np.array_equal(o[2], on[2])
+
+
+def test_gqa_equals_mha_with_repeated_kv():
+    x = W.varlen_prefill(seed=8, lengths=[20, 7], Hq=8, Hkv=2, D=8, dtype=torch.float32)
+    o, lse, _ = oracle.prefill(x.q, x.k, x.v, x.cu_q, x.cu_k, 8, 2, 0.4, True)
+    k4, v4 = x.k.repeat_interleave(4, 1), x.v.repeat_interleave(4, 1)
+    om, lm, _ = oracle.prefill(x.q, k4, v4, x.cu_q, x.cu_k, 8, 8, 0.4, True)
+    assert np.array_equal(o, om) and np.array_equal(lse, lm)
+    # a transposed head map (h % Hkv instead of h // G) would differ
+    kt, vt = x.k.repeat(1, 4, 1), x.v.repeat(1, 4, 1)
+    ot, _, _ = oracle.prefill(x.q, kt, vt, x.cu_q, x.cu_k, 8, 8, 0.4, True)
+    assert not np.allclose(o, ot)
+
+
+def test_causal_row_equals_prefix_attention():
+    x = W.varlen_prefill(seed=10, lengths=[24], Hq=2, Hkv=1, D=8, dtype=torch.float32)
+    o, lse, _ = oracle.prefill(x.q, x.k, x.v, x.cu_q, x.cu_k, 2, 1, 0.6, True)
+    for i in (0, 5, 23):
+        cu_q = torch.tensor([0, 1], dtype=torch.int32)
+        cu_k = torch.tensor([0, i + 1], dtype=torch.int32)
+        oi, li, _ = oracle.prefill(x.q[i:i + 1], x.k[:i + 1], x.v[:i + 1], cu_q, cu_k, 2, 1, 0.6, False)
+        assert np.max(np.abs(oi[0] - o[i])) < TOL and np.max(np.abs(li[0] - lse[i])) < TOL
+
+
+def _small_paged(seed=13, hot=False):
+    return W.paged_decode(seed=seed, B=4, Hq=4, Hkv=2, D=16, page=16, pool=200, lengths=[1, 100, 700, 33],
+                          lmax=1024, hot=hot)
+
+
+def test_paged_block_table_permutation_invariance():
+    x = _small_paged()
+    o, lse, _ = oracle.decode(x.q, x.k_cache, x.v_cache, x.block_table, x.seq_lens, x.scale)
+    perm = torch.randperm(x.pool, generator=torch.Generator().manual_seed(99))
+    inv = torch.empty_like(perm)
+    inv[perm] = torch.arange(x.pool)
+    kc2, vc2 = x.k_cache[perm].contiguous(), x.v_cache[perm].contiguous()   # page p moves to inv[p]
+    bt2 = x.block_table.clone()
+    m = bt2 >= 0
+    bt2[m] = inv[bt2[m].long()].to(torch.int32)
+    o2, lse2, _ = oracle.decode(x.q, kc2, vc2, bt2, x.seq_lens, x.scale)
+    assert np.array_equal(o, o2) and np.array_equal(lse, lse2)
+    # a table that is not remapped reads other pages and changes the result
+    o3, _, _ = oracle.decode(x.q, kc2, vc2, x.block_table, x.seq_lens, x.scale)
+    assert not np.allclose(o[1:], o3[1:])
+
+
+def test_paged_equals_contiguous():
+    x = _small_paged()
+    lens = x.lens.tolist()
+    kk, vv = [], []
+    for b, L in enumerate(lens):
+        for j in range(L):
+            p = int(x.block_table[b, j // 16])
+            kk.append(x.k_cache[p, :, j % 16])
+            vv.append(x.v_cache[p, :, j % 16])
+    k, v = torch.stack(kk), torch.stack(vv)
+    cu_k = torch.tensor([0] + list(np.cumsum(lens)), dtype=torch.int32)
+    cu_q = torch.arange(5, dtype=torch.int32)
+    o, lse, _ = oracle.decode(x.q, x.k_cache, x.v_cache, x.block_table, x.seq_lens, x.scale)
+    op, lp, _ = oracle.prefill(x.q, k, v, cu_q, cu_k, 4, 2, x.scale, False)
+    assert np.max(np.abs(o - op)) < TOL and np.max(np.abs(lse - lp)) < TOL
+
+
+@pytest.mark.parametrize("S", [1, 2, 7, 32, 64])
+def test_split_merge_equals_unsplit(S):
+    x = _small_paged()
+    o, lse, _ = oracle.decode(x.q, x.k_cache, x.v_cache, x.block_table, x.seq_lens, x.scale)
+    os_, ls_, _ = oracle.decode(x.q, x.k_cache, x.v_cache, x.block_table, x.seq_lens, x.scale, mode="split",
+                                tile=128, splits=S)
+    assert np.max(np.abs(o - os_)) < TOL and np.max(np.abs(lse - ls_)) < TOL
+
+
+def test_skip_threshold_zero_is_dense():
+    x = _small_paged(hot=True)
+    o, lse, _ = oracle.decode(x.q, x.k_cache, x.v_cache, x.block_table, x.seq_lens, x.scale)
+    o0, l0, m0 = oracle.decode(x.q, x.k_cache, x.v_cache, x.block_table, x.seq_lens, x.scale, mode="skip", thr=0.0)
+    assert np.max(np.abs(o - o0)) < TOL and np.max(np.abs(lse - l0)) < TOL
+    assert set(np.unique(m0)) <= {0, 2}
+    xp = W.tiny_dense(seed=1000)
+    for causal in (False, True):
+        od, ld, _ = oracle.prefill(xp.q, xp.k, xp.v, xp.cu_q, xp.cu_k, 4, 2, xp.scale, causal)
+        os_, ls_, ms = oracle.prefill(xp.q, xp.k, xp.v, xp.cu_q, xp.cu_k, 4, 2, xp.scale, causal, mode="skip",
+                                      thr=0.0)
+        assert np.max(np.abs(od - os_)) < TOL and np.max(np.abs(ld - ls_)) < TOL
+        assert set(np.unique(ms)) <= {0, 2}
+
+
+def _decode_scores(x, b, h):
+    L = int(x.lens[b])
+    g = h // (x.Hq // x.Hkv)
+    q = _f64(x.q[b, h])
+    ks = np.stack([_f64(x.k_cache[int(x.block_table[b, j // x.page]), g, j % x.page]) for j in range(L)])
+    vs = np.stack([_f64(x.v_cache[int(x.block_table[b, j // x.page]), g, j % x.page]) for j in range(L)])
+    return x.scale * ks @ q, vs
+
+
+def test_skip_prefix_max_lemma_nesting_and_error_bound():
+    x = _small_paged(hot=True)
+    maps = {}
+    outs = {}
+    for thr in (0.01, 0.1, 0.5):
+        o, lse, m = oracle.decode(x.q, x.k_cache, x.v_cache, x.block_table, x.seq_lens, x.scale, mode="skip",
+                                  thr=thr)
+        maps[thr], outs[thr] = m, o
+    od, _, _ = oracle.decode(x.q, x.k_cache, x.v_cache, x.block_table, x.seq_lens, x.scale)
+    nskip = 0
+    for b in range(x.B):
+        L = int(x.lens[b])
+        nt = (L + 31) // 32
+        for h in range(x.Hq):
+            s, vs = _decode_scores(x, b, h)
+            tmax = np.array([s[32 * t:32 * t + 32].max() for t in range(nt)])
+            for thr, m in maps.items():
+                # decisions follow the prefix max of all earlier tiles, skipped ones included
+                pref = np.concatenate([[-np.inf], np.maximum.accumulate(tmax)[:-1]])
+                want = (pref > -np.inf) & (np.exp(tmax - pref) < thr)
+                assert np.array_equal(m[b, h, :nt] == 1, want)
+                assert np.all(m[b, h, nt:] == 2)
+                # the tile holding the global max is never skipped
+                assert m[b, h, int(np.argmax(tmax))] == 0
+                # error bound against dense attention
+                M = s.max()
+                skipped = np.repeat(m[b, h, :nt] == 1, 32)[:L]
+                A = np.exp(s[~skipped] - M).sum()
+                Bd = np.exp(s[skipped] - M).sum()
+                assert Bd < thr * max(1, skipped.sum())
+                bound = Bd / (A + Bd) * (vs.max(0) - vs.min(0))
+                assert np.all(np.abs(outs[thr][b, h] - od[b, h]) <= bound + 1e-12)
+                nskip += int(skipped.any())
+    # skip sets are nested as the threshold grows
+    assert np.all((maps[0.01] == 1) <= (maps[0.1] == 1)) and np.all((maps[0.1] == 1) <= (maps[0.5] == 1))
+    assert nskip > 0
+
+
+def test_smallseq_invariants():
+    xs = W.smallseq_cross(seed=17, B=64, H=4, D=32)
+    o, w = oracle.smallseq(xs.q, xs.k, xs.v, xs.cu_kv, 16, xs.scale)
+    cu = xs.cu_kv.tolist()
+    v = _f64(xs.v)
+    for b in range(64):
+        s = cu[b + 1] - cu[b]
+        assert np.all(w[b, :, 0, s:] == 0)
+        # o = W . V
+        assert np.max(np.abs(np.einsum("hj,jhd->hd", w[b, :, 0, :s], v[cu[b]:cu[b + 1]]) - o[b])) < 1e-12
+    # equals dense prefill with one query per sequence
+    cu_q = torch.arange(65, dtype=torch.int32)
+    op, _, _ = oracle.prefill(xs.q, xs.k, xs.v, cu_q, xs.cu_kv, 4, 4, xs.scale, False)
+    assert np.max(np.abs(o - op)) < TOL
+    # a zero-length sequence gives zero output and zero weights
+    cu0 = xs.cu_kv.clone()
+    cu0[1] = cu0[0]
+    o0, w0 = oracle.smallseq(xs.q[:1], xs.k, xs.v, cu0[:2], 16, xs.scale)
+    assert np.all(o0 == 0) and np.all(w0 == 0)
+
+
+def test_hot_key_workload_makes_most_tiles_skippable():
+    x = W.paged_decode(seed=5, B=2, Hq=8, Hkv=2, D=128, page=16, pool=1200, lengths=[4000, 6000], lmax=8192,
+                       hot=True)
+    _, _, m = oracle.decode(x.q, x.k_cache, x.v_cache, x.block_table, x.seq_lens, x.scale, mode="skip", thr=0.1)
+    visited = m != 2
+    frac = (m == 1).sum() / visited.sum()
+    assert frac > 0.5, frac
