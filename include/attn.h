@@ -1,0 +1,133 @@
+/*
+ * attn.h -- C ABI of libattn.so, FlashAttention-style tiled attention with online softmax for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The operations are the ones the source pages describe:
+ *   - varlen prefill: "Model-Optimizer: Add Triton unified attention kernel with HuggingFace integration"
+ *     (variable-length batching, GQA, causal and non-causal masking), sequences packed THD with
+ *     cu_seqlens as in "ROCm TransformerEngine: Integrate CK varlen cross attention", change list;
+ *   - one-token paged decode with split-K and skip-softmax: "Model-Optimizer: Add split-k decode kernel
+ *     for skip softmax", What does this PR do (one sequential split of 32-token tiles when skip-softmax
+ *     is on, 32 splits of 128-token tiles when it is off, threshold validated and passed at run time)
+ *     and Usage (query, key_cache, value_cache, block_table, sequence_lengths, threshold);
+ *   - skip-softmax itself: "TensorRT-LLM: Skip Softmax Attention", Description -- a whole KV tile is
+ *     skipped (no exp, no P.V, no rescale) when exp(tile_max - running_max) < threshold;
+ *   - small-seq cross-attention: "ROCm TransformerEngine: Integrate CK varlen cross attention for
+ *     small-seq (s_q=1, s_kv<=16)", change list (one query per sequence, 2..16 keys, huge batch,
+ *     head_dim 128, BF16, attention weights written as [tokens_q, h_q, 1, max_seqlen_kv]).
+ *
+ * Conventions shared by every entry point
+ *   - Every data pointer is a DEVICE pointer, owned by the caller, to a dense row-major array.  The
+ *     library never allocates device memory, never synchronizes the stream, keeps no state besides a
+ *     thread-local error message, and is reentrant.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).  Work is enqueued on it
+ *     and the call returns before the GPU finishes.
+ *   - Arguments are validated on the host before any HIP runtime call; a rejected call launches
+ *     nothing and returns ATTN_ERR_INVALID / _UNSUPPORTED / _WORKSPACE.  Device-side contents
+ *     (monotone cu_seqlens, in-range block_table entries, seq_lens within the table) are
+ *     preconditions and are not checked.  ATTN_ERR_HIP reports a failed launch.
+ *   - GQA: query head h reads KV head h / (Hq / Hkv).
+ *   - Logits are scale * q.k; LSE outputs are the natural-log log-sum-exp of those logits, fp32; a row
+ *     that sees no key gets o = 0 and lse = -inf.
+ *   - skip_threshold must lie in [0, 1]; 0 reproduces dense attention.  Skip decisions are taken per
+ *     (query row, 32-key tile), tiles aligned to key 0 and visited in ascending order; the first
+ *     visited tile is never skipped.  Skip maps hold one byte per (row, tile):
+ *     0 = processed, 1 = skipped, 2 = not visited (no visible key).
+ */
+#ifndef ATTN_H
+#define ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    ATTN_OK = 0,
+    ATTN_ERR_INVALID = 1,     /* bad argument value or a required pointer is NULL            */
+    ATTN_ERR_UNSUPPORTED = 2, /* valid request this build has no kernel for (dtype, D, page) */
+    ATTN_ERR_WORKSPACE = 3,   /* workspace missing or smaller than the size query returned   */
+    ATTN_ERR_HIP = 4          /* the HIP runtime reported an error while launching           */
+} attn_status_t;
+
+typedef enum { ATTN_F32 = 0, ATTN_BF16 = 1 } attn_dtype_t;
+
+/* Width of the tiles skip decisions are taken on, in keys. */
+#define ATTN_SKIP_TILE 32
+
+/*
+ * Varlen prefill.
+ *   q [tq, Hq, D], k and v [tk, Hkv, D], o [tq, Hq, D], all of `dtype` (fp32 or bf16); tq = cu_seqlens_q[B],
+ *   tk = cu_seqlens_k[B].  cu_seqlens_q / cu_seqlens_k: int32 [B + 1], non-decreasing, starting at 0.
+ *   max_seqlen_q / max_seqlen_k: host upper bounds of the per-sequence lengths (size the launch grid).
+ *   causal != 0: query i of a sequence with Lq queries and Lk keys sees keys j <= i + Lk - Lq.
+ *   skip_threshold: see above; accumulation is fp32 and the P.V product is bf16 for bf16 inputs.
+ *   lse: nullable fp32 [tq, Hq].  skip_map: nullable uint8 [tq, Hq, skip_map_stride] with
+ *   skip_map_stride >= ceil(max_seqlen_k / 32); every entry of a row is written (2 past its visible keys).
+ *   Supported: bf16 with D in {64, 128}; fp32 with D = 64.  B == 0 is a no-op.
+ */
+attn_status_t attn_prefill_varlen(attn_dtype_t dtype, const void *q, const void *k, const void *v,
+                                  const int32_t *cu_seqlens_q, const int32_t *cu_seqlens_k, int32_t B,
+                                  int32_t max_seqlen_q, int32_t max_seqlen_k, int32_t Hq, int32_t Hkv,
+                                  int32_t D, float scale, int32_t causal, float skip_threshold, void *o,
+                                  float *lse, uint8_t *skip_map, int32_t skip_map_stride, void *stream);
+
+/*
+ * Bytes of workspace attn_decode_paged needs for the split-K schedule (num_splits > 1):
+ * per-split fp32 outputs [B, Hq, num_splits, D] and fp32 LSEs [B, Hq, num_splits].  0 when
+ * num_splits <= 1 (the sequential schedule needs none).  num_splits = 0 means the default for a
+ * dense call (32).
+ */
+size_t attn_decode_paged_workspace_size(int32_t B, int32_t Hq, int32_t D, int32_t num_splits);
+
+/*
+ * One-token paged decode: the single query token of batch row b attends to all seq_lens[b] cached keys.
+ *   q [B, Hq, D] bf16;  o [B, Hq, D] bf16;  lse nullable fp32 [B, Hq].
+ *   k_cache, v_cache: bf16 [num_pages, Hkv, page_size, D] -- one (page, kv head) is a contiguous
+ *   page_size x D slab.  Key j of row b is slot j % page_size of page block_table[b][j / page_size].
+ *   block_table: int32 [B, max_pages_per_seq], row-major; entries past ceil(seq_lens[b] / page_size)
+ *   are never read.  seq_lens: int32 [B], each in [0, max_pages_per_seq * page_size].
+ *   Cache slots past seq_lens[b] in the last page may hold anything (NaN included); they are masked.
+ *   num_splits: 0 = default (32 when skip_threshold == 0, else 1).  num_splits > 1 runs split-K over
+ *   128-key tiles: each split takes a contiguous run of ceil(ntiles / num_splits) tiles, writes
+ *   (O_s, lse_s) to the workspace and a second kernel merges them by log-sum-exp.  num_splits == 1
+ *   runs one sequential split over 32-key tiles with skip-softmax at `skip_threshold`; skip_threshold
+ *   > 0 requires num_splits == 1.  num_splits must be in [0, 64].
+ *   workspace: device buffer of at least attn_decode_paged_workspace_size() bytes (may be NULL when
+ *   that size is 0).  skip_map: nullable uint8 [B, Hq, skip_map_stride], sequential schedule only,
+ *   skip_map_stride >= ceil(max_pages_per_seq * page_size / 32).
+ *   Supported: D = 128, page_size = 16, Hq / Hkv <= 16.  B == 0 is a no-op.
+ */
+attn_status_t attn_decode_paged(const void *q, const void *k_cache, const void *v_cache,
+                                const int32_t *block_table, const int32_t *seq_lens, int32_t B, int32_t Hq,
+                                int32_t Hkv, int32_t D, int32_t page_size, int32_t num_pages,
+                                int32_t max_pages_per_seq, float scale, float skip_threshold,
+                                int32_t num_splits, void *workspace, size_t workspace_bytes, void *o,
+                                float *lse, uint8_t *skip_map, int32_t skip_map_stride, void *stream);
+
+/*
+ * Small-seq cross-attention (s_q = 1): sequence b has one query token and
+ * s_b = cu_seqlens_kv[b + 1] - cu_seqlens_kv[b] keys, non-causal, H query heads = H KV heads.
+ *   q [B, H, D], k and v [cu_seqlens_kv[B], H, D], o [B, H, D], all bf16.
+ *   max_seqlen_kv: host value in [0, 16], >= every s_b; it is the last dimension of the weights.
+ *   attn_weights: nullable bf16 [B, H, 1, max_seqlen_kv]; entry j < s_b is softmax probability j,
+ *   entries s_b <= j < max_seqlen_kv are 0.  lse: nullable fp32 [B, H].
+ *   Supported: D = 128.  B == 0 is a no-op.
+ */
+attn_status_t attn_smallseq_cross(const void *q, const void *k, const void *v, const int32_t *cu_seqlens_kv,
+                                  int32_t B, int32_t H, int32_t D, int32_t max_seqlen_kv, float scale,
+                                  void *o, void *attn_weights, float *lse, void *stream);
+
+/* Static description of a status code. */
+const char *attn_status_string(attn_status_t s);
+
+/* Detail of the calling thread's last failed call ("" if none). */
+const char *attn_last_error_message(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_H */

@@ -1,0 +1,238 @@
+// C ABI of libattn.so (declared in include/attn.h): host-side validation, schedule choice and launch.
+// Every check runs before the first HIP runtime call, so a rejected call never touches the device.
+#include "attn.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "launch.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+attn_status_t fail(attn_status_t s, const char *fmt, ...)
+{
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return s;
+}
+
+attn_status_t ok()
+{
+    g_last_error.clear();
+    return ATTN_OK;
+}
+
+attn_status_t hip_status(hipError_t e, const char *what)
+{
+    if (e != hipSuccess)
+        return fail(ATTN_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+    return ok();
+}
+
+bool bad_threshold(float thr) { return !(thr >= 0.f && thr <= 1.f); } // also rejects NaN
+
+// ln(threshold) as the kernels compare it: tile_max - running_max < ln(thr); thr = 0 never skips.
+float log2_threshold(float thr) { return thr > 0.f ? std::log2(thr) : -INFINITY; }
+
+constexpr int kDefaultSplits = 32;
+constexpr int kMaxSplits = 64;
+
+int resolve_splits(int num_splits, float thr) { return num_splits != 0 ? num_splits : (thr == 0.f ? kDefaultSplits : 1); }
+
+} // namespace
+
+extern "C" {
+
+const char *attn_status_string(attn_status_t s)
+{
+    switch (s) {
+    case ATTN_OK: return "ok";
+    case ATTN_ERR_INVALID: return "invalid argument";
+    case ATTN_ERR_UNSUPPORTED: return "unsupported configuration";
+    case ATTN_ERR_WORKSPACE: return "workspace too small";
+    case ATTN_ERR_HIP: return "HIP runtime error";
+    }
+    return "unknown status";
+}
+
+const char *attn_last_error_message(void) { return g_last_error.c_str(); }
+
+size_t attn_decode_paged_workspace_size(int32_t B, int32_t Hq, int32_t D, int32_t num_splits)
+{
+    const int S = num_splits == 0 ? kDefaultSplits : num_splits;
+    if (B <= 0 || Hq <= 0 || D <= 0 || S <= 1)
+        return 0;
+    return (size_t)B * Hq * S * ((size_t)D + 1) * sizeof(float);
+}
+
+attn_status_t attn_decode_paged(const void *q, const void *k_cache, const void *v_cache,
+                                const int32_t *block_table, const int32_t *seq_lens, int32_t B, int32_t Hq,
+                                int32_t Hkv, int32_t D, int32_t page_size, int32_t num_pages,
+                                int32_t max_pages_per_seq, float scale, float skip_threshold,
+                                int32_t num_splits, void *workspace, size_t workspace_bytes, void *o,
+                                float *lse, uint8_t *skip_map, int32_t skip_map_stride, void *stream)
+{
+    if (B < 0)
+        return fail(ATTN_ERR_INVALID, "attn_decode_paged: B = %d < 0", B);
+    if (Hq <= 0 || Hkv <= 0 || Hq % Hkv)
+        return fail(ATTN_ERR_INVALID, "attn_decode_paged: Hq = %d must be a positive multiple of Hkv = %d", Hq, Hkv);
+    if (bad_threshold(skip_threshold))
+        return fail(ATTN_ERR_INVALID, "attn_decode_paged: skip_threshold %g outside [0, 1]", (double)skip_threshold);
+    if (num_splits < 0 || num_splits > kMaxSplits)
+        return fail(ATTN_ERR_INVALID, "attn_decode_paged: num_splits %d outside [0, %d]", num_splits, kMaxSplits);
+    const int S = resolve_splits(num_splits, skip_threshold);
+    if (skip_threshold > 0.f && S > 1)
+        return fail(ATTN_ERR_INVALID, "attn_decode_paged: skip_threshold > 0 needs one sequential split, got %d", S);
+    if (!std::isfinite(scale))
+        return fail(ATTN_ERR_INVALID, "attn_decode_paged: scale is not finite");
+    if (num_pages <= 0 || max_pages_per_seq <= 0 || page_size <= 0)
+        return fail(ATTN_ERR_INVALID, "attn_decode_paged: num_pages, max_pages_per_seq and page_size must be > 0");
+    if (skip_map && S > 1)
+        return fail(ATTN_ERR_INVALID, "attn_decode_paged: skip_map needs the sequential schedule (num_splits = 1)");
+    if (skip_map && (int64_t)skip_map_stride * attn::kSkipTile < (int64_t)max_pages_per_seq * page_size)
+        return fail(ATTN_ERR_INVALID, "attn_decode_paged: skip_map_stride %d < ceil(max_pages_per_seq * page_size / 32)",
+                    skip_map_stride);
+    if (D != 128)
+        return fail(ATTN_ERR_UNSUPPORTED, "attn_decode_paged: D = %d (built for 128)", D);
+    if (page_size != 16)
+        return fail(ATTN_ERR_UNSUPPORTED, "attn_decode_paged: page_size = %d (built for 16)", page_size);
+    if (Hq / Hkv > 16)
+        return fail(ATTN_ERR_UNSUPPORTED, "attn_decode_paged: Hq / Hkv = %d > 16", Hq / Hkv);
+    if (B == 0)
+        return ok();
+    if (!q || !k_cache || !v_cache || !block_table || !seq_lens || !o)
+        return fail(ATTN_ERR_INVALID, "attn_decode_paged: a required pointer is NULL");
+    const float scale_log2 = scale * 1.4426950408889634f;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (S > 1) {
+        const size_t need = attn_decode_paged_workspace_size(B, Hq, D, S);
+        if (!workspace || workspace_bytes < need)
+            return fail(ATTN_ERR_WORKSPACE, "attn_decode_paged: workspace %zu bytes, need %zu", workspace_bytes, need);
+        attn::SplitArgs a{};
+        a.q = static_cast<const uint16_t *>(q);
+        a.kc = static_cast<const uint16_t *>(k_cache);
+        a.vc = static_cast<const uint16_t *>(v_cache);
+        a.bt = block_table;
+        a.seq_lens = seq_lens;
+        a.Hq = Hq;
+        a.Hkv = Hkv;
+        a.G = Hq / Hkv;
+        a.max_pages = max_pages_per_seq;
+        a.num_splits = S;
+        a.scale_log2 = scale_log2;
+        a.ws_o = static_cast<float *>(workspace);
+        a.ws_lse = a.ws_o + (size_t)B * Hq * S * D;
+        return hip_status(attn::launch_decode_split(a, B, static_cast<uint16_t *>(o), lse, st), "decode split-K launch");
+    }
+    attn::SeqArgs a{};
+    a.q = static_cast<const uint16_t *>(q);
+    a.kc = static_cast<const uint16_t *>(k_cache);
+    a.vc = static_cast<const uint16_t *>(v_cache);
+    a.bt = block_table;
+    a.seq_lens = seq_lens;
+    a.Hq = Hq;
+    a.Hkv = Hkv;
+    a.G = Hq / Hkv;
+    a.max_pages = max_pages_per_seq;
+    a.scale_log2 = scale_log2;
+    a.log2_thr = log2_threshold(skip_threshold);
+    a.o = static_cast<uint16_t *>(o);
+    a.lse = lse;
+    a.skip_map = skip_map;
+    a.map_stride = skip_map_stride;
+    return hip_status(attn::launch_decode_seq(a, B, st), "decode sequential launch");
+}
+
+attn_status_t attn_smallseq_cross(const void *q, const void *k, const void *v, const int32_t *cu_seqlens_kv,
+                                  int32_t B, int32_t H, int32_t D, int32_t max_seqlen_kv, float scale,
+                                  void *o, void *attn_weights, float *lse, void *stream)
+{
+    if (B < 0)
+        return fail(ATTN_ERR_INVALID, "attn_smallseq_cross: B = %d < 0", B);
+    if (H <= 0)
+        return fail(ATTN_ERR_INVALID, "attn_smallseq_cross: H = %d", H);
+    if (max_seqlen_kv < 0 || max_seqlen_kv > 16)
+        return fail(ATTN_ERR_INVALID, "attn_smallseq_cross: max_seqlen_kv = %d outside [0, 16]", max_seqlen_kv);
+    if (!std::isfinite(scale))
+        return fail(ATTN_ERR_INVALID, "attn_smallseq_cross: scale is not finite");
+    if (D != 128)
+        return fail(ATTN_ERR_UNSUPPORTED, "attn_smallseq_cross: D = %d (built for 128)", D);
+    if (B == 0)
+        return ok();
+    if (!q || !k || !v || !cu_seqlens_kv || !o)
+        return fail(ATTN_ERR_INVALID, "attn_smallseq_cross: a required pointer is NULL");
+    attn::SmallArgs a{};
+    a.q = static_cast<const uint16_t *>(q);
+    a.k = static_cast<const uint16_t *>(k);
+    a.v = static_cast<const uint16_t *>(v);
+    a.cu = cu_seqlens_kv;
+    a.B = B;
+    a.H = H;
+    a.max_s = max_seqlen_kv;
+    a.scale_log2 = scale * 1.4426950408889634f;
+    a.o = static_cast<uint16_t *>(o);
+    a.w = static_cast<uint16_t *>(attn_weights);
+    a.lse = lse;
+    return hip_status(attn::launch_smallseq(a, static_cast<hipStream_t>(stream)), "small-seq launch");
+}
+
+attn_status_t attn_prefill_varlen(attn_dtype_t dtype, const void *q, const void *k, const void *v,
+                                  const int32_t *cu_seqlens_q, const int32_t *cu_seqlens_k, int32_t B,
+                                  int32_t max_seqlen_q, int32_t max_seqlen_k, int32_t Hq, int32_t Hkv,
+                                  int32_t D, float scale, int32_t causal, float skip_threshold, void *o,
+                                  float *lse, uint8_t *skip_map, int32_t skip_map_stride, void *stream)
+{
+    if (dtype != ATTN_F32 && dtype != ATTN_BF16)
+        return fail(ATTN_ERR_INVALID, "attn_prefill_varlen: unknown dtype %d", (int)dtype);
+    if (B < 0 || max_seqlen_q < 0 || max_seqlen_k < 0)
+        return fail(ATTN_ERR_INVALID, "attn_prefill_varlen: negative B or max_seqlen");
+    if (Hq <= 0 || Hkv <= 0 || Hq % Hkv)
+        return fail(ATTN_ERR_INVALID, "attn_prefill_varlen: Hq = %d must be a positive multiple of Hkv = %d", Hq, Hkv);
+    if (bad_threshold(skip_threshold))
+        return fail(ATTN_ERR_INVALID, "attn_prefill_varlen: skip_threshold %g outside [0, 1]", (double)skip_threshold);
+    if (!std::isfinite(scale))
+        return fail(ATTN_ERR_INVALID, "attn_prefill_varlen: scale is not finite");
+    if (skip_map && (int64_t)skip_map_stride * attn::kSkipTile < (int64_t)max_seqlen_k)
+        return fail(ATTN_ERR_INVALID, "attn_prefill_varlen: skip_map_stride %d < ceil(max_seqlen_k / 32)", skip_map_stride);
+    if (dtype == ATTN_BF16 && D != 64 && D != 128)
+        return fail(ATTN_ERR_UNSUPPORTED, "attn_prefill_varlen: bf16 D = %d (built for 64 and 128)", D);
+    if (dtype == ATTN_F32 && D != 64)
+        return fail(ATTN_ERR_UNSUPPORTED, "attn_prefill_varlen: fp32 D = %d (built for 64)", D);
+    if (B == 0 || max_seqlen_q == 0)
+        return ok();
+    if (!q || !k || !v || !cu_seqlens_q || !cu_seqlens_k || !o)
+        return fail(ATTN_ERR_INVALID, "attn_prefill_varlen: a required pointer is NULL");
+    attn::PrefillArgs a{};
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.cu_q = cu_seqlens_q;
+    a.cu_k = cu_seqlens_k;
+    a.B = B;
+    a.max_q = max_seqlen_q;
+    a.max_k = max_seqlen_k;
+    a.Hq = Hq;
+    a.Hkv = Hkv;
+    a.G = Hq / Hkv;
+    a.causal = causal != 0;
+    a.scale_log2 = scale * 1.4426950408889634f;
+    a.log2_thr = log2_threshold(skip_threshold);
+    a.o = o;
+    a.lse = lse;
+    a.skip_map = skip_map;
+    a.map_stride = skip_map_stride;
+    return hip_status(attn::launch_prefill(a, dtype == ATTN_BF16, D, static_cast<hipStream_t>(stream)),
+                      "prefill launch");
+}
+
+} // extern "C"

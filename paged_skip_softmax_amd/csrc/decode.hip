@@ -1,0 +1,405 @@
+// One-token paged-KV decode for gfx950: split-K (two kernels) and the sequential skip-softmax schedule.
+//
+// Schedules ("Model-Optimizer: Add split-k decode kernel for skip softmax", What does this PR do):
+//  * skip-softmax off: the keys of a sequence are cut into 128-key tiles and the tiles into num_splits
+//    contiguous runs of ceil(ntiles / num_splits) tiles.  Every (batch row, KV head, split) is one
+//    workgroup that writes a partial (O_s, lse_s) for the G query heads of the KV head; a second small
+//    kernel merges the partials of a row: lse = log sum_s e^{lse_s}, O = sum_s e^{lse_s - lse} O_s.
+//  * skip-softmax on: one sequential split over 32-key tiles.  Tile t of query row r is skipped (no exp,
+//    no P.V, no rescale) when exp(tmax_t - m) < threshold, m the running max before the tile
+//    ("TensorRT-LLM: Skip Softmax Attention", Description).  Because a skipped tile lies below the
+//    running max (threshold <= 1), the running max before tile t always equals the max of tmax over
+//    all earlier tiles, skipped or not.  So the waves of the workgroup take consecutive tiles in
+//    rounds, publish their tile maxima in LDS, and each decides exactly from the prefix max -- the
+//    decisions of one sequential pass, taken in parallel.  V of a tile is read only when at least one
+//    query row of the group keeps it.
+//
+// Cache layout: [num_pages, Hkv, 16, D] bf16, so one (page, KV head) is a contiguous 4 KB slab.
+//
+// Per 32-key chunk (two pages) a wave computes, for the G query heads of its KV head:
+//   S^T[32 keys x 16] = K[32 x 128] . Q^T[128 x 16]      8 MFMA 16x16x32 (columns >= G are zero)
+//   online softmax in the log2 domain (scale * log2 e folded into one FMA)
+//   O^T[128 x 16] += V^T[128 x 32] . P^T[32 x 16]         8 MFMA 16x16x32
+// K goes straight from HBM into MFMA operand registers (each lane loads 16 B of one key row).  V is
+// loaded with fully coalesced 16-B loads (each wave instruction reads 1 KB of a slab), stored to a
+// wave-private LDS tile with a padded row pitch, and read back column-wise as the transposed operand.
+// The key order inside the P.V contraction follows the S^T register layout (lane group j holds keys
+// 4j..4j+3 of each page), so P needs no shuffle between the two products.  Each wave keeps its own
+// online-softmax state; the states are merged through LDS at the end of the workgroup.
+#include "kcommon.h"
+#include "launch.h"
+
+namespace attn {
+
+constexpr int kPage = 16;
+constexpr int kD = 128;
+constexpr int kSplitTile = 128;
+constexpr int kSplitWaves = 4;
+constexpr int kSeqWaves = 8;
+constexpr int kVPitch = kD + 8;                   // LDS row pitch (bf16 elements, 272 B)
+constexpr int kVTile = 2 * kPage * kVPitch;       // one wave's V staging tile (elements)
+
+// Q^T operand: lane (n = lane%16, j = lane/16) holds head g*G+n, d = 32 s + 8 j .. +8.
+__device__ __forceinline__ void load_q_operand(const uint16_t *q, int b, int g, int Hq, int G, int lane,
+                                               bf16x8 qop[4])
+{
+    const int n = lane & 15, j = lane >> 4;
+    if (n < G) {
+        const uint16_t *qp = q + ((size_t)b * Hq + (size_t)g * G + n) * kD + 8 * j;
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+            qop[s] = as_bf16x8(ld16(qp + 32 * s));
+    } else {
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+            qop[s] = as_bf16x8(make_uint4(0, 0, 0, 0));
+    }
+}
+
+// K rows of two pages in MFMA A-operand order: key lane%16 of the page, d = 32 s + 8 (lane/16).
+__device__ __forceinline__ void load_k_chunk(const uint16_t *kp0, const uint16_t *kp1, int lane, uint4 kr[2][4])
+{
+    const int off = (lane & 15) * kD + 8 * (lane >> 4);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+        kr[0][s] = ld16(kp0 + off + 32 * s);
+        kr[1][s] = ld16(kp1 + off + 32 * s);
+    }
+}
+
+// V slabs of two pages, coalesced: lane reads key lane/16 + 4 r, d = 8 (lane%16) .. +8.
+__device__ __forceinline__ void load_v_chunk(const uint16_t *vp0, const uint16_t *vp1, int lane, uint4 vr[2][4])
+{
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        vr[0][r] = ld16(vp0 + 8 * lane + 512 * r);
+        vr[1][r] = ld16(vp1 + 8 * lane + 512 * r);
+    }
+}
+
+// Raw scores q.k of the chunk: sc[pg][i] = key 16 pg + 4 j + i for head lane%16; keys at or past
+// tend are set to -inf.  Returns the chunk max of the lane's head (raw units, across lane groups).
+__device__ __forceinline__ float chunk_scores(const uint4 kr[2][4], const bf16x8 qop[4], int tok0, int tend,
+                                              int lane, f32x4 sc[2])
+{
+    const int j = lane >> 4;
+#pragma unroll
+    for (int pg = 0; pg < 2; ++pg) {
+        sc[pg] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+            sc[pg] = mfma16(as_bf16x8(kr[pg][s]), qop[s], sc[pg]);
+    }
+    const bool partial = tok0 + 2 * kPage > tend;
+    float cmax = kNegInf;
+#pragma unroll
+    for (int pg = 0; pg < 2; ++pg)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            if (partial && tok0 + kPage * pg + 4 * j + i >= tend)
+                sc[pg][i] = kNegInf;
+            cmax = fmaxf(cmax, sc[pg][i]);
+        }
+    return max_across_groups16(cmax);
+}
+
+// Online-softmax state of one wave.  Lane (n, j) holds head n; m is in the log2 domain, l is this
+// lane's partial sum (reduced over j at the end), acc[db][i] = O^T[d = 16 db + 4 j + i][n].
+struct WaveState {
+    float m, l;
+    f32x4 acc[kD / 16];
+};
+
+__device__ __forceinline__ void state_init(WaveState &st)
+{
+    st.m = kNegInf;
+    st.l = 0.f;
+#pragma unroll
+    for (int db = 0; db < kD / 16; ++db)
+        st.acc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+}
+
+// Folds one chunk into the state.  keep == false (per lane, i.e. per head) leaves that head's state
+// untouched: p = 0 and no rescale.  cmax_l2: chunk max in log2 units.  Keys at or past tend have their
+// V zeroed in LDS so that 0 * NaN never reaches the accumulator.  vt: this wave's LDS tile.
+__device__ __forceinline__ void chunk_update(WaveState &st, const f32x4 sc[2], float cmax_l2, bool keep,
+                                             const uint4 vr[2][4], int tok0, int tend, float scale_log2,
+                                             uint16_t *vt, int lane)
+{
+    const int n = lane & 15, j = lane >> 4;
+    const float m_new = keep ? fmaxf(st.m, cmax_l2) : st.m;
+    const float m_use = m_new == kNegInf ? 0.f : m_new;
+    const float alpha = keep ? exp2_fast(st.m - m_use) : 1.f;
+    float p[2][4], psum = 0.f;
+#pragma unroll
+    for (int pg = 0; pg < 2; ++pg)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            p[pg][i] = keep ? exp2_fast(fmaf(sc[pg][i], scale_log2, -m_use)) : 0.f;
+            psum += p[pg][i];
+        }
+    st.l = fmaf(st.l, alpha, psum);
+    st.m = m_new;
+#pragma unroll
+    for (int db = 0; db < kD / 16; ++db)
+        st.acc[db] *= alpha;
+
+    const bool partial = tok0 + 2 * kPage > tend;
+#pragma unroll
+    for (int pg = 0; pg < 2; ++pg)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int key = (lane >> 4) + 4 * r;
+            uint4 v = vr[pg][r];
+            if (partial && tok0 + kPage * pg + key >= tend)
+                v = make_uint4(0, 0, 0, 0);
+            st16(vt + (pg * kPage + key) * kVPitch + 8 * (lane & 15), v);
+        }
+    __builtin_amdgcn_wave_barrier();
+    bf16x8 pop;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        pop[i] = (__bf16)p[0][i];
+        pop[4 + i] = (__bf16)p[1][i];
+    }
+#pragma unroll
+    for (int db = 0; db < kD / 16; ++db) {
+        const int d = 16 * db + n;
+        bf16x8 va;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            va[i] = __builtin_bit_cast(__bf16, vt[(4 * j + i) * kVPitch + d]);
+            va[4 + i] = __builtin_bit_cast(__bf16, vt[(kPage + 4 * j + i) * kVPitch + d]);
+        }
+        st.acc[db] = mfma16(va, pop, st.acc[db]);
+    }
+    __builtin_amdgcn_wave_barrier();
+}
+
+// Merges the W wave states of the workgroup (through LDS at `smem`, which must hold
+// W * 16 * (D + 2) floats and is reused after a barrier) and calls out(h, d, o, lse_natural) for
+// every head h < G and d < D.  lse is -inf and o = 0 for a head that saw no key.
+template <int W, typename Out>
+__device__ __forceinline__ void merge_waves(WaveState &st, void *smem, int G, Out out)
+{
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int n = lane & 15, j = lane >> 4;
+    st.l = sum_across_groups16(st.l);
+    __syncthreads();
+    float *red_acc = static_cast<float *>(smem);
+    float *red_m = red_acc + W * 16 * kD;
+    float *red_l = red_m + W * 16;
+    if (n < G) {
+#pragma unroll
+        for (int db = 0; db < kD / 16; ++db)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                red_acc[(w * 16 + n) * kD + 16 * db + 4 * j + i] = st.acc[db][i];
+        if (j == 0) {
+            red_m[w * 16 + n] = st.m;
+            red_l[w * 16 + n] = st.l;
+        }
+    }
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < G * kD; idx += blockDim.x) {
+        const int h = idx / kD, d = idx % kD;
+        float M = kNegInf;
+#pragma unroll
+        for (int ww = 0; ww < W; ++ww)
+            M = fmaxf(M, red_m[ww * 16 + h]);
+        float o = 0.f, lse = kNegInf;
+        if (M != kNegInf) {
+            float den = 0.f, num = 0.f;
+#pragma unroll
+            for (int ww = 0; ww < W; ++ww) {
+                const float e = exp2_fast(red_m[ww * 16 + h] - M);
+                den = fmaf(e, red_l[ww * 16 + h], den);
+                num = fmaf(e, red_acc[(ww * 16 + h) * kD + d], num);
+            }
+            o = num / den;
+            lse = (M + __log2f(den)) * kLn2;
+        }
+        out(h, d, o, lse);
+    }
+}
+
+// ------------------------------------------------------------------ split-K
+
+__global__ __launch_bounds__(64 * kSplitWaves) void decode_split_kernel(SplitArgs a)
+{
+    const int sp = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int S = a.num_splits;
+    const int L = a.seq_lens[b];
+    const int ntiles = (L + kSplitTile - 1) / kSplitTile;
+    const int per = (ntiles + S - 1) / S;
+    const int t0 = min(sp * per * kSplitTile, L);
+    const int t1 = min((sp + 1) * per * kSplitTile, L);
+
+    __shared__ __attribute__((aligned(16))) uint16_t smem[kSplitWaves * kVTile];
+    static_assert(sizeof(smem) >= kSplitWaves * 16 * (kD + 2) * sizeof(float), "merge buffer");
+    uint16_t *vt = smem + w * kVTile;
+
+    bf16x8 qop[4];
+    load_q_operand(a.q, b, g, a.Hq, a.G, lane, qop);
+    WaveState st;
+    state_init(st);
+    const int32_t *btr = a.bt + (size_t)b * a.max_pages;
+    const size_t slab = (size_t)kPage * kD;
+    for (int tok0 = t0 + 2 * kPage * w; tok0 < t1; tok0 += 2 * kPage * kSplitWaves) {
+        const int p0 = btr[tok0 / kPage];
+        const int p1 = tok0 + kPage < t1 ? btr[tok0 / kPage + 1] : p0;
+        const size_t o0 = ((size_t)p0 * a.Hkv + g) * slab, o1 = ((size_t)p1 * a.Hkv + g) * slab;
+        uint4 kr[2][4], vr[2][4];
+        load_k_chunk(a.kc + o0, a.kc + o1, lane, kr);
+        load_v_chunk(a.vc + o0, a.vc + o1, lane, vr);
+        f32x4 sc[2];
+        const float cmax = chunk_scores(kr, qop, tok0, t1, lane, sc);
+        chunk_update(st, sc, cmax * a.scale_log2, true, vr, tok0, t1, a.scale_log2, vt, lane);
+    }
+    const size_t row0 = (size_t)b * a.Hq + (size_t)g * a.G;
+    merge_waves<kSplitWaves>(st, smem, a.G, [&](int h, int d, float o, float lse) {
+        a.ws_o[((row0 + h) * S + sp) * kD + d] = o;
+        if (d == 0)
+            a.ws_lse[(row0 + h) * S + sp] = lse;
+    });
+}
+
+struct MergeArgs {
+    const float *ws_o, *ws_lse;
+    int rows, num_splits;
+    uint16_t *o;   // [rows, D] bf16
+    float *lse;    // nullable [rows]
+};
+
+// One wave per (batch row, query head): lse = log sum_s e^{lse_s}, O = sum_s e^{lse_s - lse} O_s.
+__global__ __launch_bounds__(256) void decode_merge_kernel(MergeArgs a)
+{
+    const int lane = threadIdx.x & 63;
+    const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (row >= a.rows)
+        return;
+    const int S = a.num_splits;
+    const float ls = lane < S ? a.ws_lse[(size_t)row * S + lane] * kLog2e : kNegInf;
+    const float M = wave_max(ls);
+    float o0 = 0.f, o1 = 0.f, lse = kNegInf;
+    if (M != kNegInf) {
+        const float e = exp2_fast(ls - M);
+        const float den = wave_sum(e);
+        const float2 *src = reinterpret_cast<const float2 *>(a.ws_o + (size_t)row * S * kD) + lane;
+        for (int s = 0; s < S; ++s) {
+            const float ws = __shfl(e, s);
+            if (ws != 0.f) {
+                const float2 v = src[s * (kD / 2)];
+                o0 = fmaf(ws, v.x, o0);
+                o1 = fmaf(ws, v.y, o1);
+            }
+        }
+        o0 /= den;
+        o1 /= den;
+        lse = (M + __log2f(den)) * kLn2;
+    }
+    reinterpret_cast<uint32_t *>(a.o + (size_t)row * kD)[lane] = pack_bf16x2(o0, o1);
+    if (a.lse && lane == 0)
+        a.lse[row] = lse;
+}
+
+hipError_t launch_decode_split(const SplitArgs &a, int B, uint16_t *o, float *lse, hipStream_t stream)
+{
+    hipLaunchKernelGGL(decode_split_kernel, dim3(a.num_splits, a.Hkv, B), dim3(64 * kSplitWaves), 0, stream, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess)
+        return e;
+    MergeArgs m{a.ws_o, a.ws_lse, B * a.Hq, a.num_splits, o, lse};
+    hipLaunchKernelGGL(decode_merge_kernel, dim3((B * a.Hq + 3) / 4), dim3(256), 0, stream, m);
+    return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ sequential with skip-softmax
+
+__global__ __launch_bounds__(64 * kSeqWaves) void decode_seq_kernel(SeqArgs a)
+{
+    const int g = blockIdx.x, b = blockIdx.y;
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int n = lane & 15, j = lane >> 4;
+    const int L = a.seq_lens[b];
+    const int ntiles = (L + kSkipTile - 1) / kSkipTile;
+
+    __shared__ __attribute__((aligned(16))) uint16_t smem[kSeqWaves * kVTile];
+    static_assert(sizeof(smem) >= kSeqWaves * 16 * (kD + 2) * sizeof(float), "merge buffer");
+    __shared__ float tmax_buf[2][kSeqWaves][16];
+    uint16_t *vt = smem + w * kVTile;
+    const size_t row0 = (size_t)b * a.Hq + (size_t)g * a.G;
+
+    if (a.skip_map) // tiles with no key: "not visited"
+        for (int idx = threadIdx.x; idx < a.G * a.map_stride; idx += blockDim.x) {
+            const int h = idx / a.map_stride, t = idx % a.map_stride;
+            if (t >= ntiles)
+                a.skip_map[(row0 + h) * a.map_stride + t] = 2;
+        }
+
+    bf16x8 qop[4];
+    load_q_operand(a.q, b, g, a.Hq, a.G, lane, qop);
+    WaveState st;
+    state_init(st);
+    float run_max = kNegInf; // max of tile maxima over all earlier rounds (log2 units), head n
+    const int32_t *btr = a.bt + (size_t)b * a.max_pages;
+    const size_t slab = (size_t)kPage * kD;
+    int parity = 0;
+    for (int base = 0; base < ntiles; base += kSeqWaves, parity ^= 1) {
+        const int t = base + w;
+        const int tok0 = t * kSkipTile;
+        const bool active = t < ntiles;
+        f32x4 sc[2];
+        float tmax = kNegInf;
+        size_t o0 = 0, o1 = 0;
+        if (active) {
+            const int p0 = btr[tok0 / kPage];
+            const int p1 = tok0 + kPage < L ? btr[tok0 / kPage + 1] : p0;
+            o0 = ((size_t)p0 * a.Hkv + g) * slab;
+            o1 = ((size_t)p1 * a.Hkv + g) * slab;
+            uint4 kr[2][4];
+            load_k_chunk(a.kc + o0, a.kc + o1, lane, kr);
+            tmax = chunk_scores(kr, qop, tok0, L, lane, sc) * a.scale_log2;
+        }
+        if (j == 0)
+            tmax_buf[parity][w][n] = tmax;
+        __syncthreads();
+        float prefix = run_max, round_max = run_max;
+#pragma unroll
+        for (int ww = 0; ww < kSeqWaves; ++ww) {
+            const float tm = tmax_buf[parity][ww][n];
+            if (ww < w)
+                prefix = fmaxf(prefix, tm);
+            round_max = fmaxf(round_max, tm);
+        }
+        run_max = round_max;
+        if (active) {
+            // skip iff a running max exists and tmax - m < log2(threshold)
+            const bool skip = prefix != kNegInf && tmax - prefix < a.log2_thr;
+            const bool keep = !skip;
+            // V is needed when any real head of the group keeps the tile
+            const bool any_keep = __any(keep && n < a.G);
+            if (any_keep) {
+                uint4 vr[2][4];
+                load_v_chunk(a.vc + o0, a.vc + o1, lane, vr);
+                chunk_update(st, sc, tmax, keep, vr, tok0, L, a.scale_log2, vt, lane);
+            }
+            if (a.skip_map && j == 0 && n < a.G)
+                a.skip_map[(row0 + n) * a.map_stride + t] = skip ? 1 : 0;
+        }
+    }
+    merge_waves<kSeqWaves>(st, smem, a.G, [&](int h, int d, float o, float lse) {
+        a.o[(row0 + h) * kD + d] = f32_to_bf16(o);
+        if (a.lse && d == 0)
+            a.lse[row0 + h] = lse;
+    });
+}
+
+hipError_t launch_decode_seq(const SeqArgs &a, int B, hipStream_t stream)
+{
+    hipLaunchKernelGGL(decode_seq_kernel, dim3(a.Hkv, B), dim3(64 * kSeqWaves), 0, stream, a);
+    return hipGetLastError();
+}
+
+} // namespace attn

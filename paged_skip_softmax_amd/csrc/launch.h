@@ -1,0 +1,67 @@
+// Kernel argument blocks and launchers shared by the C ABI (api.cpp) and the kernel sources.
+// Plain structs passed by value as kernel arguments.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace attn {
+
+constexpr int kSkipTile = 32; // keys per skip decision
+
+// Split-K paged decode (num_splits > 1): partials into the workspace, then the merge.
+struct SplitArgs {
+    const uint16_t *q;      // [B, Hq, D] bf16
+    const uint16_t *kc;     // [pages, Hkv, 16, D] bf16
+    const uint16_t *vc;
+    const int32_t *bt;      // [B, max_pages]
+    const int32_t *seq_lens;
+    int Hq, Hkv, G, max_pages, num_splits;
+    float scale_log2;       // scale * log2(e)
+    float *ws_o;            // [B, Hq, S, D]
+    float *ws_lse;          // [B, Hq, S], natural log
+};
+
+// Sequential paged decode with skip-softmax over 32-key tiles (num_splits == 1).
+struct SeqArgs {
+    const uint16_t *q, *kc, *vc;
+    const int32_t *bt, *seq_lens;
+    int Hq, Hkv, G, max_pages;
+    float scale_log2;
+    float log2_thr;         // log2(threshold); -inf disables skipping
+    uint16_t *o;            // [B, Hq, D] bf16
+    float *lse;             // nullable [B, Hq]
+    uint8_t *skip_map;      // nullable [B, Hq, map_stride]
+    int map_stride;
+};
+
+// Small-seq cross-attention (s_q = 1, s_kv <= 16).
+struct SmallArgs {
+    const uint16_t *q, *k, *v; // [B, H, D], [T, H, D] x2
+    const int32_t *cu;         // [B + 1]
+    int B, H, max_s;
+    float scale_log2;
+    uint16_t *o;               // [B, H, D]
+    uint16_t *w;               // nullable [B, H, 1, max_s]
+    float *lse;                // nullable [B, H]
+};
+
+// Varlen prefill.
+struct PrefillArgs {
+    const void *q, *k, *v;
+    const int32_t *cu_q, *cu_k;
+    int B, max_q, max_k, Hq, Hkv, G;
+    bool causal;
+    float scale_log2;
+    float log2_thr;
+    void *o;
+    float *lse;
+    uint8_t *skip_map;
+    int map_stride;
+};
+
+hipError_t launch_decode_split(const SplitArgs &a, int B, uint16_t *o, float *lse, hipStream_t stream);
+hipError_t launch_decode_seq(const SeqArgs &a, int B, hipStream_t stream);
+hipError_t launch_smallseq(const SmallArgs &a, hipStream_t stream);
+hipError_t launch_prefill(const PrefillArgs &a, bool bf16, int D, hipStream_t stream);
+
+} // namespace attn

@@ -1,0 +1,124 @@
+"""The C ABI without a GPU: the library loads, exports every declared entry point, and rejects bad
+arguments with the documented status before any HIP runtime call (no compute call is made here)."""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+from paged_skip_softmax_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+INVALID, UNSUPPORTED, WORKSPACE = _lib.ATTN_ERR_INVALID, _lib.ATTN_ERR_UNSUPPORTED, _lib.ATTN_ERR_WORKSPACE
+FAKE = 0x1000  # a non-NULL pointer value; validation fails before anything could dereference it
+
+
+def _declared():
+    text = open(os.path.join(ROOT, "include", "attn.h")).read()
+    return sorted(set(re.findall(r"^\w[\w \*]*?\b(attn_\w+)\s*\(", text, re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _lib.load()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = _declared()
+    assert set(names) == set(_lib.SIGNATURES), names
+    for n in names:
+        assert hasattr(lib, n)
+
+
+def _decode(lib, **kw):
+    a = dict(q=FAKE, kc=FAKE, vc=FAKE, bt=FAKE, sl=FAKE, B=2, Hq=8, Hkv=2, D=128, page=16, pages=100, maxp=10,
+             scale=0.1, thr=0.0, splits=0, ws=FAKE, wsb=1 << 30, o=FAKE, lse=None, map=None, stride=5, stream=None)
+    a.update(kw)
+    return lib.attn_decode_paged(a["q"], a["kc"], a["vc"], a["bt"], a["sl"], a["B"], a["Hq"], a["Hkv"], a["D"],
+                                 a["page"], a["pages"], a["maxp"], a["scale"], a["thr"], a["splits"], a["ws"],
+                                 a["wsb"], a["o"], a["lse"], a["map"], a["stride"], a["stream"])
+
+
+def test_decode_validation(lib):
+    assert _decode(lib, B=-1) == INVALID
+    assert _decode(lib, Hq=7) == INVALID
+    for thr in (float("nan"), -0.01, 1.01, math.inf):
+        assert _decode(lib, thr=thr) == INVALID
+    assert _decode(lib, splits=65) == INVALID
+    assert _decode(lib, splits=-1) == INVALID
+    assert _decode(lib, thr=0.1, splits=32) == INVALID
+    assert _decode(lib, scale=math.nan) == INVALID
+    assert _decode(lib, map=FAKE, splits=32) == INVALID
+    assert _decode(lib, map=FAKE, splits=1, stride=4) == INVALID
+    assert _decode(lib, D=64) == UNSUPPORTED
+    assert _decode(lib, page=32) == UNSUPPORTED
+    assert _decode(lib, Hq=34, Hkv=2) == UNSUPPORTED
+    assert _decode(lib, q=None) == INVALID
+    assert _decode(lib, wsb=100) == WORKSPACE
+    assert _decode(lib, ws=None) == WORKSPACE
+    assert _decode(lib, B=0) == _lib.ATTN_OK
+    _decode(lib, splits=99)
+    assert b"num_splits" in lib.attn_last_error_message()
+
+
+def test_workspace_size(lib):
+    assert lib.attn_decode_paged_workspace_size(64, 32, 128, 32) == 64 * 32 * 32 * 129 * 4
+    assert lib.attn_decode_paged_workspace_size(64, 32, 128, 0) == 64 * 32 * 32 * 129 * 4
+    assert lib.attn_decode_paged_workspace_size(64, 32, 128, 1) == 0
+    assert lib.attn_decode_paged_workspace_size(0, 32, 128, 32) == 0
+
+
+def _prefill(lib, **kw):
+    a = dict(dt=_lib.ATTN_BF16, q=FAKE, k=FAKE, v=FAKE, cq=FAKE, ck=FAKE, B=2, mq=10, mk=10, Hq=8, Hkv=2, D=128,
+             scale=0.1, causal=1, thr=0.0, o=FAKE, lse=None, map=None, stride=1, stream=None)
+    a.update(kw)
+    return lib.attn_prefill_varlen(a["dt"], a["q"], a["k"], a["v"], a["cq"], a["ck"], a["B"], a["mq"], a["mk"],
+                                   a["Hq"], a["Hkv"], a["D"], a["scale"], a["causal"], a["thr"], a["o"], a["lse"],
+                                   a["map"], a["stride"], a["stream"])
+
+
+def test_prefill_validation(lib):
+    assert _prefill(lib, dt=7) == INVALID
+    assert _prefill(lib, B=-1) == INVALID
+    assert _prefill(lib, Hkv=3) == INVALID
+    assert _prefill(lib, thr=2.0) == INVALID
+    assert _prefill(lib, thr=float("nan")) == INVALID
+    assert _prefill(lib, map=FAKE, mk=100, stride=3) == INVALID
+    assert _prefill(lib, D=96) == UNSUPPORTED
+    assert _prefill(lib, dt=_lib.ATTN_F32, D=128) == UNSUPPORTED
+    assert _prefill(lib, k=None) == INVALID
+    assert _prefill(lib, B=0) == _lib.ATTN_OK
+    assert _prefill(lib, mq=0) == _lib.ATTN_OK
+
+
+def _small(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, cu=FAKE, B=4, H=16, D=128, ms=16, scale=0.1, o=FAKE, w=None, lse=None,
+             stream=None)
+    a.update(kw)
+    return lib.attn_smallseq_cross(a["q"], a["k"], a["v"], a["cu"], a["B"], a["H"], a["D"], a["ms"], a["scale"],
+                                   a["o"], a["w"], a["lse"], a["stream"])
+
+
+def test_smallseq_validation(lib):
+    assert _small(lib, ms=17) == INVALID
+    assert _small(lib, ms=-1) == INVALID
+    assert _small(lib, B=-2) == INVALID
+    assert _small(lib, H=0) == INVALID
+    assert _small(lib, D=64) == UNSUPPORTED
+    assert _small(lib, cu=None) == INVALID
+    assert _small(lib, B=0) == _lib.ATTN_OK
+
+
+def test_status_strings(lib):
+    for s in range(5):
+        assert lib.attn_status_string(s)
+    assert lib.attn_status_string(99) == b"unknown status"
+
+
+def test_python_binding_raises_without_gpu_tensors():
+    import torch
+    import paged_skip_softmax_amd as attn
+    q = torch.zeros(2, 8, 128, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        attn.attn_decode_paged(q, q, q, q, q)

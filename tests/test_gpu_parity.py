@@ -1,0 +1,243 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle, element by element.
+
+Tolerances: max-abs error 1e-5 for fp32 outputs and 2e-2 for bf16 outputs (unit-variance V).  Skip-softmax
+decisions come from fp32 scores on the GPU and fp64 scores in the oracle, so near a threshold several
+skip sets are correct: the test requires >= 99.9 % agreement of the GPU skip map with the oracle's own
+decisions over visited (row, tile) pairs, an exact match of which tiles are visited at all, and compares
+the outputs against the oracle replaying the GPU's skip map.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import paged_skip_softmax_amd as attn
+from paged_skip_softmax_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+F32_TOL = 1e-5
+BF16_TOL = 2e-2
+DEV = "cuda"
+
+
+def _np(t):
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def _check_map(gpu_map, ora_map, min_agree=0.999):
+    g = gpu_map.cpu().numpy() if isinstance(gpu_map, torch.Tensor) else gpu_map
+    o = ora_map
+    assert g.shape == o.shape
+    # the visited set is pure indexing: exact
+    assert np.array_equal(g == 2, o == 2), "visited tiles differ"
+    vis = o != 2
+    agree = (g[vis] == o[vis]).mean() if vis.any() else 1.0
+    assert agree >= min_agree, f"skip-map agreement {agree:.5f}"
+    return g, agree
+
+
+# ------------------------------------------------------------------ prefill
+
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("thr", [0.0, 0.1])
+def test_tiny_dense_fp32(causal, thr):
+    x = W.tiny_dense(seed=1000, device=DEV)
+    o, lse, smap = attn.attn_prefill_varlen(x.q, x.k, x.v, x.cu_q, x.cu_k, x.max_q, x.max_k, scale=x.scale,
+                                            causal=causal, skip_threshold=thr, return_lse=True,
+                                            return_skip_map=True)
+    torch.cuda.synchronize()
+    mode = "skip"
+    oo, ol, om = oracle.prefill(x.q.cpu(), x.k.cpu(), x.v.cpu(), x.cu_q.cpu(), x.cu_k.cpu(), x.Hq, x.Hkv, x.scale,
+                                causal, mode=mode, thr=thr, tile=32, stride=smap.shape[-1])
+    g, _ = _check_map(smap, om)
+    if thr == 0:
+        assert set(np.unique(g)) <= {0, 2}
+        od, ld, _ = oracle.prefill(x.q.cpu(), x.k.cpu(), x.v.cpu(), x.cu_q.cpu(), x.cu_k.cpu(), x.Hq, x.Hkv,
+                                   x.scale, causal)
+        assert np.max(np.abs(_np(o) - od)) <= F32_TOL
+    else:
+        assert (g == 1).any(), "threshold 0.1 skipped nothing"
+    # compare against the oracle replaying the GPU's decisions
+    orp, lrp, _ = oracle.prefill(x.q.cpu(), x.k.cpu(), x.v.cpu(), x.cu_q.cpu(), x.cu_k.cpu(), x.Hq, x.Hkv, x.scale,
+                                 causal, mode="skip", tile=32, replay=np.where(g == 2, 0, g).reshape(-1, g.shape[-1]),
+                                 stride=g.shape[-1])
+    assert np.max(np.abs(_np(o) - orp)) <= F32_TOL
+    assert np.max(np.abs(_np(lse) - lrp)) <= F32_TOL
+
+
+@pytest.mark.parametrize("D", [128, 64])
+@pytest.mark.parametrize("causal", [True, False])
+def test_prefill_bf16_varlen_ragged(D, causal):
+    lens = [1, 17, 128, 0, 129, 300, 64, 255]
+    x = W.varlen_prefill(seed=31, device=DEV, lengths=lens, Hq=8, Hkv=2, D=D)
+    o, lse, _ = attn.attn_prefill_varlen(x.q, x.k, x.v, x.cu_q, x.cu_k, x.max_q, x.max_k, causal=causal,
+                                         return_lse=True)
+    torch.cuda.synchronize()
+    od, ld, _ = oracle.prefill(x.q.cpu(), x.k.cpu(), x.v.cpu(), x.cu_q.cpu(), x.cu_k.cpu(), 8, 2, x.scale, causal)
+    assert np.max(np.abs(_np(o) - od)) <= BF16_TOL
+    assert np.max(np.abs(_np(lse) - ld)) <= 1e-3
+
+
+def test_prefill_bf16_cross_lengths_and_empty_keys():
+    # Lq != Lk (bottom-right causal alignment) and a sequence with queries but no keys
+    Hq, Hkv, D = 4, 4, 128
+    lq, lk = [5, 70, 33, 8], [40, 70, 0, 200]
+    g = torch.Generator(device=DEV).manual_seed(3)
+    q = torch.randn(sum(lq), Hq, D, generator=g, device=DEV).bfloat16()
+    k = torch.randn(sum(lk), Hkv, D, generator=g, device=DEV).bfloat16()
+    v = torch.randn(sum(lk), Hkv, D, generator=g, device=DEV).bfloat16()
+    cq = torch.tensor([0] + list(np.cumsum(lq)), dtype=torch.int32, device=DEV)
+    ck = torch.tensor([0] + list(np.cumsum(lk)), dtype=torch.int32, device=DEV)
+    for causal in (True, False):
+        o, lse, _ = attn.attn_prefill_varlen(q, k, v, cq, ck, max(lq), max(lk), causal=causal, return_lse=True)
+        torch.cuda.synchronize()
+        od, ld, _ = oracle.prefill(q.cpu(), k.cpu(), v.cpu(), cq.cpu(), ck.cpu(), Hq, Hkv, 1 / math.sqrt(D), causal)
+        assert np.max(np.abs(_np(o) - od)) <= BF16_TOL
+        fin = np.isfinite(ld)
+        assert np.array_equal(fin, np.isfinite(_np(lse)))
+        assert np.max(np.abs(_np(lse)[fin] - ld[fin])) <= 1e-3
+        assert np.all(_np(o)[75:108] == 0)  # the sequence with no keys
+
+
+def test_prefill_bf16_skip_replay():
+    lens = [300, 517, 64]
+    x = W.varlen_prefill(seed=41, device=DEV, lengths=lens, Hq=4, Hkv=1, D=128)
+    # hot keys: queries share a component along one direction u; two 32-key runs of every sequence get a
+    # large component along u, so their logits sit ~4 above the rest and later tiles become skippable
+    g = torch.Generator(device=DEV).manual_seed(4)
+    u = torch.randn(128, generator=g, device=DEV)
+    u = u / u.norm()
+    qb = (x.q.float() + 3 * u).bfloat16().contiguous()
+    k = x.k.float()
+    cu = x.cu_q.tolist()
+    for b in range(3):
+        for t0 in (cu[b] + 32, cu[b] + 96):
+            if t0 + 32 <= cu[b + 1]:
+                k[t0:t0 + 32, 0] += 15 * u
+    kb = k.bfloat16().contiguous()
+    x.q = qb
+    for thr in (0.01, 0.1):
+        o, lse, smap = attn.attn_prefill_varlen(x.q, kb, x.v, x.cu_q, x.cu_k, x.max_q, x.max_k, causal=True,
+                                                skip_threshold=thr, return_lse=True, return_skip_map=True)
+        torch.cuda.synchronize()
+        _, _, om = oracle.prefill(x.q.cpu(), kb.cpu(), x.v.cpu(), x.cu_q.cpu(), x.cu_k.cpu(), 4, 1, x.scale, True,
+                                  mode="skip", thr=thr, stride=smap.shape[-1])
+        g, _ = _check_map(smap, om)
+        if thr == 0.1:
+            assert (g == 1).mean() > 0.05, "the hot-key input should make tiles skippable"
+        orp, _, _ = oracle.prefill(x.q.cpu(), kb.cpu(), x.v.cpu(), x.cu_q.cpu(), x.cu_k.cpu(), 4, 1, x.scale, True,
+                                   mode="skip", replay=np.where(g == 2, 0, g).reshape(-1, g.shape[-1]),
+                                   stride=g.shape[-1])
+        assert np.max(np.abs(_np(o) - orp)) <= BF16_TOL
+
+
+# ------------------------------------------------------------------ paged decode
+
+def _small_decode(hot=False, seed=51):
+    lengths = [1, 15, 16, 17, 127, 128, 129, 1000, 4097, 33]
+    return W.paged_decode(seed=seed, device=DEV, B=len(lengths), Hq=8, Hkv=2, D=128, page=16, pool=1000,
+                          lengths=lengths, lmax=4112, hot=hot)
+
+
+def _decode_oracle(x, **kw):
+    return oracle.decode(x.q.cpu(), x.k_cache.cpu(), x.v_cache.cpu(), x.block_table.cpu(), x.seq_lens.cpu(),
+                         x.scale, **kw)
+
+
+@pytest.mark.parametrize("splits", [2, 7, 32, 64])
+def test_decode_split_k(splits):
+    x = _small_decode()
+    o, lse, _ = attn.attn_decode_paged(x.q, x.k_cache, x.v_cache, x.block_table, x.seq_lens, num_splits=splits,
+                                       return_lse=True)
+    torch.cuda.synchronize()
+    od, ld, _ = _decode_oracle(x)
+    assert np.isfinite(_np(o)).all(), "NaN poison reached the output"
+    assert np.max(np.abs(_np(o) - od)) <= BF16_TOL
+    assert np.max(np.abs(_np(lse) - ld)) <= 1e-3
+
+
+def test_decode_zero_length_and_block_table_permutation():
+    x = _small_decode()
+    sl = x.seq_lens.clone()
+    sl[3] = 0
+    o, lse, _ = attn.attn_decode_paged(x.q, x.k_cache, x.v_cache, x.block_table, sl, return_lse=True)
+    torch.cuda.synchronize()
+    assert torch.all(o[3] == 0) and torch.all(torch.isneginf(lse[3]))
+    # permuting the pool and remapping the table gives bit-identical output
+    o1, _, _ = attn.attn_decode_paged(x.q, x.k_cache, x.v_cache, x.block_table, x.seq_lens)
+    perm = torch.randperm(x.pool, generator=torch.Generator().manual_seed(5)).to(DEV)
+    inv = torch.empty_like(perm)
+    inv[perm] = torch.arange(x.pool, device=DEV)
+    bt2 = x.block_table.clone()
+    m = bt2 >= 0
+    bt2[m] = inv[bt2[m].long()].to(torch.int32)
+    o2, _, _ = attn.attn_decode_paged(x.q, x.k_cache[perm].contiguous(), x.v_cache[perm].contiguous(), bt2,
+                                      x.seq_lens)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2)
+
+
+@pytest.mark.parametrize("thr", [0.0, 0.01, 0.1, 0.5])
+def test_decode_sequential_skip(thr):
+    x = _small_decode(hot=True)
+    o, lse, smap = attn.attn_decode_paged(x.q, x.k_cache, x.v_cache, x.block_table, x.seq_lens, num_splits=1,
+                                          skip_threshold=thr, return_lse=True, return_skip_map=True)
+    torch.cuda.synchronize()
+    assert np.isfinite(_np(o)).all()
+    _, _, om = _decode_oracle(x, mode="skip", thr=thr, tile=32, stride=smap.shape[-1])
+    g, _ = _check_map(smap, om)
+    if thr == 0:
+        assert set(np.unique(g)) <= {0, 2}
+        od, _, _ = _decode_oracle(x)
+        assert np.max(np.abs(_np(o) - od)) <= BF16_TOL
+    orp, lrp, _ = _decode_oracle(x, mode="skip", tile=32, replay=np.where(g == 2, 0, g).reshape(-1, g.shape[-1]),
+                                 stride=g.shape[-1])
+    assert np.max(np.abs(_np(o) - orp)) <= BF16_TOL
+    assert np.max(np.abs(_np(lse) - lrp)) <= 1e-3
+
+
+def test_decode_deterministic():
+    x = _small_decode()
+    a1, _, _ = attn.attn_decode_paged(x.q, x.k_cache, x.v_cache, x.block_table, x.seq_lens)
+    a2, _, _ = attn.attn_decode_paged(x.q, x.k_cache, x.v_cache, x.block_table, x.seq_lens)
+    s1, _, _ = attn.attn_decode_paged(x.q, x.k_cache, x.v_cache, x.block_table, x.seq_lens, num_splits=1,
+                                      skip_threshold=0.1)
+    s2, _, _ = attn.attn_decode_paged(x.q, x.k_cache, x.v_cache, x.block_table, x.seq_lens, num_splits=1,
+                                      skip_threshold=0.1)
+    torch.cuda.synchronize()
+    assert torch.equal(a1, a2) and torch.equal(s1, s2)
+
+
+# ------------------------------------------------------------------ small-seq
+
+@pytest.mark.parametrize("fixed", [None, 2, 4, 6, 8, 12, 16])
+def test_smallseq(fixed):
+    x = W.smallseq_cross(seed=61, device=DEV, B=3000, fixed=fixed)
+    o, w, lse = attn.attn_smallseq_cross(x.q, x.k, x.v, x.cu_kv, x.max_s, return_lse=True)
+    torch.cuda.synchronize()
+    rows = [(b, h) for b in range(0, 3000, 7) for h in range(16)]
+    oo, ow = oracle.smallseq(x.q.cpu(), x.k.cpu(), x.v.cpu(), x.cu_kv.cpu(), x.max_s, x.scale, rows=rows)
+    r = np.array(rows)
+    assert np.max(np.abs(_np(o)[r[:, 0], r[:, 1]] - oo)) <= BF16_TOL
+    assert np.max(np.abs(_np(w)[r[:, 0], r[:, 1], 0] - ow)) <= BF16_TOL
+    # padding weights are exactly zero
+    s = x.lens.numpy()
+    wn = _np(w)[:, :, 0]
+    for b in range(0, 3000, 97):
+        assert np.all(wn[b, :, s[b]:] == 0)
+
+
+def test_smallseq_zero_length():
+    x = W.smallseq_cross(seed=62, device=DEV, B=64)
+    lens = x.lens.clone()
+    lens[5] = 0  # sequence 5 has no keys
+    cu = torch.zeros(65, dtype=torch.int32)
+    cu[1:] = torch.cumsum(lens, 0)
+    T = int(cu[-1])
+    o, w, lse = attn.attn_smallseq_cross(x.q, x.k[:T].contiguous(), x.v[:T].contiguous(), cu.to(DEV), 16,
+                                         return_lse=True)
+    torch.cuda.synchronize()
+    assert torch.all(o[5] == 0) and torch.all(w[5] == 0) and torch.all(torch.isneginf(lse[5]))
