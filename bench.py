@@ -1,0 +1,275 @@
+"""Benchmark of the attention hot path on one MI355X.
+
+One step = one pass of every hot-path kernel over its synthetic workload, inputs resident in HBM:
+  prefill  varlen causal prefill, bf16: 16 sequences, lengths uniform in [256, 4096], THD, Hq=32, Hkv=8,
+           D=128 (the workload the headline metric is quoted on)
+  decode   paged one-token decode, split-K: B=64, Hq=32, Hkv=8, D=128, contexts uniform in [1024, 32768],
+           16-token pages in a 140,000-page pool, 32 splits of 128-key tiles (+ the merge kernel)
+  skip     the same decode shapes with hot keys, one sequential split of 32-key tiles, threshold
+           0, 0.01 and 0.1
+  smallseq small-seq cross-attention: 30720 sequences, s_q=1, s_kv in {2,4,6,8,12,16}, H=16, D=128
+
+value = prefill TFLOP/s (algorithmic FLOPs 4 D Hq sum_b L_b (L_b + 1) / 2 over the kernel's event time);
+the decode, skip and small-seq figures ride along in the same JSON line.  Kernel times come from HIP
+events recorded on the stream the kernels are launched on (torch's current stream).
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
+
+
+def _parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=10)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--seed", type=int, default=0)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--only", default="", help="comma list of prefill,decode,skip,smallseq (profiling runs)")
+    return p.parse_args()
+
+
+def _traffic_from_profiles(kernel: str):
+    """HBM bytes per launch measured by rocprofv3 counters, if a summary for this kernel build exists."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        with open(path) as f:
+            data = json.load(f)
+        ent = data.get(kernel)
+        if not ent:
+            return None
+        src = os.path.join(ROOT, ent["source"])
+        import hashlib
+        digest = hashlib.sha256(open(src, "rb").read()).hexdigest()
+        if digest != ent.get("source_sha256"):
+            return None  # the kernel changed since the counters were taken
+        return float(ent["bytes_per_launch"])
+    except Exception:
+        return None
+
+
+def main():
+    args = _parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (every path here runs on a "
+              "single MI355X)", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import paged_skip_softmax_amd as attn
+    from paged_skip_softmax_amd import workloads as W
+
+    only = set(args.only.split(",")) if args.only else {"prefill", "decode", "skip", "smallseq"}
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    t_gen = time.time()
+    work = {}
+    if "prefill" in only:
+        work["prefill"] = W.varlen_prefill(seed=1001 + args.seed, device=dev)
+    if "decode" in only:
+        work["decode"] = W.paged_decode(seed=1002 + args.seed, device=dev)
+    if "skip" in only:
+        work["skip"] = W.paged_decode_hot(seed=1002 + args.seed, device=dev)
+    if "smallseq" in only:
+        work["smallseq"] = W.smallseq_cross(seed=1004 + args.seed, device=dev)
+    torch.cuda.synchronize()
+    print(f"# inputs generated in {time.time() - t_gen:.1f} s", file=sys.stderr, flush=True)
+
+    calls = {}  # name -> zero-arg launcher
+    if "prefill" in only:
+        x = work["prefill"]
+        o_pf = torch.empty_like(x.q)
+        calls["prefill"] = lambda: attn.attn_prefill_varlen(x.q, x.k, x.v, x.cu_q, x.cu_k, x.max_q, x.max_k,
+                                                            causal=True, out=o_pf)
+    if "decode" in only:
+        d = work["decode"]
+        ws = torch.empty(attn.attn_decode_paged_workspace_size(d.B, d.Hq, d.D, 32), dtype=torch.uint8, device=dev)
+        o_dc = torch.empty_like(d.q)
+        calls["decode"] = lambda: attn.attn_decode_paged(d.q, d.k_cache, d.v_cache, d.block_table, d.seq_lens,
+                                                         num_splits=32, workspace=ws, out=o_dc)
+    if "skip" in only:
+        s = work["skip"]
+        o_sk = torch.empty_like(s.q)
+        for thr in (0.0, 0.01, 0.1):
+            calls[f"skip_{thr}"] = (lambda thr=thr: attn.attn_decode_paged(
+                s.q, s.k_cache, s.v_cache, s.block_table, s.seq_lens, num_splits=1, skip_threshold=thr, out=o_sk))
+    if "smallseq" in only:
+        c = work["smallseq"]
+        o_ss = torch.empty_like(c.q)
+        w_ss = torch.empty((c.B, c.H, 1, c.max_s), dtype=torch.bfloat16, device=dev)
+        calls["smallseq"] = lambda: attn.attn_smallseq_cross(c.q, c.k, c.v, c.cu_kv, c.max_s, out=o_ss)
+
+    names = list(calls)
+    stream = torch.cuda.current_stream()
+
+    def step(record):
+        for nm in names:
+            if record is None:
+                calls[nm]()
+            else:
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                calls[nm]()
+                e1.record(stream)
+                record[nm].append((e0, e1))
+
+    for _ in range(args.warmup):
+        step(None)
+    torch.cuda.synchronize()
+    rec = {nm: [] for nm in names}
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(rec)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms = {nm: float(np.mean([a.elapsed_time(b) for a, b in rec[nm]])) for nm in names}
+    ms_min = {nm: float(np.min([a.elapsed_time(b) for a, b in rec[nm]])) for nm in names}
+    ms_per_step = (t1 - t0) * 1e3 / max(1, args.steps)
+    print(f"# kernel ms (mean over {args.steps} steps): " + ", ".join(f"{k}={v:.4f}" for k, v in ms.items()),
+          file=sys.stderr, flush=True)
+
+    out = {}
+    rooflines = []
+    if "prefill" in only:
+        L = work["prefill"].lens.double()
+        flops = 4.0 * 128 * 32 * float((L * (L + 1) / 2).sum())
+        tflops = flops / (ms["prefill"] * 1e-3) / 1e12
+        out["prefill"] = {"ms": ms["prefill"], "ms_min": ms_min["prefill"], "flop": flops, "tflops": tflops,
+                          "frac_peak": tflops / PEAK_BF16_TFLOPS}
+        rooflines.append({"kernel": "prefill_bf16_kernel<128,false>", "bound": "mfma", "achieved": tflops,
+                          "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": tflops / PEAK_BF16_TFLOPS,
+                          "traffic": _traffic_from_profiles("prefill_bf16_kernel"), "ms": ms["prefill"]})
+    if "decode" in only:
+        d = work["decode"]
+        kv = 4.0 * d.Hkv * d.D * float(d.lens.sum())
+        gbps = kv / (ms["decode"] * 1e-3) / 1e9
+        part = d.B * d.Hq * 32 * (d.D + 1) * 4 * 2
+        out["decode"] = {"ms": ms["decode"], "ms_min": ms_min["decode"], "kv_bytes": kv, "kv_GBps": gbps,
+                         "frac_peak": gbps / PEAK_HBM_GBPS, "split_partial_bytes": part,
+                         "note": "time covers the split kernel and the merge kernel"}
+        rooflines.append({"kernel": "decode_split_kernel+decode_merge_kernel", "bound": "hbm", "achieved": gbps,
+                          "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": gbps / PEAK_HBM_GBPS,
+                          "traffic": _traffic_from_profiles("decode_split_kernel"), "ms": ms["decode"]})
+    if "skip" in only:
+        s = work["skip"]
+        G = s.Hq // s.Hkv
+        res = {}
+        kbytes = 2.0 * s.Hkv * s.D * float(s.lens.sum())
+        for thr in (0.0, 0.01, 0.1):
+            _, _, smap = attn.attn_decode_paged(s.q, s.k_cache, s.v_cache, s.block_table, s.seq_lens, num_splits=1,
+                                                skip_threshold=thr, return_skip_map=True)
+            torch.cuda.synchronize()
+            m = smap.view(s.B, s.Hkv, G, -1)
+            vis = m[:, :, 0] != 2
+            f_r = float((smap == 1).sum()) / float((smap != 2).sum())
+            vskip = (m == 1).all(2) & vis
+            f_v = float(vskip.sum()) / float(vis.sum())
+            # algorithmic bytes: all K, V of the tiles some row of the group keeps (32-key tiles)
+            kept_tiles_v = float((vis & ~vskip).sum())
+            vbytes_kept = kbytes * (kept_tiles_v / float(vis.sum()))
+            t = ms[f"skip_{thr}"]
+            res[str(thr)] = {"ms": t, "ms_min": ms_min[f"skip_{thr}"], "row_tile_skip_frac": f_r,
+                             "group_v_tile_skip_frac": f_v, "bytes_read_alg": kbytes + vbytes_kept,
+                             "GBps_alg": (kbytes + vbytes_kept) / (t * 1e-3) / 1e9,
+                             "dense_equiv_GBps": 2 * kbytes / (t * 1e-3) / 1e9,
+                             "ideal_speedup_vs_thr0": 2.0 / (2.0 - f_v)}
+        for thr in ("0.01", "0.1"):
+            res[thr]["speedup_vs_thr0"] = res["0.0"]["ms"] / res[thr]["ms"]
+            if "decode" in out:
+                res[thr]["speedup_vs_splitk_dense"] = out["decode"]["ms"] / res[thr]["ms"]
+        out["skip"] = res
+        g0 = res["0.0"]["GBps_alg"]
+        rooflines.append({"kernel": "decode_seq_kernel(thr=0)", "bound": "hbm", "achieved": g0,
+                          "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": g0 / PEAK_HBM_GBPS,
+                          "traffic": _traffic_from_profiles("decode_seq_kernel"), "ms": res["0.0"]["ms"]})
+    if "smallseq" in only:
+        c = work["smallseq"]
+        kv = 4.0 * c.H * c.D * float(c.lens.sum())
+        tot = kv + 2.0 * 2 * c.B * c.H * c.D + 2.0 * c.B * c.H * c.max_s
+        gbps = kv / (ms["smallseq"] * 1e-3) / 1e9
+        out["smallseq"] = {"ms": ms["smallseq"], "ms_min": ms_min["smallseq"], "kv_bytes": kv, "kv_GBps": gbps,
+                           "all_bytes": tot, "all_GBps": tot / (ms["smallseq"] * 1e-3) / 1e9,
+                           "frac_peak": gbps / PEAK_HBM_GBPS}
+        rooflines.append({"kernel": "smallseq_kernel", "bound": "hbm", "achieved": gbps, "peak": PEAK_HBM_GBPS,
+                          "unit": "GB/s", "frac": gbps / PEAK_HBM_GBPS,
+                          "traffic": _traffic_from_profiles("smallseq_kernel"), "ms": ms["smallseq"]})
+
+    # the dominant kernel: the largest share of the step
+    dom = max(rooflines, key=lambda r: r["ms"]) if rooflines else None
+    roofline = None
+    if dom:
+        roofline = {k: dom[k] for k in ("bound", "achieved", "peak", "unit", "frac", "traffic")}
+        roofline["kernel"] = dom["kernel"]
+
+    cpu = None
+    if not args.no_cpu_baseline and "prefill" in only:
+        cpu = _cpu_baseline(work["prefill"])
+
+    headline = out.get("prefill", {}).get("tflops")
+    line = {
+        "metric": "prefill TFLOP/s & decode KV GB/s vs MI355X peak; skip-softmax speedup",
+        "value": headline,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "varlen causal prefill bf16: 16 seqs, L~U[256,4096] THD, Hq=32, Hkv=8, D=128",
+                   "step_also_runs": ["paged decode split-K B=64 L~U[1024,32768] page 16, 32x128-key splits",
+                                      "sequential skip decode thr {0,0.01,0.1} on hot keys",
+                                      "small-seq cross B=30720 s_kv in {2..16} H=16 D=128"],
+                   "seed": args.seed},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "kernels": out,
+        "rooflines": rooflines,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def _cpu_baseline(x):
+    """The fp64 oracle on a bounded sample of the prefill workload, on this host's cores."""
+    import numpy as np
+
+    import oracle
+    threads = int(os.environ.get("OMP_NUM_THREADS") or os.cpu_count() or 1)
+    q, k, v = x.q.cpu(), x.k.cpu(), x.v.cpu()
+    cu = x.cu_q.cpu()
+    L = x.lens.numpy()
+    b = int(np.argmax(L))  # the longest sequence
+    start = int(cu[b])
+    step = 1
+    rows = [(start + i, h) for i in range(0, int(L[b]), step) for h in range(x.Hq)]
+    t0 = time.perf_counter()
+    oracle.prefill(q, k, v, x.cu_q.cpu(), x.cu_k.cpu(), x.Hq, x.Hkv, x.scale, True, rows=rows)
+    dt = time.perf_counter() - t0
+    flops = sum(4.0 * x.D * (i + 1) for i in range(0, int(L[b]), step)) * x.Hq
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"every {step}th causal query row of the longest sequence (L={int(L[b])}), all {x.Hq} heads: "
+                      f"{len(rows)} rows, {flops:.3e} FLOP in {dt:.2f} s"}
+
+
+if __name__ == "__main__":
+    main()
