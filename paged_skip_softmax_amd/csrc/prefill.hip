@@ -4,15 +4,22 @@
 //
 // bf16 kernel: one workgroup of 4 waves per (query head, sequence, 128-row query tile); each wave owns
 // 32 query rows and keeps Q^T in registers as the MFMA B operand for the whole loop.  Per 64-key
-// iteration the workgroup stages the K and V tiles in LDS (coalesced 16-B loads, padded rows) and
-// every wave computes
+// iteration every wave computes
 //   S^T[64 keys x 32 rows] = K[64 x D] . Q^T[D x 32]      2 x D/16 MFMA 32x32x16 (bf16, fp32 acc)
 //   online softmax in the log2 domain (scale * log2 e folded into one FMA)
 //   O^T[D x 32] += V^T[D x 64] . P^T[64 x 32]              D/32 x 4 MFMA 32x32x16
-// The key order inside P.V follows the S^T register layout, so P feeds the second product straight
-// from registers.  Query tiles are dispatched from the last (the most keys under a causal mask) to the
-// first.  The two 32-key halves of an iteration are exactly the skip tiles (tiles aligned to key 0);
-// a tile skipped by every row of a wave costs no exp and no P.V.
+// K and V tiles are double-buffered in LDS: while a wave computes on tile i, its lanes already hold
+// tile i+1 in registers (coalesced 16-B loads issued at the top of the iteration) and store it to the
+// other buffer afterwards, so one barrier per iteration suffices and HBM latency hides behind the
+// MFMAs.  K is read back as the A operand with 16-B reads; V, stored key-major as loaded, is read back
+// transposed with ds_read_b64_tr_b16 (lane j of each 16-lane group addresses key k0 + j/4, dims
+// 4(j%4)..+3, and receives dims of its own column for keys k0..k0+3).  The key order inside P.V follows
+// the S^T register layout, so P feeds the second product straight from registers.
+// The running max used for the exponentials is only raised when a row's max grows by more than 2^8
+// (log2 units), so the O and l rescale is rare; the result is the same softmax, with P <= 2^8.
+// Query tiles are dispatched from the last (the most keys under a causal mask) to the first.  The two
+// 32-key halves of an iteration are exactly the skip tiles (tiles aligned to key 0); skip decisions use
+// the exact running max, and a tile skipped by every row of a wave costs no exp and no P.V.
 //
 // fp32 kernel: one lane per query row on the vector ALUs (exact fp32 products, no reduced-precision
 // operand), 32-key K/V tiles staged in LDS, the same online softmax and the same skip rule.
@@ -24,21 +31,37 @@ namespace attn {
 constexpr int kBM = 128;     // query rows per workgroup
 constexpr int kBN = 64;      // keys per iteration
 constexpr int kPrefWaves = 4;
+constexpr float kRescaleSlack = 8.f; // log2 units the stale max may trail the true max
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
 
 template <int D>
 struct PrefillSmem {
-    static constexpr int kPitch = D + 8; // bf16 elements per LDS row (16-B aligned, conflict-free)
-    uint16_t k[kBN * kPitch];
-    uint16_t v[kBN * kPitch];
+    static constexpr int kKP = D + 8;  // K row pitch (elements): 16-B row reads spread over all banks
+    static constexpr int kVP = D + 16; // V row pitch (elements): transposed 8-B reads spread over banks
+    uint16_t k[2][kBN * kKP];
+    uint16_t v[2][kBN * kVP];
 };
 
-template <int D, bool SKIP>
-__global__ __launch_bounds__(64 * kPrefWaves) void prefill_bf16_kernel(PrefillArgs a)
+// Transposed LDS read: 4 consecutive keys of one dim column (see the file comment).
+__device__ __forceinline__ uint2 lds_read_tr(const uint16_t *p)
 {
-    constexpr int kPitch = PrefillSmem<D>::kPitch;
+    const i16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4 *)(p));
+    return __builtin_bit_cast(uint2, r);
+}
+
+template <int D, bool SKIP>
+__global__ __launch_bounds__(64 * kPrefWaves) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void prefill_bf16_kernel(PrefillArgs a)
+{
+    using Smem = PrefillSmem<D>;
+    constexpr int KP = Smem::kKP, VP = Smem::kVP;
     constexpr int kSteps = D / 16;  // MFMA k-steps over D
     constexpr int kDB = D / 32;     // 32-wide d blocks of the output
-    __shared__ __attribute__((aligned(16))) PrefillSmem<D> sm;
+    constexpr int kChunks = D / 8;  // 16-B chunks per key row
+    constexpr int kRowsPerPass = 64 * kPrefWaves / kChunks;
+    constexpr int kPasses = kBN / kRowsPerPass;
+    __shared__ __attribute__((aligned(16))) Smem sm;
 
     const int h = blockIdx.x, b = blockIdx.y;
     const int qt = gridDim.z - 1 - blockIdx.z;
@@ -76,7 +99,8 @@ __global__ __launch_bounds__(64 * kPrefWaves) void prefill_bf16_kernel(PrefillAr
 #pragma unroll
         for (int i = 0; i < 16; ++i)
             acc[db][i] = 0.f;
-    float m = kNegInf, l = 0.f;
+    float m = kNegInf, l = 0.f;   // m: max used for the exponentials (may trail the true max)
+    float m_true = kNegInf;       // exact running max over processed tiles (skip decisions)
 
     uint8_t *maprow = nullptr;
     if (SKIP && a.skip_map && row_ok) {
@@ -86,112 +110,136 @@ __global__ __launch_bounds__(64 * kPrefWaves) void prefill_bf16_kernel(PrefillAr
                 maprow[t] = 2;
     }
 
-    constexpr int kChunks = D / 8;               // 16-B chunks per key row
-    constexpr int kRowsPerPass = 256 / kChunks;
-    for (int kb = 0; kb < kend; kb += kBN) {
-        __syncthreads();
+    // cooperative tile loads: thread -> (key tid / kChunks + p * kRowsPerPass, chunk tid % kChunks)
+    const int ld_key = tid / kChunks, ld_c = tid % kChunks;
+    uint4 kn[kPasses], vn[kPasses];
+    auto load_tile = [&](int kb) {
 #pragma unroll
-        for (int p = 0; p < kBN / kRowsPerPass; ++p) {
-            const int key = tid / kChunks + p * kRowsPerPass, c = tid % kChunks;
-            uint4 kv = make_uint4(0, 0, 0, 0), vv = make_uint4(0, 0, 0, 0);
-            if (kb + key < Lk) {
-                const size_t off = ((size_t)(k0 + kb + key) * a.Hkv + g) * D + 8 * c;
-                kv = ld16(kg + off);
-                vv = ld16(vg + off);
+        for (int p = 0; p < kPasses; ++p) {
+            const int key = kb + ld_key + p * kRowsPerPass;
+            kn[p] = make_uint4(0, 0, 0, 0);
+            vn[p] = make_uint4(0, 0, 0, 0);
+            if (key < Lk) {
+                const size_t off = ((size_t)(k0 + key) * a.Hkv + g) * D + 8 * ld_c;
+                kn[p] = ld16(kg + off);
+                vn[p] = ld16(vg + off);
             }
-            st16(sm.k + key * kPitch + 8 * c, kv);
-            st16(sm.v + key * kPitch + 8 * c, vv);
         }
-        __syncthreads();
-        if (kb >= kend_w)
-            continue; // every row of this wave is past the diagonal
+    };
+    auto store_tile = [&](int buf) {
+#pragma unroll
+        for (int p = 0; p < kPasses; ++p) {
+            const int key = ld_key + p * kRowsPerPass;
+            st16(sm.k[buf] + key * KP + 8 * ld_c, kn[p]);
+            st16(sm.v[buf] + key * VP + 8 * ld_c, vn[p]);
+        }
+    };
 
-        f32x16 sc[2];
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-#pragma unroll
-            for (int i = 0; i < 16; ++i)
-                sc[kk][i] = 0.f;
-#pragma unroll
-            for (int s = 0; s < kSteps; ++s) {
-                const bf16x8 ka = as_bf16x8(ld16(sm.k + (32 * kk + n) * kPitch + 16 * s + 8 * J));
-                sc[kk] = mfma32(ka, qop[s], sc[kk]);
-            }
-        }
-        // mask keys past the sequence and past the causal diagonal
-        const bool need_mask = kb + kBN > Lk || (a.causal && kb + kBN - 1 > m0 + 32 * w + diag);
-        if (need_mask) {
-#pragma unroll
-            for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const int key = kb + 32 * kk + 8 * (i / 4) + 4 * J + (i % 4);
-                    if (key >= kend_row)
-                        sc[kk][i] = kNegInf;
-                }
-        }
-        float tmax[2];
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-            float t = sc[kk][0];
-#pragma unroll
-            for (int i = 1; i < 16; ++i)
-                t = fmaxf(t, sc[kk][i]);
-            tmax[kk] = fmaxf(t, __shfl_xor(t, 32)) * a.scale_log2;
-        }
-        bool use[2] = {true, true};
-        float m_new = m;
-        if (SKIP) {
+    const int niter = (kend + kBN - 1) / kBN;
+    if (niter > 0) {
+        load_tile(0);
+        store_tile(0);
+    }
+    __syncthreads();
+    // transposed-read lane address: key offset j/4 within the 4-key group, dims 4 (j%4) of the
+    // 16-dim half (lane/16) % 2 of the 32-dim block
+    const int tr_key = (lane & 15) >> 2;
+    const int tr_dim = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+
+    for (int it = 0; it < niter; ++it) {
+        const int kb = it * kBN, cur = it & 1;
+        if (it + 1 < niter)
+            load_tile(kb + kBN);
+        if (kb < kend_w) {
+            const uint16_t *Kl = sm.k[cur];
+            const uint16_t *Vl = sm.v[cur];
+            f32x16 sc[2];
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk) {
-                const bool visited = tmax[kk] != kNegInf;
-                const bool skip = visited && m_new != kNegInf && tmax[kk] - m_new < a.log2_thr;
-                use[kk] = visited && !skip;
-                if (use[kk])
-                    m_new = fmaxf(m_new, tmax[kk]);
-                // tiles past the row's last visible key were marked 2 up front
-                if (maprow && J == 0 && visited)
-                    maprow[(kb >> 5) + kk] = skip ? 1 : 0;
+#pragma unroll
+                for (int i = 0; i < 16; ++i)
+                    sc[kk][i] = 0.f;
+#pragma unroll
+                for (int s = 0; s < kSteps; ++s)
+                    sc[kk] = mfma32(as_bf16x8(ld16(Kl + (32 * kk + n) * KP + 16 * s + 8 * J)), qop[s], sc[kk]);
             }
-        } else {
-            m_new = fmaxf(m, fmaxf(tmax[0], tmax[1]));
-        }
-        const float m_use = m_new == kNegInf ? 0.f : m_new;
-        const float alpha = exp2_fast(m - m_use);
-        m = m_new;
-        l *= alpha;
+            // mask keys past the sequence and past the causal diagonal
+            const bool need_mask = kb + kBN > Lk || (a.causal && kb + kBN - 1 > m0 + 32 * w + diag);
+            if (need_mask) {
 #pragma unroll
-        for (int db = 0; db < kDB; ++db)
-            acc[db] *= alpha;
+                for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-            if (SKIP && !__any(use[kk]))
-                continue; // no row of the wave keeps this tile: no exp, no P.V
-            float p[16];
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                p[i] = (!SKIP || use[kk]) ? exp2_fast(fmaf(sc[kk][i], a.scale_log2, -m_use)) : 0.f;
-                l += p[i];
-            }
-#pragma unroll
-            for (int u = 0; u < 2; ++u) {
-                bf16x8 pop;
-#pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    pop[e] = (__bf16)p[8 * u + e];
-#pragma unroll
-                for (int db = 0; db < kDB; ++db) {
-                    const int d = 32 * db + n;
-                    bf16x8 va;
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        const int key = 32 * kk + 16 * u + 8 * (e / 4) + 4 * J + (e % 4);
-                        va[e] = __builtin_bit_cast(__bf16, sm.v[key * kPitch + d]);
+                    for (int i = 0; i < 16; ++i) {
+                        const int key = kb + 32 * kk + 8 * (i / 4) + 4 * J + (i % 4);
+                        if (key >= kend_row)
+                            sc[kk][i] = kNegInf;
                     }
-                    acc[db] = mfma32(va, pop, acc[db]);
+            }
+            float tmax[2];
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) {
+                float t = sc[kk][0];
+#pragma unroll
+                for (int i = 1; i < 16; ++i)
+                    t = fmaxf(t, sc[kk][i]);
+                tmax[kk] = fmaxf(t, __shfl_xor(t, 32)) * a.scale_log2;
+            }
+            bool use[2] = {true, true};
+            if (SKIP) {
+#pragma unroll
+                for (int kk = 0; kk < 2; ++kk) {
+                    const bool visited = tmax[kk] != kNegInf;
+                    const bool skip = visited && m_true != kNegInf && tmax[kk] - m_true < a.log2_thr;
+                    use[kk] = visited && !skip;
+                    if (use[kk])
+                        m_true = fmaxf(m_true, tmax[kk]);
+                    // tiles past the row's last visible key were marked 2 up front
+                    if (maprow && J == 0 && visited)
+                        maprow[(kb >> 5) + kk] = skip ? 1 : 0;
+                }
+            }
+            const float m_tile = fmaxf(use[0] ? tmax[0] : kNegInf, use[1] ? tmax[1] : kNegInf);
+            const bool raise = m_tile > m + kRescaleSlack;
+            if (__any(raise)) {
+                const float m_new = raise ? m_tile : m;
+                const float alpha = exp2_fast(m - m_new); // m = -inf -> 0 (acc and l are still 0)
+                m = m_new;
+                l *= alpha;
+#pragma unroll
+                for (int db = 0; db < kDB; ++db)
+                    acc[db] *= alpha;
+            }
+            const float m_use = m == kNegInf ? 0.f : m;
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) {
+                if (SKIP && !__any(use[kk]))
+                    continue; // no row of the wave keeps this tile: no exp, no P.V
+                float p[16];
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    p[i] = (!SKIP || use[kk]) ? exp2_fast(fmaf(sc[kk][i], a.scale_log2, -m_use)) : 0.f;
+                    l += p[i];
+                }
+#pragma unroll
+                for (int u = 0; u < 2; ++u) {
+                    bf16x8 pop;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)
+                        pop[e] = (__bf16)p[8 * u + e];
+                    const int ka = 32 * kk + 16 * u + 4 * J + tr_key; // keys k0..k0+3 of slots 0..3
+#pragma unroll
+                    for (int db = 0; db < kDB; ++db) {
+                        const uint16_t *vp = Vl + ka * VP + 32 * db + tr_dim;
+                        const uint2 lo = lds_read_tr(vp);
+                        const uint2 hi = lds_read_tr(vp + 8 * VP); // keys k0+8..k0+11: slots 4..7
+                        acc[db] = mfma32(as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y)), pop, acc[db]);
+                    }
                 }
             }
         }
+        if (it + 1 < niter)
+            store_tile(cur ^ 1);
+        __syncthreads();
     }
 
     l += __shfl_xor(l, 32);
