@@ -208,6 +208,8 @@ attn_status_t attn_prefill_varlen(attn_dtype_t dtype, const void *q, const void 
         return fail(ATTN_ERR_UNSUPPORTED, "attn_prefill_varlen: bf16 D = %d (built for 64 and 128)", D);
     if (dtype == ATTN_F32 && D != 64)
         return fail(ATTN_ERR_UNSUPPORTED, "attn_prefill_varlen: fp32 D = %d (built for 64)", D);
+    if (dtype == ATTN_BF16 && (int64_t)max_seqlen_k * Hkv * D * 2 >= ((int64_t)1 << 31))
+        return fail(ATTN_ERR_UNSUPPORTED, "attn_prefill_varlen: max_seqlen_k * Hkv * D * 2 must stay below 2^31 bytes");
     if (B == 0 || max_seqlen_q == 0)
         return ok();
     if (!q || !k || !v || !cu_seqlens_q || !cu_seqlens_k || !o)

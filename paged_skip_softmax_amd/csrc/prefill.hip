@@ -8,10 +8,10 @@
 //   S^T[64 keys x 32 rows] = K[64 x D] . Q^T[D x 32]      2 x D/16 MFMA 32x32x16 (bf16, fp32 acc)
 //   online softmax in the log2 domain (scale * log2 e folded into one FMA)
 //   O^T[D x 32] += V^T[D x 64] . P^T[64 x 32]              D/32 x 4 MFMA 32x32x16
-// K and V tiles are double-buffered in LDS: while a wave computes on tile i, its lanes already hold
-// tile i+1 in registers (coalesced 16-B loads issued at the top of the iteration) and store it to the
-// other buffer afterwards, so one barrier per iteration suffices and HBM latency hides behind the
-// MFMAs.  K is read back as the A operand with 16-B reads; V, stored key-major as loaded, is read back
+// K and V tiles are double-buffered in LDS: once a wave has issued the QK^T MFMAs of tile i, its
+// lanes load tile i+1 into registers (coalesced 16-B buffer loads; rows past the sequence read as 0)
+// and store it to the other buffer after the P.V product, so one barrier per iteration suffices and
+// the load latency hides behind the softmax and P.V of tile i.  K is read back as the A operand with 16-B reads; V, stored key-major as loaded, is read back
 // transposed with ds_read_b64_tr_b16 (lane j of each 16-lane group addresses key k0 + j/4, dims
 // 4(j%4)..+3, and receives dims of its own column for keys k0..k0+3).  The key order inside P.V follows
 // the S^T register layout, so P feeds the second product straight from registers.
@@ -42,6 +42,16 @@ struct PrefillSmem {
     uint16_t k[2][kBN * kKP];
     uint16_t v[2][kBN * kVP];
 };
+
+// Buffer-resource word 3 for gfx9-family raw buffers (32-bit data format, no swizzle).
+constexpr int kBufWord3 = 0x00020000;
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ uint4 buffer_ld16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff)
+{
+    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0);
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
 
 // Transposed LDS read: 4 consecutive keys of one dim column (see the file comment).
 __device__ __forceinline__ uint2 lds_read_tr(const uint16_t *p)
@@ -110,20 +120,24 @@ void prefill_bf16_kernel(PrefillArgs a)
                 maprow[t] = 2;
     }
 
-    // cooperative tile loads: thread -> (key tid / kChunks + p * kRowsPerPass, chunk tid % kChunks)
+    // cooperative tile loads: thread -> (key tid / kChunks + p * kRowsPerPass, chunk tid % kChunks),
+    // through buffer resources covering exactly this sequence's rows of KV head g: rows past the
+    // sequence read as zero (range-checked by the hardware), so the loads need no branch or clamp.
+    // The per-thread offset stays in one VGPR; the tile and pass offsets go in the scalar offset.
     const int ld_key = tid / kChunks, ld_c = tid % kChunks;
+    const uint32_t row_bytes = (uint32_t)a.Hkv * D * 2;
+    const uint32_t seq_bytes = Lk > 0 ? ((uint32_t)(Lk - 1) * a.Hkv + 1) * D * 2 : 0;
+    const size_t head0 = ((size_t)k0 * a.Hkv + g) * D;
+    const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc((void *)(kg + head0), 0, seq_bytes, kBufWord3);
+    const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc((void *)(vg + head0), 0, seq_bytes, kBufWord3);
+    const uint32_t voff = ld_key * row_bytes + 16 * ld_c;
     uint4 kn[kPasses], vn[kPasses];
     auto load_tile = [&](int kb) {
 #pragma unroll
         for (int p = 0; p < kPasses; ++p) {
-            const int key = kb + ld_key + p * kRowsPerPass;
-            kn[p] = make_uint4(0, 0, 0, 0);
-            vn[p] = make_uint4(0, 0, 0, 0);
-            if (key < Lk) {
-                const size_t off = ((size_t)(k0 + key) * a.Hkv + g) * D + 8 * ld_c;
-                kn[p] = ld16(kg + off);
-                vn[p] = ld16(vg + off);
-            }
+            const uint32_t soff = (uint32_t)(kb + p * kRowsPerPass) * row_bytes;
+            kn[p] = buffer_ld16(krs, voff, soff);
+            vn[p] = buffer_ld16(vrs, voff, soff);
         }
     };
     auto store_tile = [&](int buf) {
@@ -148,21 +162,25 @@ void prefill_bf16_kernel(PrefillArgs a)
 
     for (int it = 0; it < niter; ++it) {
         const int kb = it * kBN, cur = it & 1;
-        if (it + 1 < niter)
-            load_tile(kb + kBN);
         if (kb < kend_w) {
             const uint16_t *Kl = sm.k[cur];
             const uint16_t *Vl = sm.v[cur];
             f32x16 sc[2];
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk) {
+                uint4 kop[kSteps];
+#pragma unroll
+                for (int s = 0; s < kSteps; ++s)
+                    kop[s] = ld16(Kl + (32 * kk + n) * KP + 16 * s + 8 * J);
 #pragma unroll
                 for (int i = 0; i < 16; ++i)
                     sc[kk][i] = 0.f;
 #pragma unroll
                 for (int s = 0; s < kSteps; ++s)
-                    sc[kk] = mfma32(as_bf16x8(ld16(Kl + (32 * kk + n) * KP + 16 * s + 8 * J)), qop[s], sc[kk]);
+                    sc[kk] = mfma32(as_bf16x8(kop[s]), qop[s], sc[kk]);
             }
+            if (it + 1 < niter)
+                load_tile(kb + kBN);
             // mask keys past the sequence and past the causal diagonal
             const bool need_mask = kb + kBN > Lk || (a.causal && kb + kBN - 1 > m0 + 32 * w + diag);
             if (need_mask) {
