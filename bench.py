@@ -39,6 +39,8 @@ def _parse():
     p.add_argument("--seed", type=int, default=0)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--only", default="", help="comma list of prefill,decode,skip,smallseq (profiling runs)")
+    p.add_argument("--calib-copy", action="store_true",
+                   help="also run one plain 1 GiB device-to-device copy (scales HBM byte counters)")
     return p.parse_args()
 
 
@@ -144,6 +146,15 @@ def main():
     ms_per_step = (t1 - t0) * 1e3 / max(1, args.steps)
     print(f"# kernel ms (mean over {args.steps} steps): " + ", ".join(f"{k}={v:.4f}" for k, v in ms.items()),
           file=sys.stderr, flush=True)
+
+    if args.calib_copy:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        src.fill_(1)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     out = {}
     rooflines = []

@@ -63,5 +63,6 @@ hipError_t launch_decode_split(const SplitArgs &a, int B, uint16_t *o, float *ls
 hipError_t launch_decode_seq(const SeqArgs &a, int B, hipStream_t stream);
 hipError_t launch_smallseq(const SmallArgs &a, hipStream_t stream);
 hipError_t launch_prefill(const PrefillArgs &a, bool bf16, int D, hipStream_t stream);
+hipError_t launch_prefill_d128(const PrefillArgs &a, hipStream_t stream); // dense bf16, D = 128
 
 } // namespace attn

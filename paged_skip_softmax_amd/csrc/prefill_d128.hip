@@ -1,0 +1,409 @@
+// Dense bf16 varlen prefill, head dim 128, for gfx950: the fast path of attn_prefill_varlen
+// ("Model-Optimizer: Add Triton unified attention kernel": variable-length batching, GQA, causal and
+// non-causal; sequences packed THD with cu_seqlens).
+//
+// Work split.  A workgroup of 4 waves takes one query tile of one sequence for NH query heads of one
+// KV head's group times RB blocks of 32 query rows (NH * RB = 4, NH the largest power of two dividing
+// the group size, at most 4), so every K/V tile staged in LDS serves NH heads: the group's query heads
+// share their KV head (GQA) and read it from LDS once.  Two workgroups share a CU.  Workgroups are
+// numbered so that the hardware's round-robin over the 8 XCDs gives each XCD a contiguous run of work
+// items ordered (KV head, sequence, query tile from the last): the query tiles of one sequence and KV
+// head run together on one XCD and find their K and V in its L2.  Each wave keeps Q^T of its 32 rows in
+// registers as the MFMA B operand for the whole loop.
+//
+// Per 64-key tile a wave computes
+//   S^T[64 keys x 32 rows] = K[64 x 128] . Q^T[128 x 32]     16 MFMA 32x32x16 (bf16 in, fp32 acc)
+//   online softmax in the log2 domain (scale * log2 e folded into one FMA)
+//   O^T[128 x 32] += V^T[128 x 64] . P^T[64 x 32]            16 MFMA 32x32x16
+// The key order inside P.V follows the S^T register layout, so P feeds the second product straight from
+// registers.  The QK^T of tile t+1 is issued in the same basic block as the softmax of tile t.
+//
+// Memory pipeline.  K and V tiles travel HBM -> LDS with buffer loads that write LDS directly (no
+// registers, no LDS store instructions), each in a two-stage ring with K one tile ahead of V: while the
+// waves use K(t+1) and V(t), the loads of K(t+2) and V(t+1) are in flight.  Each load instruction of a
+// wave fills 1 KB of LDS (4 key rows); rows past the sequence are outside the buffer resource and read
+// as zero.  LDS rows are not padded: the 16-byte chunks of a row are XOR-swizzled (slot = chunk ^
+// swz(row % 16)), which keeps both the 16-B reads of K and the transposed 8-B reads of V
+// (ds_read_b64_tr_b16) free of bank conflicts.  Waits are explicit: vmcnt of the wave's own loads,
+// then s_barrier.
+//
+// The running max used for the exponentials is only raised when a row's max grows by more than 2^8
+// (log2 units), so the O and l rescale is rare; the result is the same softmax with P <= 2^8.
+#include "kcommon.h"
+#include "launch.h"
+
+namespace attn {
+namespace {
+
+constexpr int D = 128;
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kBN = 64;                         // keys per tile
+constexpr int kTileChunks = kBN * D / 8;        // 16-B chunks in one K (or V) tile
+constexpr int kLoadsPerWave = kTileChunks / kThreads; // 1-KB load instructions per wave per tile
+constexpr float kSlack = 8.f;
+constexpr int kBufWord3 = 0x00020000;           // raw buffer resource word 3 (gfx9 family)
+constexpr int kXcds = 8;
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// Two-stage rings for K and V, one LDS array per stage.
+__shared__ __attribute__((aligned(1024))) uint4 k_st0[kTileChunks], k_st1[kTileChunks];
+__shared__ __attribute__((aligned(1024))) uint4 v_st0[kTileChunks], v_st1[kTileChunks];
+
+template <int ST> __device__ __forceinline__ uint4 *kbuf() { return ST == 0 ? k_st0 : k_st1; }
+template <int ST> __device__ __forceinline__ uint4 *vbuf() { return ST == 0 ? v_st0 : v_st1; }
+
+// XOR swizzle of the 16 chunk slots of a 256-B LDS row.
+__device__ __forceinline__ int swz(int r)
+{
+    return ((r & 1) ? 10 : 0) ^ ((r & 2) ? 4 : 0) ^ ((r & 4) ? 1 : 0) ^ ((r & 8) ? 2 : 0);
+}
+
+// s_waitcnt immediates (gfx9 layout: vmcnt [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8]).
+constexpr int wait_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+
+__device__ __forceinline__ void compiler_fence() { asm volatile("" ::: "memory"); }
+
+// Workgroup barrier without a memory-model fence: the caller has already waited for what it needs.
+__device__ __forceinline__ void barrier()
+{
+    compiler_fence();
+    __builtin_amdgcn_s_barrier();
+    compiler_fence();
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt()
+{
+    compiler_fence();
+    __builtin_amdgcn_s_waitcnt(wait_vm(N));
+    compiler_fence();
+}
+
+__device__ __forceinline__ uint2 lds_read_tr(const char *p)
+{
+    const i16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4 *)(p));
+    return __builtin_bit_cast(uint2, r);
+}
+
+// Raw buffer resource: base address, no stride, num_records bytes, gfx9 word 3.
+__device__ __forceinline__ i32x4 make_rsrc(const void *base, uint32_t num_records)
+{
+    const uint64_t a = reinterpret_cast<uint64_t>(base);
+    return i32x4{(int)(uint32_t)a, (int)(uint32_t)(a >> 32), (int)num_records, kBufWord3};
+}
+
+// LDS byte address of a shared-memory pointer.
+__device__ __forceinline__ uint32_t lds_addr(const void *p)
+{
+    return (uint32_t)(uintptr_t)((__attribute__((address_space(3))) const void *)(p));
+}
+
+// One 16-byte-per-lane buffer load written straight to LDS: lane l's data lands at lds + 16 l.  Written
+// as inline asm so that the compiler does not fold it into its own wait bookkeeping (which cannot tell
+// the LDS stages apart and would drain every load in flight before each LDS read); the loads return
+// no registers, and every wait for them is explicit (wait_vmcnt).
+__device__ __forceinline__ void dma16(uint32_t lds, uint32_t voff, i32x4 rsrc, uint32_t soff)
+{
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+                 :
+                 : "s"(lds), "v"(voff), "s"(rsrc), "s"(soff)
+                 : "memory");
+}
+
+struct Loader {
+    i32x4 krs, vrs;
+    uint32_t voff[kLoadsPerWave]; // this lane's byte offsets for its 4-row blocks
+    uint32_t tile_bytes;          // global bytes between consecutive 64-key tiles
+    int rb0;                      // first of this wave's 4-row blocks
+
+    __device__ __forceinline__ void issue(const i32x4 &rs, uint4 *dst, int t) const
+    {
+        const uint32_t soff = (uint32_t)t * tile_bytes;
+#pragma unroll
+        for (int p = 0; p < kLoadsPerWave; ++p)
+            dma16(__builtin_amdgcn_readfirstlane(lds_addr(dst + (rb0 + p) * 64)), voff[p], rs, soff);
+    }
+    template <int ST> __device__ __forceinline__ void issue_k(int t) const { issue(krs, kbuf<ST>(), t); }
+    template <int ST> __device__ __forceinline__ void issue_v(int t) const { issue(vrs, vbuf<ST>(), t); }
+};
+
+struct Wave {
+    bf16x8 qop[D / 16];
+    f32x16 acc[D / 32];
+    float m, l;
+    uint32_t ka[D / 16];       // K operand read offsets within a tile (per k-step)
+    uint32_t va[2][D / 32];    // V transposed-read offsets within a tile ([key half][d block])
+};
+
+template <int ST>
+__device__ __forceinline__ void qk_tile(const Wave &wv, f32x16 sc[2])
+{
+    const char *kt = reinterpret_cast<const char *>(kbuf<ST>());
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+            sc[kk][i] = 0.f;
+#pragma unroll
+        for (int s = 0; s < D / 16; ++s)
+            sc[kk] = mfma32(as_bf16x8(ld16(kt + kk * 32 * 256 + wv.ka[s])), wv.qop[s], sc[kk]);
+    }
+}
+
+// Masks keys at or past the row's limit (causal diagonal or sequence end).  key(kk, i) = kb + 32 kk +
+// 8 (i / 4) + 4 J + i % 4.
+__device__ __forceinline__ void mask_tile(f32x16 sc[2], int limit_minus_kb, int J)
+{
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+            if (32 * kk + 8 * (i / 4) + 4 * J + (i % 4) >= limit_minus_kb)
+                sc[kk][i] = kNegInf;
+}
+
+// Softmax of tile t (scores sc) fused with the QK^T of tile t+1 (into nxt; on the last tile it reads a
+// stale stage and its result is never used) and the P.V of tile t.
+template <int ST_V, int ST_K>
+__device__ __forceinline__ void softmax_pv(Wave &wv, f32x16 sc[2], f32x16 nxt[2], float scale_log2)
+{
+    float t0 = sc[0][0], t1 = sc[1][0];
+#pragma unroll
+    for (int i = 1; i < 16; ++i) {
+        t0 = fmaxf(t0, sc[0][i]);
+        t1 = fmaxf(t1, sc[1][i]);
+    }
+    float tm = fmaxf(t0, t1);
+    tm = fmaxf(tm, __shfl_xor(tm, 32)) * scale_log2;
+    const bool raise = tm > wv.m + kSlack;
+    if (__any(raise)) {
+        const float m_new = raise ? tm : wv.m;
+        const float alpha = exp2_fast(wv.m - m_new); // m = -inf -> 0 (acc and l still 0)
+        wv.m = m_new;
+        wv.l *= alpha;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+            wv.acc[db] *= alpha;
+    }
+    const float m_use = wv.m == kNegInf ? 0.f : wv.m;
+
+    qk_tile<ST_K>(wv, nxt);
+    uint32_t pk[2][8];
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+        for (int i = 0; i < 16; i += 2) {
+            const float p0 = exp2_fast(fmaf(sc[kk][i], scale_log2, -m_use));
+            const float p1 = exp2_fast(fmaf(sc[kk][i + 1], scale_log2, -m_use));
+            wv.l += p0 + p1;
+            pk[kk][i / 2] = pack_bf16x2(p0, p1);
+        }
+    const char *vt = reinterpret_cast<const char *>(vbuf<ST_V>());
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const bf16x8 pop = __builtin_bit_cast(bf16x8, make_uint4(pk[kk][4 * u], pk[kk][4 * u + 1],
+                                                                      pk[kk][4 * u + 2], pk[kk][4 * u + 3]));
+            const char *vk = vt + (32 * kk + 16 * u) * 256;
+#pragma unroll
+            for (int db = 0; db < D / 32; ++db) {
+                const uint2 lo = lds_read_tr(vk + wv.va[0][db]);
+                const uint2 hi = lds_read_tr(vk + wv.va[1][db]);
+                wv.acc[db] = mfma32(as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y)), pop, wv.acc[db]);
+            }
+        }
+}
+
+struct IterCtx {
+    int niter, Lk;
+    bool causal;
+    int first_row_w, diag, kend_row, J;
+    float scale_log2;
+};
+
+// Tile t, with P = t % 2: V(t) in V stage P and K(t+1) in K stage 1-P were loaded during tile t-1.
+// Wait for them, barrier, start loading K(t+2) into K stage P (freed by K(t)) and V(t+1) into V stage
+// 1-P (freed by V(t-1)), then softmax and P.V of tile t with the QK^T of tile t+1.
+template <int P>
+__device__ __forceinline__ void iteration(int t, const IterCtx &c, const Loader &ld, Wave &wv, f32x16 sc[2],
+                                          f32x16 nxt[2])
+{
+    wait_vmcnt<0>();
+    barrier();
+    if (t + 2 < c.niter)
+        ld.issue_k<P>(t + 2);
+    if (t + 1 < c.niter)
+        ld.issue_v<1 - P>(t + 1);
+    const int kb = t * kBN;
+    if (kb + kBN > c.Lk || (c.causal && kb + kBN - 1 > c.first_row_w + c.diag))
+        mask_tile(sc, c.kend_row - kb, c.J);
+    softmax_pv<P, 1 - P>(wv, sc, nxt, c.scale_log2);
+    sc[0] = nxt[0];
+    sc[1] = nxt[1];
+}
+
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void prefill_d128_kernel(PrefillArgs a, int NH, int RB, int nqt, int nunits)
+{
+    // XCD-aware work order: block i runs on XCD i % 8; XCD x takes units [x * per, (x + 1) * per)
+    const int per = gridDim.x / kXcds;
+    const int unit = (blockIdx.x % kXcds) * per + blockIdx.x / kXcds;
+    if (unit >= nunits)
+        return;
+    const int hchunks = a.G / NH;
+    const int gh = unit / (a.B * nqt), rem = unit % (a.B * nqt);
+    const int b = rem / nqt;
+    const int qt = nqt - 1 - rem % nqt;
+    const int g = gh / hchunks, hc = gh % hchunks;
+    const int rows_wg = 32 * RB;
+    const int q0 = a.cu_q[b], Lq = a.cu_q[b + 1] - q0;
+    const int k0 = a.cu_k[b], Lk = a.cu_k[b + 1] - k0;
+    const int m0 = qt * rows_wg;
+    if (m0 >= Lq)
+        return;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int n = lane & 31, J = lane >> 5;
+    const int h = g * a.G + hc * NH + (w % NH);
+    const int rbk = w / NH;
+    const int qi = m0 + 32 * rbk + n;
+    const bool row_ok = qi < Lq;
+    const int diag = Lk - Lq;
+    const int last_row = min(m0 + rows_wg, Lq) - 1;
+    const int kend = a.causal ? max(0, min(Lk, last_row + 1 + diag)) : Lk;
+    const int kend_row = a.causal ? max(0, min(Lk, qi + 1 + diag)) : Lk;
+    const int first_row_w = m0 + 32 * rbk;
+    const int niter = (kend + kBN - 1) / kBN;
+
+    // zero the LDS rings once, so that stale contents never hold NaN
+    {
+        uint4 *const bufs[4] = {k_st0, k_st1, v_st0, v_st1};
+#pragma unroll
+        for (int bi = 0; bi < 4; ++bi)
+            for (int i = tid; i < kTileChunks; i += kThreads)
+                bufs[bi][i] = make_uint4(0, 0, 0, 0);
+    }
+
+    // loads: wave w fills 4-row blocks rb0 .. rb0+3 of each tile; lane -> row 4 rb + lane/16, slot lane%16
+    Loader ld;
+    {
+        const uint16_t *kg = static_cast<const uint16_t *>(a.k);
+        const uint16_t *vg = static_cast<const uint16_t *>(a.v);
+        const size_t head0 = ((size_t)k0 * a.Hkv + (size_t)g) * D;
+        const uint32_t row_bytes = (uint32_t)a.Hkv * D * 2;
+        const uint32_t seq_bytes = Lk > 0 ? ((uint32_t)(Lk - 1) * a.Hkv + 1) * D * 2 : 0;
+        ld.krs = make_rsrc(kg + head0, seq_bytes);
+        ld.vrs = make_rsrc(vg + head0, seq_bytes);
+        ld.rb0 = kLoadsPerWave * w;
+        ld.tile_bytes = kBN * row_bytes;
+#pragma unroll
+        for (int p = 0; p < kLoadsPerWave; ++p) {
+            const int row = 4 * (ld.rb0 + p) + (lane >> 4);
+            const int chunk = (lane & 15) ^ swz(row & 15);
+            ld.voff[p] = (uint32_t)row * row_bytes + 16 * chunk;
+        }
+    }
+
+    Wave wv;
+    {
+        const uint16_t *qg = static_cast<const uint16_t *>(a.q);
+#pragma unroll
+        for (int s = 0; s < D / 16; ++s)
+            wv.qop[s] = row_ok ? as_bf16x8(ld16(qg + ((size_t)(q0 + qi) * a.Hq + h) * D + 16 * s + 8 * J))
+                               : as_bf16x8(make_uint4(0, 0, 0, 0));
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+                wv.acc[db][i] = 0.f;
+        wv.m = kNegInf;
+        wv.l = 0.f;
+        // settle the Q loads and the LDS zeroing before the first barrier; no later compiler-inserted
+        // wait inside the loop is then needed for them (such a wait would also drain the loads in flight)
+        compiler_fence();
+        __builtin_amdgcn_s_waitcnt(0);
+        barrier();
+        // K operand (A of S^T): key row n of the 32-key block, dims 16 s + 8 J: chunk 2 s + J
+        const uint32_t kA = n * 256 + 16 * (J ^ swz(n & 15));
+#pragma unroll
+        for (int s = 0; s < D / 16; ++s)
+            wv.ka[s] = kA ^ (32 * s);
+        // V operand (A of O^T) by transposed reads: lane (16-lane group G, index j) addresses key
+        // 8 half + 4 J + j/4 of a 16-key block, dims 32 db + 16 (G % 2) + 4 (j % 4)
+        const int G16 = lane >> 4, j = lane & 15;
+        const int x = 2 * (G16 & 1) + ((j & 3) >> 1);
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+            const int r = 8 * hf + 4 * J + (j >> 2);
+            const uint32_t vT = r * 256 + 8 * (j & 1) + 16 * (x ^ swz(r));
+#pragma unroll
+            for (int db = 0; db < D / 32; ++db)
+                wv.va[hf][db] = vT ^ (64 * db);
+        }
+    }
+
+    f32x16 sc[2], nxt[2];
+    if (niter > 0) {
+        // prologue: K(0), V(0), K(1); wait, then the scores of tile 0
+        ld.issue_k<0>(0);
+        ld.issue_v<0>(0);
+        if (niter > 1)
+            ld.issue_k<1>(1);
+        wait_vmcnt<0>();
+        barrier();
+        qk_tile<0>(wv, sc);
+    }
+    IterCtx c{niter, Lk, a.causal, first_row_w, diag, kend_row, J, a.scale_log2};
+    for (int t = 0; t < niter; t += 2) {
+        iteration<0>(t, c, ld, wv, sc, nxt);
+        if (t + 1 < niter)
+            iteration<1>(t + 1, c, ld, wv, sc, nxt);
+    }
+
+    wv.l += __shfl_xor(wv.l, 32);
+    if (!row_ok)
+        return;
+    const float inv = wv.l > 0.f ? 1.f / wv.l : 0.f;
+    uint16_t *og = static_cast<uint16_t *>(a.o) + ((size_t)(q0 + qi) * a.Hq + h) * D;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            uint2 pk;
+            pk.x = pack_bf16x2(wv.acc[db][4 * r] * inv, wv.acc[db][4 * r + 1] * inv);
+            pk.y = pack_bf16x2(wv.acc[db][4 * r + 2] * inv, wv.acc[db][4 * r + 3] * inv);
+            *reinterpret_cast<uint2 *>(og + 32 * db + 8 * r + 4 * J) = pk;
+        }
+    if (a.lse && J == 0)
+        a.lse[(size_t)(q0 + qi) * a.Hq + h] = wv.l > 0.f ? (wv.m + __log2f(wv.l)) * kLn2 : kNegInf;
+}
+
+} // namespace
+
+// Heads per workgroup: the largest power of two dividing the group size, at most 4.
+static int heads_per_wg(int G)
+{
+    int nh = 1;
+    while (nh < kWaves && G % (2 * nh) == 0)
+        nh *= 2;
+    return nh;
+}
+
+hipError_t launch_prefill_d128(const PrefillArgs &a, hipStream_t stream)
+{
+    const int NH = heads_per_wg(a.G), RB = kWaves / NH;
+    const int rows = 32 * RB;
+    const int nqt = (a.max_q + rows - 1) / rows;
+    const long units = (long)a.Hkv * (a.G / NH) * a.B * nqt;
+    const long blocks = (units + kXcds - 1) / kXcds * kXcds;
+    if (blocks > 0x7fffffff)
+        return hipErrorInvalidValue;
+    hipLaunchKernelGGL(prefill_d128_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, stream, a, NH, RB, nqt,
+                       (int)units);
+    return hipGetLastError();
+}
+
+} // namespace attn
