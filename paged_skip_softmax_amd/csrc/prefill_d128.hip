@@ -27,8 +27,9 @@
 // (ds_read_b64_tr_b16) free of bank conflicts.  Waits are explicit: vmcnt of the wave's own loads,
 // then s_barrier.
 //
-// The running max used for the exponentials is only raised when a row's max grows by more than 2^8
-// (log2 units), so the O and l rescale is rare; the result is the same softmax with P <= 2^8.
+// The running max used for the exponentials is only raised when a row's max exceeds it by more than 8
+// (log2 units, a factor 2^8), so the O and l rescale is rare; the result is the same softmax computed
+// with unnormalised weights P <= 2^8.
 #include "kcommon.h"
 #include "launch.h"
 
@@ -48,12 +49,20 @@ constexpr int kXcds = 8;
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 
-// Two-stage rings for K and V, one LDS array per stage.
+constexpr int kStages = 2;
+
+// Two-stage rings for K and V, one LDS array per stage (64 KB per workgroup).
 __shared__ __attribute__((aligned(1024))) uint4 k_st0[kTileChunks], k_st1[kTileChunks];
 __shared__ __attribute__((aligned(1024))) uint4 v_st0[kTileChunks], v_st1[kTileChunks];
 
-template <int ST> __device__ __forceinline__ uint4 *kbuf() { return ST == 0 ? k_st0 : k_st1; }
-template <int ST> __device__ __forceinline__ uint4 *vbuf() { return ST == 0 ? v_st0 : v_st1; }
+template <int ST> __device__ __forceinline__ uint4 *kbuf()
+{
+    return ST == 0 ? k_st0 : k_st1;
+}
+template <int ST> __device__ __forceinline__ uint4 *vbuf()
+{
+    return ST == 0 ? v_st0 : v_st1;
+}
 
 // XOR swizzle of the 16 chunk slots of a 256-B LDS row.
 __device__ __forceinline__ int swz(int r)
@@ -117,17 +126,17 @@ struct Loader {
     i32x4 krs, vrs;
     uint32_t voff[kLoadsPerWave]; // this lane's byte offsets for its 4-row blocks
     uint32_t tile_bytes;          // global bytes between consecutive 64-key tiles
-    int rb0;                      // first of this wave's 4-row blocks
+    uint32_t m0k[kStages], m0v[kStages]; // LDS byte address of this wave's first 4-row block per stage
 
-    __device__ __forceinline__ void issue(const i32x4 &rs, uint4 *dst, int t) const
+    __device__ __forceinline__ void issue(const i32x4 &rs, uint32_t m0, int t) const
     {
         const uint32_t soff = (uint32_t)t * tile_bytes;
 #pragma unroll
         for (int p = 0; p < kLoadsPerWave; ++p)
-            dma16(__builtin_amdgcn_readfirstlane(lds_addr(dst + (rb0 + p) * 64)), voff[p], rs, soff);
+            dma16(m0 + p * 1024, voff[p], rs, soff);
     }
-    template <int ST> __device__ __forceinline__ void issue_k(int t) const { issue(krs, kbuf<ST>(), t); }
-    template <int ST> __device__ __forceinline__ void issue_v(int t) const { issue(vrs, vbuf<ST>(), t); }
+    template <int ST> __device__ __forceinline__ void issue_k(int t) const { issue(krs, m0k[ST], t); }
+    template <int ST> __device__ __forceinline__ void issue_v(int t) const { issue(vrs, m0v[ST], t); }
 };
 
 struct Wave {
@@ -165,10 +174,23 @@ __device__ __forceinline__ void mask_tile(f32x16 sc[2], int limit_minus_kb, int 
                 sc[kk][i] = kNegInf;
 }
 
-// Softmax of tile t (scores sc) fused with the QK^T of tile t+1 (into nxt; on the last tile it reads a
-// stale stage and its result is never used) and the P.V of tile t.
-template <int ST_V, int ST_K>
-__device__ __forceinline__ void softmax_pv(Wave &wv, f32x16 sc[2], f32x16 nxt[2], float scale_log2)
+// Keeps a computed value at this point of the instruction stream (the compiler would otherwise sink it
+// to its first use and undo the interleaving below).
+__device__ __forceinline__ void anchor(uint32_t v) { asm volatile("" ::"v"(v)); }
+__device__ __forceinline__ void anchor(float v) { asm volatile("" ::"v"(v)); }
+// No instruction may be scheduled across this point.
+__device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
+
+struct IterCtx {
+    int niter, Lk;
+    bool causal;
+    int first_row_w, diag, kend_row, J;
+    float scale_log2;
+};
+
+// Row max of a masked score tile in log2 units, and whether it raises the running max by more than the
+// slack (then the O and l rescale is due before the tile's exponentials).
+__device__ __forceinline__ void tile_max(const f32x16 sc[2], float scale_log2, Wave &wv, float &tm, bool &raise)
 {
     float t0 = sc[0][0], t1 = sc[1][0];
 #pragma unroll
@@ -176,9 +198,39 @@ __device__ __forceinline__ void softmax_pv(Wave &wv, f32x16 sc[2], f32x16 nxt[2]
         t0 = fmaxf(t0, sc[0][i]);
         t1 = fmaxf(t1, sc[1][i]);
     }
-    float tm = fmaxf(t0, t1);
+    tm = fmaxf(t0, t1);
     tm = fmaxf(tm, __shfl_xor(tm, 32)) * scale_log2;
-    const bool raise = tm > wv.m + kSlack;
+    raise = tm > wv.m + kSlack;
+}
+
+__device__ __forceinline__ bool needs_mask(int t, const IterCtx &c)
+{
+    const int kb = t * kBN;
+    return kb + kBN > c.Lk || (c.causal && kb + kBN - 1 > c.first_row_w + c.diag);
+}
+
+// Tile t held in stage ST = t % 2 (K(t+1) in the other stage).  K runs one tile ahead of V: when tile
+// t starts, K(t+1) and V(t) must be resident.
+//   wait for the wave's loads, barrier (every wave is done with K(t) and V(t-1)), then start loading
+//   K(t+2) and V(t+1) into those two stages;
+//   (a) rescale O and l when the max rose by more than the slack;
+//   (b) QK^T of tile t+1, with the exponentials of tile t placed between its MFMAs;
+//   (c) mask tile t+1 where it crosses the diagonal or the sequence end;
+//   (d) P.V of tile t, with the row max of tile t+1 placed between its MFMAs.
+// On the last tile, (b)-(d) compute scores from a stale K stage that are never used.
+template <int ST>
+__device__ __forceinline__ void iteration(int t, const IterCtx &c, const Loader &ld, Wave &wv, f32x16 sc[2],
+                                          float &tm, bool &raise)
+{
+    wait_vmcnt<0>();
+    barrier();
+    if (t + 2 < c.niter)
+        ld.issue_k<ST>(t + 2);
+    if (t + 1 < c.niter)
+        ld.issue_v<(ST + 1) % kStages>(t + 1);
+    constexpr int P = ST;
+
+    // (a)
     if (__any(raise)) {
         const float m_new = raise ? tm : wv.m;
         const float alpha = exp2_fast(wv.m - m_new); // m = -inf -> 0 (acc and l still 0)
@@ -189,61 +241,75 @@ __device__ __forceinline__ void softmax_pv(Wave &wv, f32x16 sc[2], f32x16 nxt[2]
             wv.acc[db] *= alpha;
     }
     const float m_use = wv.m == kNegInf ? 0.f : wv.m;
+    const float sl = c.scale_log2;
 
-    qk_tile<ST_K>(wv, nxt);
+    // (b) 16 MFMA steps, alternating the two 32-key blocks of tile t+1; K operands read two steps ahead
+    f32x16 nx[2];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        nx[0][i] = 0.f;
+        nx[1][i] = 0.f;
+    }
     uint32_t pk[2][8];
+    {
+        const char *kt = reinterpret_cast<const char *>(kbuf<(P + 1) % kStages>());
+        auto kop = [&](int step) { return ld16(kt + (step & 1) * 32 * 256 + wv.ka[step >> 1]); };
+        uint4 k0 = kop(0), k1 = kop(1);
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-        for (int i = 0; i < 16; i += 2) {
-            const float p0 = exp2_fast(fmaf(sc[kk][i], scale_log2, -m_use));
-            const float p1 = exp2_fast(fmaf(sc[kk][i + 1], scale_log2, -m_use));
+        for (int step = 0; step < 16; ++step) {
+            const uint4 k2 = step + 2 < 16 ? kop(step + 2) : k0;
+            nx[step & 1] = mfma32(as_bf16x8(k0), wv.qop[step >> 1], nx[step & 1]);
+            const int kk = step >> 3, i = 2 * (step & 7);
+            const float p0 = exp2_fast(fmaf(sc[kk][i], sl, -m_use));
+            const float p1 = exp2_fast(fmaf(sc[kk][i + 1], sl, -m_use));
             wv.l += p0 + p1;
-            pk[kk][i / 2] = pack_bf16x2(p0, p1);
+            pk[kk][i >> 1] = pack_bf16x2(p0, p1);
+            anchor(pk[kk][i >> 1]);
+            sched_fence();
+            k0 = k1;
+            k1 = k2;
         }
-    const char *vt = reinterpret_cast<const char *>(vbuf<ST_V>());
+    }
+
+    // (c)
+    if (t + 1 < c.niter && needs_mask(t + 1, c))
+        mask_tile(nx, c.kend_row - (t + 1) * kBN, c.J);
+
+    // (d) 16 MFMA steps over (32-key block kk, 16-key half u, d block db), db fastest so consecutive
+    // MFMAs use different accumulators; V operands read two steps ahead
+    float t0 = nx[0][0], t1 = nx[1][0];
+    {
+        const char *vt = reinterpret_cast<const char *>(vbuf<P>());
+        auto vop = [&](int step) {
+            const char *vk = vt + (32 * (step >> 3) + 16 * ((step >> 2) & 1)) * 256;
+            const uint2 lo = lds_read_tr(vk + wv.va[0][step & 3]);
+            const uint2 hi = lds_read_tr(vk + wv.va[1][step & 3]);
+            return make_uint4(lo.x, lo.y, hi.x, hi.y);
+        };
+        uint4 v0 = vop(0), v1 = vop(1);
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
+        for (int step = 0; step < 16; ++step) {
+            const uint4 v2 = step + 2 < 16 ? vop(step + 2) : v0;
+            const int kk = step >> 3, u = (step >> 2) & 1;
             const bf16x8 pop = __builtin_bit_cast(bf16x8, make_uint4(pk[kk][4 * u], pk[kk][4 * u + 1],
                                                                       pk[kk][4 * u + 2], pk[kk][4 * u + 3]));
-            const char *vk = vt + (32 * kk + 16 * u) * 256;
-#pragma unroll
-            for (int db = 0; db < D / 32; ++db) {
-                const uint2 lo = lds_read_tr(vk + wv.va[0][db]);
-                const uint2 hi = lds_read_tr(vk + wv.va[1][db]);
-                wv.acc[db] = mfma32(as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y)), pop, wv.acc[db]);
+            wv.acc[step & 3] = mfma32(as_bf16x8(v0), pop, wv.acc[step & 3]);
+            if (step < 15) {
+                t0 = fmaxf(t0, nx[0][step + 1]);
+                t1 = fmaxf(t1, nx[1][step + 1]);
+                anchor(t0);
+                anchor(t1);
             }
+            sched_fence();
+            v0 = v1;
+            v1 = v2;
         }
-}
-
-struct IterCtx {
-    int niter, Lk;
-    bool causal;
-    int first_row_w, diag, kend_row, J;
-    float scale_log2;
-};
-
-// Tile t, with P = t % 2: V(t) in V stage P and K(t+1) in K stage 1-P were loaded during tile t-1.
-// Wait for them, barrier, start loading K(t+2) into K stage P (freed by K(t)) and V(t+1) into V stage
-// 1-P (freed by V(t-1)), then softmax and P.V of tile t with the QK^T of tile t+1.
-template <int P>
-__device__ __forceinline__ void iteration(int t, const IterCtx &c, const Loader &ld, Wave &wv, f32x16 sc[2],
-                                          f32x16 nxt[2])
-{
-    wait_vmcnt<0>();
-    barrier();
-    if (t + 2 < c.niter)
-        ld.issue_k<P>(t + 2);
-    if (t + 1 < c.niter)
-        ld.issue_v<1 - P>(t + 1);
-    const int kb = t * kBN;
-    if (kb + kBN > c.Lk || (c.causal && kb + kBN - 1 > c.first_row_w + c.diag))
-        mask_tile(sc, c.kend_row - kb, c.J);
-    softmax_pv<P, 1 - P>(wv, sc, nxt, c.scale_log2);
-    sc[0] = nxt[0];
-    sc[1] = nxt[1];
+    }
+    tm = fmaxf(t0, t1);
+    tm = fmaxf(tm, __shfl_xor(tm, 32)) * sl;
+    raise = tm > wv.m + kSlack;
+    sc[0] = nx[0];
+    sc[1] = nx[1];
 }
 
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
@@ -297,11 +363,16 @@ void prefill_d128_kernel(PrefillArgs a, int NH, int RB, int nqt, int nunits)
         const uint32_t seq_bytes = Lk > 0 ? ((uint32_t)(Lk - 1) * a.Hkv + 1) * D * 2 : 0;
         ld.krs = make_rsrc(kg + head0, seq_bytes);
         ld.vrs = make_rsrc(vg + head0, seq_bytes);
-        ld.rb0 = kLoadsPerWave * w;
+        const int rb0 = kLoadsPerWave * w;
         ld.tile_bytes = kBN * row_bytes;
+        const uint32_t wave_off = __builtin_amdgcn_readfirstlane(rb0 * 1024);
+        ld.m0k[0] = lds_addr(k_st0) + wave_off;
+        ld.m0k[1] = lds_addr(k_st1) + wave_off;
+        ld.m0v[0] = lds_addr(v_st0) + wave_off;
+        ld.m0v[1] = lds_addr(v_st1) + wave_off;
 #pragma unroll
         for (int p = 0; p < kLoadsPerWave; ++p) {
-            const int row = 4 * (ld.rb0 + p) + (lane >> 4);
+            const int row = 4 * (rb0 + p) + (lane >> 4);
             const int chunk = (lane & 15) ^ swz(row & 15);
             ld.voff[p] = (uint32_t)row * row_bytes + 16 * chunk;
         }
@@ -345,22 +416,32 @@ void prefill_d128_kernel(PrefillArgs a, int NH, int RB, int nqt, int nunits)
         }
     }
 
-    f32x16 sc[2], nxt[2];
+    f32x16 sc[2];
+    float tm = kNegInf;
+    bool raise = false;
+    IterCtx c{niter, Lk, a.causal, first_row_w, diag, kend_row, J, a.scale_log2};
     if (niter > 0) {
-        // prologue: K(0), V(0), K(1); wait, then the scores of tile 0
+        // prologue: K(0), V(0), K(1) in flight; wait for K(0), then the masked scores of tile 0 and
+        // their row max
+        constexpr int L = kLoadsPerWave;
         ld.issue_k<0>(0);
         ld.issue_v<0>(0);
-        if (niter > 1)
+        if (niter > 1) {
             ld.issue_k<1>(1);
-        wait_vmcnt<0>();
+            wait_vmcnt<2 * L>();
+        } else {
+            wait_vmcnt<L>();
+        }
         barrier();
         qk_tile<0>(wv, sc);
+        if (needs_mask(0, c))
+            mask_tile(sc, kend_row, J);
+        tile_max(sc, a.scale_log2, wv, tm, raise);
     }
-    IterCtx c{niter, Lk, a.causal, first_row_w, diag, kend_row, J, a.scale_log2};
-    for (int t = 0; t < niter; t += 2) {
-        iteration<0>(t, c, ld, wv, sc, nxt);
+    for (int t = 0; t < niter; t += kStages) {
+        iteration<0>(t, c, ld, wv, sc, tm, raise);
         if (t + 1 < niter)
-            iteration<1>(t + 1, c, ld, wv, sc, nxt);
+            iteration<1>(t + 1, c, ld, wv, sc, tm, raise);
     }
 
     wv.l += __shfl_xor(wv.l, 32);
