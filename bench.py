@@ -41,6 +41,9 @@ def _parse():
     p.add_argument("--only", default="", help="comma list of prefill,decode,skip,smallseq (profiling runs)")
     p.add_argument("--calib-copy", action="store_true",
                    help="also run one plain 1 GiB device-to-device copy (scales HBM byte counters)")
+    p.add_argument("--summarize-profiles", metavar="DIR", default="",
+                   help="no GPU work: turn the rocprofv3 csv output under DIR/prof_trace, DIR/prof_fetch and "
+                        "DIR/prof_write into the summaries under profiles/")
     return p.parse_args()
 
 
@@ -55,18 +58,27 @@ def _traffic_from_profiles(kernel: str):
         ent = data.get(kernel)
         if not ent:
             return None
-        src = os.path.join(ROOT, ent["source"])
-        import hashlib
-        digest = hashlib.sha256(open(src, "rb").read()).hexdigest()
-        if digest != ent.get("source_sha256"):
+        if _sources_digest(ent["sources"]) != ent.get("sources_sha256"):
             return None  # the kernel changed since the counters were taken
         return float(ent["bytes_per_launch"])
     except Exception:
         return None
 
 
+def _sources_digest(paths):
+    import hashlib
+    h = hashlib.sha256()
+    for rel in paths:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
 def main():
     args = _parse()
+    if args.summarize_profiles:
+        _summarize_profiles(args.summarize_profiles)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (every path here runs on a "
               "single MI355X)", file=sys.stderr)
@@ -148,6 +160,7 @@ def main():
           file=sys.stderr, flush=True)
 
     if args.calib_copy:
+        # a plain device-to-device copy of 1 GiB: 2^20 KiB read and 2^20 KiB written
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
         src.fill_(1)
@@ -164,9 +177,9 @@ def main():
         tflops = flops / (ms["prefill"] * 1e-3) / 1e12
         out["prefill"] = {"ms": ms["prefill"], "ms_min": ms_min["prefill"], "flop": flops, "tflops": tflops,
                           "frac_peak": tflops / PEAK_BF16_TFLOPS}
-        rooflines.append({"kernel": "prefill_bf16_kernel<128,false>", "bound": "mfma", "achieved": tflops,
+        rooflines.append({"kernel": "prefill_d128_kernel", "bound": "mfma", "achieved": tflops,
                           "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": tflops / PEAK_BF16_TFLOPS,
-                          "traffic": _traffic_from_profiles("prefill_bf16_kernel"), "ms": ms["prefill"]})
+                          "traffic": _traffic_from_profiles("prefill_d128_kernel"), "ms": ms["prefill"]})
     if "decode" in only:
         d = work["decode"]
         kv = 4.0 * d.Hkv * d.D * float(d.lens.sum())
@@ -280,6 +293,140 @@ def _cpu_baseline(x):
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
             "sample": f"every {step}th causal query row of the longest sequence (L={int(L[b])}), all {x.Hq} heads: "
                       f"{len(rows)} rows, {flops:.3e} FLOP in {dt:.2f} s"}
+
+
+# ---- rocprofv3 summaries -------------------------------------------------------------------------------
+
+# kernel -> (workload the bench runs it on, summary file stem, sources it is built from)
+_KSRC = ["paged_skip_softmax_amd/csrc/kcommon.h", "paged_skip_softmax_amd/csrc/launch.h"]
+PROFILED = {
+    "prefill_d128_kernel": ("varlen causal prefill bf16, 16 seqs L~U[256,4096], Hq=32, Hkv=8, D=128",
+                            "prefill_d128_kernel.varlen_causal_16seq_L256-4096_Hq32_Hkv8_D128",
+                            ["paged_skip_softmax_amd/csrc/prefill_d128.hip"] + _KSRC),
+    "decode_split_kernel": ("paged decode B=64, L~U[1024,32768], page 16, 32 splits of 128-key tiles",
+                            "decode_split_kernel.paged_decode_B64_L1k-32k_page16_32splits",
+                            ["paged_skip_softmax_amd/csrc/decode.hip"] + _KSRC),
+    "decode_merge_kernel": ("merge of the 32 split partials, B=64, Hq=32, D=128",
+                            "decode_merge_kernel.paged_decode_B64_Hq32_32splits",
+                            ["paged_skip_softmax_amd/csrc/decode.hip"] + _KSRC),
+    "decode_seq_kernel": ("sequential skip decode on hot keys, B=64, L~U[1024,32768], 32-key tiles, "
+                          "threshold 0 / 0.01 / 0.1 in turn",
+                          "decode_seq_kernel.paged_decode_hot_B64_thr0-0.01-0.1",
+                          ["paged_skip_softmax_amd/csrc/decode.hip"] + _KSRC),
+    "smallseq_kernel": ("small-seq cross-attention B=30720, s_kv in {2,4,6,8,12,16}, H=16, D=128",
+                        "smallseq_kernel.smallseq_cross_B30720_H16_D128",
+                        ["paged_skip_softmax_amd/csrc/smallseq.hip"] + _KSRC),
+}
+PROFILE_COMMANDS = {
+    "trace": "rocprofv3 --kernel-trace --stats -f csv -d gpurun_out/prof_trace -o run -- "
+             "python3 bench.py --steps 5 --warmup 2 --no-cpu-baseline",
+    "fetch": "rocprofv3 --pmc FETCH_SIZE -f csv -d gpurun_out/prof_fetch -o run -- "
+             "python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline --calib-copy",
+    "write": "rocprofv3 --pmc WRITE_SIZE -f csv -d gpurun_out/prof_write -o run -- "
+             "python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline --calib-copy",
+    "summary": "python3 bench.py --summarize-profiles gpurun_out",
+}
+
+
+def _csv(dirpath, suffix):
+    import csv
+    import glob
+    hits = sorted(glob.glob(os.path.join(dirpath, "**", "*" + suffix), recursive=True))
+    if not hits:
+        raise FileNotFoundError(f"no *{suffix} under {dirpath}")
+    with open(hits[0]) as f:
+        return list(csv.DictReader(f))
+
+
+def _match(name):
+    for k in PROFILED:
+        if k + "(" in name or k + "<" in name:
+            return k
+    if "copyBuffer" in name:
+        return "copy"
+    return None
+
+
+def _per_dispatch_counter(rows, counter):
+    """kernel key -> list of per-dispatch values (summed over the counter's instances), dispatch order."""
+    agg, key, order = {}, {}, []
+    for r in rows:
+        if r["Counter_Name"] != counter:
+            continue
+        d = int(r["Dispatch_Id"])
+        if d not in agg:
+            agg[d] = 0.0
+            key[d] = _match(r["Kernel_Name"])
+            order.append(d)
+        agg[d] += float(r["Counter_Value"])
+    out = {}
+    for d in sorted(order):
+        if key[d]:
+            out.setdefault(key[d], []).append(agg[d])
+    return out
+
+
+def _summarize_profiles(base):
+    import numpy as np
+    trace = _csv(os.path.join(base, "prof_trace"), "kernel_trace.csv")
+    stats = _csv(os.path.join(base, "prof_trace"), "kernel_stats.csv")
+    fetch = _per_dispatch_counter(_csv(os.path.join(base, "prof_fetch"), "counter_collection.csv"), "FETCH_SIZE")
+    write = _per_dispatch_counter(_csv(os.path.join(base, "prof_write"), "counter_collection.csv"), "WRITE_SIZE")
+    if "copy" not in fetch or "copy" not in write:
+        raise RuntimeError("the 1 GiB calibration copy is missing from the counter runs")
+    kib = float(1 << 20)
+    # the 1 GiB copy is the largest copy dispatch of each run
+    c_fetch, c_write = max(fetch["copy"]), max(write["copy"])
+    f_fetch = kib / c_fetch
+    f_write = kib / c_write
+    durs = {}
+    for r in trace:
+        k = _match(r["Kernel_Name"])
+        if k and k != "copy":
+            durs.setdefault(k, []).append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+    outdir = os.path.join(ROOT, "profiles")
+    os.makedirs(outdir, exist_ok=True)
+    traffic = {}
+    cmds = "\n".join(f"#   {k}: {v}" for k, v in PROFILE_COMMANDS.items())
+    for k, (workload, stem, srcs) in PROFILED.items():
+        if k not in durs:
+            continue
+        st = [r for r in stats if _match(r["Name"]) == k]
+        lines = [f"# {k} on: {workload}",
+                 "# commands (repository root, TMPDIR=/tmp; the summary step runs on any host):", cmds, ""]
+        for r in st:
+            lines.append(f"kernel-trace --stats: calls {r['Calls']}, average {float(r['AverageNs']) / 1e3:.2f} us, "
+                         f"min {float(r['MinNs']) / 1e3:.2f} us, max {float(r['MaxNs']) / 1e3:.2f} us, "
+                         f"{float(r['Percentage']):.2f}% of GPU kernel time")
+        d = np.array(durs[k], dtype=np.float64) / 1e3
+        lines.append(f"kernel_trace.csv: {len(d)} dispatches, mean {d.mean():.2f} us, median {np.median(d):.2f} us")
+        if k == "decode_seq_kernel" and len(d) % 3 == 0:
+            for i, thr in enumerate(("0", "0.01", "0.1")):
+                lines.append(f"  threshold {thr}: mean {d[i::3].mean():.2f} us over {len(d[i::3])} dispatches")
+        fk = fetch.get(k, [])
+        wk = write.get(k, [])
+        if fk and wk:
+            fm, wm = float(np.mean(fk)), float(np.mean(wk))
+            byts = (fm * f_fetch + wm * f_write) * 1024.0
+            lines += [f"FETCH_SIZE {fm:.0f} KiB / dispatch (mean of {len(fk)}), WRITE_SIZE {wm:.0f} KiB / dispatch "
+                      f"(mean of {len(wk)})",
+                      f"calibration: the 1 GiB copy read FETCH_SIZE {c_fetch:.0f} KiB and WRITE_SIZE "
+                      f"{c_write:.0f} KiB, factors {f_fetch:.4f} (fetch) and {f_write:.4f} (write)",
+                      f"HBM traffic per launch (scaled): {byts / 1e6:.1f} MB"]
+            if k == "decode_seq_kernel" and len(fk) % 3 == 0 and len(wk) % 3 == 0:
+                for i, thr in enumerate(("0", "0.01", "0.1")):
+                    b_i = (np.mean(fk[i::3]) * f_fetch + np.mean(wk[i::3]) * f_write) * 1024.0
+                    lines.append(f"  threshold {thr}: {b_i / 1e6:.1f} MB per launch")
+                byts = (np.mean(fk[0::3]) * f_fetch + np.mean(wk[0::3]) * f_write) * 1024.0
+            traffic[k] = {"bytes_per_launch": float(byts), "fetch_kib": fm, "write_kib": wm,
+                          "fetch_factor": f_fetch, "write_factor": f_write, "sources": srcs,
+                          "sources_sha256": _sources_digest(srcs), "summary": f"profiles/{stem}.txt"}
+        with open(os.path.join(outdir, stem + ".txt"), "w") as f:
+            f.write("\n".join(lines) + "\n")
+        print(f"wrote profiles/{stem}.txt")
+    with open(os.path.join(outdir, "traffic.json"), "w") as f:
+        json.dump(traffic, f, indent=1, sort_keys=True)
+    print("wrote profiles/traffic.json")
 
 
 if __name__ == "__main__":
