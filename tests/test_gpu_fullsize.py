@@ -1,0 +1,139 @@
+"""GPU parity at the full workload sizes, in the launch configuration the benchmark times.
+
+The oracle checks sampled outputs (prefill: a fixed sample of query rows of every sequence, all heads;
+decode: a sample of batch rows, all heads) or every output where the fp64 work stays within seconds
+(skip decode maps and outputs, small-seq).  Same tolerances as the small parity tests: 2e-2 max-abs
+for bf16 outputs, 1e-3 for LSE, >= 99.9 % skip-map agreement with exact visited sets, skip outputs
+compared against the oracle replaying the GPU's decisions.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import paged_skip_softmax_amd as attn
+from paged_skip_softmax_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+BF16_TOL = 2e-2
+LSE_TOL = 1e-3
+DEV = "cuda"
+
+
+def _np(t):
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def _check_map(g, o, min_agree=0.999):
+    assert g.shape == o.shape
+    assert np.array_equal(g == 2, o == 2), "visited tiles differ"
+    vis = o != 2
+    agree = float((g[vis] == o[vis]).mean())
+    assert agree >= min_agree, f"skip-map agreement {agree:.5f}"
+    return agree
+
+
+def test_full_varlen_prefill_sampled_rows():
+    x = W.varlen_prefill(seed=1001, device=DEV)           # 16 sequences, L in [256, 4096], Hq 32, Hkv 8, D 128
+    o = torch.empty_like(x.q)
+    _, lse, _ = attn.attn_prefill_varlen(x.q, x.k, x.v, x.cu_q, x.cu_k, x.max_q, x.max_k, causal=True, out=o,
+                                         return_lse=True)
+    torch.cuda.synchronize()
+    on, ln = _np(o), _np(lse)
+    assert np.isfinite(on).all()
+    cu = x.cu_q.cpu().tolist()
+    rng = np.random.default_rng(11)
+    toks = []
+    for b in range(x.B):
+        L = cu[b + 1] - cu[b]
+        # the first rows, the rows around the 32/64-row tile edges, the last rows and a random sample
+        pick = {0, 1, 31, 32, 63, 64, L // 2, L - 2, L - 1}
+        pick |= set(rng.choice(L, size=min(L, 40), replace=False).tolist())
+        toks += [cu[b] + i for i in sorted(p for p in pick if 0 <= p < L)]
+    rows = [(t, h) for t in toks for h in range(x.Hq)]
+    od, ld, _ = oracle.prefill(x.q.cpu(), x.k.cpu(), x.v.cpu(), x.cu_q.cpu(), x.cu_k.cpu(), x.Hq, x.Hkv, x.scale,
+                               True, rows=rows)
+    r = np.array(rows)
+    assert np.max(np.abs(on[r[:, 0], r[:, 1]] - od)) <= BF16_TOL
+    assert np.max(np.abs(ln[r[:, 0], r[:, 1]] - ld)) <= LSE_TOL
+
+
+@pytest.fixture(scope="module")
+def decode_host():
+    """The full paged-decode workload (B 64, L in [1024, 32768], 140,000-page pool) and its host copy."""
+    x = W.paged_decode(seed=1002, device=DEV)
+    host = dict(q=x.q.cpu(), k=x.k_cache.cpu(), v=x.v_cache.cpu(), bt=x.block_table.cpu(), sl=x.seq_lens.cpu())
+    return x, host
+
+
+def test_full_paged_decode_split_k_sampled_rows(decode_host):
+    x, h = decode_host
+    ws = torch.empty(attn.attn_decode_paged_workspace_size(x.B, x.Hq, x.D, 32), dtype=torch.uint8, device=DEV)
+    o, lse, _ = attn.attn_decode_paged(x.q, x.k_cache, x.v_cache, x.block_table, x.seq_lens, num_splits=32,
+                                       workspace=ws, return_lse=True)
+    torch.cuda.synchronize()
+    on, ln = _np(o), _np(lse)
+    assert np.isfinite(on).all(), "NaN poison reached the output"
+    L = h["sl"].numpy()
+    bs = sorted({int(np.argmax(L)), int(np.argmin(L))} | set(range(0, x.B, 5)))
+    rows = [(b, hh) for b in bs for hh in range(x.Hq)]
+    od, ld, _ = oracle.decode(h["q"], h["k"], h["v"], h["bt"], h["sl"], x.scale, rows=rows)
+    r = np.array(rows)
+    assert np.max(np.abs(on[r[:, 0], r[:, 1]] - od)) <= BF16_TOL
+    assert np.max(np.abs(ln[r[:, 0], r[:, 1]] - ld)) <= LSE_TOL
+
+
+@pytest.fixture(scope="module")
+def hot_host():
+    x = W.paged_decode_hot(seed=1002, device=DEV)
+    host = dict(q=x.q.cpu(), k=x.k_cache.cpu(), v=x.v_cache.cpu(), bt=x.block_table.cpu(), sl=x.seq_lens.cpu())
+    return x, host
+
+
+@pytest.mark.parametrize("thr", [0.0, 0.01, 0.1])
+def test_full_skip_decode_all_rows(hot_host, thr):
+    x, h = hot_host
+    o, lse, smap = attn.attn_decode_paged(x.q, x.k_cache, x.v_cache, x.block_table, x.seq_lens, num_splits=1,
+                                          skip_threshold=thr, return_lse=True, return_skip_map=True)
+    torch.cuda.synchronize()
+    on, ln = _np(o), _np(lse)
+    assert np.isfinite(on).all()
+    g = smap.cpu().numpy()
+    _, _, om = oracle.decode(h["q"], h["k"], h["v"], h["bt"], h["sl"], x.scale, mode="skip", thr=thr, tile=32,
+                             stride=g.shape[-1])
+    _check_map(g, om)
+    if thr == 0.0:
+        assert set(np.unique(g)) <= {0, 2}
+    if thr == 0.1:
+        assert (g == 1).sum() / (g != 2).sum() > 0.5, "the hot-key workload should make most tiles skippable"
+    orp, lrp, _ = oracle.decode(h["q"], h["k"], h["v"], h["bt"], h["sl"], x.scale, mode="skip", tile=32,
+                                replay=np.where(g == 2, 0, g).reshape(-1, g.shape[-1]), stride=g.shape[-1])
+    assert np.max(np.abs(on - orp)) <= BF16_TOL
+    assert np.max(np.abs(ln - lrp)) <= LSE_TOL
+
+
+def test_full_smallseq_all_rows():
+    x = W.smallseq_cross(seed=1004, device=DEV)              # B 30720, s_kv in {2..16}, H 16, D 128
+    o, w, lse = attn.attn_smallseq_cross(x.q, x.k, x.v, x.cu_kv, x.max_s, return_lse=True)
+    torch.cuda.synchronize()
+    od, wd = oracle.smallseq(x.q.cpu(), x.k.cpu(), x.v.cpu(), x.cu_kv.cpu(), x.max_s, x.scale)
+    assert np.max(np.abs(_np(o) - od)) <= BF16_TOL
+    assert np.max(np.abs(_np(w) - wd)) <= BF16_TOL
+
+
+def test_empty_batch_is_a_no_op():
+    # B = 0 for every entry point: nothing is launched, nothing fails
+    z32 = torch.zeros(1, dtype=torch.int32, device=DEV)
+    e = torch.empty((0, 4, 128), dtype=torch.bfloat16, device=DEV)
+    o, _, _ = attn.attn_prefill_varlen(e, torch.empty((0, 1, 128), dtype=torch.bfloat16, device=DEV),
+                                       torch.empty((0, 1, 128), dtype=torch.bfloat16, device=DEV), z32, z32, 0, 0)
+    assert o.shape == (0, 4, 128)
+    kc = torch.zeros((1, 1, 16, 128), dtype=torch.bfloat16, device=DEV)
+    o, _, _ = attn.attn_decode_paged(e, kc, kc, torch.zeros((0, 1), dtype=torch.int32, device=DEV),
+                                     torch.zeros(0, dtype=torch.int32, device=DEV))
+    assert o.shape == (0, 4, 128)
+    o, w, _ = attn.attn_smallseq_cross(e, torch.empty((0, 4, 128), dtype=torch.bfloat16, device=DEV),
+                                       torch.empty((0, 4, 128), dtype=torch.bfloat16, device=DEV), z32, 16)
+    torch.cuda.synchronize()
+    assert o.shape == (0, 4, 128) and w.shape == (0, 4, 1, 16)
