@@ -12,7 +12,9 @@
 //    all earlier tiles, skipped or not.  So the waves of the workgroup take consecutive tiles in
 //    rounds, publish their tile maxima in LDS, and each decides exactly from the prefix max -- the
 //    decisions of one sequential pass, taken in parallel.  V of a tile is read only when at least one
-//    query row of the group keeps it.
+//    query row of the group keeps it.  The K rows of the next round are loaded while the current round
+//    runs, and the batch rows are dispatched longest first, so that the longest sequences (the critical
+//    path of a one-split-per-sequence schedule) start at once and the short ones fill in behind them.
 //
 // Cache layout: [num_pages, Hkv, 16, D] bf16, so one (page, KV head) is a contiguous 4 KB slab.
 //
@@ -38,6 +40,9 @@ constexpr int kSplitWaves = 4;
 constexpr int kSeqWaves = 8;
 constexpr int kVPitch = kD + 8;                   // LDS row pitch (bf16 elements, 272 B)
 constexpr int kVTile = 2 * kPage * kVPitch;       // one wave's V staging tile (elements)
+// s_waitcnt immediate that waits for LDS / scalar memory only (vmcnt and expcnt at their maxima; gfx9
+// layout: vmcnt [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8])
+constexpr int kWaitLdsOnly = 0xF | (0x7 << 4) | (0x3 << 14);
 
 // Q^T operand: lane (n = lane%16, j = lane/16) holds head g*G+n, d = 32 s + 8 j .. +8.
 __device__ __forceinline__ void load_q_operand(const uint16_t *q, int b, int g, int Hq, int G, int lane,
@@ -317,9 +322,37 @@ hipError_t launch_decode_split(const SplitArgs &a, int B, uint16_t *o, float *ls
 
 // ------------------------------------------------------------------ sequential with skip-softmax
 
+// Sequences of up to this batch size are scheduled longest first.
+constexpr int kLptMaxBatch = 1024;
+
+// Batch row of the workgroup at dispatch position `pos`: with B <= kLptMaxBatch the rows are taken
+// in order of decreasing length (ties by index), so that the longest sequences start first and the
+// short ones fill in behind them; otherwise in index order.
+__device__ __forceinline__ int lpt_row(const int32_t *seq_lens, int B, int pos, int *slot)
+{
+    if (B > kLptMaxBatch)
+        return pos;
+    if (threadIdx.x == 0)
+        *slot = pos;
+    __syncthreads();
+    for (int i = threadIdx.x; i < B; i += blockDim.x) {
+        const int Li = seq_lens[i];
+        int rank = 0;
+        for (int jj = 0; jj < B; ++jj) {
+            const int Lj = seq_lens[jj];
+            rank += (Lj > Li) || (Lj == Li && jj < i);
+        }
+        if (rank == pos)
+            *slot = i;
+    }
+    __syncthreads();
+    return *slot;
+}
+
 __global__ __launch_bounds__(64 * kSeqWaves) void decode_seq_kernel(SeqArgs a)
 {
-    const int g = blockIdx.x, b = blockIdx.y;
+    __shared__ int row_slot;
+    const int g = blockIdx.x, b = lpt_row(a.seq_lens, gridDim.y, blockIdx.y, &row_slot);
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int n = lane & 15, j = lane >> 4;
     const int L = a.seq_lens[b];
@@ -345,26 +378,46 @@ __global__ __launch_bounds__(64 * kSeqWaves) void decode_seq_kernel(SeqArgs a)
     float run_max = kNegInf; // max of tile maxima over all earlier rounds (log2 units), head n
     const int32_t *btr = a.bt + (size_t)b * a.max_pages;
     const size_t slab = (size_t)kPage * kD;
+    const size_t head_off = (size_t)g * slab;
+    const size_t page_stride = (size_t)a.Hkv * slab;
+    // Slab offsets of the two pages of tile t; a tile past the end borrows the sequence's first tile,
+    // so that every round can load unconditionally (a tile past the end is never used).
+    auto tile_pages = [&](int t, size_t &o0, size_t &o1) {
+        const int tt = t < ntiles ? t : 0;
+        const int tok0 = tt * kSkipTile;
+        const int p0 = btr[tok0 / kPage];
+        const int p1 = tok0 + kPage < L ? btr[tok0 / kPage + 1] : p0;
+        o0 = (size_t)p0 * page_stride + head_off;
+        o1 = (size_t)p1 * page_stride + head_off;
+    };
+    // The K rows of round r+1 are loaded while round r runs: scores of a round never wait for HBM
+    // unless the previous round read no V at all.
+    size_t o0 = 0, o1 = 0;
+    uint4 kr[2][4];
+    if (ntiles > 0) {
+        tile_pages(w, o0, o1);
+        load_k_chunk(a.kc + o0, a.kc + o1, lane, kr);
+    }
     int parity = 0;
     for (int base = 0; base < ntiles; base += kSeqWaves, parity ^= 1) {
         const int t = base + w;
         const int tok0 = t * kSkipTile;
         const bool active = t < ntiles;
+        size_t n0, n1;
+        tile_pages(t + kSeqWaves, n0, n1);
+        uint4 kn[2][4];
+        load_k_chunk(a.kc + n0, a.kc + n1, lane, kn);
         f32x4 sc[2];
         float tmax = kNegInf;
-        size_t o0 = 0, o1 = 0;
-        if (active) {
-            const int p0 = btr[tok0 / kPage];
-            const int p1 = tok0 + kPage < L ? btr[tok0 / kPage + 1] : p0;
-            o0 = ((size_t)p0 * a.Hkv + g) * slab;
-            o1 = ((size_t)p1 * a.Hkv + g) * slab;
-            uint4 kr[2][4];
-            load_k_chunk(a.kc + o0, a.kc + o1, lane, kr);
+        if (active)
             tmax = chunk_scores(kr, qop, tok0, L, lane, sc) * a.scale_log2;
-        }
         if (j == 0)
             tmax_buf[parity][w][n] = tmax;
-        __syncthreads();
+        // LDS write visible, then a plain barrier: the K loads of the next round stay in flight
+        __builtin_amdgcn_s_waitcnt(kWaitLdsOnly);
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
         float prefix = run_max, round_max = run_max;
 #pragma unroll
         for (int ww = 0; ww < kSeqWaves; ++ww) {
@@ -388,6 +441,13 @@ __global__ __launch_bounds__(64 * kSeqWaves) void decode_seq_kernel(SeqArgs a)
             if (a.skip_map && j == 0 && n < a.G)
                 a.skip_map[(row0 + n) * a.map_stride + t] = skip ? 1 : 0;
         }
+#pragma unroll
+        for (int pg = 0; pg < 2; ++pg)
+#pragma unroll
+            for (int s4 = 0; s4 < 4; ++s4)
+                kr[pg][s4] = kn[pg][s4];
+        o0 = n0;
+        o1 = n1;
     }
     merge_waves<kSeqWaves>(st, smem, a.G, [&](int h, int d, float o, float lse) {
         a.o[(row0 + h) * kD + d] = f32_to_bf16(o);
