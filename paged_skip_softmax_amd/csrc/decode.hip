@@ -187,7 +187,7 @@ __device__ __forceinline__ void chunk_update(WaveState &st, const f32x4 sc[2], f
 template <int W, typename Out>
 __device__ __forceinline__ void merge_waves(WaveState &st, void *smem, int G, Out out)
 {
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int n = lane & 15, j = lane >> 4;
     st.l = sum_across_groups16(st.l);
     __syncthreads();
@@ -233,7 +233,7 @@ __device__ __forceinline__ void merge_waves(WaveState &st, void *smem, int G, Ou
 __global__ __launch_bounds__(64 * kSplitWaves) void decode_split_kernel(SplitArgs a)
 {
     const int sp = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int S = a.num_splits;
     const int L = a.seq_lens[b];
     const int ntiles = (L + kSplitTile - 1) / kSplitTile;
@@ -251,16 +251,45 @@ __global__ __launch_bounds__(64 * kSplitWaves) void decode_split_kernel(SplitArg
     state_init(st);
     const int32_t *btr = a.bt + (size_t)b * a.max_pages;
     const size_t slab = (size_t)kPage * kD;
-    for (int tok0 = t0 + 2 * kPage * w; tok0 < t1; tok0 += 2 * kPage * kSplitWaves) {
-        const int p0 = btr[tok0 / kPage];
-        const int p1 = tok0 + kPage < t1 ? btr[tok0 / kPage + 1] : p0;
-        const size_t o0 = ((size_t)p0 * a.Hkv + g) * slab, o1 = ((size_t)p1 * a.Hkv + g) * slab;
+    // software pipeline: the K and V of the wave's next chunk are loaded before the current chunk is
+    // computed; a chunk past the split's end borrows the split's first chunk (never used)
+    auto chunk_off = [&](int tok0, size_t &o0, size_t &o1) {
+        const int tt = tok0 < t1 ? tok0 : t0;
+        const int p0 = btr[tt / kPage];
+        const int p1 = tt + kPage < t1 ? btr[tt / kPage + 1] : p0;
+        o0 = ((size_t)p0 * a.Hkv + g) * slab;
+        o1 = ((size_t)p1 * a.Hkv + g) * slab;
+    };
+    const int step = 2 * kPage * kSplitWaves;
+    int tok0 = t0 + 2 * kPage * w;
+    if (tok0 < t1) {
+        size_t o0, o1;
+        chunk_off(tok0, o0, o1);
         uint4 kr[2][4], vr[2][4];
         load_k_chunk(a.kc + o0, a.kc + o1, lane, kr);
         load_v_chunk(a.vc + o0, a.vc + o1, lane, vr);
-        f32x4 sc[2];
-        const float cmax = chunk_scores(kr, qop, tok0, t1, lane, sc);
-        chunk_update(st, sc, cmax * a.scale_log2, true, vr, tok0, t1, a.scale_log2, vt, lane);
+        for (; tok0 < t1; tok0 += step) {
+            size_t n0, n1;
+            chunk_off(tok0 + step, n0, n1);
+            uint4 kn[2][4], vn[2][4];
+            const bool more = tok0 + step < t1;
+            if (more) {
+                load_k_chunk(a.kc + n0, a.kc + n1, lane, kn);
+                load_v_chunk(a.vc + n0, a.vc + n1, lane, vn);
+            }
+            f32x4 sc[2];
+            const float cmax = chunk_scores(kr, qop, tok0, t1, lane, sc);
+            chunk_update(st, sc, cmax * a.scale_log2, true, vr, tok0, t1, a.scale_log2, vt, lane);
+            if (more) {
+#pragma unroll
+                for (int pg = 0; pg < 2; ++pg)
+#pragma unroll
+                    for (int s4 = 0; s4 < 4; ++s4) {
+                        kr[pg][s4] = kn[pg][s4];
+                        vr[pg][s4] = vn[pg][s4];
+                    }
+            }
+        }
     }
     const size_t row0 = (size_t)b * a.Hq + (size_t)g * a.G;
     merge_waves<kSplitWaves>(st, smem, a.G, [&](int h, int d, float o, float lse) {
@@ -353,7 +382,7 @@ __global__ __launch_bounds__(64 * kSeqWaves) void decode_seq_kernel(SeqArgs a)
 {
     __shared__ int row_slot;
     const int g = blockIdx.x, b = lpt_row(a.seq_lens, gridDim.y, blockIdx.y, &row_slot);
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int n = lane & 15, j = lane >> 4;
     const int L = a.seq_lens[b];
     const int ntiles = (L + kSkipTile - 1) / kSkipTile;
