@@ -220,7 +220,9 @@ void prefill_bf16_kernel(PrefillArgs a)
             const bool raise = m_tile > m + kRescaleSlack;
             if (__any(raise)) {
                 const float m_new = raise ? m_tile : m;
-                const float alpha = exp2_fast(m - m_new); // m = -inf -> 0 (acc and l are still 0)
+                // raising from m = -inf gives 0 (acc and l are still 0); rows that do not raise keep their
+                // state (also rows that have seen no key yet, whose m - m_new would be -inf - -inf)
+                const float alpha = raise ? exp2_fast(m - m_new) : 1.f;
                 m = m_new;
                 l *= alpha;
 #pragma unroll

@@ -233,7 +233,9 @@ __device__ __forceinline__ void iteration(int t, const IterCtx &c, const Loader 
     // (a)
     if (__any(raise)) {
         const float m_new = raise ? tm : wv.m;
-        const float alpha = exp2_fast(wv.m - m_new); // m = -inf -> 0 (acc and l still 0)
+        // raising from m = -inf gives 0 (acc and l are still 0); rows that do not raise keep their state
+        // (also rows that have seen no key yet, whose m - m_new would be -inf - -inf)
+        const float alpha = raise ? exp2_fast(wv.m - m_new) : 1.f;
         wv.m = m_new;
         wv.l *= alpha;
 #pragma unroll

@@ -102,6 +102,49 @@ def test_prefill_bf16_cross_lengths_and_empty_keys():
         assert np.all(_np(o)[75:108] == 0)  # the sequence with no keys
 
 
+@pytest.mark.parametrize("D", [128, 64])
+@pytest.mark.parametrize("thr", [0.0, 0.1])
+def test_prefill_bf16_causal_more_queries_than_keys(D, thr):
+    # bottom-right causal with Lq > Lk: the first Lq - Lk rows see no key while later rows of the same
+    # 32-row block do; those rows must come out as o = 0, lse = -inf (no NaN from an empty running max)
+    Hq, Hkv = 4, 2
+    lq, lk = [70, 100, 45], [40, 3, 45]
+    g = torch.Generator(device=DEV).manual_seed(8)
+    q = torch.randn(sum(lq), Hq, D, generator=g, device=DEV).bfloat16()
+    k = torch.randn(sum(lk), Hkv, D, generator=g, device=DEV).bfloat16()
+    v = torch.randn(sum(lk), Hkv, D, generator=g, device=DEV).bfloat16()
+    cq = torch.tensor([0] + list(np.cumsum(lq)), dtype=torch.int32, device=DEV)
+    ck = torch.tensor([0] + list(np.cumsum(lk)), dtype=torch.int32, device=DEV)
+    o, lse, smap = attn.attn_prefill_varlen(q, k, v, cq, ck, max(lq), max(lk), causal=True, skip_threshold=thr,
+                                            return_lse=True, return_skip_map=True)
+    torch.cuda.synchronize()
+    on, ln = _np(o), _np(lse)
+    assert np.isfinite(on).all()
+    g_map = smap.cpu().numpy()
+    _, _, om = oracle.prefill(q.cpu(), k.cpu(), v.cpu(), cq.cpu(), ck.cpu(), Hq, Hkv, 1 / math.sqrt(D), True,
+                              mode="skip", thr=thr, stride=g_map.shape[-1])
+    _check_map(g_map, om)
+    od, ld, _ = oracle.prefill(q.cpu(), k.cpu(), v.cpu(), cq.cpu(), ck.cpu(), Hq, Hkv, 1 / math.sqrt(D), True,
+                               mode="skip", replay=np.where(g_map == 2, 0, g_map).reshape(-1, g_map.shape[-1]),
+                               stride=g_map.shape[-1])
+    assert np.max(np.abs(on - od)) <= BF16_TOL
+    fin = np.isfinite(ld)
+    assert not fin.all(), "some rows should see no key"
+    assert np.array_equal(fin, np.isfinite(ln))
+    assert np.max(np.abs(ln[fin] - ld[fin])) <= 1e-3
+    assert np.all(on[~fin] == 0)
+    if thr == 0.0:
+        # without a skip map the dense path runs (the D = 128 fast kernel for D = 128)
+        o2, l2, _ = attn.attn_prefill_varlen(q, k, v, cq, ck, max(lq), max(lk), causal=True, return_lse=True)
+        torch.cuda.synchronize()
+        o2n, l2n = _np(o2), _np(l2)
+        assert np.isfinite(o2n).all()
+        assert np.max(np.abs(o2n - od)) <= BF16_TOL
+        assert np.array_equal(fin, np.isfinite(l2n))
+        assert np.max(np.abs(l2n[fin] - ld[fin])) <= 1e-3
+        assert np.all(o2n[~fin] == 0)
+
+
 def test_prefill_bf16_skip_replay():
     lens = [300, 517, 64]
     x = W.varlen_prefill(seed=41, device=DEV, lengths=lens, Hq=4, Hkv=1, D=128)
