@@ -245,6 +245,14 @@ def main():
     cpu = None
     if not args.no_cpu_baseline and "prefill" in only:
         cpu = _cpu_baseline(work["prefill"])
+    if not args.no_cpu_baseline:
+        # the oracle on a bounded sample of every other workload too (a baseline only, never the target)
+        if "decode" in out:
+            out["decode"]["cpu_oracle"] = _cpu_decode(work["decode"], "dense", 0.0)
+        if "skip" in out:
+            out["skip"]["cpu_oracle_thr0.1"] = _cpu_decode(work["skip"], "skip", 0.1)
+        if "smallseq" in out:
+            out["smallseq"]["cpu_oracle"] = _cpu_smallseq(work["smallseq"])
 
     headline = out.get("prefill", {}).get("tflops")
     line = {
@@ -273,12 +281,55 @@ def main():
     print(json.dumps(line), flush=True)
 
 
+def _threads():
+    return int(os.environ.get("OMP_NUM_THREADS") or os.cpu_count() or 1)
+
+
+def _cpu_decode(d, mode, thr):
+    """The fp64 oracle on the eight longest batch rows of a paged-decode workload, all heads, in GB/s of
+    KV read (dense accounting).  Only the pages of those rows are copied to the host."""
+    import numpy as np
+    import torch
+
+    import oracle
+    L = d.lens.numpy()
+    bs = [int(b) for b in np.argsort(-L)[:8]]
+    bt = d.block_table[bs]
+    used = torch.unique(bt[bt >= 0])
+    bt_h = torch.full_like(bt, -1)
+    m = bt >= 0
+    bt_h[m] = torch.searchsorted(used, bt[m]).to(torch.int32)
+    kc, vc = d.k_cache[used].cpu(), d.v_cache[used].cpu()
+    q, sl = d.q[bs].cpu(), d.seq_lens[bs].cpu()
+    t0 = time.perf_counter()
+    oracle.decode(q, kc, vc, bt_h.cpu(), sl, d.scale, mode=mode, thr=thr, tile=32)
+    dt = time.perf_counter() - t0
+    kv = 4.0 * d.Hkv * d.D * float(sl.sum())
+    return {"value": kv / dt / 1e9, "unit": "GB/s", "cores": _threads(), "kind": "oracle",
+            "sample": f"the 8 longest batch rows (L = {[int(L[b]) for b in bs]}), all {d.Hq} heads, mode {mode}"
+                      f"{' thr ' + str(thr) if mode == 'skip' else ''}: {kv / 1e9:.2f} GB of KV in {dt:.2f} s"}
+
+
+def _cpu_smallseq(c):
+    """The fp64 oracle on the first 4096 sequences of the small-seq workload, all heads, in GB/s of KV."""
+    import oracle
+    n = 4096
+    T = int(c.cu_kv[n])
+    q, k, v, cu = c.q[:n].cpu(), c.k[:T].cpu(), c.v[:T].cpu(), c.cu_kv[:n + 1].cpu()
+    t0 = time.perf_counter()
+    oracle.smallseq(q, k, v, cu, c.max_s, c.scale)
+    dt = time.perf_counter() - t0
+    kv = 4.0 * c.H * c.D * T
+    return {"value": kv / dt / 1e9, "unit": "GB/s", "cores": _threads(), "kind": "oracle",
+            "sample": f"the first {n} sequences ({T} keys), all {c.H} heads: {kv / 1e9:.3f} GB of KV in {dt:.2f} s"}
+
+
 def _cpu_baseline(x):
     """The fp64 oracle on a bounded sample of the prefill workload, on this host's cores."""
     import numpy as np
 
     import oracle
-    threads = int(os.environ.get("OMP_NUM_THREADS") or os.cpu_count() or 1)
+    threads = _threads()
     q, k, v = x.q.cpu(), x.k.cpu(), x.v.cpu()
     cu = x.cu_q.cpu()
     L = x.lens.numpy()
