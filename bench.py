@@ -169,6 +169,8 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
+    achievable = _achievable(torch, dev)
+
     out = {}
     rooflines = []
     if "prefill" in only:
@@ -277,8 +279,46 @@ def main():
         "cpu_baseline": cpu,
         "kernels": out,
         "rooflines": rooflines,
+        "achievable_context": achievable,
     }
     print(json.dumps(line), flush=True)
+
+
+def _achievable(torch, dev):
+    """What plain library kernels reach on this GPU in the same session (context for the fractions of
+    the published peaks): a 1 GiB device copy (HBM read + write) and a large bf16 GEMM (hipBLASLt)."""
+    res = {}
+    src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(10):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / 10
+    res["copy_1GiB_GBps"] = 2.0 * (1 << 30) / (ms * 1e-3) / 1e9
+    del src, dst
+    n = 8192
+    a = torch.randn(n, n, device=dev, dtype=torch.bfloat16)
+    b = torch.randn(n, n, device=dev, dtype=torch.bfloat16)
+    for _ in range(3):
+        c = a @ b
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(10):
+        c = a @ b
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / 10
+    res["gemm_bf16_8192_TFLOPs"] = 2.0 * n ** 3 / (ms * 1e-3) / 1e12
+    del a, b, c
+    torch.cuda.empty_cache()
+    return res
 
 
 def _threads():
