@@ -38,7 +38,8 @@ def _parse():
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--seed", type=int, default=0)
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--only", default="", help="comma list of prefill,decode,skip,smallseq (profiling runs)")
+    p.add_argument("--only", default="",
+                   help="comma list of prefill,prefill_skip,decode,skip,smallseq (profiling runs)")
     p.add_argument("--calib-copy", action="store_true",
                    help="also run one plain 1 GiB device-to-device copy (scales HBM byte counters)")
     p.add_argument("--summarize-profiles", metavar="DIR", default="",
@@ -89,13 +90,16 @@ def main():
     import paged_skip_softmax_amd as attn
     from paged_skip_softmax_amd import workloads as W
 
-    only = set(args.only.split(",")) if args.only else {"prefill", "decode", "skip", "smallseq"}
+    only = (set(args.only.split(",")) if args.only
+            else {"prefill", "prefill_skip", "decode", "skip", "smallseq"})
     dev = "cuda:0"
     torch.cuda.set_device(0)
     t_gen = time.time()
     work = {}
     if "prefill" in only:
         work["prefill"] = W.varlen_prefill(seed=1001 + args.seed, device=dev)
+    if "prefill_skip" in only:
+        work["prefill_skip"] = W.varlen_prefill_hot(seed=1001 + args.seed, device=dev)
     if "decode" in only:
         work["decode"] = W.paged_decode(seed=1002 + args.seed, device=dev)
     if "skip" in only:
@@ -111,6 +115,12 @@ def main():
         o_pf = torch.empty_like(x.q)
         calls["prefill"] = lambda: attn.attn_prefill_varlen(x.q, x.k, x.v, x.cu_q, x.cu_k, x.max_q, x.max_k,
                                                             causal=True, out=o_pf)
+    if "prefill_skip" in only:
+        xh = work["prefill_skip"]
+        o_ph = torch.empty_like(xh.q)
+        for thr in (0.0, 0.01, 0.1):
+            calls[f"prefill_skip_{thr}"] = (lambda thr=thr: attn.attn_prefill_varlen(
+                xh.q, xh.k, xh.v, xh.cu_q, xh.cu_k, xh.max_q, xh.max_k, causal=True, skip_threshold=thr, out=o_ph))
     if "decode" in only:
         d = work["decode"]
         ws = torch.empty(attn.attn_decode_paged_workspace_size(d.B, d.Hq, d.D, 32), dtype=torch.uint8, device=dev)
@@ -182,6 +192,27 @@ def main():
         rooflines.append({"kernel": "prefill_d128_kernel", "bound": "mfma", "achieved": tflops,
                           "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": tflops / PEAK_BF16_TFLOPS,
                           "traffic": _traffic_from_profiles("prefill_d128_kernel"), "ms": ms["prefill"]})
+    if "prefill_skip" in only:
+        xh = work["prefill_skip"]
+        L = xh.lens.double()
+        flops = 4.0 * 128 * 32 * float((L * (L + 1) / 2).sum())
+        res = {}
+        for thr in (0.0, 0.01, 0.1):
+            t = ms[f"prefill_skip_{thr}"]
+            ent = {"ms": t, "ms_min": ms_min[f"prefill_skip_{thr}"], "dense_equiv_tflops": flops / (t * 1e-3) / 1e12}
+            if thr > 0:
+                _, _, smap = attn.attn_prefill_varlen(xh.q, xh.k, xh.v, xh.cu_q, xh.cu_k, xh.max_q, xh.max_k,
+                                                      causal=True, skip_threshold=thr, return_skip_map=True)
+                torch.cuda.synchronize()
+                vis = smap != 2
+                frac = float((smap == 1).sum()) / float(vis.sum())
+                del smap
+                ent["row_subtile_skip_frac"] = frac
+                # P.V is half of the MFMA work; the exponentials of skipped tiles are still computed
+                ent["ideal_speedup_pv_only"] = 1.0 / (1.0 - 0.5 * frac)
+                ent["speedup_vs_dense"] = ms["prefill_skip_0.0"] / t
+            res[str(thr)] = ent
+        out["prefill_skip"] = res
     if "decode" in only:
         d = work["decode"]
         kv = 4.0 * d.Hkv * d.D * float(d.lens.sum())
@@ -271,7 +302,8 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": "varlen causal prefill bf16: 16 seqs, L~U[256,4096] THD, Hq=32, Hkv=8, D=128",
-                   "step_also_runs": ["paged decode split-K B=64 L~U[1024,32768] page 16, 32x128-key splits",
+                   "step_also_runs": ["the same prefill shapes with hot keys, skip-softmax thr {0,0.01,0.1}",
+                                      "paged decode split-K B=64 L~U[1024,32768] page 16, 32x128-key splits",
                                       "sequential skip decode thr {0,0.01,0.1} on hot keys",
                                       "small-seq cross B=30720 s_kv in {2..16} H=16 D=128"],
                    "seed": args.seed},

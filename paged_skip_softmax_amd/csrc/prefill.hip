@@ -383,12 +383,7 @@ hipError_t launch_prefill(const PrefillArgs &a, bool bf16, int D, hipStream_t st
     if (bf16) {
         dim3 grid(a.Hq, a.B, (a.max_q + kBM - 1) / kBM), block(64 * kPrefWaves);
         if (D == 128) {
-            if (!skip)
-                return launch_prefill_d128(a, stream);
-            if (skip)
-                hipLaunchKernelGGL((prefill_bf16_kernel<128, true>), grid, block, 0, stream, a);
-            else
-                hipLaunchKernelGGL((prefill_bf16_kernel<128, false>), grid, block, 0, stream, a);
+            return launch_prefill_d128(a, stream);
         } else if (D == 64) {
             if (skip)
                 hipLaunchKernelGGL((prefill_bf16_kernel<64, true>), grid, block, 0, stream, a);

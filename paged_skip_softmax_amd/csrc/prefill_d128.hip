@@ -147,7 +147,25 @@ struct Wave {
     uint32_t va[2][D / 32];    // V transposed-read offsets within a tile ([key half][d block])
 };
 
-template <int ST>
+// LDS operand offsets.  The dense kernel keeps all of them in registers; the skip-softmax kernel, which
+// needs registers for its decisions, derives them from the first with one XOR per read.
+// (The base offset is passed through an empty asm so that the compiler cannot hoist the XORs out of the
+// loop into eight live registers again.)
+__device__ __forceinline__ uint32_t opaque(uint32_t v)
+{
+    asm volatile("" : "+v"(v));
+    return v;
+}
+template <bool COMPACT> __device__ __forceinline__ uint32_t k_off(const Wave &wv, int s)
+{
+    return COMPACT ? (opaque(wv.ka[0]) ^ (32 * s)) : wv.ka[s];
+}
+template <bool COMPACT> __device__ __forceinline__ uint32_t v_off(const Wave &wv, int hf, int db)
+{
+    return COMPACT ? (opaque(wv.va[hf][0]) ^ (64 * db)) : wv.va[hf][db];
+}
+
+template <int ST, bool COMPACT>
 __device__ __forceinline__ void qk_tile(const Wave &wv, f32x16 sc[2])
 {
     const char *kt = reinterpret_cast<const char *>(kbuf<ST>());
@@ -158,7 +176,7 @@ __device__ __forceinline__ void qk_tile(const Wave &wv, f32x16 sc[2])
             sc[kk][i] = 0.f;
 #pragma unroll
         for (int s = 0; s < D / 16; ++s)
-            sc[kk] = mfma32(as_bf16x8(ld16(kt + kk * 32 * 256 + wv.ka[s])), wv.qop[s], sc[kk]);
+            sc[kk] = mfma32(as_bf16x8(ld16(kt + kk * 32 * 256 + k_off<COMPACT>(wv, s))), wv.qop[s], sc[kk]);
     }
 }
 
@@ -186,20 +204,52 @@ struct IterCtx {
     bool causal;
     int first_row_w, diag, kend_row, J;
     float scale_log2;
+    float log2_thr;  // log2(threshold), -inf when skipping is off
+    uint8_t *maprow; // this lane's skip-map row (lanes J = 0 of rows in range), or null
+    int map_stride;
 };
 
-// Row max of a masked score tile in log2 units, and whether it raises the running max by more than the
-// slack (then the O and l rescale is due before the tile's exponentials).
-__device__ __forceinline__ void tile_max(const f32x16 sc[2], float scale_log2, Wave &wv, float &tm, bool &raise)
+// Skip-softmax state of the lane's row: the exact running max (log2 units) and which 32-key halves of
+// the current tile are kept.  A skipped half never raises the running max (threshold <= 1), so the max
+// before any half is the max over all earlier halves, skipped or not: the decisions below are those of
+// the sequential definition.
+struct SkipState {
+    float m_true;
+    bool keep[2];
+};
+
+// Statistics of tile t from the lane's partial maxima t0, t1 of its two 32-key halves: the row max
+// tm of the kept halves (log2 units) and whether it raises the exponent offset by more than the slack
+// (then the O and l rescale is due before the tile's exponentials).  With SKIP, first the two skip
+// decisions of the row: a visited half is skipped when the running max exists and
+// tmax_half - running max < log2(threshold); the skip map gets 0 (kept), 1 (skipped) or 2 (no visible
+// key).
+template <bool SKIP>
+__device__ __forceinline__ void tile_stats(float t0, float t1, int t, const IterCtx &c, const Wave &wv,
+                                           SkipState &ss, float &tm, bool &raise)
 {
-    float t0 = sc[0][0], t1 = sc[1][0];
-#pragma unroll
-    for (int i = 1; i < 16; ++i) {
-        t0 = fmaxf(t0, sc[0][i]);
-        t1 = fmaxf(t1, sc[1][i]);
+    const float sl = c.scale_log2;
+    if (!SKIP) {
+        tm = fmaxf(t0, t1);
+        tm = fmaxf(tm, __shfl_xor(tm, 32)) * sl;
+    } else {
+        const float h0 = fmaxf(t0, __shfl_xor(t0, 32)) * sl;
+        const float h1 = fmaxf(t1, __shfl_xor(t1, 32)) * sl;
+        const int kb = t * kBN;
+        const bool vis0 = kb < c.kend_row, vis1 = kb + 32 < c.kend_row;
+        const bool skip0 = vis0 && ss.m_true != kNegInf && h0 - ss.m_true < c.log2_thr;
+        const float m1 = vis0 ? fmaxf(ss.m_true, h0) : ss.m_true;
+        const bool skip1 = vis1 && m1 != kNegInf && h1 - m1 < c.log2_thr;
+        ss.m_true = vis1 ? fmaxf(m1, h1) : m1;
+        ss.keep[0] = vis0 && !skip0;
+        ss.keep[1] = vis1 && !skip1;
+        if (c.maprow && t < c.niter) {
+            c.maprow[2 * t] = vis0 ? (skip0 ? 1 : 0) : 2;
+            if (2 * t + 1 < c.map_stride)
+                c.maprow[2 * t + 1] = vis1 ? (skip1 ? 1 : 0) : 2;
+        }
+        tm = fmaxf(ss.keep[0] ? h0 : kNegInf, ss.keep[1] ? h1 : kNegInf);
     }
-    tm = fmaxf(t0, t1);
-    tm = fmaxf(tm, __shfl_xor(tm, 32)) * scale_log2;
     raise = tm > wv.m + kSlack;
 }
 
@@ -218,9 +268,9 @@ __device__ __forceinline__ bool needs_mask(int t, const IterCtx &c)
 //   (c) mask tile t+1 where it crosses the diagonal or the sequence end;
 //   (d) P.V of tile t, with the row max of tile t+1 placed between its MFMAs.
 // On the last tile, (b)-(d) compute scores from a stale K stage that are never used.
-template <int ST>
+template <int ST, bool SKIP>
 __device__ __forceinline__ void iteration(int t, const IterCtx &c, const Loader &ld, Wave &wv, f32x16 sc[2],
-                                          float &tm, bool &raise)
+                                          float &tm, bool &raise, SkipState &ss)
 {
     wait_vmcnt<0>();
     barrier();
@@ -255,17 +305,29 @@ __device__ __forceinline__ void iteration(int t, const IterCtx &c, const Loader 
     uint32_t pk[2][8];
     {
         const char *kt = reinterpret_cast<const char *>(kbuf<(P + 1) % kStages>());
-        auto kop = [&](int step) { return ld16(kt + (step & 1) * 32 * 256 + wv.ka[step >> 1]); };
+        auto kop = [&](int step) { return ld16(kt + (step & 1) * 32 * 256 + k_off<SKIP>(wv, step >> 1)); };
         uint4 k0 = kop(0), k1 = kop(1);
 #pragma unroll
         for (int step = 0; step < 16; ++step) {
             const uint4 k2 = step + 2 < 16 ? kop(step + 2) : k0;
             nx[step & 1] = mfma32(as_bf16x8(k0), wv.qop[step >> 1], nx[step & 1]);
             const int kk = step >> 3, i = 2 * (step & 7);
-            const float p0 = exp2_fast(fmaf(sc[kk][i], sl, -m_use));
-            const float p1 = exp2_fast(fmaf(sc[kk][i + 1], sl, -m_use));
-            wv.l += p0 + p1;
-            pk[kk][i >> 1] = pack_bf16x2(p0, p1);
+            if (!SKIP) {
+                const float p0 = exp2_fast(fmaf(sc[kk][i], sl, -m_use));
+                const float p1 = exp2_fast(fmaf(sc[kk][i + 1], sl, -m_use));
+                wv.l += p0 + p1;
+                pk[kk][i >> 1] = pack_bf16x2(p0, p1);
+            } else {
+                // a skipped half adds nothing and is not rescaled; when every row of the wave skips it,
+                // the exponentials are branched over
+                float p0 = 0.f, p1 = 0.f;
+                if (ss.keep[kk]) {
+                    p0 = exp2_fast(fmaf(sc[kk][i], sl, -m_use));
+                    p1 = exp2_fast(fmaf(sc[kk][i + 1], sl, -m_use));
+                    wv.l += p0 + p1;
+                }
+                pk[kk][i >> 1] = pack_bf16x2(p0, p1);
+            }
             anchor(pk[kk][i >> 1]);
             sched_fence();
             k0 = k1;
@@ -284,8 +346,8 @@ __device__ __forceinline__ void iteration(int t, const IterCtx &c, const Loader 
         const char *vt = reinterpret_cast<const char *>(vbuf<P>());
         auto vop = [&](int step) {
             const char *vk = vt + (32 * (step >> 3) + 16 * ((step >> 2) & 1)) * 256;
-            const uint2 lo = lds_read_tr(vk + wv.va[0][step & 3]);
-            const uint2 hi = lds_read_tr(vk + wv.va[1][step & 3]);
+            const uint2 lo = lds_read_tr(vk + v_off<SKIP>(wv, 0, step & 3));
+            const uint2 hi = lds_read_tr(vk + v_off<SKIP>(wv, 1, step & 3));
             return make_uint4(lo.x, lo.y, hi.x, hi.y);
         };
         uint4 v0 = vop(0), v1 = vop(1);
@@ -307,13 +369,12 @@ __device__ __forceinline__ void iteration(int t, const IterCtx &c, const Loader 
             v1 = v2;
         }
     }
-    tm = fmaxf(t0, t1);
-    tm = fmaxf(tm, __shfl_xor(tm, 32)) * sl;
-    raise = tm > wv.m + kSlack;
+    tile_stats<SKIP>(t0, t1, t + 1, c, wv, ss, tm, raise);
     sc[0] = nx[0];
     sc[1] = nx[1];
 }
 
+template <bool SKIP>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void prefill_d128_kernel(PrefillArgs a, int NH, int RB, int nqt, int nunits)
 {
@@ -418,10 +479,20 @@ void prefill_d128_kernel(PrefillArgs a, int NH, int RB, int nqt, int nunits)
         }
     }
 
+    // skip map: the row's entries past the workgroup's last tile are "not visited" up front; the others
+    // are written tile by tile
+    uint8_t *maprow = nullptr;
+    if (SKIP && a.skip_map && row_ok && J == 0) {
+        maprow = a.skip_map + ((size_t)(q0 + qi) * a.Hq + h) * a.map_stride;
+        for (int e = 2 * niter; e < a.map_stride; ++e)
+            maprow[e] = 2;
+    }
+
     f32x16 sc[2];
     float tm = kNegInf;
     bool raise = false;
-    IterCtx c{niter, Lk, a.causal, first_row_w, diag, kend_row, J, a.scale_log2};
+    SkipState ss{kNegInf, {true, true}};
+    IterCtx c{niter, Lk, a.causal, first_row_w, diag, kend_row, J, a.scale_log2, a.log2_thr, maprow, a.map_stride};
     if (niter > 0) {
         // prologue: K(0), V(0), K(1) in flight; wait for K(0), then the masked scores of tile 0 and
         // their row max
@@ -435,15 +506,21 @@ void prefill_d128_kernel(PrefillArgs a, int NH, int RB, int nqt, int nunits)
             wait_vmcnt<L>();
         }
         barrier();
-        qk_tile<0>(wv, sc);
+        qk_tile<0, SKIP>(wv, sc);
         if (needs_mask(0, c))
             mask_tile(sc, kend_row, J);
-        tile_max(sc, a.scale_log2, wv, tm, raise);
+        float t0 = sc[0][0], t1 = sc[1][0];
+#pragma unroll
+        for (int i = 1; i < 16; ++i) {
+            t0 = fmaxf(t0, sc[0][i]);
+            t1 = fmaxf(t1, sc[1][i]);
+        }
+        tile_stats<SKIP>(t0, t1, 0, c, wv, ss, tm, raise);
     }
     for (int t = 0; t < niter; t += kStages) {
-        iteration<0>(t, c, ld, wv, sc, tm, raise);
+        iteration<0, SKIP>(t, c, ld, wv, sc, tm, raise, ss);
         if (t + 1 < niter)
-            iteration<1>(t + 1, c, ld, wv, sc, tm, raise);
+            iteration<1, SKIP>(t + 1, c, ld, wv, sc, tm, raise, ss);
     }
 
     wv.l += __shfl_xor(wv.l, 32);
@@ -484,8 +561,13 @@ hipError_t launch_prefill_d128(const PrefillArgs &a, hipStream_t stream)
     const long blocks = (units + kXcds - 1) / kXcds * kXcds;
     if (blocks > 0x7fffffff)
         return hipErrorInvalidValue;
-    hipLaunchKernelGGL(prefill_d128_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, stream, a, NH, RB, nqt,
-                       (int)units);
+    const bool skip = a.log2_thr != kNegInf || a.skip_map != nullptr;
+    if (skip)
+        hipLaunchKernelGGL(prefill_d128_kernel<true>, dim3((unsigned)blocks), dim3(kThreads), 0, stream, a, NH, RB,
+                           nqt, (int)units);
+    else
+        hipLaunchKernelGGL(prefill_d128_kernel<false>, dim3((unsigned)blocks), dim3(kThreads), 0, stream, a, NH, RB,
+                           nqt, (int)units);
     return hipGetLastError();
 }
 

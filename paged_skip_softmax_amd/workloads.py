@@ -14,6 +14,8 @@ Workloads (sizes are the defaults; tests pass reduced sizes):
 
 * ``tiny_dense``        B=2, Hq=4, Hkv=2, D=64, S=128, fp32, cu_seqlens [0,128,256].
 * ``varlen_prefill``    16 sequences, lengths uniform in [256, 4096], THD packed, Hq=32, Hkv=8, D=128, bf16.
+* ``varlen_prefill_hot`` ``varlen_prefill`` plus an attention-sink run and 2 % hot 32-key runs per
+                        sequence aligned with the queries of each KV head's group (prefill skip-softmax).
 * ``paged_decode``      B=64, Hq=32, Hkv=8, D=128, context lengths uniform in [1024, 32768], 16-token pages
                         in a 140,000-page pool laid out [page, kv_head, slot, D]; the block table holds
                         consecutive slices of one seeded permutation of the pool, padded with -1.  Pages no
@@ -88,6 +90,42 @@ def varlen_prefill(seed=1001, device="cpu", nseq=16, lmin=256, lmax=4096, Hq=32,
     return SimpleNamespace(q=q, k=k, v=v, cu_q=cu.to(device), cu_k=cu.to(device), lens=lens,
                            B=len(lens), Hq=Hq, Hkv=Hkv, D=D, max_q=int(lens.max()), max_k=int(lens.max()),
                            scale=1.0 / math.sqrt(D), dtype=dtype)
+
+
+def varlen_prefill_hot(seed=1001, device="cpu", q_align=2.0, k_boost=24.0, hot_frac=0.02, hot_run=32, **kw):
+    """``varlen_prefill`` plus hot keys that most later key tiles fall far below (prefill skip-softmax).
+
+    Per sequence b and KV head g a seeded unit direction u is drawn; every query of the group's heads
+    gets ``q_align * u`` added and every key of the sequence's hot runs gets ``k_boost * u`` added (before
+    rounding to bf16), which lifts the hot logits by about q_align * k_boost / sqrt(D) (4.2 at the
+    defaults).  The hot runs are the first 32 keys of the sequence (an attention sink) plus
+    max(0, round(hot_frac * L / hot_run) - 1) further distinct 32-aligned full runs chosen by seed.  With
+    the same seed the lengths, V and the unperturbed parts of Q and K equal ``varlen_prefill``'s."""
+    x = varlen_prefill(seed=seed, device=device, **kw)
+    G = x.Hq // x.Hkv
+    g = _gen(seed, _S_HOT)
+    u = torch.randn(x.B, x.Hkv, x.D, generator=g, dtype=torch.float32)
+    u = (u / u.norm(dim=-1, keepdim=True)).to(device)
+    q = x.q.float()
+    k = x.k.float()
+    cu = x.cu_q.cpu().tolist()
+    hot_tiles = []
+    for b in range(x.B):
+        L = cu[b + 1] - cu[b]
+        q[cu[b]:cu[b + 1]].view(L, x.Hkv, G, x.D).add_(q_align * u[b][None, :, None, :])
+        nfull = L // hot_run
+        extra = max(0, int(round(hot_frac * L / hot_run)) - 1)
+        tiles = [0] if L > 0 else []
+        if nfull > 1 and extra > 0:
+            tiles += sorted((1 + torch.randperm(nfull - 1, generator=g)[:extra]).tolist())
+        hot_tiles.append(tiles)
+        for t in tiles:
+            j0, j1 = cu[b] + t * hot_run, min(cu[b] + (t + 1) * hot_run, cu[b + 1])
+            k[j0:j1].add_(k_boost * u[b][None, :, :])
+    x.q = q.to(x.dtype)
+    x.k = k.to(x.dtype)
+    x.hot_tiles = hot_tiles
+    return x
 
 
 def _page_table(lens, page, pool, max_pages, seed):

@@ -60,6 +60,44 @@ def test_full_varlen_prefill_sampled_rows():
 
 
 @pytest.fixture(scope="module")
+def prefill_hot():
+    return W.varlen_prefill_hot(seed=1001, device=DEV)     # the full prefill shapes plus hot keys
+
+
+@pytest.mark.parametrize("thr", [0.01, 0.1])
+def test_full_skip_prefill_sampled_rows(prefill_hot, thr):
+    x = prefill_hot
+    o, lse, smap = attn.attn_prefill_varlen(x.q, x.k, x.v, x.cu_q, x.cu_k, x.max_q, x.max_k, causal=True,
+                                            skip_threshold=thr, return_lse=True, return_skip_map=True)
+    # the same call without a map (the timed configuration) gives the same output
+    o2, _, _ = attn.attn_prefill_varlen(x.q, x.k, x.v, x.cu_q, x.cu_k, x.max_q, x.max_k, causal=True,
+                                        skip_threshold=thr)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o2)
+    on, ln, g = _np(o), _np(lse), smap.cpu().numpy()
+    assert np.isfinite(on).all()
+    cu = x.cu_q.cpu().tolist()
+    rng = np.random.default_rng(12)
+    toks = []
+    for b in range(x.B):
+        L = cu[b + 1] - cu[b]
+        pick = {0, 31, 32, 63, 64, L // 2, L - 1} | set(rng.choice(L, size=min(L, 24), replace=False).tolist())
+        toks += [cu[b] + i for i in sorted(p for p in pick if 0 <= p < L)]
+    rows = [(t, h) for t in toks for h in range(x.Hq)]
+    r = np.array(rows)
+    gm = g[r[:, 0], r[:, 1]]
+    qc, kc, vc = x.q.cpu(), x.k.cpu(), x.v.cpu()
+    _, _, om = oracle.prefill(qc, kc, vc, x.cu_q.cpu(), x.cu_k.cpu(), x.Hq, x.Hkv, x.scale, True, mode="skip",
+                              thr=thr, rows=rows, stride=g.shape[-1])
+    _check_map(gm, om)
+    assert (gm == 1).sum() / (gm != 2).sum() > 0.3, "the hot-key prefill input should make tiles skippable"
+    od, ld, _ = oracle.prefill(qc, kc, vc, x.cu_q.cpu(), x.cu_k.cpu(), x.Hq, x.Hkv, x.scale, True, mode="skip",
+                               rows=rows, replay=np.where(gm == 2, 0, gm), stride=g.shape[-1])
+    assert np.max(np.abs(on[r[:, 0], r[:, 1]] - od)) <= BF16_TOL
+    assert np.max(np.abs(ln[r[:, 0], r[:, 1]] - ld)) <= LSE_TOL
+
+
+@pytest.fixture(scope="module")
 def decode_host():
     """The full paged-decode workload (B 64, L in [1024, 32768], 140,000-page pool) and its host copy."""
     x = W.paged_decode(seed=1002, device=DEV)

@@ -363,3 +363,25 @@ def test_hot_key_workload_makes_most_tiles_skippable():
     visited = m != 2
     frac = (m == 1).sum() / visited.sum()
     assert frac > 0.5, frac
+
+
+def test_hot_key_prefill_workload():
+    # same seed: V and the unperturbed keys equal the plain workload's; the sink run is always hot; and
+    # the skip-softmax definition then skips most (row, tile) pairs at threshold 0.1 (parity unpinned
+    # beyond these properties: the generator is a reading of the pages)
+    lens = [1500, 2100]
+    x = W.varlen_prefill_hot(seed=9, lengths=lens, Hq=8, Hkv=2, D=128)
+    y = W.varlen_prefill(seed=9, lengths=lens, Hq=8, Hkv=2, D=128)
+    assert torch.equal(x.v, y.v)
+    assert all(t[0] == 0 for t in x.hot_tiles)
+    cu = y.cu_q.tolist()
+    hot = torch.zeros(cu[-1], dtype=torch.bool)
+    for b, tiles in enumerate(x.hot_tiles):
+        for t in tiles:
+            hot[cu[b] + 32 * t: cu[b] + 32 * (t + 1)] = True
+    assert torch.equal(x.k[~hot], y.k[~hot]) and not torch.equal(x.k[hot], y.k[hot])
+    rows = [(t, h) for t in range(0, cu[-1], 7) for h in range(8)]
+    _, _, m = oracle.prefill(x.q, x.k, x.v, x.cu_q, x.cu_k, 8, 2, x.scale, True, mode="skip", thr=0.1,
+                             rows=rows, stride=(max(lens) + 31) // 32)
+    visited = m != 2
+    assert (m == 1).sum() / visited.sum() > 0.5
