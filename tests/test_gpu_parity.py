@@ -81,6 +81,31 @@ def test_prefill_bf16_varlen_ragged(D, causal):
     assert np.max(np.abs(_np(lse) - ld)) <= 1e-3
 
 
+@pytest.mark.parametrize("Hq,Hkv", [(8, 8), (16, 2), (32, 2), (12, 3), (6, 2)])
+@pytest.mark.parametrize("thr", [0.0, 0.1])
+def test_prefill_bf16_gqa_groupings(Hq, Hkv, thr):
+    # group sizes 1, 8, 16 and non-powers of two (the workgroup takes the largest power of two dividing
+    # the group size as its number of heads)
+    lens = [77, 200, 33]
+    x = W.varlen_prefill(seed=35, device=DEV, lengths=lens, Hq=Hq, Hkv=Hkv, D=128)
+    o, lse, smap = attn.attn_prefill_varlen(x.q, x.k, x.v, x.cu_q, x.cu_k, x.max_q, x.max_k, causal=True,
+                                            skip_threshold=thr, return_lse=True, return_skip_map=thr > 0)
+    torch.cuda.synchronize()
+    if thr == 0:
+        od, ld, _ = oracle.prefill(x.q.cpu(), x.k.cpu(), x.v.cpu(), x.cu_q.cpu(), x.cu_k.cpu(), Hq, Hkv, x.scale,
+                                   True)
+    else:
+        g = smap.cpu().numpy()
+        _, _, om = oracle.prefill(x.q.cpu(), x.k.cpu(), x.v.cpu(), x.cu_q.cpu(), x.cu_k.cpu(), Hq, Hkv, x.scale,
+                                  True, mode="skip", thr=thr, stride=g.shape[-1])
+        _check_map(g, om)
+        od, ld, _ = oracle.prefill(x.q.cpu(), x.k.cpu(), x.v.cpu(), x.cu_q.cpu(), x.cu_k.cpu(), Hq, Hkv, x.scale,
+                                   True, mode="skip", replay=np.where(g == 2, 0, g).reshape(-1, g.shape[-1]),
+                                   stride=g.shape[-1])
+    assert np.max(np.abs(_np(o) - od)) <= BF16_TOL
+    assert np.max(np.abs(_np(lse) - ld)) <= 1e-3
+
+
 def test_prefill_bf16_cross_lengths_and_empty_keys():
     # Lq != Lk (bottom-right causal alignment) and a sequence with queries but no keys
     Hq, Hkv, D = 4, 4, 128
@@ -188,6 +213,22 @@ def _small_decode(hot=False, seed=51):
 def _decode_oracle(x, **kw):
     return oracle.decode(x.q.cpu(), x.k_cache.cpu(), x.v_cache.cpu(), x.block_table.cpu(), x.seq_lens.cpu(),
                          x.scale, **kw)
+
+
+@pytest.mark.parametrize("Hq,Hkv", [(8, 8), (16, 2), (32, 2), (12, 4)])
+@pytest.mark.parametrize("splits", [1, 32])
+def test_decode_gqa_groupings(Hq, Hkv, splits):
+    # group sizes 1, 8, 16 (the largest supported) and 3
+    lengths = [1, 33, 500, 1000]
+    x = W.paged_decode(seed=53, device=DEV, B=len(lengths), Hq=Hq, Hkv=Hkv, D=128, page=16, pool=300,
+                       lengths=lengths, lmax=1024)
+    o, lse, _ = attn.attn_decode_paged(x.q, x.k_cache, x.v_cache, x.block_table, x.seq_lens, num_splits=splits,
+                                       return_lse=True)
+    torch.cuda.synchronize()
+    od, ld, _ = _decode_oracle(x)
+    assert np.isfinite(_np(o)).all()
+    assert np.max(np.abs(_np(o) - od)) <= BF16_TOL
+    assert np.max(np.abs(_np(lse) - ld)) <= 1e-3
 
 
 @pytest.mark.parametrize("splits", [2, 7, 32, 64])
