@@ -189,9 +189,9 @@ def main():
         tflops = flops / (ms["prefill"] * 1e-3) / 1e12
         out["prefill"] = {"ms": ms["prefill"], "ms_min": ms_min["prefill"], "flop": flops, "tflops": tflops,
                           "frac_peak": tflops / PEAK_BF16_TFLOPS}
-        rooflines.append({"kernel": "prefill_d128_kernel", "bound": "mfma", "achieved": tflops,
+        rooflines.append({"kernel": "prefill_d128_kernel<false>", "bound": "mfma", "achieved": tflops,
                           "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": tflops / PEAK_BF16_TFLOPS,
-                          "traffic": _traffic_from_profiles("prefill_d128_kernel"), "ms": ms["prefill"]})
+                          "traffic": _traffic_from_profiles("prefill_d128_kernel<false>"), "ms": ms["prefill"]})
     if "prefill_skip" in only:
         xh = work["prefill_skip"]
         L = xh.lens.double()
@@ -423,9 +423,13 @@ def _cpu_baseline(x):
 # kernel -> (workload the bench runs it on, summary file stem, sources it is built from)
 _KSRC = ["paged_skip_softmax_amd/csrc/kcommon.h", "paged_skip_softmax_amd/csrc/launch.h"]
 PROFILED = {
-    "prefill_d128_kernel": ("varlen causal prefill bf16, 16 seqs L~U[256,4096], Hq=32, Hkv=8, D=128",
-                            "prefill_d128_kernel.varlen_causal_16seq_L256-4096_Hq32_Hkv8_D128",
-                            ["paged_skip_softmax_amd/csrc/prefill_d128.hip"] + _KSRC),
+    "prefill_d128_kernel<false>": ("varlen causal prefill bf16, 16 seqs L~U[256,4096], Hq=32, Hkv=8, D=128",
+                                   "prefill_d128_kernel.varlen_causal_16seq_L256-4096_Hq32_Hkv8_D128",
+                                   ["paged_skip_softmax_amd/csrc/prefill_d128.hip"] + _KSRC),
+    "prefill_d128_kernel<true>": ("skip-softmax prefill on the hot-key prefill input (same shapes), "
+                                  "threshold 0.01 and 0.1 in turn",
+                                  "prefill_d128_kernel_skip.varlen_causal_hot_16seq_thr0.01-0.1",
+                                  ["paged_skip_softmax_amd/csrc/prefill_d128.hip"] + _KSRC),
     "decode_split_kernel": ("paged decode B=64, L~U[1024,32768], page 16, 32 splits of 128-key tiles",
                             "decode_split_kernel.paged_decode_B64_L1k-32k_page16_32splits",
                             ["paged_skip_softmax_amd/csrc/decode.hip"] + _KSRC),
@@ -439,6 +443,13 @@ PROFILED = {
     "smallseq_kernel": ("small-seq cross-attention B=30720, s_kv in {2,4,6,8,12,16}, H=16, D=128",
                         "smallseq_kernel.smallseq_cross_B30720_H16_D128",
                         ["paged_skip_softmax_amd/csrc/smallseq.hip"] + _KSRC),
+}
+# kernels launched more than once per step: the role of each launch, in launch order (the first role
+# is the one the roofline and traffic.json refer to)
+ROLES = {
+    "prefill_d128_kernel<false>": ["varlen causal prefill", "hot-key prefill input, dense"],
+    "prefill_d128_kernel<true>": ["threshold 0.01", "threshold 0.1"],
+    "decode_seq_kernel": ["threshold 0", "threshold 0.01", "threshold 0.1"],
 }
 PROFILE_COMMANDS = {
     "trace": "rocprofv3 --kernel-trace --stats -f csv -d gpurun_out/prof_trace -o run -- "
@@ -523,9 +534,11 @@ def _summarize_profiles(base):
                          f"{float(r['Percentage']):.2f}% of GPU kernel time")
         d = np.array(durs[k], dtype=np.float64) / 1e3
         lines.append(f"kernel_trace.csv: {len(d)} dispatches, mean {d.mean():.2f} us, median {np.median(d):.2f} us")
-        if k == "decode_seq_kernel" and len(d) % 3 == 0:
-            for i, thr in enumerate(("0", "0.01", "0.1")):
-                lines.append(f"  threshold {thr}: mean {d[i::3].mean():.2f} us over {len(d[i::3])} dispatches")
+        roles = ROLES.get(k, [])
+        nr = len(roles)
+        if nr and len(d) % nr == 0:
+            for i, role in enumerate(roles):
+                lines.append(f"  {role}: mean {d[i::nr].mean():.2f} us over {len(d[i::nr])} dispatches")
         fk = fetch.get(k, [])
         wk = write.get(k, [])
         if fk and wk:
@@ -536,11 +549,11 @@ def _summarize_profiles(base):
                       f"calibration: the 1 GiB copy read FETCH_SIZE {c_fetch:.0f} KiB and WRITE_SIZE "
                       f"{c_write:.0f} KiB, factors {f_fetch:.4f} (fetch) and {f_write:.4f} (write)",
                       f"HBM traffic per launch (scaled): {byts / 1e6:.1f} MB"]
-            if k == "decode_seq_kernel" and len(fk) % 3 == 0 and len(wk) % 3 == 0:
-                for i, thr in enumerate(("0", "0.01", "0.1")):
-                    b_i = (np.mean(fk[i::3]) * f_fetch + np.mean(wk[i::3]) * f_write) * 1024.0
-                    lines.append(f"  threshold {thr}: {b_i / 1e6:.1f} MB per launch")
-                byts = (np.mean(fk[0::3]) * f_fetch + np.mean(wk[0::3]) * f_write) * 1024.0
+            if nr and len(fk) % nr == 0 and len(wk) % nr == 0:
+                for i, role in enumerate(roles):
+                    b_i = (np.mean(fk[i::nr]) * f_fetch + np.mean(wk[i::nr]) * f_write) * 1024.0
+                    lines.append(f"  {role}: {b_i / 1e6:.1f} MB per launch")
+                byts = (np.mean(fk[0::nr]) * f_fetch + np.mean(wk[0::nr]) * f_write) * 1024.0
             traffic[k] = {"bytes_per_launch": float(byts), "fetch_kib": fm, "write_kib": wm,
                           "fetch_factor": f_fetch, "write_factor": f_write, "sources": srcs,
                           "sources_sha256": _sources_digest(srcs), "summary": f"profiles/{stem}.txt"}
