@@ -38,7 +38,7 @@ constexpr int kD = 128;
 constexpr int kSplitTile = 128;
 constexpr int kSplitWaves = 4;
 constexpr int kSeqWaves = 8;
-constexpr int kVPitch = kD + 8;                   // LDS row pitch (bf16 elements, 272 B)
+constexpr int kVPitch = kD + 16;                  // LDS row pitch (bf16 elements, 288 B)
 constexpr int kVTile = 2 * kPage * kVPitch;       // one wave's V staging tile (elements)
 // s_waitcnt immediate that waits for LDS / scalar memory only (vmcnt and expcnt at their maxima; gfx9
 // layout: vmcnt [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8])
@@ -124,6 +124,16 @@ __device__ __forceinline__ void state_init(WaveState &st)
         st.acc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
 }
 
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+// 8-byte transposed LDS read (ds_read_b64_tr_b16): in each 16-lane group, lane i receives element i
+// of the 16 consecutive columns the group addresses, from each of the 4 rows it addresses.
+__device__ __forceinline__ uint2 lds_read_tr(const uint16_t *p)
+{
+    const i16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4 *)(p));
+    return __builtin_bit_cast(uint2, r);
+}
+
 // Folds one chunk into the state.  keep == false (per lane, i.e. per head) leaves that head's state
 // untouched: p = 0 and no rescale.  cmax_l2: chunk max in log2 units.  Keys at or past tend have their
 // V zeroed in LDS so that 0 * NaN never reaches the accumulator.  vt: this wave's LDS tile.
@@ -161,22 +171,17 @@ __device__ __forceinline__ void chunk_update(WaveState &st, const f32x4 sc[2], f
             st16(vt + (pg * kPage + key) * kVPitch + 8 * (lane & 15), v);
         }
     __builtin_amdgcn_wave_barrier();
-    bf16x8 pop;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        pop[i] = (__bf16)p[0][i];
-        pop[4 + i] = (__bf16)p[1][i];
-    }
+    const bf16x8 pop = as_bf16x8(make_uint4(pack_bf16x2(p[0][0], p[0][1]), pack_bf16x2(p[0][2], p[0][3]),
+                                            pack_bf16x2(p[1][0], p[1][1]), pack_bf16x2(p[1][2], p[1][3])));
+    // V^T operand by transposed reads: in lane group j, lane (n) addresses key 4 j + n / 4 (then 16 +
+    // 4 j + n / 4) and dims 16 db + 4 (n % 4) .. +3, and receives keys 4 j .. 4 j + 3 of dim 16 db + n
+    const uint16_t *v0 = vt + (4 * j + (n >> 2)) * kVPitch + 4 * (n & 3);
+    const uint16_t *v1 = v0 + kPage * kVPitch;
 #pragma unroll
     for (int db = 0; db < kD / 16; ++db) {
-        const int d = 16 * db + n;
-        bf16x8 va;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            va[i] = __builtin_bit_cast(__bf16, vt[(4 * j + i) * kVPitch + d]);
-            va[4 + i] = __builtin_bit_cast(__bf16, vt[(kPage + 4 * j + i) * kVPitch + d]);
-        }
-        st.acc[db] = mfma16(va, pop, st.acc[db]);
+        const uint2 lo = lds_read_tr(v0 + 16 * db);
+        const uint2 hi = lds_read_tr(v1 + 16 * db);
+        st.acc[db] = mfma16(as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y)), pop, st.acc[db]);
     }
     __builtin_amdgcn_wave_barrier();
 }
