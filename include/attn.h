@@ -66,7 +66,9 @@ typedef enum { ATTN_F32 = 0, ATTN_BF16 = 1 } attn_dtype_t;
  *   skip_threshold: see above; accumulation is fp32 and the P.V product is bf16 for bf16 inputs.
  *   lse: nullable fp32 [tq, Hq].  skip_map: nullable uint8 [tq, Hq, skip_map_stride] with
  *   skip_map_stride >= ceil(max_seqlen_k / 32); every entry of a row is written (2 past its visible keys).
- *   Supported: bf16 with D in {64, 128}; fp32 with D = 64.  B == 0 is a no-op.
+ *   Supported: bf16 with D in {64, 128}; fp32 with D = 64.  B == 0 is a no-op.  bf16 needs
+ *   max_seqlen_k * Hkv * D * 2 < 2^31 and, for D = 128 with a skip map, B * max_seqlen_q * Hq *
+ *   skip_map_stride < 2^32 (else ATTN_ERR_UNSUPPORTED).
  */
 attn_status_t attn_prefill_varlen(attn_dtype_t dtype, const void *q, const void *k, const void *v,
                                   const int32_t *cu_seqlens_q, const int32_t *cu_seqlens_k, int32_t B,

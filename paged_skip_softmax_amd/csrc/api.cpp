@@ -210,6 +210,10 @@ attn_status_t attn_prefill_varlen(attn_dtype_t dtype, const void *q, const void 
         return fail(ATTN_ERR_UNSUPPORTED, "attn_prefill_varlen: fp32 D = %d (built for 64)", D);
     if (dtype == ATTN_BF16 && (int64_t)max_seqlen_k * Hkv * D * 2 >= ((int64_t)1 << 31))
         return fail(ATTN_ERR_UNSUPPORTED, "attn_prefill_varlen: max_seqlen_k * Hkv * D * 2 must stay below 2^31 bytes");
+    if (dtype == ATTN_BF16 && D == 128 && skip_map &&
+        (uint64_t)B * (uint64_t)max_seqlen_q * (uint64_t)Hq * (uint64_t)skip_map_stride >= ((uint64_t)1 << 32))
+        return fail(ATTN_ERR_UNSUPPORTED, "attn_prefill_varlen: a skip map of B * max_seqlen_q * Hq * stride bytes must "
+                                          "stay below 2^32");
     if (B == 0 || max_seqlen_q == 0)
         return ok();
     if (!q || !k || !v || !cu_seqlens_q || !cu_seqlens_k || !o)

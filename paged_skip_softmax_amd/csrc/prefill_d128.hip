@@ -147,25 +147,7 @@ struct Wave {
     uint32_t va[2][D / 32];    // V transposed-read offsets within a tile ([key half][d block])
 };
 
-// LDS operand offsets.  The dense kernel keeps all of them in registers; the skip-softmax kernel, which
-// needs registers for its decisions, derives them from the first with one XOR per read.
-// (The base offset is passed through an empty asm so that the compiler cannot hoist the XORs out of the
-// loop into eight live registers again.)
-__device__ __forceinline__ uint32_t opaque(uint32_t v)
-{
-    asm volatile("" : "+v"(v));
-    return v;
-}
-template <bool COMPACT> __device__ __forceinline__ uint32_t k_off(const Wave &wv, int s)
-{
-    return COMPACT ? (opaque(wv.ka[0]) ^ (32 * s)) : wv.ka[s];
-}
-template <bool COMPACT> __device__ __forceinline__ uint32_t v_off(const Wave &wv, int hf, int db)
-{
-    return COMPACT ? (opaque(wv.va[hf][0]) ^ (64 * db)) : wv.va[hf][db];
-}
-
-template <int ST, bool COMPACT>
+template <int ST>
 __device__ __forceinline__ void qk_tile(const Wave &wv, f32x16 sc[2])
 {
     const char *kt = reinterpret_cast<const char *>(kbuf<ST>());
@@ -176,7 +158,7 @@ __device__ __forceinline__ void qk_tile(const Wave &wv, f32x16 sc[2])
             sc[kk][i] = 0.f;
 #pragma unroll
         for (int s = 0; s < D / 16; ++s)
-            sc[kk] = mfma32(as_bf16x8(ld16(kt + kk * 32 * 256 + k_off<COMPACT>(wv, s))), wv.qop[s], sc[kk]);
+            sc[kk] = mfma32(as_bf16x8(ld16(kt + kk * 32 * 256 + wv.ka[s])), wv.qop[s], sc[kk]);
     }
 }
 
@@ -205,7 +187,8 @@ struct IterCtx {
     int first_row_w, diag, kend_row, J;
     float scale_log2;
     float log2_thr;  // log2(threshold), -inf when skipping is off
-    uint8_t *maprow; // this lane's skip-map row (lanes J = 0 of rows in range), or null
+    uint8_t *map;      // skip map, or null
+    uint32_t map_row;  // byte offset of this lane's map row; ~0u for lanes that write none
     int map_stride;
 };
 
@@ -243,10 +226,11 @@ __device__ __forceinline__ void tile_stats(float t0, float t1, int t, const Iter
         ss.m_true = vis1 ? fmaxf(m1, h1) : m1;
         ss.keep[0] = vis0 && !skip0;
         ss.keep[1] = vis1 && !skip1;
-        if (c.maprow && t < c.niter) {
-            c.maprow[2 * t] = vis0 ? (skip0 ? 1 : 0) : 2;
+        if (c.map && c.map_row != ~0u && t < c.niter) {
+            uint8_t *mr = c.map + c.map_row;
+            mr[2 * t] = vis0 ? (skip0 ? 1 : 0) : 2;
             if (2 * t + 1 < c.map_stride)
-                c.maprow[2 * t + 1] = vis1 ? (skip1 ? 1 : 0) : 2;
+                mr[2 * t + 1] = vis1 ? (skip1 ? 1 : 0) : 2;
         }
         tm = fmaxf(ss.keep[0] ? h0 : kNegInf, ss.keep[1] ? h1 : kNegInf);
     }
@@ -305,7 +289,7 @@ __device__ __forceinline__ void iteration(int t, const IterCtx &c, const Loader 
     uint32_t pk[2][8];
     {
         const char *kt = reinterpret_cast<const char *>(kbuf<(P + 1) % kStages>());
-        auto kop = [&](int step) { return ld16(kt + (step & 1) * 32 * 256 + k_off<SKIP>(wv, step >> 1)); };
+        auto kop = [&](int step) { return ld16(kt + (step & 1) * 32 * 256 + wv.ka[step >> 1]); };
         uint4 k0 = kop(0), k1 = kop(1);
 #pragma unroll
         for (int step = 0; step < 16; ++step) {
@@ -346,8 +330,8 @@ __device__ __forceinline__ void iteration(int t, const IterCtx &c, const Loader 
         const char *vt = reinterpret_cast<const char *>(vbuf<P>());
         auto vop = [&](int step) {
             const char *vk = vt + (32 * (step >> 3) + 16 * ((step >> 2) & 1)) * 256;
-            const uint2 lo = lds_read_tr(vk + v_off<SKIP>(wv, 0, step & 3));
-            const uint2 hi = lds_read_tr(vk + v_off<SKIP>(wv, 1, step & 3));
+            const uint2 lo = lds_read_tr(vk + wv.va[0][step & 3]);
+            const uint2 hi = lds_read_tr(vk + wv.va[1][step & 3]);
             return make_uint4(lo.x, lo.y, hi.x, hi.y);
         };
         uint4 v0 = vop(0), v1 = vop(1);
@@ -482,8 +466,10 @@ void prefill_d128_kernel(PrefillArgs a, int NH, int RB, int nqt, int nunits)
     // skip map: the row's entries past the workgroup's last tile are "not visited" up front; the others
     // are written tile by tile
     uint8_t *maprow = nullptr;
+    uint32_t map_row = ~0u;
     if (SKIP && a.skip_map && row_ok && J == 0) {
-        maprow = a.skip_map + ((size_t)(q0 + qi) * a.Hq + h) * a.map_stride;
+        map_row = (uint32_t)(((size_t)(q0 + qi) * a.Hq + h) * a.map_stride);
+        maprow = a.skip_map + map_row;
         for (int e = 2 * niter; e < a.map_stride; ++e)
             maprow[e] = 2;
     }
@@ -492,7 +478,8 @@ void prefill_d128_kernel(PrefillArgs a, int NH, int RB, int nqt, int nunits)
     float tm = kNegInf;
     bool raise = false;
     SkipState ss{kNegInf, {true, true}};
-    IterCtx c{niter, Lk, a.causal, first_row_w, diag, kend_row, J, a.scale_log2, a.log2_thr, maprow, a.map_stride};
+    IterCtx c{niter, Lk, a.causal, first_row_w, diag, kend_row, J, a.scale_log2, a.log2_thr, SKIP ? a.skip_map : nullptr, map_row,
+              a.map_stride};
     if (niter > 0) {
         // prologue: K(0), V(0), K(1) in flight; wait for K(0), then the masked scores of tile 0 and
         // their row max
@@ -506,7 +493,7 @@ void prefill_d128_kernel(PrefillArgs a, int NH, int RB, int nqt, int nunits)
             wait_vmcnt<L>();
         }
         barrier();
-        qk_tile<0, SKIP>(wv, sc);
+        qk_tile<0>(wv, sc);
         if (needs_mask(0, c))
             mask_tile(sc, kend_row, J);
         float t0 = sc[0][0], t1 = sc[1][0];

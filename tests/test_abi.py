@@ -90,6 +90,10 @@ def test_prefill_validation(lib):
     assert _prefill(lib, k=None) == INVALID
     assert _prefill(lib, B=0) == _lib.ATTN_OK
     assert _prefill(lib, mq=0) == _lib.ATTN_OK
+    # size limits of the bf16 kernels: K/V rows of one sequence addressed in 31 bits, skip-map offsets in 32
+    assert _prefill(lib, mk=1 << 20, Hkv=8, Hq=8) == UNSUPPORTED
+    assert _prefill(lib, map=FAKE, B=4096, mq=4096, mk=4096, Hq=32, Hkv=8, stride=128) == UNSUPPORTED
+    assert b"2^32" in lib.attn_last_error_message()
 
 
 def _small(lib, **kw):
