@@ -452,13 +452,13 @@ ROLES = {
     "decode_seq_kernel": ["threshold 0", "threshold 0.01", "threshold 0.1"],
 }
 PROFILE_COMMANDS = {
-    "trace": "rocprofv3 --kernel-trace --stats -f csv -d gpurun_out/prof_trace -o run -- "
+    "trace": "rocprofv3 --kernel-trace --stats -f csv -d {out}/prof_trace -o run -- "
              "python3 bench.py --steps 5 --warmup 2 --no-cpu-baseline",
-    "fetch": "rocprofv3 --pmc FETCH_SIZE -f csv -d gpurun_out/prof_fetch -o run -- "
+    "fetch": "rocprofv3 --pmc FETCH_SIZE -f csv -d {out}/prof_fetch -o run -- "
              "python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline --calib-copy",
-    "write": "rocprofv3 --pmc WRITE_SIZE -f csv -d gpurun_out/prof_write -o run -- "
+    "write": "rocprofv3 --pmc WRITE_SIZE -f csv -d {out}/prof_write -o run -- "
              "python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline --calib-copy",
-    "summary": "python3 bench.py --summarize-profiles gpurun_out",
+    "summary": "python3 bench.py --summarize-profiles {out}",
 }
 
 
@@ -521,7 +521,7 @@ def _summarize_profiles(base):
     outdir = os.path.join(ROOT, "profiles")
     os.makedirs(outdir, exist_ok=True)
     traffic = {}
-    cmds = "\n".join(f"#   {k}: {v}" for k, v in PROFILE_COMMANDS.items())
+    cmds = "\n".join(f"#   {k}: {v.format(out=base)}" for k, v in PROFILE_COMMANDS.items())
     for k, (workload, stem, srcs) in PROFILED.items():
         if k not in durs:
             continue

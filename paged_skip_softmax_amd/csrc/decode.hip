@@ -24,7 +24,8 @@
 //   O^T[128 x 16] += V^T[128 x 32] . P^T[32 x 16]         8 MFMA 16x16x32
 // K goes straight from HBM into MFMA operand registers (each lane loads 16 B of one key row).  V is
 // loaded with fully coalesced 16-B loads (each wave instruction reads 1 KB of a slab), stored to a
-// wave-private LDS tile with a padded row pitch, and read back column-wise as the transposed operand.
+// wave-private LDS tile with a padded row pitch, and read back as the transposed operand with
+// ds_read_b64_tr_b16 (two 8-B reads per MFMA).
 // The key order inside the P.V contraction follows the S^T register layout (lane group j holds keys
 // 4j..4j+3 of each page), so P needs no shuffle between the two products.  Each wave keeps its own
 // online-softmax state; the states are merged through LDS at the end of the workgroup.

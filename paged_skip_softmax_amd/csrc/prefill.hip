@@ -2,6 +2,9 @@
 // variable-length batching, GQA, causal and non-causal; sequences packed THD with cu_seqlens), with
 // optional skip-softmax on 32-key tiles ("TensorRT-LLM: Skip Softmax Attention", Description).
 //
+// Head dim 128 in bf16 runs in prefill_d128.hip; this file holds the bf16 kernel for head dim 64 and
+// the fp32 kernel.
+//
 // bf16 kernel: one workgroup of 4 waves per (query head, sequence, 128-row query tile); each wave owns
 // 32 query rows and keeps Q^T in registers as the MFMA B operand for the whole loop.  Per 64-key
 // iteration every wave computes
@@ -11,12 +14,14 @@
 // K and V tiles are double-buffered in LDS: once a wave has issued the QK^T MFMAs of tile i, its
 // lanes load tile i+1 into registers (coalesced 16-B buffer loads; rows past the sequence read as 0)
 // and store it to the other buffer after the P.V product, so one barrier per iteration suffices and
-// the load latency hides behind the softmax and P.V of tile i.  K is read back as the A operand with 16-B reads; V, stored key-major as loaded, is read back
+// the load latency hides behind the softmax and P.V of tile i.  K is read back as the A operand with
+// 16-B reads; V, stored key-major as loaded, is read back
 // transposed with ds_read_b64_tr_b16 (lane j of each 16-lane group addresses key k0 + j/4, dims
 // 4(j%4)..+3, and receives dims of its own column for keys k0..k0+3).  The key order inside P.V follows
 // the S^T register layout, so P feeds the second product straight from registers.
-// The running max used for the exponentials is only raised when a row's max grows by more than 2^8
-// (log2 units), so the O and l rescale is rare; the result is the same softmax, with P <= 2^8.
+// The running max used for the exponentials is only raised when a row's max exceeds it by more than 8
+// (log2 units, a factor 2^8), so the O and l rescale is rare; the result is the same softmax, with
+// unnormalised weights P <= 2^8.
 // Query tiles are dispatched from the last (the most keys under a causal mask) to the first.  The two
 // 32-key halves of an iteration are exactly the skip tiles (tiles aligned to key 0); skip decisions use
 // the exact running max, and a tile skipped by every row of a wave costs no exp and no P.V.

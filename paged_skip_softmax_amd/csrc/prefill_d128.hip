@@ -1,6 +1,8 @@
-// Dense bf16 varlen prefill, head dim 128, for gfx950: the fast path of attn_prefill_varlen
+// bf16 varlen prefill, head dim 128, for gfx950: the D = 128 path of attn_prefill_varlen
 // ("Model-Optimizer: Add Triton unified attention kernel": variable-length batching, GQA, causal and
-// non-causal; sequences packed THD with cu_seqlens).
+// non-causal; sequences packed THD with cu_seqlens), dense (prefill_d128_kernel<false>) and with
+// skip-softmax on 32-key tiles ("TensorRT-LLM: Skip Softmax Attention", Description;
+// prefill_d128_kernel<true>).
 //
 // Work split.  A workgroup of 4 waves takes one query tile of one sequence for NH query heads of one
 // KV head's group times RB blocks of 32 query rows (NH * RB = 4, NH the largest power of two dividing
@@ -30,6 +32,12 @@
 // The running max used for the exponentials is only raised when a row's max exceeds it by more than 8
 // (log2 units, a factor 2^8), so the O and l rescale is rare; the result is the same softmax computed
 // with unnormalised weights P <= 2^8.
+//
+// Skip-softmax.  The two 32-key halves of a 64-key tile are the skip tiles (aligned to key 0).  Their
+// row maxima come out of the same interleaved max as the dense tile max; each row keeps its exact
+// running max beside the lazy one, and a half is skipped when the running max exists and its max is
+// below it by more than -log2(threshold).  A skipped half contributes nothing (its exponentials are
+// branched over when every row of the wave skips it) and never raises the running max.
 #include "kcommon.h"
 #include "launch.h"
 
