@@ -11,6 +11,8 @@ Modes: ``"dense"`` (the plain masked-softmax definition), ``"skip"`` (skip-softm
 tiles in ascending order with threshold ``thr``, optionally replaying a given skip map) and ``"split"``
 (split-K over ``tile``-key tiles in ``splits`` contiguous chunks merged by log-sum-exp).
 Skip-map codes: 0 processed, 1 skipped, 2 not visited.
+
+``prefill_backward`` gives the gradients (dq, dk, dv) of the dense varlen prefill for an output gradient.
 """
 from __future__ import annotations
 
@@ -45,7 +47,8 @@ def _load():
         lib.orc_prefill_rows.argtypes = [I, P, P, P, P, P, I, I, I, I, D, I, I, D, I, I, P, I, P, I, P, P, P]
         lib.orc_decode_rows.argtypes = [P, P, P, P, P, I, I, I, I, I, I, D, I, D, I, I, P, I, P, I, P, P, P]
         lib.orc_smallseq_rows.argtypes = [I, P, P, P, P, I, I, I, I, D, P, I, P, P]
-        for f in (lib.orc_prefill_rows, lib.orc_decode_rows, lib.orc_smallseq_rows):
+        lib.orc_prefill_bwd.argtypes = [I, P, P, P, P, P, P, I, I, I, I, D, I, P, P, P]
+        for f in (lib.orc_prefill_rows, lib.orc_decode_rows, lib.orc_smallseq_rows, lib.orc_prefill_bwd):
             f.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -179,3 +182,25 @@ def smallseq(q, k, v, cu_kv, max_s, scale, rows=None):
         o = o.reshape(B, H, D)
         w = w.reshape(B, H, 1, max(int(max_s), 0))
     return o, w
+
+
+def prefill_backward(q, k, v, dout, cu_q, cu_k, Hq, Hkv, scale, causal):
+    """Gradients (dq, dk, dv) of the dense varlen prefill for the output gradient ``dout`` (all rows)."""
+    qa, dt = _np(q)
+    ka, dk_ = _np(k)
+    va, dv_ = _np(v)
+    ga, dg = _np(dout)
+    assert dt == dk_ == dv_ == dg and dt in (0, 1)
+    cq, _ = _np(cu_q)
+    ck, _ = _np(cu_k)
+    B = len(cq) - 1
+    D = qa.shape[-1]
+    dq = np.zeros(qa.shape, dtype=np.float64)
+    dk = np.zeros(ka.shape, dtype=np.float64)
+    dv = np.zeros(va.shape, dtype=np.float64)
+    rc = _load().orc_prefill_bwd(dt, _ptr(qa), _ptr(ka), _ptr(va), _ptr(ga), _ptr(cq), _ptr(ck), B, Hq, Hkv, D,
+                                 float(scale), int(bool(causal)), _ptr(dq), _ptr(dk), _ptr(dv))
+    if rc != 0:
+        raise ValueError("oracle backward rejected its arguments")
+    return dq, dk, dv
+

@@ -27,6 +27,8 @@
  *               [s c, (s+1) c) and is attended densely to (o_s, lse_s); then
  *               lse = log sum_{finite} exp(lse_s) and o = sum_s exp(lse_s - lse) o_s.
  *
+ * Plus the backward of the dense prefill (orc_prefill_bwd, at the end of this file).
+ *
  * Inputs are read as the exact bytes the GPU reads (fp32, or bf16 widened exactly to fp64); all
  * arithmetic is in fp64.
  *
@@ -365,3 +367,94 @@ int orc_smallseq_rows(int dtype, const void *q, const void *k, const void *v, co
     }
     return bad ? -1 : 0;
 }
+
+/*
+ * Backward of the dense varlen prefill (the gradients of the masked-softmax definition above), for the
+ * next step the source pages list after the forward kernels ("Model-Optimizer: Add Triton unified
+ * attention kernel with HuggingFace integration", description: the kernel serves training as well).
+ * With p_j = exp(s_j - lse), s_j = scale q.k_j over the visible keys of a row and dO the output
+ * gradient:
+ *   dP_j = dO.v_j,  Dsum = sum_j p_j dP_j,  dS_j = p_j (dP_j - Dsum)
+ *   dq   = scale sum_j dS_j k_j
+ *   dk_j += scale dS_j q,  dv_j += p_j dO          (summed over every query row and query head of the group)
+ * Inputs as for orc_prefill_rows plus dout [tq, Hq, D] of the same dtype; outputs fp64 dq [tq, Hq, D],
+ * dk and dv [tk, Hkv, D] (fully written).  One task per (sequence, KV head), so no two tasks touch the
+ * same output.
+ */
+int orc_prefill_bwd(int dtype, const void *q, const void *k, const void *v, const void *dout, const int32_t *cu_q,
+                    const int32_t *cu_k, int B, int Hq, int Hkv, int D, double scale, int causal, double *dq,
+                    double *dk, double *dv)
+{
+    if (B < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv || D <= 0)
+        return -1;
+    const int G = Hq / Hkv;
+    const size_t tq = B ? (size_t)cu_q[B] : 0, tk = B ? (size_t)cu_k[B] : 0;
+    memset(dq, 0, sizeof(double) * tq * Hq * D);
+    memset(dk, 0, sizeof(double) * tk * Hkv * D);
+    memset(dv, 0, sizeof(double) * tk * Hkv * D);
+#pragma omp parallel for schedule(dynamic, 1) collapse(2)
+    for (int b = 0; b < B; ++b)
+        for (int g = 0; g < Hkv; ++g) {
+            const int Lq = cu_q[b + 1] - cu_q[b], Lk = cu_k[b + 1] - cu_k[b];
+            double *K = malloc(sizeof(double) * ((size_t)Lk * D + 1));
+            double *V = malloc(sizeof(double) * ((size_t)Lk * D + 1));
+            double *qd = malloc(sizeof(double) * D), *go = malloc(sizeof(double) * D);
+            double *s = malloc(sizeof(double) * ((size_t)Lk + 1)), *dp = malloc(sizeof(double) * ((size_t)Lk + 1));
+            for (int j = 0; j < Lk; ++j)
+                for (int d = 0; d < D; ++d) {
+                    const size_t src = ((size_t)(cu_k[b] + j) * Hkv + g) * D + d;
+                    K[(size_t)j * D + d] = widen(k, dtype, src);
+                    V[(size_t)j * D + d] = widen(v, dtype, src);
+                }
+            for (int hh = 0; hh < G; ++hh) {
+                const int h = g * G + hh;
+                for (int i = 0; i < Lq; ++i) {
+                    const size_t row = ((size_t)(cu_q[b] + i) * Hq + h) * D;
+                    int n = Lk;
+                    if (causal) {
+                        n = i + 1 + (Lk - Lq);
+                        n = n < 0 ? 0 : (n > Lk ? Lk : n);
+                    }
+                    if (n == 0)
+                        continue; /* a row with no key: o = 0 regardless of q, k, v */
+                    for (int d = 0; d < D; ++d) {
+                        qd[d] = widen(q, dtype, row + d);
+                        go[d] = widen(dout, dtype, row + d);
+                    }
+                    double m = -INFINITY;
+                    for (int j = 0; j < n; ++j) {
+                        s[j] = scale * dot(qd, K + (size_t)j * D, D);
+                        if (s[j] > m)
+                            m = s[j];
+                    }
+                    double sum = 0.0;
+                    for (int j = 0; j < n; ++j)
+                        sum += exp(s[j] - m);
+                    const double lse = m + log(sum);
+                    double dsum = 0.0;
+                    for (int j = 0; j < n; ++j) {
+                        s[j] = exp(s[j] - lse); /* s now holds p */
+                        dp[j] = dot(go, V + (size_t)j * D, D);
+                        dsum += s[j] * dp[j];
+                    }
+                    for (int j = 0; j < n; ++j) {
+                        const double ds = s[j] * (dp[j] - dsum);
+                        const size_t kv = ((size_t)(cu_k[b] + j) * Hkv + g) * D;
+                        for (int d = 0; d < D; ++d) {
+                            dq[row + d] += scale * ds * K[(size_t)j * D + d];
+                            dk[kv + d] += scale * ds * qd[d];
+                            dv[kv + d] += s[j] * go[d];
+                        }
+                    }
+                }
+            }
+            free(K);
+            free(V);
+            free(qd);
+            free(go);
+            free(s);
+            free(dp);
+        }
+    return 0;
+}
+

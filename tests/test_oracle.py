@@ -385,3 +385,77 @@ def test_hot_key_prefill_workload():
                              rows=rows, stride=(max(lens) + 31) // 32)
     visited = m != 2
     assert (m == 1).sum() / visited.sum() > 0.5
+
+
+# ---------------------------------------------------------------- backward (gradients of the dense definition)
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_matches_torch_autograd(causal):
+    # library special case: float64 SDPA with the KV heads repeated, per sequence; the gradients of the
+    # repeated K/V are summed over each KV head's group
+    lens, Hq, Hkv, D = [5, 17, 33], 4, 2, 16
+    G = Hq // Hkv
+    x = W.varlen_prefill(seed=71, lengths=lens, Hq=Hq, Hkv=Hkv, D=D, dtype=torch.float32)
+    dout = W.varlen_prefill(seed=72, lengths=lens, Hq=Hq, Hkv=Hkv, D=D, dtype=torch.float32).q
+    scale = 0.3
+    dq, dk, dv = oracle.prefill_backward(x.q, x.k, x.v, dout, x.cu_q, x.cu_k, Hq, Hkv, scale, causal)
+    cu = x.cu_q.tolist()
+    for b, L in enumerate(lens):
+        sl = slice(cu[b], cu[b + 1])
+        q = x.q[sl].double().permute(1, 0, 2).clone().requires_grad_(True)
+        k = x.k[sl].double().permute(1, 0, 2).clone().requires_grad_(True)
+        v = x.v[sl].double().permute(1, 0, 2).clone().requires_grad_(True)
+        o = torch.nn.functional.scaled_dot_product_attention(
+            q[None], k.repeat_interleave(G, 0)[None], v.repeat_interleave(G, 0)[None], is_causal=causal,
+            scale=scale)[0]
+        (o * dout[sl].double().permute(1, 0, 2)).sum().backward()
+        assert np.max(np.abs(dq[sl] - q.grad.permute(1, 0, 2).numpy())) < 1e-10
+        assert np.max(np.abs(dk[sl] - k.grad.permute(1, 0, 2).numpy())) < 1e-10
+        assert np.max(np.abs(dv[sl] - v.grad.permute(1, 0, 2).numpy())) < 1e-10
+
+
+def test_backward_matches_finite_differences():
+    # central differences of L = sum(O * dO) with the forward oracle, on inputs that are multiples of
+    # 2^-10 so that x +- 2^-10 is exact in fp32; the error of the difference is O(eps^2)
+    rng = np.random.default_rng(3)
+    L, Hq, Hkv, D = 9, 2, 1, 8
+    q = (np.round(rng.standard_normal((L, Hq, D)) * 1024) / 1024).astype(np.float32)
+    k = (np.round(rng.standard_normal((L, Hkv, D)) * 1024) / 1024).astype(np.float32)
+    v = (np.round(rng.standard_normal((L, Hkv, D)) * 1024) / 1024).astype(np.float32)
+    g = rng.standard_normal((L, Hq, D)).astype(np.float32)
+    cu = np.array([0, L], dtype=np.int32)
+    scale = 0.5
+
+    def loss(q_, k_, v_):
+        o, _, _ = oracle.prefill(q_, k_, v_, cu, cu, Hq, Hkv, scale, True)
+        return float(np.sum(o * g.astype(np.float64)))
+
+    dq, dk, dv = oracle.prefill_backward(q, k, v, g, cu, cu, Hq, Hkv, scale, True)
+    eps = 2.0 ** -10
+    for name, arr, grad in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+        for idx in [(0, 0, 0), (3, 0, 5), (8, arr.shape[1] - 1, 7), (5, 0, 2)]:
+            plus, minus = arr.copy(), arr.copy()
+            plus[idx] += eps
+            minus[idx] -= eps
+            args_p = {"q": q, "k": k, "v": v}
+            args_m = dict(args_p)
+            args_p[name], args_m[name] = plus, minus
+            fd = (loss(args_p["q"], args_p["k"], args_p["v"]) - loss(args_m["q"], args_m["k"], args_m["v"])) / (2 * eps)
+            assert abs(fd - grad[idx]) < 1e-5, (name, idx, fd, grad[idx])
+
+
+def test_backward_rows_without_keys_and_unseen_keys():
+    # causal with Lq > Lk: the first Lq - Lk rows see no key and get dq = 0; with Lk > Lq every key is
+    # seen by some row, and a row's gradient does not depend on keys past its diagonal
+    x = W.varlen_prefill(seed=74, lengths=[12], Hq=2, Hkv=1, D=8, dtype=torch.float32)
+    dout = W.varlen_prefill(seed=75, lengths=[12], Hq=2, Hkv=1, D=8, dtype=torch.float32).q
+    cq = torch.tensor([0, 12], dtype=torch.int32)
+    ck = torch.tensor([0, 7], dtype=torch.int32)
+    dq, dk, dv = oracle.prefill_backward(x.q, x.k[:7], x.v[:7], dout, cq, ck, 2, 1, 0.4, True)
+    assert np.all(dq[:5] == 0) and np.any(dq[5:] != 0)
+    # the last key is seen only by the last row: its dv is that row's p times dO, summed over the heads
+    o, lse, _ = oracle.prefill(x.q, x.k[:7], x.v[:7], cq, ck, 2, 1, 0.4, True, rows=[(11, 0), (11, 1)])
+    s = np.array([0.4 * float(x.q[11, h].double() @ x.k[6, 0].double()) for h in range(2)])
+    p_last = np.exp(s - lse)
+    expect = sum(p_last[h] * dout[11, h].double().numpy() for h in range(2))
+    assert np.max(np.abs(dv[6, 0] - expect)) < 1e-12
