@@ -122,6 +122,31 @@ attn_status_t attn_smallseq_cross(const void *q, const void *k, const void *v, c
                                   int32_t B, int32_t H, int32_t D, int32_t max_seqlen_kv, float scale,
                                   void *o, void *attn_weights, float *lse, void *stream);
 
+/*
+ * Backward of the dense varlen prefill: the gradients dq, dk, dv of the masked-softmax attention
+ * o = softmax(scale q k^T + mask) v for an output gradient dout ("Model-Optimizer: Add Triton unified
+ * attention kernel with HuggingFace integration", summary: the Triton kernel has an autograd backward
+ * beside its forward).  With P = exp(scale q k^T - lse) over the visible keys:
+ *   dv = P^T dout,  dk = scale dS^T q,  dq = scale dS k,  dS = P * (dout v^T - rowsum(dout * o))
+ * with dk and dv summed over the query heads of each KV head's group.
+ *   q, o, dout, dq [tq, Hq, D]; k, v, dk, dv [tk, Hkv, D]; all bf16; cu_seqlens_q / cu_seqlens_k,
+ *   max_seqlen_q / max_seqlen_k, causal and scale as for the forward call that produced o and lse.
+ *   lse: fp32 [tq, Hq], the forward's natural-log LSE (-inf for rows with no visible key).
+ *   workspace: at least attn_prefill_varlen_backward_workspace_size(B, max_seqlen_q, Hq) bytes
+ *   (B * max_seqlen_q * Hq * 4) of device memory owned by the caller; no initialisation needed; it
+ *   receives rowsum(dout * o) per (token, query head).  dq, dk, dv are fully written (rows with no
+ *   visible key and keys no query sees get 0).
+ *   Supported: bf16 with D = 128 and B * max_seqlen_q * Hq < 2^31 (else ATTN_ERR_UNSUPPORTED).
+ *   B == 0 is a no-op.  Asynchronous on `stream`, like the forward.
+ */
+size_t attn_prefill_varlen_backward_workspace_size(int32_t B, int32_t max_seqlen_q, int32_t Hq);
+attn_status_t attn_prefill_varlen_backward(attn_dtype_t dtype, const void *q, const void *k, const void *v,
+                                           const void *o, const void *dout, const float *lse,
+                                           const int32_t *cu_seqlens_q, const int32_t *cu_seqlens_k, int32_t B,
+                                           int32_t max_seqlen_q, int32_t max_seqlen_k, int32_t Hq, int32_t Hkv,
+                                           int32_t D, float scale, int32_t causal, void *dq, void *dk, void *dv,
+                                           void *workspace, size_t workspace_bytes, void *stream);
+
 /* Static description of a status code. */
 const char *attn_status_string(attn_status_t s);
 

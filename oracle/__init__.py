@@ -47,7 +47,7 @@ def _load():
         lib.orc_prefill_rows.argtypes = [I, P, P, P, P, P, I, I, I, I, D, I, I, D, I, I, P, I, P, I, P, P, P]
         lib.orc_decode_rows.argtypes = [P, P, P, P, P, I, I, I, I, I, I, D, I, D, I, I, P, I, P, I, P, P, P]
         lib.orc_smallseq_rows.argtypes = [I, P, P, P, P, I, I, I, I, D, P, I, P, P]
-        lib.orc_prefill_bwd.argtypes = [I, P, P, P, P, P, P, I, I, I, I, D, I, P, P, P]
+        lib.orc_prefill_bwd.argtypes = [I, P, P, P, P, P, P, P, I, I, I, I, D, I, P, P, P]
         for f in (lib.orc_prefill_rows, lib.orc_decode_rows, lib.orc_smallseq_rows, lib.orc_prefill_bwd):
             f.restype = ctypes.c_int
         _lib = lib
@@ -184,13 +184,20 @@ def smallseq(q, k, v, cu_kv, max_s, scale, rows=None):
     return o, w
 
 
-def prefill_backward(q, k, v, dout, cu_q, cu_k, Hq, Hkv, scale, causal):
-    """Gradients (dq, dk, dv) of the dense varlen prefill for the output gradient ``dout`` (all rows)."""
+def prefill_backward(q, k, v, dout, cu_q, cu_k, Hq, Hkv, scale, causal, o=None):
+    """Gradients (dq, dk, dv) of the dense varlen prefill for the output gradient ``dout`` (all rows).
+
+    o (optional, dout's dtype and shape): a stored forward output; the row dots dO.o then replace the exact
+    sum_j p_j dP_j in dS, as a backward that reads the saved output computes them."""
     qa, dt = _np(q)
     ka, dk_ = _np(k)
     va, dv_ = _np(v)
     ga, dg = _np(dout)
     assert dt == dk_ == dv_ == dg and dt in (0, 1)
+    oa = None
+    if o is not None:
+        oa, do_ = _np(o)
+        assert do_ == dt and oa.shape == ga.shape
     cq, _ = _np(cu_q)
     ck, _ = _np(cu_k)
     B = len(cq) - 1
@@ -198,8 +205,9 @@ def prefill_backward(q, k, v, dout, cu_q, cu_k, Hq, Hkv, scale, causal):
     dq = np.zeros(qa.shape, dtype=np.float64)
     dk = np.zeros(ka.shape, dtype=np.float64)
     dv = np.zeros(va.shape, dtype=np.float64)
-    rc = _load().orc_prefill_bwd(dt, _ptr(qa), _ptr(ka), _ptr(va), _ptr(ga), _ptr(cq), _ptr(ck), B, Hq, Hkv, D,
-                                 float(scale), int(bool(causal)), _ptr(dq), _ptr(dk), _ptr(dv))
+    rc = _load().orc_prefill_bwd(dt, _ptr(qa), _ptr(ka), _ptr(va), _ptr(ga), None if oa is None else _ptr(oa),
+                                 _ptr(cq), _ptr(ck), B, Hq, Hkv, D, float(scale), int(bool(causal)), _ptr(dq),
+                                 _ptr(dk), _ptr(dv))
     if rc != 0:
         raise ValueError("oracle backward rejected its arguments")
     return dq, dk, dv

@@ -369,21 +369,23 @@ int orc_smallseq_rows(int dtype, const void *q, const void *k, const void *v, co
 }
 
 /*
- * Backward of the dense varlen prefill (the gradients of the masked-softmax definition above), for the
- * next step the source pages list after the forward kernels ("Model-Optimizer: Add Triton unified
- * attention kernel with HuggingFace integration", description: the kernel serves training as well).
- * With p_j = exp(s_j - lse), s_j = scale q.k_j over the visible keys of a row and dO the output
- * gradient:
- *   dP_j = dO.v_j,  Dsum = sum_j p_j dP_j,  dS_j = p_j (dP_j - Dsum)
+ * Backward of the dense varlen prefill (the gradients of the masked-softmax definition above); the
+ * Triton kernel of "Model-Optimizer: Add Triton unified attention kernel with HuggingFace integration"
+ * (summary) has an autograd backward beside its forward.  With p_j = exp(s_j - lse), s_j = scale q.k_j
+ * over the visible keys of a row and dO the output gradient:
+ *   dP_j = dO.v_j,  Dsum = dO.o = sum_j p_j dP_j,  dS_j = p_j (dP_j - Dsum)
  *   dq   = scale sum_j dS_j k_j
  *   dk_j += scale dS_j q,  dv_j += p_j dO          (summed over every query row and query head of the group)
- * Inputs as for orc_prefill_rows plus dout [tq, Hq, D] of the same dtype; outputs fp64 dq [tq, Hq, D],
- * dk and dv [tk, Hkv, D] (fully written).  One task per (sequence, KV head), so no two tasks touch the
- * same output.
+ * Inputs as for orc_prefill_rows plus dout [tq, Hq, D] of the same dtype, and o (nullable, same dtype and
+ * layout as dout): a stored forward output.  Without o, Dsum is the exact sum_j p_j dP_j; with o it is
+ * the row dot dO.o of the stored output, as a backward that reads the saved output computes it (equal to
+ * the former when o is the exact output; a rounded o shifts every dS_j of the row by -p_j * the dot of
+ * dO with the rounding).  Outputs fp64 dq [tq, Hq, D], dk and dv [tk, Hkv, D] (fully written).  One task
+ * per (sequence, KV head), so no two tasks touch the same output.
  */
-int orc_prefill_bwd(int dtype, const void *q, const void *k, const void *v, const void *dout, const int32_t *cu_q,
-                    const int32_t *cu_k, int B, int Hq, int Hkv, int D, double scale, int causal, double *dq,
-                    double *dk, double *dv)
+int orc_prefill_bwd(int dtype, const void *q, const void *k, const void *v, const void *dout, const void *o,
+                    const int32_t *cu_q, const int32_t *cu_k, int B, int Hq, int Hkv, int D, double scale, int causal,
+                    double *dq, double *dk, double *dv)
 {
     if (B < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv || D <= 0)
         return -1;
@@ -436,6 +438,11 @@ int orc_prefill_bwd(int dtype, const void *q, const void *k, const void *v, cons
                         s[j] = exp(s[j] - lse); /* s now holds p */
                         dp[j] = dot(go, V + (size_t)j * D, D);
                         dsum += s[j] * dp[j];
+                    }
+                    if (o) {
+                        dsum = 0.0;
+                        for (int d = 0; d < D; ++d)
+                            dsum += go[d] * widen(o, dtype, row + d);
                     }
                     for (int j = 0; j < n; ++j) {
                         const double ds = s[j] * (dp[j] - dsum);

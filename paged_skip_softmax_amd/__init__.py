@@ -17,8 +17,8 @@ import torch
 from . import _lib
 from ._lib import SKIP_TILE, AttnError  # noqa: F401
 
-__all__ = ["attn_prefill_varlen", "attn_decode_paged", "attn_decode_paged_workspace_size",
-           "attn_smallseq_cross", "AttnError", "SKIP_TILE"]
+__all__ = ["attn_prefill_varlen", "attn_prefill_varlen_backward", "attn_prefill_varlen_backward_workspace_size",
+           "attn_decode_paged", "attn_decode_paged_workspace_size", "attn_smallseq_cross", "AttnError", "SKIP_TILE"]
 
 
 def _stream(t: torch.Tensor) -> int:
@@ -80,6 +80,50 @@ def attn_prefill_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_s
                                        D, float(scale), int(bool(causal)), float(skip_threshold),
                                        out.data_ptr(), _ptr(lse), _ptr(smap), stride, _stream(q)))
     return out, lse, smap
+
+
+def attn_prefill_varlen_backward_workspace_size(B: int, max_seqlen_q: int, Hq: int) -> int:
+    """Workspace bytes of the prefill backward (the per-row rowsum(dO * O))."""
+    return int(_lib.load().attn_prefill_varlen_backward_workspace_size(B, max_seqlen_q, Hq))
+
+
+def attn_prefill_varlen_backward(q, k, v, o, dout, lse, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, *,
+                                 scale=None, causal=True, workspace=None, dq=None, dk=None, dv=None):
+    """Gradients of the dense varlen prefill from its output o and LSE.  Returns (dq, dk, dv)."""
+    lib = _lib.load()
+    dev = q.device
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout)):
+        _cuda_contig(name, t, torch.bfloat16, dev)
+    _cuda_contig("lse", lse, torch.float32, dev)
+    for name, t in (("cu_seqlens_q", cu_seqlens_q), ("cu_seqlens_k", cu_seqlens_k)):
+        _cuda_contig(name, t, torch.int32, dev)
+    _need(q.dim() == 3 and k.dim() == 3 and k.shape == v.shape, "q [tq,Hq,D], k/v [tk,Hkv,D]")
+    _need(o.shape == q.shape and dout.shape == q.shape, "o and dout must match q")
+    tq, Hq, D = q.shape
+    Hkv = k.shape[1]
+    _need(k.shape[2] == D, "head dims differ")
+    _need(lse.shape == (tq, Hq), "lse must be [tq, Hq]")
+    B = cu_seqlens_q.numel() - 1
+    _need(B >= 0 and cu_seqlens_k.numel() == B + 1, "cu_seqlens must both have B + 1 entries")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    need = attn_prefill_varlen_backward_workspace_size(B, int(max_seqlen_q), Hq)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    for name, t, ref in (("dq", dq, q), ("dk", dk, k), ("dv", dv, v)):
+        _cuda_contig(name, t, torch.bfloat16, dev)
+        _need(t.shape == ref.shape, f"{name} must match its input's shape")
+    _lib.check(lib.attn_prefill_varlen_backward(_lib.ATTN_BF16, q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                                o.data_ptr(), dout.data_ptr(), lse.data_ptr(),
+                                                cu_seqlens_q.data_ptr(), cu_seqlens_k.data_ptr(), B,
+                                                int(max_seqlen_q), int(max_seqlen_k), Hq, Hkv, D, float(scale),
+                                                int(bool(causal)), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                                                _ptr(workspace), ws_bytes, _stream(q)))
+    return dq, dk, dv
 
 
 def attn_decode_paged(q, k_cache, v_cache, block_table, seq_lens, *, scale=None, skip_threshold=0.0, num_splits=0,

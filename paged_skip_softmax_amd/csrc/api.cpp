@@ -153,6 +153,68 @@ attn_status_t attn_decode_paged(const void *q, const void *k_cache, const void *
     return hip_status(attn::launch_decode_seq(a, B, st), "decode sequential launch");
 }
 
+size_t attn_prefill_varlen_backward_workspace_size(int32_t B, int32_t max_seqlen_q, int32_t Hq)
+{
+    if (B <= 0 || max_seqlen_q <= 0 || Hq <= 0)
+        return 0;
+    // rowsum(dO * O) per (token, query head); B * max_seqlen_q bounds the token count
+    return (size_t)B * max_seqlen_q * Hq * sizeof(float);
+}
+
+attn_status_t attn_prefill_varlen_backward(attn_dtype_t dtype, const void *q, const void *k, const void *v,
+                                           const void *o, const void *dout, const float *lse,
+                                           const int32_t *cu_seqlens_q, const int32_t *cu_seqlens_k, int32_t B,
+                                           int32_t max_seqlen_q, int32_t max_seqlen_k, int32_t Hq, int32_t Hkv,
+                                           int32_t D, float scale, int32_t causal, void *dq, void *dk, void *dv,
+                                           void *workspace, size_t workspace_bytes, void *stream)
+{
+    if (dtype != ATTN_F32 && dtype != ATTN_BF16)
+        return fail(ATTN_ERR_INVALID, "attn_prefill_varlen_backward: unknown dtype %d", (int)dtype);
+    if (B < 0 || max_seqlen_q < 0 || max_seqlen_k < 0)
+        return fail(ATTN_ERR_INVALID, "attn_prefill_varlen_backward: negative B or max_seqlen");
+    if (Hq <= 0 || Hkv <= 0 || Hq % Hkv)
+        return fail(ATTN_ERR_INVALID, "attn_prefill_varlen_backward: Hq = %d must be a positive multiple of Hkv = %d",
+                    Hq, Hkv);
+    if (!std::isfinite(scale))
+        return fail(ATTN_ERR_INVALID, "attn_prefill_varlen_backward: scale is not finite");
+    if (dtype != ATTN_BF16 || D != 128)
+        return fail(ATTN_ERR_UNSUPPORTED, "attn_prefill_varlen_backward: built for bf16 with D = 128");
+    if ((int64_t)B * max_seqlen_q * Hq >= ((int64_t)1 << 31))
+        return fail(ATTN_ERR_UNSUPPORTED, "attn_prefill_varlen_backward: B * max_seqlen_q * Hq must stay below 2^31");
+    if (B == 0)
+        return ok();
+    if (!q || !k || !v || !o || !dout || !lse || !cu_seqlens_q || !cu_seqlens_k || !dq || !dk || !dv)
+        return fail(ATTN_ERR_INVALID, "attn_prefill_varlen_backward: a required pointer is NULL");
+    const size_t need = attn_prefill_varlen_backward_workspace_size(B, max_seqlen_q, Hq);
+    if (need && (!workspace || workspace_bytes < need))
+        return fail(ATTN_ERR_WORKSPACE, "attn_prefill_varlen_backward: workspace %zu bytes, need %zu", workspace_bytes,
+                    need);
+    attn::BwdArgs a{};
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.o = o;
+    a.dout = dout;
+    a.lse = lse;
+    a.dsum = static_cast<float *>(workspace);
+    a.cu_q = cu_seqlens_q;
+    a.cu_k = cu_seqlens_k;
+    a.B = B;
+    a.max_q = max_seqlen_q;
+    a.max_k = max_seqlen_k;
+    a.Hq = Hq;
+    a.Hkv = Hkv;
+    a.G = Hq / Hkv;
+    a.causal = causal != 0;
+    a.scale = scale;
+    a.scale_log2 = scale * 1.4426950408889634f;
+    a.dq = dq;
+    a.dk = dk;
+    a.dv = dv;
+    return hip_status(attn::launch_prefill_bwd(a, static_cast<hipStream_t>(stream)),
+                      "prefill backward launch");
+}
+
 attn_status_t attn_smallseq_cross(const void *q, const void *k, const void *v, const int32_t *cu_seqlens_kv,
                                   int32_t B, int32_t H, int32_t D, int32_t max_seqlen_kv, float scale,
                                   void *o, void *attn_weights, float *lse, void *stream)

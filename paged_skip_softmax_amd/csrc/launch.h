@@ -59,10 +59,23 @@ struct PrefillArgs {
     int map_stride;
 };
 
+// Backward of the dense bf16 varlen prefill (D = 128).
+struct BwdArgs {
+    const void *q, *k, *v, *o, *dout;
+    const float *lse;          // [tq, Hq] natural log, from the forward
+    float *dsum;               // [tq, Hq] workspace: rowsum(dO * O)
+    const int32_t *cu_q, *cu_k;
+    int B, max_q, max_k, Hq, Hkv, G;
+    bool causal;
+    float scale, scale_log2;
+    void *dq, *dk, *dv;        // bf16, like q, k, v
+};
+
 hipError_t launch_decode_split(const SplitArgs &a, int B, uint16_t *o, float *lse, hipStream_t stream);
 hipError_t launch_decode_seq(const SeqArgs &a, int B, hipStream_t stream);
 hipError_t launch_smallseq(const SmallArgs &a, hipStream_t stream);
 hipError_t launch_prefill(const PrefillArgs &a, bool bf16, int D, hipStream_t stream);
-hipError_t launch_prefill_d128(const PrefillArgs &a, hipStream_t stream); // dense bf16, D = 128
+hipError_t launch_prefill_d128(const PrefillArgs &a, hipStream_t stream); // bf16, D = 128
+hipError_t launch_prefill_bwd(const BwdArgs &a, hipStream_t stream);
 
 } // namespace attn

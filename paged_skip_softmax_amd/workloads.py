@@ -36,7 +36,7 @@ from types import SimpleNamespace
 import torch
 
 # stream ids: one independent generator per purpose
-_S_LEN, _S_Q, _S_K, _S_V, _S_PERM, _S_HOT = range(6)
+_S_LEN, _S_Q, _S_K, _S_V, _S_PERM, _S_HOT, _S_DO = range(7)
 
 
 def _gen(seed: int, stream: int, device="cpu") -> torch.Generator:
@@ -126,6 +126,11 @@ def varlen_prefill_hot(seed=1001, device="cpu", q_align=2.0, k_boost=24.0, hot_f
     x.k = k.to(x.dtype)
     x.hot_tiles = hot_tiles
     return x
+
+
+def grad_output(x, seed=1005, device="cpu"):
+    """A seeded standard-normal output gradient dO shaped like x.q (backward inputs)."""
+    return _randn(tuple(x.q.shape), seed, _S_DO, device, x.q.dtype)
 
 
 def _page_table(lens, page, pool, max_pages, seed):

@@ -96,6 +96,35 @@ def test_prefill_validation(lib):
     assert b"2^32" in lib.attn_last_error_message()
 
 
+def _backward(lib, **kw):
+    a = dict(dt=_lib.ATTN_BF16, q=FAKE, k=FAKE, v=FAKE, o=FAKE, do=FAKE, lse=FAKE, cq=FAKE, ck=FAKE, B=2, mq=10,
+             mk=10, Hq=8, Hkv=2, D=128, scale=0.1, causal=1, dq=FAKE, dk=FAKE, dv=FAKE, ws=FAKE, wsb=1 << 20,
+             stream=None)
+    a.update(kw)
+    return lib.attn_prefill_varlen_backward(a["dt"], a["q"], a["k"], a["v"], a["o"], a["do"], a["lse"], a["cq"],
+                                            a["ck"], a["B"], a["mq"], a["mk"], a["Hq"], a["Hkv"], a["D"], a["scale"],
+                                            a["causal"], a["dq"], a["dk"], a["dv"], a["ws"], a["wsb"], a["stream"])
+
+
+def test_backward_validation(lib):
+    assert lib.attn_prefill_varlen_backward_workspace_size(3, 100, 8) == 3 * 100 * 8 * 4
+    assert lib.attn_prefill_varlen_backward_workspace_size(0, 100, 8) == 0
+    assert _backward(lib, dt=5) == INVALID
+    assert _backward(lib, B=-1) == INVALID
+    assert _backward(lib, Hq=6, Hkv=4) == INVALID
+    assert _backward(lib, scale=math.inf) == INVALID
+    assert _backward(lib, D=64) == UNSUPPORTED
+    assert _backward(lib, dt=_lib.ATTN_F32) == UNSUPPORTED
+    assert _backward(lib, B=1 << 16, mq=1 << 12, Hq=8) == UNSUPPORTED
+    assert _backward(lib, lse=None) == INVALID
+    assert _backward(lib, dv=None) == INVALID
+    assert _backward(lib, wsb=2 * 10 * 8 * 4 - 1) == WORKSPACE
+    assert _backward(lib, ws=None) == WORKSPACE
+    assert _backward(lib, B=0) == _lib.ATTN_OK
+    _backward(lib, D=96)
+    assert b"D = 128" in lib.attn_last_error_message()
+
+
 def _small(lib, **kw):
     a = dict(q=FAKE, k=FAKE, v=FAKE, cu=FAKE, B=4, H=16, D=128, ms=16, scale=0.1, o=FAKE, w=None, lse=None,
              stream=None)

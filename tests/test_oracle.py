@@ -414,6 +414,43 @@ def test_backward_matches_torch_autograd(causal):
         assert np.max(np.abs(dv[sl] - v.grad.permute(1, 0, 2).numpy())) < 1e-10
 
 
+@pytest.mark.parametrize("causal", [True, False])
+def test_backward_with_stored_output_matches_autograd(causal):
+    # with a stored output o' the row dot dO.o' replaces sum_j p_j dP_j; that equals the gradient of
+    # sum(dO * O) - sum_i delta_i * LSE_i with the constant delta_i = dO_i.(o'_i - O_i), since
+    # d LSE_i / d s_ij = p_ij.  Autograd of float64 torch ops (masked logsumexp and softmax) pins it.
+    lens, Hq, Hkv, D = [5, 17, 33], 4, 2, 16
+    G = Hq // Hkv
+    x = W.varlen_prefill(seed=76, lengths=lens, Hq=Hq, Hkv=Hkv, D=D, dtype=torch.float32)
+    dout = W.varlen_prefill(seed=77, lengths=lens, Hq=Hq, Hkv=Hkv, D=D, dtype=torch.float32).q
+    scale = 0.3
+    o_exact, _, _ = oracle.prefill(x.q, x.k, x.v, x.cu_q, x.cu_k, Hq, Hkv, scale, causal)
+    rng = np.random.default_rng(78)
+    o_st = (o_exact + 0.05 * rng.standard_normal(o_exact.shape)).astype(np.float32)
+    dq, dk, dv = oracle.prefill_backward(x.q, x.k, x.v, dout, x.cu_q, x.cu_k, Hq, Hkv, scale, causal,
+                                         o=torch.from_numpy(o_st))
+    cu = x.cu_q.tolist()
+    for b, L in enumerate(lens):
+        sl = slice(cu[b], cu[b + 1])
+        q = x.q[sl].double().permute(1, 0, 2).clone().requires_grad_(True)
+        k = x.k[sl].double().permute(1, 0, 2).clone().requires_grad_(True)
+        v = x.v[sl].double().permute(1, 0, 2).clone().requires_grad_(True)
+        s = scale * q @ k.repeat_interleave(G, 0).transpose(1, 2)
+        if causal:
+            s = s.masked_fill(torch.ones(L, L, dtype=torch.bool).triu(1), -math.inf)
+        lse = torch.logsumexp(s, dim=-1)
+        o = torch.softmax(s, dim=-1) @ v.repeat_interleave(G, 0)
+        g = dout[sl].double().permute(1, 0, 2)
+        delta = (g * (torch.from_numpy(o_st[sl]).double().permute(1, 0, 2) - o.detach())).sum(-1)
+        ((o * g).sum() - (delta * lse).sum()).backward()
+        assert np.max(np.abs(dq[sl] - q.grad.permute(1, 0, 2).numpy())) < 1e-10
+        assert np.max(np.abs(dk[sl] - k.grad.permute(1, 0, 2).numpy())) < 1e-10
+        assert np.max(np.abs(dv[sl] - v.grad.permute(1, 0, 2).numpy())) < 1e-10
+    # the stored output shifts dq and dk, never dv
+    dq0, dk0, dv0 = oracle.prefill_backward(x.q, x.k, x.v, dout, x.cu_q, x.cu_k, Hq, Hkv, scale, causal)
+    assert np.array_equal(dv, dv0) and np.max(np.abs(dq - dq0)) > 1e-3
+
+
 def test_backward_matches_finite_differences():
     # central differences of L = sum(O * dO) with the forward oracle, on inputs that are multiples of
     # 2^-10 so that x +- 2^-10 is exact in fp32; the error of the difference is O(eps^2)
