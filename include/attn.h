@@ -136,7 +136,8 @@ attn_status_t attn_smallseq_cross(const void *q, const void *k, const void *v, c
  *   (B * max_seqlen_q * Hq * 4) of device memory owned by the caller; no initialisation needed; it
  *   receives rowsum(dout * o) per (token, query head).  dq, dk, dv are fully written (rows with no
  *   visible key and keys no query sees get 0).
- *   Supported: bf16 with D = 128 and B * max_seqlen_q * Hq < 2^31 (else ATTN_ERR_UNSUPPORTED).
+ *   Supported: bf16 with D = 128, B * max_seqlen_q * Hq < 2^31, max_seqlen_q * Hq * D * 2 < 2^31 and
+ *   max_seqlen_k * Hkv * D * 2 < 2^31 (else ATTN_ERR_UNSUPPORTED).
  *   B == 0 is a no-op.  Asynchronous on `stream`, like the forward.
  */
 size_t attn_prefill_varlen_backward_workspace_size(int32_t B, int32_t max_seqlen_q, int32_t Hq);

@@ -181,6 +181,9 @@ attn_status_t attn_prefill_varlen_backward(attn_dtype_t dtype, const void *q, co
         return fail(ATTN_ERR_UNSUPPORTED, "attn_prefill_varlen_backward: built for bf16 with D = 128");
     if ((int64_t)B * max_seqlen_q * Hq >= ((int64_t)1 << 31))
         return fail(ATTN_ERR_UNSUPPORTED, "attn_prefill_varlen_backward: B * max_seqlen_q * Hq must stay below 2^31");
+    // the kernels address one sequence's rows of all heads with 32-bit byte offsets
+    if ((int64_t)max_seqlen_q * Hq * D * 2 >= ((int64_t)1 << 31) || (int64_t)max_seqlen_k * Hkv * D * 2 >= ((int64_t)1 << 31))
+        return fail(ATTN_ERR_UNSUPPORTED, "attn_prefill_varlen_backward: max_seqlen * heads * D * 2 must stay below 2^31");
     if (B == 0)
         return ok();
     if (!q || !k || !v || !o || !dout || !lse || !cu_seqlens_q || !cu_seqlens_k || !dq || !dk || !dv)

@@ -21,6 +21,7 @@
 //      dQ^T += K^T dS^T             (K^T by transposed LDS reads)
 #include "kcommon.h"
 #include "launch.h"
+#include "lds_dma.h"
 
 namespace attn {
 namespace {
@@ -28,22 +29,8 @@ namespace {
 constexpr int D = 128;
 constexpr int kRowBytes = D * 2; // one bf16 row of 128 dims
 
-typedef short i16x4 __attribute__((ext_vector_type(4)));
-
-// XOR swizzle of the 16 chunk slots of a 256-B LDS row (as in the forward kernel).
-__device__ __forceinline__ int swz(int r)
-{
-    return ((r & 1) ? 10 : 0) ^ ((r & 2) ? 4 : 0) ^ ((r & 4) ? 1 : 0) ^ ((r & 8) ? 2 : 0);
-}
-
 // Byte offset of 16-byte chunk c of row r in a swizzled tile.
 __device__ __forceinline__ uint32_t chunk_off(int r, int c) { return (uint32_t)(r * kRowBytes + 16 * (c ^ swz(r & 15))); }
-
-__device__ __forceinline__ uint2 lds_read_tr(const char *p)
-{
-    const i16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4 *)(p));
-    return __builtin_bit_cast(uint2, r);
-}
 
 // Copies rows [r0, r0 + nrows) of a [tokens, H, D] bf16 tensor (head h, rows past `valid` zero) into a
 // swizzled LDS tile, cooperatively over the workgroup's threads.
@@ -95,131 +82,354 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdArgs a)
 
 // ------------------------------------------------------------------ dK, dV
 
+constexpr int kXcds = 8;
 constexpr int kKvWaves = 4;
-constexpr int kKeysPerWave = 16;
-constexpr int kKeysPerWg = kKvWaves * kKeysPerWave;
-constexpr int kQRows = 32; // query rows per staged tile
+constexpr int kKvThreads = 64 * kKvWaves;
+constexpr int kKeysPerWave = 32;
+constexpr int kKeysPerWg = kKvWaves * kKeysPerWave; // 128
+constexpr int kQRows = 64;                          // query rows per staged tile
+constexpr int kQTileBytes = kQRows * kRowBytes;     // 16 KB
+constexpr int kQLoads = kQTileBytes / 1024 / kKvWaves; // 1-KB direct-to-LDS loads per wave per tile
+constexpr int kQStages = 3;
 
-__global__ __launch_bounds__(64 * kKvWaves) void bwd_dkdv_kernel(BwdArgs a, int nkt)
+// One stage of the Q / dO ring: the two tiles (swizzled rows) and the rows' LSE and Dsum.
+struct alignas(1024) QStage {
+    char q[kQTileBytes];
+    char g[kQTileBytes];
+    float lse[kQRows];
+    float dsum[kQRows];
+};
+__shared__ QStage q_ring[kQStages];
+
+// What one lane needs to issue the direct-to-LDS loads of a Q / dO tile.
+struct QLoader {
+    i32x4 qrs, grs, lrs, drs;  // buffer resources of Q, dO (from head 0 of the sequence), lse, Dsum
+    uint32_t voff[kQLoads];    // lane's byte offsets inside a tile of rows (4-row blocks of the wave)
+    uint32_t loff;             // lane's byte offset of its LSE / Dsum row
+    uint32_t row_bytes;        // global bytes between consecutive rows of one head
+    int Hq, w;
+
+    // rows [r0, r0 + 64) of head h into stage st (rows past the sequence read as zero)
+    __device__ __forceinline__ void issue(int st, int r0, int h) const
+    {
+        const uint32_t soff = (uint32_t)r0 * row_bytes + (uint32_t)h * kRowBytes;
+        const uint32_t wq = lds_addr(q_ring[st].q) + w * (kQLoads * 1024);
+        const uint32_t wg = lds_addr(q_ring[st].g) + w * (kQLoads * 1024);
+#pragma unroll
+        for (int p = 0; p < kQLoads; ++p) {
+            dma16(wq + p * 1024, voff[p], qrs, soff);
+            dma16(wg + p * 1024, voff[p], grs, soff);
+        }
+        const uint32_t soff4 = ((uint32_t)r0 * Hq + h) * 4;
+        if (w == 0)
+            dma4(lds_addr(q_ring[st].lse), loff, lrs, soff4);
+        else if (w == 1)
+            dma4(lds_addr(q_ring[st].dsum), loff, drs, soff4);
+    }
+};
+
+// A 32-row block of a staged tile: its Q and dO rows, their LSE and Dsum, and its first query row.
+struct Blk {
+    const char *q, *g;
+    const float *lse, *dsum;
+    int row0;
+    bool full; // every row of the block sees every key of the wave
+};
+
+// A operand of S / dP, k-step s: 16 B of row n of the block, dims 16 s + 8 J.
+__device__ __forceinline__ bf16x8 rd_rows(const char *rows, uint32_t rowA, int s)
 {
-    // unit = (KV head g, sequence b, key block kt)
-    const int unit = blockIdx.x;
-    const int kt = unit % nkt, b = (unit / nkt) % a.B, g = unit / (nkt * a.B);
+    return as_bf16x8(ld16(rows + (rowA ^ (32 * s))));
+}
+
+// A operand of dV^T / dK^T for 16-row half u and 32-dim block db of a block, by transposed reads:
+// dims 32 db + lane % 32, k-slot 8 J + e <-> row 16 u + 8 (e/4) + 4 J + e%4.
+__device__ __forceinline__ bf16x8 rd_cols(const char *rows, const uint32_t trA[2], int u, int db)
+{
+    const char *base = rows + 16 * u * kRowBytes;
+    const uint2 lo = lds_read_tr(base + (trA[0] ^ (64 * db)));
+    const uint2 hi = lds_read_tr(base + (trA[1] ^ (64 * db)));
+    return as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
+}
+
+__device__ __forceinline__ bf16x8 half_op(const uint32_t x[8], int u)
+{
+    return as_bf16x8(make_uint4(x[4 * u], x[4 * u + 1], x[4 * u + 2], x[4 * u + 3]));
+}
+
+// Per-lane constants of the dK / dV wave.
+struct KvLane {
+    uint32_t rowA;    // A-operand read offset (row n, chunk J)
+    uint32_t trA[2];  // transposed-read offsets (16-row halves' lower and upper 8 rows)
+    int J;
+    int lo_row, span; // the rows that see the lane's key: [lo_row, lo_row + span)
+    float sl;         // scale * log2(e)
+};
+
+// One pipeline step of a wave over 32-row blocks: with C, dV^T += dO^T P and dK^T += Q^T dS of an
+// older block (bc; its packed P and dS in pkc, skc); with S, S = Q K^T and dP = dO V^T of a new block
+// (bs) into sc, dp; with P, P = exp(scale S - lse) and dS = P (dP - Dsum) of the block in between (bp;
+// its scores scp, dpp) into pkn, skn.  The 8 k-steps issue up to 4 MFMAs each, operands read two
+// k-steps ahead, and two of the 16 P / dS elements are placed between the MFMAs of each k-step.
+// Register i of a score block <-> row 8 (i/4) + 4 J + i%4 of the block; pk[j] packs registers 2j, 2j+1.
+template <bool C, bool S, bool P>
+__device__ __forceinline__ void kv_step(const KvLane &L, const bf16x8 kop[8], const bf16x8 vop[8], f32x16 dk[4],
+                                        f32x16 dv[4], const Blk &bc, const uint32_t pkc[8], const uint32_t skc[8],
+                                        const Blk &bs, f32x16 &sc, f32x16 &dp, const Blk &bp, const f32x16 &scp,
+                                        const f32x16 &dpp, uint32_t pkn[8], uint32_t skn[8])
+{
+    if (S) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            sc[i] = 0.f;
+            dp[i] = 0.f;
+        }
+    }
+    bf16x8 cg0, cq0, cg1, cq1, aq0, ag0, aq1, ag1;
+    if (C) {
+        cg0 = rd_cols(bc.g, L.trA, 0, 0);
+        cq0 = rd_cols(bc.q, L.trA, 0, 0);
+        cg1 = rd_cols(bc.g, L.trA, 0, 1);
+        cq1 = rd_cols(bc.q, L.trA, 0, 1);
+    }
+    if (S) {
+        aq0 = rd_rows(bs.q, L.rowA, 0);
+        ag0 = rd_rows(bs.g, L.rowA, 0);
+        aq1 = rd_rows(bs.q, L.rowA, 1);
+        ag1 = rd_rows(bs.g, L.rowA, 1);
+    }
+    float4 l4, d4;
+    if (P) {
+        l4 = *reinterpret_cast<const float4 *>(bp.lse + 4 * L.J);
+        d4 = *reinterpret_cast<const float4 *>(bp.dsum + 4 * L.J);
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        const int u = k >> 2, db = k & 3;
+        bf16x8 cg2 = cg0, cq2 = cq0, aq2 = aq0, ag2 = ag0;
+        if (k + 2 < 8) {
+            if (C) {
+                cg2 = rd_cols(bc.g, L.trA, (k + 2) >> 2, (k + 2) & 3);
+                cq2 = rd_cols(bc.q, L.trA, (k + 2) >> 2, (k + 2) & 3);
+            }
+            if (S) {
+                aq2 = rd_rows(bs.q, L.rowA, k + 2);
+                ag2 = rd_rows(bs.g, L.rowA, k + 2);
+            }
+        }
+        float4 l4n = l4, d4n = d4;
+        if (P && (k & 1) && k < 7) {
+            const int i4 = (k + 1) >> 1;
+            l4n = *reinterpret_cast<const float4 *>(bp.lse + 8 * i4 + 4 * L.J);
+            d4n = *reinterpret_cast<const float4 *>(bp.dsum + 8 * i4 + 4 * L.J);
+        }
+        if (C)
+            dv[db] = mfma32(cg0, half_op(pkc, u), dv[db]);
+        if (S)
+            sc = mfma32(aq0, kop[k], sc);
+        if (P) {
+            // registers 2k, 2k+1: rows 8 (k/2) + 4 J + 2 (k%2) + {0, 1}
+            const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dsv[4] = {d4.x, d4.y, d4.z, d4.w};
+            float p[2], ds[2];
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                const int i = 2 * k + e, r = i & 3;
+                const int row = bp.row0 + 8 * (i >> 2) + 4 * L.J + r;
+                const bool vis = bp.full || (uint32_t)(row - L.lo_row) < (uint32_t)L.span;
+                const float arg = fmaf(scp[i], L.sl, -lv[r] * kLog2e);
+                p[e] = exp2_fast(vis ? arg : kNegInf);
+                ds[e] = p[e] * (dpp[i] - dsv[r]);
+            }
+            pkn[k] = pack_bf16x2(p[0], p[1]);
+            skn[k] = pack_bf16x2(ds[0], ds[1]);
+            anchor(pkn[k]);
+            anchor(skn[k]);
+        }
+        if (C)
+            dk[db] = mfma32(cq0, half_op(skc, u), dk[db]);
+        if (S)
+            dp = mfma32(ag0, vop[k], dp);
+        sched_fence();
+        cg0 = cg1;
+        cq0 = cq1;
+        cg1 = cg2;
+        cq1 = cq2;
+        aq0 = aq1;
+        ag0 = ag1;
+        aq1 = aq2;
+        ag1 = ag2;
+        if (k & 1) {
+            l4 = l4n;
+            d4 = d4n;
+        }
+    }
+}
+
+// dK, dV of 128 keys of one (sequence, KV head): wave w owns keys kb0 + 32 w .. +31, whose K and V stay in
+// registers as the B operands of S = Q K^T and dP = dO V^T.  The loop runs over the query heads of the
+// group and, per head, over the 64-row query tiles that see any of the keys, staged in a three-stage
+// direct-to-LDS ring.  A wave works in 32-row blocks through a three-deep software pipeline: while the
+// MFMAs of S and dP [32 rows x 32 keys] of block j run (A operands: 16-B LDS reads of Q and dO rows),
+// so do those of dV^T += dO^T P and dK^T += Q^T dS [128 dims x 32 keys] of block j-2 (A operands:
+// transposed LDS reads), and P and dS of block j-1 are computed between them.  P and dS feed the B
+// operand from registers in the S register order.
+__global__ __launch_bounds__(kKvThreads) void bwd_dkdv_kernel(BwdArgs a, int nkt, int nunits)
+{
+    // XCD-aware order: block i runs on XCD i % 8, which takes a contiguous run of units ordered (KV
+    // head, key block, sequence): each XCD serves whole KV heads of every sequence (even load), and
+    // starts with the key blocks that see the most query rows (the first ones, under the causal mask);
+    // the key blocks of one sequence that run at the same time stream the same Q and dO tiles through
+    // the XCD's L2
+    const int per = gridDim.x / kXcds;
+    const int unit = (blockIdx.x % kXcds) * per + blockIdx.x / kXcds;
+    if (unit >= nunits)
+        return;
+    const int g = unit / (nkt * a.B), rem = unit % (nkt * a.B);
+    const int kt = rem / a.B, b = rem % a.B;
     const int q0 = a.cu_q[b], Lq = a.cu_q[b + 1] - q0;
     const int k0 = a.cu_k[b], Lk = a.cu_k[b + 1] - k0;
     const int kb0 = kt * kKeysPerWg;
     if (kb0 >= Lk)
         return;
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    const int n16 = lane & 15, g4 = lane >> 4;
-    const int kw = kb0 + kKeysPerWave * w;    // the wave's first key
-    const int key = kw + n16;                 // the lane's key (MFMA column)
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int n = lane & 31, J = lane >> 5;
+    const int kw = kb0 + kKeysPerWave * w; // the wave's first key
+    const int key = kw + n;                // the lane's key (MFMA column)
     const int diag = Lk - Lq;
 
-    __shared__ __attribute__((aligned(16))) char q_t[kQRows * kRowBytes];
-    __shared__ __attribute__((aligned(16))) char do_t[kQRows * kRowBytes];
-    __shared__ float lse_t[kQRows], dsum_t[kQRows];
-
-    // K^T and V^T as B operands: lane (key n16, group g4) holds dims 32 s + 8 g4 .. +8 of its key
-    const uint16_t *kg = static_cast<const uint16_t *>(a.k), *vg = static_cast<const uint16_t *>(a.v);
-    bf16x8 kop[4], vop[4];
+    KvLane L;
+    L.J = J;
+    L.lo_row = key >= Lk ? Lq : (a.causal ? key - diag : 0);
+    L.span = max(0, Lq - L.lo_row);
+    L.sl = a.scale_log2;
+    // A operand: row n, dims 16 s + 8 J at chunk 2 s + J; transposed reads: 16-lane group G16, index j
+    // addresses row 8 hf + 4 J + j/4 of a 16-row half, dims 32 db + 16 (G16 % 2) + 4 (j % 4)
+    L.rowA = n * kRowBytes + 16 * (J ^ swz(n & 15));
+    {
+        const int G16 = lane >> 4, j = lane & 15;
+        const int x = 2 * (G16 & 1) + ((j & 3) >> 1);
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-        uint4 kv = make_uint4(0, 0, 0, 0), vv = make_uint4(0, 0, 0, 0);
-        if (key < Lk) {
-            const size_t off = ((size_t)(k0 + key) * a.Hkv + g) * D + 32 * s + 8 * g4;
-            kv = ld16(kg + off);
-            vv = ld16(vg + off);
+        for (int hf = 0; hf < 2; ++hf) {
+            const int r = 8 * hf + 4 * J + (j >> 2);
+            L.trA[hf] = r * kRowBytes + 8 * (j & 1) + 16 * (x ^ swz(r));
         }
-        kop[s] = as_bf16x8(kv);
-        vop[s] = as_bf16x8(vv);
-    }
-    f32x4 dk[8], dv[8]; // [16 dims x 16 keys] blocks db: lane holds dims 16 db + 4 g4 + i of its key
-#pragma unroll
-    for (int db = 0; db < 8; ++db) {
-        dk[db] = f32x4{0.f, 0.f, 0.f, 0.f};
-        dv[db] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
 
-    // the first query row that sees key kb0
-    const int row_start = a.causal ? max(0, kb0 - diag) : 0;
-    const int qt_first = row_start / kQRows, nqt = (Lq + kQRows - 1) / kQRows;
-    const uint16_t *qg = static_cast<const uint16_t *>(a.q), *dog = static_cast<const uint16_t *>(a.dout);
-    // transposed-read addresses (dims 16 db + lane's column, rows 4 g4 .. +3 and 16 + 4 g4 .. +3)
-    const int trow_lo = 4 * g4 + (n16 >> 2), trow_hi = 16 + trow_lo;
-    const int tcol_chunk = (n16 & 3) >> 1, tcol_half = 8 * (n16 & 1);
+    // K and V as B operands: lane (key n, J) holds dims 16 s + 8 J .. +8
+    bf16x8 kop[8], vop[8];
+    {
+        const uint16_t *kg = static_cast<const uint16_t *>(a.k), *vg = static_cast<const uint16_t *>(a.v);
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+            uint4 kv = make_uint4(0, 0, 0, 0), vv = make_uint4(0, 0, 0, 0);
+            if (key < Lk) {
+                const size_t off = ((size_t)(k0 + key) * a.Hkv + g) * D + 16 * s + 8 * J;
+                kv = ld16(kg + off);
+                vv = ld16(vg + off);
+            }
+            kop[s] = as_bf16x8(kv);
+            vop[s] = as_bf16x8(vv);
+        }
+    }
+    f32x16 dk[4], dv[4]; // [128 dims x 32 keys] in blocks db of 32 dims: register i <-> dim 32 db + 8 (i/4) + 4 J + i%4
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            dk[db][i] = 0.f;
+            dv[db][i] = 0.f;
+        }
 
-    for (int hh = 0; hh < a.G; ++hh) {
-        const int h = g * a.G + hh;
-        for (int qt = qt_first; qt < nqt; ++qt) {
-            const int r0 = qt * kQRows;
-            __syncthreads(); // the previous tile is no longer read
-            stage_rows(q_t, qg, (size_t)q0 + r0, a.Hq, h, kQRows, Lq - r0, tid, 64 * kKvWaves);
-            stage_rows(do_t, dog, (size_t)q0 + r0, a.Hq, h, kQRows, Lq - r0, tid, 64 * kKvWaves);
-            if (tid < kQRows) {
-                const int r = r0 + tid;
-                lse_t[tid] = r < Lq ? a.lse[(size_t)(q0 + r) * a.Hq + h] * kLog2e : 0.f;
-                dsum_t[tid] = r < Lq ? a.dsum[(size_t)(q0 + r) * a.Hq + h] : 0.f;
-            }
-            __syncthreads();
+    QLoader ld;
+    {
+        const uint32_t row_bytes = (uint32_t)a.Hq * kRowBytes;
+        const uint32_t seq_bytes = (uint32_t)Lq * row_bytes; // rows past the sequence read as zero
+        ld.qrs = make_rsrc(static_cast<const uint16_t *>(a.q) + (size_t)q0 * a.Hq * D, seq_bytes);
+        ld.grs = make_rsrc(static_cast<const uint16_t *>(a.dout) + (size_t)q0 * a.Hq * D, seq_bytes);
+        ld.lrs = make_rsrc(a.lse + (size_t)q0 * a.Hq, (uint32_t)Lq * a.Hq * 4);
+        ld.drs = make_rsrc(a.dsum + (size_t)q0 * a.Hq, (uint32_t)Lq * a.Hq * 4);
+        ld.row_bytes = row_bytes;
+        ld.Hq = a.Hq;
+        ld.w = w;
+        ld.loff = (uint32_t)lane * a.Hq * 4;
+#pragma unroll
+        for (int p = 0; p < kQLoads; ++p) {
+            const int row = 4 * (kQLoads * w + p) + (lane >> 4);
+            ld.voff[p] = (uint32_t)row * row_bytes + 16 * ((lane & 15) ^ swz(row & 15));
+        }
+    }
 
-            // S and dP for the 2 row blocks of 16
-            f32x4 s[2], dp[2];
-#pragma unroll
-            for (int rb = 0; rb < 2; ++rb) {
-                s[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
-                dp[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
-                const int r = 16 * rb + n16;
-#pragma unroll
-                for (int st = 0; st < 4; ++st) {
-                    const uint32_t off = chunk_off(r, 4 * st + g4);
-                    s[rb] = mfma16(as_bf16x8(ld16(q_t + off)), kop[st], s[rb]);
-                    dp[rb] = mfma16(as_bf16x8(ld16(do_t + off)), vop[st], dp[rb]);
-                }
-            }
-            // P and dS: lane holds rows 16 rb + 4 g4 + i of its key
-            float p[2][4], ds[2][4];
-#pragma unroll
-            for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int rt = 16 * rb + 4 * g4 + i, row = r0 + rt;
-                    const bool vis = row < Lq && key < Lk && (!a.causal || key <= row + diag);
-                    const float pv = vis ? exp2_fast(fmaf(s[rb][i], a.scale_log2, -lse_t[rt])) : 0.f;
-                    p[rb][i] = pv;
-                    ds[rb][i] = pv * (dp[rb][i] - dsum_t[rt]);
-                }
-            // k-slot e of the row contraction <-> row 16 (e / 4) + 4 g4 + e % 4
-            const bf16x8 pop = as_bf16x8(make_uint4(pack_bf16x2(p[0][0], p[0][1]), pack_bf16x2(p[0][2], p[0][3]),
-                                                    pack_bf16x2(p[1][0], p[1][1]), pack_bf16x2(p[1][2], p[1][3])));
-            const bf16x8 dsop = as_bf16x8(make_uint4(pack_bf16x2(ds[0][0], ds[0][1]), pack_bf16x2(ds[0][2], ds[0][3]),
-                                                     pack_bf16x2(ds[1][0], ds[1][1]), pack_bf16x2(ds[1][2], ds[1][3])));
-#pragma unroll
-            for (int db = 0; db < 8; ++db) {
-                const int c = 2 * db + tcol_chunk;
-                const uint32_t lo = chunk_off(trow_lo, c) + tcol_half, hi = chunk_off(trow_hi, c) + tcol_half;
-                const uint2 glo = lds_read_tr(do_t + lo), ghi = lds_read_tr(do_t + hi);
-                dv[db] = mfma16(as_bf16x8(make_uint4(glo.x, glo.y, ghi.x, ghi.y)), pop, dv[db]);
-                const uint2 qlo = lds_read_tr(q_t + lo), qhi = lds_read_tr(q_t + hi);
-                dk[db] = mfma16(as_bf16x8(make_uint4(qlo.x, qlo.y, qhi.x, qhi.y)), dsop, dk[db]);
-            }
+    // tiles: for every query head of the group, the 64-row tiles from the first that sees key kb0
+    const int qt_first = (a.causal ? max(0, kb0 - diag) : 0) / kQRows;
+    const int nq = (Lq + kQRows - 1) / kQRows - qt_first;
+    const int ntiles = nq > 0 ? a.G * nq : 0;
+    auto tile_row0 = [&](int t) { return (qt_first + t % nq) * kQRows; };
+    auto tile_head = [&](int t) { return g * a.G + t / nq; };
+    auto blk = [&](int j) {
+        const int t = j >> 1, rb = j & 1, st = t % kQStages;
+        Blk x;
+        x.q = q_ring[st].q + rb * 32 * kRowBytes;
+        x.g = q_ring[st].g + rb * 32 * kRowBytes;
+        x.lse = q_ring[st].lse + 32 * rb;
+        x.dsum = q_ring[st].dsum + 32 * rb;
+        x.row0 = tile_row0(t) + 32 * rb;
+        x.full = x.row0 + 32 <= Lq && kw + kKeysPerWave <= Lk &&
+                 (!a.causal || kw + kKeysPerWave - 1 - diag <= x.row0);
+        return x;
+    };
+    // tile t is loaded one tile ahead; its stage is read until the step that finishes its blocks
+    auto next_tile = [&](int t) {
+        wait_vmcnt<0>();
+        barrier(); // tile t is in LDS for every wave; every wave is done with tile t - 2
+        if (t + 1 < ntiles)
+            ld.issue((t + 1) % kQStages, tile_row0(t + 1), tile_head(t + 1));
+    };
+
+    if (ntiles > 0) {
+        const int nb = 2 * ntiles;
+        f32x16 sc, dp, scp, dpp;
+        uint32_t pka[8], ska[8], pkb[8], skb[8];
+        ld.issue(0, tile_row0(0), tile_head(0));
+        // steps 0 and 1: S of blocks 0, 1; P of block 0
+        next_tile(0);
+        {
+            const Blk b0 = blk(0), b1 = blk(1);
+            kv_step<false, true, false>(L, kop, vop, dk, dv, b0, pka, ska, b0, scp, dpp, b0, sc, dp, pkb, skb);
+            kv_step<false, true, true>(L, kop, vop, dk, dv, b0, pka, ska, b1, sc, dp, b0, scp, dpp, pkb, skb);
+        }
+        // step j (2 <= j < nb): C of block j-2, S of block j, P of block j-1; pkb/skb hold P, dS of block
+        // j-2 at its start; sc, dp the scores of block j-1
+        for (int j = 2; j < nb; j += 2) {
+            next_tile(j >> 1);
+            const Blk bm2 = blk(j - 2), bm1 = blk(j - 1), bj = blk(j), bj1 = blk(j + 1);
+            kv_step<true, true, true>(L, kop, vop, dk, dv, bm2, pkb, skb, bj, scp, dpp, bm1, sc, dp, pka, ska);
+            kv_step<true, true, true>(L, kop, vop, dk, dv, bm1, pka, ska, bj1, sc, dp, bj, scp, dpp, pkb, skb);
+        }
+        // steps nb and nb+1: C of blocks nb-2, nb-1; P of block nb-1
+        {
+            const Blk bm2 = blk(nb - 2), bm1 = blk(nb - 1);
+            kv_step<true, false, true>(L, kop, vop, dk, dv, bm2, pkb, skb, bm2, scp, dpp, bm1, sc, dp, pka, ska);
+            kv_step<true, false, false>(L, kop, vop, dk, dv, bm1, pka, ska, bm1, scp, dpp, bm1, sc, dp, pkb, skb);
         }
     }
 
     if (key >= Lk)
         return;
-    uint16_t *dkg = static_cast<uint16_t *>(a.dk) + ((size_t)(k0 + key) * a.Hkv + g) * D + 4 * g4;
-    uint16_t *dvg = static_cast<uint16_t *>(a.dv) + ((size_t)(k0 + key) * a.Hkv + g) * D + 4 * g4;
+    uint16_t *dkg = static_cast<uint16_t *>(a.dk) + ((size_t)(k0 + key) * a.Hkv + g) * D + 4 * J;
+    uint16_t *dvg = static_cast<uint16_t *>(a.dv) + ((size_t)(k0 + key) * a.Hkv + g) * D + 4 * J;
 #pragma unroll
-    for (int db = 0; db < 8; ++db) {
-        uint2 pk, pv;
-        pk.x = pack_bf16x2(dk[db][0] * a.scale, dk[db][1] * a.scale);
-        pk.y = pack_bf16x2(dk[db][2] * a.scale, dk[db][3] * a.scale);
-        pv.x = pack_bf16x2(dv[db][0], dv[db][1]);
-        pv.y = pack_bf16x2(dv[db][2], dv[db][3]);
-        *reinterpret_cast<uint2 *>(dkg + 16 * db) = pk;
-        *reinterpret_cast<uint2 *>(dvg + 16 * db) = pv;
-    }
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            uint2 pk, pv;
+            pk.x = pack_bf16x2(dk[db][4 * r] * a.scale, dk[db][4 * r + 1] * a.scale);
+            pk.y = pack_bf16x2(dk[db][4 * r + 2] * a.scale, dk[db][4 * r + 3] * a.scale);
+            pv.x = pack_bf16x2(dv[db][4 * r], dv[db][4 * r + 1]);
+            pv.y = pack_bf16x2(dv[db][4 * r + 2], dv[db][4 * r + 3]);
+            *reinterpret_cast<uint2 *>(dkg + 32 * db + 8 * r) = pk;
+            *reinterpret_cast<uint2 *>(dvg + 32 * db + 8 * r) = pv;
+        }
 }
 
 // ------------------------------------------------------------------ dQ
@@ -367,13 +577,15 @@ hipError_t launch_prefill_bwd(const BwdArgs &a, hipStream_t stream)
         hipLaunchKernelGGL(bwd_prep_kernel, dim3((unsigned)((slots + 15) / 16)), dim3(256), 0, stream, a);
     const int nkt = (a.max_k + kKeysPerWg - 1) / kKeysPerWg;
     const long units_kv = (long)a.Hkv * a.B * nkt;
+    const long blocks_kv = (units_kv + kXcds - 1) / kXcds * kXcds;
     const int NH = heads_per_wg_bwd(a.G), RB = kDqWaves / NH;
     const int nqt = (a.max_q + 32 * RB - 1) / (32 * RB);
     const long units_q = (long)a.Hkv * (a.G / NH) * a.B * nqt;
-    if (units_kv > 0x7fffffff || units_q > 0x7fffffff)
+    if (blocks_kv > 0x7fffffff || units_q > 0x7fffffff)
         return hipErrorInvalidValue;
     if (units_kv > 0)
-        hipLaunchKernelGGL(bwd_dkdv_kernel, dim3((unsigned)units_kv), dim3(64 * kKvWaves), 0, stream, a, nkt);
+        hipLaunchKernelGGL(bwd_dkdv_kernel, dim3((unsigned)blocks_kv), dim3(kKvThreads), 0, stream, a, nkt,
+                           (int)units_kv);
     if (units_q > 0)
         hipLaunchKernelGGL(bwd_dq_kernel, dim3((unsigned)units_q), dim3(64 * kDqWaves), 0, stream, a, NH, RB, nqt);
     return hipGetLastError();

@@ -40,6 +40,7 @@
 // branched over when every row of the wave skips it) and never raises the running max.
 #include "kcommon.h"
 #include "launch.h"
+#include "lds_dma.h"
 
 namespace attn {
 namespace {
@@ -51,11 +52,7 @@ constexpr int kBN = 64;                         // keys per tile
 constexpr int kTileChunks = kBN * D / 8;        // 16-B chunks in one K (or V) tile
 constexpr int kLoadsPerWave = kTileChunks / kThreads; // 1-KB load instructions per wave per tile
 constexpr float kSlack = 8.f;
-constexpr int kBufWord3 = 0x00020000;           // raw buffer resource word 3 (gfx9 family)
 constexpr int kXcds = 8;
-
-typedef short i16x4 __attribute__((ext_vector_type(4)));
-typedef int i32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kStages = 2;
 
@@ -70,64 +67,6 @@ template <int ST> __device__ __forceinline__ uint4 *kbuf()
 template <int ST> __device__ __forceinline__ uint4 *vbuf()
 {
     return ST == 0 ? v_st0 : v_st1;
-}
-
-// XOR swizzle of the 16 chunk slots of a 256-B LDS row.
-__device__ __forceinline__ int swz(int r)
-{
-    return ((r & 1) ? 10 : 0) ^ ((r & 2) ? 4 : 0) ^ ((r & 4) ? 1 : 0) ^ ((r & 8) ? 2 : 0);
-}
-
-// s_waitcnt immediates (gfx9 layout: vmcnt [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8]).
-constexpr int wait_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
-
-__device__ __forceinline__ void compiler_fence() { asm volatile("" ::: "memory"); }
-
-// Workgroup barrier without a memory-model fence: the caller has already waited for what it needs.
-__device__ __forceinline__ void barrier()
-{
-    compiler_fence();
-    __builtin_amdgcn_s_barrier();
-    compiler_fence();
-}
-
-template <int N>
-__device__ __forceinline__ void wait_vmcnt()
-{
-    compiler_fence();
-    __builtin_amdgcn_s_waitcnt(wait_vm(N));
-    compiler_fence();
-}
-
-__device__ __forceinline__ uint2 lds_read_tr(const char *p)
-{
-    const i16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4 *)(p));
-    return __builtin_bit_cast(uint2, r);
-}
-
-// Raw buffer resource: base address, no stride, num_records bytes, gfx9 word 3.
-__device__ __forceinline__ i32x4 make_rsrc(const void *base, uint32_t num_records)
-{
-    const uint64_t a = reinterpret_cast<uint64_t>(base);
-    return i32x4{(int)(uint32_t)a, (int)(uint32_t)(a >> 32), (int)num_records, kBufWord3};
-}
-
-// LDS byte address of a shared-memory pointer.
-__device__ __forceinline__ uint32_t lds_addr(const void *p)
-{
-    return (uint32_t)(uintptr_t)((__attribute__((address_space(3))) const void *)(p));
-}
-
-// One 16-byte-per-lane buffer load written straight to LDS: lane l's data lands at lds + 16 l.  Written
-// as inline asm so that the compiler does not fold it into its own wait bookkeeping (which cannot tell
-// the LDS stages apart and would drain every load in flight before each LDS read); the loads return
-// no registers, and every wait for them is explicit (wait_vmcnt).
-__device__ __forceinline__ void dma16(uint32_t lds, uint32_t voff, i32x4 rsrc, uint32_t soff)
-{
-    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
-                 :
-                 : "s"(lds), "v"(voff), "s"(rsrc), "s"(soff)
-                 : "memory");
 }
 
 struct Loader {
@@ -181,13 +120,6 @@ __device__ __forceinline__ void mask_tile(f32x16 sc[2], int limit_minus_kb, int 
             if (32 * kk + 8 * (i / 4) + 4 * J + (i % 4) >= limit_minus_kb)
                 sc[kk][i] = kNegInf;
 }
-
-// Keeps a computed value at this point of the instruction stream (the compiler would otherwise sink it
-// to its first use and undo the interleaving below).
-__device__ __forceinline__ void anchor(uint32_t v) { asm volatile("" ::"v"(v)); }
-__device__ __forceinline__ void anchor(float v) { asm volatile("" ::"v"(v)); }
-// No instruction may be scheduled across this point.
-__device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
 
 struct IterCtx {
     int niter, Lk;

@@ -116,6 +116,8 @@ def test_backward_validation(lib):
     assert _backward(lib, D=64) == UNSUPPORTED
     assert _backward(lib, dt=_lib.ATTN_F32) == UNSUPPORTED
     assert _backward(lib, B=1 << 16, mq=1 << 12, Hq=8) == UNSUPPORTED
+    assert _backward(lib, mq=1 << 17, Hq=64, Hkv=8) == UNSUPPORTED
+    assert _backward(lib, mk=1 << 20, Hq=8, Hkv=8) == UNSUPPORTED
     assert _backward(lib, lse=None) == INVALID
     assert _backward(lib, dv=None) == INVALID
     assert _backward(lib, wsb=2 * 10 * 8 * 4 - 1) == WORKSPACE
