@@ -133,8 +133,8 @@ attn_status_t attn_smallseq_cross(const void *q, const void *k, const void *v, c
  *   max_seqlen_q / max_seqlen_k, causal and scale as for the forward call that produced o and lse.
  *   lse: fp32 [tq, Hq], the forward's natural-log LSE (-inf for rows with no visible key).
  *   workspace: at least attn_prefill_varlen_backward_workspace_size(B, max_seqlen_q, Hq) bytes
- *   (B * max_seqlen_q * Hq * 4) of device memory owned by the caller; no initialisation needed; it
- *   receives rowsum(dout * o) per (token, query head).  dq, dk, dv are fully written (rows with no
+ *   (B * max_seqlen_q * Hq * 8) of device memory owned by the caller; no initialisation needed; it
+ *   receives rowsum(dout * o) and lse * log2(e) per (token, query head).  dq, dk, dv are fully written (rows with no
  *   visible key and keys no query sees get 0).
  *   Supported: bf16 with D = 128, B * max_seqlen_q * Hq < 2^31, max_seqlen_q * Hq * D * 2 < 2^31 and
  *   max_seqlen_k * Hkv * D * 2 < 2^31 (else ATTN_ERR_UNSUPPORTED).

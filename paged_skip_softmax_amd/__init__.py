@@ -83,7 +83,7 @@ def attn_prefill_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_s
 
 
 def attn_prefill_varlen_backward_workspace_size(B: int, max_seqlen_q: int, Hq: int) -> int:
-    """Workspace bytes of the prefill backward (the per-row rowsum(dO * O))."""
+    """Workspace bytes of the prefill backward (per row: rowsum(dO * O) and lse * log2(e))."""
     return int(_lib.load().attn_prefill_varlen_backward_workspace_size(B, max_seqlen_q, Hq))
 
 

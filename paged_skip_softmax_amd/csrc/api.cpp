@@ -157,8 +157,8 @@ size_t attn_prefill_varlen_backward_workspace_size(int32_t B, int32_t max_seqlen
 {
     if (B <= 0 || max_seqlen_q <= 0 || Hq <= 0)
         return 0;
-    // rowsum(dO * O) per (token, query head); B * max_seqlen_q bounds the token count
-    return (size_t)B * max_seqlen_q * Hq * sizeof(float);
+    // rowsum(dO * O) and lse * log2(e) per (token, query head); B * max_seqlen_q bounds the token count
+    return 2 * (size_t)B * max_seqlen_q * Hq * sizeof(float);
 }
 
 attn_status_t attn_prefill_varlen_backward(attn_dtype_t dtype, const void *q, const void *k, const void *v,
@@ -200,6 +200,7 @@ attn_status_t attn_prefill_varlen_backward(attn_dtype_t dtype, const void *q, co
     a.dout = dout;
     a.lse = lse;
     a.dsum = static_cast<float *>(workspace);
+    a.lse2 = a.dsum + (size_t)B * max_seqlen_q * Hq;
     a.cu_q = cu_seqlens_q;
     a.cu_k = cu_seqlens_k;
     a.B = B;

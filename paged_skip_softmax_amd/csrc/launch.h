@@ -64,6 +64,7 @@ struct BwdArgs {
     const void *q, *k, *v, *o, *dout;
     const float *lse;          // [tq, Hq] natural log, from the forward
     float *dsum;               // [tq, Hq] workspace: rowsum(dO * O)
+    float *lse2;               // [tq, Hq] workspace: lse * log2(e)
     const int32_t *cu_q, *cu_k;
     int B, max_q, max_k, Hq, Hkv, G;
     bool causal;

@@ -6,7 +6,7 @@
 //   dV = P^T dO,  dK = scale dS^T Q,  dQ = scale dS K         (dK, dV summed over a KV head's group)
 //
 // Three kernels, no atomics:
-//  * bwd_prep: Dsum per (token, query head), fp32, into the caller's workspace.
+//  * bwd_prep: Dsum and lse * log2(e) per (token, query head), fp32, into the caller's workspace.
 //  * bwd_dkdv: a workgroup of 4 waves owns 64 keys of one (sequence, KV head), 16 keys per wave, whose
 //    K and V stay in registers as MFMA B operands; it walks every query tile of 32 rows that sees any
 //    of its keys, for every query head of the group.  The workgroup stages each Q and dO tile in LDS
@@ -46,7 +46,7 @@ __device__ __forceinline__ void stage_rows(char *tile, const uint16_t *src, size
     }
 }
 
-// ------------------------------------------------------------------ Dsum
+// ------------------------------------------------------------------ Dsum and lse in log2 units
 
 __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdArgs a)
 {
@@ -78,6 +78,8 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdArgs a)
     s += __shfl_xor(s, 1);
     if (live && c == 0)
         a.dsum[row] = s;
+    if (live && c == 1)
+        a.lse2[row] = a.lse[row] * kLog2e;
 }
 
 // ------------------------------------------------------------------ dK, dV
@@ -92,7 +94,7 @@ constexpr int kQTileBytes = kQRows * kRowBytes;     // 16 KB
 constexpr int kQLoads = kQTileBytes / 1024 / kKvWaves; // 1-KB direct-to-LDS loads per wave per tile
 constexpr int kQStages = 3;
 
-// One stage of the Q / dO ring: the two tiles (swizzled rows) and the rows' LSE and Dsum.
+// One stage of the Q / dO ring: the two tiles (swizzled rows) and the rows' lse * log2(e) and Dsum.
 struct alignas(1024) QStage {
     char q[kQTileBytes];
     char g[kQTileBytes];
@@ -103,7 +105,7 @@ __shared__ QStage q_ring[kQStages];
 
 // What one lane needs to issue the direct-to-LDS loads of a Q / dO tile.
 struct QLoader {
-    i32x4 qrs, grs, lrs, drs;  // buffer resources of Q, dO (from head 0 of the sequence), lse, Dsum
+    i32x4 qrs, grs, lrs, drs;  // buffer resources of Q, dO (from head 0 of the sequence), lse2, Dsum
     uint32_t voff[kQLoads];    // lane's byte offsets inside a tile of rows (4-row blocks of the wave)
     uint32_t loff;             // lane's byte offset of its LSE / Dsum row
     uint32_t row_bytes;        // global bytes between consecutive rows of one head
@@ -169,7 +171,7 @@ struct KvLane {
 // One pipeline step of a wave over 32-row blocks: with C, dV^T += dO^T P and dK^T += Q^T dS of an
 // older block (bc; its packed P and dS in pkc, skc); with S, S = Q K^T and dP = dO V^T of a new block
 // (bs) into sc, dp; with P, P = exp(scale S - lse) and dS = P (dP - Dsum) of the block in between (bp;
-// its scores scp, dpp) into pkn, skn.  The 8 k-steps issue up to 4 MFMAs each, operands read two
+// its scores scp, dpp) into pkn, skn, zero where the row does not see the key.  The 8 k-steps issue up to 4 MFMAs each, operands read two
 // k-steps ahead, and two of the 16 P / dS elements are placed between the MFMAs of each k-step.
 // Register i of a score block <-> row 8 (i/4) + 4 J + i%4 of the block; pk[j] packs registers 2j, 2j+1.
 template <bool C, bool S, bool P>
@@ -234,10 +236,7 @@ __device__ __forceinline__ void kv_step(const KvLane &L, const bf16x8 kop[8], co
 #pragma unroll
             for (int e = 0; e < 2; ++e) {
                 const int i = 2 * k + e, r = i & 3;
-                const int row = bp.row0 + 8 * (i >> 2) + 4 * L.J + r;
-                const bool vis = bp.full || (uint32_t)(row - L.lo_row) < (uint32_t)L.span;
-                const float arg = fmaf(scp[i], L.sl, -lv[r] * kLog2e);
-                p[e] = exp2_fast(vis ? arg : kNegInf);
+                p[e] = exp2_fast(fmaf(scp[i], L.sl, -lv[r]));
                 ds[e] = p[e] * (dpp[i] - dsv[r]);
             }
             pkn[k] = pack_bf16x2(p[0], p[1]);
@@ -261,6 +260,24 @@ __device__ __forceinline__ void kv_step(const KvLane &L, const bf16x8 kop[8], co
         if (k & 1) {
             l4 = l4n;
             d4 = d4n;
+        }
+    }
+    // Blocks that cross the causal diagonal or an end of the sequence: zero the entries whose row does
+    // not see the lane's key (their values above may be anything, infinities and NaN included, since
+    // rows past the sequence and keys past the diagonal were not kept out of the exponentials).
+    if (P && !bp.full) {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            uint32_t m = 0;
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                const int i = 2 * k + e;
+                const int row = bp.row0 + 8 * (i >> 2) + 4 * L.J + (i & 3);
+                if ((uint32_t)(row - L.lo_row) < (uint32_t)L.span)
+                    m |= 0xffffu << (16 * e);
+            }
+            pkn[k] &= m;
+            skn[k] &= m;
         }
     }
 }
@@ -347,7 +364,7 @@ __global__ __launch_bounds__(kKvThreads) void bwd_dkdv_kernel(BwdArgs a, int nkt
         const uint32_t seq_bytes = (uint32_t)Lq * row_bytes; // rows past the sequence read as zero
         ld.qrs = make_rsrc(static_cast<const uint16_t *>(a.q) + (size_t)q0 * a.Hq * D, seq_bytes);
         ld.grs = make_rsrc(static_cast<const uint16_t *>(a.dout) + (size_t)q0 * a.Hq * D, seq_bytes);
-        ld.lrs = make_rsrc(a.lse + (size_t)q0 * a.Hq, (uint32_t)Lq * a.Hq * 4);
+        ld.lrs = make_rsrc(a.lse2 + (size_t)q0 * a.Hq, (uint32_t)Lq * a.Hq * 4);
         ld.drs = make_rsrc(a.dsum + (size_t)q0 * a.Hq, (uint32_t)Lq * a.Hq * 4);
         ld.row_bytes = row_bytes;
         ld.Hq = a.Hq;
@@ -364,51 +381,67 @@ __global__ __launch_bounds__(kKvThreads) void bwd_dkdv_kernel(BwdArgs a, int nkt
     const int qt_first = (a.causal ? max(0, kb0 - diag) : 0) / kQRows;
     const int nq = (Lq + kQRows - 1) / kQRows - qt_first;
     const int ntiles = nq > 0 ? a.G * nq : 0;
-    auto tile_row0 = [&](int t) { return (qt_first + t % nq) * kQRows; };
-    auto tile_head = [&](int t) { return g * a.G + t / nq; };
-    auto blk = [&](int j) {
-        const int t = j >> 1, rb = j & 1, st = t % kQStages;
+    // a tile's place: ring stage, first row, query head (advanced one tile at a time)
+    struct Tile {
+        int st, row0, h;
+    };
+    const int row_first = qt_first * kQRows, row_end = (qt_first + nq) * kQRows;
+    auto advance = [&](Tile t) {
+        t.st = t.st == kQStages - 1 ? 0 : t.st + 1;
+        t.row0 += kQRows;
+        if (t.row0 == row_end) {
+            t.row0 = row_first;
+            ++t.h;
+        }
+        return t;
+    };
+    auto blk = [&](const Tile &t, int rb) {
         Blk x;
-        x.q = q_ring[st].q + rb * 32 * kRowBytes;
-        x.g = q_ring[st].g + rb * 32 * kRowBytes;
-        x.lse = q_ring[st].lse + 32 * rb;
-        x.dsum = q_ring[st].dsum + 32 * rb;
-        x.row0 = tile_row0(t) + 32 * rb;
+        x.q = q_ring[t.st].q + rb * 32 * kRowBytes;
+        x.g = q_ring[t.st].g + rb * 32 * kRowBytes;
+        x.lse = q_ring[t.st].lse + 32 * rb;
+        x.dsum = q_ring[t.st].dsum + 32 * rb;
+        x.row0 = t.row0 + 32 * rb;
         x.full = x.row0 + 32 <= Lq && kw + kKeysPerWave <= Lk &&
                  (!a.causal || kw + kKeysPerWave - 1 - diag <= x.row0);
         return x;
     };
-    // tile t is loaded one tile ahead; its stage is read until the step that finishes its blocks
-    auto next_tile = [&](int t) {
+    // tile t (in `cur`) was loaded one tile ahead; its stage is read until the step that finishes its
+    // blocks, two tiles later
+    auto next_tile = [&](const Tile &cur, int t) {
         wait_vmcnt<0>();
         barrier(); // tile t is in LDS for every wave; every wave is done with tile t - 2
-        if (t + 1 < ntiles)
-            ld.issue((t + 1) % kQStages, tile_row0(t + 1), tile_head(t + 1));
+        if (t + 1 < ntiles) {
+            const Tile nx = advance(cur);
+            ld.issue(nx.st, nx.row0, nx.h);
+        }
     };
 
     if (ntiles > 0) {
-        const int nb = 2 * ntiles;
         f32x16 sc, dp, scp, dpp;
         uint32_t pka[8], ska[8], pkb[8], skb[8];
-        ld.issue(0, tile_row0(0), tile_head(0));
+        Tile prev{0, row_first, g * a.G};
+        ld.issue(prev.st, prev.row0, prev.h);
         // steps 0 and 1: S of blocks 0, 1; P of block 0
-        next_tile(0);
+        next_tile(prev, 0);
         {
-            const Blk b0 = blk(0), b1 = blk(1);
+            const Blk b0 = blk(prev, 0), b1 = blk(prev, 1);
             kv_step<false, true, false>(L, kop, vop, dk, dv, b0, pka, ska, b0, scp, dpp, b0, sc, dp, pkb, skb);
             kv_step<false, true, true>(L, kop, vop, dk, dv, b0, pka, ska, b1, sc, dp, b0, scp, dpp, pkb, skb);
         }
-        // step j (2 <= j < nb): C of block j-2, S of block j, P of block j-1; pkb/skb hold P, dS of block
-        // j-2 at its start; sc, dp the scores of block j-1
-        for (int j = 2; j < nb; j += 2) {
-            next_tile(j >> 1);
-            const Blk bm2 = blk(j - 2), bm1 = blk(j - 1), bj = blk(j), bj1 = blk(j + 1);
+        // tile t: step 2t runs C of block 2t-2, S of block 2t, P of block 2t-1; step 2t+1 one block later.
+        // At its start pkb/skb hold P, dS of block 2t-2 and sc, dp the scores of block 2t-1.
+        for (int t = 1; t < ntiles; ++t) {
+            const Tile cur = advance(prev);
+            next_tile(cur, t);
+            const Blk bm2 = blk(prev, 0), bm1 = blk(prev, 1), bj = blk(cur, 0), bj1 = blk(cur, 1);
             kv_step<true, true, true>(L, kop, vop, dk, dv, bm2, pkb, skb, bj, scp, dpp, bm1, sc, dp, pka, ska);
             kv_step<true, true, true>(L, kop, vop, dk, dv, bm1, pka, ska, bj1, sc, dp, bj, scp, dpp, pkb, skb);
+            prev = cur;
         }
-        // steps nb and nb+1: C of blocks nb-2, nb-1; P of block nb-1
+        // the last two steps: C of the last two blocks; P of the last block
         {
-            const Blk bm2 = blk(nb - 2), bm1 = blk(nb - 1);
+            const Blk bm2 = blk(prev, 0), bm1 = blk(prev, 1);
             kv_step<true, false, true>(L, kop, vop, dk, dv, bm2, pkb, skb, bm2, scp, dpp, bm1, sc, dp, pka, ska);
             kv_step<true, false, false>(L, kop, vop, dk, dv, bm1, pka, ska, bm1, scp, dpp, bm1, sc, dp, pkb, skb);
         }
@@ -435,13 +468,149 @@ __global__ __launch_bounds__(kKvThreads) void bwd_dkdv_kernel(BwdArgs a, int nkt
 // ------------------------------------------------------------------ dQ
 
 constexpr int kDqWaves = 4;
-constexpr int kKeysPerTile = 32;
+constexpr int kDqThreads = 64 * kDqWaves;
+constexpr int kKTile = 64;                            // keys per staged tile
+constexpr int kKTileBytes = kKTile * kRowBytes;       // 16 KB
+constexpr int kKLoads = kKTileBytes / 1024 / kDqWaves; // 1-KB direct-to-LDS loads per wave per tile
+constexpr int kKStages = 3;
 
-__global__ __launch_bounds__(64 * kDqWaves) void bwd_dq_kernel(BwdArgs a, int NH, int RB, int nqt)
+// One stage of the K / V ring (swizzled rows).
+struct alignas(1024) KStage {
+    char k[kKTileBytes];
+    char v[kKTileBytes];
+};
+__shared__ KStage k_ring[kKStages];
+
+struct KLoader {
+    i32x4 krs, vrs;          // buffer resources of K, V (the sequence's rows of one KV head)
+    uint32_t voff[kKLoads];  // lane's byte offsets inside a tile of rows (4-row blocks of the wave)
+    uint32_t tile_bytes;     // global bytes between consecutive tiles
+    int w;
+
+    // keys [64 t, 64 t + 64) into stage st (keys past the sequence read as zero)
+    __device__ __forceinline__ void issue(int st, int t) const
+    {
+        const uint32_t soff = (uint32_t)t * tile_bytes;
+        const uint32_t wk = lds_addr(k_ring[st].k) + w * (kKLoads * 1024);
+        const uint32_t wv = lds_addr(k_ring[st].v) + w * (kKLoads * 1024);
+#pragma unroll
+        for (int p = 0; p < kKLoads; ++p) {
+            dma16(wk + p * 1024, voff[p], krs, soff);
+            dma16(wv + p * 1024, voff[p], vrs, soff);
+        }
+    }
+};
+
+// A 32-key block of a staged tile: its K and V rows and its first key.
+struct KBlk {
+    const char *k, *v;
+    int kb;
+    bool full; // every row of the wave sees every key of the block
+};
+
+// Per-lane constants of the dQ wave.
+struct QLane {
+    uint32_t rowA, trA[2];
+    int J;
+    int kend_row;     // the lane's row sees keys [0, kend_row) (0 for rows past the sequence)
+    float sl, lse2, dsum;
+};
+
+// One pipeline step of a dQ wave over 32-key blocks: with C, dQ^T += K^T dS^T of an older block (bc;
+// its packed dS^T in skc); with S, S^T = K Q^T and dP^T = V dO^T of a new block (bs) into sc, dp; with
+// P, dS^T = P (dP - Dsum), P = exp(scale S - lse), of the block in between (bp; its scores scp, dpp) into
+// skn, zero where the row does not see the key.  Register i of a score block <-> key
+// 8 (i/4) + 4 J + i%4 of the block; skn[j] packs registers 2j, 2j+1.
+template <bool C, bool S, bool P>
+__device__ __forceinline__ void q_step(const QLane &L, const bf16x8 qop[8], const bf16x8 gop[8], f32x16 dq[4],
+                                       const KBlk &bc, const uint32_t skc[8], const KBlk &bs, f32x16 &sc, f32x16 &dp,
+                                       const KBlk &bp, const f32x16 &scp, const f32x16 &dpp, uint32_t skn[8])
 {
-    const int unit = blockIdx.x;
+    if (S) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            sc[i] = 0.f;
+            dp[i] = 0.f;
+        }
+    }
+    bf16x8 ck0, ck1, ak0, av0, ak1, av1;
+    if (C) {
+        ck0 = rd_cols(bc.k, L.trA, 0, 0);
+        ck1 = rd_cols(bc.k, L.trA, 0, 1);
+    }
+    if (S) {
+        ak0 = rd_rows(bs.k, L.rowA, 0);
+        av0 = rd_rows(bs.v, L.rowA, 0);
+        ak1 = rd_rows(bs.k, L.rowA, 1);
+        av1 = rd_rows(bs.v, L.rowA, 1);
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        const int u = k >> 2, db = k & 3;
+        bf16x8 ck2 = ck0, ak2 = ak0, av2 = av0;
+        if (k + 2 < 8) {
+            if (C)
+                ck2 = rd_cols(bc.k, L.trA, (k + 2) >> 2, (k + 2) & 3);
+            if (S) {
+                ak2 = rd_rows(bs.k, L.rowA, k + 2);
+                av2 = rd_rows(bs.v, L.rowA, k + 2);
+            }
+        }
+        if (S)
+            sc = mfma32(ak0, qop[k], sc);
+        if (P) {
+            float d[2];
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                const int i = 2 * k + e;
+                const float p = exp2_fast(fmaf(scp[i], L.sl, -L.lse2));
+                d[e] = p * (dpp[i] - L.dsum);
+            }
+            skn[k] = pack_bf16x2(d[0], d[1]);
+            anchor(skn[k]);
+        }
+        if (C)
+            dq[db] = mfma32(ck0, half_op(skc, u), dq[db]);
+        if (S)
+            dp = mfma32(av0, gop[k], dp);
+        sched_fence();
+        ck0 = ck1;
+        ck1 = ck2;
+        ak0 = ak1;
+        av0 = av1;
+        ak1 = ak2;
+        av1 = av2;
+    }
+    if (P && !bp.full) {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            uint32_t m = 0;
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                const int i = 2 * k + e;
+                if (bp.kb + 8 * (i >> 2) + 4 * L.J + (i & 3) < L.kend_row)
+                    m |= 0xffffu << (16 * e);
+            }
+            skn[k] &= m;
+        }
+    }
+}
+
+// dQ of 32 query rows per wave: the forward's work split (4 waves, NH query heads of one KV head's group
+// times 4 / NH blocks of 32 rows; the group's heads share each K / V tile in LDS) and XCD-aware order.
+// Q^T and dO^T of the wave's rows stay in registers as the B operands; K and V tiles of 64 keys stream
+// through a three-stage direct-to-LDS ring.  Per 32-key block a wave computes S^T = K Q^T and
+// dP^T = V dO^T (A operands: 16-B LDS reads of K and V rows), dS^T, and dQ^T += K^T dS^T (A operand:
+// transposed LDS reads of K), in the three-deep block pipeline of the dK / dV kernel.
+__global__ __launch_bounds__(kDqThreads) void bwd_dq_kernel(BwdArgs a, int NH, int RB, int nqt, int nunits)
+{
+    const int per = gridDim.x / kXcds;
+    const int unit = (blockIdx.x % kXcds) * per + blockIdx.x / kXcds;
+    if (unit >= nunits)
+        return;
     const int hchunks = a.G / NH;
-    const int qt = nqt - 1 - unit % nqt, b = (unit / nqt) % a.B, gh = unit / (nqt * a.B);
+    const int gh = unit / (a.B * nqt), rem = unit % (a.B * nqt);
+    const int b = rem / nqt, qt = nqt - 1 - rem % nqt;
     const int g = gh / hchunks, hc = gh % hchunks;
     const int rows_wg = 32 * RB;
     const int q0 = a.cu_q[b], Lq = a.cu_q[b + 1] - q0;
@@ -449,98 +618,113 @@ __global__ __launch_bounds__(64 * kDqWaves) void bwd_dq_kernel(BwdArgs a, int NH
     const int m0 = qt * rows_wg;
     if (m0 >= Lq)
         return;
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int n = lane & 31, J = lane >> 5;
     const int h = g * a.G + hc * NH + (w % NH);
-    const int qi = m0 + 32 * (w / NH) + n; // the lane's row (MFMA column)
+    const int row_w = m0 + 32 * (w / NH); // the wave's first row
+    const int qi = row_w + n;             // the lane's row (MFMA column)
     const bool row_ok = qi < Lq;
     const int diag = Lk - Lq;
     const int last_row = min(m0 + rows_wg, Lq) - 1;
     const int kend = a.causal ? max(0, min(Lk, last_row + 1 + diag)) : Lk;
-    const int kend_row = a.causal ? max(0, min(Lk, qi + 1 + diag)) : Lk;
 
-    __shared__ __attribute__((aligned(16))) char k_t[kKeysPerTile * kRowBytes];
-    __shared__ __attribute__((aligned(16))) char v_t[kKeysPerTile * kRowBytes];
+    QLane L;
+    L.J = J;
+    L.kend_row = !row_ok ? 0 : (a.causal ? max(0, min(Lk, qi + 1 + diag)) : Lk);
+    L.sl = a.scale_log2;
+    L.lse2 = row_ok ? a.lse2[(size_t)(q0 + qi) * a.Hq + h] : 0.f;
+    L.dsum = row_ok ? a.dsum[(size_t)(q0 + qi) * a.Hq + h] : 0.f;
+    L.rowA = n * kRowBytes + 16 * (J ^ swz(n & 15));
+    {
+        const int G16 = lane >> 4, j = lane & 15;
+        const int x = 2 * (G16 & 1) + ((j & 3) >> 1);
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+            const int r = 8 * hf + 4 * J + (j >> 2);
+            L.trA[hf] = r * kRowBytes + 8 * (j & 1) + 16 * (x ^ swz(r));
+        }
+    }
 
     // Q^T and dO^T as B operands: lane (row n, J) holds dims 16 s + 8 J .. +8
-    const uint16_t *qg = static_cast<const uint16_t *>(a.q), *dog = static_cast<const uint16_t *>(a.dout);
     bf16x8 qop[8], gop[8];
+    {
+        const uint16_t *qg = static_cast<const uint16_t *>(a.q), *dog = static_cast<const uint16_t *>(a.dout);
 #pragma unroll
-    for (int s = 0; s < 8; ++s) {
-        uint4 qv = make_uint4(0, 0, 0, 0), gv = make_uint4(0, 0, 0, 0);
-        if (row_ok) {
-            const size_t off = ((size_t)(q0 + qi) * a.Hq + h) * D + 16 * s + 8 * J;
-            qv = ld16(qg + off);
-            gv = ld16(dog + off);
+        for (int s = 0; s < 8; ++s) {
+            uint4 qv = make_uint4(0, 0, 0, 0), gv = make_uint4(0, 0, 0, 0);
+            if (row_ok) {
+                const size_t off = ((size_t)(q0 + qi) * a.Hq + h) * D + 16 * s + 8 * J;
+                qv = ld16(qg + off);
+                gv = ld16(dog + off);
+            }
+            qop[s] = as_bf16x8(qv);
+            gop[s] = as_bf16x8(gv);
         }
-        qop[s] = as_bf16x8(qv);
-        gop[s] = as_bf16x8(gv);
     }
-    const float lse2 = row_ok ? a.lse[(size_t)(q0 + qi) * a.Hq + h] * kLog2e : 0.f;
-    const float dsum = row_ok ? a.dsum[(size_t)(q0 + qi) * a.Hq + h] : 0.f;
-    f32x16 dq[4]; // dQ^T [128 dims x 32 rows]: block db, register i -> dim 32 db + 8 (i / 4) + 4 J + i % 4
+    f32x16 dq[4]; // dQ^T [128 dims x 32 rows]: block db, register i <-> dim 32 db + 8 (i/4) + 4 J + i%4
 #pragma unroll
     for (int db = 0; db < 4; ++db)
 #pragma unroll
         for (int i = 0; i < 16; ++i)
             dq[db][i] = 0.f;
 
-    // transposed reads of K (A operand of dQ^T): lane (16-lane group G16, index j) addresses key
-    // 8 hf + 4 J + j / 4 of a 16-key block, dims 32 db + 16 (G16 % 2) + 4 (j % 4)
-    const int G16 = lane >> 4, j = lane & 15;
-    const int xcol = 2 * (G16 & 1) + ((j & 3) >> 1);
-    const uint16_t *kg = static_cast<const uint16_t *>(a.k), *vg = static_cast<const uint16_t *>(a.v);
+    KLoader ld;
+    {
+        const uint16_t *kg = static_cast<const uint16_t *>(a.k), *vg = static_cast<const uint16_t *>(a.v);
+        const size_t head0 = ((size_t)k0 * a.Hkv + g) * D;
+        const uint32_t row_bytes = (uint32_t)a.Hkv * kRowBytes;
+        const uint32_t seq_bytes = Lk > 0 ? ((uint32_t)(Lk - 1) * a.Hkv + 1) * kRowBytes : 0;
+        ld.krs = make_rsrc(kg + head0, seq_bytes);
+        ld.vrs = make_rsrc(vg + head0, seq_bytes);
+        ld.tile_bytes = kKTile * row_bytes;
+        ld.w = w;
+#pragma unroll
+        for (int p = 0; p < kKLoads; ++p) {
+            const int row = 4 * (kKLoads * w + p) + (lane >> 4);
+            ld.voff[p] = (uint32_t)row * row_bytes + 16 * ((lane & 15) ^ swz(row & 15));
+        }
+    }
 
-    for (int kb = 0; kb < kend; kb += kKeysPerTile) {
-        __syncthreads();
-        stage_rows(k_t, kg, (size_t)k0 + kb, a.Hkv, g, kKeysPerTile, Lk - kb, tid, 64 * kDqWaves);
-        stage_rows(v_t, vg, (size_t)k0 + kb, a.Hkv, g, kKeysPerTile, Lk - kb, tid, 64 * kDqWaves);
-        __syncthreads();
-        // S^T and dP^T [32 keys x 32 rows]: A operand = key row n, dims 16 s + 8 J
-        f32x16 s, dp;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            s[i] = 0.f;
-            dp[i] = 0.f;
+    const int ntiles = (kend + kKTile - 1) / kKTile;
+    auto blk = [&](int st, int t, int kk) {
+        KBlk x;
+        x.k = k_ring[st].k + kk * 32 * kRowBytes;
+        x.v = k_ring[st].v + kk * 32 * kRowBytes;
+        x.kb = t * kKTile + 32 * kk;
+        x.full = row_w + 32 <= Lq && x.kb + 32 <= Lk && (!a.causal || x.kb + 31 <= row_w + diag);
+        return x;
+    };
+    auto next_tile = [&](int st, int t) {
+        wait_vmcnt<0>();
+        barrier(); // tile t is in LDS for every wave; every wave is done with tile t - 2
+        if (t + 1 < ntiles)
+            ld.issue(st == kKStages - 1 ? 0 : st + 1, t + 1);
+    };
+
+    if (ntiles > 0) {
+        f32x16 sc, dp, scp, dpp;
+        uint32_t ska[8], skb[8];
+        ld.issue(0, 0);
+        next_tile(0, 0);
+        {
+            const KBlk b0 = blk(0, 0, 0), b1 = blk(0, 0, 1);
+            q_step<false, true, false>(L, qop, gop, dq, b0, ska, b0, scp, dpp, b0, sc, dp, skb);
+            q_step<false, true, true>(L, qop, gop, dq, b0, ska, b1, sc, dp, b0, scp, dpp, skb);
         }
-#pragma unroll
-        for (int st = 0; st < 8; ++st) {
-            const uint32_t off = chunk_off(n, 2 * st + J);
-            s = mfma32(as_bf16x8(ld16(k_t + off)), qop[st], s);
-            dp = mfma32(as_bf16x8(ld16(v_t + off)), gop[st], dp);
+        int sp = 0; // stage of tile t - 1
+        for (int t = 1; t < ntiles; ++t) {
+            const int st = sp == kKStages - 1 ? 0 : sp + 1;
+            next_tile(st, t);
+            const KBlk bm2 = blk(sp, t - 1, 0), bm1 = blk(sp, t - 1, 1), bj = blk(st, t, 0), bj1 = blk(st, t, 1);
+            q_step<true, true, true>(L, qop, gop, dq, bm2, skb, bj, scp, dpp, bm1, sc, dp, ska);
+            q_step<true, true, true>(L, qop, gop, dq, bm1, ska, bj1, sc, dp, bj, scp, dpp, skb);
+            sp = st;
         }
-        // P^T, dS^T: register i <-> key kb + 8 (i / 4) + 4 J + i % 4 of the lane's row
-        uint32_t dsk[8];
-#pragma unroll
-        for (int i = 0; i < 16; i += 2) {
-            float d2[2];
-#pragma unroll
-            for (int e = 0; e < 2; ++e) {
-                const int ii = i + e;
-                const int keyi = kb + 8 * (ii / 4) + 4 * J + (ii % 4);
-                const bool vis = row_ok && keyi < kend_row;
-                const float pv = vis ? exp2_fast(fmaf(s[ii], a.scale_log2, -lse2)) : 0.f;
-                d2[e] = pv * (dp[ii] - dsum);
-            }
-            dsk[i >> 1] = pack_bf16x2(d2[0], d2[1]);
-        }
-        // dQ^T += K^T dS^T over the two 16-key halves u
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            const bf16x8 dsop = as_bf16x8(make_uint4(dsk[4 * u], dsk[4 * u + 1], dsk[4 * u + 2], dsk[4 * u + 3]));
-#pragma unroll
-            for (int db = 0; db < 4; ++db) {
-                uint2 lo, hi;
-                {
-                    const int rw = 16 * u + 4 * J + (j >> 2);
-                    lo = lds_read_tr(k_t + chunk_off(rw, 4 * db + xcol) + 8 * (j & 1));
-                }
-                {
-                    const int rw = 16 * u + 8 + 4 * J + (j >> 2);
-                    hi = lds_read_tr(k_t + chunk_off(rw, 4 * db + xcol) + 8 * (j & 1));
-                }
-                dq[db] = mfma32(as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y)), dsop, dq[db]);
-            }
+        {
+            const KBlk bm2 = blk(sp, ntiles - 1, 0), bm1 = blk(sp, ntiles - 1, 1);
+            q_step<true, false, true>(L, qop, gop, dq, bm2, skb, bm2, scp, dpp, bm1, sc, dp, ska);
+            q_step<true, false, false>(L, qop, gop, dq, bm1, ska, bm1, scp, dpp, bm1, sc, dp, skb);
         }
     }
 
@@ -581,13 +765,15 @@ hipError_t launch_prefill_bwd(const BwdArgs &a, hipStream_t stream)
     const int NH = heads_per_wg_bwd(a.G), RB = kDqWaves / NH;
     const int nqt = (a.max_q + 32 * RB - 1) / (32 * RB);
     const long units_q = (long)a.Hkv * (a.G / NH) * a.B * nqt;
-    if (blocks_kv > 0x7fffffff || units_q > 0x7fffffff)
+    const long blocks_q = (units_q + kXcds - 1) / kXcds * kXcds;
+    if (blocks_kv > 0x7fffffff || blocks_q > 0x7fffffff)
         return hipErrorInvalidValue;
     if (units_kv > 0)
         hipLaunchKernelGGL(bwd_dkdv_kernel, dim3((unsigned)blocks_kv), dim3(kKvThreads), 0, stream, a, nkt,
                            (int)units_kv);
     if (units_q > 0)
-        hipLaunchKernelGGL(bwd_dq_kernel, dim3((unsigned)units_q), dim3(64 * kDqWaves), 0, stream, a, NH, RB, nqt);
+        hipLaunchKernelGGL(bwd_dq_kernel, dim3((unsigned)blocks_q), dim3(kDqThreads), 0, stream, a, NH, RB, nqt,
+                           (int)units_q);
     return hipGetLastError();
 }
 

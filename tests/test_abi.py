@@ -107,7 +107,7 @@ def _backward(lib, **kw):
 
 
 def test_backward_validation(lib):
-    assert lib.attn_prefill_varlen_backward_workspace_size(3, 100, 8) == 3 * 100 * 8 * 4
+    assert lib.attn_prefill_varlen_backward_workspace_size(3, 100, 8) == 3 * 100 * 8 * 8
     assert lib.attn_prefill_varlen_backward_workspace_size(0, 100, 8) == 0
     assert _backward(lib, dt=5) == INVALID
     assert _backward(lib, B=-1) == INVALID
@@ -120,7 +120,7 @@ def test_backward_validation(lib):
     assert _backward(lib, mk=1 << 20, Hq=8, Hkv=8) == UNSUPPORTED
     assert _backward(lib, lse=None) == INVALID
     assert _backward(lib, dv=None) == INVALID
-    assert _backward(lib, wsb=2 * 10 * 8 * 4 - 1) == WORKSPACE
+    assert _backward(lib, wsb=2 * 10 * 8 * 8 - 1) == WORKSPACE
     assert _backward(lib, ws=None) == WORKSPACE
     assert _backward(lib, B=0) == _lib.ATTN_OK
     _backward(lib, D=96)
