@@ -39,7 +39,7 @@ def _parse():
     p.add_argument("--seed", type=int, default=0)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--only", default="",
-                   help="comma list of prefill,prefill_skip,decode,skip,smallseq (profiling runs)")
+                   help="comma list of prefill,prefill_skip,decode,skip,smallseq,prefill_bwd (profiling runs)")
     p.add_argument("--calib-copy", action="store_true",
                    help="also run one plain 1 GiB device-to-device copy (scales HBM byte counters)")
     p.add_argument("--summarize-profiles", metavar="DIR", default="",
@@ -91,7 +91,7 @@ def main():
     from paged_skip_softmax_amd import workloads as W
 
     only = (set(args.only.split(",")) if args.only
-            else {"prefill", "prefill_skip", "decode", "skip", "smallseq"})
+            else {"prefill", "prefill_skip", "decode", "skip", "smallseq", "prefill_bwd"})
     dev = "cuda:0"
     torch.cuda.set_device(0)
     t_gen = time.time()
@@ -108,6 +108,21 @@ def main():
         work["smallseq"] = W.smallseq_cross(seed=1004 + args.seed, device=dev)
     torch.cuda.synchronize()
     print(f"# inputs generated in {time.time() - t_gen:.1f} s", file=sys.stderr, flush=True)
+
+    # rows past the hot path (timed after it, outside the step): the prefill backward
+    nxt = {}
+    if "prefill_bwd" in only:
+        xb = work.get("prefill") or W.varlen_prefill(seed=1001 + args.seed, device=dev)
+        work["prefill_bwd"] = xb
+        do_b = W.grad_output(xb, seed=1005 + args.seed, device=dev)
+        o_b, lse_b, _ = attn.attn_prefill_varlen(xb.q, xb.k, xb.v, xb.cu_q, xb.cu_k, xb.max_q, xb.max_k, causal=True,
+                                                 return_lse=True)
+        ws_b = torch.empty(attn.attn_prefill_varlen_backward_workspace_size(xb.B, xb.max_q, xb.Hq),
+                           dtype=torch.uint8, device=dev)
+        g_b = (torch.empty_like(xb.q), torch.empty_like(xb.k), torch.empty_like(xb.v))
+        nxt["prefill_bwd"] = lambda: attn.attn_prefill_varlen_backward(
+            xb.q, xb.k, xb.v, o_b, do_b, lse_b, xb.cu_q, xb.cu_k, xb.max_q, xb.max_k, causal=True, workspace=ws_b,
+            dq=g_b[0], dk=g_b[1], dv=g_b[2])
 
     calls = {}  # name -> zero-arg launcher
     if "prefill" in only:
@@ -166,6 +181,21 @@ def main():
     ms = {nm: float(np.mean([a.elapsed_time(b) for a, b in rec[nm]])) for nm in names}
     ms_min = {nm: float(np.min([a.elapsed_time(b) for a, b in rec[nm]])) for nm in names}
     ms_per_step = (t1 - t0) * 1e3 / max(1, args.steps)
+    for nm, fn in nxt.items():
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        evs = []
+        for _ in range(args.steps):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            evs.append((e0, e1))
+        torch.cuda.synchronize()
+        ms[nm] = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+        ms_min[nm] = float(np.min([a.elapsed_time(b) for a, b in evs]))
     print(f"# kernel ms (mean over {args.steps} steps): " + ", ".join(f"{k}={v:.4f}" for k, v in ms.items()),
           file=sys.stderr, flush=True)
 
@@ -268,6 +298,20 @@ def main():
                           "unit": "GB/s", "frac": gbps / PEAK_HBM_GBPS,
                           "traffic": _traffic_from_profiles("smallseq_kernel"), "ms": ms["smallseq"]})
 
+    if "prefill_bwd" in only:
+        L = work["prefill_bwd"].lens.double()
+        fwd_flops = 4.0 * 128 * 32 * float((L * (L + 1) / 2).sum())
+        t = ms["prefill_bwd"]
+        # algorithmic: the five products S (recomputed), dP, dV, dK, dQ = 2.5x the forward's two; the dQ
+        # kernel recomputes S and dP once more (executed: 3.5x)
+        tf = 2.5 * fwd_flops / (t * 1e-3) / 1e12
+        out["prefill_bwd"] = {"ms": t, "ms_min": ms_min["prefill_bwd"], "flop_alg": 2.5 * fwd_flops, "tflops_alg": tf,
+                              "tflops_executed": 3.5 * fwd_flops / (t * 1e-3) / 1e12,
+                              "frac_peak": tf / PEAK_BF16_TFLOPS,
+                              "note": "one call: bwd_prep + bwd_dkdv + bwd_dq; timed outside the step"}
+        if "prefill" in out:
+            out["prefill_bwd"]["bwd_over_fwd_time"] = t / out["prefill"]["ms"]
+
     # the dominant kernel: the largest share of the step
     dom = max(rooflines, key=lambda r: r["ms"]) if rooflines else None
     roofline = None
@@ -306,6 +350,7 @@ def main():
                                       "paged decode split-K B=64 L~U[1024,32768] page 16, 32x128-key splits",
                                       "sequential skip decode thr {0,0.01,0.1} on hot keys",
                                       "small-seq cross B=30720 s_kv in {2..16} H=16 D=128"],
+                   "timed_after_the_step": ["the prefill backward (dq, dk, dv) on the prefill shapes"],
                    "seed": args.seed},
         "roofline": roofline,
         "cpu_baseline": cpu,
@@ -422,14 +467,17 @@ def _cpu_baseline(x):
 
 # kernel -> (workload the bench runs it on, summary file stem, sources it is built from)
 _KSRC = ["paged_skip_softmax_amd/csrc/kcommon.h", "paged_skip_softmax_amd/csrc/launch.h"]
+_LDS = "paged_skip_softmax_amd/csrc/lds_dma.h"
+_BWD = ["paged_skip_softmax_amd/csrc/prefill_bwd.hip", _LDS] + _KSRC
+_BWD_W = "prefill backward on the prefill shapes (16 seqs L~U[256,4096], Hq=32, Hkv=8, D=128, causal)"
 PROFILED = {
     "prefill_d128_kernel<false>": ("varlen causal prefill bf16, 16 seqs L~U[256,4096], Hq=32, Hkv=8, D=128",
                                    "prefill_d128_kernel.varlen_causal_16seq_L256-4096_Hq32_Hkv8_D128",
-                                   ["paged_skip_softmax_amd/csrc/prefill_d128.hip"] + _KSRC),
+                                   ["paged_skip_softmax_amd/csrc/prefill_d128.hip", _LDS] + _KSRC),
     "prefill_d128_kernel<true>": ("skip-softmax prefill on the hot-key prefill input (same shapes), "
                                   "threshold 0.01 and 0.1 in turn",
                                   "prefill_d128_kernel_skip.varlen_causal_hot_16seq_thr0.01-0.1",
-                                  ["paged_skip_softmax_amd/csrc/prefill_d128.hip"] + _KSRC),
+                                  ["paged_skip_softmax_amd/csrc/prefill_d128.hip", _LDS] + _KSRC),
     "decode_split_kernel": ("paged decode B=64, L~U[1024,32768], page 16, 32 splits of 128-key tiles",
                             "decode_split_kernel.paged_decode_B64_L1k-32k_page16_32splits",
                             ["paged_skip_softmax_amd/csrc/decode.hip"] + _KSRC),
@@ -443,6 +491,10 @@ PROFILED = {
     "smallseq_kernel": ("small-seq cross-attention B=30720, s_kv in {2,4,6,8,12,16}, H=16, D=128",
                         "smallseq_kernel.smallseq_cross_B30720_H16_D128",
                         ["paged_skip_softmax_amd/csrc/smallseq.hip"] + _KSRC),
+    "bwd_prep_kernel": (_BWD_W + ": rowsum(dO * O) and lse * log2(e)",
+                        "bwd_prep_kernel.varlen_causal_16seq_L256-4096_Hq32", _BWD),
+    "bwd_dkdv_kernel": (_BWD_W + ": dK, dV", "bwd_dkdv_kernel.varlen_causal_16seq_L256-4096_Hq32_Hkv8_D128", _BWD),
+    "bwd_dq_kernel": (_BWD_W + ": dQ", "bwd_dq_kernel.varlen_causal_16seq_L256-4096_Hq32_Hkv8_D128", _BWD),
 }
 # kernels launched more than once per step: the role of each launch, in launch order (the first role
 # is the one the roofline and traffic.json refer to)
