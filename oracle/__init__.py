@@ -48,7 +48,9 @@ def _load():
         lib.orc_decode_rows.argtypes = [P, P, P, P, P, I, I, I, I, I, I, D, I, D, I, I, P, I, P, I, P, P, P]
         lib.orc_smallseq_rows.argtypes = [I, P, P, P, P, I, I, I, I, D, P, I, P, P]
         lib.orc_prefill_bwd.argtypes = [I, P, P, P, P, P, P, P, I, I, I, I, D, I, P, P, P]
-        for f in (lib.orc_prefill_rows, lib.orc_decode_rows, lib.orc_smallseq_rows, lib.orc_prefill_bwd):
+        lib.orc_smallseq_bwd.argtypes = [I, P, P, P, P, P, P, I, I, I, I, D, P, P, P]
+        for f in (lib.orc_prefill_rows, lib.orc_decode_rows, lib.orc_smallseq_rows, lib.orc_prefill_bwd,
+                  lib.orc_smallseq_bwd):
             f.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -182,6 +184,27 @@ def smallseq(q, k, v, cu_kv, max_s, scale, rows=None):
         o = o.reshape(B, H, D)
         w = w.reshape(B, H, 1, max(int(max_s), 0))
     return o, w
+
+
+def smallseq_backward(q, k, v, w, dout, cu_kv, max_s, scale):
+    """Gradients (dq, dk, dv) of the small-seq cross-attention from the stored weights w [B, H, 1, max_s]."""
+    qa, dt = _np(q)
+    ka, dk_ = _np(k)
+    va, dv_ = _np(v)
+    wa, dw_ = _np(w)
+    ga, dg = _np(dout)
+    assert dt == dk_ == dv_ == dw_ == dg and dt in (0, 1)
+    cu, _ = _np(cu_kv)
+    B, H, D = qa.shape
+    assert wa.shape == (B, H, 1, int(max_s)) and ga.shape == qa.shape
+    dq = np.zeros(qa.shape, dtype=np.float64)
+    dk = np.zeros(ka.shape, dtype=np.float64)
+    dv = np.zeros(va.shape, dtype=np.float64)
+    rc = _load().orc_smallseq_bwd(dt, _ptr(qa), _ptr(ka), _ptr(va), _ptr(wa), _ptr(ga), _ptr(cu), B, H, D,
+                                  int(max_s), float(scale), _ptr(dq), _ptr(dk), _ptr(dv))
+    if rc != 0:
+        raise ValueError("oracle smallseq backward rejected its arguments")
+    return dq, dk, dv
 
 
 def prefill_backward(q, k, v, dout, cu_q, cu_k, Hq, Hkv, scale, causal, o=None):

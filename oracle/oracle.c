@@ -27,7 +27,8 @@
  *               [s c, (s+1) c) and is attended densely to (o_s, lse_s); then
  *               lse = log sum_{finite} exp(lse_s) and o = sum_s exp(lse_s - lse) o_s.
  *
- * Plus the backward of the dense prefill (orc_prefill_bwd, at the end of this file).
+ * Plus the backward of the dense prefill (orc_prefill_bwd) and of the small-seq cross-attention from
+ * its stored attention weights (orc_smallseq_bwd), at the end of this file.
  *
  * Inputs are read as the exact bytes the GPU reads (fp32, or bf16 widened exactly to fp64); all
  * arithmetic is in fp64.
@@ -465,3 +466,60 @@ int orc_prefill_bwd(int dtype, const void *q, const void *k, const void *v, cons
     return 0;
 }
 
+/*
+ * Backward of the small-seq cross-attention from its stored attention weights ("ROCm TransformerEngine:
+ * Integrate CK varlen cross attention for small-seq (s_q=1, s_kv<=16)", change list: the backward takes
+ * grad_V, grad_attn, the softmax backward and grad_Q / grad_K, and reads the weights the forward wrote).
+ * Per (sequence b, head h) with s = cu_kv[b+1] - cu_kv[b] keys, stored weights w_j = w[b, h, 0, j]
+ * (entries j >= s are padding and not read) and output gradient dO:
+ *   grad_V:   dv_j = w_j dO
+ *   grad_attn: dw_j = dO . v_j
+ *   softmax backward: ds_j = w_j (dw_j - sum_j' w_j' dw_j')
+ *   grad_Q:   dq = scale sum_j ds_j k_j          grad_K: dk_j = scale ds_j q
+ * q, dout [B, H, D]; k, v [total_kv, H, D]; w [B, H, 1, max_s]; all of dtype; outputs fp64 dq [B, H, D],
+ * dk, dv [total_kv, H, D], fully written.  Each key belongs to one sequence, so tasks never overlap.
+ */
+int orc_smallseq_bwd(int dtype, const void *q, const void *k, const void *v, const void *w, const void *dout,
+                     const int32_t *cu_kv, int B, int H, int D, int max_s, double scale, double *dq, double *dk,
+                     double *dv)
+{
+    if (B < 0 || H <= 0 || D <= 0 || max_s < 0)
+        return -1;
+    const size_t tk = B ? (size_t)cu_kv[B] : 0;
+    memset(dq, 0, sizeof(double) * (size_t)B * H * D);
+    memset(dk, 0, sizeof(double) * tk * H * D);
+    memset(dv, 0, sizeof(double) * tk * H * D);
+    int bad = 0;
+#pragma omp parallel for schedule(dynamic, 16) collapse(2) reduction(| : bad)
+    for (int b = 0; b < B; ++b)
+        for (int h = 0; h < H; ++h) {
+            const int n = cu_kv[b + 1] - cu_kv[b];
+            if (n < 0 || n > max_s) {
+                bad = 1;
+                continue;
+            }
+            const size_t row = ((size_t)b * H + h) * D;
+            double *dw = malloc(sizeof(double) * ((size_t)n + 1)), *wj = malloc(sizeof(double) * ((size_t)n + 1));
+            double sum = 0.0;
+            for (int j = 0; j < n; ++j) {
+                const size_t kv = ((size_t)(cu_kv[b] + j) * H + h) * D;
+                wj[j] = widen(w, dtype, ((size_t)b * H + h) * max_s + j);
+                dw[j] = 0.0;
+                for (int d = 0; d < D; ++d)
+                    dw[j] += widen(dout, dtype, row + d) * widen(v, dtype, kv + d);
+                sum += wj[j] * dw[j];
+            }
+            for (int j = 0; j < n; ++j) {
+                const size_t kv = ((size_t)(cu_kv[b] + j) * H + h) * D;
+                const double ds = wj[j] * (dw[j] - sum);
+                for (int d = 0; d < D; ++d) {
+                    dv[kv + d] = wj[j] * widen(dout, dtype, row + d);
+                    dk[kv + d] = scale * ds * widen(q, dtype, row + d);
+                    dq[row + d] += scale * ds * widen(k, dtype, kv + d);
+                }
+            }
+            free(dw);
+            free(wj);
+        }
+    return bad ? -1 : 0;
+}

@@ -211,7 +211,7 @@ def paged_decode_hot(seed=1002, device="cpu", **kw):
 
 
 def smallseq_cross(seed=1004, device="cpu", B=30720, H=16, D=128, choices=(2, 4, 6, 8, 12, 16),
-                   fixed=None):
+                   fixed=None, dtype=torch.bfloat16):
     """s_q = 1 cross-attention inputs; ``fixed`` forces every s_kv to one value."""
     if fixed is not None:
         lens = torch.full((B,), int(fixed), dtype=torch.int64)
@@ -220,8 +220,8 @@ def smallseq_cross(seed=1004, device="cpu", B=30720, H=16, D=128, choices=(2, 4,
         lens = torch.tensor(choices, dtype=torch.int64)[idx]
     cu = _cu(lens)
     T = int(cu[-1])
-    q = _randn((B, H, D), seed, _S_Q, device, torch.bfloat16)
-    k = _randn((T, H, D), seed, _S_K, device, torch.bfloat16)
-    v = _randn((T, H, D), seed, _S_V, device, torch.bfloat16)
+    q = _randn((B, H, D), seed, _S_Q, device, dtype)
+    k = _randn((T, H, D), seed, _S_K, device, dtype)
+    v = _randn((T, H, D), seed, _S_V, device, dtype)
     return SimpleNamespace(q=q, k=k, v=v, cu_kv=cu.to(device), lens=lens, B=B, H=H, D=D,
-                           max_s=int(lens.max()) if B else 0, scale=1.0 / math.sqrt(D), dtype=torch.bfloat16)
+                           max_s=int(lens.max()) if B else 0, scale=1.0 / math.sqrt(D), dtype=dtype)

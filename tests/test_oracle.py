@@ -496,3 +496,63 @@ def test_backward_rows_without_keys_and_unseen_keys():
     p_last = np.exp(s - lse)
     expect = sum(p_last[h] * dout[11, h].double().numpy() for h in range(2))
     assert np.max(np.abs(dv[6, 0] - expect)) < 1e-12
+
+
+def _smallseq_fixture(lens, H=3, D=16, seed=81):
+    """fp32 small-seq inputs with the given key counts, the exact softmax weights (float64 torch,
+    stored as fp32, zero padded) and an output gradient."""
+    g = torch.Generator().manual_seed(seed)
+    B, T, ms = len(lens), sum(lens), max(lens)
+    q = torch.randn(B, H, D, generator=g)
+    k = torch.randn(T, H, D, generator=g)
+    v = torch.randn(T, H, D, generator=g)
+    do = torch.randn(B, H, D, generator=g)
+    cu = torch.tensor([0] + list(np.cumsum(lens)), dtype=torch.int32)
+    scale = D ** -0.5
+    w = torch.zeros(B, H, 1, ms, dtype=torch.float64)
+    for b, n in enumerate(lens):
+        if n:
+            s = scale * torch.einsum("hd,jhd->hj", q[b].double(), k[cu[b]:cu[b + 1]].double())
+            w[b, :, 0, :n] = torch.softmax(s, dim=-1)
+    return q, k, v, do, cu, ms, scale, w.float()
+
+
+def test_smallseq_backward_matches_torch_autograd():
+    # the stored weights are the exact softmax rounded to fp32; float64 autograd of o = softmax(scale q k^T) v
+    # differs from the stored-weights backward only by that rounding (relative ~6e-8)
+    lens = [1, 3, 16, 0, 7, 2]
+    q, k, v, do, cu, ms, scale, w = _smallseq_fixture(lens)
+    dq, dk, dv = oracle.smallseq_backward(q, k, v, w, do, cu, ms, scale)
+    for b, n in enumerate(lens):
+        qb = q[b].double().clone().requires_grad_(True)
+        kb = k[cu[b]:cu[b + 1]].double().clone().requires_grad_(True)
+        vb = v[cu[b]:cu[b + 1]].double().clone().requires_grad_(True)
+        if n == 0:
+            assert np.all(dq[b] == 0)
+            continue
+        p = torch.softmax(scale * torch.einsum("hd,jhd->hj", qb, kb), dim=-1)
+        o = torch.einsum("hj,jhd->hd", p, vb)
+        (o * do[b].double()).sum().backward()
+        assert np.max(np.abs(dq[b] - qb.grad.numpy())) < 1e-5
+        assert np.max(np.abs(dk[cu[b]:cu[b + 1]] - kb.grad.numpy())) < 1e-5
+        assert np.max(np.abs(dv[cu[b]:cu[b + 1]] - vb.grad.numpy())) < 1e-5
+
+
+def test_smallseq_backward_padding_and_closed_forms():
+    lens = [1, 5, 0, 4]
+    q, k, v, do, cu, ms, scale, w = _smallseq_fixture(lens, seed=82)
+    dq, dk, dv = oracle.smallseq_backward(q, k, v, w, do, cu, ms, scale)
+    # weights past a sequence's key count are padding and never read
+    w2 = w.clone()
+    for b, n in enumerate(lens):
+        w2[b, :, 0, n:] = 7.0
+    assert all(np.array_equal(x, y) for x, y in zip((dq, dk, dv), oracle.smallseq_backward(q, k, v, w2, do, cu, ms,
+                                                                                           scale)))
+    # one key: w = 1, so dv = dO, and the softmax backward leaves ds = 0 (dq = dk = 0)
+    assert np.max(np.abs(dv[0] - do[0].double().numpy())) < 1e-12
+    assert np.all(dq[0] == 0) and np.all(dk[0] == 0)
+    # a sequence with no key: dq = 0
+    assert np.all(dq[2] == 0)
+    # the weights enter dv linearly: doubling w doubles dv
+    _, _, dv2 = oracle.smallseq_backward(q, k, v, w * 2, do, cu, ms, scale)
+    assert np.max(np.abs(dv2 - 2 * dv)) < 1e-12
