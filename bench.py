@@ -39,7 +39,8 @@ def _parse():
     p.add_argument("--seed", type=int, default=0)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--only", default="",
-                   help="comma list of prefill,prefill_skip,decode,skip,smallseq,prefill_bwd (profiling runs)")
+                   help="comma list of prefill,prefill_skip,decode,skip,smallseq,prefill_bwd,smallseq_bwd "
+                        "(profiling runs)")
     p.add_argument("--calib-copy", action="store_true",
                    help="also run one plain 1 GiB device-to-device copy (scales HBM byte counters)")
     p.add_argument("--summarize-profiles", metavar="DIR", default="",
@@ -91,7 +92,7 @@ def main():
     from paged_skip_softmax_amd import workloads as W
 
     only = (set(args.only.split(",")) if args.only
-            else {"prefill", "prefill_skip", "decode", "skip", "smallseq", "prefill_bwd"})
+            else {"prefill", "prefill_skip", "decode", "skip", "smallseq", "prefill_bwd", "smallseq_bwd"})
     dev = "cuda:0"
     torch.cuda.set_device(0)
     t_gen = time.time()
@@ -123,6 +124,15 @@ def main():
         nxt["prefill_bwd"] = lambda: attn.attn_prefill_varlen_backward(
             xb.q, xb.k, xb.v, o_b, do_b, lse_b, xb.cu_q, xb.cu_k, xb.max_q, xb.max_k, causal=True, workspace=ws_b,
             dq=g_b[0], dk=g_b[1], dv=g_b[2])
+
+    if "smallseq_bwd" in only:
+        cb = work.get("smallseq") or W.smallseq_cross(seed=1004 + args.seed, device=dev)
+        work["smallseq_bwd"] = cb
+        do_s = W.grad_output(cb, seed=1006 + args.seed, device=dev)
+        _, w_s, _ = attn.attn_smallseq_cross(cb.q, cb.k, cb.v, cb.cu_kv, cb.max_s)
+        gs = (torch.empty_like(cb.q), torch.empty_like(cb.k), torch.empty_like(cb.v))
+        nxt["smallseq_bwd"] = lambda: attn.attn_smallseq_cross_backward(
+            cb.q, cb.k, cb.v, w_s, do_s, cb.cu_kv, cb.max_s, dq=gs[0], dk=gs[1], dv=gs[2])
 
     calls = {}  # name -> zero-arg launcher
     if "prefill" in only:
@@ -312,6 +322,16 @@ def main():
         if "prefill" in out:
             out["prefill_bwd"]["bwd_over_fwd_time"] = t / out["prefill"]["ms"]
 
+    if "smallseq_bwd" in only:
+        c = work["smallseq_bwd"]
+        nk = float(c.lens.sum())
+        # read K, V and write dK, dV per key; read q, dO and write dq per sequence; the stored weights read
+        byts = 4.0 * c.H * c.D * 2 * nk + 3.0 * c.B * c.H * c.D * 2 + 2.0 * c.H * nk
+        t = ms["smallseq_bwd"]
+        gb = byts / (t * 1e-3) / 1e9
+        out["smallseq_bwd"] = {"ms": t, "ms_min": ms_min["smallseq_bwd"], "bytes_alg": byts, "GBps": gb,
+                               "frac_peak": gb / PEAK_HBM_GBPS, "note": "one launch; timed outside the step"}
+
     # the dominant kernel: the largest share of the step
     dom = max(rooflines, key=lambda r: r["ms"]) if rooflines else None
     roofline = None
@@ -350,7 +370,8 @@ def main():
                                       "paged decode split-K B=64 L~U[1024,32768] page 16, 32x128-key splits",
                                       "sequential skip decode thr {0,0.01,0.1} on hot keys",
                                       "small-seq cross B=30720 s_kv in {2..16} H=16 D=128"],
-                   "timed_after_the_step": ["the prefill backward (dq, dk, dv) on the prefill shapes"],
+                   "timed_after_the_step": ["the prefill backward (dq, dk, dv) on the prefill shapes",
+                                            "the small-seq backward from the stored weights on the small-seq shapes"],
                    "seed": args.seed},
         "roofline": roofline,
         "cpu_baseline": cpu,
@@ -491,6 +512,9 @@ PROFILED = {
     "smallseq_kernel": ("small-seq cross-attention B=30720, s_kv in {2,4,6,8,12,16}, H=16, D=128",
                         "smallseq_kernel.smallseq_cross_B30720_H16_D128",
                         ["paged_skip_softmax_amd/csrc/smallseq.hip"] + _KSRC),
+    "smallseq_bwd_kernel": ("small-seq backward from the stored weights, B=30720, s_kv in {2,4,6,8,12,16}, H=16, "
+                            "D=128", "smallseq_bwd_kernel.smallseq_cross_B30720_H16_D128",
+                            ["paged_skip_softmax_amd/csrc/smallseq.hip"] + _KSRC),
     "bwd_prep_kernel": (_BWD_W + ": rowsum(dO * O) and lse * log2(e)",
                         "bwd_prep_kernel.varlen_causal_16seq_L256-4096_Hq32", _BWD),
     "bwd_dkdv_kernel": (_BWD_W + ": dK, dV", "bwd_dkdv_kernel.varlen_causal_16seq_L256-4096_Hq32_Hkv8_D128", _BWD),

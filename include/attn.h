@@ -123,6 +123,23 @@ attn_status_t attn_smallseq_cross(const void *q, const void *k, const void *v, c
                                   void *o, void *attn_weights, float *lse, void *stream);
 
 /*
+ * Backward of the small-seq cross-attention from the attention weights its forward stored
+ * ("ROCm TransformerEngine: Integrate CK varlen cross attention for small-seq (s_q=1, s_kv<=16)",
+ * change list: grad_V, grad_attn, the softmax backward and grad_Q / grad_K; the weights buffer is
+ * written by the forward and read by the backward).  Per (sequence b, head h) with s_b keys, stored
+ * weights w_j and output gradient dout:
+ *   dv_j = w_j dout,  dw_j = dout . v_j,  ds_j = w_j (dw_j - sum_j' w_j' dw_j'),
+ *   dq = scale sum_j ds_j k_j,  dk_j = scale ds_j q.
+ *   q, dout, dq [B, H, D]; k, v, dk, dv [cu_seqlens_kv[B], H, D]; attn_weights [B, H, 1, max_seqlen_kv]
+ *   (as attn_smallseq_cross writes it; entries j >= s_b are not read); all bf16.  dq, dk, dv are fully
+ *   written.  max_seqlen_kv in [0, 16], >= every s_b.  Supported: D = 128.  B == 0 is a no-op.
+ */
+attn_status_t attn_smallseq_cross_backward(const void *q, const void *k, const void *v, const void *attn_weights,
+                                           const void *dout, const int32_t *cu_seqlens_kv, int32_t B, int32_t H,
+                                           int32_t D, int32_t max_seqlen_kv, float scale, void *dq, void *dk,
+                                           void *dv, void *stream);
+
+/*
  * Backward of the dense varlen prefill: the gradients dq, dk, dv of the masked-softmax attention
  * o = softmax(scale q k^T + mask) v for an output gradient dout ("Model-Optimizer: Add Triton unified
  * attention kernel with HuggingFace integration", summary: the Triton kernel has an autograd backward

@@ -18,7 +18,8 @@ from . import _lib
 from ._lib import SKIP_TILE, AttnError  # noqa: F401
 
 __all__ = ["attn_prefill_varlen", "attn_prefill_varlen_backward", "attn_prefill_varlen_backward_workspace_size",
-           "attn_decode_paged", "attn_decode_paged_workspace_size", "attn_smallseq_cross", "AttnError", "SKIP_TILE"]
+           "attn_decode_paged", "attn_decode_paged_workspace_size", "attn_smallseq_cross",
+           "attn_smallseq_cross_backward", "AttnError", "SKIP_TILE"]
 
 
 def _stream(t: torch.Tensor) -> int:
@@ -187,3 +188,32 @@ def attn_smallseq_cross(q, k, v, cu_seqlens_kv, max_seqlen_kv, *, scale=None, re
                                        int(max_seqlen_kv), float(scale), out.data_ptr(), _ptr(w), _ptr(lse),
                                        _stream(q)))
     return out, w, lse
+
+
+def attn_smallseq_cross_backward(q, k, v, attn_weights, dout, cu_seqlens_kv, max_seqlen_kv, *, scale=None, dq=None,
+                                 dk=None, dv=None):
+    """Gradients of the s_q = 1 cross-attention from its stored weights.  Returns (dq, dk, dv)."""
+    lib = _lib.load()
+    dev = q.device
+    for name, t in (("q", q), ("k", k), ("v", v), ("attn_weights", attn_weights), ("dout", dout)):
+        _cuda_contig(name, t, torch.bfloat16, dev)
+    _cuda_contig("cu_seqlens_kv", cu_seqlens_kv, torch.int32, dev)
+    _need(q.dim() == 3 and k.dim() == 3 and k.shape == v.shape and k.shape[1:] == q.shape[1:],
+          "q [B,H,D], k/v [T,H,D]")
+    B, H, D = q.shape
+    _need(dout.shape == q.shape, "dout must match q")
+    _need(attn_weights.shape == (B, H, 1, int(max_seqlen_kv)), "attn_weights must be [B, H, 1, max_seqlen_kv]")
+    _need(cu_seqlens_kv.numel() == B + 1, "cu_seqlens_kv must have B + 1 entries")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    for name, t, ref in (("dq", dq, q), ("dk", dk, k), ("dv", dv, v)):
+        _cuda_contig(name, t, torch.bfloat16, dev)
+        _need(t.shape == ref.shape, f"{name} must match its input's shape")
+    _lib.check(lib.attn_smallseq_cross_backward(q.data_ptr(), k.data_ptr(), v.data_ptr(), attn_weights.data_ptr(),
+                                                dout.data_ptr(), cu_seqlens_kv.data_ptr(), B, H, D,
+                                                int(max_seqlen_kv), float(scale), dq.data_ptr(), dk.data_ptr(),
+                                                dv.data_ptr(), _stream(q)))
+    return dq, dk, dv

@@ -252,6 +252,43 @@ attn_status_t attn_smallseq_cross(const void *q, const void *k, const void *v, c
     return hip_status(attn::launch_smallseq(a, static_cast<hipStream_t>(stream)), "small-seq launch");
 }
 
+attn_status_t attn_smallseq_cross_backward(const void *q, const void *k, const void *v, const void *attn_weights,
+                                           const void *dout, const int32_t *cu_seqlens_kv, int32_t B, int32_t H,
+                                           int32_t D, int32_t max_seqlen_kv, float scale, void *dq, void *dk,
+                                           void *dv, void *stream)
+{
+    if (B < 0)
+        return fail(ATTN_ERR_INVALID, "attn_smallseq_cross_backward: B = %d < 0", B);
+    if (H <= 0)
+        return fail(ATTN_ERR_INVALID, "attn_smallseq_cross_backward: H = %d", H);
+    if (max_seqlen_kv < 0 || max_seqlen_kv > 16)
+        return fail(ATTN_ERR_INVALID, "attn_smallseq_cross_backward: max_seqlen_kv = %d outside [0, 16]",
+                    max_seqlen_kv);
+    if (!std::isfinite(scale))
+        return fail(ATTN_ERR_INVALID, "attn_smallseq_cross_backward: scale is not finite");
+    if (D != 128)
+        return fail(ATTN_ERR_UNSUPPORTED, "attn_smallseq_cross_backward: D = %d (built for 128)", D);
+    if (B == 0)
+        return ok();
+    if (!q || !k || !v || !dout || !cu_seqlens_kv || !dq || !dk || !dv || (max_seqlen_kv > 0 && !attn_weights))
+        return fail(ATTN_ERR_INVALID, "attn_smallseq_cross_backward: a required pointer is NULL");
+    attn::SmallBwdArgs a{};
+    a.q = static_cast<const uint16_t *>(q);
+    a.k = static_cast<const uint16_t *>(k);
+    a.v = static_cast<const uint16_t *>(v);
+    a.w = static_cast<const uint16_t *>(attn_weights);
+    a.dout = static_cast<const uint16_t *>(dout);
+    a.cu = cu_seqlens_kv;
+    a.B = B;
+    a.H = H;
+    a.max_s = max_seqlen_kv;
+    a.scale = scale;
+    a.dq = static_cast<uint16_t *>(dq);
+    a.dk = static_cast<uint16_t *>(dk);
+    a.dv = static_cast<uint16_t *>(dv);
+    return hip_status(attn::launch_smallseq_bwd(a, static_cast<hipStream_t>(stream)), "small-seq backward launch");
+}
+
 attn_status_t attn_prefill_varlen(attn_dtype_t dtype, const void *q, const void *k, const void *v,
                                   const int32_t *cu_seqlens_q, const int32_t *cu_seqlens_k, int32_t B,
                                   int32_t max_seqlen_q, int32_t max_seqlen_k, int32_t Hq, int32_t Hkv,

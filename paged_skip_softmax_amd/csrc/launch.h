@@ -45,6 +45,15 @@ struct SmallArgs {
     float *lse;                // nullable [B, H]
 };
 
+// Small-seq backward from the stored attention weights.
+struct SmallBwdArgs {
+    const uint16_t *q, *k, *v, *w, *dout; // [B, H, D], [T, H, D] x2, [B, H, 1, max_s], [B, H, D]
+    const int32_t *cu;                    // [B + 1]
+    int B, H, max_s;
+    float scale;
+    uint16_t *dq, *dk, *dv;               // [B, H, D], [T, H, D] x2
+};
+
 // Varlen prefill.
 struct PrefillArgs {
     const void *q, *k, *v;
@@ -78,5 +87,6 @@ hipError_t launch_smallseq(const SmallArgs &a, hipStream_t stream);
 hipError_t launch_prefill(const PrefillArgs &a, bool bf16, int D, hipStream_t stream);
 hipError_t launch_prefill_d128(const PrefillArgs &a, hipStream_t stream); // bf16, D = 128
 hipError_t launch_prefill_bwd(const BwdArgs &a, hipStream_t stream);
+hipError_t launch_smallseq_bwd(const SmallBwdArgs &a, hipStream_t stream);
 
 } // namespace attn

@@ -145,6 +145,23 @@ def test_smallseq_validation(lib):
     assert _small(lib, B=0) == _lib.ATTN_OK
 
 
+def test_smallseq_backward_validation(lib):
+    def call(**kw):
+        a = dict(q=FAKE, k=FAKE, v=FAKE, w=FAKE, do=FAKE, cu=FAKE, B=4, H=16, D=128, ms=16, scale=0.1, dq=FAKE,
+                 dk=FAKE, dv=FAKE, stream=None)
+        a.update(kw)
+        return lib.attn_smallseq_cross_backward(a["q"], a["k"], a["v"], a["w"], a["do"], a["cu"], a["B"], a["H"],
+                                                a["D"], a["ms"], a["scale"], a["dq"], a["dk"], a["dv"], a["stream"])
+    assert call(ms=17) == INVALID
+    assert call(B=-1) == INVALID
+    assert call(H=0) == INVALID
+    assert call(scale=math.nan) == INVALID
+    assert call(D=64) == UNSUPPORTED
+    assert call(w=None) == INVALID
+    assert call(dk=None) == INVALID
+    assert call(B=0) == _lib.ATTN_OK
+
+
 def test_status_strings(lib):
     for s in range(5):
         assert lib.attn_status_string(s)

@@ -172,3 +172,59 @@ def test_backward_full_size_sampled_sequences():
                                       x.Hkv, x.scale, True, o=stored[b][0])
         for name, g, r in zip(("dq", "dk", "dv"), (dq[s], dk[s], dv[s]), ref):
             _check(f"{name} of sequence {b} (L {lens[b]})", g, r)
+
+
+# ------------------------------------------------------------------ small-seq backward
+
+def _smallseq_stored(x):
+    """The oracle's attention weights rounded to bf16 (the stored forward state)."""
+    _, w = oracle.smallseq(x.q.cpu(), x.k.cpu(), x.v.cpu(), x.cu_kv.cpu(), x.max_s, x.scale)
+    return torch.from_numpy(w).to(torch.bfloat16)
+
+
+def _smallseq_check(x, do, w):
+    got = attn.attn_smallseq_cross_backward(x.q, x.k, x.v, w.to(DEV), do, x.cu_kv, x.max_s, scale=x.scale)
+    torch.cuda.synchronize()
+    ref = oracle.smallseq_backward(x.q.cpu(), x.k.cpu(), x.v.cpu(), w, do.cpu(), x.cu_kv.cpu(), x.max_s, x.scale)
+    _grads(got, ref)
+    return got, ref
+
+
+@pytest.mark.parametrize("H", [16, 20])
+@pytest.mark.parametrize("fixed", [None, 1, 16])
+def test_smallseq_backward(H, fixed):
+    # key counts from {2..16} (or all 1 / all 16), plus H = 20 for a partial block of 16 heads
+    x = W.smallseq_cross(seed=71, device=DEV, B=257, H=H, fixed=fixed)
+    do = W.grad_output(x, seed=72, device=DEV)
+    _smallseq_check(x, do, _smallseq_stored(x))
+
+
+def test_smallseq_backward_zero_length():
+    # sequences without keys: dq = 0; the other sequences are unaffected
+    g = torch.Generator(device=DEV).manual_seed(5)
+    lens = [3, 0, 16, 0, 1]
+    H, D = 16, 128
+    q = torch.randn(len(lens), H, D, generator=g, device=DEV).bfloat16()
+    k = torch.randn(sum(lens), H, D, generator=g, device=DEV).bfloat16()
+    v = torch.randn(sum(lens), H, D, generator=g, device=DEV).bfloat16()
+    do = torch.randn(len(lens), H, D, generator=g, device=DEV).bfloat16()
+    cu = torch.tensor([0] + list(np.cumsum(lens)), dtype=torch.int32, device=DEV)
+    from types import SimpleNamespace
+    x = SimpleNamespace(q=q, k=k, v=v, cu_kv=cu, max_s=16, scale=D ** -0.5)
+    got, _ = _smallseq_check(x, do, _smallseq_stored(x))
+    dq = _np(got[0])
+    assert np.all(dq[1] == 0) and np.all(dq[3] == 0)
+
+
+def test_smallseq_backward_full_size_chained():
+    # the full small-seq workload (B 30720, s_kv in {2..16}, H 16): every gradient against the oracle on
+    # the oracle's stored weights; then the GPU forward's own weights chained into the GPU backward (its
+    # weights differ from the oracle's by bf16 rounding, so the chained gradients get the L2 bound)
+    x = W.smallseq_cross(seed=1004, device=DEV)
+    do = W.grad_output(x, seed=1006, device=DEV)
+    _, ref = _smallseq_check(x, do, _smallseq_stored(x))
+    _, w_gpu, _ = attn.attn_smallseq_cross(x.q, x.k, x.v, x.cu_kv, x.max_s)
+    chained = attn.attn_smallseq_cross_backward(x.q, x.k, x.v, w_gpu, do, x.cu_kv, x.max_s)
+    torch.cuda.synchronize()
+    for name, g, r in zip(("dq", "dk", "dv"), chained, ref):
+        _check(f"chained {name}", g, r, elementwise=False)
