@@ -49,8 +49,9 @@ def _load():
         lib.orc_smallseq_rows.argtypes = [I, P, P, P, P, I, I, I, I, D, P, I, P, P]
         lib.orc_prefill_bwd.argtypes = [I, P, P, P, P, P, P, P, I, I, I, I, D, I, P, P, P]
         lib.orc_smallseq_bwd.argtypes = [I, P, P, P, P, P, P, I, I, I, I, D, P, P, P]
+        lib.orc_paged_multi_rows.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, D, P, I, P, P]
         for f in (lib.orc_prefill_rows, lib.orc_decode_rows, lib.orc_smallseq_rows, lib.orc_prefill_bwd,
-                  lib.orc_smallseq_bwd):
+                  lib.orc_smallseq_bwd, lib.orc_paged_multi_rows):
             f.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -184,6 +185,33 @@ def smallseq(q, k, v, cu_kv, max_s, scale, rows=None):
         o = o.reshape(B, H, D)
         w = w.reshape(B, H, 1, max(int(max_s), 0))
     return o, w
+
+
+def decode_multi(q, cu_q, k_cache, v_cache, block_table, seq_lens, scale, rows=None):
+    """Multi-token paged decode: q [total_q, Hq, D] THD with cu_q; rows: (token, head) pairs."""
+    qa, dt = _np(q)
+    ka, dk = _np(k_cache)
+    va, dv = _np(v_cache)
+    assert dt == dk == dv == 1, "paged decode is bf16"
+    cq, _ = _np(cu_q)
+    bt, _ = _np(block_table)
+    sl, _ = _np(seq_lens)
+    T, Hq, D = qa.shape
+    B = len(sl)
+    Hkv, page = ka.shape[1], ka.shape[2]
+    allrows = [(t, h) for t in range(T) for h in range(Hq)] if rows is None else None
+    r = _rows_arg(rows, allrows)
+    n = len(r)
+    o = np.zeros((n, D))
+    lse = np.zeros(n)
+    rc = _load().orc_paged_multi_rows(_ptr(qa), _ptr(cq), _ptr(ka), _ptr(va), _ptr(bt), _ptr(sl), B, Hq, Hkv, D,
+                                      page, bt.shape[1], float(scale), _ptr(r), n, _ptr(o), _ptr(lse))
+    if rc != 0:
+        raise ValueError("oracle multi-token decode rejected its arguments")
+    if rows is None:
+        o = o.reshape(T, Hq, D)
+        lse = lse.reshape(T, Hq)
+    return o, lse
 
 
 def smallseq_backward(q, k, v, w, dout, cu_kv, max_s, scale):

@@ -27,8 +27,9 @@
  *               [s c, (s+1) c) and is attended densely to (o_s, lse_s); then
  *               lse = log sum_{finite} exp(lse_s) and o = sum_s exp(lse_s - lse) o_s.
  *
- * Plus the backward of the dense prefill (orc_prefill_bwd) and of the small-seq cross-attention from
- * its stored attention weights (orc_smallseq_bwd), at the end of this file.
+ * Plus multi-token paged decode (orc_paged_multi_rows), the backward of the dense prefill
+ * (orc_prefill_bwd) and of the small-seq cross-attention from its stored attention weights
+ * (orc_smallseq_bwd), at the end of this file.
  *
  * Inputs are read as the exact bytes the GPU reads (fp32, or bf16 widened exactly to fp64); all
  * arithmetic is in fp64.
@@ -521,5 +522,62 @@ int orc_smallseq_bwd(int dtype, const void *q, const void *k, const void *v, con
             free(dw);
             free(wj);
         }
+    return bad ? -1 : 0;
+}
+
+/*
+ * Multi-token paged decode: the paged cache of "Model-Optimizer: Add split-k decode kernel for skip
+ * softmax" (its description keeps multi-token decode on the shared attention kernel, whose summary gives
+ * causal masking over variable-length batches).  Sequence b has Lq_b = cu_q[b+1] - cu_q[b] new query
+ * tokens, the last Lq_b of its seq_lens[b] cached keys; its token i sees the keys
+ * j < clamp(seq_lens[b] - Lq_b + i + 1, 0, seq_lens[b]) (bottom-right causal), key j living in page
+ * block_table[b * max_pages + j / page], slot j % page.  Dense definition per row.
+ * q [total_q, Hq, D] bf16; caches [num_pages, Hkv, page, D] bf16.  rows: (token, head) pairs;
+ * o [n_rows, D], lse [n_rows].
+ */
+int orc_paged_multi_rows(const void *q, const int32_t *cu_q, const void *kc, const void *vc,
+                         const int32_t *block_table, const int32_t *seq_lens, int B, int Hq, int Hkv, int D, int page,
+                         int max_pages, double scale, const int32_t *rows, int n_rows, double *o, double *lse)
+{
+    if (B < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv || D <= 0 || page <= 0)
+        return -1;
+    const int G = Hq / Hkv, tq = B ? cu_q[B] : 0;
+    int bad = 0;
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : bad)
+    for (int r = 0; r < n_rows; ++r) {
+        const int t = rows[2 * r], h = rows[2 * r + 1];
+        if (t < 0 || t >= tq || h < 0 || h >= Hq) {
+            bad = 1;
+            continue;
+        }
+        int b = 0;
+        while (cu_q[b + 1] <= t)
+            ++b;
+        const int L = seq_lens[b], Lq = cu_q[b + 1] - cu_q[b], i = t - cu_q[b];
+        if (L < 0 || L > max_pages * page) {
+            bad = 1;
+            continue;
+        }
+        int n = L - Lq + i + 1;
+        n = n < 0 ? 0 : (n > L ? L : n);
+        const int g = h / G;
+        double *qd = malloc(sizeof(double) * D);
+        double *K = malloc(sizeof(double) * ((size_t)n * D + 1));
+        double *V = malloc(sizeof(double) * ((size_t)n * D + 1));
+        for (int d = 0; d < D; ++d)
+            qd[d] = widen(q, ORC_BF16, ((size_t)t * Hq + h) * D + d);
+        for (int j = 0; j < n; ++j) {
+            const int pg = block_table[(size_t)b * max_pages + j / page];
+            for (int d = 0; d < D; ++d) {
+                const size_t src = (((size_t)pg * Hkv + g) * page + j % page) * D + d;
+                K[(size_t)j * D + d] = widen(kc, ORC_BF16, src);
+                V[(size_t)j * D + d] = widen(vc, ORC_BF16, src);
+            }
+        }
+        dense_row(qd, K, V, n, D, scale, o + (size_t)r * D, lse + r, NULL);
+        free(qd);
+        free(K);
+        free(V);
+    }
     return bad ? -1 : 0;
 }

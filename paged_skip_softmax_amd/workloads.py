@@ -36,7 +36,7 @@ from types import SimpleNamespace
 import torch
 
 # stream ids: one independent generator per purpose
-_S_LEN, _S_Q, _S_K, _S_V, _S_PERM, _S_HOT, _S_DO = range(7)
+_S_LEN, _S_Q, _S_K, _S_V, _S_PERM, _S_HOT, _S_DO, _S_QLEN = range(8)
 
 
 def _gen(seed: int, stream: int, device="cpu") -> torch.Generator:
@@ -208,6 +208,21 @@ def paged_decode(seed=1002, device="cpu", B=64, Hq=32, Hkv=8, D=128, lmin=1024, 
 def paged_decode_hot(seed=1002, device="cpu", **kw):
     """The hot-key decode workload; with the same seed its lengths, Q, V and table equal paged_decode's."""
     return paged_decode(seed=seed, device=device, hot=True, **kw)
+
+
+def paged_decode_multi(seed=1003, device="cpu", qmin=1, qmax=4, **kw):
+    """Multi-token paged decode: ``paged_decode``'s cache plus Lq_b ~ U{qmin..qmax} new query tokens per
+    sequence (at most L_b), packed THD with cu_seqlens_q; they are the last Lq_b of the L_b cached keys."""
+    x = paged_decode(seed=seed, device=device, **kw)
+    g = _gen(seed, _S_QLEN)
+    ql = torch.randint(qmin, qmax + 1, (x.B,), generator=g, dtype=torch.int64)
+    ql = torch.minimum(ql, x.lens)
+    cu = _cu(ql)
+    x.q = _randn((int(cu[-1]), x.Hq, x.D), seed, _S_Q, device, torch.bfloat16)
+    x.cu_q = cu.to(device)
+    x.qlens = ql
+    x.max_q = int(ql.max()) if x.B else 0
+    return x
 
 
 def smallseq_cross(seed=1004, device="cpu", B=30720, H=16, D=128, choices=(2, 4, 6, 8, 12, 16),

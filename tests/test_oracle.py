@@ -556,3 +556,55 @@ def test_smallseq_backward_padding_and_closed_forms():
     # the weights enter dv linearly: doubling w doubles dv
     _, _, dv2 = oracle.smallseq_backward(q, k, v, w * 2, do, cu, ms, scale)
     assert np.max(np.abs(dv2 - 2 * dv)) < 1e-12
+
+
+def _paged_from_contiguous(k, v, lens, Hkv, D, page=16, seed=91):
+    """A bf16 paged cache [pages, Hkv, page, D] holding the contiguous k, v [sum(lens), Hkv, D] through a
+    permuted block table; unused slots NaN."""
+    g = torch.Generator().manual_seed(seed)
+    npg = [(L + page - 1) // page for L in lens]
+    pool = sum(npg) + 3
+    perm = torch.randperm(pool, generator=g)
+    maxp = max(npg)
+    bt = torch.full((len(lens), maxp), -1, dtype=torch.int32)
+    kc = torch.full((pool, Hkv, page, D), float("nan"), dtype=torch.bfloat16)
+    vc = kc.clone()
+    off, tok = 0, 0
+    for b, L in enumerate(lens):
+        for p in range(npg[b]):
+            pg = int(perm[off + p])
+            bt[b, p] = pg
+            n = min(page, L - p * page)
+            kc[pg, :, :n] = k[tok + p * page:tok + p * page + n].transpose(0, 1)
+            vc[pg, :, :n] = v[tok + p * page:tok + p * page + n].transpose(0, 1)
+        off += npg[b]
+        tok += L
+    return kc, vc, bt
+
+
+def test_decode_multi_equals_contiguous_causal_prefill():
+    # the paged multi-token rows equal the (separately pinned) contiguous varlen prefill with bottom-right
+    # causal alignment, Lq != Lk, over the same keys
+    lens, qlens, Hq, Hkv, D = [20, 33, 5, 16], [3, 1, 5, 16], 4, 2, 16
+    g = torch.Generator().manual_seed(90)
+    k = torch.randn(sum(lens), Hkv, D, generator=g).bfloat16()
+    v = torch.randn(sum(lens), Hkv, D, generator=g).bfloat16()
+    q = torch.randn(sum(qlens), Hq, D, generator=g).bfloat16()
+    kc, vc, bt = _paged_from_contiguous(k, v, lens, Hkv, D)
+    cu_q = torch.tensor([0] + list(np.cumsum(qlens)), dtype=torch.int32)
+    cu_k = torch.tensor([0] + list(np.cumsum(lens)), dtype=torch.int32)
+    sl = torch.tensor(lens, dtype=torch.int32)
+    om, lm = oracle.decode_multi(q, cu_q, kc, vc, bt, sl, 0.25)
+    op, lp, _ = oracle.prefill(q, k, v, cu_q, cu_k, Hq, Hkv, 0.25, True)
+    assert np.max(np.abs(om - op)) < 1e-12
+    assert np.max(np.abs(lm - lp)) < 1e-12
+
+
+def test_decode_multi_one_token_equals_decode():
+    # with one new token per sequence the rows are the (separately pinned) one-token paged decode
+    x = W.paged_decode(seed=93, B=5, Hq=8, Hkv=2, D=32, lmin=1, lmax=70, pool=64)
+    cu_q = torch.arange(x.B + 1, dtype=torch.int32)
+    om, lm = oracle.decode_multi(x.q, cu_q, x.k_cache, x.v_cache, x.block_table, x.seq_lens, x.scale)
+    od, ld, _ = oracle.decode(x.q, x.k_cache, x.v_cache, x.block_table, x.seq_lens, x.scale)
+    assert np.max(np.abs(om - od)) < 1e-12
+    assert np.max(np.abs(lm - ld)) < 1e-12
