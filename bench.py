@@ -39,8 +39,8 @@ def _parse():
     p.add_argument("--seed", type=int, default=0)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--only", default="",
-                   help="comma list of prefill,prefill_skip,decode,skip,smallseq,prefill_bwd,smallseq_bwd "
-                        "(profiling runs)")
+                   help="comma list of prefill,prefill_skip,decode,skip,smallseq,prefill_bwd,smallseq_bwd,"
+                        "decode_multi (profiling runs)")
     p.add_argument("--calib-copy", action="store_true",
                    help="also run one plain 1 GiB device-to-device copy (scales HBM byte counters)")
     p.add_argument("--summarize-profiles", metavar="DIR", default="",
@@ -92,7 +92,8 @@ def main():
     from paged_skip_softmax_amd import workloads as W
 
     only = (set(args.only.split(",")) if args.only
-            else {"prefill", "prefill_skip", "decode", "skip", "smallseq", "prefill_bwd", "smallseq_bwd"})
+            else {"prefill", "prefill_skip", "decode", "skip", "smallseq", "prefill_bwd", "smallseq_bwd",
+                  "decode_multi"})
     dev = "cuda:0"
     torch.cuda.set_device(0)
     t_gen = time.time()
@@ -133,6 +134,16 @@ def main():
         gs = (torch.empty_like(cb.q), torch.empty_like(cb.k), torch.empty_like(cb.v))
         nxt["smallseq_bwd"] = lambda: attn.attn_smallseq_cross_backward(
             cb.q, cb.k, cb.v, w_s, do_s, cb.cu_kv, cb.max_s, dq=gs[0], dk=gs[1], dv=gs[2])
+
+    if "decode_multi" in only:
+        dm = W.paged_decode_multi(seed=1002 + args.seed, device=dev)
+        work["decode_multi"] = dm
+        ws_m = torch.empty(attn.attn_decode_paged_multi_workspace_size(dm.q.shape[0], dm.Hq, dm.D, 32),
+                           dtype=torch.uint8, device=dev)
+        o_m = torch.empty_like(dm.q)
+        nxt["decode_multi"] = lambda: attn.attn_decode_paged_multi(
+            dm.q, dm.cu_q, dm.max_q, dm.k_cache, dm.v_cache, dm.block_table, dm.seq_lens, num_splits=32,
+            workspace=ws_m, out=o_m)
 
     calls = {}  # name -> zero-arg launcher
     if "prefill" in only:
@@ -332,6 +343,18 @@ def main():
         out["smallseq_bwd"] = {"ms": t, "ms_min": ms_min["smallseq_bwd"], "bytes_alg": byts, "GBps": gb,
                                "frac_peak": gb / PEAK_HBM_GBPS, "note": "one launch; timed outside the step"}
 
+    if "decode_multi" in only:
+        dm = work["decode_multi"]
+        # every cached key of every KV head once (one 16-row block per group when Lq * G <= 16)
+        kv = 4.0 * dm.Hkv * dm.D * float(dm.lens.sum())
+        t = ms["decode_multi"]
+        gb = kv / (t * 1e-3) / 1e9
+        out["decode_multi"] = {"ms": t, "ms_min": ms_min["decode_multi"], "kv_bytes": kv, "kv_GBps": gb,
+                               "frac_peak": gb / PEAK_HBM_GBPS, "tokens": int(dm.q.shape[0]),
+                               "note": "split kernel + merge; timed outside the step"}
+        if "decode" in out:
+            out["decode_multi"]["time_over_one_token_decode"] = t / out["decode"]["ms"]
+
     # the dominant kernel: the largest share of the step
     dom = max(rooflines, key=lambda r: r["ms"]) if rooflines else None
     roofline = None
@@ -371,7 +394,9 @@ def main():
                                       "sequential skip decode thr {0,0.01,0.1} on hot keys",
                                       "small-seq cross B=30720 s_kv in {2..16} H=16 D=128"],
                    "timed_after_the_step": ["the prefill backward (dq, dk, dv) on the prefill shapes",
-                                            "the small-seq backward from the stored weights on the small-seq shapes"],
+                                            "the small-seq backward from the stored weights on the small-seq shapes",
+                                            "multi-token paged decode: the paged-decode cache with 1..4 new tokens "
+                                            "per sequence, 32 splits"],
                    "seed": args.seed},
         "roofline": roofline,
         "cpu_baseline": cpu,
@@ -505,6 +530,12 @@ PROFILED = {
     "decode_merge_kernel": ("merge of the 32 split partials, B=64, Hq=32, D=128",
                             "decode_merge_kernel.paged_decode_B64_Hq32_32splits",
                             ["paged_skip_softmax_amd/csrc/decode.hip"] + _KSRC),
+    "decode_multi_kernel": ("multi-token paged decode: the paged-decode cache (B=64, L~U[1024,32768]) with 1..4 new "
+                            "tokens per sequence, 32 splits", "decode_multi_kernel.paged_decode_B64_L1k-32k_q1-4_32splits",
+                            ["paged_skip_softmax_amd/csrc/decode.hip"] + _KSRC),
+    "decode_merge_multi_kernel": ("merge of the 32 split partials of the multi-token decode (1..4 tokens x 32 heads "
+                                  "per sequence, B=64)", "decode_merge_multi_kernel.paged_decode_B64_q1-4_32splits",
+                                  ["paged_skip_softmax_amd/csrc/decode.hip"] + _KSRC),
     "decode_seq_kernel": ("sequential skip decode on hot keys, B=64, L~U[1024,32768], 32-key tiles, "
                           "threshold 0 / 0.01 / 0.1 in turn",
                           "decode_seq_kernel.paged_decode_hot_B64_thr0-0.01-0.1",

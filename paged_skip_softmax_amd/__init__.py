@@ -18,7 +18,8 @@ from . import _lib
 from ._lib import SKIP_TILE, AttnError  # noqa: F401
 
 __all__ = ["attn_prefill_varlen", "attn_prefill_varlen_backward", "attn_prefill_varlen_backward_workspace_size",
-           "attn_decode_paged", "attn_decode_paged_workspace_size", "attn_smallseq_cross",
+           "attn_decode_paged", "attn_decode_paged_workspace_size", "attn_decode_paged_multi",
+           "attn_decode_paged_multi_workspace_size", "attn_smallseq_cross",
            "attn_smallseq_cross_backward", "AttnError", "SKIP_TILE"]
 
 
@@ -163,6 +164,47 @@ def attn_decode_paged(q, k_cache, v_cache, block_table, seq_lens, *, scale=None,
                                      float(skip_threshold), int(splits), _ptr(workspace), ws_bytes, out.data_ptr(),
                                      _ptr(lse), _ptr(smap), stride, _stream(q)))
     return out, lse, smap
+
+
+def attn_decode_paged_multi_workspace_size(total_q: int, Hq: int, D: int, num_splits: int = 0) -> int:
+    """Workspace bytes of the multi-token decode's split-K partials."""
+    return int(_lib.load().attn_decode_paged_multi_workspace_size(total_q, Hq, D, num_splits))
+
+
+def attn_decode_paged_multi(q, cu_seqlens_q, max_seqlen_q, k_cache, v_cache, block_table, seq_lens, *, scale=None,
+                            num_splits=0, workspace=None, out=None, return_lse=False):
+    """Multi-token paged decode (THD queries, bottom-right causal).  Returns (o, lse or None)."""
+    lib = _lib.load()
+    dev = q.device
+    _cuda_contig("q", q, torch.bfloat16)
+    for name, t in (("k_cache", k_cache), ("v_cache", v_cache)):
+        _cuda_contig(name, t, torch.bfloat16, dev)
+    for name, t in (("cu_seqlens_q", cu_seqlens_q), ("block_table", block_table), ("seq_lens", seq_lens)):
+        _cuda_contig(name, t, torch.int32, dev)
+    _need(q.dim() == 3 and k_cache.dim() == 4 and k_cache.shape == v_cache.shape,
+          "q [total_q,Hq,D], caches [pages,Hkv,page,D]")
+    total_q, Hq, D = q.shape
+    num_pages, Hkv, page, Dk = k_cache.shape
+    _need(Dk == D, "head dims differ")
+    B = seq_lens.numel()
+    _need(cu_seqlens_q.numel() == B + 1 and block_table.dim() == 2 and block_table.shape[0] == B,
+          "cu_seqlens_q [B + 1], block_table [B, max_pages], seq_lens [B]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    need = attn_decode_paged_multi_workspace_size(total_q, Hq, D, num_splits)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    if out is None:
+        out = torch.empty_like(q)
+    _cuda_contig("out", out, torch.bfloat16, dev)
+    lse = torch.empty((total_q, Hq), dtype=torch.float32, device=dev) if return_lse else None
+    _lib.check(lib.attn_decode_paged_multi(q.data_ptr(), cu_seqlens_q.data_ptr(), total_q, int(max_seqlen_q),
+                                           k_cache.data_ptr(), v_cache.data_ptr(), block_table.data_ptr(),
+                                           seq_lens.data_ptr(), B, Hq, Hkv, D, page, num_pages, block_table.shape[1],
+                                           float(scale), int(num_splits), _ptr(workspace), ws_bytes, out.data_ptr(),
+                                           _ptr(lse), _stream(q)))
+    return out, lse
 
 
 def attn_smallseq_cross(q, k, v, cu_seqlens_kv, max_seqlen_kv, *, scale=None, return_weights=True,

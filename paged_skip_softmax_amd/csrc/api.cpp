@@ -4,6 +4,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -217,6 +218,72 @@ attn_status_t attn_prefill_varlen_backward(attn_dtype_t dtype, const void *q, co
     a.dv = dv;
     return hip_status(attn::launch_prefill_bwd(a, static_cast<hipStream_t>(stream)),
                       "prefill backward launch");
+}
+
+size_t attn_decode_paged_multi_workspace_size(int32_t total_q, int32_t Hq, int32_t D, int32_t num_splits)
+{
+    if (total_q <= 0 || Hq <= 0 || D <= 0)
+        return 0;
+    const int S = num_splits == 0 ? kDefaultSplits : num_splits;
+    return (size_t)total_q * Hq * S * (D + 1) * sizeof(float);
+}
+
+attn_status_t attn_decode_paged_multi(const void *q, const int32_t *cu_seqlens_q, int32_t total_q,
+                                      int32_t max_seqlen_q, const void *k_cache, const void *v_cache,
+                                      const int32_t *block_table, const int32_t *seq_lens, int32_t B, int32_t Hq,
+                                      int32_t Hkv, int32_t D, int32_t page_size, int32_t num_pages,
+                                      int32_t max_pages_per_seq, float scale, int32_t num_splits, void *workspace,
+                                      size_t workspace_bytes, void *o, float *lse, void *stream)
+{
+    if (B < 0 || total_q < 0 || max_seqlen_q < 0)
+        return fail(ATTN_ERR_INVALID, "attn_decode_paged_multi: negative B, total_q or max_seqlen_q");
+    if (Hq <= 0 || Hkv <= 0 || Hq % Hkv)
+        return fail(ATTN_ERR_INVALID, "attn_decode_paged_multi: Hq = %d must be a positive multiple of Hkv = %d", Hq,
+                    Hkv);
+    if (num_splits < 0 || num_splits > kMaxSplits)
+        return fail(ATTN_ERR_INVALID, "attn_decode_paged_multi: num_splits %d outside [0, %d]", num_splits,
+                    kMaxSplits);
+    if (!std::isfinite(scale))
+        return fail(ATTN_ERR_INVALID, "attn_decode_paged_multi: scale is not finite");
+    if (num_pages <= 0 || max_pages_per_seq <= 0 || page_size <= 0)
+        return fail(ATTN_ERR_INVALID, "attn_decode_paged_multi: num_pages, max_pages_per_seq and page_size must be > 0");
+    if (D != 128)
+        return fail(ATTN_ERR_UNSUPPORTED, "attn_decode_paged_multi: D = %d (built for 128)", D);
+    if (page_size != 16)
+        return fail(ATTN_ERR_UNSUPPORTED, "attn_decode_paged_multi: page_size = %d (built for 16)", page_size);
+    if ((int64_t)max_seqlen_q * (Hq / Hkv) > 64)
+        return fail(ATTN_ERR_UNSUPPORTED, "attn_decode_paged_multi: max_seqlen_q * Hq / Hkv = %lld > 64 (a query "
+                                          "chunk this long belongs to a prefill kernel)",
+                    (long long)max_seqlen_q * (Hq / Hkv));
+    if (B == 0 || total_q == 0)
+        return ok();
+    if (!q || !cu_seqlens_q || !k_cache || !v_cache || !block_table || !seq_lens || !o)
+        return fail(ATTN_ERR_INVALID, "attn_decode_paged_multi: a required pointer is NULL");
+    const int S = num_splits == 0 ? kDefaultSplits : num_splits;
+    const size_t need = attn_decode_paged_multi_workspace_size(total_q, Hq, D, S);
+    if (!workspace || workspace_bytes < need)
+        return fail(ATTN_ERR_WORKSPACE, "attn_decode_paged_multi: workspace %zu bytes, need %zu", workspace_bytes,
+                    need);
+    const int G = Hq / Hkv;
+    attn::MultiArgs a{};
+    a.q = static_cast<const uint16_t *>(q);
+    a.cu_q = cu_seqlens_q;
+    a.kc = static_cast<const uint16_t *>(k_cache);
+    a.vc = static_cast<const uint16_t *>(v_cache);
+    a.bt = block_table;
+    a.seq_lens = seq_lens;
+    a.Hq = Hq;
+    a.Hkv = Hkv;
+    a.G = G;
+    a.max_pages = max_pages_per_seq;
+    a.num_splits = S;
+    a.ncb = std::max(1, (max_seqlen_q * G + 15) / 16);
+    a.scale_log2 = scale * 1.4426950408889634f;
+    a.ws_o = static_cast<float *>(workspace);
+    a.ws_lse = a.ws_o + (size_t)total_q * Hq * S * D;
+    return hip_status(attn::launch_decode_multi(a, B, total_q, static_cast<uint16_t *>(o), lse,
+                                                static_cast<hipStream_t>(stream)),
+                      "multi-token decode launch");
 }
 
 attn_status_t attn_smallseq_cross(const void *q, const void *k, const void *v, const int32_t *cu_seqlens_kv,

@@ -313,7 +313,7 @@ struct MergeArgs {
 };
 
 // One wave per (batch row, query head): lse = log sum_s e^{lse_s}, O = sum_s e^{lse_s - lse} O_s.
-__global__ __launch_bounds__(256) void decode_merge_kernel(MergeArgs a)
+__device__ __forceinline__ void merge_rows(const MergeArgs &a)
 {
     const int lane = threadIdx.x & 63;
     const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -344,6 +344,11 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(MergeArgs a)
         a.lse[row] = lse;
 }
 
+__global__ __launch_bounds__(256) void decode_merge_kernel(MergeArgs a) { merge_rows(a); }
+
+// The same merge for the (token, head) rows of the multi-token decode (a name of its own in traces).
+__global__ __launch_bounds__(256) void decode_merge_multi_kernel(MergeArgs a) { merge_rows(a); }
+
 hipError_t launch_decode_split(const SplitArgs &a, int B, uint16_t *o, float *lse, hipStream_t stream)
 {
     hipLaunchKernelGGL(decode_split_kernel, dim3(a.num_splits, a.Hkv, B), dim3(64 * kSplitWaves), 0, stream, a);
@@ -352,6 +357,141 @@ hipError_t launch_decode_split(const SplitArgs &a, int B, uint16_t *o, float *ls
         return e;
     MergeArgs m{a.ws_o, a.ws_lse, B * a.Hq, a.num_splits, o, lse};
     hipLaunchKernelGGL(decode_merge_kernel, dim3((B * a.Hq + 3) / 4), dim3(256), 0, stream, m);
+    return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ multi-token decode (split-K)
+
+// Raw scores of a chunk for per-column key limits: keys at or past lim (the lane's column) are -inf;
+// lim_min (wave-uniform) lets chunks below every column's limit skip the masking.
+__device__ __forceinline__ float chunk_scores_lim(const uint4 kr[2][4], const bf16x8 qop[4], int tok0, int lim,
+                                                  int lim_min, int lane, f32x4 sc[2])
+{
+    const int j = lane >> 4;
+#pragma unroll
+    for (int pg = 0; pg < 2; ++pg) {
+        sc[pg] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+            sc[pg] = mfma16(as_bf16x8(kr[pg][s]), qop[s], sc[pg]);
+    }
+    const bool partial = tok0 + 2 * kPage > lim_min;
+    float cmax = kNegInf;
+#pragma unroll
+    for (int pg = 0; pg < 2; ++pg)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            if (partial && tok0 + kPage * pg + 4 * j + i >= lim)
+                sc[pg][i] = kNegInf;
+            cmax = fmaxf(cmax, sc[pg][i]);
+        }
+    return max_across_groups16(cmax);
+}
+
+// Multi-token decode: sequence b has Lq = cu_q[b+1] - cu_q[b] new tokens, the last Lq of its L cached
+// keys; token i sees keys [0, L - Lq + i + 1) (bottom-right causal).  The Lq * G (token, head) rows of a
+// KV head's group ride in the MFMA's 16 columns, 16 rows per workgroup (column n <-> row 16 cb + n:
+// token (16 cb + n) / G, head g G + (16 cb + n) % G), so one read of the cache serves up to 16 rows;
+// otherwise the same split-K schedule, chunk pipeline and partials as decode_split_kernel, over the
+// keys the block's last token sees.
+__global__ __launch_bounds__(64 * kSplitWaves) void decode_multi_kernel(MultiArgs a)
+{
+    const int sp = blockIdx.x, g = blockIdx.y, b = blockIdx.z / a.ncb, cb = blockIdx.z % a.ncb;
+    const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int q0 = a.cu_q[b], Lq = a.cu_q[b + 1] - q0;
+    const int r0 = 16 * cb;
+    if (r0 >= Lq * a.G)
+        return;
+    const int nc = min(16, Lq * a.G - r0); // columns in use
+    const int L = a.seq_lens[b];
+    const int n = lane & 15, j = lane >> 4;
+    const bool col_ok = n < nc;
+    const int ti = (r0 + n) / a.G;         // the column's token
+    auto key_end = [&](int i) { return max(0, min(L, L - Lq + i + 1)); };
+    const int kend = key_end((r0 + nc - 1) / a.G); // keys the block's last token sees
+    const int S = a.num_splits;
+    const int ntiles = (kend + kSplitTile - 1) / kSplitTile;
+    const int per = (ntiles + S - 1) / S;
+    const int t0 = min(sp * per * kSplitTile, kend);
+    const int t1 = min((sp + 1) * per * kSplitTile, kend);
+    const int lim = col_ok ? min(key_end(ti), t1) : 0;
+    const int lim_min = min(key_end(r0 / a.G), t1);
+
+    __shared__ __attribute__((aligned(16))) uint16_t smem[kSplitWaves * kVTile];
+    static_assert(sizeof(smem) >= kSplitWaves * 16 * (kD + 2) * sizeof(float), "merge buffer");
+    uint16_t *vt = smem + w * kVTile;
+
+    // Q^T operand: lane (n, j) holds the column's row, d = 32 s + 8 j .. +8
+    bf16x8 qop[4];
+    if (col_ok) {
+        const uint16_t *qp = a.q + ((size_t)(q0 + ti) * a.Hq + (size_t)g * a.G + (r0 + n) % a.G) * kD + 8 * j;
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+            qop[s] = as_bf16x8(ld16(qp + 32 * s));
+    } else {
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+            qop[s] = as_bf16x8(make_uint4(0, 0, 0, 0));
+    }
+    WaveState st;
+    state_init(st);
+    const int32_t *btr = a.bt + (size_t)b * a.max_pages;
+    const size_t slab = (size_t)kPage * kD;
+    auto chunk_off = [&](int tok0, size_t &o0, size_t &o1) {
+        const int tt = tok0 < t1 ? tok0 : t0;
+        const int p0 = btr[tt / kPage];
+        const int p1 = tt + kPage < t1 ? btr[tt / kPage + 1] : p0;
+        o0 = ((size_t)p0 * a.Hkv + g) * slab;
+        o1 = ((size_t)p1 * a.Hkv + g) * slab;
+    };
+    const int step = 2 * kPage * kSplitWaves;
+    int tok0 = t0 + 2 * kPage * w;
+    if (tok0 < t1) {
+        size_t o0, o1;
+        chunk_off(tok0, o0, o1);
+        uint4 kr[2][4], vr[2][4];
+        load_k_chunk(a.kc + o0, a.kc + o1, lane, kr);
+        load_v_chunk(a.vc + o0, a.vc + o1, lane, vr);
+        for (; tok0 < t1; tok0 += step) {
+            size_t n0, n1;
+            chunk_off(tok0 + step, n0, n1);
+            uint4 kn[2][4], vn[2][4];
+            const bool more = tok0 + step < t1;
+            if (more) {
+                load_k_chunk(a.kc + n0, a.kc + n1, lane, kn);
+                load_v_chunk(a.vc + n0, a.vc + n1, lane, vn);
+            }
+            f32x4 sc[2];
+            const float cmax = chunk_scores_lim(kr, qop, tok0, lim, lim_min, lane, sc);
+            chunk_update(st, sc, cmax * a.scale_log2, true, vr, tok0, t1, a.scale_log2, vt, lane);
+            if (more) {
+#pragma unroll
+                for (int pg = 0; pg < 2; ++pg)
+#pragma unroll
+                    for (int s4 = 0; s4 < 4; ++s4) {
+                        kr[pg][s4] = kn[pg][s4];
+                        vr[pg][s4] = vn[pg][s4];
+                    }
+            }
+        }
+    }
+    merge_waves<kSplitWaves>(st, smem, nc, [&](int h, int d, float o, float lse) {
+        const size_t row = (size_t)(q0 + (r0 + h) / a.G) * a.Hq + (size_t)g * a.G + (r0 + h) % a.G;
+        a.ws_o[(row * S + sp) * kD + d] = o;
+        if (d == 0)
+            a.ws_lse[row * S + sp] = lse;
+    });
+}
+
+hipError_t launch_decode_multi(const MultiArgs &a, int B, int total_q, uint16_t *o, float *lse, hipStream_t stream)
+{
+    hipLaunchKernelGGL(decode_multi_kernel, dim3(a.num_splits, a.Hkv, B * a.ncb), dim3(64 * kSplitWaves), 0, stream,
+                       a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess)
+        return e;
+    MergeArgs m{a.ws_o, a.ws_lse, total_q * a.Hq, a.num_splits, o, lse};
+    hipLaunchKernelGGL(decode_merge_multi_kernel, dim3((total_q * a.Hq + 3) / 4), dim3(256), 0, stream, m);
     return hipGetLastError();
 }
 

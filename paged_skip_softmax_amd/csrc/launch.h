@@ -21,6 +21,18 @@ struct SplitArgs {
     float *ws_lse;          // [B, Hq, S], natural log
 };
 
+// Multi-token paged decode: split-K over the cache for the (token, head) rows of each KV head's group.
+struct MultiArgs {
+    const uint16_t *q;      // [total_q, Hq, D] bf16
+    const int32_t *cu_q;    // [B + 1]
+    const uint16_t *kc, *vc;
+    const int32_t *bt, *seq_lens;
+    int Hq, Hkv, G, max_pages, num_splits, ncb; // ncb: 16-row blocks per (sequence, KV head)
+    float scale_log2;
+    float *ws_o;            // [total_q, Hq, S, D]
+    float *ws_lse;          // [total_q, Hq, S]
+};
+
 // Sequential paged decode with skip-softmax over 32-key tiles (num_splits == 1).
 struct SeqArgs {
     const uint16_t *q, *kc, *vc;
@@ -83,6 +95,7 @@ struct BwdArgs {
 
 hipError_t launch_decode_split(const SplitArgs &a, int B, uint16_t *o, float *lse, hipStream_t stream);
 hipError_t launch_decode_seq(const SeqArgs &a, int B, hipStream_t stream);
+hipError_t launch_decode_multi(const MultiArgs &a, int B, int total_q, uint16_t *o, float *lse, hipStream_t stream);
 hipError_t launch_smallseq(const SmallArgs &a, hipStream_t stream);
 hipError_t launch_prefill(const PrefillArgs &a, bool bf16, int D, hipStream_t stream);
 hipError_t launch_prefill_d128(const PrefillArgs &a, hipStream_t stream); // bf16, D = 128

@@ -210,9 +210,10 @@ def paged_decode_hot(seed=1002, device="cpu", **kw):
     return paged_decode(seed=seed, device=device, hot=True, **kw)
 
 
-def paged_decode_multi(seed=1003, device="cpu", qmin=1, qmax=4, **kw):
-    """Multi-token paged decode: ``paged_decode``'s cache plus Lq_b ~ U{qmin..qmax} new query tokens per
-    sequence (at most L_b), packed THD with cu_seqlens_q; they are the last Lq_b of the L_b cached keys."""
+def paged_decode_multi(seed=1002, device="cpu", qmin=1, qmax=4, **kw):
+    """Multi-token paged decode: ``paged_decode``'s cache (the same one for the same seed) plus
+    Lq_b ~ U{qmin..qmax} new query tokens per sequence (at most L_b), packed THD with cu_seqlens_q; they
+    are the last Lq_b of the L_b cached keys."""
     x = paged_decode(seed=seed, device=device, **kw)
     g = _gen(seed, _S_QLEN)
     ql = torch.randint(qmin, qmax + 1, (x.B,), generator=g, dtype=torch.int64)

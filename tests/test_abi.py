@@ -162,6 +162,29 @@ def test_smallseq_backward_validation(lib):
     assert call(B=0) == _lib.ATTN_OK
 
 
+def test_decode_multi_validation(lib):
+    def call(**kw):
+        a = dict(q=FAKE, cq=FAKE, tq=10, mq=4, kc=FAKE, vc=FAKE, bt=FAKE, sl=FAKE, B=4, Hq=32, Hkv=8, D=128, page=16,
+                 pages=100, maxp=10, scale=0.1, splits=0, ws=FAKE, wsb=1 << 30, o=FAKE, lse=None, stream=None)
+        a.update(kw)
+        return lib.attn_decode_paged_multi(a["q"], a["cq"], a["tq"], a["mq"], a["kc"], a["vc"], a["bt"], a["sl"],
+                                           a["B"], a["Hq"], a["Hkv"], a["D"], a["page"], a["pages"], a["maxp"],
+                                           a["scale"], a["splits"], a["ws"], a["wsb"], a["o"], a["lse"], a["stream"])
+    assert lib.attn_decode_paged_multi_workspace_size(10, 32, 128, 0) == 10 * 32 * 32 * 129 * 4
+    assert lib.attn_decode_paged_multi_workspace_size(10, 32, 128, 7) == 10 * 32 * 7 * 129 * 4
+    assert call(B=-1) == INVALID
+    assert call(Hkv=5) == INVALID
+    assert call(splits=65) == INVALID
+    assert call(scale=math.inf) == INVALID
+    assert call(D=64) == UNSUPPORTED
+    assert call(page=32) == UNSUPPORTED
+    assert call(mq=17) == UNSUPPORTED   # 17 tokens x 4 heads > 64 rows
+    assert call(cq=None) == INVALID
+    assert call(wsb=100) == WORKSPACE
+    assert call(B=0) == _lib.ATTN_OK
+    assert call(tq=0) == _lib.ATTN_OK
+
+
 def test_status_strings(lib):
     for s in range(5):
         assert lib.attn_status_string(s)

@@ -1,0 +1,87 @@
+"""GPU parity of the multi-token paged decode (bottom-right causal over the paged cache) against the fp64
+oracle, through the C ABI.  Same bars as the one-token decode: 2e-2 max-abs on the bf16 outputs (unit
+variance V), 1e-3 on the LSE, exact agreement on which rows see no key."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import paged_skip_softmax_amd as attn
+from paged_skip_softmax_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+BF16_TOL = 2e-2
+LSE_TOL = 1e-3
+
+
+def _np(t):
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def _compare(x, o, lse, rows=None):
+    od, ld = oracle.decode_multi(x.q.cpu(), x.cu_q.cpu(), x.k_cache.cpu(), x.v_cache.cpu(), x.block_table.cpu(),
+                                 x.seq_lens.cpu(), x.scale, rows=rows)
+    on, ln = _np(o), _np(lse)
+    if rows is not None:
+        r = np.array(rows)
+        on, ln = on[r[:, 0], r[:, 1]], ln[r[:, 0], r[:, 1]]
+    assert np.isfinite(on).all(), "NaN poison reached the output"
+    assert np.max(np.abs(on - od)) <= BF16_TOL
+    fin = np.isfinite(ld)
+    assert np.array_equal(fin, np.isfinite(ln))
+    if fin.any():
+        assert np.max(np.abs(ln[fin] - ld[fin])) <= LSE_TOL
+    assert np.all(on[~fin] == 0)
+
+
+@pytest.mark.parametrize("splits", [1, 7, 32])
+def test_decode_multi_small(splits):
+    # 12 sequences of 1..300 cached keys, 1..8 new tokens each (G = 4: up to 2 blocks of 16 rows)
+    x = W.paged_decode_multi(seed=61, device=DEV, B=12, Hq=8, Hkv=2, lmin=1, lmax=300, pool=400, qmin=1, qmax=8)
+    o, lse = attn.attn_decode_paged_multi(x.q, x.cu_q, x.max_q, x.k_cache, x.v_cache, x.block_table, x.seq_lens,
+                                          num_splits=splits, return_lse=True)
+    torch.cuda.synchronize()
+    _compare(x, o, lse)
+
+
+@pytest.mark.parametrize("Hq,Hkv,qmax", [(8, 8, 64), (32, 2, 4), (12, 3, 16)])
+def test_decode_multi_groupings(Hq, Hkv, qmax):
+    # G = 1 with up to 64 tokens, G = 16 with up to 4, G = 4 with up to 16: every row-block count 1..4
+    x = W.paged_decode_multi(seed=62, device=DEV, B=6, Hq=Hq, Hkv=Hkv, lmin=40, lmax=500, pool=300, qmin=1,
+                             qmax=qmax)
+    o, lse = attn.attn_decode_paged_multi(x.q, x.cu_q, x.max_q, x.k_cache, x.v_cache, x.block_table, x.seq_lens,
+                                          return_lse=True)
+    torch.cuda.synchronize()
+    _compare(x, o, lse)
+
+
+def test_decode_multi_tokens_without_keys():
+    # more new tokens than cached keys: the leading tokens see no key (o = 0, lse = -inf); a one-key
+    # sequence and an empty one
+    x = W.paged_decode_multi(seed=63, device=DEV, B=4, Hq=8, Hkv=2, lengths=[5, 1, 0, 40], pool=64, qmin=1, qmax=1)
+    lq = torch.tensor([9, 3, 2, 16])
+    cu = torch.cat([torch.zeros(1, dtype=torch.int64), lq.cumsum(0)])
+    g = torch.Generator(device=DEV).manual_seed(64)
+    x.q = torch.randn(int(cu[-1]), x.Hq, x.D, generator=g, device=DEV).bfloat16()
+    x.cu_q = cu.to(torch.int32).to(DEV)
+    o, lse = attn.attn_decode_paged_multi(x.q, x.cu_q, 16, x.k_cache, x.v_cache, x.block_table, x.seq_lens,
+                                          num_splits=4, return_lse=True)
+    torch.cuda.synchronize()
+    _compare(x, o, lse)
+    assert not np.isfinite(_np(lse)).all()
+
+
+def test_decode_multi_full_size_sampled():
+    # the full paged-decode cache (B 64, L in [1024, 32768], 140,000-page pool) with 1..4 new tokens per
+    # sequence, 32 splits (the benchmark's configuration); every token and head of a sample of sequences
+    x = W.paged_decode_multi(seed=1002, device=DEV)
+    o, lse = attn.attn_decode_paged_multi(x.q, x.cu_q, x.max_q, x.k_cache, x.v_cache, x.block_table, x.seq_lens,
+                                          num_splits=32, return_lse=True)
+    torch.cuda.synchronize()
+    L = x.lens.numpy()
+    cu = x.cu_q.cpu().tolist()
+    bs = sorted({int(np.argmax(L)), int(np.argmin(L))} | set(range(0, x.B, 7)))
+    rows = [(t, h) for b in bs for t in range(cu[b], cu[b + 1]) for h in range(x.Hq)]
+    _compare(x, o, lse, rows=rows)
