@@ -40,7 +40,7 @@ def _parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--only", default="",
                    help="comma list of prefill,prefill_skip,decode,skip,smallseq,prefill_bwd,smallseq_bwd,"
-                        "decode_multi (profiling runs)")
+                        "decode_multi,prefill_paged (profiling runs)")
     p.add_argument("--calib-copy", action="store_true",
                    help="also run one plain 1 GiB device-to-device copy (scales HBM byte counters)")
     p.add_argument("--summarize-profiles", metavar="DIR", default="",
@@ -93,7 +93,7 @@ def main():
 
     only = (set(args.only.split(",")) if args.only
             else {"prefill", "prefill_skip", "decode", "skip", "smallseq", "prefill_bwd", "smallseq_bwd",
-                  "decode_multi"})
+                  "decode_multi", "prefill_paged"})
     dev = "cuda:0"
     torch.cuda.set_device(0)
     t_gen = time.time()
@@ -138,12 +138,19 @@ def main():
     if "decode_multi" in only:
         dm = W.paged_decode_multi(seed=1002 + args.seed, device=dev)
         work["decode_multi"] = dm
-        ws_m = torch.empty(attn.attn_decode_paged_multi_workspace_size(dm.q.shape[0], dm.Hq, dm.D, 32),
-                           dtype=torch.uint8, device=dev)
+        ws_m = torch.empty(attn.attn_decode_paged_multi_workspace_size(dm.q.shape[0], dm.max_q, dm.Hq, dm.Hkv, dm.D,
+                                                                       32), dtype=torch.uint8, device=dev)
         o_m = torch.empty_like(dm.q)
         nxt["decode_multi"] = lambda: attn.attn_decode_paged_multi(
             dm.q, dm.cu_q, dm.max_q, dm.k_cache, dm.v_cache, dm.block_table, dm.seq_lens, num_splits=32,
             workspace=ws_m, out=o_m)
+
+    if "prefill_paged" in only:
+        pp = W.paged_decode_multi(seed=1002 + args.seed, device=dev, qmin=256, qmax=256)
+        work["prefill_paged"] = pp
+        o_pp = torch.empty_like(pp.q)
+        nxt["prefill_paged"] = lambda: attn.attn_decode_paged_multi(
+            pp.q, pp.cu_q, pp.max_q, pp.k_cache, pp.v_cache, pp.block_table, pp.seq_lens, out=o_pp)
 
     calls = {}  # name -> zero-arg launcher
     if "prefill" in only:
@@ -355,6 +362,21 @@ def main():
         if "decode" in out:
             out["decode_multi"]["time_over_one_token_decode"] = t / out["decode"]["ms"]
 
+    if "prefill_paged" in only:
+        pp = work["prefill_paged"]
+        Lk = pp.lens.double()
+        Lq = pp.qlens.double()
+        # token i of a sequence sees L - Lq + i + 1 keys
+        pairs = float((Lq * (Lk - Lq) + Lq * (Lq + 1) / 2).sum())
+        flops = 4.0 * pp.D * pp.Hq * pairs
+        t = ms["prefill_paged"]
+        tf = flops / (t * 1e-3) / 1e12
+        out["prefill_paged"] = {"ms": t, "ms_min": ms_min["prefill_paged"], "flop": flops, "tflops": tf,
+                                "frac_peak": tf / PEAK_BF16_TFLOPS, "tokens": int(pp.q.shape[0]),
+                                "note": "the prefill kernel with page-gathered K/V; timed outside the step"}
+        if "prefill" in out:
+            out["prefill_paged"]["tflops_over_contiguous_prefill"] = tf / out["prefill"]["tflops"]
+
     # the dominant kernel: the largest share of the step
     dom = max(rooflines, key=lambda r: r["ms"]) if rooflines else None
     roofline = None
@@ -396,7 +418,9 @@ def main():
                    "timed_after_the_step": ["the prefill backward (dq, dk, dv) on the prefill shapes",
                                             "the small-seq backward from the stored weights on the small-seq shapes",
                                             "multi-token paged decode: the paged-decode cache with 1..4 new tokens "
-                                            "per sequence, 32 splits"],
+                                            "per sequence, 32 splits",
+                                            "chunked prefill over the paged-decode cache: 256 new tokens per "
+                                            "sequence"],
                    "seed": args.seed},
         "roofline": roofline,
         "cpu_baseline": cpu,

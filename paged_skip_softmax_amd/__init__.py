@@ -166,14 +166,16 @@ def attn_decode_paged(q, k_cache, v_cache, block_table, seq_lens, *, scale=None,
     return out, lse, smap
 
 
-def attn_decode_paged_multi_workspace_size(total_q: int, Hq: int, D: int, num_splits: int = 0) -> int:
-    """Workspace bytes of the multi-token decode's split-K partials."""
-    return int(_lib.load().attn_decode_paged_multi_workspace_size(total_q, Hq, D, num_splits))
+def attn_decode_paged_multi_workspace_size(total_q: int, max_seqlen_q: int, Hq: int, Hkv: int, D: int,
+                                           num_splits: int = 0) -> int:
+    """Workspace bytes of the multi-token decode (the split-K partials; 0 for long query chunks)."""
+    return int(_lib.load().attn_decode_paged_multi_workspace_size(total_q, max_seqlen_q, Hq, Hkv, D, num_splits))
 
 
 def attn_decode_paged_multi(q, cu_seqlens_q, max_seqlen_q, k_cache, v_cache, block_table, seq_lens, *, scale=None,
                             num_splits=0, workspace=None, out=None, return_lse=False):
-    """Multi-token paged decode (THD queries, bottom-right causal).  Returns (o, lse or None)."""
+    """Several new tokens per sequence over the paged cache (THD queries, bottom-right causal): split-K
+    decode for short query chunks, the paged prefill kernel for long ones.  Returns (o, lse or None)."""
     lib = _lib.load()
     dev = q.device
     _cuda_contig("q", q, torch.bfloat16)
@@ -191,7 +193,7 @@ def attn_decode_paged_multi(q, cu_seqlens_q, max_seqlen_q, k_cache, v_cache, blo
           "cu_seqlens_q [B + 1], block_table [B, max_pages], seq_lens [B]")
     if scale is None:
         scale = 1.0 / math.sqrt(D)
-    need = attn_decode_paged_multi_workspace_size(total_q, Hq, D, num_splits)
+    need = attn_decode_paged_multi_workspace_size(total_q, int(max_seqlen_q), Hq, Hkv, D, num_splits)
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()

@@ -220,10 +220,17 @@ attn_status_t attn_prefill_varlen_backward(attn_dtype_t dtype, const void *q, co
                       "prefill backward launch");
 }
 
-size_t attn_decode_paged_multi_workspace_size(int32_t total_q, int32_t Hq, int32_t D, int32_t num_splits)
+// Query rows per KV head up to which the multi-token call runs the split-K decode kernel (rows packed
+// into 16-column MFMA blocks, each block reading the cache once); beyond it, the paged prefill kernel.
+constexpr int kMultiSplitRows = 64;
+
+size_t attn_decode_paged_multi_workspace_size(int32_t total_q, int32_t max_seqlen_q, int32_t Hq, int32_t Hkv,
+                                              int32_t D, int32_t num_splits)
 {
-    if (total_q <= 0 || Hq <= 0 || D <= 0)
+    if (total_q <= 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv || D <= 0 || max_seqlen_q <= 0)
         return 0;
+    if ((int64_t)max_seqlen_q * (Hq / Hkv) > kMultiSplitRows)
+        return 0; // the paged prefill kernel needs no workspace
     const int S = num_splits == 0 ? kDefaultSplits : num_splits;
     return (size_t)total_q * Hq * S * (D + 1) * sizeof(float);
 }
@@ -251,20 +258,44 @@ attn_status_t attn_decode_paged_multi(const void *q, const int32_t *cu_seqlens_q
         return fail(ATTN_ERR_UNSUPPORTED, "attn_decode_paged_multi: D = %d (built for 128)", D);
     if (page_size != 16)
         return fail(ATTN_ERR_UNSUPPORTED, "attn_decode_paged_multi: page_size = %d (built for 16)", page_size);
-    if ((int64_t)max_seqlen_q * (Hq / Hkv) > 64)
-        return fail(ATTN_ERR_UNSUPPORTED, "attn_decode_paged_multi: max_seqlen_q * Hq / Hkv = %lld > 64 (a query "
-                                          "chunk this long belongs to a prefill kernel)",
-                    (long long)max_seqlen_q * (Hq / Hkv));
+    if ((int64_t)B * max_seqlen_q * Hq >= ((int64_t)1 << 31))
+        return fail(ATTN_ERR_UNSUPPORTED, "attn_decode_paged_multi: B * max_seqlen_q * Hq must stay below 2^31");
     if (B == 0 || total_q == 0)
         return ok();
     if (!q || !cu_seqlens_q || !k_cache || !v_cache || !block_table || !seq_lens || !o)
         return fail(ATTN_ERR_INVALID, "attn_decode_paged_multi: a required pointer is NULL");
+    const int G = Hq / Hkv;
+    if ((int64_t)max_seqlen_q * G > kMultiSplitRows) {
+        // long query chunks: the prefill kernel with K / V tiles gathered page by page
+        attn::PrefillArgs a{};
+        a.q = q;
+        a.k = k_cache;
+        a.v = v_cache;
+        a.cu_q = cu_seqlens_q;
+        a.cu_k = nullptr;
+        a.B = B;
+        a.max_q = max_seqlen_q;
+        a.max_k = max_pages_per_seq * page_size;
+        a.Hq = Hq;
+        a.Hkv = Hkv;
+        a.G = G;
+        a.causal = true;
+        a.scale_log2 = scale * 1.4426950408889634f;
+        a.log2_thr = -INFINITY;
+        a.o = o;
+        a.lse = lse;
+        a.skip_map = nullptr;
+        a.map_stride = 0;
+        a.bt = block_table;
+        a.seq_lens = seq_lens;
+        a.max_pages = max_pages_per_seq;
+        return hip_status(attn::launch_prefill_d128(a, static_cast<hipStream_t>(stream)), "paged prefill launch");
+    }
     const int S = num_splits == 0 ? kDefaultSplits : num_splits;
-    const size_t need = attn_decode_paged_multi_workspace_size(total_q, Hq, D, S);
+    const size_t need = attn_decode_paged_multi_workspace_size(total_q, max_seqlen_q, Hq, Hkv, D, S);
     if (!workspace || workspace_bytes < need)
         return fail(ATTN_ERR_WORKSPACE, "attn_decode_paged_multi: workspace %zu bytes, need %zu", workspace_bytes,
                     need);
-    const int G = Hq / Hkv;
     attn::MultiArgs a{};
     a.q = static_cast<const uint16_t *>(q);
     a.cu_q = cu_seqlens_q;

@@ -78,6 +78,10 @@ struct PrefillArgs {
     float *lse;
     uint8_t *skip_map;
     int map_stride;
+    // paged K / V (null bt: contiguous THD k, v with cu_k): k, v are [num_pages, Hkv, 16, D] caches,
+    // sequence b's key j in page bt[b * max_pages + j / 16], and it has seq_lens[b] keys
+    const int32_t *bt, *seq_lens;
+    int max_pages;
 };
 
 // Backward of the dense bf16 varlen prefill (D = 128).

@@ -69,21 +69,54 @@ template <int ST> __device__ __forceinline__ uint4 *vbuf()
     return ST == 0 ? v_st0 : v_st1;
 }
 
+// Issues the direct-to-LDS loads of K and V tiles.  Contiguous K / V: one buffer resource over the
+// sequence's rows of the KV head, tile t at a scalar offset.  Paged K / V: wave w loads the 16 keys of
+// page 4 t + w of the sequence (one 4 KB slab of the cache) through a resource over that slab alone,
+// cut at the sequence's last key; the page number comes from the block table.
+template <bool PAGED>
 struct Loader {
     i32x4 krs, vrs;
     uint32_t voff[kLoadsPerWave]; // this lane's byte offsets for its 4-row blocks
     uint32_t tile_bytes;          // global bytes between consecutive 64-key tiles
     uint32_t m0k[kStages], m0v[kStages]; // LDS byte address of this wave's first 4-row block per stage
+    // paged only
+    const int32_t *btr;           // the sequence's block-table row
+    const uint16_t *kc, *vc;      // the caches
+    size_t head_off, page_elems;  // elements to the KV head's slab in a page; elements per page
+    int Lk, w;                    // keys of the sequence; the (wave-uniform) wave index
+    uint32_t zero;                // 0 in a scalar register (the buffer loads' scalar offset)
 
-    __device__ __forceinline__ void issue(const i32x4 &rs, uint32_t m0, int t) const
+    // the wave's page of tile t (0 when the page lies past the sequence)
+    __device__ __forceinline__ int page_of(int t) const { return 64 * t + 16 * w < Lk ? btr[4 * t + w] : 0; }
+    __device__ __forceinline__ i32x4 page_rsrc(const uint16_t *cache, int t, int page) const
     {
-        const uint32_t soff = (uint32_t)t * tile_bytes;
+        const int nkeys = max(0, min(16, Lk - 64 * t - 16 * w));
+        const i32x4 r =
+            make_rsrc(nkeys > 0 ? cache + (size_t)page * page_elems + head_off : cache, (uint32_t)nkeys * 256);
+        // wave-uniform by construction; said explicitly so the words stay in scalar registers
+        return i32x4{__builtin_amdgcn_readfirstlane(r[0]), __builtin_amdgcn_readfirstlane(r[1]),
+                     __builtin_amdgcn_readfirstlane(r[2]), r[3]};
+    }
+    __device__ __forceinline__ void issue(const i32x4 &rs, uint32_t m0, uint32_t soff) const
+    {
 #pragma unroll
         for (int p = 0; p < kLoadsPerWave; ++p)
             dma16(m0 + p * 1024, voff[p], rs, soff);
     }
-    template <int ST> __device__ __forceinline__ void issue_k(int t) const { issue(krs, m0k[ST], t); }
-    template <int ST> __device__ __forceinline__ void issue_v(int t) const { issue(vrs, m0v[ST], t); }
+    template <int ST> __device__ __forceinline__ void issue_k(int t, int page) const
+    {
+        if (PAGED)
+            issue(page_rsrc(kc, t, page), m0k[ST], zero);
+        else
+            issue(krs, m0k[ST], (uint32_t)t * tile_bytes);
+    }
+    template <int ST> __device__ __forceinline__ void issue_v(int t, int page) const
+    {
+        if (PAGED)
+            issue(page_rsrc(vc, t, page), m0v[ST], zero);
+        else
+            issue(vrs, m0v[ST], (uint32_t)t * tile_bytes);
+    }
 };
 
 struct Wave {
@@ -192,16 +225,24 @@ __device__ __forceinline__ bool needs_mask(int t, const IterCtx &c)
 //   (c) mask tile t+1 where it crosses the diagonal or the sequence end;
 //   (d) P.V of tile t, with the row max of tile t+1 placed between its MFMAs.
 // On the last tile, (b)-(d) compute scores from a stale K stage that are never used.
-template <int ST, bool SKIP>
-__device__ __forceinline__ void iteration(int t, const IterCtx &c, const Loader &ld, Wave &wv, f32x16 sc[2],
+template <int ST, bool SKIP, bool PAGED>
+__device__ __forceinline__ void iteration(int t, const IterCtx &c, const Loader<PAGED> &ld, Wave &wv, f32x16 sc[2],
                                           float &tm, bool &raise, SkipState &ss)
 {
+    // paged: the block-table reads go out before the wait, so the barrier covers their latency
+    int page_k = 0, page_v = 0;
+    if (PAGED) {
+        if (t + 2 < c.niter)
+            page_k = ld.page_of(t + 2);
+        if (t + 1 < c.niter)
+            page_v = ld.page_of(t + 1);
+    }
     wait_vmcnt<0>();
     barrier();
     if (t + 2 < c.niter)
-        ld.issue_k<ST>(t + 2);
+        ld.template issue_k<ST>(t + 2, page_k);
     if (t + 1 < c.niter)
-        ld.issue_v<(ST + 1) % kStages>(t + 1);
+        ld.template issue_v<(ST + 1) % kStages>(t + 1, page_v);
     constexpr int P = ST;
 
     // (a)
@@ -298,7 +339,7 @@ __device__ __forceinline__ void iteration(int t, const IterCtx &c, const Loader 
     sc[1] = nx[1];
 }
 
-template <bool SKIP>
+template <bool SKIP, bool PAGED>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void prefill_d128_kernel(PrefillArgs a, int NH, int RB, int nqt, int nunits)
 {
@@ -314,7 +355,8 @@ void prefill_d128_kernel(PrefillArgs a, int NH, int RB, int nqt, int nunits)
     const int g = gh / hchunks, hc = gh % hchunks;
     const int rows_wg = 32 * RB;
     const int q0 = a.cu_q[b], Lq = a.cu_q[b + 1] - q0;
-    const int k0 = a.cu_k[b], Lk = a.cu_k[b + 1] - k0;
+    const int k0 = PAGED ? 0 : a.cu_k[b];
+    const int Lk = PAGED ? a.seq_lens[b] : a.cu_k[b + 1] - k0;
     const int m0 = qt * rows_wg;
     if (m0 >= Lq)
         return;
@@ -341,17 +383,29 @@ void prefill_d128_kernel(PrefillArgs a, int NH, int RB, int nqt, int nunits)
     }
 
     // loads: wave w fills 4-row blocks rb0 .. rb0+3 of each tile; lane -> row 4 rb + lane/16, slot lane%16
-    Loader ld;
+    Loader<PAGED> ld;
     {
         const uint16_t *kg = static_cast<const uint16_t *>(a.k);
         const uint16_t *vg = static_cast<const uint16_t *>(a.v);
-        const size_t head0 = ((size_t)k0 * a.Hkv + (size_t)g) * D;
-        const uint32_t row_bytes = (uint32_t)a.Hkv * D * 2;
-        const uint32_t seq_bytes = Lk > 0 ? ((uint32_t)(Lk - 1) * a.Hkv + 1) * D * 2 : 0;
-        ld.krs = make_rsrc(kg + head0, seq_bytes);
-        ld.vrs = make_rsrc(vg + head0, seq_bytes);
+        // contiguous: rows of the KV head Hkv * D apart; paged: the 16 rows of a page slab are adjacent
+        const uint32_t row_bytes = PAGED ? D * 2 : (uint32_t)a.Hkv * D * 2;
+        if (!PAGED) {
+            const size_t head0 = ((size_t)k0 * a.Hkv + (size_t)g) * D;
+            const uint32_t seq_bytes = Lk > 0 ? ((uint32_t)(Lk - 1) * a.Hkv + 1) * D * 2 : 0;
+            ld.krs = make_rsrc(kg + head0, seq_bytes);
+            ld.vrs = make_rsrc(vg + head0, seq_bytes);
+            ld.tile_bytes = kBN * row_bytes;
+        } else {
+            ld.btr = a.bt + (size_t)b * a.max_pages;
+            ld.kc = kg;
+            ld.vc = vg;
+            ld.head_off = (size_t)g * 16 * D;
+            ld.page_elems = (size_t)a.Hkv * 16 * D;
+            ld.Lk = Lk;
+            ld.w = __builtin_amdgcn_readfirstlane(w);
+            asm volatile("s_mov_b32 %0, 0" : "=s"(ld.zero));
+        }
         const int rb0 = kLoadsPerWave * w;
-        ld.tile_bytes = kBN * row_bytes;
         const uint32_t wave_off = __builtin_amdgcn_readfirstlane(rb0 * 1024);
         ld.m0k[0] = lds_addr(k_st0) + wave_off;
         ld.m0k[1] = lds_addr(k_st1) + wave_off;
@@ -361,7 +415,8 @@ void prefill_d128_kernel(PrefillArgs a, int NH, int RB, int nqt, int nunits)
         for (int p = 0; p < kLoadsPerWave; ++p) {
             const int row = 4 * (rb0 + p) + (lane >> 4);
             const int chunk = (lane & 15) ^ swz(row & 15);
-            ld.voff[p] = (uint32_t)row * row_bytes + 16 * chunk;
+            // paged: the row within the wave's page (the tile row's swizzle is the same: 16 | 16 w)
+            ld.voff[p] = (uint32_t)(PAGED ? row - 16 * w : row) * row_bytes + 16 * chunk;
         }
     }
 
@@ -424,10 +479,11 @@ void prefill_d128_kernel(PrefillArgs a, int NH, int RB, int nqt, int nunits)
         // prologue: K(0), V(0), K(1) in flight; wait for K(0), then the masked scores of tile 0 and
         // their row max
         constexpr int L = kLoadsPerWave;
-        ld.issue_k<0>(0);
-        ld.issue_v<0>(0);
+        const int pg0 = PAGED ? ld.page_of(0) : 0;
+        ld.template issue_k<0>(0, pg0);
+        ld.template issue_v<0>(0, pg0);
         if (niter > 1) {
-            ld.issue_k<1>(1);
+            ld.template issue_k<1>(1, PAGED ? ld.page_of(1) : 0);
             wait_vmcnt<2 * L>();
         } else {
             wait_vmcnt<L>();
@@ -445,9 +501,9 @@ void prefill_d128_kernel(PrefillArgs a, int NH, int RB, int nqt, int nunits)
         tile_stats<SKIP>(t0, t1, 0, c, wv, ss, tm, raise);
     }
     for (int t = 0; t < niter; t += kStages) {
-        iteration<0, SKIP>(t, c, ld, wv, sc, tm, raise, ss);
+        iteration<0, SKIP, PAGED>(t, c, ld, wv, sc, tm, raise, ss);
         if (t + 1 < niter)
-            iteration<1, SKIP>(t + 1, c, ld, wv, sc, tm, raise, ss);
+            iteration<1, SKIP, PAGED>(t + 1, c, ld, wv, sc, tm, raise, ss);
     }
 
     wv.l += __shfl_xor(wv.l, 32);
@@ -489,12 +545,17 @@ hipError_t launch_prefill_d128(const PrefillArgs &a, hipStream_t stream)
     if (blocks > 0x7fffffff)
         return hipErrorInvalidValue;
     const bool skip = a.log2_thr != kNegInf || a.skip_map != nullptr;
-    if (skip)
-        hipLaunchKernelGGL(prefill_d128_kernel<true>, dim3((unsigned)blocks), dim3(kThreads), 0, stream, a, NH, RB,
-                           nqt, (int)units);
-    else
-        hipLaunchKernelGGL(prefill_d128_kernel<false>, dim3((unsigned)blocks), dim3(kThreads), 0, stream, a, NH, RB,
-                           nqt, (int)units);
+    const dim3 grid((unsigned)blocks), block(kThreads);
+    if (a.bt) {
+        if (skip)
+            hipLaunchKernelGGL((prefill_d128_kernel<true, true>), grid, block, 0, stream, a, NH, RB, nqt, (int)units);
+        else
+            hipLaunchKernelGGL((prefill_d128_kernel<false, true>), grid, block, 0, stream, a, NH, RB, nqt, (int)units);
+    } else if (skip) {
+        hipLaunchKernelGGL((prefill_d128_kernel<true, false>), grid, block, 0, stream, a, NH, RB, nqt, (int)units);
+    } else {
+        hipLaunchKernelGGL((prefill_d128_kernel<false, false>), grid, block, 0, stream, a, NH, RB, nqt, (int)units);
+    }
     return hipGetLastError();
 }
 

@@ -170,15 +170,16 @@ def test_decode_multi_validation(lib):
         return lib.attn_decode_paged_multi(a["q"], a["cq"], a["tq"], a["mq"], a["kc"], a["vc"], a["bt"], a["sl"],
                                            a["B"], a["Hq"], a["Hkv"], a["D"], a["page"], a["pages"], a["maxp"],
                                            a["scale"], a["splits"], a["ws"], a["wsb"], a["o"], a["lse"], a["stream"])
-    assert lib.attn_decode_paged_multi_workspace_size(10, 32, 128, 0) == 10 * 32 * 32 * 129 * 4
-    assert lib.attn_decode_paged_multi_workspace_size(10, 32, 128, 7) == 10 * 32 * 7 * 129 * 4
+    assert lib.attn_decode_paged_multi_workspace_size(10, 4, 32, 8, 128, 0) == 10 * 32 * 32 * 129 * 4
+    assert lib.attn_decode_paged_multi_workspace_size(10, 4, 32, 8, 128, 7) == 10 * 32 * 7 * 129 * 4
+    assert lib.attn_decode_paged_multi_workspace_size(10, 17, 32, 8, 128, 0) == 0  # the paged prefill path
     assert call(B=-1) == INVALID
     assert call(Hkv=5) == INVALID
     assert call(splits=65) == INVALID
     assert call(scale=math.inf) == INVALID
     assert call(D=64) == UNSUPPORTED
     assert call(page=32) == UNSUPPORTED
-    assert call(mq=17) == UNSUPPORTED   # 17 tokens x 4 heads > 64 rows
+    assert call(mq=1 << 20, B=1 << 10) == UNSUPPORTED
     assert call(cq=None) == INVALID
     assert call(wsb=100) == WORKSPACE
     assert call(B=0) == _lib.ATTN_OK

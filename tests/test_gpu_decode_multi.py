@@ -85,3 +85,52 @@ def test_decode_multi_full_size_sampled():
     bs = sorted({int(np.argmax(L)), int(np.argmin(L))} | set(range(0, x.B, 7)))
     rows = [(t, h) for b in bs for t in range(cu[b], cu[b + 1]) for h in range(x.Hq)]
     _compare(x, o, lse, rows=rows)
+
+
+# ------------------------------------------------------------------ long query chunks: the paged prefill kernel
+
+@pytest.mark.parametrize("Hq,Hkv,qmin,qmax", [(8, 2, 20, 200), (8, 8, 65, 130), (32, 8, 17, 70)])
+def test_paged_prefill_chunks(Hq, Hkv, qmin, qmax):
+    # Lq * G > 64 rows per KV head: the prefill kernel with page-gathered K / V tiles (ragged chunks and
+    # contexts, every tile-edge case: partial pages, partial 64-key tiles, the causal diagonal)
+    x = W.paged_decode_multi(seed=65, device=DEV, B=7, Hq=Hq, Hkv=Hkv, lmin=70, lmax=1500, pool=800, qmin=qmin,
+                             qmax=qmax)
+    assert x.max_q * (Hq // Hkv) > 64
+    o, lse = attn.attn_decode_paged_multi(x.q, x.cu_q, x.max_q, x.k_cache, x.v_cache, x.block_table, x.seq_lens,
+                                          return_lse=True)
+    torch.cuda.synchronize()
+    _compare(x, o, lse)
+
+
+def test_paged_prefill_whole_sequences_and_tokens_without_keys():
+    # Lq = L (the whole sequence is new), Lq > L (leading tokens without a key), and an empty cache
+    x = W.paged_decode_multi(seed=66, device=DEV, B=4, Hq=8, Hkv=2, lengths=[100, 33, 0, 64], pool=64, qmin=1,
+                             qmax=1)
+    lq = torch.tensor([100, 50, 20, 64])
+    cu = torch.cat([torch.zeros(1, dtype=torch.int64), lq.cumsum(0)])
+    g = torch.Generator(device=DEV).manual_seed(67)
+    x.q = torch.randn(int(cu[-1]), x.Hq, x.D, generator=g, device=DEV).bfloat16()
+    x.cu_q = cu.to(torch.int32).to(DEV)
+    o, lse = attn.attn_decode_paged_multi(x.q, x.cu_q, 100, x.k_cache, x.v_cache, x.block_table, x.seq_lens,
+                                          return_lse=True)
+    torch.cuda.synchronize()
+    _compare(x, o, lse)
+
+
+def test_paged_prefill_full_size_sampled():
+    # the full paged-decode cache with 256-token chunks (a chunked prefill over contexts of 1k-32k keys);
+    # the first, last and a sample of tokens of several sequences, all heads
+    x = W.paged_decode_multi(seed=1002, device=DEV, qmin=256, qmax=256)
+    o, lse = attn.attn_decode_paged_multi(x.q, x.cu_q, x.max_q, x.k_cache, x.v_cache, x.block_table, x.seq_lens,
+                                          return_lse=True)
+    torch.cuda.synchronize()
+    L = x.lens.numpy()
+    cu = x.cu_q.cpu().tolist()
+    rng = np.random.default_rng(68)
+    bs = sorted({int(np.argmax(L)), int(np.argmin(L))} | set(range(0, x.B, 16)))
+    rows = []
+    for b in bs:
+        n = cu[b + 1] - cu[b]
+        toks = {0, 1, 63, 64, n - 1} | set(rng.choice(n, size=6, replace=False).tolist())
+        rows += [(cu[b] + t, h) for t in sorted(toks) for h in range(x.Hq)]
+    _compare(x, o, lse, rows=rows)
