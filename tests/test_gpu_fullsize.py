@@ -175,3 +175,54 @@ def test_empty_batch_is_a_no_op():
                                        torch.empty((0, 4, 128), dtype=torch.bfloat16, device=DEV), z32, 16)
     torch.cuda.synchronize()
     assert o.shape == (0, 4, 128) and w.shape == (0, 4, 1, 16)
+
+
+def test_prefill_one_long_sequence_sampled():
+    # one causal sequence of 131,072 tokens (Hq 8, Hkv 1): 2,048 key tiles per row at the end, 4,096
+    # query tiles, K/V row offsets near the top of the supported range; sampled rows, all heads
+    L = 131072
+    x = W.varlen_prefill(seed=1011, device=DEV, lengths=[L], Hq=8, Hkv=1)
+    o, lse, _ = attn.attn_prefill_varlen(x.q, x.k, x.v, x.cu_q, x.cu_k, x.max_q, x.max_k, causal=True,
+                                         return_lse=True)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(13)
+    toks = sorted({0, 1, 31, 32, 63, 64, 4095, 4096, L // 2, L - 65, L - 64, L - 2, L - 1}
+                  | set(rng.choice(L, size=24, replace=False).tolist()))
+    rows = [(t, h) for t in toks for h in range(x.Hq)]
+    od, ld, _ = oracle.prefill(x.q.cpu(), x.k.cpu(), x.v.cpu(), x.cu_q.cpu(), x.cu_k.cpu(), x.Hq, x.Hkv, x.scale,
+                               True, rows=rows)
+    r = np.array(rows)
+    assert np.max(np.abs(_np(o)[r[:, 0], r[:, 1]] - od)) <= BF16_TOL
+    assert np.max(np.abs(_np(lse)[r[:, 0], r[:, 1]] - ld)) <= LSE_TOL
+
+
+def test_prefill_many_short_sequences():
+    # 4,096 sequences of 1..16 tokens: every query tile is partial, most workgroups see one key tile;
+    # every row against the oracle
+    g = torch.Generator().manual_seed(14)
+    lens = torch.randint(1, 17, (4096,), generator=g).tolist()
+    x = W.varlen_prefill(seed=1012, device=DEV, lengths=lens, Hq=32, Hkv=8)
+    o, lse, _ = attn.attn_prefill_varlen(x.q, x.k, x.v, x.cu_q, x.cu_k, x.max_q, x.max_k, causal=True,
+                                         return_lse=True)
+    torch.cuda.synchronize()
+    od, ld, _ = oracle.prefill(x.q.cpu(), x.k.cpu(), x.v.cpu(), x.cu_q.cpu(), x.cu_k.cpu(), x.Hq, x.Hkv, x.scale,
+                               True)
+    assert np.max(np.abs(_np(o) - od)) <= BF16_TOL
+    assert np.max(np.abs(_np(lse) - ld)) <= LSE_TOL
+
+
+@pytest.mark.parametrize("splits", [64, 1])
+def test_decode_one_long_context(splits):
+    # one sequence of 262,144 cached tokens (16,384 pages): 2,048 128-key tiles over 64 splits, or the
+    # sequential schedule's 8,192 32-key tiles; every head against the oracle
+    L = 262144
+    x = W.paged_decode(seed=1013, device=DEV, B=1, lengths=[L], lmax=L, pool=L // 16 + 8)
+    ws = torch.empty(attn.attn_decode_paged_workspace_size(x.B, x.Hq, x.D, splits), dtype=torch.uint8, device=DEV)
+    o, lse, _ = attn.attn_decode_paged(x.q, x.k_cache, x.v_cache, x.block_table, x.seq_lens, num_splits=splits,
+                                       workspace=ws, return_lse=True)
+    torch.cuda.synchronize()
+    od, ld, _ = oracle.decode(x.q.cpu(), x.k_cache.cpu(), x.v_cache.cpu(), x.block_table.cpu(), x.seq_lens.cpu(),
+                              x.scale)
+    assert np.isfinite(_np(o)).all()
+    assert np.max(np.abs(_np(o) - od)) <= BF16_TOL
+    assert np.max(np.abs(_np(lse) - ld)) <= LSE_TOL
