@@ -315,23 +315,48 @@ __device__ __forceinline__ void iteration(int t, const IterCtx &c, const Loader<
             const uint2 hi = lds_read_tr(vk + wv.va[1][step & 3]);
             return make_uint4(lo.x, lo.y, hi.x, hi.y);
         };
-        uint4 v0 = vop(0), v1 = vop(1);
+        if (!SKIP) {
+            uint4 v0 = vop(0), v1 = vop(1);
 #pragma unroll
-        for (int step = 0; step < 16; ++step) {
-            const uint4 v2 = step + 2 < 16 ? vop(step + 2) : v0;
-            const int kk = step >> 3, u = (step >> 2) & 1;
-            const bf16x8 pop = __builtin_bit_cast(bf16x8, make_uint4(pk[kk][4 * u], pk[kk][4 * u + 1],
-                                                                      pk[kk][4 * u + 2], pk[kk][4 * u + 3]));
-            wv.acc[step & 3] = mfma32(as_bf16x8(v0), pop, wv.acc[step & 3]);
-            if (step < 15) {
-                t0 = fmaxf(t0, nx[0][step + 1]);
-                t1 = fmaxf(t1, nx[1][step + 1]);
-                anchor(t0);
-                anchor(t1);
+            for (int step = 0; step < 16; ++step) {
+                const uint4 v2 = step + 2 < 16 ? vop(step + 2) : v0;
+                const int kk = step >> 3, u = (step >> 2) & 1;
+                const bf16x8 pop = __builtin_bit_cast(bf16x8, make_uint4(pk[kk][4 * u], pk[kk][4 * u + 1],
+                                                                          pk[kk][4 * u + 2], pk[kk][4 * u + 3]));
+                wv.acc[step & 3] = mfma32(as_bf16x8(v0), pop, wv.acc[step & 3]);
+                if (step < 15) {
+                    t0 = fmaxf(t0, nx[0][step + 1]);
+                    t1 = fmaxf(t1, nx[1][step + 1]);
+                    anchor(t0);
+                    anchor(t1);
+                }
+                sched_fence();
+                v0 = v1;
+                v1 = v2;
             }
-            sched_fence();
-            v0 = v1;
-            v1 = v2;
+        } else {
+            // the row maxima of tile t+1 first; then a tile that no row of the wave keeps (both 32-key
+            // halves skipped or unseen by every row: P = 0 throughout) leaves its P.V out by one uniform
+            // branch
+#pragma unroll
+            for (int i = 1; i < 16; ++i) {
+                t0 = fmaxf(t0, nx[0][i]);
+                t1 = fmaxf(t1, nx[1][i]);
+            }
+            if (__any(ss.keep[0] || ss.keep[1])) {
+                uint4 v0 = vop(0), v1 = vop(1);
+#pragma unroll
+                for (int step = 0; step < 16; ++step) {
+                    const uint4 v2 = step + 2 < 16 ? vop(step + 2) : v0;
+                    const int kk = step >> 3, u = (step >> 2) & 1;
+                    const bf16x8 pop = __builtin_bit_cast(
+                        bf16x8, make_uint4(pk[kk][4 * u], pk[kk][4 * u + 1], pk[kk][4 * u + 2], pk[kk][4 * u + 3]));
+                    wv.acc[step & 3] = mfma32(as_bf16x8(v0), pop, wv.acc[step & 3]);
+                    sched_fence();
+                    v0 = v1;
+                    v1 = v2;
+                }
+            }
         }
     }
     tile_stats<SKIP>(t0, t1, t + 1, c, wv, ss, tm, raise);
