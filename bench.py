@@ -41,12 +41,25 @@ def _parse():
     p.add_argument("--only", default="",
                    help="comma list of prefill,prefill_skip,decode,skip,smallseq,prefill_bwd,smallseq_bwd,"
                         "decode_multi,prefill_paged (profiling runs)")
+    p.add_argument("--launch-log", metavar="PATH", default="",
+                   help="write the bench's calls, in launch order, to PATH (JSON; profiling runs)")
     p.add_argument("--calib-copy", action="store_true",
                    help="also run one plain 1 GiB device-to-device copy (scales HBM byte counters)")
     p.add_argument("--summarize-profiles", metavar="DIR", default="",
                    help="no GPU work: turn the rocprofv3 csv output under DIR/prof_trace, DIR/prof_fetch and "
                         "DIR/prof_write into the summaries under profiles/")
     return p.parse_args()
+
+
+# Every library call the bench makes, in launch order (its name is the call's role in the profiles).
+LAUNCH_LOG = []
+
+
+def _logged(name, fn):
+    def call():
+        LAUNCH_LOG.append(name)
+        return fn()
+    return call
 
 
 def _traffic_from_profiles(kernel: str):
@@ -102,6 +115,7 @@ def main():
         work["prefill"] = W.varlen_prefill(seed=1001 + args.seed, device=dev)
     if "prefill_skip" in only:
         work["prefill_skip"] = W.varlen_prefill_hot(seed=1001 + args.seed, device=dev)
+        work["prefill_sink"] = W.varlen_prefill_sink(seed=1001 + args.seed, device=dev)
     if "decode" in only:
         work["decode"] = W.paged_decode(seed=1002 + args.seed, device=dev)
     if "skip" in only:
@@ -117,6 +131,7 @@ def main():
         xb = work.get("prefill") or W.varlen_prefill(seed=1001 + args.seed, device=dev)
         work["prefill_bwd"] = xb
         do_b = W.grad_output(xb, seed=1005 + args.seed, device=dev)
+        LAUNCH_LOG.append("setup_prefill_fwd")
         o_b, lse_b, _ = attn.attn_prefill_varlen(xb.q, xb.k, xb.v, xb.cu_q, xb.cu_k, xb.max_q, xb.max_k, causal=True,
                                                  return_lse=True)
         ws_b = torch.empty(attn.attn_prefill_varlen_backward_workspace_size(xb.B, xb.max_q, xb.Hq),
@@ -130,6 +145,7 @@ def main():
         cb = work.get("smallseq") or W.smallseq_cross(seed=1004 + args.seed, device=dev)
         work["smallseq_bwd"] = cb
         do_s = W.grad_output(cb, seed=1006 + args.seed, device=dev)
+        LAUNCH_LOG.append("setup_smallseq_fwd")
         _, w_s, _ = attn.attn_smallseq_cross(cb.q, cb.k, cb.v, cb.cu_kv, cb.max_s)
         gs = (torch.empty_like(cb.q), torch.empty_like(cb.k), torch.empty_like(cb.v))
         nxt["smallseq_bwd"] = lambda: attn.attn_smallseq_cross_backward(
@@ -164,6 +180,11 @@ def main():
         for thr in (0.0, 0.01, 0.1):
             calls[f"prefill_skip_{thr}"] = (lambda thr=thr: attn.attn_prefill_varlen(
                 xh.q, xh.k, xh.v, xh.cu_q, xh.cu_k, xh.max_q, xh.max_k, causal=True, skip_threshold=thr, out=o_ph))
+        # the coherent-sink input: timed after the step, for the speedup-vs-skipped-fraction curve
+        xs = work["prefill_sink"]
+        for thr in (0.0, 0.01, 0.1):
+            nxt[f"prefill_sink_{thr}"] = (lambda thr=thr: attn.attn_prefill_varlen(
+                xs.q, xs.k, xs.v, xs.cu_q, xs.cu_k, xs.max_q, xs.max_k, causal=True, skip_threshold=thr, out=o_ph))
     if "decode" in only:
         d = work["decode"]
         ws = torch.empty(attn.attn_decode_paged_workspace_size(d.B, d.Hq, d.D, 32), dtype=torch.uint8, device=dev)
@@ -182,6 +203,8 @@ def main():
         w_ss = torch.empty((c.B, c.H, 1, c.max_s), dtype=torch.bfloat16, device=dev)
         calls["smallseq"] = lambda: attn.attn_smallseq_cross(c.q, c.k, c.v, c.cu_kv, c.max_s, out=o_ss)
 
+    calls = {k: _logged(k, f) for k, f in calls.items()}
+    nxt = {k: _logged(k, f) for k, f in nxt.items()}
     names = list(calls)
     stream = torch.cuda.current_stream()
 
@@ -247,29 +270,38 @@ def main():
         tflops = flops / (ms["prefill"] * 1e-3) / 1e12
         out["prefill"] = {"ms": ms["prefill"], "ms_min": ms_min["prefill"], "flop": flops, "tflops": tflops,
                           "frac_peak": tflops / PEAK_BF16_TFLOPS}
-        rooflines.append({"kernel": "prefill_d128_kernel<false>", "bound": "mfma", "achieved": tflops,
+        rooflines.append({"kernel": PF, "bound": "mfma", "achieved": tflops,
                           "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": tflops / PEAK_BF16_TFLOPS,
-                          "traffic": _traffic_from_profiles("prefill_d128_kernel<false>"), "ms": ms["prefill"]})
+                          "traffic": _traffic_from_profiles(PF), "ms": ms["prefill"]})
     if "prefill_skip" in only:
-        xh = work["prefill_skip"]
-        L = xh.lens.double()
-        flops = 4.0 * 128 * 32 * float((L * (L + 1) / 2).sum())
         res = {}
-        for thr in (0.0, 0.01, 0.1):
-            t = ms[f"prefill_skip_{thr}"]
-            ent = {"ms": t, "ms_min": ms_min[f"prefill_skip_{thr}"], "dense_equiv_tflops": flops / (t * 1e-3) / 1e12}
-            if thr > 0:
-                _, _, smap = attn.attn_prefill_varlen(xh.q, xh.k, xh.v, xh.cu_q, xh.cu_k, xh.max_q, xh.max_k,
-                                                      causal=True, skip_threshold=thr, return_skip_map=True)
-                torch.cuda.synchronize()
-                vis = smap != 2
-                frac = float((smap == 1).sum()) / float(vis.sum())
-                del smap
-                ent["row_subtile_skip_frac"] = frac
-                # P.V is half of the MFMA work; the exponentials of skipped tiles are still computed
-                ent["ideal_speedup_pv_only"] = 1.0 / (1.0 - 0.5 * frac)
-                ent["speedup_vs_dense"] = ms["prefill_skip_0.0"] / t
-            res[str(thr)] = ent
+        curve = []
+        for inp, key in (("hot", "prefill_skip"), ("sink", "prefill_sink")):
+            xh = work[key]
+            L = xh.lens.double()
+            flops = 4.0 * 128 * 32 * float((L * (L + 1) / 2).sum())
+            sub = {}
+            for thr in (0.0, 0.01, 0.1):
+                t = ms[f"{key}_{thr}"]
+                ent = {"ms": t, "ms_min": ms_min[f"{key}_{thr}"], "dense_equiv_tflops": flops / (t * 1e-3) / 1e12}
+                if thr > 0:
+                    LAUNCH_LOG.append(f"map_{key}_{thr}")
+                    _, _, smap = attn.attn_prefill_varlen(xh.q, xh.k, xh.v, xh.cu_q, xh.cu_k, xh.max_q, xh.max_k,
+                                                          causal=True, skip_threshold=thr, return_skip_map=True)
+                    torch.cuda.synchronize()
+                    row_frac, wave_frac = _skip_fractions(torch, xh, smap)
+                    del smap
+                    ent["row_subtile_skip_frac"] = row_frac
+                    # the kernel leaves out a 64-key tile's P.V (half the MFMA work) when no row of the
+                    # wave's 32 rows keeps it
+                    ent["wave_tile_skip_frac"] = wave_frac
+                    ent["ideal_speedup_pv_only"] = 1.0 / (1.0 - 0.5 * wave_frac)
+                    ent["speedup_vs_dense"] = ms[f"{key}_0.0"] / t
+                    curve.append({"input": inp, "thr": thr, "row_skip": row_frac, "wave_tile_skip": wave_frac,
+                                  "speedup": ent["speedup_vs_dense"]})
+                sub[str(thr)] = ent
+            res[inp] = sub
+        res["curve"] = curve
         out["prefill_skip"] = res
     if "decode" in only:
         d = work["decode"]
@@ -288,6 +320,7 @@ def main():
         res = {}
         kbytes = 2.0 * s.Hkv * s.D * float(s.lens.sum())
         for thr in (0.0, 0.01, 0.1):
+            LAUNCH_LOG.append(f"map_skip_{thr}")
             _, _, smap = attn.attn_decode_paged(s.q, s.k_cache, s.v_cache, s.block_table, s.seq_lens, num_splits=1,
                                                 skip_threshold=thr, return_skip_map=True)
             torch.cuda.synchronize()
@@ -415,7 +448,8 @@ def main():
                                       "paged decode split-K B=64 L~U[1024,32768] page 16, 32x128-key splits",
                                       "sequential skip decode thr {0,0.01,0.1} on hot keys",
                                       "small-seq cross B=30720 s_kv in {2..16} H=16 D=128"],
-                   "timed_after_the_step": ["the prefill backward (dq, dk, dv) on the prefill shapes",
+                   "timed_after_the_step": ["skip-softmax prefill thr {0,0.01,0.1} on the coherent-sink input",
+                                            "the prefill backward (dq, dk, dv) on the prefill shapes",
                                             "the small-seq backward from the stored weights on the small-seq shapes",
                                             "multi-token paged decode: the paged-decode cache with 1..4 new tokens "
                                             "per sequence, 32 splits",
@@ -429,6 +463,33 @@ def main():
         "achievable_context": achievable,
     }
     print(json.dumps(line), flush=True)
+    if args.launch_log:
+        os.makedirs(os.path.dirname(os.path.abspath(args.launch_log)), exist_ok=True)
+        with open(args.launch_log, "w") as f:
+            json.dump(LAUNCH_LOG, f)
+
+
+def _skip_fractions(torch, x, smap):
+    """Fractions of visited (row, 32-key half) pairs skipped, and of (32-row wave block, 64-key tile)
+    pairs in which no row keeps either half (the unit whose P.V the kernel leaves out)."""
+    vis = smap != 2
+    row = float((smap == 1).sum()) / float(vis.sum())
+    cu = x.cu_q.cpu().tolist()
+    ws = wv = 0
+    for b in range(x.B):
+        n = cu[b + 1] - cu[b]
+        m = smap[cu[b]:cu[b + 1]]                                  # [n, H, S]
+        nb, S = (n + 31) // 32, m.shape[-1]
+        pad_r = torch.full((nb * 32 - n, m.shape[1], S), 2, dtype=m.dtype, device=m.device)
+        m = torch.cat([m, pad_r])
+        if S % 2:
+            m = torch.cat([m, torch.full((m.shape[0], m.shape[1], 1), 2, dtype=m.dtype, device=m.device)], -1)
+        m = m.view(nb, 32, m.shape[1], -1, 2)                      # [blocks, 32 rows, H, tiles, halves]
+        kept = (m == 0).any(-1).any(1)                             # some row keeps some half
+        seen = (m != 2).any(-1).any(1)
+        ws += int((seen & ~kept).sum())
+        wv += int(seen.sum())
+    return row, ws / max(1, wv)
 
 
 def _achievable(torch, dev):
@@ -540,55 +601,84 @@ _KSRC = ["paged_skip_softmax_amd/csrc/kcommon.h", "paged_skip_softmax_amd/csrc/l
 _LDS = "paged_skip_softmax_amd/csrc/lds_dma.h"
 _BWD = ["paged_skip_softmax_amd/csrc/prefill_bwd.hip", _LDS] + _KSRC
 _BWD_W = "prefill backward on the prefill shapes (16 seqs L~U[256,4096], Hq=32, Hkv=8, D=128, causal)"
+PF = "prefill_d128_kernel<false, false>"   # dense prefill, contiguous K / V
+PS = "prefill_d128_kernel<true, false>"    # skip-softmax prefill
+PP = "prefill_d128_kernel<false, true>"    # dense prefill, page-gathered K / V
+
+# kernel -> (workload, summary file stem, source files, headline role: the bench call whose launches
+# the summary's traffic figure and traffic.json refer to)
 PROFILED = {
-    "prefill_d128_kernel<false>": ("varlen causal prefill bf16, 16 seqs L~U[256,4096], Hq=32, Hkv=8, D=128",
-                                   "prefill_d128_kernel.varlen_causal_16seq_L256-4096_Hq32_Hkv8_D128",
-                                   ["paged_skip_softmax_amd/csrc/prefill_d128.hip", _LDS] + _KSRC),
-    "prefill_d128_kernel<true>": ("skip-softmax prefill on the hot-key prefill input (same shapes), "
-                                  "threshold 0.01 and 0.1 in turn",
-                                  "prefill_d128_kernel_skip.varlen_causal_hot_16seq_thr0.01-0.1",
-                                  ["paged_skip_softmax_amd/csrc/prefill_d128.hip", _LDS] + _KSRC),
+    PF: ("varlen causal prefill bf16, 16 seqs L~U[256,4096], Hq=32, Hkv=8, D=128",
+         "prefill_d128_kernel.varlen_causal_16seq_L256-4096_Hq32_Hkv8_D128",
+         ["paged_skip_softmax_amd/csrc/prefill_d128.hip", _LDS] + _KSRC, "prefill"),
+    PS: ("skip-softmax prefill on the hot-key and the coherent-sink prefill inputs (same shapes), thresholds "
+         "0.01 and 0.1", "prefill_d128_kernel_skip.varlen_causal_hot_sink_16seq_thr0.01-0.1",
+         ["paged_skip_softmax_amd/csrc/prefill_d128.hip", _LDS] + _KSRC, "prefill_skip_0.1"),
+    PP: ("chunked prefill over the paged-decode cache (B=64, L~U[1024,32768], page 16), 256 new tokens per "
+         "sequence", "prefill_d128_kernel_paged.paged_cache_B64_L1k-32k_q256",
+         ["paged_skip_softmax_amd/csrc/prefill_d128.hip", _LDS] + _KSRC, "prefill_paged"),
     "decode_split_kernel": ("paged decode B=64, L~U[1024,32768], page 16, 32 splits of 128-key tiles",
                             "decode_split_kernel.paged_decode_B64_L1k-32k_page16_32splits",
-                            ["paged_skip_softmax_amd/csrc/decode.hip"] + _KSRC),
+                            ["paged_skip_softmax_amd/csrc/decode.hip"] + _KSRC, "decode"),
     "decode_merge_kernel": ("merge of the 32 split partials, B=64, Hq=32, D=128",
                             "decode_merge_kernel.paged_decode_B64_Hq32_32splits",
-                            ["paged_skip_softmax_amd/csrc/decode.hip"] + _KSRC),
+                            ["paged_skip_softmax_amd/csrc/decode.hip"] + _KSRC, "decode"),
     "decode_multi_kernel": ("multi-token paged decode: the paged-decode cache (B=64, L~U[1024,32768]) with 1..4 new "
                             "tokens per sequence, 32 splits", "decode_multi_kernel.paged_decode_B64_L1k-32k_q1-4_32splits",
-                            ["paged_skip_softmax_amd/csrc/decode.hip"] + _KSRC),
+                            ["paged_skip_softmax_amd/csrc/decode.hip"] + _KSRC, "decode_multi"),
     "decode_merge_multi_kernel": ("merge of the 32 split partials of the multi-token decode (1..4 tokens x 32 heads "
                                   "per sequence, B=64)", "decode_merge_multi_kernel.paged_decode_B64_q1-4_32splits",
-                                  ["paged_skip_softmax_amd/csrc/decode.hip"] + _KSRC),
+                                  ["paged_skip_softmax_amd/csrc/decode.hip"] + _KSRC, "decode_multi"),
     "decode_seq_kernel": ("sequential skip decode on hot keys, B=64, L~U[1024,32768], 32-key tiles, "
-                          "threshold 0 / 0.01 / 0.1 in turn",
-                          "decode_seq_kernel.paged_decode_hot_B64_thr0-0.01-0.1",
-                          ["paged_skip_softmax_amd/csrc/decode.hip"] + _KSRC),
+                          "threshold 0 / 0.01 / 0.1", "decode_seq_kernel.paged_decode_hot_B64_thr0-0.01-0.1",
+                          ["paged_skip_softmax_amd/csrc/decode.hip"] + _KSRC, "skip_0.0"),
     "smallseq_kernel": ("small-seq cross-attention B=30720, s_kv in {2,4,6,8,12,16}, H=16, D=128",
                         "smallseq_kernel.smallseq_cross_B30720_H16_D128",
-                        ["paged_skip_softmax_amd/csrc/smallseq.hip"] + _KSRC),
+                        ["paged_skip_softmax_amd/csrc/smallseq.hip"] + _KSRC, "smallseq"),
     "smallseq_bwd_kernel": ("small-seq backward from the stored weights, B=30720, s_kv in {2,4,6,8,12,16}, H=16, "
                             "D=128", "smallseq_bwd_kernel.smallseq_cross_B30720_H16_D128",
-                            ["paged_skip_softmax_amd/csrc/smallseq.hip"] + _KSRC),
+                            ["paged_skip_softmax_amd/csrc/smallseq.hip"] + _KSRC, "smallseq_bwd"),
     "bwd_prep_kernel": (_BWD_W + ": rowsum(dO * O) and lse * log2(e)",
-                        "bwd_prep_kernel.varlen_causal_16seq_L256-4096_Hq32", _BWD),
-    "bwd_dkdv_kernel": (_BWD_W + ": dK, dV", "bwd_dkdv_kernel.varlen_causal_16seq_L256-4096_Hq32_Hkv8_D128", _BWD),
-    "bwd_dq_kernel": (_BWD_W + ": dQ", "bwd_dq_kernel.varlen_causal_16seq_L256-4096_Hq32_Hkv8_D128", _BWD),
+                        "bwd_prep_kernel.varlen_causal_16seq_L256-4096_Hq32", _BWD, "prefill_bwd"),
+    "bwd_dkdv_kernel": (_BWD_W + ": dK, dV", "bwd_dkdv_kernel.varlen_causal_16seq_L256-4096_Hq32_Hkv8_D128", _BWD,
+                        "prefill_bwd"),
+    "bwd_dq_kernel": (_BWD_W + ": dQ", "bwd_dq_kernel.varlen_causal_16seq_L256-4096_Hq32_Hkv8_D128", _BWD,
+                      "prefill_bwd"),
 }
-# kernels launched more than once per step: the role of each launch, in launch order (the first role
-# is the one the roofline and traffic.json refer to)
-ROLES = {
-    "prefill_d128_kernel<false>": ["varlen causal prefill", "hot-key prefill input, dense"],
-    "prefill_d128_kernel<true>": ["threshold 0.01", "threshold 0.1"],
-    "decode_seq_kernel": ["threshold 0", "threshold 0.01", "threshold 0.1"],
-}
+
+
+def call_kernels(call):
+    """The kernels one bench call launches, in order (keys of PROFILED)."""
+    if call in ("prefill", "setup_prefill_fwd", "prefill_skip_0.0", "prefill_sink_0.0"):
+        return [PF]
+    if call.startswith(("prefill_skip_", "prefill_sink_", "map_prefill_")):
+        return [PS]
+    if call == "prefill_paged":
+        return [PP]
+    if call == "decode":
+        return ["decode_split_kernel", "decode_merge_kernel"]
+    if call.startswith(("skip_", "map_skip_")):
+        return ["decode_seq_kernel"]
+    if call in ("smallseq", "setup_smallseq_fwd"):
+        return ["smallseq_kernel"]
+    if call == "smallseq_bwd":
+        return ["smallseq_bwd_kernel"]
+    if call == "prefill_bwd":
+        return ["bwd_prep_kernel", "bwd_dkdv_kernel", "bwd_dq_kernel"]
+    if call == "decode_multi":
+        return ["decode_multi_kernel", "decode_merge_multi_kernel"]
+    return []
+
+
 PROFILE_COMMANDS = {
     "trace": "rocprofv3 --kernel-trace --stats -f csv -d {out}/prof_trace -o run -- "
-             "python3 bench.py --steps 5 --warmup 2 --no-cpu-baseline",
+             "python3 bench.py --steps 5 --warmup 2 --no-cpu-baseline --launch-log {out}/prof_trace/launch_log.json",
     "fetch": "rocprofv3 --pmc FETCH_SIZE -f csv -d {out}/prof_fetch -o run -- "
-             "python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline --calib-copy",
+             "python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline --calib-copy "
+             "--launch-log {out}/prof_fetch/launch_log.json",
     "write": "rocprofv3 --pmc WRITE_SIZE -f csv -d {out}/prof_write -o run -- "
-             "python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline --calib-copy",
+             "python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline --calib-copy "
+             "--launch-log {out}/prof_write/launch_log.json",
     "summary": "python3 bench.py --summarize-profiles {out}",
 }
 
@@ -631,6 +721,26 @@ def _per_dispatch_counter(rows, counter):
     return out
 
 
+def _roles(base, run, k, n):
+    """The role (bench call) of each of the n dispatches of kernel k in one profiled run, from the run's
+    launch log; None when there is no log or it does not account for exactly n dispatches."""
+    path = os.path.join(base, run, "launch_log.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        log = json.load(f)
+    roles = [c for c in log for kk in call_kernels(c) if kk == k]
+    return roles if len(roles) == n else None
+
+
+def _by_role(values, roles):
+    """role -> values, roles in first-launch order."""
+    out = {}
+    for v, r in zip(values, roles):
+        out.setdefault(r, []).append(v)
+    return out
+
+
 def _summarize_profiles(base):
     import numpy as np
     trace = _csv(os.path.join(base, "prof_trace"), "kernel_trace.csv")
@@ -645,7 +755,7 @@ def _summarize_profiles(base):
     f_fetch = kib / c_fetch
     f_write = kib / c_write
     durs = {}
-    for r in trace:
+    for r in sorted(trace, key=lambda r: int(r["Start_Timestamp"])):
         k = _match(r["Kernel_Name"])
         if k and k != "copy":
             durs.setdefault(k, []).append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
@@ -653,7 +763,7 @@ def _summarize_profiles(base):
     os.makedirs(outdir, exist_ok=True)
     traffic = {}
     cmds = "\n".join(f"#   {k}: {v.format(out=base)}" for k, v in PROFILE_COMMANDS.items())
-    for k, (workload, stem, srcs) in PROFILED.items():
+    for k, (workload, stem, srcs, headline) in PROFILED.items():
         if k not in durs:
             continue
         st = [r for r in stats if _match(r["Name"]) == k]
@@ -665,11 +775,11 @@ def _summarize_profiles(base):
                          f"{float(r['Percentage']):.2f}% of GPU kernel time")
         d = np.array(durs[k], dtype=np.float64) / 1e3
         lines.append(f"kernel_trace.csv: {len(d)} dispatches, mean {d.mean():.2f} us, median {np.median(d):.2f} us")
-        roles = ROLES.get(k, [])
-        nr = len(roles)
-        if nr and len(d) % nr == 0:
-            for i, role in enumerate(roles):
-                lines.append(f"  {role}: mean {d[i::nr].mean():.2f} us over {len(d[i::nr])} dispatches")
+        roles = _roles(base, "prof_trace", k, len(d))
+        if roles:
+            lines.append("  per bench call (from the run's launch log):")
+            for role, v in _by_role(list(d), roles).items():
+                lines.append(f"    {role}: mean {np.mean(v):.2f} us over {len(v)} dispatches")
         fk = fetch.get(k, [])
         wk = write.get(k, [])
         if fk and wk:
@@ -679,13 +789,20 @@ def _summarize_profiles(base):
                       f"(mean of {len(wk)})",
                       f"calibration: the 1 GiB copy read FETCH_SIZE {c_fetch:.0f} KiB and WRITE_SIZE "
                       f"{c_write:.0f} KiB, factors {f_fetch:.4f} (fetch) and {f_write:.4f} (write)",
-                      f"HBM traffic per launch (scaled): {byts / 1e6:.1f} MB"]
-            if nr and len(fk) % nr == 0 and len(wk) % nr == 0:
-                for i, role in enumerate(roles):
-                    b_i = (np.mean(fk[i::nr]) * f_fetch + np.mean(wk[i::nr]) * f_write) * 1024.0
-                    lines.append(f"  {role}: {b_i / 1e6:.1f} MB per launch")
-                byts = (np.mean(fk[0::nr]) * f_fetch + np.mean(wk[0::nr]) * f_write) * 1024.0
-            traffic[k] = {"bytes_per_launch": float(byts), "fetch_kib": fm, "write_kib": wm,
+                      f"HBM traffic per launch (scaled), all dispatches: {byts / 1e6:.1f} MB"]
+            rf, rw = _roles(base, "prof_fetch", k, len(fk)), _roles(base, "prof_write", k, len(wk))
+            if rf and rw:
+                bf, bw = _by_role(fk, rf), _by_role(wk, rw)
+                lines.append("  per bench call:")
+                for role in bf:
+                    if role in bw:
+                        b_i = (np.mean(bf[role]) * f_fetch + np.mean(bw[role]) * f_write) * 1024.0
+                        lines.append(f"    {role}: {b_i / 1e6:.1f} MB per launch")
+                if headline in bf and headline in bw:
+                    fm, wm = float(np.mean(bf[headline])), float(np.mean(bw[headline]))
+                    byts = (fm * f_fetch + wm * f_write) * 1024.0
+                    lines.append(f"traffic.json: the {headline} launches, {byts / 1e6:.1f} MB per launch")
+            traffic[k] = {"bytes_per_launch": float(byts), "fetch_kib": fm, "write_kib": wm, "role": headline,
                           "fetch_factor": f_fetch, "write_factor": f_write, "sources": srcs,
                           "sources_sha256": _sources_digest(srcs), "summary": f"profiles/{stem}.txt"}
         with open(os.path.join(outdir, stem + ".txt"), "w") as f:

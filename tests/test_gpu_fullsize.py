@@ -59,9 +59,12 @@ def test_full_varlen_prefill_sampled_rows():
     assert np.max(np.abs(ln[r[:, 0], r[:, 1]] - ld)) <= LSE_TOL
 
 
-@pytest.fixture(scope="module")
-def prefill_hot():
-    return W.varlen_prefill_hot(seed=1001, device=DEV)     # the full prefill shapes plus hot keys
+@pytest.fixture(scope="module", params=["hot", "sink"])
+def prefill_hot(request):
+    # the full prefill shapes plus hot keys; "sink": the coherent attention-sink variant
+    if request.param == "sink":
+        return W.varlen_prefill_sink(seed=1001, device=DEV)
+    return W.varlen_prefill_hot(seed=1001, device=DEV)
 
 
 @pytest.mark.parametrize("thr", [0.01, 0.1])
