@@ -42,7 +42,8 @@ attn_status_t hip_status(hipError_t e, const char *what)
 
 bool bad_threshold(float thr) { return !(thr >= 0.f && thr <= 1.f); } // also rejects NaN
 
-// ln(threshold) as the kernels compare it: tile_max - running_max < ln(thr); thr = 0 never skips.
+// log2(threshold): the kernels compare in the log2 domain, tile_max - running_max < log2(thr) (both in
+// log2 units); thr = 0 gives -inf, which never skips.
 float log2_threshold(float thr) { return thr > 0.f ? std::log2(thr) : -INFINITY; }
 
 constexpr int kDefaultSplits = 32;

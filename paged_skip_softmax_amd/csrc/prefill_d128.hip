@@ -1,8 +1,9 @@
-// bf16 varlen prefill, head dim 128, for gfx950: the D = 128 path of attn_prefill_varlen
-// ("Model-Optimizer: Add Triton unified attention kernel": variable-length batching, GQA, causal and
-// non-causal; sequences packed THD with cu_seqlens), dense (prefill_d128_kernel<false>) and with
-// skip-softmax on 32-key tiles ("TensorRT-LLM: Skip Softmax Attention", Description;
-// prefill_d128_kernel<true>).
+// bf16 varlen prefill, head dim 128, for gfx950: the D = 128 path of attn_prefill_varlen and the
+// long-query route of attn_decode_paged_multi ("Model-Optimizer: Add Triton unified attention kernel":
+// variable-length batching, GQA, causal and non-causal; sequences packed THD with cu_seqlens, or K / V
+// read through a block table from the paged cache).  One kernel template, prefill_d128_kernel<SKIP,
+// PAGED>: SKIP adds skip-softmax on 32-key tiles ("TensorRT-LLM: Skip Softmax Attention",
+// Description); PAGED takes K and V from [num_pages, Hkv, 16, D] caches instead of THD tensors.
 //
 // Work split.  A workgroup of 4 waves takes one query tile of one sequence for NH query heads of one
 // KV head's group times RB blocks of 32 query rows (NH * RB = 4, NH the largest power of two dividing
@@ -24,9 +25,12 @@
 // registers, no LDS store instructions), each in a two-stage ring with K one tile ahead of V: while the
 // waves use K(t+1) and V(t), the loads of K(t+2) and V(t+1) are in flight.  Each load instruction of a
 // wave fills 1 KB of LDS (4 key rows); rows past the sequence are outside the buffer resource and read
-// as zero.  LDS rows are not padded: the 16-byte chunks of a row are XOR-swizzled (slot = chunk ^
-// swz(row % 16)), which keeps both the 16-B reads of K and the transposed 8-B reads of V
-// (ds_read_b64_tr_b16) free of bank conflicts.  Waits are explicit: vmcnt of the wave's own loads,
+// as zero.  Paged: the four loads of wave w for tile t are exactly the 16 keys of one cache page (the
+// block-table entry 4t + w), through a buffer resource built per page whose size ends at the sequence's
+// last key; the block-table entries are read before the barrier that precedes the loads.
+// LDS rows are not padded: the 16-byte chunks of a row are XOR-swizzled (slot = chunk ^ swz(row % 16)),
+// which keeps both the 16-B reads of K and the transposed 8-B reads of V (ds_read_b64_tr_b16) free of
+// bank conflicts.  Waits are explicit: vmcnt of the wave's own loads,
 // then s_barrier.
 //
 // The running max used for the exponentials is only raised when a row's max exceeds it by more than 8
@@ -36,8 +40,9 @@
 // Skip-softmax.  The two 32-key halves of a 64-key tile are the skip tiles (aligned to key 0).  Their
 // row maxima come out of the same interleaved max as the dense tile max; each row keeps its exact
 // running max beside the lazy one, and a half is skipped when the running max exists and its max is
-// below it by more than -log2(threshold).  A skipped half contributes nothing (its exponentials are
-// branched over when every row of the wave skips it) and never raises the running max.
+// below it by more than -log2(threshold).  A skipped half contributes nothing and never raises the
+// running max; its exponentials are left out by a wave-uniform branch when every row of the wave
+// skips it, and the P.V products of a 64-key tile when every row skips both halves.
 #include "kcommon.h"
 #include "launch.h"
 #include "lds_dma.h"
