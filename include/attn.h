@@ -68,7 +68,8 @@ typedef enum { ATTN_F32 = 0, ATTN_BF16 = 1 } attn_dtype_t;
  *   skip_map_stride >= ceil(max_seqlen_k / 32); every entry of a row is written (2 past its visible keys).
  *   Supported: bf16 with D in {64, 128}; fp32 with D = 64.  B == 0 is a no-op.  bf16 needs
  *   max_seqlen_k * Hkv * D * 2 < 2^31 and, for D = 128 with a skip map, B * max_seqlen_q * Hq *
- *   skip_map_stride < 2^32 (else ATTN_ERR_UNSUPPORTED).
+ *   skip_map_stride < 2^32; D = 64 needs B <= 65535 and max_seqlen_q <= 65535 * 64 (grid dimensions)
+ *   (else ATTN_ERR_UNSUPPORTED).
  */
 attn_status_t attn_prefill_varlen(attn_dtype_t dtype, const void *q, const void *k, const void *v,
                                   const int32_t *cu_seqlens_q, const int32_t *cu_seqlens_k, int32_t B,
@@ -100,7 +101,8 @@ size_t attn_decode_paged_workspace_size(int32_t B, int32_t Hq, int32_t D, int32_
  *   workspace: device buffer of at least attn_decode_paged_workspace_size() bytes (may be NULL when
  *   that size is 0).  skip_map: nullable uint8 [B, Hq, skip_map_stride], sequential schedule only,
  *   skip_map_stride >= ceil(max_pages_per_seq * page_size / 32).
- *   Supported: D = 128, page_size = 16, Hq / Hkv <= 16.  B == 0 is a no-op.
+ *   Supported: D = 128, page_size = 16, Hq / Hkv <= 16, B <= 65535 (a grid dimension; else
+ *   ATTN_ERR_UNSUPPORTED).  B == 0 is a no-op.
  */
 attn_status_t attn_decode_paged(const void *q, const void *k_cache, const void *v_cache,
                                 const int32_t *block_table, const int32_t *seq_lens, int32_t B, int32_t Hq,
@@ -120,12 +122,13 @@ attn_status_t attn_decode_paged(const void *q, const void *k_cache, const void *
  *   max_seqlen_q >= every Lq_b; caches, block_table, seq_lens, page_size as for attn_decode_paged.
  *   num_splits in [0, 64] (0 = 32; the split-K schedule only).  workspace: at least
  *   attn_decode_paged_multi_workspace_size(total_q, max_seqlen_q, Hq, Hkv, D, num_splits) bytes
- *   (caller-owned, no initialisation; may be NULL when that is 0).  lse: nullable fp32 [total_q, Hq] (natural log; -inf for a token that sees no key,
- *   whose output is 0).
+ *   (caller-owned, no initialisation; may be NULL when that is 0).  lse: nullable fp32 [total_q, Hq]
+ *   (natural log; -inf for a token that sees no key, whose output is 0).
  *   Two schedules: with max_seqlen_q * Hq / Hkv <= 64 query rows per KV head, split-K over the cache with
  *   the rows in 16-row blocks (each block reads the cache once) and a merge kernel; beyond that (a
  *   chunked prefill), the prefill kernel with its K / V tiles gathered page by page, no split, no
- *   workspace.  Supported: D = 128, page_size = 16, B * max_seqlen_q * Hq < 2^31 (else
+ *   workspace.  Supported: D = 128, page_size = 16, B * max_seqlen_q * Hq < 2^31 and, on the split-K
+ *   schedule, B * ceil(max_seqlen_q * Hq / Hkv / 16) <= 65535 (a grid dimension) (else
  *   ATTN_ERR_UNSUPPORTED).  B == 0 or total_q == 0 is a no-op.
  */
 size_t attn_decode_paged_multi_workspace_size(int32_t total_q, int32_t max_seqlen_q, int32_t Hq, int32_t Hkv,

@@ -48,6 +48,7 @@ float log2_threshold(float thr) { return thr > 0.f ? std::log2(thr) : -INFINITY;
 
 constexpr int kDefaultSplits = 32;
 constexpr int kMaxSplits = 64;
+constexpr int64_t kMaxGridYZ = 65535; // largest y or z grid dimension a launch here may use
 
 int resolve_splits(int num_splits, float thr) { return num_splits != 0 ? num_splits : (thr == 0.f ? kDefaultSplits : 1); }
 
@@ -110,6 +111,8 @@ attn_status_t attn_decode_paged(const void *q, const void *k_cache, const void *
         return fail(ATTN_ERR_UNSUPPORTED, "attn_decode_paged: page_size = %d (built for 16)", page_size);
     if (Hq / Hkv > 16)
         return fail(ATTN_ERR_UNSUPPORTED, "attn_decode_paged: Hq / Hkv = %d > 16", Hq / Hkv);
+    if (B > kMaxGridYZ)
+        return fail(ATTN_ERR_UNSUPPORTED, "attn_decode_paged: B = %d above %d (a grid dimension)", B, (int)kMaxGridYZ);
     if (B == 0)
         return ok();
     if (!q || !k_cache || !v_cache || !block_table || !seq_lens || !o)
@@ -293,6 +296,10 @@ attn_status_t attn_decode_paged_multi(const void *q, const int32_t *cu_seqlens_q
         return hip_status(attn::launch_prefill_d128(a, static_cast<hipStream_t>(stream)), "paged prefill launch");
     }
     const int S = num_splits == 0 ? kDefaultSplits : num_splits;
+    const int ncb = std::max(1, (max_seqlen_q * G + 15) / 16);
+    if ((int64_t)B * ncb > kMaxGridYZ)
+        return fail(ATTN_ERR_UNSUPPORTED, "attn_decode_paged_multi: B * ceil(max_seqlen_q * Hq / Hkv / 16) = %lld above %d "
+                                          "(a grid dimension)", (long long)B * ncb, (int)kMaxGridYZ);
     const size_t need = attn_decode_paged_multi_workspace_size(total_q, max_seqlen_q, Hq, Hkv, D, S);
     if (!workspace || workspace_bytes < need)
         return fail(ATTN_ERR_WORKSPACE, "attn_decode_paged_multi: workspace %zu bytes, need %zu", workspace_bytes,
@@ -309,7 +316,7 @@ attn_status_t attn_decode_paged_multi(const void *q, const int32_t *cu_seqlens_q
     a.G = G;
     a.max_pages = max_pages_per_seq;
     a.num_splits = S;
-    a.ncb = std::max(1, (max_seqlen_q * G + 15) / 16);
+    a.ncb = ncb;
     a.scale_log2 = scale * 1.4426950408889634f;
     a.ws_o = static_cast<float *>(workspace);
     a.ws_lse = a.ws_o + (size_t)total_q * Hq * S * D;
@@ -416,6 +423,9 @@ attn_status_t attn_prefill_varlen(attn_dtype_t dtype, const void *q, const void 
         (uint64_t)B * (uint64_t)max_seqlen_q * (uint64_t)Hq * (uint64_t)skip_map_stride >= ((uint64_t)1 << 32))
         return fail(ATTN_ERR_UNSUPPORTED, "attn_prefill_varlen: a skip map of B * max_seqlen_q * Hq * stride bytes must "
                                           "stay below 2^32");
+    if (D == 64 && (B > kMaxGridYZ || ((int64_t)max_seqlen_q + 63) / 64 > kMaxGridYZ))
+        return fail(ATTN_ERR_UNSUPPORTED, "attn_prefill_varlen: D = 64 needs B <= %d and max_seqlen_q <= %lld (grid "
+                                          "dimensions)", (int)kMaxGridYZ, (long long)kMaxGridYZ * 64);
     if (B == 0 || max_seqlen_q == 0)
         return ok();
     if (!q || !k || !v || !cu_seqlens_q || !cu_seqlens_k || !o)

@@ -5,6 +5,8 @@
 //    contiguous runs of ceil(ntiles / num_splits) tiles.  Every (batch row, KV head, split) is one
 //    workgroup that writes a partial (O_s, lse_s) for the G query heads of the KV head; a second small
 //    kernel merges the partials of a row: lse = log sum_s e^{lse_s}, O = sum_s e^{lse_s - lse} O_s.
+//    The KV head is the fastest grid dimension: the Hkv slabs of a page lie next to each other in the
+//    cache, so the workgroups running together read whole pages rather than one slab of many pages.
 //  * skip-softmax on: one sequential split over 32-key tiles.  Tile t of query row r is skipped (no exp,
 //    no P.V, no rescale) when exp(tmax_t - m) < threshold, m the running max before the tile
 //    ("TensorRT-LLM: Skip Softmax Attention", Description).  Because a skipped tile lies below the
@@ -238,7 +240,7 @@ __device__ __forceinline__ void merge_waves(WaveState &st, void *smem, int G, Ou
 
 __global__ __launch_bounds__(64 * kSplitWaves) void decode_split_kernel(SplitArgs a)
 {
-    const int sp = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+    const int g = blockIdx.x, sp = blockIdx.y, b = blockIdx.z;
     const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int S = a.num_splits;
     const int L = a.seq_lens[b];
@@ -312,6 +314,8 @@ struct MergeArgs {
     float *lse;    // nullable [rows]
 };
 
+constexpr int kMergeBatch = 16; // partial loads a merge wave has in flight together
+
 // One wave per (batch row, query head): lse = log sum_s e^{lse_s}, O = sum_s e^{lse_s - lse} O_s.
 __device__ __forceinline__ void merge_rows(const MergeArgs &a)
 {
@@ -326,14 +330,27 @@ __device__ __forceinline__ void merge_rows(const MergeArgs &a)
     if (M != kNegInf) {
         const float e = exp2_fast(ls - M);
         const float den = wave_sum(e);
+        // every split wrote a finite partial (o = 0 where it saw no key, weight e = 0), so the loads go
+        // out unconditionally, kMergeBatch at a time
         const float2 *src = reinterpret_cast<const float2 *>(a.ws_o + (size_t)row * S * kD) + lane;
-        for (int s = 0; s < S; ++s) {
-            const float ws = __shfl(e, s);
-            if (ws != 0.f) {
-                const float2 v = src[s * (kD / 2)];
-                o0 = fmaf(ws, v.x, o0);
-                o1 = fmaf(ws, v.y, o1);
+        int s = 0;
+        for (; s + kMergeBatch <= S; s += kMergeBatch) {
+            float2 v[kMergeBatch];
+#pragma unroll
+            for (int u = 0; u < kMergeBatch; ++u)
+                v[u] = src[(s + u) * (kD / 2)];
+#pragma unroll
+            for (int u = 0; u < kMergeBatch; ++u) {
+                const float ws = __shfl(e, s + u);
+                o0 = fmaf(ws, v[u].x, o0);
+                o1 = fmaf(ws, v[u].y, o1);
             }
+        }
+        for (; s < S; ++s) {
+            const float ws = __shfl(e, s);
+            const float2 v = src[s * (kD / 2)];
+            o0 = fmaf(ws, v.x, o0);
+            o1 = fmaf(ws, v.y, o1);
         }
         o0 /= den;
         o1 /= den;
@@ -351,7 +368,7 @@ __global__ __launch_bounds__(256) void decode_merge_multi_kernel(MergeArgs a) { 
 
 hipError_t launch_decode_split(const SplitArgs &a, int B, uint16_t *o, float *lse, hipStream_t stream)
 {
-    hipLaunchKernelGGL(decode_split_kernel, dim3(a.num_splits, a.Hkv, B), dim3(64 * kSplitWaves), 0, stream, a);
+    hipLaunchKernelGGL(decode_split_kernel, dim3(a.Hkv, a.num_splits, B), dim3(64 * kSplitWaves), 0, stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return e;
@@ -396,7 +413,7 @@ __device__ __forceinline__ float chunk_scores_lim(const uint4 kr[2][4], const bf
 // keys the block's last token sees.
 __global__ __launch_bounds__(64 * kSplitWaves) void decode_multi_kernel(MultiArgs a)
 {
-    const int sp = blockIdx.x, g = blockIdx.y, b = blockIdx.z / a.ncb, cb = blockIdx.z % a.ncb;
+    const int g = blockIdx.x, sp = blockIdx.y, b = blockIdx.z / a.ncb, cb = blockIdx.z % a.ncb;
     const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int q0 = a.cu_q[b], Lq = a.cu_q[b + 1] - q0;
     const int r0 = 16 * cb;
@@ -485,7 +502,7 @@ __global__ __launch_bounds__(64 * kSplitWaves) void decode_multi_kernel(MultiArg
 
 hipError_t launch_decode_multi(const MultiArgs &a, int B, int total_q, uint16_t *o, float *lse, hipStream_t stream)
 {
-    hipLaunchKernelGGL(decode_multi_kernel, dim3(a.num_splits, a.Hkv, B * a.ncb), dim3(64 * kSplitWaves), 0, stream,
+    hipLaunchKernelGGL(decode_multi_kernel, dim3(a.Hkv, a.num_splits, B * a.ncb), dim3(64 * kSplitWaves), 0, stream,
                        a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)

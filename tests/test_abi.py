@@ -58,6 +58,9 @@ def test_decode_validation(lib):
     assert _decode(lib, wsb=100) == WORKSPACE
     assert _decode(lib, ws=None) == WORKSPACE
     assert _decode(lib, B=0) == _lib.ATTN_OK
+    # B is a grid dimension of both schedules
+    assert _decode(lib, B=65536) == UNSUPPORTED
+    assert _decode(lib, B=65536, thr=0.1, splits=1) == UNSUPPORTED
     _decode(lib, splits=99)
     assert b"num_splits" in lib.attn_last_error_message()
 
@@ -94,6 +97,11 @@ def test_prefill_validation(lib):
     assert _prefill(lib, mk=1 << 20, Hkv=8, Hq=8) == UNSUPPORTED
     assert _prefill(lib, map=FAKE, B=4096, mq=4096, mk=4096, Hq=32, Hkv=8, stride=128) == UNSUPPORTED
     assert b"2^32" in lib.attn_last_error_message()
+    # the D = 64 kernels put B and the query tiles in grid dimensions; the D = 128 kernel uses one
+    for dt in (_lib.ATTN_BF16, _lib.ATTN_F32):
+        assert _prefill(lib, dt=dt, D=64, B=65536) == UNSUPPORTED
+        assert _prefill(lib, dt=dt, D=64, mq=65535 * 64 + 1) == UNSUPPORTED
+    assert _prefill(lib, B=0, D=128, mq=65535 * 64 + 1) == _lib.ATTN_OK
 
 
 def _backward(lib, **kw):
@@ -180,6 +188,9 @@ def test_decode_multi_validation(lib):
     assert call(D=64) == UNSUPPORTED
     assert call(page=32) == UNSUPPORTED
     assert call(mq=1 << 20, B=1 << 10) == UNSUPPORTED
+    # 8 tokens x 4 heads = 2 blocks of 16 rows per sequence: B * 2 grid blocks in z
+    assert call(B=32768, mq=8) == UNSUPPORTED
+    assert call(B=32767, mq=8, wsb=100) == WORKSPACE  # within the grid; fails on the workspace next
     assert call(cq=None) == INVALID
     assert call(wsb=100) == WORKSPACE
     assert call(B=0) == _lib.ATTN_OK
