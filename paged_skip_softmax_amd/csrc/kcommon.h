@@ -63,6 +63,20 @@ __device__ __forceinline__ float sum_across_groups16(float v)
     return v + __shfl_xor(v, 32);
 }
 
+// Max / sum of v over lanes l and l ^ 32, by v_permlane32_swap (a VALU op; no LDS round trip).  The
+// swap exchanges the upper half of its first operand with the lower half of its second: with both set
+// to v, lane l ends up holding {own, other} (l < 32) or {other, own} (l >= 32).
+__device__ __forceinline__ float max_halves(float v)
+{
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_halves(float v)
+{
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // Full-wave reductions.
 __device__ __forceinline__ float wave_max(float v)
 {

@@ -61,6 +61,7 @@ constexpr int kXcds = 8;
 
 constexpr int kStages = 2;
 
+
 // Two-stage rings for K and V, one LDS array per stage (64 KB per workgroup).
 __shared__ __attribute__((aligned(1024))) uint4 k_st0[kTileChunks], k_st1[kTileChunks];
 __shared__ __attribute__((aligned(1024))) uint4 v_st0[kTileChunks], v_st1[kTileChunks];
@@ -192,10 +193,10 @@ __device__ __forceinline__ void tile_stats(float t0, float t1, int t, const Iter
     const float sl = c.scale_log2;
     if (!SKIP) {
         tm = fmaxf(t0, t1);
-        tm = fmaxf(tm, __shfl_xor(tm, 32)) * sl;
+        tm = max_halves(tm) * sl;
     } else {
-        const float h0 = fmaxf(t0, __shfl_xor(t0, 32)) * sl;
-        const float h1 = fmaxf(t1, __shfl_xor(t1, 32)) * sl;
+        const float h0 = max_halves(t0) * sl;
+        const float h1 = max_halves(t1) * sl;
         const int kb = t * kBN;
         const bool vis0 = kb < c.kend_row, vis1 = kb + 32 < c.kend_row;
         const bool skip0 = vis0 && ss.m_true != kNegInf && h0 - ss.m_true < c.log2_thr;
@@ -222,17 +223,21 @@ __device__ __forceinline__ bool needs_mask(int t, const IterCtx &c)
 }
 
 // Tile t held in stage ST = t % 2 (K(t+1) in the other stage).  K runs one tile ahead of V: when tile
-// t starts, K(t+1) and V(t) must be resident.
-//   wait for the wave's loads, barrier (every wave is done with K(t) and V(t-1)), then start loading
-//   K(t+2) and V(t+1) into those two stages;
+// t starts, K(t+1) and V(t) must be resident.  t0, t1: the lane's partial maxima of the two 32-key
+// halves of tile t on entry, of tile t+1 on return.
+//   wait for the wave's loads, barrier (every wave is done with K(t) and V(t-1)); read the first two K
+//   operands of (b), then start loading K(t+2) and V(t+1) into those two stages, and take the row
+//   statistics (and skip decisions) of tile t while the reads are in flight;
 //   (a) rescale O and l when the max rose by more than the slack;
-//   (b) QK^T of tile t+1, with the exponentials of tile t placed between its MFMAs;
+//   (b) QK^T of tile t+1, with the exponentials and row sums of tile t placed between its MFMAs, at
+//       raised wave priority (the two waves of a SIMD belong to different workgroups; the one in its
+//       MFMA-and-exponential phase goes first, the other fills the gaps);
 //   (c) mask tile t+1 where it crosses the diagonal or the sequence end;
 //   (d) P.V of tile t, with the row max of tile t+1 placed between its MFMAs.
 // On the last tile, (b)-(d) compute scores from a stale K stage that are never used.
 template <int ST, bool SKIP, bool PAGED>
 __device__ __forceinline__ void iteration(int t, const IterCtx &c, const Loader<PAGED> &ld, Wave &wv, f32x16 sc[2],
-                                          float &tm, bool &raise, SkipState &ss)
+                                          float &t0, float &t1, SkipState &ss)
 {
     // paged: the block-table reads go out before the wait, so the barrier covers their latency
     int page_k = 0, page_v = 0;
@@ -244,11 +249,18 @@ __device__ __forceinline__ void iteration(int t, const IterCtx &c, const Loader<
     }
     wait_vmcnt<0>();
     barrier();
+    constexpr int P = ST;
+    const char *kt = reinterpret_cast<const char *>(kbuf<(P + 1) % kStages>());
+    auto kop = [&](int step) { return ld16(kt + (step & 1) * 32 * 256 + wv.ka[step >> 1]); };
+    uint4 k0 = kop(0), k1 = kop(1);
+    sched_fence();
     if (t + 2 < c.niter)
         ld.template issue_k<ST>(t + 2, page_k);
     if (t + 1 < c.niter)
         ld.template issue_v<(ST + 1) % kStages>(t + 1, page_v);
-    constexpr int P = ST;
+    float tm;
+    bool raise;
+    tile_stats<SKIP>(t0, t1, t, c, wv, ss, tm, raise);
 
     // (a)
     if (__any(raise)) {
@@ -265,6 +277,9 @@ __device__ __forceinline__ void iteration(int t, const IterCtx &c, const Loader<
     const float m_use = wv.m == kNegInf ? 0.f : wv.m;
     const float sl = c.scale_log2;
 
+    sched_fence();
+    __builtin_amdgcn_s_setprio(1);
+    sched_fence();
     // (b) 16 MFMA steps, alternating the two 32-key blocks of tile t+1; K operands read two steps ahead
     f32x16 nx[2];
 #pragma unroll
@@ -274,9 +289,6 @@ __device__ __forceinline__ void iteration(int t, const IterCtx &c, const Loader<
     }
     uint32_t pk[2][8];
     {
-        const char *kt = reinterpret_cast<const char *>(kbuf<(P + 1) % kStages>());
-        auto kop = [&](int step) { return ld16(kt + (step & 1) * 32 * 256 + wv.ka[step >> 1]); };
-        uint4 k0 = kop(0), k1 = kop(1);
 #pragma unroll
         for (int step = 0; step < 16; ++step) {
             const uint4 k2 = step + 2 < 16 ? kop(step + 2) : k0;
@@ -286,6 +298,7 @@ __device__ __forceinline__ void iteration(int t, const IterCtx &c, const Loader<
                 const float p0 = exp2_fast(fmaf(sc[kk][i], sl, -m_use));
                 const float p1 = exp2_fast(fmaf(sc[kk][i + 1], sl, -m_use));
                 wv.l += p0 + p1;
+                anchor(wv.l);
                 pk[kk][i >> 1] = pack_bf16x2(p0, p1);
             } else {
                 // a skipped half adds nothing and is not rescaled; when every row of the wave skips it,
@@ -296,6 +309,7 @@ __device__ __forceinline__ void iteration(int t, const IterCtx &c, const Loader<
                     p1 = exp2_fast(fmaf(sc[kk][i + 1], sl, -m_use));
                     wv.l += p0 + p1;
                 }
+                anchor(wv.l);
                 pk[kk][i >> 1] = pack_bf16x2(p0, p1);
             }
             anchor(pk[kk][i >> 1]);
@@ -305,13 +319,17 @@ __device__ __forceinline__ void iteration(int t, const IterCtx &c, const Loader<
         }
     }
 
+    sched_fence();
+    __builtin_amdgcn_s_setprio(0);
+    sched_fence();
     // (c)
     if (t + 1 < c.niter && needs_mask(t + 1, c))
         mask_tile(nx, c.kend_row - (t + 1) * kBN, c.J);
 
     // (d) 16 MFMA steps over (32-key block kk, 16-key half u, d block db), db fastest so consecutive
     // MFMAs use different accumulators; V operands read two steps ahead
-    float t0 = nx[0][0], t1 = nx[1][0];
+    t0 = nx[0][0];
+    t1 = nx[1][0];
     {
         const char *vt = reinterpret_cast<const char *>(vbuf<P>());
         auto vop = [&](int step) {
@@ -364,7 +382,6 @@ __device__ __forceinline__ void iteration(int t, const IterCtx &c, const Loader<
             }
         }
     }
-    tile_stats<SKIP>(t0, t1, t + 1, c, wv, ss, tm, raise);
     sc[0] = nx[0];
     sc[1] = nx[1];
 }
@@ -500,8 +517,7 @@ void prefill_d128_kernel(PrefillArgs a, int NH, int RB, int nqt, int nunits)
     }
 
     f32x16 sc[2];
-    float tm = kNegInf;
-    bool raise = false;
+    float t0 = kNegInf, t1 = kNegInf;
     SkipState ss{kNegInf, {true, true}};
     IterCtx c{niter, Lk, a.causal, first_row_w, diag, kend_row, J, a.scale_log2, a.log2_thr, SKIP ? a.skip_map : nullptr, map_row,
               a.map_stride};
@@ -522,21 +538,21 @@ void prefill_d128_kernel(PrefillArgs a, int NH, int RB, int nqt, int nunits)
         qk_tile<0>(wv, sc);
         if (needs_mask(0, c))
             mask_tile(sc, kend_row, J);
-        float t0 = sc[0][0], t1 = sc[1][0];
+        t0 = sc[0][0];
+        t1 = sc[1][0];
 #pragma unroll
         for (int i = 1; i < 16; ++i) {
             t0 = fmaxf(t0, sc[0][i]);
             t1 = fmaxf(t1, sc[1][i]);
         }
-        tile_stats<SKIP>(t0, t1, 0, c, wv, ss, tm, raise);
     }
     for (int t = 0; t < niter; t += kStages) {
-        iteration<0, SKIP, PAGED>(t, c, ld, wv, sc, tm, raise, ss);
+        iteration<0, SKIP, PAGED>(t, c, ld, wv, sc, t0, t1, ss);
         if (t + 1 < niter)
-            iteration<1, SKIP, PAGED>(t + 1, c, ld, wv, sc, tm, raise, ss);
+            iteration<1, SKIP, PAGED>(t + 1, c, ld, wv, sc, t0, t1, ss);
     }
 
-    wv.l += __shfl_xor(wv.l, 32);
+    wv.l = sum_halves(wv.l);
     if (!row_ok)
         return;
     const float inv = wv.l > 0.f ? 1.f / wv.l : 0.f;
