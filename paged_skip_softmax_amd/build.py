@@ -24,8 +24,10 @@ FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall",
          "-I", os.path.join(ROOT, "include"), "-I", CSRC]
 
 
-# Per-source extras.  The dense D=128 prefill kernel never produces NaN (its LDS tiles start zeroed and
-# rows past a sequence read as zero), so max() of MFMA results needs no NaN canonicalisation.
+# Per-source extras.  No NaN reaches a used value in the D=128 prefill kernels: every K / V row they use
+# arrives by their own loads (rows past a sequence read as zero), and LDS left over from earlier work is
+# only read for the scores of the tile past the last, which are discarded; so max() of MFMA results
+# needs no NaN canonicalisation.
 EXTRA = {"prefill_d128.hip": ["-fno-honor-nans"]}
 
 

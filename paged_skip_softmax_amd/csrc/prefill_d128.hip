@@ -420,14 +420,6 @@ void prefill_d128_kernel(PrefillArgs a, int NH, int RB, int nqt, int nunits)
     const int first_row_w = m0 + 32 * rbk;
     const int niter = (kend + kBN - 1) / kBN;
 
-    // zero the LDS rings once, so that stale contents never hold NaN
-    {
-        uint4 *const bufs[4] = {k_st0, k_st1, v_st0, v_st1};
-#pragma unroll
-        for (int bi = 0; bi < 4; ++bi)
-            for (int i = tid; i < kTileChunks; i += kThreads)
-                bufs[bi][i] = make_uint4(0, 0, 0, 0);
-    }
 
     // loads: wave w fills 4-row blocks rb0 .. rb0+3 of each tile; lane -> row 4 rb + lane/16, slot lane%16
     Loader<PAGED> ld;
@@ -467,6 +459,15 @@ void prefill_d128_kernel(PrefillArgs a, int NH, int RB, int nqt, int nunits)
         }
     }
 
+    // the first K / V tiles go out before anything else
+    if (niter > 0) {
+        const int pg0 = PAGED ? ld.page_of(0) : 0;
+        ld.template issue_k<0>(0, pg0);
+        ld.template issue_v<0>(0, pg0);
+        if (niter > 1)
+            ld.template issue_k<1>(1, PAGED ? ld.page_of(1) : 0);
+    }
+
     Wave wv;
     {
         const uint16_t *qg = static_cast<const uint16_t *>(a.q);
@@ -481,7 +482,7 @@ void prefill_d128_kernel(PrefillArgs a, int NH, int RB, int nqt, int nunits)
                 wv.acc[db][i] = 0.f;
         wv.m = kNegInf;
         wv.l = 0.f;
-        // settle the Q loads and the LDS zeroing before the first barrier; no later compiler-inserted
+        // settle the Q loads (and the first tiles) before the first barrier; no later compiler-inserted
         // wait inside the loop is then needed for them (such a wait would also drain the loads in flight)
         compiler_fence();
         __builtin_amdgcn_s_waitcnt(0);
@@ -522,19 +523,7 @@ void prefill_d128_kernel(PrefillArgs a, int NH, int RB, int nqt, int nunits)
     IterCtx c{niter, Lk, a.causal, first_row_w, diag, kend_row, J, a.scale_log2, a.log2_thr, SKIP ? a.skip_map : nullptr, map_row,
               a.map_stride};
     if (niter > 0) {
-        // prologue: K(0), V(0), K(1) in flight; wait for K(0), then the masked scores of tile 0 and
-        // their row max
-        constexpr int L = kLoadsPerWave;
-        const int pg0 = PAGED ? ld.page_of(0) : 0;
-        ld.template issue_k<0>(0, pg0);
-        ld.template issue_v<0>(0, pg0);
-        if (niter > 1) {
-            ld.template issue_k<1>(1, PAGED ? ld.page_of(1) : 0);
-            wait_vmcnt<2 * L>();
-        } else {
-            wait_vmcnt<L>();
-        }
-        barrier();
+        // prologue: K(0), V(0), K(1) arrived with the Q rows; the masked scores of tile 0 and their row max
         qk_tile<0>(wv, sc);
         if (needs_mask(0, c))
             mask_tile(sc, kend_row, J);
