@@ -14,9 +14,10 @@
 //    all earlier tiles, skipped or not.  So the waves of the workgroup take consecutive tiles in
 //    rounds, publish their tile maxima in LDS, and each decides exactly from the prefix max -- the
 //    decisions of one sequential pass, taken in parallel.  V of a tile is read only when at least one
-//    query row of the group keeps it.  The K rows of the next round are loaded while the current round
-//    runs, and the batch rows are dispatched longest first, so that the longest sequences (the critical
-//    path of a one-split-per-sequence schedule) start at once and the short ones fill in behind them.
+//    query row of the group keeps it.  The K rows run two rounds ahead (requested after a round's V,
+//    so that waiting for that V leaves them in flight), and the batch rows are dispatched longest
+//    first, so that the longest sequences (the critical path of a one-split-per-sequence schedule)
+//    start at once and the short ones fill in behind them.
 //
 // Cache layout: [num_pages, Hkv, 16, D] bf16, so one (page, KV head) is a contiguous 4 KB slab.
 //
@@ -568,7 +569,10 @@ __global__ __launch_bounds__(64 * kSeqWaves) void decode_seq_kernel(SeqArgs a)
     WaveState st;
     state_init(st);
     float run_max = kNegInf; // max of tile maxima over all earlier rounds (log2 units), head n
-    const int32_t *btr = a.bt + (size_t)b * a.max_pages;
+    // the block table through the constant address space: read-only for the kernel, so its uniform reads
+    // are scalar loads, which leave the vector-memory counter (and the loads in flight) alone
+    const __attribute__((address_space(4))) int32_t *btr =
+        (const __attribute__((address_space(4))) int32_t *)(a.bt + (size_t)b * a.max_pages);
     const size_t slab = (size_t)kPage * kD;
     const size_t head_off = (size_t)g * slab;
     const size_t page_stride = (size_t)a.Hkv * slab;
@@ -582,30 +586,30 @@ __global__ __launch_bounds__(64 * kSeqWaves) void decode_seq_kernel(SeqArgs a)
         o0 = (size_t)p0 * page_stride + head_off;
         o1 = (size_t)p1 * page_stride + head_off;
     };
-    // The K rows of round r+1 are loaded while round r runs: scores of a round never wait for HBM
-    // unless the previous round read no V at all.
-    size_t o0 = 0, o1 = 0;
-    uint4 kr[2][4];
+    // K rows run two rounds ahead: the K of round r+2 is requested after round r's V, so that waiting
+    // for that V (loads complete in order) leaves the K of rounds r+1 and r+2 in flight.  The three K
+    // buffers rotate by name (the loop is unrolled by three): a register copy would wait for its load.
+    size_t o0 = 0, o1 = 0, n0 = 0, n1 = 0;
+    uint4 kb[3][2][4];
     if (ntiles > 0) {
         tile_pages(w, o0, o1);
-        load_k_chunk(a.kc + o0, a.kc + o1, lane, kr);
+        load_k_chunk(a.kc + o0, a.kc + o1, lane, kb[0]);
+        tile_pages(w + kSeqWaves, n0, n1);
+        load_k_chunk(a.kc + n0, a.kc + n1, lane, kb[1]);
     }
     int parity = 0;
-    for (int base = 0; base < ntiles; base += kSeqWaves, parity ^= 1) {
+    // one round: scores of tile base + w from kc, the round's decisions, its V, the K of round r+2 into kq
+    auto round = [&](int base, uint4 (&kc)[2][4], uint4 (&kq)[2][4]) {
         const int t = base + w;
         const int tok0 = t * kSkipTile;
         const bool active = t < ntiles;
-        size_t n0, n1;
-        tile_pages(t + kSeqWaves, n0, n1);
-        uint4 kn[2][4];
-        load_k_chunk(a.kc + n0, a.kc + n1, lane, kn);
         f32x4 sc[2];
         float tmax = kNegInf;
         if (active)
-            tmax = chunk_scores(kr, qop, tok0, L, lane, sc) * a.scale_log2;
+            tmax = chunk_scores(kc, qop, tok0, L, lane, sc) * a.scale_log2;
         if (j == 0)
             tmax_buf[parity][w][n] = tmax;
-        // LDS write visible, then a plain barrier: the K loads of the next round stay in flight
+        // LDS write visible, then a plain barrier: the K loads of the next rounds stay in flight
         __builtin_amdgcn_s_waitcnt(kWaitLdsOnly);
         asm volatile("" ::: "memory");
         __builtin_amdgcn_s_barrier();
@@ -619,27 +623,41 @@ __global__ __launch_bounds__(64 * kSeqWaves) void decode_seq_kernel(SeqArgs a)
             round_max = fmaxf(round_max, tm);
         }
         run_max = round_max;
+        bool keep = false, any_keep = false;
+        uint4 vr[2][4];
         if (active) {
             // skip iff a running max exists and tmax - m < log2(threshold)
             const bool skip = prefix != kNegInf && tmax - prefix < a.log2_thr;
-            const bool keep = !skip;
+            keep = !skip;
             // V is needed when any real head of the group keeps the tile
-            const bool any_keep = __any(keep && n < a.G);
-            if (any_keep) {
-                uint4 vr[2][4];
+            any_keep = __any(keep && n < a.G);
+            if (any_keep)
                 load_v_chunk(a.vc + o0, a.vc + o1, lane, vr);
-                chunk_update(st, sc, tmax, keep, vr, tok0, L, a.scale_log2, vt, lane);
-            }
             if (a.skip_map && j == 0 && n < a.G)
                 a.skip_map[(row0 + n) * a.map_stride + t] = skip ? 1 : 0;
         }
-#pragma unroll
-        for (int pg = 0; pg < 2; ++pg)
-#pragma unroll
-            for (int s4 = 0; s4 < 4; ++s4)
-                kr[pg][s4] = kn[pg][s4];
+        size_t q0, q1;
+        tile_pages(t + 2 * kSeqWaves, q0, q1);
+        load_k_chunk(a.kc + q0, a.kc + q1, lane, kq);
+        if (active && any_keep)
+            chunk_update(st, sc, tmax, keep, vr, tok0, L, a.scale_log2, vt, lane);
         o0 = n0;
         o1 = n1;
+        n0 = q0;
+        n1 = q1;
+        parity ^= 1;
+    };
+    for (int base = 0; base < ntiles;) {
+        round(base, kb[0], kb[2]);
+        base += kSeqWaves;
+        if (base >= ntiles)
+            break;
+        round(base, kb[1], kb[0]);
+        base += kSeqWaves;
+        if (base >= ntiles)
+            break;
+        round(base, kb[2], kb[1]);
+        base += kSeqWaves;
     }
     merge_waves<kSeqWaves>(st, smem, a.G, [&](int h, int d, float o, float lse) {
         a.o[(row0 + h) * kD + d] = f32_to_bf16(o);
