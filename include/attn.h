@@ -117,19 +117,24 @@ attn_status_t attn_decode_paged(const void *q, const void *k_cache, const void *
  * attention kernel, whose summary gives causal masking over variable-length batches).  Sequence b has
  * Lq_b = cu_seqlens_q[b + 1] - cu_seqlens_q[b] new query tokens, the last Lq_b of its seq_lens[b]
  * cached keys (already in the cache); its token i sees keys j < seq_lens[b] - Lq_b + i + 1 (bottom-right
- * causal; none when that is <= 0).  Dense (no skip-softmax).
+ * causal; none when that is <= 0).  Skip-softmax as in attn_prefill_varlen ("TensorRT-LLM: Skip Softmax
+ * Attention", Description): per (token, head) row and 32-key tile, tiles aligned to key 0 of the cache.
  *   q, o [total_q, Hq, D] bf16 THD (total_q = cu_seqlens_q[B]); cu_seqlens_q int32 [B + 1];
  *   max_seqlen_q >= every Lq_b; caches, block_table, seq_lens, page_size as for attn_decode_paged.
- *   num_splits in [0, 64] (0 = 32; the split-K schedule only).  workspace: at least
- *   attn_decode_paged_multi_workspace_size(total_q, max_seqlen_q, Hq, Hkv, D, num_splits) bytes
- *   (caller-owned, no initialisation; may be NULL when that is 0).  lse: nullable fp32 [total_q, Hq]
- *   (natural log; -inf for a token that sees no key, whose output is 0).
- *   Two schedules: with max_seqlen_q * Hq / Hkv <= 64 query rows per KV head, split-K over the cache with
- *   the rows in 16-row blocks (each block reads the cache once) and a merge kernel; beyond that (a
- *   chunked prefill), the prefill kernel with its K / V tiles gathered page by page, no split, no
- *   workspace.  Supported: D = 128, page_size = 16, B * max_seqlen_q * Hq < 2^31 and, on the split-K
- *   schedule, B * ceil(max_seqlen_q * Hq / Hkv / 16) <= 65535 (a grid dimension) (else
- *   ATTN_ERR_UNSUPPORTED).  B == 0 or total_q == 0 is a no-op.
+ *   skip_threshold in [0, 1] (0 = dense).  num_splits in [0, 64] (0 = 32; the split-K schedule only).
+ *   workspace: at least attn_decode_paged_multi_workspace_size(total_q, max_seqlen_q, Hq, Hkv, D,
+ *   num_splits) bytes (caller-owned, no initialisation; may be NULL when that is 0; unused when
+ *   skip-softmax is on).  lse: nullable fp32 [total_q, Hq] (natural log; -inf for a token that sees no
+ *   key, whose output is 0).  skip_map: nullable uint8 [total_q, Hq, skip_map_stride] with
+ *   skip_map_stride >= ceil(max_pages_per_seq * page_size / 32); 0 = kept, 1 = skipped, 2 = not visited
+ *   (every entry of a row is written).
+ *   Schedules: dense with max_seqlen_q * Hq / Hkv <= 64 query rows per KV head, split-K over the cache
+ *   with the rows in 16-row blocks (each block reads the cache once) and a merge kernel; otherwise (a
+ *   chunked prefill, or skip_threshold > 0, or a skip map) the prefill kernel with its K / V tiles
+ *   gathered page by page, no split, no workspace.  Supported: D = 128, page_size = 16,
+ *   B * max_seqlen_q * Hq < 2^31, a skip map below 2^32 bytes and, on the split-K schedule,
+ *   B * ceil(max_seqlen_q * Hq / Hkv / 16) <= 65535 (a grid dimension) (else ATTN_ERR_UNSUPPORTED).
+ *   B == 0 or total_q == 0 is a no-op.
  */
 size_t attn_decode_paged_multi_workspace_size(int32_t total_q, int32_t max_seqlen_q, int32_t Hq, int32_t Hkv,
                                               int32_t D, int32_t num_splits);
@@ -137,8 +142,9 @@ attn_status_t attn_decode_paged_multi(const void *q, const int32_t *cu_seqlens_q
                                       int32_t max_seqlen_q, const void *k_cache, const void *v_cache,
                                       const int32_t *block_table, const int32_t *seq_lens, int32_t B, int32_t Hq,
                                       int32_t Hkv, int32_t D, int32_t page_size, int32_t num_pages,
-                                      int32_t max_pages_per_seq, float scale, int32_t num_splits, void *workspace,
-                                      size_t workspace_bytes, void *o, float *lse, void *stream);
+                                      int32_t max_pages_per_seq, float scale, float skip_threshold,
+                                      int32_t num_splits, void *workspace, size_t workspace_bytes, void *o,
+                                      float *lse, uint8_t *skip_map, int32_t skip_map_stride, void *stream);
 
 /*
  * Small-seq cross-attention (s_q = 1): sequence b has one query token and

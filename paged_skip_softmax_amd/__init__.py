@@ -173,9 +173,11 @@ def attn_decode_paged_multi_workspace_size(total_q: int, max_seqlen_q: int, Hq: 
 
 
 def attn_decode_paged_multi(q, cu_seqlens_q, max_seqlen_q, k_cache, v_cache, block_table, seq_lens, *, scale=None,
-                            num_splits=0, workspace=None, out=None, return_lse=False):
+                            skip_threshold=0.0, num_splits=0, workspace=None, out=None, return_lse=False,
+                            return_skip_map=False):
     """Several new tokens per sequence over the paged cache (THD queries, bottom-right causal): split-K
-    decode for short query chunks, the paged prefill kernel for long ones.  Returns (o, lse or None)."""
+    decode for short dense query chunks, the paged prefill kernel for long ones and for skip-softmax.
+    Returns (o, lse or None, skip_map or None)."""
     lib = _lib.load()
     dev = q.device
     _cuda_contig("q", q, torch.bfloat16)
@@ -193,7 +195,8 @@ def attn_decode_paged_multi(q, cu_seqlens_q, max_seqlen_q, k_cache, v_cache, blo
           "cu_seqlens_q [B + 1], block_table [B, max_pages], seq_lens [B]")
     if scale is None:
         scale = 1.0 / math.sqrt(D)
-    need = attn_decode_paged_multi_workspace_size(total_q, int(max_seqlen_q), Hq, Hkv, D, num_splits)
+    skip = skip_threshold > 0 or return_skip_map
+    need = 0 if skip else attn_decode_paged_multi_workspace_size(total_q, int(max_seqlen_q), Hq, Hkv, D, num_splits)
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
@@ -201,12 +204,14 @@ def attn_decode_paged_multi(q, cu_seqlens_q, max_seqlen_q, k_cache, v_cache, blo
         out = torch.empty_like(q)
     _cuda_contig("out", out, torch.bfloat16, dev)
     lse = torch.empty((total_q, Hq), dtype=torch.float32, device=dev) if return_lse else None
+    stride = max(1, (block_table.shape[1] * page + SKIP_TILE - 1) // SKIP_TILE)
+    smap = torch.empty((total_q, Hq, stride), dtype=torch.uint8, device=dev) if return_skip_map else None
     _lib.check(lib.attn_decode_paged_multi(q.data_ptr(), cu_seqlens_q.data_ptr(), total_q, int(max_seqlen_q),
                                            k_cache.data_ptr(), v_cache.data_ptr(), block_table.data_ptr(),
                                            seq_lens.data_ptr(), B, Hq, Hkv, D, page, num_pages, block_table.shape[1],
-                                           float(scale), int(num_splits), _ptr(workspace), ws_bytes, out.data_ptr(),
-                                           _ptr(lse), _stream(q)))
-    return out, lse
+                                           float(scale), float(skip_threshold), int(num_splits), _ptr(workspace),
+                                           ws_bytes, out.data_ptr(), _ptr(lse), _ptr(smap), stride, _stream(q)))
+    return out, lse, smap
 
 
 def attn_smallseq_cross(q, k, v, cu_seqlens_kv, max_seqlen_kv, *, scale=None, return_weights=True,

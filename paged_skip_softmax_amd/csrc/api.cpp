@@ -243,11 +243,15 @@ attn_status_t attn_decode_paged_multi(const void *q, const int32_t *cu_seqlens_q
                                       int32_t max_seqlen_q, const void *k_cache, const void *v_cache,
                                       const int32_t *block_table, const int32_t *seq_lens, int32_t B, int32_t Hq,
                                       int32_t Hkv, int32_t D, int32_t page_size, int32_t num_pages,
-                                      int32_t max_pages_per_seq, float scale, int32_t num_splits, void *workspace,
-                                      size_t workspace_bytes, void *o, float *lse, void *stream)
+                                      int32_t max_pages_per_seq, float scale, float skip_threshold,
+                                      int32_t num_splits, void *workspace, size_t workspace_bytes, void *o,
+                                      float *lse, uint8_t *skip_map, int32_t skip_map_stride, void *stream)
 {
     if (B < 0 || total_q < 0 || max_seqlen_q < 0)
         return fail(ATTN_ERR_INVALID, "attn_decode_paged_multi: negative B, total_q or max_seqlen_q");
+    if (bad_threshold(skip_threshold))
+        return fail(ATTN_ERR_INVALID, "attn_decode_paged_multi: skip_threshold %g outside [0, 1]",
+                    (double)skip_threshold);
     if (Hq <= 0 || Hkv <= 0 || Hq % Hkv)
         return fail(ATTN_ERR_INVALID, "attn_decode_paged_multi: Hq = %d must be a positive multiple of Hkv = %d", Hq,
                     Hkv);
@@ -264,13 +268,21 @@ attn_status_t attn_decode_paged_multi(const void *q, const int32_t *cu_seqlens_q
         return fail(ATTN_ERR_UNSUPPORTED, "attn_decode_paged_multi: page_size = %d (built for 16)", page_size);
     if ((int64_t)B * max_seqlen_q * Hq >= ((int64_t)1 << 31))
         return fail(ATTN_ERR_UNSUPPORTED, "attn_decode_paged_multi: B * max_seqlen_q * Hq must stay below 2^31");
+    if (skip_map && (int64_t)skip_map_stride * attn::kSkipTile < (int64_t)max_pages_per_seq * page_size)
+        return fail(ATTN_ERR_INVALID,
+                    "attn_decode_paged_multi: skip_map_stride %d < ceil(max_pages_per_seq * page_size / 32)",
+                    skip_map_stride);
+    if (skip_map && (uint64_t)total_q * (uint64_t)Hq * (uint64_t)skip_map_stride >= ((uint64_t)1 << 32))
+        return fail(ATTN_ERR_UNSUPPORTED, "attn_decode_paged_multi: a skip map of total_q * Hq * stride bytes must "
+                                          "stay below 2^32");
     if (B == 0 || total_q == 0)
         return ok();
     if (!q || !cu_seqlens_q || !k_cache || !v_cache || !block_table || !seq_lens || !o)
         return fail(ATTN_ERR_INVALID, "attn_decode_paged_multi: a required pointer is NULL");
     const int G = Hq / Hkv;
-    if ((int64_t)max_seqlen_q * G > kMultiSplitRows) {
-        // long query chunks: the prefill kernel with K / V tiles gathered page by page
+    const bool skip = skip_threshold > 0.f || skip_map;
+    if (skip || (int64_t)max_seqlen_q * G > kMultiSplitRows) {
+        // long query chunks, or skip-softmax: the prefill kernel with K / V tiles gathered page by page
         attn::PrefillArgs a{};
         a.q = q;
         a.k = k_cache;
@@ -285,11 +297,11 @@ attn_status_t attn_decode_paged_multi(const void *q, const int32_t *cu_seqlens_q
         a.G = G;
         a.causal = true;
         a.scale_log2 = scale * 1.4426950408889634f;
-        a.log2_thr = -INFINITY;
+        a.log2_thr = log2_threshold(skip_threshold);
         a.o = o;
         a.lse = lse;
-        a.skip_map = nullptr;
-        a.map_stride = 0;
+        a.skip_map = skip_map;
+        a.map_stride = skip_map ? skip_map_stride : 0;
         a.bt = block_table;
         a.seq_lens = seq_lens;
         a.max_pages = max_pages_per_seq;

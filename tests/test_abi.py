@@ -173,11 +173,13 @@ def test_smallseq_backward_validation(lib):
 def test_decode_multi_validation(lib):
     def call(**kw):
         a = dict(q=FAKE, cq=FAKE, tq=10, mq=4, kc=FAKE, vc=FAKE, bt=FAKE, sl=FAKE, B=4, Hq=32, Hkv=8, D=128, page=16,
-                 pages=100, maxp=10, scale=0.1, splits=0, ws=FAKE, wsb=1 << 30, o=FAKE, lse=None, stream=None)
+                 pages=100, maxp=10, scale=0.1, thr=0.0, splits=0, ws=FAKE, wsb=1 << 30, o=FAKE, lse=None, map=None,
+                 stride=5, stream=None)
         a.update(kw)
         return lib.attn_decode_paged_multi(a["q"], a["cq"], a["tq"], a["mq"], a["kc"], a["vc"], a["bt"], a["sl"],
                                            a["B"], a["Hq"], a["Hkv"], a["D"], a["page"], a["pages"], a["maxp"],
-                                           a["scale"], a["splits"], a["ws"], a["wsb"], a["o"], a["lse"], a["stream"])
+                                           a["scale"], a["thr"], a["splits"], a["ws"], a["wsb"], a["o"], a["lse"],
+                                           a["map"], a["stride"], a["stream"])
     assert lib.attn_decode_paged_multi_workspace_size(10, 4, 32, 8, 128, 0) == 10 * 32 * 32 * 129 * 4
     assert lib.attn_decode_paged_multi_workspace_size(10, 4, 32, 8, 128, 7) == 10 * 32 * 7 * 129 * 4
     assert lib.attn_decode_paged_multi_workspace_size(10, 17, 32, 8, 128, 0) == 0  # the paged prefill path
@@ -191,6 +193,12 @@ def test_decode_multi_validation(lib):
     # 8 tokens x 4 heads = 2 blocks of 16 rows per sequence: B * 2 grid blocks in z
     assert call(B=32768, mq=8) == UNSUPPORTED
     assert call(B=32767, mq=8, wsb=100) == WORKSPACE  # within the grid; fails on the workspace next
+    for thr in (float("nan"), -0.5, 1.5):
+        assert call(thr=thr) == INVALID
+    assert call(map=FAKE, stride=4) == INVALID  # 10 pages of 16 keys need 5 tiles
+    assert call(map=FAKE, tq=1 << 17, B=4, mq=1 << 9, maxp=1 << 11, stride=1 << 10) == UNSUPPORTED  # 2^32 B map
+    # skip-softmax takes the paged prefill kernel: no workspace needed, and no split-K grid limit
+    assert call(thr=0.1, ws=None, wsb=0, B=0) == _lib.ATTN_OK
     assert call(cq=None) == INVALID
     assert call(wsb=100) == WORKSPACE
     assert call(B=0) == _lib.ATTN_OK
