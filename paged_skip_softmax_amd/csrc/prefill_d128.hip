@@ -27,7 +27,8 @@
 // wave fills 1 KB of LDS (4 key rows); rows past the sequence are outside the buffer resource and read
 // as zero.  Paged: the four loads of wave w for tile t are exactly the 16 keys of one cache page (the
 // block-table entry 4t + w), through a buffer resource built per page whose size ends at the sequence's
-// last key; the block-table entries are read before the barrier that precedes the loads.
+// last key; the block-table entries are read (scalar loads: the table is read through the constant
+// address space) before the barrier that precedes the loads.
 // LDS rows are not padded: the 16-byte chunks of a row are XOR-swizzled (slot = chunk ^ swz(row % 16)),
 // which keeps both the 16-B reads of K and the transposed 8-B reads of V (ds_read_b64_tr_b16) free of
 // bank conflicts.  Waits are explicit: vmcnt of the wave's own loads,
@@ -86,7 +87,8 @@ struct Loader {
     uint32_t tile_bytes;          // global bytes between consecutive 64-key tiles
     uint32_t m0k[kStages], m0v[kStages]; // LDS byte address of this wave's first 4-row block per stage
     // paged only
-    const int32_t *btr;           // the sequence's block-table row
+    const __attribute__((address_space(4))) int32_t *btr; // the sequence's block-table row (read-only:
+                                                          // scalar loads, outside the vector-memory count)
     const uint16_t *kc, *vc;      // the caches
     size_t head_off, page_elems;  // elements to the KV head's slab in a page; elements per page
     int Lk, w;                    // keys of the sequence; the (wave-uniform) wave index
@@ -435,7 +437,7 @@ void prefill_d128_kernel(PrefillArgs a, int NH, int RB, int nqt, int nunits)
             ld.vrs = make_rsrc(vg + head0, seq_bytes);
             ld.tile_bytes = kBN * row_bytes;
         } else {
-            ld.btr = a.bt + (size_t)b * a.max_pages;
+            ld.btr = (const __attribute__((address_space(4))) int32_t *)(a.bt + (size_t)b * a.max_pages);
             ld.kc = kg;
             ld.vc = vg;
             ld.head_off = (size_t)g * 16 * D;
