@@ -6,6 +6,8 @@ decode: a sample of batch rows, all heads) or every output where the fp64 work s
 for bf16 outputs, 1e-3 for LSE, >= 99.9 % skip-map agreement with exact visited sets, skip outputs
 compared against the oracle replaying the GPU's decisions.
 """
+import math
+
 import numpy as np
 import pytest
 import torch
@@ -182,7 +184,7 @@ def test_empty_batch_is_a_no_op():
 
 def test_prefill_one_long_sequence_sampled():
     # one causal sequence of 131,072 tokens (Hq 8, Hkv 1): 2,048 key tiles per row at the end, 4,096
-    # query tiles, K/V row offsets near the top of the supported range; sampled rows, all heads
+    # query tiles (the offsets at the 2^31-byte limit are the next test's); sampled rows, all heads
     L = 131072
     x = W.varlen_prefill(seed=1011, device=DEV, lengths=[L], Hq=8, Hkv=1)
     o, lse, _ = attn.attn_prefill_varlen(x.q, x.k, x.v, x.cu_q, x.cu_k, x.max_q, x.max_k, causal=True,
@@ -197,6 +199,31 @@ def test_prefill_one_long_sequence_sampled():
     r = np.array(rows)
     assert np.max(np.abs(_np(o)[r[:, 0], r[:, 1]] - od)) <= BF16_TOL
     assert np.max(np.abs(_np(lse)[r[:, 0], r[:, 1]] - ld)) <= LSE_TOL
+
+
+def test_prefill_kv_offsets_at_the_limit():
+    # one sequence whose K / V rows of a KV head span just under 2^31 bytes, the host's limit for
+    # max_seqlen_k * Hkv * D * 2: 1,048,000 keys with Hkv 8 (2.15 GB each for K and V), 64 queries,
+    # bottom-right causal and non-causal; the buffer sizes and tile offsets of the direct-to-LDS loads
+    # sit near the top of 32 bits.  Sampled rows (the oracle sums a million keys per row).
+    Lk, Lq, Hq, Hkv, D = 1_048_000, 64, 8, 8, 128
+    assert Lk * Hkv * D * 2 < 2 ** 31 <= (Lk + 1024) * Hkv * D * 2
+    g = torch.Generator(device=DEV).manual_seed(21)
+    q = torch.randn(Lq, Hq, D, generator=g, device=DEV).bfloat16()
+    k = torch.randn(Lk, Hkv, D, generator=g, device=DEV).bfloat16()
+    v = torch.randn(Lk, Hkv, D, generator=g, device=DEV).bfloat16()
+    cq = torch.tensor([0, Lq], dtype=torch.int32, device=DEV)
+    ck = torch.tensor([0, Lk], dtype=torch.int32, device=DEV)
+    kc, vc = k.cpu(), v.cpu()
+    rows = [(t, h) for t in (0, 31, 32, 63) for h in range(Hq)]
+    r = np.array(rows)
+    for causal in (True, False):
+        o, lse, _ = attn.attn_prefill_varlen(q, k, v, cq, ck, Lq, Lk, causal=causal, return_lse=True)
+        torch.cuda.synchronize()
+        od, ld, _ = oracle.prefill(q.cpu(), kc, vc, cq.cpu(), ck.cpu(), Hq, Hkv, 1 / math.sqrt(D), causal,
+                                   rows=rows)
+        assert np.max(np.abs(_np(o)[r[:, 0], r[:, 1]] - od)) <= BF16_TOL
+        assert np.max(np.abs(_np(lse)[r[:, 0], r[:, 1]] - ld)) <= LSE_TOL
 
 
 def test_prefill_many_short_sequences():
