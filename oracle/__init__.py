@@ -50,8 +50,13 @@ def _load():
         lib.orc_prefill_bwd.argtypes = [I, P, P, P, P, P, P, P, I, I, I, I, D, I, P, P, P]
         lib.orc_smallseq_bwd.argtypes = [I, P, P, P, P, P, P, I, I, I, I, D, P, P, P]
         lib.orc_paged_multi_rows.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, D, P, I, P, P]
+        F = ctypes.c_float
+        lib.orc_decode_qdq_rows.argtypes = [P, P, P, P, P, I, I, I, I, I, I, D, D, F, F, P, I, I, P, P, P]
+        lib.orc_fp_round.argtypes = [I, P, P, ctypes.c_size_t]
+        lib.orc_nvfp4_qdq.argtypes = [P, ctypes.c_size_t, I, F, P]
         for f in (lib.orc_prefill_rows, lib.orc_decode_rows, lib.orc_smallseq_rows, lib.orc_prefill_bwd,
-                  lib.orc_smallseq_bwd, lib.orc_paged_multi_rows):
+                  lib.orc_smallseq_bwd, lib.orc_paged_multi_rows, lib.orc_decode_qdq_rows, lib.orc_fp_round,
+                  lib.orc_nvfp4_qdq):
             f.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -162,6 +167,58 @@ def decode(q, k_cache, v_cache, block_table, seq_lens, scale, mode="dense", thr=
         if mp is not None:
             mp = mp.reshape(B, Hq, stride)
     return o, lse, mp
+
+
+def decode_qdq(q, k_cache, v_cache, block_table, seq_lens, scale, thr=0.0, p_amax=0.0, v_amax=0.0, rows=None):
+    """One-token paged decode in one sequential pass of 32-key tiles with skip threshold ``thr`` and NVFP4
+    fake quantization of P (``p_amax`` > 0) and V (``v_amax`` > 0).  Returns (o, lse, skip map)."""
+    qa, dt = _np(q)
+    ka, dk = _np(k_cache)
+    va, dv = _np(v_cache)
+    assert dt == dk == dv == 1, "paged decode is bf16"
+    bt, _ = _np(block_table)
+    sl, _ = _np(seq_lens)
+    B, Hq, D = qa.shape
+    Hkv, page = ka.shape[1], ka.shape[2]
+    max_pages = bt.shape[1]
+    allrows = [(b, h) for b in range(B) for h in range(Hq)] if rows is None else None
+    r = _rows_arg(rows, allrows)
+    n = len(r)
+    maxk = int(sl.max()) if B else 0
+    stride = max(1, (max(maxk, max_pages * page) + 31) // 32)
+    o = np.zeros((n, D))
+    lse = np.zeros(n)
+    mp = np.zeros((n, stride), dtype=np.uint8)
+    rc = _load().orc_decode_qdq_rows(_ptr(qa), _ptr(ka), _ptr(va), _ptr(bt), _ptr(sl), B, Hq, Hkv, D, page,
+                                     max_pages, float(scale), float(thr), float(p_amax), float(v_amax), _ptr(r), n,
+                                     stride, _ptr(o), _ptr(lse), _ptr(mp))
+    if rc != 0:
+        raise ValueError("oracle decode_qdq rejected its arguments")
+    if rows is None:
+        o = o.reshape(B, Hq, D)
+        lse = lse.reshape(B, Hq)
+        mp = mp.reshape(B, Hq, stride)
+    return o, lse, mp
+
+
+def fp_round(fmt, y):
+    """Nearest value of the E2M1 (``fmt="e2m1"``) or E4M3 (``"e4m3"``) grid to each y >= 0 (fp32), ties to
+    the even code, saturating at the top."""
+    ya = np.ascontiguousarray(np.asarray(y, dtype=np.float32))
+    out = np.empty_like(ya)
+    if _load().orc_fp_round({"e2m1": 0, "e4m3": 1}[fmt], _ptr(ya), _ptr(out), ya.size) != 0:
+        raise ValueError("fp_round: values must be >= 0")
+    return out
+
+
+def nvfp4_qdq(x, amax):
+    """NVFP4 fake quantization (fp32) of x along its last dimension, in blocks of 16, tensor amax ``amax``."""
+    xa = np.ascontiguousarray(np.asarray(x, dtype=np.float32))
+    out = np.empty_like(xa)
+    length = xa.shape[-1]
+    if _load().orc_nvfp4_qdq(_ptr(xa), xa.size // max(length, 1), length, float(amax), _ptr(out)) != 0:
+        raise ValueError("nvfp4_qdq rejected its arguments")
+    return out
 
 
 def smallseq(q, k, v, cu_kv, max_s, scale, rows=None):

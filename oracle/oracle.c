@@ -27,6 +27,10 @@
  *               [s c, (s+1) c) and is attended densely to (o_s, lse_s); then
  *               lse = log sum_{finite} exp(lse_s) and o = sum_s exp(lse_s - lse) o_s.
  *
+ * NVFP4 fake quantization of P and V under skip-softmax in the one-token decode (orc_decode_qdq_rows,
+ * with the quantizer itself exported as orc_nvfp4_qdq and orc_fp_round) follows the plain reading of the
+ * format stated at nvfp4_block; its rounding decisions are taken in fp32, the precision the format is
+ * defined in.
  * Plus multi-token paged decode (orc_paged_multi_rows), the backward of the dense prefill
  * (orc_prefill_bwd) and of the small-seq cross-attention from its stored attention weights
  * (orc_smallseq_bwd), at the end of this file.
@@ -64,6 +68,106 @@ static double dot(const double *a, const double *b, int D)
     return s;
 }
 
+/*
+ * NVFP4 fake quantization (quantize, then dequantize), "Model-Optimizer: Add split-k decode kernel for
+ * skip softmax", What does this PR do and Usage (P and V quantized to NVFP4 in the one-token decode,
+ * each with an amax).  The pages name the format but print no recipe; this is the format's published
+ * definition, read plainly:
+ *   - a tensor is cut into blocks of 16 consecutive values along its last dimension;
+ *   - each element is an E2M1 code: sign, 2 exponent bits (bias 1), 1 mantissa bit, subnormals,
+ *     magnitudes {0, 0.5, 1, 1.5, 2, 3, 4, 6};
+ *   - each block has one E4M3 scale code: 4 exponent bits (bias 7), 3 mantissa bits, subnormals,
+ *     largest finite 448 (the all-ones pattern is NaN);
+ *   - one fp32 scale per tensor, from amax, maps amax to the largest element times the largest scale,
+ *     6 * 448 = 2688.
+ * In fp32, each rounding to the nearest grid value, ties to the even code, saturating at the top:
+ *   enc = 448 / amax, dec = amax / 2688
+ *   scale code c_b = e4m3(max_i |x_i| * enc),  block scale s_b = c_b * dec
+ *   x^_i = sign(x_i) * e2m1(|x_i| * (1 / s_b)) * s_b,   and x^_i = 0 when s_b = 0.
+ * The grids are enumerated code by code, so that each rounding is a plain nearest-point search.
+ */
+enum { ORC_E2M1 = 0, ORC_E4M3 = 1 };
+
+/* Non-negative value of code c (ascending with c) of a minifloat with eb exponent bits (bias b) and mb
+ * mantissa bits, subnormals at exponent field 0. */
+static double minifloat_value(int c, int mb, int bias)
+{
+    int e = c >> mb, m = c & ((1 << mb) - 1);
+    double frac = (double)m / (double)(1 << mb);
+    return e == 0 ? ldexp(frac, 1 - bias) : ldexp(1.0 + frac, e - bias);
+}
+
+/* Nearest grid value to y >= 0 (ties to the even code, values above the top go to the top). */
+static float fp_round(int fmt, float y)
+{
+    int mb = fmt == ORC_E2M1 ? 1 : 3, bias = fmt == ORC_E2M1 ? 1 : 7;
+    int ncodes = fmt == ORC_E2M1 ? 8 : 127; /* E4M3 codes 0..126; 127 (exponent and mantissa all ones) is NaN */
+    if ((double)y >= minifloat_value(ncodes - 1, mb, bias)) /* saturate (far above the top the distances */
+        return (float)minifloat_value(ncodes - 1, mb, bias); /* to the top codes round to a false tie) */
+    int best = 0;
+    double bd = fabs((double)y);
+    for (int c = 1; c < ncodes; ++c) {
+        double d = fabs((double)y - minifloat_value(c, mb, bias));
+        if (d < bd || (d == bd && (c & 1) == 0)) {
+            bd = d;
+            best = c;
+        }
+    }
+    return (float)minifloat_value(best, mb, bias);
+}
+
+/* Quantize-dequantize n <= 16 values that form one block, in place. */
+static void nvfp4_block(float *x, int n, float amax)
+{
+    float enc = 448.0f / amax, dec = amax / 2688.0f;
+    float bmax = 0.0f;
+    for (int i = 0; i < n; ++i)
+        if (fabsf(x[i]) > bmax)
+            bmax = fabsf(x[i]);
+    float sb = fp_round(ORC_E4M3, bmax * enc) * dec;
+    float inv = sb > 0.0f ? 1.0f / sb : 0.0f;
+    for (int i = 0; i < n; ++i) {
+        float mag = fp_round(ORC_E2M1, fabsf(x[i]) * inv) * sb;
+        x[i] = x[i] < 0.0f ? -mag : mag;
+    }
+}
+
+/* Round to the nearest bf16 (ties to even): the dtype a bf16 tensor's fake quantization returns. */
+static float round_bf16(float f)
+{
+    uint32_t u;
+    memcpy(&u, &f, sizeof u);
+    u = (u + 0x7FFFu + ((u >> 16) & 1u)) & 0xFFFF0000u;
+    memcpy(&f, &u, sizeof f);
+    return f;
+}
+
+/* Exported for the tests: y[i] rounded to the grid of fmt (ORC_E2M1 or ORC_E4M3), y[i] >= 0. */
+int orc_fp_round(int fmt, const float *y, float *out, size_t n)
+{
+    if (fmt != ORC_E2M1 && fmt != ORC_E4M3)
+        return -1;
+    for (size_t i = 0; i < n; ++i) {
+        if (!(y[i] >= 0.0f))
+            return -1;
+        out[i] = fp_round(fmt, y[i]);
+    }
+    return 0;
+}
+
+/* Exported for the tests: NVFP4 fake quantization of rows x [rows, len] (blocks of 16 along each row,
+ * the last one ragged), in fp32, into out. */
+int orc_nvfp4_qdq(const float *x, size_t rows, int len, float amax, float *out)
+{
+    if (len <= 0 || !(amax > 0.0f) || isinf(amax))
+        return -1;
+    memcpy(out, x, sizeof(float) * rows * (size_t)len);
+    for (size_t r = 0; r < rows; ++r)
+        for (int b0 = 0; b0 < len; b0 += 16)
+            nvfp4_block(out + r * (size_t)len + b0, len - b0 < 16 ? len - b0 : 16, amax);
+    return 0;
+}
+
 /* The plain definition.  K, V: n rows of D.  p (nullable) receives the n probabilities. */
 static void dense_row(const double *q, const double *K, const double *V, int n, int D, double scale,
                       double *o, double *lse, double *p)
@@ -96,13 +200,17 @@ static void dense_row(const double *q, const double *K, const double *V, int n, 
 }
 
 /* Skip-softmax over `tile`-key tiles in ascending order.  map: one code per tile slot (width stride);
- * replay (nullable): decisions to impose, 1 = skip, 0 = process.  Returns 0, or -1 on a bad replay. */
+ * replay (nullable): decisions to impose, 1 = skip, 0 = process.  Returns 0, or -1 on a bad replay.
+ * p_amax > 0 fake-quantizes P to NVFP4 before P.V: the unnormalized probabilities exp(s_j - m) of a
+ * processed tile, m the running max including the tile (so that P lies in [0, 1]), are rounded to fp32
+ * and quantized in blocks of 16 consecutive keys counted from key 0 (tile must be a multiple of 16);
+ * the row sum l takes the unquantized values.  Returns -1 if tile is not a multiple of 16 then. */
 static int skip_row(const double *q, const double *K, const double *V, int n, int D, double scale,
-                    int tile, double thr, const uint8_t *replay, int stride, double *o, double *lse,
-                    uint8_t *map)
+                    int tile, double thr, const uint8_t *replay, int stride, float p_amax, double *o,
+                    double *lse, uint8_t *map)
 {
     int ntiles = (n + tile - 1) / tile;
-    if (ntiles > stride)
+    if (ntiles > stride || (p_amax > 0.0f && tile % 16))
         return -1;
     if (map)
         for (int t = 0; t < stride; ++t)
@@ -139,11 +247,22 @@ static int skip_row(const double *q, const double *K, const double *V, int n, in
         for (int d = 0; d < D; ++d)
             acc[d] *= alpha;
         for (int j = j0; j < j1; ++j) {
-            double e = exp(s[j - j0] - m_new);
-            l += e;
-            for (int d = 0; d < D; ++d)
-                acc[d] += e * V[(size_t)j * D + d];
+            s[j - j0] = exp(s[j - j0] - m_new); /* s now holds P of the tile */
+            l += s[j - j0];
         }
+        if (p_amax > 0.0f)
+            for (int b0 = j0; b0 < j1; b0 += 16) {
+                float blk[16];
+                int cnt = j1 - b0 < 16 ? j1 - b0 : 16;
+                for (int i = 0; i < cnt; ++i)
+                    blk[i] = (float)s[b0 - j0 + i];
+                nvfp4_block(blk, cnt, p_amax);
+                for (int i = 0; i < cnt; ++i)
+                    s[b0 - j0 + i] = blk[i];
+            }
+        for (int j = j0; j < j1; ++j)
+            for (int d = 0; d < D; ++d)
+                acc[d] += s[j - j0] * V[(size_t)j * D + d];
         m = m_new;
     }
     if (rc == 0) {
@@ -200,14 +319,16 @@ static void split_row(const double *q, const double *K, const double *V, int n, 
 
 static int run_mode(int mode, const double *q, const double *K, const double *V, int n, int D,
                     double scale, int tile, double thr, int splits, const uint8_t *replay, int stride,
-                    double *o, double *lse, uint8_t *map)
+                    float p_amax, double *o, double *lse, uint8_t *map)
 {
+    if (p_amax != 0.0f && mode != MODE_SKIP)
+        return -1;
     switch (mode) {
     case MODE_DENSE:
         dense_row(q, K, V, n, D, scale, o, lse, NULL);
         return 0;
     case MODE_SKIP:
-        return skip_row(q, K, V, n, D, scale, tile, thr, replay, stride, o, lse, map);
+        return skip_row(q, K, V, n, D, scale, tile, thr, replay, stride, p_amax, o, lse, map);
     case MODE_SPLIT:
         if (splits < 1)
             return -1;
@@ -267,7 +388,7 @@ int orc_prefill_rows(int dtype, const void *q, const void *k, const void *v, con
                 V[(size_t)j * D + d] = widen(v, dtype, src);
             }
         if (run_mode(mode, qd, K, V, n, D, scale, tile, thr, splits, replay ? replay + (size_t)r * stride : NULL,
-                     stride, o + (size_t)r * D, lse + r, map ? map + (size_t)r * stride : NULL))
+                     stride, 0.0f, o + (size_t)r * D, lse + r, map ? map + (size_t)r * stride : NULL))
             bad = 1;
         free(qd);
         free(K);
@@ -282,10 +403,11 @@ int orc_prefill_rows(int dtype, const void *q, const void *k, const void *v, con
  * sees all seq_lens[b] cached keys.  q [B, Hq, D] bf16; caches [num_pages, Hkv, page, D] bf16.
  * rows: n_rows pairs (b, head).  Outputs as for orc_prefill_rows.
  */
-int orc_decode_rows(const void *q, const void *kc, const void *vc, const int32_t *block_table,
-                    const int32_t *seq_lens, int B, int Hq, int Hkv, int D, int page, int max_pages,
-                    double scale, int mode, double thr, int tile, int splits, const int32_t *rows,
-                    int n_rows, const uint8_t *replay, int stride, double *o, double *lse, uint8_t *map)
+static int decode_rows(const void *q, const void *kc, const void *vc, const int32_t *block_table,
+                       const int32_t *seq_lens, int B, int Hq, int Hkv, int D, int page, int max_pages,
+                       double scale, int mode, double thr, int tile, int splits, const int32_t *rows,
+                       int n_rows, const uint8_t *replay, int stride, float p_amax, float v_amax, double *o,
+                       double *lse, uint8_t *map)
 {
     if (B < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv || D <= 0 || page <= 0 || (mode != MODE_DENSE && tile <= 0))
         return -1;
@@ -310,15 +432,55 @@ int orc_decode_rows(const void *q, const void *kc, const void *vc, const int32_t
                 K[(size_t)j * D + d] = widen(kc, ORC_BF16, src);
                 V[(size_t)j * D + d] = widen(vc, ORC_BF16, src);
             }
+            if (v_amax > 0.0f) /* V [n, D] in blocks of 16 along D, back to bf16 */
+                for (int d0 = 0; d0 < D; d0 += 16) {
+                    float blk[16];
+                    int cnt = D - d0 < 16 ? D - d0 : 16;
+                    for (int i = 0; i < cnt; ++i)
+                        blk[i] = (float)V[(size_t)j * D + d0 + i];
+                    nvfp4_block(blk, cnt, v_amax);
+                    for (int i = 0; i < cnt; ++i)
+                        V[(size_t)j * D + d0 + i] = round_bf16(blk[i]);
+                }
         }
         if (run_mode(mode, qd, K, V, n, D, scale, tile, thr, splits, replay ? replay + (size_t)r * stride : NULL,
-                     stride, o + (size_t)r * D, lse + r, map ? map + (size_t)r * stride : NULL))
+                     stride, p_amax, o + (size_t)r * D, lse + r, map ? map + (size_t)r * stride : NULL))
             bad = 1;
         free(qd);
         free(K);
         free(V);
     }
     return bad ? -1 : 0;
+}
+
+int orc_decode_rows(const void *q, const void *kc, const void *vc, const int32_t *block_table,
+                    const int32_t *seq_lens, int B, int Hq, int Hkv, int D, int page, int max_pages,
+                    double scale, int mode, double thr, int tile, int splits, const int32_t *rows,
+                    int n_rows, const uint8_t *replay, int stride, double *o, double *lse, uint8_t *map)
+{
+    return decode_rows(q, kc, vc, block_table, seq_lens, B, Hq, Hkv, D, page, max_pages, scale, mode, thr, tile,
+                       splits, rows, n_rows, replay, stride, 0.0f, 0.0f, o, lse, map);
+}
+
+/*
+ * One-token paged decode with NVFP4 fake quantization of P and V ("Model-Optimizer: Add split-k decode
+ * kernel for skip softmax", What does this PR do: skip-softmax together with NVFP4 P/V QDQ, in the one
+ * sequential split of 32-key tiles; Usage: p_qdq / v_qdq with their amax).  The sequential skip pass of
+ * skip_row with tile = 32 and threshold thr (thr = 0 skips nothing), where
+ *   - V, when v_amax > 0, is replaced by its fake quantization: every key's D values in blocks of 16,
+ *     the result rounded back to bf16, the cache's dtype;
+ *   - P, when p_amax > 0, is fake-quantized per tile as skip_row describes.
+ * amax = 0 leaves that side unquantized.  Arguments and outputs as for orc_decode_rows.
+ */
+int orc_decode_qdq_rows(const void *q, const void *kc, const void *vc, const int32_t *block_table,
+                        const int32_t *seq_lens, int B, int Hq, int Hkv, int D, int page, int max_pages,
+                        double scale, double thr, float p_amax, float v_amax, const int32_t *rows, int n_rows,
+                        int stride, double *o, double *lse, uint8_t *map)
+{
+    if (!(p_amax >= 0.0f) || !(v_amax >= 0.0f) || isinf(p_amax) || isinf(v_amax))
+        return -1;
+    return decode_rows(q, kc, vc, block_table, seq_lens, B, Hq, Hkv, D, page, max_pages, scale, MODE_SKIP, thr, 32,
+                       1, rows, n_rows, NULL, stride, p_amax, v_amax, o, lse, map);
 }
 
 /*

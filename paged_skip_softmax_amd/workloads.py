@@ -25,6 +25,8 @@ Workloads (sizes are the defaults; tests pass reduced sizes):
                         max(1, round(0.02 * L / 32)) distinct 32-aligned full 32-token runs gets
                         ``4 * sum_h q_h / |q_h|`` (sum over the query heads of the KV head's group) added to
                         every key of the run, before rounding to bf16.
+* ``paged_decode_exact`` ``paged_decode`` with integer Q (16 entries of +-1 per head row) and K (entries in
+                        {-1, 0, 1}), so that every score is an exact integer.
 * ``smallseq_cross``    B=30720 sequences with s_q=1 and s_kv drawn from {2,4,6,8,12,16}, H=16, D=128, bf16,
                         THD packed K/V with cu_seqlens_kv.
 """
@@ -36,7 +38,7 @@ from types import SimpleNamespace
 import torch
 
 # stream ids: one independent generator per purpose
-_S_LEN, _S_Q, _S_K, _S_V, _S_PERM, _S_HOT, _S_DO, _S_QLEN = range(8)
+_S_LEN, _S_Q, _S_K, _S_V, _S_PERM, _S_HOT, _S_DO, _S_QLEN, _S_EXACT = range(9)
 
 
 def _gen(seed: int, stream: int, device="cpu") -> torch.Generator:
@@ -216,6 +218,27 @@ def paged_decode(seed=1002, device="cpu", B=64, Hq=32, Hkv=8, D=128, lmin=1024, 
 def paged_decode_hot(seed=1002, device="cpu", **kw):
     """The hot-key decode workload; with the same seed its lengths, Q, V and table equal paged_decode's."""
     return paged_decode(seed=seed, device=device, hot=True, **kw)
+
+
+def paged_decode_exact(seed=1006, device="cpu", q_nnz=16, **kw):
+    """``paged_decode`` (built on the CPU, then moved) with small-integer Q and K: each query head row has
+    q_nnz entries +-1 at random positions and zeros elsewhere, every key entry is -1, 0 or +1 (the slots
+    past a sequence's end stay NaN).  Every score q.k is then an integer in [-q_nnz, q_nnz], which bf16
+    products and an fp32 sum give exactly; V is paged_decode's."""
+    x = paged_decode(seed=seed, device="cpu", **kw)
+    g = _gen(seed, _S_EXACT)
+    B, Hq, D = x.q.shape
+    pos = torch.rand((B, Hq, D), generator=g).argsort(-1)[..., :q_nnz]
+    sign = (torch.randint(0, 2, (B, Hq, q_nnz), generator=g) * 2 - 1).float()
+    q = torch.zeros(B, Hq, D).scatter_(-1, pos, sign)
+    kint = torch.randint(-1, 2, tuple(x.k_cache.shape), generator=g).to(torch.bfloat16)
+    kc = torch.where(torch.isnan(x.k_cache), x.k_cache, kint)
+    x.q = q.to(torch.bfloat16).to(device)
+    x.k_cache = kc.to(device)
+    x.v_cache = x.v_cache.to(device)
+    x.block_table = x.block_table.to(device)
+    x.seq_lens = x.seq_lens.to(device)
+    return x
 
 
 def paged_decode_multi(seed=1002, device="cpu", qmin=1, qmax=4, **kw):

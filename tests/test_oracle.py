@@ -608,3 +608,164 @@ def test_decode_multi_one_token_equals_decode():
     od, ld, _ = oracle.decode(x.q, x.k_cache, x.v_cache, x.block_table, x.seq_lens, x.scale)
     assert np.max(np.abs(om - od)) < 1e-12
     assert np.max(np.abs(lm - ld)) < 1e-12
+
+
+# ---------------------------------------------------------------- NVFP4 fake quantization of P and V
+
+E2M1 = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]  # the format's table of magnitudes
+
+
+def test_e2m1_grid_ties_and_saturation():
+    assert list(oracle.fp_round("e2m1", E2M1)) == E2M1
+    # midpoints go to the code with an even mantissa bit: 0, 1, 2 and 4 are even, 0.5, 1.5, 3 and 6 odd
+    mids = [0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0]
+    assert list(oracle.fp_round("e2m1", mids)) == [0.0, 1.0, 1.0, 2.0, 2.0, 4.0, 4.0]
+    assert list(oracle.fp_round("e2m1", [0.26, 0.74, 2.51, 4.99, 5.01])) == [0.5, 0.5, 3.0, 4.0, 6.0]
+    assert list(oracle.fp_round("e2m1", [6.0, 6.9, 7.0, 1e3, 3e38])) == [6.0] * 5
+
+
+def test_e4m3_matches_torch_float8_in_range():
+    # in [0, 448] the rounding is torch's float32 -> float8_e4m3fn conversion (round to nearest even)
+    g = torch.Generator().manual_seed(5)
+    y = torch.cat([torch.rand(20000, generator=g) * 448, torch.rand(20000, generator=g) * 2.0 ** -5,
+                   torch.rand(5000, generator=g) * 2.0 ** -8, torch.tensor([0.0, 2.0 ** -10, 3 * 2.0 ** -10,
+                                                                             2.0 ** -9, 2.0 ** -6, 448.0, 440.0])])
+    ref = y.to(torch.float8_e4m3fn).float().numpy()
+    assert np.array_equal(oracle.fp_round("e4m3", y.numpy()), ref)
+
+
+def test_e4m3_grid_and_saturation():
+    r = oracle.fp_round("e4m3", [448.0, 460.0, 464.0, 1e6, 2.0 ** -9, 2.0 ** -10, 1.5 * 2.0 ** -10, 248.0])
+    # 448 is the largest finite value; the saturating rounding keeps everything above it at 448; the
+    # smallest subnormal is 2^-9, its half-way point goes to 0 (even), 248 lies between 240 (odd mantissa)
+    # and 256 (even) and goes to 256
+    assert list(r) == [448.0, 448.0, 448.0, 448.0, 2.0 ** -9, 0.0, 2.0 ** -9, 256.0]
+    sweep = np.concatenate([np.linspace(0, 460, 400001, dtype=np.float32),
+                            np.linspace(0, 2.0 ** -5, 100001, dtype=np.float32)])
+    assert len(np.unique(oracle.fp_round("e4m3", sweep))) == 127  # 0 and the 126 positive finite codes
+
+
+def test_nvfp4_identity_on_the_grid_and_sign():
+    # amax = 6 * 448 gives enc = 1/6 and dec = 1: a block with max 6 gets scale code 1, and values on the
+    # E2M1 grid come back unchanged, with their signs
+    x = np.array([6.0, -3.0, 1.5, 0.5, 0.0, -6.0, 4.0, 2.0, 1.0, -0.5, 3.0, -1.5, 0.0, 4.0, -2.0, 1.0], np.float32)
+    assert np.array_equal(oracle.nvfp4_qdq(x, 2688.0), x)
+
+
+def test_nvfp4_hand_worked_block():
+    # amax 1: a block with max 1 gets scale code e4m3(448) = 448 and block scale 448 / 2688 = 1/6, so the
+    # values are 6x rounded to E2M1, divided by 6: 0.3 -> 1.8 -> 2, -0.05 -> -0.3 -> -0.5, 0.7 -> 4.2 -> 4,
+    # 0.9 -> 5.4 -> 6, 0.04 -> 0.24 -> 0
+    x = np.array([1.0, 0.3, -0.05, 0.7, 0.9, 0.04] + [0.0] * 10, np.float32)
+    want = np.array([1.0, 2 / 6, -0.5 / 6, 4 / 6, 1.0, 0.0] + [0.0] * 10)
+    assert np.max(np.abs(oracle.nvfp4_qdq(x, 1.0) - want)) < 1e-6
+
+
+def test_nvfp4_saturates_at_amax_and_zero_block():
+    # a block whose max exceeds amax gets the largest scale code, and its largest values come back as amax
+    x = np.array([5.0, -2.0, 0.5] + [0.0] * 13, np.float32)
+    out = oracle.nvfp4_qdq(x, 1.0)
+    assert abs(out[0] - 1.0) < 1e-6 and abs(out[1] + 1.0) < 1e-6
+    assert np.array_equal(oracle.nvfp4_qdq(np.zeros(16, np.float32), 1.0), np.zeros(16))
+
+
+def test_nvfp4_blocks_are_16_along_the_last_dim_and_scale_by_powers_of_two():
+    g = np.random.default_rng(7)
+    x = g.standard_normal((3, 40)).astype(np.float32)
+    out = oracle.nvfp4_qdq(x, 4.0)
+    # blocks [0,16), [16,32), [32,40) of each row are independent
+    for r in range(3):
+        for b0, b1 in ((0, 16), (16, 32), (32, 40)):
+            assert np.array_equal(out[r, b0:b1], oracle.nvfp4_qdq(x[r, b0:b1], 4.0))
+    # every value is sign * (E2M1 magnitude) * (its block's scale), and the block scale is
+    # e4m3(block max * 448 / amax) * amax / 2688: the error is at most half the widest step, 1 * scale
+    for r in range(3):
+        blk = x[r, :16]
+        s = oracle.fp_round("e4m3", [np.float32(np.abs(blk).max()) * np.float32(448 / 4.0)])[0] * (4.0 / 2688)
+        assert np.all(np.abs(blk - out[r, :16]) <= s * (1 + 1e-6))
+        codes = np.abs(out[r, :16]) / s
+        assert np.all(np.min(np.abs(codes[:, None] - np.array(E2M1)[None]), axis=1) < 1e-5)
+    # a power-of-two factor on both x and amax commutes with the quantizer
+    assert np.array_equal(oracle.nvfp4_qdq(x * 8, 32.0), out * 8)
+    assert np.array_equal(oracle.nvfp4_qdq(x / 4, 1.0), out / 4)
+
+
+def _exact_decode(seed, lengths, Hq=4, Hkv=2, D=32, q_nnz=8):
+    return W.paged_decode_exact(seed=seed, B=len(lengths), Hq=Hq, Hkv=Hkv, D=D, lengths=lengths,
+                                lmax=max(lengths), pool=sum((L + 15) // 16 for L in lengths) + 5, q_nnz=q_nnz)
+
+
+def test_decode_qdq_off_is_the_dense_decode():
+    x = W.paged_decode(seed=95, B=4, Hq=8, Hkv=2, D=32, lmin=1, lmax=150, pool=64)
+    o, lse, m = oracle.decode_qdq(x.q, x.k_cache, x.v_cache, x.block_table, x.seq_lens, x.scale)
+    od, ld, _ = oracle.decode(x.q, x.k_cache, x.v_cache, x.block_table, x.seq_lens, x.scale)
+    assert np.max(np.abs(o - od)) < 1e-12 and np.max(np.abs(lse - ld)) < 1e-12
+
+
+def test_decode_qdq_v_only_is_decode_of_the_quantized_cache():
+    # V fake-quantized per key in blocks of 16 along D and rounded back to bf16, then the plain decode
+    x = W.paged_decode(seed=96, B=3, Hq=4, Hkv=2, D=48, lmin=1, lmax=90, pool=40)
+    vq = torch.from_numpy(oracle.nvfp4_qdq(x.v_cache.float().numpy(), 1.5)).to(torch.bfloat16)
+    o, lse, _ = oracle.decode_qdq(x.q, x.k_cache, x.v_cache, x.block_table, x.seq_lens, x.scale, v_amax=1.5)
+    od, ld, _ = oracle.decode(x.q, x.k_cache, vq, x.block_table, x.seq_lens, x.scale)
+    assert np.max(np.abs(o - od)) < 1e-12 and np.max(np.abs(lse - ld)) < 1e-12
+
+
+def test_decode_qdq_p_brute_force_sequential_tiles():
+    # brute force of the sequential pass on tiny rows: per 32-key tile, P = exp(s - m) with m the running
+    # max including the tile, quantized in 16-key blocks, accumulated with the rescale exp(m_old - m);
+    # the denominator sums the unquantized P
+    lens = [1, 15, 16, 17, 32, 33, 70, 100]
+    x = W.paged_decode(seed=97, B=len(lens), Hq=4, Hkv=1, D=16, lengths=lens, lmax=100, pool=40)
+    scale = 0.9
+    o, lse, _ = oracle.decode_qdq(x.q, x.k_cache, x.v_cache, x.block_table, x.seq_lens, scale, p_amax=1.0)
+    q, kc, vc, bt = _f64(x.q), _f64(x.k_cache), _f64(x.v_cache), x.block_table.numpy()
+    for b, L in enumerate(lens):
+        keys = [bt[b, j // 16] for j in range(L)]
+        K = np.stack([kc[keys[j], 0, j % 16] for j in range(L)])
+        V = np.stack([vc[keys[j], 0, j % 16] for j in range(L)])
+        for h in range(4):
+            s = scale * (K @ q[b, h])
+            m, l, acc = -np.inf, 0.0, np.zeros(16)
+            for j0 in range(0, L, 32):
+                st = s[j0:j0 + 32]
+                mn = max(m, st.max())
+                p = np.exp(st - mn)
+                pq = np.concatenate([oracle.nvfp4_qdq(p[i:i + 16].astype(np.float32), 1.0).astype(np.float64)
+                                     for i in range(0, len(p), 16)])
+                a = 0.0 if m == -np.inf else math.exp(m - mn)
+                l = l * a + p.sum()
+                acc = acc * a + pq @ V[j0:j0 + 32]
+                m = mn
+            assert np.max(np.abs(o[b, h] - acc / l)) < 1e-12
+            assert abs(lse[b, h] - (m + math.log(l))) < 1e-12
+
+
+def test_decode_qdq_p_top_block_on_the_sixths_grid():
+    # one tile, one key block: the block holding the tile max has P max 1, scale code 448 and block scale
+    # 1/6, so the quantized P takes only values of the E2M1 grid / 6; with V = e_d the output row times l
+    # shows those values directly
+    lens = [16]
+    x = _exact_decode(98, lens, Hq=1, Hkv=1, D=16)
+    vc = torch.zeros_like(x.v_cache)
+    pg = int(x.block_table[0, 0])
+    vc[pg, 0, :16] = torch.eye(16, dtype=torch.bfloat16)
+    o, lse, _ = oracle.decode_qdq(x.q, x.k_cache, vc, x.block_table, x.seq_lens, math.log(2), p_amax=1.0)
+    # o = sum_j pq_j e_j / l with l = sum_j exp(s_j - max s) = exp(lse - max s)
+    l = math.exp(lse[0, 0] - np.max(math.log(2) * _f64(x.k_cache)[pg, 0, :16] @ _f64(x.q)[0, 0]))
+    vals = np.sort(o[0, 0] * l)
+    assert abs(vals[-1] - 1.0) < 1e-6
+    grid6 = np.array(E2M1) / 6
+    assert np.all(np.min(np.abs(vals[:, None] - grid6[None]), axis=1) < 1e-6)
+
+
+def test_decode_qdq_skip_decisions_unchanged_by_quantization():
+    # the decisions depend on the scores alone: the map with P and V quantized equals the unquantized one
+    x = _exact_decode(99, [40, 200, 333, 64], Hq=4, Hkv=2, D=32, q_nnz=8)
+    _, _, m0 = oracle.decode_qdq(x.q, x.k_cache, x.v_cache, x.block_table, x.seq_lens, math.log(2), thr=0.1)
+    _, _, m1 = oracle.decode_qdq(x.q, x.k_cache, x.v_cache, x.block_table, x.seq_lens, math.log(2), thr=0.1,
+                                 p_amax=1.0, v_amax=1.0)
+    assert np.array_equal(m0, m1) and (m0 == 1).any()
+    od, _, md = oracle.decode(x.q, x.k_cache, x.v_cache, x.block_table, x.seq_lens, math.log(2), mode="skip",
+                              thr=0.1, stride=m0.shape[-1])
+    assert np.array_equal(md, m0)
