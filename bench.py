@@ -6,7 +6,7 @@ One step = one pass of every hot-path kernel over its synthetic workload, inputs
   decode   paged one-token decode, split-K: B=64, Hq=32, Hkv=8, D=128, contexts uniform in [1024, 32768],
            16-token pages in a 140,000-page pool, 32 splits of 128-key tiles (+ the merge kernel)
   skip     the same decode shapes with hot keys, one sequential split of 32-key tiles, threshold
-           0, 0.01 and 0.1
+           0, 0.01 and 0.1; and at threshold 0 and 0.1 with NVFP4 fake quantization of P and V (amax 1)
   smallseq small-seq cross-attention: 30720 sequences, s_q=1, s_kv in {2,4,6,8,12,16}, H=16, D=128
 
 value = prefill TFLOP/s (algorithmic FLOPs 4 D Hq sum_b L_b (L_b + 1) / 2 over the kernel's event time);
@@ -197,6 +197,11 @@ def main():
         for thr in (0.0, 0.01, 0.1):
             calls[f"skip_{thr}"] = (lambda thr=thr: attn.attn_decode_paged(
                 s.q, s.k_cache, s.v_cache, s.block_table, s.seq_lens, num_splits=1, skip_threshold=thr, out=o_sk))
+        # NVFP4 fake quantization of P and V (amax 1 for both, as in the usage the pages print)
+        for thr in (0.0, 0.1):
+            calls[f"qdq_{thr}"] = (lambda thr=thr: attn.attn_decode_paged_qdq(
+                s.q, s.k_cache, s.v_cache, s.block_table, s.seq_lens, skip_threshold=thr, p_amax=1.0, v_amax=1.0,
+                out=o_sk))
     if "smallseq" in only:
         c = work["smallseq"]
         o_ss = torch.empty_like(c.q)
@@ -342,7 +347,17 @@ def main():
             res[thr]["speedup_vs_thr0"] = res["0.0"]["ms"] / res[thr]["ms"]
             if "decode" in out:
                 res[thr]["speedup_vs_splitk_dense"] = out["decode"]["ms"] / res[thr]["ms"]
+        for thr in ("0.0", "0.1"):
+            t = ms[f"qdq_{thr}"]
+            by = res[thr]["bytes_read_alg"]
+            res[thr]["nvfp4_qdq"] = {"ms": t, "ms_min": ms_min[f"qdq_{thr}"], "GBps_alg": by / (t * 1e-3) / 1e9,
+                                     "time_over_unquantized": t / res[thr]["ms"]}
         out["skip"] = res
+        gq = res["0.0"]["nvfp4_qdq"]["GBps_alg"]
+        rooflines.append({"kernel": "decode_seq_qdq_kernel(thr=0, P and V NVFP4)", "bound": "hbm", "achieved": gq,
+                          "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": gq / PEAK_HBM_GBPS,
+                          "traffic": _traffic_from_profiles("decode_seq_qdq_kernel"),
+                          "ms": res["0.0"]["nvfp4_qdq"]["ms"]})
         g0 = res["0.0"]["GBps_alg"]
         rooflines.append({"kernel": "decode_seq_kernel(thr=0)", "bound": "hbm", "achieved": g0,
                           "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": g0 / PEAK_HBM_GBPS,
@@ -631,6 +646,10 @@ PROFILED = {
     "decode_seq_kernel": ("sequential skip decode on hot keys, B=64, L~U[1024,32768], 32-key tiles, "
                           "threshold 0 / 0.01 / 0.1", "decode_seq_kernel.paged_decode_hot_B64_thr0-0.01-0.1",
                           ["paged_skip_softmax_amd/csrc/decode.hip"] + _KSRC, "skip_0.0"),
+    "decode_seq_qdq_kernel": ("sequential decode with NVFP4 fake quantization of P and V (amax 1) on hot keys, "
+                              "B=64, L~U[1024,32768], 32-key tiles, threshold 0 / 0.1",
+                              "decode_seq_qdq_kernel.paged_decode_hot_B64_nvfp4_pv_thr0-0.1",
+                              ["paged_skip_softmax_amd/csrc/decode.hip"] + _KSRC, "qdq_0.0"),
     "smallseq_kernel": ("small-seq cross-attention B=30720, s_kv in {2,4,6,8,12,16}, H=16, D=128",
                         "smallseq_kernel.smallseq_cross_B30720_H16_D128",
                         ["paged_skip_softmax_amd/csrc/smallseq.hip"] + _KSRC, "smallseq"),
@@ -658,6 +677,8 @@ def call_kernels(call):
         return ["decode_split_kernel", "decode_merge_kernel"]
     if call.startswith(("skip_", "map_skip_")):
         return ["decode_seq_kernel"]
+    if call.startswith("qdq_"):
+        return ["decode_seq_qdq_kernel"]
     if call in ("smallseq", "setup_smallseq_fwd"):
         return ["smallseq_kernel"]
     if call == "smallseq_bwd":

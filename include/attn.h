@@ -112,6 +112,33 @@ attn_status_t attn_decode_paged(const void *q, const void *k_cache, const void *
                                 float *lse, uint8_t *skip_map, int32_t skip_map_stride, void *stream);
 
 /*
+ * One-token paged decode with NVFP4 fake quantization of P and V ("Model-Optimizer: Add split-k decode
+ * kernel for skip softmax", What does this PR do: skip-softmax together with NVFP4 P/V quantize-dequantize
+ * in the sequential schedule; Usage: p_qdq / v_qdq with p_qdq_amax / v_qdq_amax).  The sequential
+ * schedule of attn_decode_paged (num_splits = 1, 32-key tiles, skip_threshold in [0, 1], 0 = dense) with:
+ *   - V (v_amax > 0): every key's D values fake-quantized in blocks of 16 consecutive values along D and
+ *     rounded back to bf16 before the P.V product;
+ *   - P (p_amax > 0): the unnormalized probabilities exp(s - m) of a kept tile, m the sequential pass's
+ *     running max including the tile (P in [0, 1]), fake-quantized in blocks of the 16 keys of a page
+ *     (keys 16 i .. 16 i + 15 of the sequence) before P.V; the softmax denominator sums the unquantized P.
+ * NVFP4 (the pages give no recipe; this is the format read plainly): E2M1 elements {0, 0.5, 1, 1.5, 2, 3,
+ * 4, 6}, one E4M3 scale code per block (largest 448), per-tensor factors enc = 448 / amax and
+ * dec = amax / 2688, all in fp32: block scale s = e4m3(max |x| * enc) * dec, x^ = sign(x) *
+ * e2m1(|x| * (1 / s)) * s (0 when s = 0), each rounding to nearest even, saturating.  Values above amax
+ * saturate at about amax.
+ *   amax: 0 turns that side off; otherwise in [1e-20, 1e20] (else ATTN_ERR_INVALID).  With both 0 the
+ *   result is attn_decode_paged's with num_splits = 1, from the same schedule.
+ *   Every other argument, layout, ownership and error as for attn_decode_paged with num_splits = 1 (no
+ *   workspace).  Stream-ordered, asynchronous.
+ */
+attn_status_t attn_decode_paged_qdq(const void *q, const void *k_cache, const void *v_cache,
+                                    const int32_t *block_table, const int32_t *seq_lens, int32_t B, int32_t Hq,
+                                    int32_t Hkv, int32_t D, int32_t page_size, int32_t num_pages,
+                                    int32_t max_pages_per_seq, float scale, float skip_threshold, float p_amax,
+                                    float v_amax, void *o, float *lse, uint8_t *skip_map, int32_t skip_map_stride,
+                                    void *stream);
+
+/*
  * Multi-token paged decode (several new tokens per sequence over the paged cache; "Model-Optimizer: Add
  * split-k decode kernel for skip softmax", description: multi-token decode stays on the shared
  * attention kernel, whose summary gives causal masking over variable-length batches).  Sequence b has

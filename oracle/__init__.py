@@ -51,7 +51,7 @@ def _load():
         lib.orc_smallseq_bwd.argtypes = [I, P, P, P, P, P, P, I, I, I, I, D, P, P, P]
         lib.orc_paged_multi_rows.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, D, P, I, P, P]
         F = ctypes.c_float
-        lib.orc_decode_qdq_rows.argtypes = [P, P, P, P, P, I, I, I, I, I, I, D, D, F, F, P, I, I, P, P, P]
+        lib.orc_decode_qdq_rows.argtypes = [P, P, P, P, P, I, I, I, I, I, I, D, D, F, F, P, I, P, I, P, P, P]
         lib.orc_fp_round.argtypes = [I, P, P, ctypes.c_size_t]
         lib.orc_nvfp4_qdq.argtypes = [P, ctypes.c_size_t, I, F, P]
         for f in (lib.orc_prefill_rows, lib.orc_decode_rows, lib.orc_smallseq_rows, lib.orc_prefill_bwd,
@@ -169,9 +169,11 @@ def decode(q, k_cache, v_cache, block_table, seq_lens, scale, mode="dense", thr=
     return o, lse, mp
 
 
-def decode_qdq(q, k_cache, v_cache, block_table, seq_lens, scale, thr=0.0, p_amax=0.0, v_amax=0.0, rows=None):
-    """One-token paged decode in one sequential pass of 32-key tiles with skip threshold ``thr`` and NVFP4
-    fake quantization of P (``p_amax`` > 0) and V (``v_amax`` > 0).  Returns (o, lse, skip map)."""
+def decode_qdq(q, k_cache, v_cache, block_table, seq_lens, scale, thr=0.0, p_amax=0.0, v_amax=0.0, rows=None,
+               replay=None):
+    """One-token paged decode in one sequential pass of 32-key tiles with skip threshold ``thr`` (or the
+    decisions of ``replay`` [rows, stride], 1 = skip) and NVFP4 fake quantization of P (``p_amax`` > 0) and
+    V (``v_amax`` > 0).  Returns (o, lse, skip map)."""
     qa, dt = _np(q)
     ka, dk = _np(k_cache)
     va, dv = _np(v_cache)
@@ -186,12 +188,16 @@ def decode_qdq(q, k_cache, v_cache, block_table, seq_lens, scale, thr=0.0, p_ama
     n = len(r)
     maxk = int(sl.max()) if B else 0
     stride = max(1, (max(maxk, max_pages * page) + 31) // 32)
+    rp = None
+    if replay is not None:
+        rp = np.ascontiguousarray(np.asarray(replay, dtype=np.uint8).reshape(n, -1))
+        stride = rp.shape[1]
     o = np.zeros((n, D))
     lse = np.zeros(n)
     mp = np.zeros((n, stride), dtype=np.uint8)
     rc = _load().orc_decode_qdq_rows(_ptr(qa), _ptr(ka), _ptr(va), _ptr(bt), _ptr(sl), B, Hq, Hkv, D, page,
                                      max_pages, float(scale), float(thr), float(p_amax), float(v_amax), _ptr(r), n,
-                                     stride, _ptr(o), _ptr(lse), _ptr(mp))
+                                     _ptr(rp), stride, _ptr(o), _ptr(lse), _ptr(mp))
     if rc != 0:
         raise ValueError("oracle decode_qdq rejected its arguments")
     if rows is None:

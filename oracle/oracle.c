@@ -470,17 +470,18 @@ int orc_decode_rows(const void *q, const void *kc, const void *vc, const int32_t
  *   - V, when v_amax > 0, is replaced by its fake quantization: every key's D values in blocks of 16,
  *     the result rounded back to bf16, the cache's dtype;
  *   - P, when p_amax > 0, is fake-quantized per tile as skip_row describes.
- * amax = 0 leaves that side unquantized.  Arguments and outputs as for orc_decode_rows.
+ * amax = 0 leaves that side unquantized.  replay (nullable, [n_rows, stride]) imposes the skip decisions
+ * as in skip_row.  Arguments and outputs as for orc_decode_rows.
  */
 int orc_decode_qdq_rows(const void *q, const void *kc, const void *vc, const int32_t *block_table,
                         const int32_t *seq_lens, int B, int Hq, int Hkv, int D, int page, int max_pages,
                         double scale, double thr, float p_amax, float v_amax, const int32_t *rows, int n_rows,
-                        int stride, double *o, double *lse, uint8_t *map)
+                        const uint8_t *replay, int stride, double *o, double *lse, uint8_t *map)
 {
     if (!(p_amax >= 0.0f) || !(v_amax >= 0.0f) || isinf(p_amax) || isinf(v_amax))
         return -1;
     return decode_rows(q, kc, vc, block_table, seq_lens, B, Hq, Hkv, D, page, max_pages, scale, MODE_SKIP, thr, 32,
-                       1, rows, n_rows, NULL, stride, p_amax, v_amax, o, lse, map);
+                       1, rows, n_rows, replay, stride, p_amax, v_amax, o, lse, map);
 }
 
 /*

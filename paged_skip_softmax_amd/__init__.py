@@ -18,7 +18,7 @@ from . import _lib
 from ._lib import SKIP_TILE, AttnError  # noqa: F401
 
 __all__ = ["attn_prefill_varlen", "attn_prefill_varlen_backward", "attn_prefill_varlen_backward_workspace_size",
-           "attn_decode_paged", "attn_decode_paged_workspace_size", "attn_decode_paged_multi",
+           "attn_decode_paged", "attn_decode_paged_workspace_size", "attn_decode_paged_qdq", "attn_decode_paged_multi",
            "attn_decode_paged_multi_workspace_size", "attn_smallseq_cross",
            "attn_smallseq_cross_backward", "AttnError", "SKIP_TILE"]
 
@@ -163,6 +163,40 @@ def attn_decode_paged(q, k_cache, v_cache, block_table, seq_lens, *, scale=None,
                                      seq_lens.data_ptr(), B, Hq, Hkv, D, page, num_pages, max_pages, float(scale),
                                      float(skip_threshold), int(splits), _ptr(workspace), ws_bytes, out.data_ptr(),
                                      _ptr(lse), _ptr(smap), stride, _stream(q)))
+    return out, lse, smap
+
+
+def attn_decode_paged_qdq(q, k_cache, v_cache, block_table, seq_lens, *, scale=None, skip_threshold=0.0,
+                          p_amax=0.0, v_amax=0.0, out=None, return_lse=False, return_skip_map=False):
+    """One-token paged decode, sequential schedule, with NVFP4 fake quantization of P (``p_amax`` > 0) and
+    V (``v_amax`` > 0).  Returns (o, lse or None, skip_map or None)."""
+    lib = _lib.load()
+    dev = q.device
+    _cuda_contig("q", q, torch.bfloat16)
+    for name, t in (("k_cache", k_cache), ("v_cache", v_cache)):
+        _cuda_contig(name, t, torch.bfloat16, dev)
+    _cuda_contig("block_table", block_table, torch.int32, dev)
+    _cuda_contig("seq_lens", seq_lens, torch.int32, dev)
+    _need(q.dim() == 3 and k_cache.dim() == 4 and k_cache.shape == v_cache.shape,
+          "q [B,Hq,D], caches [pages,Hkv,page,D]")
+    B, Hq, D = q.shape
+    num_pages, Hkv, page, Dk = k_cache.shape
+    _need(Dk == D, "head dims differ")
+    _need(block_table.dim() == 2 and block_table.shape[0] == B and seq_lens.shape == (B,),
+          "block_table [B, max_pages], seq_lens [B]")
+    max_pages = block_table.shape[1]
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty_like(q)
+    _cuda_contig("out", out, torch.bfloat16, dev)
+    lse = torch.empty((B, Hq), dtype=torch.float32, device=dev) if return_lse else None
+    stride = max(1, (max_pages * page + SKIP_TILE - 1) // SKIP_TILE)
+    smap = torch.empty((B, Hq, stride), dtype=torch.uint8, device=dev) if return_skip_map else None
+    _lib.check(lib.attn_decode_paged_qdq(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+                                         block_table.data_ptr(), seq_lens.data_ptr(), B, Hq, Hkv, D, page, num_pages,
+                                         max_pages, float(scale), float(skip_threshold), float(p_amax),
+                                         float(v_amax), out.data_ptr(), _ptr(lse), _ptr(smap), stride, _stream(q)))
     return out, lse, smap
 
 

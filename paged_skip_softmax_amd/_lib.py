@@ -19,6 +19,8 @@ SIGNATURES = {
     "attn_decode_paged_workspace_size": (_Z, [_I, _I, _I, _I]),
     "attn_decode_paged": (ctypes.c_int, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _F, _I, _P, _Z, _P, _P,
                                          _P, _I, _P]),
+    "attn_decode_paged_qdq": (ctypes.c_int, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _F, _F, _F, _P,
+                                             _P, _P, _I, _P]),
     "attn_decode_paged_multi_workspace_size": (_Z, [_I, _I, _I, _I, _I, _I]),
     "attn_decode_paged_multi": (ctypes.c_int, [_P, _P, _I, _I, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _F,
                                                _I, _P, _Z, _P, _P, _P, _I, _P]),

@@ -49,6 +49,9 @@ float log2_threshold(float thr) { return thr > 0.f ? std::log2(thr) : -INFINITY;
 constexpr int kDefaultSplits = 32;
 constexpr int kMaxSplits = 64;
 constexpr int64_t kMaxGridYZ = 65535; // largest y or z grid dimension a launch here may use
+// NVFP4 amax range: keeps 448 / amax, amax / 2688 and every block scale and its reciprocal normal fp32
+constexpr float kMinQdqAmax = 1e-20f;
+constexpr float kMaxQdqAmax = 1e20f;
 
 int resolve_splits(int num_splits, float thr) { return num_splits != 0 ? num_splits : (thr == 0.f ? kDefaultSplits : 1); }
 
@@ -156,6 +159,76 @@ attn_status_t attn_decode_paged(const void *q, const void *k_cache, const void *
     a.skip_map = skip_map;
     a.map_stride = skip_map_stride;
     return hip_status(attn::launch_decode_seq(a, B, st), "decode sequential launch");
+}
+
+attn_status_t attn_decode_paged_qdq(const void *q, const void *k_cache, const void *v_cache,
+                                    const int32_t *block_table, const int32_t *seq_lens, int32_t B, int32_t Hq,
+                                    int32_t Hkv, int32_t D, int32_t page_size, int32_t num_pages,
+                                    int32_t max_pages_per_seq, float scale, float skip_threshold, float p_amax,
+                                    float v_amax, void *o, float *lse, uint8_t *skip_map, int32_t skip_map_stride,
+                                    void *stream)
+{
+    if (B < 0)
+        return fail(ATTN_ERR_INVALID, "attn_decode_paged_qdq: B = %d < 0", B);
+    if (Hq <= 0 || Hkv <= 0 || Hq % Hkv)
+        return fail(ATTN_ERR_INVALID, "attn_decode_paged_qdq: Hq = %d must be a positive multiple of Hkv = %d", Hq,
+                    Hkv);
+    if (bad_threshold(skip_threshold))
+        return fail(ATTN_ERR_INVALID, "attn_decode_paged_qdq: skip_threshold %g outside [0, 1]",
+                    (double)skip_threshold);
+    if (!std::isfinite(scale))
+        return fail(ATTN_ERR_INVALID, "attn_decode_paged_qdq: scale is not finite");
+    for (float amax : {p_amax, v_amax})
+        if (!(amax == 0.f || (amax >= kMinQdqAmax && amax <= kMaxQdqAmax)))
+            return fail(ATTN_ERR_INVALID, "attn_decode_paged_qdq: amax %g is neither 0 (off) nor in [%g, %g]",
+                        (double)amax, (double)kMinQdqAmax, (double)kMaxQdqAmax);
+    if (num_pages <= 0 || max_pages_per_seq <= 0 || page_size <= 0)
+        return fail(ATTN_ERR_INVALID,
+                    "attn_decode_paged_qdq: num_pages, max_pages_per_seq and page_size must be > 0");
+    if (skip_map && (int64_t)skip_map_stride * attn::kSkipTile < (int64_t)max_pages_per_seq * page_size)
+        return fail(ATTN_ERR_INVALID,
+                    "attn_decode_paged_qdq: skip_map_stride %d < ceil(max_pages_per_seq * page_size / 32)",
+                    skip_map_stride);
+    if (D != 128)
+        return fail(ATTN_ERR_UNSUPPORTED, "attn_decode_paged_qdq: D = %d (built for 128)", D);
+    if (page_size != 16)
+        return fail(ATTN_ERR_UNSUPPORTED, "attn_decode_paged_qdq: page_size = %d (built for 16)", page_size);
+    if (Hq / Hkv > 16)
+        return fail(ATTN_ERR_UNSUPPORTED, "attn_decode_paged_qdq: Hq / Hkv = %d > 16", Hq / Hkv);
+    if (B > kMaxGridYZ)
+        return fail(ATTN_ERR_UNSUPPORTED, "attn_decode_paged_qdq: B = %d above %d (a grid dimension)", B,
+                    (int)kMaxGridYZ);
+    if (B == 0)
+        return ok();
+    if (!q || !k_cache || !v_cache || !block_table || !seq_lens || !o)
+        return fail(ATTN_ERR_INVALID, "attn_decode_paged_qdq: a required pointer is NULL");
+    attn::SeqArgs a{};
+    a.q = static_cast<const uint16_t *>(q);
+    a.kc = static_cast<const uint16_t *>(k_cache);
+    a.vc = static_cast<const uint16_t *>(v_cache);
+    a.bt = block_table;
+    a.seq_lens = seq_lens;
+    a.Hq = Hq;
+    a.Hkv = Hkv;
+    a.G = Hq / Hkv;
+    a.max_pages = max_pages_per_seq;
+    a.scale_log2 = scale * 1.4426950408889634f;
+    a.log2_thr = log2_threshold(skip_threshold);
+    a.o = static_cast<uint16_t *>(o);
+    a.lse = lse;
+    a.skip_map = skip_map;
+    a.map_stride = skip_map_stride;
+    a.p_qdq = p_amax > 0.f;
+    a.v_qdq = v_amax > 0.f;
+    if (a.p_qdq) {
+        a.p_enc = 448.f / p_amax;
+        a.p_dec = p_amax / 2688.f;
+    }
+    if (a.v_qdq) {
+        a.v_enc = 448.f / v_amax;
+        a.v_dec = v_amax / 2688.f;
+    }
+    return hip_status(attn::launch_decode_seq(a, B, static_cast<hipStream_t>(stream)), "decode QDQ launch");
 }
 
 size_t attn_prefill_varlen_backward_workspace_size(int32_t B, int32_t max_seqlen_q, int32_t Hq)

@@ -138,12 +138,91 @@ __device__ __forceinline__ uint2 lds_read_tr(const uint16_t *p)
     return __builtin_bit_cast(uint2, r);
 }
 
+// NVFP4 fake quantization ("Model-Optimizer: Add split-k decode kernel for skip softmax", What does this
+// PR do and Usage: P and V quantized to NVFP4 and back in the sequential decode, each with an amax).
+// A block of 16 values shares one E4M3 scale code; the elements are E2M1; enc = 448 / amax and
+// dec = amax / 2688 (6 * 448) are the per-tensor fp32 factors.  For a block with max |x| = b:
+//   s = e4m3(b * enc) * dec,   x^ = sign(x) * e2m1(|x| * (1 / s)) * s   (x^ = 0 when s = 0),
+// every rounding to nearest even with saturation, in fp32.
+struct Nvfp4 {
+    float enc, dec;
+};
+struct Qdq {
+    Nvfp4 p, v;
+    bool p_on, v_on;
+};
+
+// E4M3 rounding of y >= 0 (3 mantissa bits, subnormals below 2^-6, nearest even, saturating at 448):
+// gfx950's conversion to fp8 and back, after clamping to 448.
+__device__ __forceinline__ float round_e4m3(float y)
+{
+    const int p = __builtin_amdgcn_cvt_pk_fp8_f32(fminf(y, 448.f), 0.f, 0, false);
+    return __builtin_amdgcn_cvt_f32_fp8(p, 0);
+}
+
+// E2M1 rounding of two fp32 values onto +-{0, 0.5, 1, 1.5, 2, 3, 4, 6} (nearest even, saturating at
+// +-6): gfx950's conversion to packed fp4 and back, both at scale 1.
+__device__ __forceinline__ f32x2 round_e2m1_pair(float a, float b)
+{
+    const uint32_t p = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, a, b, 1.f, 0);
+    return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(p, 1.f, 0);
+}
+
+struct BlockScale {
+    float s, r; // block scale and its reciprocal (0 for an all-zero block)
+};
+
+__device__ __forceinline__ BlockScale nvfp4_block_scale(float bmax, Nvfp4 f)
+{
+    const float s = round_e4m3(bmax * f.enc) * f.dec;
+    return {s, s > 0.f ? 1.f / s : 0.f};
+}
+
+// Two values of one block; sign(x) e2m1(|x| r) = e2m1(x r), the grid being symmetric.
+__device__ __forceinline__ f32x2 nvfp4_qdq2(float x0, float x1, BlockScale b)
+{
+    const f32x2 q = round_e2m1_pair(x0 * b.r, x1 * b.r);
+    return f32x2{q.x * b.s, q.y * b.s};
+}
+
+// Max of v over the lane pair (2i, 2i + 1) (DPP quad_perm [1, 0, 3, 2]).
+__device__ __forceinline__ float max_lane_pair(float v)
+{
+    const int o = __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false);
+    return fmaxf(v, __builtin_bit_cast(float, o));
+}
+
+// V of one key row slice (8 bf16, d = 8 (lane % 16) .. +8) fake-quantized in blocks of 16 along D: the
+// block is the lane pair (2i, 2i + 1) of the 16-lane group, which holds one key.  Back to bf16.
+__device__ __forceinline__ uint4 qdq_v8(uint4 v, Nvfp4 f)
+{
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    float x[8], bmax = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        x[2 * i] = __builtin_bit_cast(float, w[i] << 16);
+        x[2 * i + 1] = __builtin_bit_cast(float, w[i] & 0xFFFF0000u);
+        bmax = fmaxf(bmax, fmaxf(fabsf(x[2 * i]), fabsf(x[2 * i + 1])));
+    }
+    const BlockScale b = nvfp4_block_scale(max_lane_pair(bmax), f);
+    uint32_t o[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const f32x2 y = nvfp4_qdq2(x[2 * i], x[2 * i + 1], b);
+        o[i] = pack_bf16x2(y.x, y.y);
+    }
+    return make_uint4(o[0], o[1], o[2], o[3]);
+}
+
 // Folds one chunk into the state.  keep == false (per lane, i.e. per head) leaves that head's state
 // untouched: p = 0 and no rescale.  cmax_l2: chunk max in log2 units.  Keys at or past tend have their
 // V zeroed in LDS so that 0 * NaN never reaches the accumulator.  vt: this wave's LDS tile.
+// QDQ: fake-quantize P (blocks of the 16 keys of a page, per head; the row sum takes the unquantized P)
+// and V (per key, blocks of 16 along D) as qq says.
+template <bool QDQ = false>
 __device__ __forceinline__ void chunk_update(WaveState &st, const f32x4 sc[2], float cmax_l2, bool keep,
                                              const uint4 vr[2][4], int tok0, int tend, float scale_log2,
-                                             uint16_t *vt, int lane)
+                                             uint16_t *vt, int lane, const Qdq &qq = Qdq{})
 {
     const int n = lane & 15, j = lane >> 4;
     const float m_new = keep ? fmaxf(st.m, cmax_l2) : st.m;
@@ -159,6 +238,18 @@ __device__ __forceinline__ void chunk_update(WaveState &st, const f32x4 sc[2], f
         }
     st.l = fmaf(st.l, alpha, psum);
     st.m = m_new;
+    if (QDQ && qq.p_on)
+#pragma unroll
+        for (int pg = 0; pg < 2; ++pg) {
+            const float bm = fmaxf(fmaxf(p[pg][0], p[pg][1]), fmaxf(p[pg][2], p[pg][3]));
+            const BlockScale b = nvfp4_block_scale(max_across_groups16(bm), qq.p);
+#pragma unroll
+            for (int i = 0; i < 4; i += 2) {
+                const f32x2 y = nvfp4_qdq2(p[pg][i], p[pg][i + 1], b);
+                p[pg][i] = y.x;
+                p[pg][i + 1] = y.y;
+            }
+        }
 #pragma unroll
     for (int db = 0; db < kD / 16; ++db)
         st.acc[db] *= alpha;
@@ -170,6 +261,8 @@ __device__ __forceinline__ void chunk_update(WaveState &st, const f32x4 sc[2], f
         for (int r = 0; r < 4; ++r) {
             const int key = (lane >> 4) + 4 * r;
             uint4 v = vr[pg][r];
+            if (QDQ && qq.v_on)
+                v = qdq_v8(v, qq.v);
             if (partial && tok0 + kPage * pg + key >= tend)
                 v = make_uint4(0, 0, 0, 0);
             st16(vt + (pg * kPage + key) * kVPitch + 8 * (lane & 15), v);
@@ -542,7 +635,11 @@ __device__ __forceinline__ int lpt_row(const int32_t *seq_lens, int B, int pos, 
     return *slot;
 }
 
-__global__ __launch_bounds__(64 * kSeqWaves) void decode_seq_kernel(SeqArgs a)
+// QDQ: NVFP4 fake quantization of P and V.  P is then taken against the sequential pass's running max
+// (the max over all earlier tiles and this one), not the wave's own, so that its blocks are quantized
+// at the scale the one sequential pass sees; the wave's state is kept relative to that same max.
+template <bool QDQ>
+__device__ __forceinline__ void decode_seq(const SeqArgs &a)
 {
     __shared__ int row_slot;
     const int g = blockIdx.x, b = lpt_row(a.seq_lens, gridDim.y, blockIdx.y, &row_slot);
@@ -566,6 +663,9 @@ __global__ __launch_bounds__(64 * kSeqWaves) void decode_seq_kernel(SeqArgs a)
 
     bf16x8 qop[4];
     load_q_operand(a.q, b, g, a.Hq, a.G, lane, qop);
+    Qdq qq{};
+    if constexpr (QDQ)
+        qq = Qdq{{a.p_enc, a.p_dec}, {a.v_enc, a.v_dec}, a.p_qdq != 0, a.v_qdq != 0};
     WaveState st;
     state_init(st);
     float run_max = kNegInf; // max of tile maxima over all earlier rounds (log2 units), head n
@@ -639,8 +739,12 @@ __global__ __launch_bounds__(64 * kSeqWaves) void decode_seq_kernel(SeqArgs a)
         size_t q0, q1;
         tile_pages(t + 2 * kSeqWaves, q0, q1);
         load_k_chunk(a.kc + q0, a.kc + q1, lane, kq);
-        if (active && any_keep)
-            chunk_update(st, sc, tmax, keep, vr, tok0, L, a.scale_log2, vt, lane);
+        if (active && any_keep) {
+            if constexpr (QDQ)
+                chunk_update<true>(st, sc, fmaxf(prefix, tmax), keep, vr, tok0, L, a.scale_log2, vt, lane, qq);
+            else
+                chunk_update(st, sc, tmax, keep, vr, tok0, L, a.scale_log2, vt, lane);
+        }
         o0 = n0;
         o1 = n1;
         n0 = q0;
@@ -666,9 +770,15 @@ __global__ __launch_bounds__(64 * kSeqWaves) void decode_seq_kernel(SeqArgs a)
     });
 }
 
+__global__ __launch_bounds__(64 * kSeqWaves) void decode_seq_kernel(SeqArgs a) { decode_seq<false>(a); }
+__global__ __launch_bounds__(64 * kSeqWaves) void decode_seq_qdq_kernel(SeqArgs a) { decode_seq<true>(a); }
+
 hipError_t launch_decode_seq(const SeqArgs &a, int B, hipStream_t stream)
 {
-    hipLaunchKernelGGL(decode_seq_kernel, dim3(a.Hkv, B), dim3(64 * kSeqWaves), 0, stream, a);
+    if (a.p_qdq || a.v_qdq)
+        hipLaunchKernelGGL(decode_seq_qdq_kernel, dim3(a.Hkv, B), dim3(64 * kSeqWaves), 0, stream, a);
+    else
+        hipLaunchKernelGGL(decode_seq_kernel, dim3(a.Hkv, B), dim3(64 * kSeqWaves), 0, stream, a);
     return hipGetLastError();
 }
 

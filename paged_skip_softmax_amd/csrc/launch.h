@@ -44,6 +44,9 @@ struct SeqArgs {
     float *lse;             // nullable [B, Hq]
     uint8_t *skip_map;      // nullable [B, Hq, map_stride]
     int map_stride;
+    // NVFP4 fake quantization of P / V (on when p_qdq / v_qdq): enc = 448 / amax, dec = amax / 2688
+    float p_enc, p_dec, v_enc, v_dec;
+    int p_qdq, v_qdq;
 };
 
 // Small-seq cross-attention (s_q = 1, s_kv <= 16).

@@ -65,6 +65,35 @@ def test_decode_validation(lib):
     assert b"num_splits" in lib.attn_last_error_message()
 
 
+def _decode_qdq(lib, **kw):
+    a = dict(q=FAKE, kc=FAKE, vc=FAKE, bt=FAKE, sl=FAKE, B=2, Hq=8, Hkv=2, D=128, page=16, pages=100, maxp=10,
+             scale=0.1, thr=0.0, pa=1.0, va=1.0, o=FAKE, lse=None, map=None, stride=5, stream=None)
+    a.update(kw)
+    return lib.attn_decode_paged_qdq(a["q"], a["kc"], a["vc"], a["bt"], a["sl"], a["B"], a["Hq"], a["Hkv"], a["D"],
+                                     a["page"], a["pages"], a["maxp"], a["scale"], a["thr"], a["pa"], a["va"],
+                                     a["o"], a["lse"], a["map"], a["stride"], a["stream"])
+
+
+def test_decode_qdq_validation(lib):
+    for bad in (-1.0, math.nan, math.inf, 1e-30, 1e30):
+        assert _decode_qdq(lib, pa=bad) == INVALID
+        assert _decode_qdq(lib, va=bad) == INVALID
+    assert b"amax" in lib.attn_last_error_message()
+    for thr in (math.nan, -0.01, 1.01):
+        assert _decode_qdq(lib, thr=thr) == INVALID
+    assert _decode_qdq(lib, B=-1) == INVALID
+    assert _decode_qdq(lib, Hq=7) == INVALID
+    assert _decode_qdq(lib, scale=math.nan) == INVALID
+    assert _decode_qdq(lib, map=FAKE, stride=4) == INVALID
+    assert _decode_qdq(lib, D=64) == UNSUPPORTED
+    assert _decode_qdq(lib, page=32) == UNSUPPORTED
+    assert _decode_qdq(lib, Hq=34, Hkv=2) == UNSUPPORTED
+    assert _decode_qdq(lib, B=65536) == UNSUPPORTED
+    assert _decode_qdq(lib, vc=None) == INVALID
+    assert _decode_qdq(lib, B=0) == _lib.ATTN_OK
+    assert _decode_qdq(lib, B=0, pa=0.0, va=0.0) == _lib.ATTN_OK
+
+
 def test_workspace_size(lib):
     assert lib.attn_decode_paged_workspace_size(64, 32, 128, 32) == 64 * 32 * 32 * 129 * 4
     assert lib.attn_decode_paged_workspace_size(64, 32, 128, 0) == 64 * 32 * 32 * 129 * 4

@@ -769,3 +769,15 @@ def test_decode_qdq_skip_decisions_unchanged_by_quantization():
     od, _, md = oracle.decode(x.q, x.k_cache, x.v_cache, x.block_table, x.seq_lens, math.log(2), mode="skip",
                               thr=0.1, stride=m0.shape[-1])
     assert np.array_equal(md, m0)
+
+
+def test_decode_qdq_replay():
+    # replaying the pass's own decisions reproduces it; replaying "keep everything" is the thr = 0 pass
+    x = _exact_decode(100, [40, 200, 333], Hq=4, Hkv=2, D=32, q_nnz=8)
+    args = (x.q, x.k_cache, x.v_cache, x.block_table, x.seq_lens, math.log(2))
+    o1, l1, m1 = oracle.decode_qdq(*args, thr=0.2, p_amax=1.0, v_amax=2.0)
+    o2, l2, _ = oracle.decode_qdq(*args, p_amax=1.0, v_amax=2.0, replay=np.where(m1 == 1, 1, 0).reshape(-1, m1.shape[-1]))
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+    o3, l3, _ = oracle.decode_qdq(*args, thr=0.0, p_amax=1.0, v_amax=2.0)
+    o4, l4, _ = oracle.decode_qdq(*args, thr=0.9, p_amax=1.0, v_amax=2.0, replay=np.zeros_like(m1).reshape(-1, m1.shape[-1]))
+    assert np.array_equal(o3, o4) and np.array_equal(l3, l4)
