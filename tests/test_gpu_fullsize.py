@@ -156,6 +156,32 @@ def test_full_skip_decode_all_rows(hot_host, thr):
     assert np.max(np.abs(ln - lrp)) <= LSE_TOL
 
 
+@pytest.mark.parametrize("thr", [0.0, 0.1])
+def test_full_skip_decode_nvfp4_sampled_rows(hot_host, thr):
+    # the benchmark's NVFP4 decode call (amax 1 for P and V) on the full hot-key workload; sampled batch
+    # rows (the longest, the shortest, every fifth) against the oracle replaying the GPU's skip map
+    x, h = hot_host
+    o, lse, smap = attn.attn_decode_paged_qdq(x.q, x.k_cache, x.v_cache, x.block_table, x.seq_lens,
+                                              skip_threshold=thr, p_amax=1.0, v_amax=1.0, return_lse=True,
+                                              return_skip_map=True)
+    torch.cuda.synchronize()
+    on, ln = _np(o), _np(lse)
+    assert np.isfinite(on).all()
+    g = smap.cpu().numpy()
+    L = h["sl"].numpy()
+    bs = sorted({int(np.argmax(L)), int(np.argmin(L))} | set(range(0, x.B, 5)))
+    rows = [(b, hh) for b in bs for hh in range(x.Hq)]
+    r = np.array(rows)
+    gm = g[r[:, 0], r[:, 1]]
+    _, _, om = oracle.decode_qdq(h["q"], h["k"], h["v"], h["bt"], h["sl"], x.scale, thr=thr, p_amax=1.0, v_amax=1.0,
+                                 rows=rows)
+    _check_map(gm, om[:, :gm.shape[-1]])
+    od, ld, _ = oracle.decode_qdq(h["q"], h["k"], h["v"], h["bt"], h["sl"], x.scale, p_amax=1.0, v_amax=1.0,
+                                  rows=rows, replay=np.where(gm == 1, 1, 0))
+    assert np.max(np.abs(on[r[:, 0], r[:, 1]] - od)) <= BF16_TOL
+    assert np.max(np.abs(ln[r[:, 0], r[:, 1]] - ld)) <= LSE_TOL
+
+
 def test_full_smallseq_all_rows():
     x = W.smallseq_cross(seed=1004, device=DEV)              # B 30720, s_kv in {2..16}, H 16, D 128
     o, w, lse = attn.attn_smallseq_cross(x.q, x.k, x.v, x.cu_kv, x.max_s, return_lse=True)
