@@ -441,6 +441,7 @@ def main():
             out["decode"]["cpu_oracle"] = _cpu_decode(work["decode"], "dense", 0.0)
         if "skip" in out:
             out["skip"]["cpu_oracle_thr0.1"] = _cpu_decode(work["skip"], "skip", 0.1)
+            out["skip"]["cpu_oracle_nvfp4_thr0.1"] = _cpu_decode(work["skip"], "nvfp4", 0.1)
         if "smallseq" in out:
             out["smallseq"]["cpu_oracle"] = _cpu_smallseq(work["smallseq"])
 
@@ -550,7 +551,8 @@ def _threads():
 
 def _cpu_decode(d, mode, thr):
     """The fp64 oracle on the eight longest batch rows of a paged-decode workload, all heads, in GB/s of
-    KV read (dense accounting).  Only the pages of those rows are copied to the host."""
+    KV read (dense accounting); mode "nvfp4" is the decode with NVFP4 P and V (amax 1).  Only the pages of
+    those rows are copied to the host."""
     import numpy as np
     import torch
 
@@ -565,12 +567,16 @@ def _cpu_decode(d, mode, thr):
     kc, vc = d.k_cache[used].cpu(), d.v_cache[used].cpu()
     q, sl = d.q[bs].cpu(), d.seq_lens[bs].cpu()
     t0 = time.perf_counter()
-    oracle.decode(q, kc, vc, bt_h.cpu(), sl, d.scale, mode=mode, thr=thr, tile=32)
+    if mode == "nvfp4":
+        oracle.decode_qdq(q, kc, vc, bt_h.cpu(), sl, d.scale, thr=thr, p_amax=1.0, v_amax=1.0)
+    else:
+        oracle.decode(q, kc, vc, bt_h.cpu(), sl, d.scale, mode=mode, thr=thr, tile=32)
     dt = time.perf_counter() - t0
     kv = 4.0 * d.Hkv * d.D * float(sl.sum())
     return {"value": kv / dt / 1e9, "unit": "GB/s", "cores": _threads(), "kind": "oracle",
             "sample": f"the 8 longest batch rows (L = {[int(L[b]) for b in bs]}), all {d.Hq} heads, mode {mode}"
-                      f"{' thr ' + str(thr) if mode == 'skip' else ''}: {kv / 1e9:.2f} GB of KV in {dt:.2f} s"}
+                      f"{' thr ' + str(thr) if mode in ('skip', 'nvfp4') else ''}"
+                      f"{' (P and V amax 1)' if mode == 'nvfp4' else ''}: {kv / 1e9:.2f} GB of KV in {dt:.2f} s"}
 
 
 def _cpu_smallseq(c):
