@@ -44,6 +44,8 @@
 // below it by more than -log2(threshold).  A skipped half contributes nothing and never raises the
 // running max; its exponentials are left out by a wave-uniform branch when every row of the wave
 // skips it, and the P.V products of a 64-key tile when every row skips both halves.
+#include <type_traits>
+
 #include "kcommon.h"
 #include "launch.h"
 #include "lds_dma.h"
@@ -290,35 +292,56 @@ __device__ __forceinline__ void iteration(int t, const IterCtx &c, const Loader<
         nx[1][i] = 0.f;
     }
     uint32_t pk[2][8];
-    {
+    // SKIP: a skipped half gets p = 0 from an infinite reference max instead of a per-row branch, so
+    // the interleave of MFMAs and exponentials stays one basic block; when no row of the wave keeps
+    // either half, the steps run without exponentials
+    float mk0 = m_use, mk1 = m_use;
+    if constexpr (SKIP) {
+        mk0 = ss.keep[0] ? m_use : __builtin_inff();
+        mk1 = ss.keep[1] ? m_use : __builtin_inff();
+    }
+    auto steps_b = [&](auto with_exp) {
 #pragma unroll
         for (int step = 0; step < 16; ++step) {
             const uint4 k2 = step + 2 < 16 ? kop(step + 2) : k0;
             nx[step & 1] = mfma32(as_bf16x8(k0), wv.qop[step >> 1], nx[step & 1]);
             const int kk = step >> 3, i = 2 * (step & 7);
-            if (!SKIP) {
-                const float p0 = exp2_fast(fmaf(sc[kk][i], sl, -m_use));
-                const float p1 = exp2_fast(fmaf(sc[kk][i + 1], sl, -m_use));
+            if constexpr (decltype(with_exp)::value) {
+                const float mk = kk ? mk1 : mk0;
+                const float p0 = exp2_fast(fmaf(sc[kk][i], sl, -mk));
+                const float p1 = exp2_fast(fmaf(sc[kk][i + 1], sl, -mk));
                 wv.l += p0 + p1;
                 anchor(wv.l);
                 pk[kk][i >> 1] = pack_bf16x2(p0, p1);
             } else {
-                // a skipped half adds nothing and is not rescaled; when every row of the wave skips it,
-                // the exponentials are branched over
-                float p0 = 0.f, p1 = 0.f;
-                if (ss.keep[kk]) {
-                    p0 = exp2_fast(fmaf(sc[kk][i], sl, -m_use));
-                    p1 = exp2_fast(fmaf(sc[kk][i + 1], sl, -m_use));
-                    wv.l += p0 + p1;
-                }
-                anchor(wv.l);
-                pk[kk][i >> 1] = pack_bf16x2(p0, p1);
+                pk[kk][i >> 1] = 0u;
             }
             anchor(pk[kk][i >> 1]);
             sched_fence();
             k0 = k1;
             k1 = k2;
         }
+    };
+    if constexpr (!SKIP) {
+#pragma unroll
+        for (int step = 0; step < 16; ++step) {
+            const uint4 k2 = step + 2 < 16 ? kop(step + 2) : k0;
+            nx[step & 1] = mfma32(as_bf16x8(k0), wv.qop[step >> 1], nx[step & 1]);
+            const int kk = step >> 3, i = 2 * (step & 7);
+            const float p0 = exp2_fast(fmaf(sc[kk][i], sl, -m_use));
+            const float p1 = exp2_fast(fmaf(sc[kk][i + 1], sl, -m_use));
+            wv.l += p0 + p1;
+            anchor(wv.l);
+            pk[kk][i >> 1] = pack_bf16x2(p0, p1);
+            anchor(pk[kk][i >> 1]);
+            sched_fence();
+            k0 = k1;
+            k1 = k2;
+        }
+    } else if (__any(ss.keep[0] || ss.keep[1])) {
+        steps_b(std::true_type{});
+    } else {
+        steps_b(std::false_type{});
     }
 
     sched_fence();
