@@ -82,6 +82,21 @@ def test_qdq_exact_scores(thr, p_amax, v_amax):
     assert np.max(np.abs(od - ou)) > BF16_TOL
 
 
+def test_qdq_exact_scores_group_of_1_and_deterministic():
+    x = _exact([1, 17, 64, 999, 2500, 0, 48], Hq=8, Hkv=8, seed=114)
+    args = (x.q, x.k_cache, x.v_cache, x.block_table, x.seq_lens)
+    o1, _, m1 = attn.attn_decode_paged_qdq(*args, scale=LN2, skip_threshold=0.2, p_amax=1.0, v_amax=2.5,
+                                           return_skip_map=True)
+    o2, _, m2 = attn.attn_decode_paged_qdq(*args, scale=LN2, skip_threshold=0.2, p_amax=1.0, v_amax=2.5,
+                                           return_skip_map=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(m1, m2)
+    od, _, om = oracle.decode_qdq(*args, LN2, thr=0.2, p_amax=1.0, v_amax=2.5)
+    assert np.array_equal(m1.cpu().numpy()[..., :om.shape[-1]], om)
+    assert np.max(np.abs(_np(o1) - od)) <= BF16_TOL
+    assert torch.all(o1[5] == 0)  # the empty sequence
+
+
 def test_qdq_exact_scores_group_of_16():
     x = _exact([1, 40, 300, 1500, 33], Hq=16, Hkv=1, seed=112)
     o, _, smap = attn.attn_decode_paged_qdq(x.q, x.k_cache, x.v_cache, x.block_table, x.seq_lens, scale=LN2,
