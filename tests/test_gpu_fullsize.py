@@ -182,6 +182,40 @@ def test_full_skip_decode_nvfp4_sampled_rows(hot_host, thr):
     assert np.max(np.abs(ln[r[:, 0], r[:, 1]] - ld)) <= LSE_TOL
 
 
+def test_decode_largest_batch():
+    # B = 65535, the largest grid dimension the decode launches use (split-K in z, sequential in y):
+    # sampled rows at both ends of the batch against the oracle, for split-K, the sequential skip decode
+    # and the NVFP4 decode
+    B = 65535
+    lens = torch.randint(1, 49, (B,), generator=torch.Generator().manual_seed(120)).tolist()
+    pool = sum((L + 15) // 16 for L in lens) + 5
+    x = W.paged_decode(seed=121, device=DEV, B=B, Hq=4, Hkv=1, D=128, lengths=lens, lmax=48, pool=pool)
+    rows = [(b, h) for b in list(range(40)) + list(range(B - 40, B)) for h in range(4)]
+    r = np.array(rows)
+    h = dict(q=x.q.cpu(), k=x.k_cache.cpu(), v=x.v_cache.cpu(), bt=x.block_table.cpu(), sl=x.seq_lens.cpu())
+    print("largest batch: split-K", flush=True)
+    o, _, _ = attn.attn_decode_paged(x.q, x.k_cache, x.v_cache, x.block_table, x.seq_lens, num_splits=32)
+    torch.cuda.synchronize()
+    od, _, _ = oracle.decode(h["q"], h["k"], h["v"], h["bt"], h["sl"], x.scale, rows=rows)
+    assert np.max(np.abs(_np(o)[r[:, 0], r[:, 1]] - od)) <= BF16_TOL
+    print("largest batch: sequential skip", flush=True)
+    o, _, smap = attn.attn_decode_paged(x.q, x.k_cache, x.v_cache, x.block_table, x.seq_lens, num_splits=1,
+                                        skip_threshold=0.1, return_skip_map=True)
+    torch.cuda.synchronize()
+    g = smap.cpu().numpy()[r[:, 0], r[:, 1]]
+    orp, _, _ = oracle.decode(h["q"], h["k"], h["v"], h["bt"], h["sl"], x.scale, mode="skip", tile=32, rows=rows,
+                              replay=np.where(g == 2, 0, g), stride=g.shape[-1])
+    assert np.max(np.abs(_np(o)[r[:, 0], r[:, 1]] - orp)) <= BF16_TOL
+    print("largest batch: NVFP4", flush=True)
+    o, _, smap = attn.attn_decode_paged_qdq(x.q, x.k_cache, x.v_cache, x.block_table, x.seq_lens,
+                                            skip_threshold=0.1, p_amax=1.0, v_amax=1.0, return_skip_map=True)
+    torch.cuda.synchronize()
+    g = smap.cpu().numpy()[r[:, 0], r[:, 1]]
+    oq, _, _ = oracle.decode_qdq(h["q"], h["k"], h["v"], h["bt"], h["sl"], x.scale, p_amax=1.0, v_amax=1.0,
+                                 rows=rows, replay=np.where(g == 1, 1, 0))
+    assert np.max(np.abs(_np(o)[r[:, 0], r[:, 1]] - oq)) <= BF16_TOL
+
+
 def test_full_smallseq_all_rows():
     x = W.smallseq_cross(seed=1004, device=DEV)              # B 30720, s_kv in {2..16}, H 16, D 128
     o, w, lse = attn.attn_smallseq_cross(x.q, x.k, x.v, x.cu_kv, x.max_s, return_lse=True)
