@@ -29,6 +29,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
+FLUSH_BYTES = 512 << 20     # written between timed calls: twice the 256 MB last-level cache
 
 
 def _parse():
@@ -39,7 +40,7 @@ def _parse():
     p.add_argument("--seed", type=int, default=0)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--only", default="",
-                   help="comma list of prefill,prefill_skip,decode,skip,smallseq,prefill_bwd,smallseq_bwd,"
+                   help="comma list of tiny,prefill,prefill_skip,decode,skip,smallseq,prefill_bwd,smallseq_bwd,"
                         "decode_multi,prefill_paged (profiling runs)")
     p.add_argument("--launch-log", metavar="PATH", default="",
                    help="write the bench's calls, in launch order, to PATH (JSON; profiling runs)")
@@ -105,12 +106,14 @@ def main():
     from paged_skip_softmax_amd import workloads as W
 
     only = (set(args.only.split(",")) if args.only
-            else {"prefill", "prefill_skip", "decode", "skip", "smallseq", "prefill_bwd", "smallseq_bwd",
+            else {"tiny", "prefill", "prefill_skip", "decode", "skip", "smallseq", "prefill_bwd", "smallseq_bwd",
                   "decode_multi", "prefill_paged"})
     dev = "cuda:0"
     torch.cuda.set_device(0)
     t_gen = time.time()
     work = {}
+    if "tiny" in only:
+        work["tiny"] = W.tiny_dense(seed=1000 + args.seed, device=dev)
     if "prefill" in only:
         work["prefill"] = W.varlen_prefill(seed=1001 + args.seed, device=dev)
     if "prefill_skip" in only:
@@ -169,6 +172,15 @@ def main():
             pp.q, pp.cu_q, pp.max_q, pp.k_cache, pp.v_cache, pp.block_table, pp.seq_lens, out=o_pp)
 
     calls = {}  # name -> zero-arg launcher
+    if "tiny" in only:
+        xt = work["tiny"]
+        o_t = torch.empty_like(xt.q)
+        for causal in (True, False):
+            for thr in (0.0, 0.1):
+                calls[f"tiny_{'causal' if causal else 'noncausal'}_{thr}"] = (
+                    lambda causal=causal, thr=thr: attn.attn_prefill_varlen(
+                        xt.q, xt.k, xt.v, xt.cu_q, xt.cu_k, xt.max_q, xt.max_k, scale=xt.scale, causal=causal,
+                        skip_threshold=thr, out=o_t))
     if "prefill" in only:
         x = work["prefill"]
         o_pf = torch.empty_like(x.q)
@@ -212,9 +224,17 @@ def main():
     nxt = {k: _logged(k, f) for k, f in nxt.items()}
     names = list(calls)
     stream = torch.cuda.current_stream()
+    # Between timed calls (outside each event pair) a 512 MiB buffer is written, which evicts the inputs
+    # the previous call streamed from the L2s (4 MB per XCD) and the 256 MB last-level cache, so every
+    # call starts cold.
+    flush_buf = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
+
+    def flush():
+        flush_buf.fill_(0)
 
     def step(record):
         for nm in names:
+            flush()
             if record is None:
                 calls[nm]()
             else:
@@ -239,10 +259,12 @@ def main():
     ms_per_step = (t1 - t0) * 1e3 / max(1, args.steps)
     for nm, fn in nxt.items():
         for _ in range(args.warmup):
+            flush()
             fn()
         torch.cuda.synchronize()
         evs = []
         for _ in range(args.steps):
+            flush()
             e0 = torch.cuda.Event(enable_timing=True)
             e1 = torch.cuda.Event(enable_timing=True)
             e0.record(stream)
@@ -252,6 +274,7 @@ def main():
         torch.cuda.synchronize()
         ms[nm] = float(np.mean([a.elapsed_time(b) for a, b in evs]))
         ms_min[nm] = float(np.min([a.elapsed_time(b) for a, b in evs]))
+    del flush_buf
     print(f"# kernel ms (mean over {args.steps} steps): " + ", ".join(f"{k}={v:.4f}" for k, v in ms.items()),
           file=sys.stderr, flush=True)
 
@@ -269,6 +292,18 @@ def main():
 
     out = {}
     rooflines = []
+    if "tiny" in only:
+        xt = work["tiny"]
+        res = {}
+        for causal in (True, False):
+            fl = _tiny_flops(xt, causal)
+            for thr in (0.0, 0.1):
+                nm = f"tiny_{'causal' if causal else 'noncausal'}_{thr}"
+                res[nm[5:]] = {"ms": ms[nm], "ms_min": ms_min[nm], "flop_dense_equiv": fl,
+                               "gflops_dense_equiv": fl / (ms[nm] * 1e-3) / 1e9}
+        res["note"] = ("fp32, B=2, Hq=4, Hkv=2, D=64, S=128, 32-key skip tiles; latency-bound (a few hundred "
+                       "workgroups), reported for completeness")
+        out["tiny_fp32"] = res
     if "prefill" in only:
         L = work["prefill"].lens.double()
         flops = 4.0 * 128 * 32 * float((L * (L + 1) / 2).sum())
@@ -444,6 +479,11 @@ def main():
             out["skip"]["cpu_oracle_nvfp4_thr0.1"] = _cpu_decode(work["skip"], "nvfp4", 0.1)
         if "smallseq" in out:
             out["smallseq"]["cpu_oracle"] = _cpu_smallseq(work["smallseq"])
+        if "tiny_fp32" in out:
+            for causal in (True, False):
+                for thr in (0.0, 0.1):
+                    out["tiny_fp32"][f"{'causal' if causal else 'noncausal'}_{thr}"]["cpu_oracle"] = _cpu_tiny(
+                        work["tiny"], causal, thr)
 
     headline = out.get("prefill", {}).get("tflops")
     line = {
@@ -460,7 +500,8 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": "varlen causal prefill bf16: 16 seqs, L~U[256,4096] THD, Hq=32, Hkv=8, D=128",
-                   "step_also_runs": ["the same prefill shapes with hot keys, skip-softmax thr {0,0.01,0.1}",
+                   "step_also_runs": ["tiny fp32 B=2 Hq=4 Hkv=2 D=64 S=128, {causal, non-causal} x thr {0, 0.1}",
+                                      "the same prefill shapes with hot keys, skip-softmax thr {0,0.01,0.1}",
                                       "paged decode split-K B=64 L~U[1024,32768] page 16, 32x128-key splits",
                                       "sequential skip decode thr {0,0.01,0.1} on hot keys",
                                       "small-seq cross B=30720 s_kv in {2..16} H=16 D=128"],
@@ -549,6 +590,45 @@ def _threads():
     return int(os.environ.get("OMP_NUM_THREADS") or os.cpu_count() or 1)
 
 
+def _cpu_model():
+    """The host CPU's model name (as lscpu reports it), from /proc/cpuinfo."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
+def _cpu_tiny(x, causal, thr):
+    """The fp64 oracle on the whole tiny fp32 workload (every row, every head), repeated until about
+    0.2 s have passed; GFLOP/s of the dense-equivalent work, and the mean time of one run."""
+    import oracle
+    q, k, v, cq, ck = x.q.cpu(), x.k.cpu(), x.v.cpu(), x.cu_q.cpu(), x.cu_k.cpu()
+    n, t0 = 0, time.perf_counter()
+    while True:
+        oracle.prefill(q, k, v, cq, ck, x.Hq, x.Hkv, x.scale, causal, mode="skip", thr=thr, tile=32)
+        n += 1
+        dt = time.perf_counter() - t0
+        if dt > 0.2:
+            break
+    fl = _tiny_flops(x, causal)
+    return {"value": fl * n / dt / 1e9, "unit": "GFLOP/s", "cores": _threads(), "kind": "oracle",
+            "cpu_model": _cpu_model(), "ms": dt / n * 1e3,
+            "sample": f"the whole workload ({x.q.shape[0] * x.Hq} rows), skip mode with thr {thr} and 32-key tiles, "
+                      f"mean of {n} runs"}
+
+
+def _tiny_flops(x, causal):
+    """4 D Hq per visible (query, key) pair."""
+    L = x.lens.double()
+    pairs = float((L * (L + 1) / 2).sum()) if causal else float((L * L).sum())
+    return 4.0 * x.D * x.Hq * pairs
+
+
 def _cpu_decode(d, mode, thr):
     """The fp64 oracle on the eight longest batch rows of a paged-decode workload, all heads, in GB/s of
     KV read (dense accounting); mode "nvfp4" is the decode with NVFP4 P and V (amax 1).  Only the pages of
@@ -574,6 +654,7 @@ def _cpu_decode(d, mode, thr):
     dt = time.perf_counter() - t0
     kv = 4.0 * d.Hkv * d.D * float(sl.sum())
     return {"value": kv / dt / 1e9, "unit": "GB/s", "cores": _threads(), "kind": "oracle",
+            "cpu_model": _cpu_model(),
             "sample": f"the 8 longest batch rows (L = {[int(L[b]) for b in bs]}), all {d.Hq} heads, mode {mode}"
                       f"{' thr ' + str(thr) if mode in ('skip', 'nvfp4') else ''}"
                       f"{' (P and V amax 1)' if mode == 'nvfp4' else ''}: {kv / 1e9:.2f} GB of KV in {dt:.2f} s"}
@@ -590,6 +671,7 @@ def _cpu_smallseq(c):
     dt = time.perf_counter() - t0
     kv = 4.0 * c.H * c.D * T
     return {"value": kv / dt / 1e9, "unit": "GB/s", "cores": _threads(), "kind": "oracle",
+            "cpu_model": _cpu_model(),
             "sample": f"the first {n} sequences ({T} keys), all {c.H} heads: {kv / 1e9:.3f} GB of KV in {dt:.2f} s"}
 
 
@@ -610,6 +692,7 @@ def _cpu_baseline(x):
     dt = time.perf_counter() - t0
     flops = sum(4.0 * x.D * (i + 1) for b in picked for i in range(int(L[b]))) * x.Hq
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "cpu_model": _cpu_model(),
             "sample": f"every causal query row of the three longest sequences (L={[int(L[b]) for b in picked]}), "
                       f"all {x.Hq} heads: {len(rows)} rows, {flops:.3e} FLOP in {dt:.2f} s"}
 
@@ -705,6 +788,8 @@ PROFILE_COMMANDS = {
     "write": "rocprofv3 --pmc WRITE_SIZE -f csv -d {out}/prof_write -o run -- "
              "python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline --calib-copy "
              "--launch-log {out}/prof_write/launch_log.json",
+    "mfma": "rocprofv3 --pmc MfmaUtil SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_BUSY_CYCLES -f csv -d {out}/prof_mfma -o run -- "
+            "python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline --launch-log {out}/prof_mfma/launch_log.json",
     "summary": "python3 bench.py --summarize-profiles {out}",
 }
 
@@ -728,18 +813,20 @@ def _match(name):
     return None
 
 
-def _per_dispatch_counter(rows, counter):
-    """kernel key -> list of per-dispatch values (summed over the counter's instances), dispatch order."""
-    agg, key, order = {}, {}, []
+def _per_dispatch_counter(rows, counter, reduce=sum):
+    """kernel key -> list of per-dispatch values (reduced over the counter's instances, summed by
+    default), dispatch order."""
+    vals, key, order = {}, {}, []
     for r in rows:
         if r["Counter_Name"] != counter:
             continue
         d = int(r["Dispatch_Id"])
-        if d not in agg:
-            agg[d] = 0.0
+        if d not in vals:
+            vals[d] = []
             key[d] = _match(r["Kernel_Name"])
             order.append(d)
-        agg[d] += float(r["Counter_Value"])
+        vals[d].append(float(r["Counter_Value"]))
+    agg = {d: float(reduce(v)) for d, v in vals.items()}
     out = {}
     for d in sorted(order):
         if key[d]:
@@ -837,6 +924,55 @@ def _summarize_profiles(base):
     with open(os.path.join(outdir, "traffic.json"), "w") as f:
         json.dump(traffic, f, indent=1, sort_keys=True)
     print("wrote profiles/traffic.json")
+    if os.path.isdir(os.path.join(base, "prof_mfma")):
+        _summarize_mfma(base, durs)
+
+
+# kernels whose matrix-core use the MFMA-busy summary reports (the contraction-bound ones)
+MFMA_KERNELS = [PF, PS, PP, "bwd_dkdv_kernel", "bwd_dq_kernel"]
+
+
+def _summarize_mfma(base, durs):
+    """MFMA busy % (rocprofv3's derived MfmaUtil: SQ_VALU_MFMA_BUSY_CYCLES over GRBM_GUI_ACTIVE times
+    the SIMD count), executed bf16 MFMA FLOPs per dispatch (SQ_INSTS_VALU_MFMA_MOPS_BF16 * 512) and the
+    SQ busy cycles, per kernel and bench call, into profiles/mfma_busy.<workload>.txt."""
+    import numpy as np
+    rows = _csv(os.path.join(base, "prof_mfma"), "counter_collection.csv")
+    util = _per_dispatch_counter(rows, "MfmaUtil", reduce=np.mean)
+    mops = _per_dispatch_counter(rows, "SQ_INSTS_VALU_MFMA_MOPS_BF16")
+    busy = _per_dispatch_counter(rows, "SQ_BUSY_CYCLES", reduce=max)
+    lines = ["# MFMA busy per kernel, rocprofv3 counters (one dispatch = one launch), bench workloads as in the",
+             "# kernel summaries of this folder",
+             "# commands (repository root, TMPDIR=/tmp; the summary step runs on any host):",
+             "\n".join(f"#   {k}: {v.format(out=base)}" for k, v in PROFILE_COMMANDS.items()),
+             "# MfmaUtil = 100 * sum(SQ_VALU_MFMA_BUSY_CYCLES) / (max(GRBM_GUI_ACTIVE) * SIMDs); executed FLOP =",
+             "# SQ_INSTS_VALU_MFMA_MOPS_BF16 * 512 (includes masked and recomputed work); clock = SQ_BUSY_CYCLES /",
+             "# the kernel's mean duration in the trace run", ""]
+    for k in MFMA_KERNELS:
+        if k not in util:
+            continue
+        u = util[k]
+        lines.append(f"{k}: MfmaUtil mean {np.mean(u):.1f} % over {len(u)} dispatches (min {np.min(u):.1f}, max "
+                     f"{np.max(u):.1f})")
+        roles = _roles(base, "prof_mfma", k, len(u))
+        if roles:
+            bu = _by_role(u, roles)
+            bm = _by_role(mops.get(k, [0.0] * len(u)), roles) if len(mops.get(k, [])) == len(u) else {}
+            bb = _by_role(busy.get(k, [0.0] * len(u)), roles) if len(busy.get(k, [])) == len(u) else {}
+            for role, v in bu.items():
+                ln = f"    {role}: MfmaUtil {np.mean(v):.1f} %"
+                if role in bm:
+                    ln += f", executed bf16 MFMA {np.mean(bm[role]) * 512:.4e} FLOP per launch"
+                if role in bb:
+                    ln += f", SQ_BUSY_CYCLES {np.mean(bb[role]):.0f}"
+                    if k in durs:
+                        ln += f" (~{np.mean(bb[role]) / (np.mean(durs[k]) * 1e-9) / 1e9:.2f} GHz over the mean " \
+                              f"trace duration)"
+                lines.append(ln)
+    path = os.path.join(ROOT, "profiles", "mfma_busy.bench_workloads.txt")
+    with open(path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("wrote profiles/mfma_busy.bench_workloads.txt")
 
 
 if __name__ == "__main__":

@@ -28,7 +28,9 @@
  *     preconditions and are not checked.  ATTN_ERR_HIP reports a failed launch.
  *   - GQA: query head h reads KV head h / (Hq / Hkv).
  *   - Logits are scale * q.k; LSE outputs are the natural-log log-sum-exp of those logits, fp32; a row
- *     that sees no key gets o = 0 and lse = -inf.
+ *     that sees no key gets o = 0 and lse = -inf.  scale must be positive with scale * log2(e) finite
+ *     (else ATTN_ERR_INVALID): masked keys are -inf before scaling and tile maxima are taken of the
+ *     unscaled scores.
  *   - skip_threshold must lie in [0, 1]; 0 reproduces dense attention.  Skip decisions are taken per
  *     (query row, 32-key tile), tiles aligned to key 0 and visited in ascending order; the first
  *     visited tile is never skipped.  Skip maps hold one byte per (row, tile):

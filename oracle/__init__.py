@@ -46,7 +46,7 @@ def _load():
         P, I, D = ctypes.c_void_p, ctypes.c_int, ctypes.c_double
         lib.orc_prefill_rows.argtypes = [I, P, P, P, P, P, I, I, I, I, D, I, I, D, I, I, P, I, P, I, P, P, P]
         lib.orc_decode_rows.argtypes = [P, P, P, P, P, I, I, I, I, I, I, D, I, D, I, I, P, I, P, I, P, P, P]
-        lib.orc_smallseq_rows.argtypes = [I, P, P, P, P, I, I, I, I, D, P, I, P, P]
+        lib.orc_smallseq_rows.argtypes = [I, P, P, P, P, I, I, I, I, D, P, I, P, P, P]
         lib.orc_prefill_bwd.argtypes = [I, P, P, P, P, P, P, P, I, I, I, I, D, I, P, P, P]
         lib.orc_smallseq_bwd.argtypes = [I, P, P, P, P, P, P, I, I, I, I, D, P, P, P]
         lib.orc_paged_multi_rows.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, D, P, I, P, P]
@@ -227,8 +227,9 @@ def nvfp4_qdq(x, amax):
     return out
 
 
-def smallseq(q, k, v, cu_kv, max_s, scale, rows=None):
-    """s_q = 1 cross-attention with attention weights.  rows: (b, head) pairs."""
+def smallseq(q, k, v, cu_kv, max_s, scale, rows=None, with_lse=False):
+    """s_q = 1 cross-attention with attention weights.  rows: (b, head) pairs.  Returns (o, w), or
+    (o, w, lse) with ``with_lse`` (lse [B, H], or [n_rows] for given rows; -inf with no key)."""
     qa, dt = _np(q)
     ka, dk = _np(k)
     va, dv = _np(v)
@@ -240,14 +241,16 @@ def smallseq(q, k, v, cu_kv, max_s, scale, rows=None):
     n = len(r)
     o = np.zeros((n, D))
     w = np.zeros((n, max(int(max_s), 0)))
+    lse = np.zeros(n)
     rc = _load().orc_smallseq_rows(dt, _ptr(qa), _ptr(ka), _ptr(va), _ptr(cu), B, H, D, int(max_s),
-                                   float(scale), _ptr(r), n, _ptr(o), _ptr(w))
+                                   float(scale), _ptr(r), n, _ptr(o), _ptr(w), _ptr(lse))
     if rc != 0:
         raise ValueError("oracle smallseq rejected its arguments")
     if rows is None:
         o = o.reshape(B, H, D)
         w = w.reshape(B, H, 1, max(int(max_s), 0))
-    return o, w
+        lse = lse.reshape(B, H)
+    return (o, w, lse) if with_lse else (o, w)
 
 
 def decode_multi(q, cu_q, k_cache, v_cache, block_table, seq_lens, scale, rows=None):

@@ -489,11 +489,12 @@ int orc_decode_qdq_rows(const void *q, const void *kc, const void *vc, const int
  * (s_q=1, s_kv<=16)": one query token per sequence, s_kv = cu_kv[b+1] - cu_kv[b] keys, non-causal,
  * H query heads = H KV heads.  Besides o it returns the attention weights w[b, h, 0, j] = p_j for
  * j < s_kv and 0 for s_kv <= j < max_s.  q [B, H, D], k/v [total_kv, H, D] (dtype).
- * rows: n_rows pairs (b, head); o [n_rows, D], w [n_rows, max_s].
+ * rows: n_rows pairs (b, head); o [n_rows, D], w [n_rows, max_s], lse (nullable) [n_rows]: the row's
+ * natural-log log-sum-exp of its logits (-inf with no key).
  */
 int orc_smallseq_rows(int dtype, const void *q, const void *k, const void *v, const int32_t *cu_kv, int B,
                       int H, int D, int max_s, double scale, const int32_t *rows, int n_rows, double *o,
-                      double *w)
+                      double *w, double *lse_out)
 {
     if (B < 0 || H <= 0 || D <= 0 || max_s < 0)
         return -1;
@@ -525,6 +526,8 @@ int orc_smallseq_rows(int dtype, const void *q, const void *k, const void *v, co
         dense_row(qd, K, V, n, D, scale, o + (size_t)r * D, &lse, p);
         for (int j = 0; j < max_s; ++j)
             w[(size_t)r * max_s + j] = j < n ? p[j] : 0.0;
+        if (lse_out)
+            lse_out[r] = lse;
         free(qd);
         free(K);
         free(V);

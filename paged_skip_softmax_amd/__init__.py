@@ -156,6 +156,7 @@ def attn_decode_paged(q, k_cache, v_cache, block_table, seq_lens, *, scale=None,
     if out is None:
         out = torch.empty_like(q)
     _cuda_contig("out", out, torch.bfloat16, dev)
+    _need(out.shape == q.shape, "out must match q")
     lse = torch.empty((B, Hq), dtype=torch.float32, device=dev) if return_lse else None
     stride = max(1, (max_pages * page + SKIP_TILE - 1) // SKIP_TILE)
     smap = torch.empty((B, Hq, stride), dtype=torch.uint8, device=dev) if return_skip_map else None
@@ -190,6 +191,7 @@ def attn_decode_paged_qdq(q, k_cache, v_cache, block_table, seq_lens, *, scale=N
     if out is None:
         out = torch.empty_like(q)
     _cuda_contig("out", out, torch.bfloat16, dev)
+    _need(out.shape == q.shape, "out must match q")
     lse = torch.empty((B, Hq), dtype=torch.float32, device=dev) if return_lse else None
     stride = max(1, (max_pages * page + SKIP_TILE - 1) // SKIP_TILE)
     smap = torch.empty((B, Hq, stride), dtype=torch.uint8, device=dev) if return_skip_map else None
@@ -237,6 +239,7 @@ def attn_decode_paged_multi(q, cu_seqlens_q, max_seqlen_q, k_cache, v_cache, blo
     if out is None:
         out = torch.empty_like(q)
     _cuda_contig("out", out, torch.bfloat16, dev)
+    _need(out.shape == q.shape, "out must match q")
     lse = torch.empty((total_q, Hq), dtype=torch.float32, device=dev) if return_lse else None
     stride = max(1, (block_table.shape[1] * page + SKIP_TILE - 1) // SKIP_TILE)
     smap = torch.empty((total_q, Hq, stride), dtype=torch.uint8, device=dev) if return_skip_map else None
@@ -265,6 +268,7 @@ def attn_smallseq_cross(q, k, v, cu_seqlens_kv, max_seqlen_kv, *, scale=None, re
     if out is None:
         out = torch.empty_like(q)
     _cuda_contig("out", out, torch.bfloat16, dev)
+    _need(out.shape == q.shape, "out must match q")
     w = torch.empty((B, H, 1, int(max_seqlen_kv)), dtype=torch.bfloat16, device=dev) if return_weights else None
     lse = torch.empty((B, H), dtype=torch.float32, device=dev) if return_lse else None
     _lib.check(lib.attn_smallseq_cross(q.data_ptr(), k.data_ptr(), v.data_ptr(), cu_seqlens_kv.data_ptr(), B, H, D,

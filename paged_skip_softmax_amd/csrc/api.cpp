@@ -42,6 +42,11 @@ attn_status_t hip_status(hipError_t e, const char *what)
 
 bool bad_threshold(float thr) { return !(thr >= 0.f && thr <= 1.f); } // also rejects NaN
 
+// The kernels mask keys with -inf before scaling and take a tile's maximum of the raw scores, so the
+// logit scale must be positive (0 turns -inf * 0 into NaN, a negative scale turns the maximum into the
+// minimum) and scale * log2(e) must stay finite.
+bool bad_scale(float scale) { return !(scale > 0.f && std::isfinite(scale * 1.4426950408889634f)); }
+
 // log2(threshold): the kernels compare in the log2 domain, tile_max - running_max < log2(thr) (both in
 // log2 units); thr = 0 gives -inf, which never skips.
 float log2_threshold(float thr) { return thr > 0.f ? std::log2(thr) : -INFINITY; }
@@ -99,8 +104,8 @@ attn_status_t attn_decode_paged(const void *q, const void *k_cache, const void *
     const int S = resolve_splits(num_splits, skip_threshold);
     if (skip_threshold > 0.f && S > 1)
         return fail(ATTN_ERR_INVALID, "attn_decode_paged: skip_threshold > 0 needs one sequential split, got %d", S);
-    if (!std::isfinite(scale))
-        return fail(ATTN_ERR_INVALID, "attn_decode_paged: scale is not finite");
+    if (bad_scale(scale))
+        return fail(ATTN_ERR_INVALID, "attn_decode_paged: scale must be positive and finite");
     if (num_pages <= 0 || max_pages_per_seq <= 0 || page_size <= 0)
         return fail(ATTN_ERR_INVALID, "attn_decode_paged: num_pages, max_pages_per_seq and page_size must be > 0");
     if (skip_map && S > 1)
@@ -176,8 +181,8 @@ attn_status_t attn_decode_paged_qdq(const void *q, const void *k_cache, const vo
     if (bad_threshold(skip_threshold))
         return fail(ATTN_ERR_INVALID, "attn_decode_paged_qdq: skip_threshold %g outside [0, 1]",
                     (double)skip_threshold);
-    if (!std::isfinite(scale))
-        return fail(ATTN_ERR_INVALID, "attn_decode_paged_qdq: scale is not finite");
+    if (bad_scale(scale))
+        return fail(ATTN_ERR_INVALID, "attn_decode_paged_qdq: scale must be positive and finite");
     for (float amax : {p_amax, v_amax})
         if (!(amax == 0.f || (amax >= kMinQdqAmax && amax <= kMaxQdqAmax)))
             return fail(ATTN_ERR_INVALID, "attn_decode_paged_qdq: amax %g is neither 0 (off) nor in [%g, %g]",
@@ -253,8 +258,8 @@ attn_status_t attn_prefill_varlen_backward(attn_dtype_t dtype, const void *q, co
     if (Hq <= 0 || Hkv <= 0 || Hq % Hkv)
         return fail(ATTN_ERR_INVALID, "attn_prefill_varlen_backward: Hq = %d must be a positive multiple of Hkv = %d",
                     Hq, Hkv);
-    if (!std::isfinite(scale))
-        return fail(ATTN_ERR_INVALID, "attn_prefill_varlen_backward: scale is not finite");
+    if (bad_scale(scale))
+        return fail(ATTN_ERR_INVALID, "attn_prefill_varlen_backward: scale must be positive and finite");
     if (dtype != ATTN_BF16 || D != 128)
         return fail(ATTN_ERR_UNSUPPORTED, "attn_prefill_varlen_backward: built for bf16 with D = 128");
     if ((int64_t)B * max_seqlen_q * Hq >= ((int64_t)1 << 31))
@@ -331,8 +336,8 @@ attn_status_t attn_decode_paged_multi(const void *q, const int32_t *cu_seqlens_q
     if (num_splits < 0 || num_splits > kMaxSplits)
         return fail(ATTN_ERR_INVALID, "attn_decode_paged_multi: num_splits %d outside [0, %d]", num_splits,
                     kMaxSplits);
-    if (!std::isfinite(scale))
-        return fail(ATTN_ERR_INVALID, "attn_decode_paged_multi: scale is not finite");
+    if (bad_scale(scale))
+        return fail(ATTN_ERR_INVALID, "attn_decode_paged_multi: scale must be positive and finite");
     if (num_pages <= 0 || max_pages_per_seq <= 0 || page_size <= 0)
         return fail(ATTN_ERR_INVALID, "attn_decode_paged_multi: num_pages, max_pages_per_seq and page_size must be > 0");
     if (D != 128)
@@ -420,8 +425,8 @@ attn_status_t attn_smallseq_cross(const void *q, const void *k, const void *v, c
         return fail(ATTN_ERR_INVALID, "attn_smallseq_cross: H = %d", H);
     if (max_seqlen_kv < 0 || max_seqlen_kv > 16)
         return fail(ATTN_ERR_INVALID, "attn_smallseq_cross: max_seqlen_kv = %d outside [0, 16]", max_seqlen_kv);
-    if (!std::isfinite(scale))
-        return fail(ATTN_ERR_INVALID, "attn_smallseq_cross: scale is not finite");
+    if (bad_scale(scale))
+        return fail(ATTN_ERR_INVALID, "attn_smallseq_cross: scale must be positive and finite");
     if (D != 128)
         return fail(ATTN_ERR_UNSUPPORTED, "attn_smallseq_cross: D = %d (built for 128)", D);
     if (B == 0)
@@ -455,8 +460,8 @@ attn_status_t attn_smallseq_cross_backward(const void *q, const void *k, const v
     if (max_seqlen_kv < 0 || max_seqlen_kv > 16)
         return fail(ATTN_ERR_INVALID, "attn_smallseq_cross_backward: max_seqlen_kv = %d outside [0, 16]",
                     max_seqlen_kv);
-    if (!std::isfinite(scale))
-        return fail(ATTN_ERR_INVALID, "attn_smallseq_cross_backward: scale is not finite");
+    if (bad_scale(scale))
+        return fail(ATTN_ERR_INVALID, "attn_smallseq_cross_backward: scale must be positive and finite");
     if (D != 128)
         return fail(ATTN_ERR_UNSUPPORTED, "attn_smallseq_cross_backward: D = %d (built for 128)", D);
     if (B == 0)
@@ -494,8 +499,8 @@ attn_status_t attn_prefill_varlen(attn_dtype_t dtype, const void *q, const void 
         return fail(ATTN_ERR_INVALID, "attn_prefill_varlen: Hq = %d must be a positive multiple of Hkv = %d", Hq, Hkv);
     if (bad_threshold(skip_threshold))
         return fail(ATTN_ERR_INVALID, "attn_prefill_varlen: skip_threshold %g outside [0, 1]", (double)skip_threshold);
-    if (!std::isfinite(scale))
-        return fail(ATTN_ERR_INVALID, "attn_prefill_varlen: scale is not finite");
+    if (bad_scale(scale))
+        return fail(ATTN_ERR_INVALID, "attn_prefill_varlen: scale must be positive and finite");
     if (skip_map && (int64_t)skip_map_stride * attn::kSkipTile < (int64_t)max_seqlen_k)
         return fail(ATTN_ERR_INVALID, "attn_prefill_varlen: skip_map_stride %d < ceil(max_seqlen_k / 32)", skip_map_stride);
     if (dtype == ATTN_BF16 && D != 64 && D != 128)

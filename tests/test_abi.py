@@ -246,3 +246,39 @@ def test_python_binding_raises_without_gpu_tensors():
     q = torch.zeros(2, 8, 128, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         attn.attn_decode_paged(q, q, q, q, q)
+
+
+@pytest.mark.parametrize("scale", [0.0, -0.1, -math.inf, math.nan, 3.0e38])
+def test_scale_must_be_positive_and_finite(lib, scale):
+    """A zero scale makes the kernels' masked -inf * 0 a NaN and a negative one turns tile maxima into
+    minima, so every entry point rejects scale <= 0 (and a scale whose log2-domain value overflows)."""
+    assert _decode(lib, scale=scale) == INVALID
+    assert _decode_qdq(lib, scale=scale) == INVALID
+    assert _prefill(lib, scale=scale) == INVALID
+    assert _backward(lib, scale=scale) == INVALID
+    assert _small(lib, scale=scale) == INVALID
+    assert b"scale" in lib.attn_last_error_message()
+
+
+def test_python_binding_checks_out_shapes():
+    """A caller-supplied out= of the wrong shape is refused before anything is launched."""
+    import torch
+    import paged_skip_softmax_amd as attn
+    from unittest import mock
+
+    # the binding's device checks run first; patch is_cuda so the shape check is what fails
+    q = torch.zeros(2, 8, 128, dtype=torch.bfloat16)
+    kc = torch.zeros(4, 2, 16, 128, dtype=torch.bfloat16)
+    bt = torch.zeros(2, 2, dtype=torch.int32)
+    sl = torch.zeros(2, dtype=torch.int32)
+    cu = torch.zeros(3, dtype=torch.int32)
+    bad = torch.zeros(1, 8, 128, dtype=torch.bfloat16)
+    with mock.patch.object(torch.Tensor, "is_cuda", new=property(lambda self: True)):
+        with pytest.raises(ValueError, match="out"):
+            attn.attn_decode_paged(q, kc, kc, bt, sl, out=bad)
+        with pytest.raises(ValueError, match="out"):
+            attn.attn_decode_paged_qdq(q, kc, kc, bt, sl, out=bad)
+        with pytest.raises(ValueError, match="out"):
+            attn.attn_decode_paged_multi(q, cu, 1, kc, kc, bt, sl, out=bad)
+        with pytest.raises(ValueError, match="out"):
+            attn.attn_smallseq_cross(q, q, q, cu, 1, out=bad)

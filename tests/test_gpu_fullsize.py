@@ -69,13 +69,15 @@ def prefill_hot(request):
     return W.varlen_prefill_hot(seed=1001, device=DEV)
 
 
+@pytest.mark.parametrize("causal", [True, False])
 @pytest.mark.parametrize("thr", [0.01, 0.1])
-def test_full_skip_prefill_sampled_rows(prefill_hot, thr):
+def test_full_skip_prefill_sampled_rows(prefill_hot, thr, causal):
     x = prefill_hot
-    o, lse, smap = attn.attn_prefill_varlen(x.q, x.k, x.v, x.cu_q, x.cu_k, x.max_q, x.max_k, causal=True,
+    print(f"full skip prefill thr {thr} causal {causal}", flush=True)
+    o, lse, smap = attn.attn_prefill_varlen(x.q, x.k, x.v, x.cu_q, x.cu_k, x.max_q, x.max_k, causal=causal,
                                             skip_threshold=thr, return_lse=True, return_skip_map=True)
     # the same call without a map (the timed configuration) gives the same output
-    o2, _, _ = attn.attn_prefill_varlen(x.q, x.k, x.v, x.cu_q, x.cu_k, x.max_q, x.max_k, causal=True,
+    o2, _, _ = attn.attn_prefill_varlen(x.q, x.k, x.v, x.cu_q, x.cu_k, x.max_q, x.max_k, causal=causal,
                                         skip_threshold=thr)
     torch.cuda.synchronize()
     assert torch.equal(o, o2)
@@ -92,11 +94,11 @@ def test_full_skip_prefill_sampled_rows(prefill_hot, thr):
     r = np.array(rows)
     gm = g[r[:, 0], r[:, 1]]
     qc, kc, vc = x.q.cpu(), x.k.cpu(), x.v.cpu()
-    _, _, om = oracle.prefill(qc, kc, vc, x.cu_q.cpu(), x.cu_k.cpu(), x.Hq, x.Hkv, x.scale, True, mode="skip",
+    _, _, om = oracle.prefill(qc, kc, vc, x.cu_q.cpu(), x.cu_k.cpu(), x.Hq, x.Hkv, x.scale, causal, mode="skip",
                               thr=thr, rows=rows, stride=g.shape[-1])
     _check_map(gm, om)
     assert (gm == 1).sum() / (gm != 2).sum() > 0.3, "the hot-key prefill input should make tiles skippable"
-    od, ld, _ = oracle.prefill(qc, kc, vc, x.cu_q.cpu(), x.cu_k.cpu(), x.Hq, x.Hkv, x.scale, True, mode="skip",
+    od, ld, _ = oracle.prefill(qc, kc, vc, x.cu_q.cpu(), x.cu_k.cpu(), x.Hq, x.Hkv, x.scale, causal, mode="skip",
                                rows=rows, replay=np.where(gm == 2, 0, gm), stride=g.shape[-1])
     assert np.max(np.abs(on[r[:, 0], r[:, 1]] - od)) <= BF16_TOL
     assert np.max(np.abs(ln[r[:, 0], r[:, 1]] - ld)) <= LSE_TOL
@@ -220,9 +222,10 @@ def test_full_smallseq_all_rows():
     x = W.smallseq_cross(seed=1004, device=DEV)              # B 30720, s_kv in {2..16}, H 16, D 128
     o, w, lse = attn.attn_smallseq_cross(x.q, x.k, x.v, x.cu_kv, x.max_s, return_lse=True)
     torch.cuda.synchronize()
-    od, wd = oracle.smallseq(x.q.cpu(), x.k.cpu(), x.v.cpu(), x.cu_kv.cpu(), x.max_s, x.scale)
+    od, wd, ld = oracle.smallseq(x.q.cpu(), x.k.cpu(), x.v.cpu(), x.cu_kv.cpu(), x.max_s, x.scale, with_lse=True)
     assert np.max(np.abs(_np(o) - od)) <= BF16_TOL
     assert np.max(np.abs(_np(w) - wd)) <= BF16_TOL
+    assert np.max(np.abs(_np(lse) - ld)) <= 1e-3
 
 
 def test_empty_batch_is_a_no_op():

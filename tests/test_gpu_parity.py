@@ -170,6 +170,53 @@ def test_prefill_bf16_causal_more_queries_than_keys(D, thr):
         assert np.all(o2n[~fin] == 0)
 
 
+@pytest.mark.parametrize("D", [128, 64])
+@pytest.mark.parametrize("thr", [0.01, 0.1])
+def test_prefill_bf16_noncausal_skip(D, thr):
+    # non-causal skip-softmax: every row visits every key tile of its sequence, the last one ragged.
+    # Lq != Lk, a sequence with no queries, one with queries but no keys, several query tiles and a
+    # ragged query tail; two hot 32-key runs per sequence make the tiles after them skippable.
+    Hq, Hkv = 8, 2
+    lq, lk = [37, 0, 130, 64, 5, 200], [300, 50, 97, 0, 517, 64]
+    gen = torch.Generator(device=DEV).manual_seed(13)
+    u = torch.randn(D, generator=gen, device=DEV)
+    u = u / u.norm()
+    q = (torch.randn(sum(lq), Hq, D, generator=gen, device=DEV) + 3 * u).bfloat16().contiguous()
+    k = torch.randn(sum(lk), Hkv, D, generator=gen, device=DEV)
+    v = torch.randn(sum(lk), Hkv, D, generator=gen, device=DEV).bfloat16().contiguous()
+    ck_l = [0] + list(np.cumsum(lk))
+    for b in range(len(lk)):
+        for t in (1, 4):
+            if 32 * (t + 1) <= lk[b]:
+                k[ck_l[b] + 32 * t:ck_l[b] + 32 * (t + 1)] += 15 * u
+    k = k.bfloat16().contiguous()
+    cq = torch.tensor([0] + list(np.cumsum(lq)), dtype=torch.int32, device=DEV)
+    ck = torch.tensor(ck_l, dtype=torch.int32, device=DEV)
+    print(f"non-causal skip prefill D {D} thr {thr}", flush=True)
+    o, lse, smap = attn.attn_prefill_varlen(q, k, v, cq, ck, max(lq), max(lk), causal=False, skip_threshold=thr,
+                                            return_lse=True, return_skip_map=True)
+    o2, _, _ = attn.attn_prefill_varlen(q, k, v, cq, ck, max(lq), max(lk), causal=False, skip_threshold=thr)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o2)  # writing the map does not change the result
+    g = smap.cpu().numpy()
+    scale = 1 / math.sqrt(D)
+    _, _, om = oracle.prefill(q.cpu(), k.cpu(), v.cpu(), cq.cpu(), ck.cpu(), Hq, Hkv, scale, False, mode="skip",
+                              thr=thr, stride=g.shape[-1])
+    _check_map(g, om)
+    assert (g == 1).mean() > 0.05, "the hot keys should make tiles skippable"
+    od, ld, _ = oracle.prefill(q.cpu(), k.cpu(), v.cpu(), cq.cpu(), ck.cpu(), Hq, Hkv, scale, False, mode="skip",
+                               replay=np.where(g == 2, 0, g).reshape(-1, g.shape[-1]), stride=g.shape[-1])
+    on, ln = _np(o), _np(lse)
+    assert np.max(np.abs(on - od)) <= BF16_TOL
+    fin = np.isfinite(ld)
+    assert np.array_equal(fin, np.isfinite(ln))
+    assert np.max(np.abs(ln[fin] - ld[fin])) <= 1e-3
+    assert np.all(on[~fin] == 0)
+    # rows of the sequence with no keys: nothing visited, o = 0, lse = -inf
+    r0 = sum(lq[:3])
+    assert np.all(g[r0:r0 + lq[3]] == 2) and np.all(on[r0:r0 + lq[3]] == 0)
+
+
 def test_prefill_bf16_skip_replay():
     lens = [300, 517, 64]
     x = W.varlen_prefill(seed=41, device=DEV, lengths=lens, Hq=4, Hkv=1, D=128)
@@ -303,10 +350,13 @@ def test_smallseq(fixed):
     o, w, lse = attn.attn_smallseq_cross(x.q, x.k, x.v, x.cu_kv, x.max_s, return_lse=True)
     torch.cuda.synchronize()
     rows = [(b, h) for b in range(0, 3000, 7) for h in range(16)]
-    oo, ow = oracle.smallseq(x.q.cpu(), x.k.cpu(), x.v.cpu(), x.cu_kv.cpu(), x.max_s, x.scale, rows=rows)
+    oo, ow, ol = oracle.smallseq(x.q.cpu(), x.k.cpu(), x.v.cpu(), x.cu_kv.cpu(), x.max_s, x.scale, rows=rows,
+                                 with_lse=True)
     r = np.array(rows)
     assert np.max(np.abs(_np(o)[r[:, 0], r[:, 1]] - oo)) <= BF16_TOL
     assert np.max(np.abs(_np(w)[r[:, 0], r[:, 1], 0] - ow)) <= BF16_TOL
+    # the fp32 LSE output: natural log of the row's sum of exp(logits)
+    assert np.max(np.abs(_np(lse)[r[:, 0], r[:, 1]] - ol)) <= 1e-3
     # padding weights are exactly zero
     s = x.lens.numpy()
     wn = _np(w)[:, :, 0]

@@ -100,17 +100,24 @@ def test_skip_replay_imposes_decisions():
 
 def test_smallseq_matches_brute_force():
     x = W.smallseq_cross(seed=5, B=6, H=3, D=8)
-    o, w = oracle.smallseq(x.q, x.k, x.v, x.cu_kv, x.max_s, 0.3)
+    o, w, lse = oracle.smallseq(x.q, x.k, x.v, x.cu_kv, x.max_s, 0.3, with_lse=True)
     q, k, v = _f64(x.q), _f64(x.k), _f64(x.v)
     cu = x.cu_kv.numpy()
     for b in range(6):
         for h in range(3):
             keys = [list(k[j, h]) for j in range(cu[b], cu[b + 1])]
             vals = [list(v[j, h]) for j in range(cu[b], cu[b + 1])]
-            ob, _, p = brute.softmax_attend(brute.scores(list(q[b, h]), keys, 0.3), vals)
+            ob, lb, p = brute.softmax_attend(brute.scores(list(q[b, h]), keys, 0.3), vals)
             assert np.max(np.abs(o[b, h] - ob)) < TOL
             assert np.max(np.abs(w[b, h, 0, :len(p)] - p)) < TOL
             assert np.all(w[b, h, 0, len(p):] == 0)
+            assert abs(lse[b, h] - lb) < TOL
+    # the rows= form returns the same LSE per (b, head), and a sequence with no key gives -inf
+    _, _, lr = oracle.smallseq(x.q, x.k, x.v, x.cu_kv, x.max_s, 0.3, rows=[(5, 2), (0, 1)], with_lse=True)
+    assert lr[0] == lse[5, 2] and lr[1] == lse[0, 1]
+    cu0 = torch.tensor([0, 0], dtype=torch.int32)
+    o0, _, l0 = oracle.smallseq(x.q[:1], x.k, x.v, cu0, 16, 0.3, with_lse=True)
+    assert l0[0, 0] == -np.inf and np.all(o0 == 0)
 
 
 # ---------------------------------------------------------------- library special case
