@@ -29,7 +29,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
-FLUSH_BYTES = 512 << 20     # written between timed calls: twice the 256 MB last-level cache
+FLUSH_BYTES = 512 << 20     # read between timed calls: twice the 256 MB last-level cache
 
 
 def _parse():
@@ -224,13 +224,14 @@ def main():
     nxt = {k: _logged(k, f) for k, f in nxt.items()}
     names = list(calls)
     stream = torch.cuda.current_stream()
-    # Between timed calls (outside each event pair) a 512 MiB buffer is written, which evicts the inputs
-    # the previous call streamed from the L2s (4 MB per XCD) and the 256 MB last-level cache, so every
-    # call starts cold.
-    flush_buf = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
+    # Between timed calls (outside each event pair) a 512 MiB buffer is read, which evicts what the
+    # previous call left in the L2s (4 MB per XCD) and the 256 MB last-level cache, so every call starts
+    # cold.  A read, not a write: written lines would stay dirty in the caches and their write-back would
+    # land inside the next timed call (measured: +5 to +14 % on the HBM-bound kernels).
+    flush_buf = torch.ones(FLUSH_BYTES // 4, dtype=torch.int32, device=dev)
 
     def flush():
-        flush_buf.fill_(0)
+        flush_buf.sum()
 
     def step(record):
         for nm in names:
@@ -946,8 +947,8 @@ def _summarize_mfma(base, durs):
              "# commands (repository root, TMPDIR=/tmp; the summary step runs on any host):",
              "\n".join(f"#   {k}: {v.format(out=base)}" for k, v in PROFILE_COMMANDS.items()),
              "# MfmaUtil = 100 * sum(SQ_VALU_MFMA_BUSY_CYCLES) / (max(GRBM_GUI_ACTIVE) * SIMDs); executed FLOP =",
-             "# SQ_INSTS_VALU_MFMA_MOPS_BF16 * 512 (includes masked and recomputed work); clock = SQ_BUSY_CYCLES /",
-             "# the kernel's mean duration in the trace run", ""]
+             "# SQ_INSTS_VALU_MFMA_MOPS_BF16 * 512 (includes masked and recomputed work); SQ_BUSY_CYCLES as the",
+             "# counter reports it (aggregated over the shader engines)", ""]
     for k in MFMA_KERNELS:
         if k not in util:
             continue
@@ -965,9 +966,6 @@ def _summarize_mfma(base, durs):
                     ln += f", executed bf16 MFMA {np.mean(bm[role]) * 512:.4e} FLOP per launch"
                 if role in bb:
                     ln += f", SQ_BUSY_CYCLES {np.mean(bb[role]):.0f}"
-                    if k in durs:
-                        ln += f" (~{np.mean(bb[role]) / (np.mean(durs[k]) * 1e-9) / 1e9:.2f} GHz over the mean " \
-                              f"trace duration)"
                 lines.append(ln)
     path = os.path.join(ROOT, "profiles", "mfma_busy.bench_workloads.txt")
     with open(path, "w") as f:

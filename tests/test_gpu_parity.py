@@ -188,7 +188,7 @@ def test_prefill_bf16_noncausal_skip(D, thr):
     for b in range(len(lk)):
         for t in (1, 4):
             if 32 * (t + 1) <= lk[b]:
-                k[ck_l[b] + 32 * t:ck_l[b] + 32 * (t + 1)] += 15 * u
+                k[ck_l[b] + 32 * t:ck_l[b] + 32 * (t + 1)] += 25 * u
     k = k.bfloat16().contiguous()
     cq = torch.tensor([0] + list(np.cumsum(lq)), dtype=torch.int32, device=DEV)
     ck = torch.tensor(ck_l, dtype=torch.int32, device=DEV)
@@ -203,7 +203,7 @@ def test_prefill_bf16_noncausal_skip(D, thr):
     _, _, om = oracle.prefill(q.cpu(), k.cpu(), v.cpu(), cq.cpu(), ck.cpu(), Hq, Hkv, scale, False, mode="skip",
                               thr=thr, stride=g.shape[-1])
     _check_map(g, om)
-    assert (g == 1).mean() > 0.05, "the hot keys should make tiles skippable"
+    assert (g == 1).sum() / (g != 2).sum() > 0.2, "the hot keys should make tiles skippable"
     od, ld, _ = oracle.prefill(q.cpu(), k.cpu(), v.cpu(), cq.cpu(), ck.cpu(), Hq, Hkv, scale, False, mode="skip",
                                replay=np.where(g == 2, 0, g).reshape(-1, g.shape[-1]), stride=g.shape[-1])
     on, ln = _np(o), _np(lse)
