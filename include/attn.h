@@ -114,6 +114,28 @@ attn_status_t attn_decode_paged(const void *q, const void *k_cache, const void *
                                 float *lse, uint8_t *skip_map, int32_t skip_map_stride, void *stream);
 
 /*
+ * attn_decode_paged for callers that cannot allocate device memory: code under HIP graph capture,
+ * tight serving loops and harnesses that forbid allocation.  Same arguments, layouts, schedules,
+ * kernels and results as attn_decode_paged, minus the workspace: the split-K partials
+ * (B * Hq * num_splits * (D + 1) * 4 bytes) go to a scratch array that the library keeps in device
+ * memory, ATTN_NOALLOC_SCRATCH_BYTES per GPU it runs on, held until the process ends.  A call that
+ * would need more returns ATTN_ERR_WORKSPACE before any HIP call (e.g. 64 MiB covers B = 64, Hq = 32
+ * with the default 32 splits, 33.8 MB).  The sequential schedule (num_splits == 1) uses no scratch.
+ * The scratch used is the one of the calling thread's current device, so `stream` must belong to
+ * that device.  The call allocates nothing (the first call on a device looks the scratch address up
+ * once).  Every call on one GPU shares that GPU's scratch and it keeps the last call's contents:
+ * calls that overlap on one GPU (different streams, or different threads) race and must be
+ * serialized by the caller; calls on one stream are ordered and safe.
+ */
+#define ATTN_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+attn_status_t attn_decode_paged_noalloc(const void *q, const void *k_cache, const void *v_cache,
+                                        const int32_t *block_table, const int32_t *seq_lens, int32_t B, int32_t Hq,
+                                        int32_t Hkv, int32_t D, int32_t page_size, int32_t num_pages,
+                                        int32_t max_pages_per_seq, float scale, float skip_threshold,
+                                        int32_t num_splits, void *o, float *lse, uint8_t *skip_map,
+                                        int32_t skip_map_stride, void *stream);
+
+/*
  * One-token paged decode with NVFP4 fake quantization of P and V ("Model-Optimizer: Add split-k decode
  * kernel for skip softmax", What does this PR do: skip-softmax together with NVFP4 P/V quantize-dequantize
  * in the sequential schedule; Usage: p_qdq / v_qdq with p_qdq_amax / v_qdq_amax).  The sequential

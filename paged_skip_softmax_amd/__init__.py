@@ -15,10 +15,11 @@ import math
 import torch
 
 from . import _lib
-from ._lib import SKIP_TILE, AttnError  # noqa: F401
+from ._lib import NOALLOC_SCRATCH_BYTES, SKIP_TILE, AttnError  # noqa: F401
 
 __all__ = ["attn_prefill_varlen", "attn_prefill_varlen_backward", "attn_prefill_varlen_backward_workspace_size",
-           "attn_decode_paged", "attn_decode_paged_workspace_size", "attn_decode_paged_qdq", "attn_decode_paged_multi",
+           "attn_decode_paged", "attn_decode_paged_workspace_size", "attn_decode_paged_noalloc",
+           "attn_decode_paged_qdq", "attn_decode_paged_multi",
            "attn_decode_paged_multi_workspace_size", "attn_smallseq_cross",
            "attn_smallseq_cross_backward", "AttnError", "SKIP_TILE"]
 
@@ -165,6 +166,47 @@ def attn_decode_paged(q, k_cache, v_cache, block_table, seq_lens, *, scale=None,
                                      float(skip_threshold), int(splits), _ptr(workspace), ws_bytes, out.data_ptr(),
                                      _ptr(lse), _ptr(smap), stride, _stream(q)))
     return out, lse, smap
+
+
+def attn_decode_paged_noalloc(q, k_cache, v_cache, block_table, seq_lens, *, scale=None, skip_threshold=0.0,
+                              num_splits=0, out, lse=None, skip_map=None):
+    """attn_decode_paged for callers that cannot allocate: the split-K partials go to the library's own
+    per-GPU scratch (NOALLOC_SCRATCH_BYTES).  Every output is caller-allocated (``out`` [B, Hq, D] bf16,
+    optional ``lse`` [B, Hq] fp32 and ``skip_map`` [B, Hq, stride] uint8); nothing is allocated here.
+    Calls that overlap on one GPU share the scratch and race.  Returns (out, lse, skip_map)."""
+    lib = _lib.load()
+    dev = q.device
+    _cuda_contig("q", q, torch.bfloat16)
+    for name, t in (("k_cache", k_cache), ("v_cache", v_cache)):
+        _cuda_contig(name, t, torch.bfloat16, dev)
+    _cuda_contig("block_table", block_table, torch.int32, dev)
+    _cuda_contig("seq_lens", seq_lens, torch.int32, dev)
+    _need(q.dim() == 3 and k_cache.dim() == 4 and k_cache.shape == v_cache.shape,
+          "q [B,Hq,D], caches [pages,Hkv,page,D]")
+    B, Hq, D = q.shape
+    num_pages, Hkv, page, Dk = k_cache.shape
+    _need(Dk == D, "head dims differ")
+    _need(block_table.dim() == 2 and block_table.shape[0] == B and seq_lens.shape == (B,),
+          "block_table [B, max_pages], seq_lens [B]")
+    max_pages = block_table.shape[1]
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    _cuda_contig("out", out, torch.bfloat16, dev)
+    _need(out.shape == q.shape, "out must match q")
+    if lse is not None:
+        _cuda_contig("lse", lse, torch.float32, dev)
+        _need(lse.shape == (B, Hq), "lse must be [B, Hq]")
+    stride = 0
+    if skip_map is not None:
+        _cuda_contig("skip_map", skip_map, torch.uint8, dev)
+        _need(skip_map.dim() == 3 and skip_map.shape[:2] == (B, Hq), "skip_map must be [B, Hq, stride]")
+        stride = skip_map.shape[2]
+    _lib.check(lib.attn_decode_paged_noalloc(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+                                             block_table.data_ptr(), seq_lens.data_ptr(), B, Hq, Hkv, D, page,
+                                             num_pages, max_pages, float(scale), float(skip_threshold),
+                                             int(num_splits), out.data_ptr(), _ptr(lse), _ptr(skip_map), stride,
+                                             _stream(q)))
+    return out, lse, skip_map
 
 
 def attn_decode_paged_qdq(q, k_cache, v_cache, block_table, seq_lens, *, scale=None, skip_threshold=0.0,

@@ -10,6 +10,7 @@ LIB_PATH = os.path.join(HERE, "libattn.so")
 ATTN_OK, ATTN_ERR_INVALID, ATTN_ERR_UNSUPPORTED, ATTN_ERR_WORKSPACE, ATTN_ERR_HIP = range(5)
 ATTN_F32, ATTN_BF16 = 0, 1
 SKIP_TILE = 32
+NOALLOC_SCRATCH_BYTES = 64 << 20  # ATTN_NOALLOC_SCRATCH_BYTES
 
 # name -> (restype, argtypes), mirroring include/attn.h
 _P, _I, _F, _Z = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
@@ -19,6 +20,8 @@ SIGNATURES = {
     "attn_decode_paged_workspace_size": (_Z, [_I, _I, _I, _I]),
     "attn_decode_paged": (ctypes.c_int, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _F, _I, _P, _Z, _P, _P,
                                          _P, _I, _P]),
+    "attn_decode_paged_noalloc": (ctypes.c_int, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _F, _I, _P, _P,
+                                                 _P, _I, _P]),
     "attn_decode_paged_qdq": (ctypes.c_int, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _F, _F, _F, _P,
                                              _P, _P, _I, _P]),
     "attn_decode_paged_multi_workspace_size": (_Z, [_I, _I, _I, _I, _I, _I]),

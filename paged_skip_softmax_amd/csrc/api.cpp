@@ -8,6 +8,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 #include <string>
 
 #include "launch.h"
@@ -86,51 +87,100 @@ size_t attn_decode_paged_workspace_size(int32_t B, int32_t Hq, int32_t D, int32_
     return (size_t)B * Hq * S * ((size_t)D + 1) * sizeof(float);
 }
 
-attn_status_t attn_decode_paged(const void *q, const void *k_cache, const void *v_cache,
-                                const int32_t *block_table, const int32_t *seq_lens, int32_t B, int32_t Hq,
-                                int32_t Hkv, int32_t D, int32_t page_size, int32_t num_pages,
-                                int32_t max_pages_per_seq, float scale, float skip_threshold,
-                                int32_t num_splits, void *workspace, size_t workspace_bytes, void *o,
-                                float *lse, uint8_t *skip_map, int32_t skip_map_stride, void *stream)
+} // extern "C"
+
+namespace {
+
+// Scratch memory of attn_decode_paged_noalloc: file-scope device memory, one copy per GPU the library
+// runs on, held until the process ends.  In host code `scratch` is only a host-side handle: every use
+// goes through the device address hipGetSymbolAddress returns for the current device.
+constexpr size_t kScratchBytes = ATTN_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxScratchDevices];
+
+// Device address of the current device's copy of `scratch`, looked up once per device.
+attn_status_t current_scratch(void **ptr)
+{
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return fail(ATTN_ERR_HIP, "attn_decode_paged_noalloc: hipGetDevice: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxScratchDevices)
+        return fail(ATTN_ERR_UNSUPPORTED, "attn_decode_paged_noalloc: device %d beyond %d", dev, kMaxScratchDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p)
+            return fail(ATTN_ERR_HIP, "attn_decode_paged_noalloc: hipGetSymbolAddress(scratch): %s",
+                        hipGetErrorString(e));
+        g_scratch_ptr[dev] = p;
+    }
+    *ptr = g_scratch_ptr[dev];
+    return ATTN_OK;
+}
+
+// attn_decode_paged with its split-K partials in `workspace`; when use_scratch is set the workspace
+// arguments are ignored and the current device's scratch (kScratchBytes) takes their place.
+attn_status_t decode_paged(const char *fn, const void *q, const void *k_cache, const void *v_cache,
+                           const int32_t *block_table, const int32_t *seq_lens, int32_t B, int32_t Hq, int32_t Hkv,
+                           int32_t D, int32_t page_size, int32_t num_pages, int32_t max_pages_per_seq, float scale,
+                           float skip_threshold, int32_t num_splits, bool use_scratch, void *workspace,
+                           size_t workspace_bytes, void *o, float *lse, uint8_t *skip_map, int32_t skip_map_stride,
+                           void *stream)
 {
     if (B < 0)
-        return fail(ATTN_ERR_INVALID, "attn_decode_paged: B = %d < 0", B);
+        return fail(ATTN_ERR_INVALID, "%s: B = %d < 0", fn, B);
     if (Hq <= 0 || Hkv <= 0 || Hq % Hkv)
-        return fail(ATTN_ERR_INVALID, "attn_decode_paged: Hq = %d must be a positive multiple of Hkv = %d", Hq, Hkv);
+        return fail(ATTN_ERR_INVALID, "%s: Hq = %d must be a positive multiple of Hkv = %d", fn, Hq, Hkv);
     if (bad_threshold(skip_threshold))
-        return fail(ATTN_ERR_INVALID, "attn_decode_paged: skip_threshold %g outside [0, 1]", (double)skip_threshold);
+        return fail(ATTN_ERR_INVALID, "%s: skip_threshold %g outside [0, 1]", fn, (double)skip_threshold);
     if (num_splits < 0 || num_splits > kMaxSplits)
-        return fail(ATTN_ERR_INVALID, "attn_decode_paged: num_splits %d outside [0, %d]", num_splits, kMaxSplits);
+        return fail(ATTN_ERR_INVALID, "%s: num_splits %d outside [0, %d]", fn, num_splits, kMaxSplits);
     const int S = resolve_splits(num_splits, skip_threshold);
     if (skip_threshold > 0.f && S > 1)
-        return fail(ATTN_ERR_INVALID, "attn_decode_paged: skip_threshold > 0 needs one sequential split, got %d", S);
+        return fail(ATTN_ERR_INVALID, "%s: skip_threshold > 0 needs one sequential split, got %d", fn, S);
     if (bad_scale(scale))
-        return fail(ATTN_ERR_INVALID, "attn_decode_paged: scale must be positive and finite");
+        return fail(ATTN_ERR_INVALID, "%s: scale must be positive and finite", fn);
     if (num_pages <= 0 || max_pages_per_seq <= 0 || page_size <= 0)
-        return fail(ATTN_ERR_INVALID, "attn_decode_paged: num_pages, max_pages_per_seq and page_size must be > 0");
+        return fail(ATTN_ERR_INVALID, "%s: num_pages, max_pages_per_seq and page_size must be > 0", fn);
     if (skip_map && S > 1)
-        return fail(ATTN_ERR_INVALID, "attn_decode_paged: skip_map needs the sequential schedule (num_splits = 1)");
+        return fail(ATTN_ERR_INVALID, "%s: skip_map needs the sequential schedule (num_splits = 1)", fn);
     if (skip_map && (int64_t)skip_map_stride * attn::kSkipTile < (int64_t)max_pages_per_seq * page_size)
-        return fail(ATTN_ERR_INVALID, "attn_decode_paged: skip_map_stride %d < ceil(max_pages_per_seq * page_size / 32)",
+        return fail(ATTN_ERR_INVALID, "%s: skip_map_stride %d < ceil(max_pages_per_seq * page_size / 32)", fn,
                     skip_map_stride);
     if (D != 128)
-        return fail(ATTN_ERR_UNSUPPORTED, "attn_decode_paged: D = %d (built for 128)", D);
+        return fail(ATTN_ERR_UNSUPPORTED, "%s: D = %d (built for 128)", fn, D);
     if (page_size != 16)
-        return fail(ATTN_ERR_UNSUPPORTED, "attn_decode_paged: page_size = %d (built for 16)", page_size);
+        return fail(ATTN_ERR_UNSUPPORTED, "%s: page_size = %d (built for 16)", fn, page_size);
     if (Hq / Hkv > 16)
-        return fail(ATTN_ERR_UNSUPPORTED, "attn_decode_paged: Hq / Hkv = %d > 16", Hq / Hkv);
+        return fail(ATTN_ERR_UNSUPPORTED, "%s: Hq / Hkv = %d > 16", fn, Hq / Hkv);
     if (B > kMaxGridYZ)
-        return fail(ATTN_ERR_UNSUPPORTED, "attn_decode_paged: B = %d above %d (a grid dimension)", B, (int)kMaxGridYZ);
+        return fail(ATTN_ERR_UNSUPPORTED, "%s: B = %d above %d (a grid dimension)", fn, B, (int)kMaxGridYZ);
     if (B == 0)
         return ok();
     if (!q || !k_cache || !v_cache || !block_table || !seq_lens || !o)
-        return fail(ATTN_ERR_INVALID, "attn_decode_paged: a required pointer is NULL");
+        return fail(ATTN_ERR_INVALID, "%s: a required pointer is NULL", fn);
     const float scale_log2 = scale * 1.4426950408889634f;
     hipStream_t st = static_cast<hipStream_t>(stream);
     if (S > 1) {
         const size_t need = attn_decode_paged_workspace_size(B, Hq, D, S);
+        if (use_scratch) {
+            // checked before any HIP call, like every other argument
+            if (need > kScratchBytes)
+                return fail(ATTN_ERR_WORKSPACE, "%s: the split-K partials need %zu bytes, above the %zu-byte scratch "
+                                                "(B * Hq * num_splits * (D + 1) * 4 must stay within it)", fn, need,
+                            kScratchBytes);
+            const attn_status_t sc = current_scratch(&workspace);
+            if (sc != ATTN_OK)
+                return sc;
+            workspace_bytes = kScratchBytes;
+        }
         if (!workspace || workspace_bytes < need)
-            return fail(ATTN_ERR_WORKSPACE, "attn_decode_paged: workspace %zu bytes, need %zu", workspace_bytes, need);
+            return fail(ATTN_ERR_WORKSPACE, "%s: workspace %zu bytes, need %zu", fn, workspace_bytes, need);
         attn::SplitArgs a{};
         a.q = static_cast<const uint16_t *>(q);
         a.kc = static_cast<const uint16_t *>(k_cache);
@@ -164,6 +214,34 @@ attn_status_t attn_decode_paged(const void *q, const void *k_cache, const void *
     a.skip_map = skip_map;
     a.map_stride = skip_map_stride;
     return hip_status(attn::launch_decode_seq(a, B, st), "decode sequential launch");
+}
+
+} // namespace
+
+extern "C" {
+
+attn_status_t attn_decode_paged(const void *q, const void *k_cache, const void *v_cache,
+                                const int32_t *block_table, const int32_t *seq_lens, int32_t B, int32_t Hq,
+                                int32_t Hkv, int32_t D, int32_t page_size, int32_t num_pages,
+                                int32_t max_pages_per_seq, float scale, float skip_threshold,
+                                int32_t num_splits, void *workspace, size_t workspace_bytes, void *o,
+                                float *lse, uint8_t *skip_map, int32_t skip_map_stride, void *stream)
+{
+    return decode_paged("attn_decode_paged", q, k_cache, v_cache, block_table, seq_lens, B, Hq, Hkv, D, page_size,
+                        num_pages, max_pages_per_seq, scale, skip_threshold, num_splits, false, workspace,
+                        workspace_bytes, o, lse, skip_map, skip_map_stride, stream);
+}
+
+attn_status_t attn_decode_paged_noalloc(const void *q, const void *k_cache, const void *v_cache,
+                                        const int32_t *block_table, const int32_t *seq_lens, int32_t B, int32_t Hq,
+                                        int32_t Hkv, int32_t D, int32_t page_size, int32_t num_pages,
+                                        int32_t max_pages_per_seq, float scale, float skip_threshold,
+                                        int32_t num_splits, void *o, float *lse, uint8_t *skip_map,
+                                        int32_t skip_map_stride, void *stream)
+{
+    return decode_paged("attn_decode_paged_noalloc", q, k_cache, v_cache, block_table, seq_lens, B, Hq, Hkv, D,
+                        page_size, num_pages, max_pages_per_seq, scale, skip_threshold, num_splits, true, nullptr, 0,
+                        o, lse, skip_map, skip_map_stride, stream);
 }
 
 attn_status_t attn_decode_paged_qdq(const void *q, const void *k_cache, const void *v_cache,

@@ -282,3 +282,26 @@ def test_python_binding_checks_out_shapes():
             attn.attn_decode_paged_multi(q, cu, 1, kc, kc, bt, sl, out=bad)
         with pytest.raises(ValueError, match="out"):
             attn.attn_smallseq_cross(q, q, q, cu, 1, out=bad)
+
+
+def test_decode_noalloc_validation(lib):
+    """The allocation-free decode: the decode's argument checks, and partials beyond the scratch rejected
+    with ATTN_ERR_WORKSPACE, all before any HIP call."""
+    def call(**kw):
+        a = dict(q=FAKE, kc=FAKE, vc=FAKE, bt=FAKE, sl=FAKE, B=2, Hq=8, Hkv=2, D=128, page=16, pages=100, maxp=10,
+                 scale=0.1, thr=0.0, splits=0, o=FAKE, lse=None, map=None, stride=5, stream=None)
+        a.update(kw)
+        return lib.attn_decode_paged_noalloc(a["q"], a["kc"], a["vc"], a["bt"], a["sl"], a["B"], a["Hq"], a["Hkv"],
+                                             a["D"], a["page"], a["pages"], a["maxp"], a["scale"], a["thr"],
+                                             a["splits"], a["o"], a["lse"], a["map"], a["stride"], a["stream"])
+    assert _lib.NOALLOC_SCRATCH_BYTES == 64 << 20
+    assert call(B=-1) == INVALID
+    assert call(scale=0.0) == INVALID
+    assert call(thr=0.1, splits=32) == INVALID
+    assert call(D=64) == UNSUPPORTED
+    assert call(q=None) == INVALID
+    assert call(B=0) == _lib.ATTN_OK
+    # 128 x 32 heads x 32 splits x 129 floats = 67.6 MB > 64 MiB; 64 rows fit (33.8 MB)
+    assert call(B=128, Hq=32, Hkv=8) == WORKSPACE
+    assert b"scratch" in lib.attn_last_error_message()
+    assert call(B=64, Hq=32, Hkv=8, splits=64) == WORKSPACE
