@@ -51,10 +51,13 @@ typedef enum {
     ATTN_ERR_INVALID = 1,     /* bad argument value or a required pointer is NULL            */
     ATTN_ERR_UNSUPPORTED = 2, /* valid request this build has no kernel for (dtype, D, page) */
     ATTN_ERR_WORKSPACE = 3,   /* workspace missing or smaller than the size query returned   */
-    ATTN_ERR_HIP = 4          /* the HIP runtime reported an error while launching           */
+    ATTN_ERR_HIP = 4,         /* the HIP runtime reported an error while launching           */
+    ATTN_STATUS_INT_RANGE = 0x7fffffff /* not a status: makes every int32 a value of the type   */
 } attn_status_t;
 
-typedef enum { ATTN_F32 = 0, ATTN_BF16 = 1 } attn_dtype_t;
+/* ATTN_DTYPE_INT_RANGE is not a dtype: it makes every int32 a value of the type, so that a code a C
+ * caller passes outside {0, 1} is well defined in the library and rejected (ATTN_ERR_INVALID). */
+typedef enum { ATTN_F32 = 0, ATTN_BF16 = 1, ATTN_DTYPE_INT_RANGE = 0x7fffffff } attn_dtype_t;
 
 /* Width of the tiles skip decisions are taken on, in keys. */
 #define ATTN_SKIP_TILE 32

@@ -14,7 +14,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 OBJ = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libattn.so")
-SOURCES = ["decode.hip", "smallseq.hip", "prefill.hip", "prefill_d128.hip", "prefill_bwd.hip", "api.cpp"]
+SOURCES = ["decode.hip", "smallseq.hip", "prefill.hip", "prefill_d128.hip", "prefill_bwd.hip", "check.hip", "api.cpp"]
 ARCH = "gfx950"
 
 # Packed fp32 VALU forms are kept out of the generated code (the compiler would otherwise form them

@@ -8,6 +8,8 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
+#include <cstring>
 #include <mutex>
 #include <string>
 
@@ -17,6 +19,13 @@ namespace {
 
 thread_local std::string g_last_error;
 
+// A diagnostics switch: set, non-empty and not "0".
+bool env_on(const char *name)
+{
+    const char *v = std::getenv(name);
+    return v && v[0] && std::strcmp(v, "0") != 0;
+}
+
 attn_status_t fail(attn_status_t s, const char *fmt, ...)
 {
     char buf[512];
@@ -25,6 +34,8 @@ attn_status_t fail(attn_status_t s, const char *fmt, ...)
     vsnprintf(buf, sizeof buf, fmt, ap);
     va_end(ap);
     g_last_error = buf;
+    if (attn::log_enabled())
+        std::fprintf(stderr, "[attn] rejected (status %d): %s\n", (int)s, buf);
     return s;
 }
 
@@ -39,6 +50,60 @@ attn_status_t hip_status(hipError_t e, const char *what)
     if (e != hipSuccess)
         return fail(ATTN_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
     return ok();
+}
+
+const char *check_what(int code)
+{
+    switch (code) {
+    case attn::kCheckCuA + 0: return "cu_seqlens (queries / kv) does not start at 0";
+    case attn::kCheckCuA + 1: return "cu_seqlens (queries / kv) decreases";
+    case attn::kCheckCuA + 2: return "a sequence is longer than max_seqlen (queries / kv)";
+    case attn::kCheckCuA + 3: return "cu_seqlens_q[B] differs from total_q";
+    case attn::kCheckCuB + 0: return "cu_seqlens_k does not start at 0";
+    case attn::kCheckCuB + 1: return "cu_seqlens_k decreases";
+    case attn::kCheckCuB + 2: return "a sequence has more keys than max_seqlen_k";
+    case attn::kCheckSeqLen: return "seq_lens outside [0, max_pages_per_seq * page_size]";
+    case attn::kCheckPage: return "a block-table entry of a visible page is outside [0, num_pages)";
+    }
+    return "unknown check failure";
+}
+
+// ATTN_CHECK=1: the call's index arrays are validated on the device (on the call's stream, which is
+// then synchronized) before anything else is launched; a failure rejects the call.
+attn_status_t device_check(const char *fn, const attn::CheckSpec &spec, void *stream)
+{
+    if (!env_on("ATTN_CHECK"))
+        return ATTN_OK;
+    attn::CheckResult r{};
+    const hipError_t e = attn::check_indices(spec, static_cast<hipStream_t>(stream), &r);
+    if (e != hipSuccess)
+        return fail(ATTN_ERR_HIP, "%s: ATTN_CHECK: %s", fn, hipGetErrorString(e));
+    if (r.code != 0)
+        return fail(ATTN_ERR_INVALID, "%s: ATTN_CHECK: %s (batch row %d)", fn, check_what(r.code), r.row);
+    return ATTN_OK;
+}
+
+attn::CheckSpec cu_spec(int B, const int32_t *cu_a, int max_a, int total_a, const int32_t *cu_b, int max_b)
+{
+    attn::CheckSpec c{};
+    c.B = B;
+    c.cu_a = cu_a;
+    c.max_a = max_a;
+    c.total_a = total_a;
+    c.cu_b = cu_b;
+    c.max_b = max_b;
+    return c;
+}
+
+attn::CheckSpec page_spec(attn::CheckSpec c, const int32_t *bt, const int32_t *seq_lens, int max_pages, int page,
+                          int num_pages)
+{
+    c.bt = bt;
+    c.seq_lens = seq_lens;
+    c.max_pages = max_pages;
+    c.page = page;
+    c.num_pages = num_pages;
+    return c;
 }
 
 bool bad_threshold(float thr) { return !(thr >= 0.f && thr <= 1.f); } // also rejects NaN
@@ -63,6 +128,18 @@ int resolve_splits(int num_splits, float thr) { return num_splits != 0 ? num_spl
 
 } // namespace
 
+namespace attn {
+
+bool log_enabled() { return env_on("ATTN_LOG"); }
+
+void log_launch(const char *kernel, dim3 grid, dim3 block)
+{
+    std::fprintf(stderr, "[attn] launch %s grid (%u, %u, %u) block (%u, %u, %u)\n", kernel, grid.x, grid.y, grid.z,
+                 block.x, block.y, block.z);
+}
+
+} // namespace attn
+
 extern "C" {
 
 const char *attn_status_string(attn_status_t s)
@@ -73,6 +150,7 @@ const char *attn_status_string(attn_status_t s)
     case ATTN_ERR_UNSUPPORTED: return "unsupported configuration";
     case ATTN_ERR_WORKSPACE: return "workspace too small";
     case ATTN_ERR_HIP: return "HIP runtime error";
+    default: break;
     }
     return "unknown status";
 }
@@ -166,14 +244,23 @@ attn_status_t decode_paged(const char *fn, const void *q, const void *k_cache, c
         return fail(ATTN_ERR_INVALID, "%s: a required pointer is NULL", fn);
     const float scale_log2 = scale * 1.4426950408889634f;
     hipStream_t st = static_cast<hipStream_t>(stream);
+    if (S > 1 && use_scratch && attn_decode_paged_workspace_size(B, Hq, D, S) > kScratchBytes)
+        return fail(ATTN_ERR_WORKSPACE, "%s: the split-K partials need %zu bytes, above the %zu-byte scratch "
+                                        "(B * Hq * num_splits * (D + 1) * 4 must stay within it)", fn,
+                    attn_decode_paged_workspace_size(B, Hq, D, S), kScratchBytes);
+    if (S > 1 && !use_scratch && (!workspace || workspace_bytes < attn_decode_paged_workspace_size(B, Hq, D, S)))
+        return fail(ATTN_ERR_WORKSPACE, "%s: workspace %zu bytes, need %zu", fn, workspace_bytes,
+                    attn_decode_paged_workspace_size(B, Hq, D, S));
+    {
+        const attn_status_t c = device_check(
+            fn, page_spec(cu_spec(B, nullptr, 0, -1, nullptr, 0), block_table, seq_lens, max_pages_per_seq, page_size,
+                          num_pages), stream);
+        if (c != ATTN_OK)
+            return c;
+    }
     if (S > 1) {
         const size_t need = attn_decode_paged_workspace_size(B, Hq, D, S);
-        if (use_scratch) {
-            // checked before any HIP call, like every other argument
-            if (need > kScratchBytes)
-                return fail(ATTN_ERR_WORKSPACE, "%s: the split-K partials need %zu bytes, above the %zu-byte scratch "
-                                                "(B * Hq * num_splits * (D + 1) * 4 must stay within it)", fn, need,
-                            kScratchBytes);
+        if (use_scratch) { // its size was checked above, before any HIP call
             const attn_status_t sc = current_scratch(&workspace);
             if (sc != ATTN_OK)
                 return sc;
@@ -285,6 +372,14 @@ attn_status_t attn_decode_paged_qdq(const void *q, const void *k_cache, const vo
         return ok();
     if (!q || !k_cache || !v_cache || !block_table || !seq_lens || !o)
         return fail(ATTN_ERR_INVALID, "attn_decode_paged_qdq: a required pointer is NULL");
+    {
+        const attn_status_t c = device_check(
+            "attn_decode_paged_qdq",
+            page_spec(cu_spec(B, nullptr, 0, -1, nullptr, 0), block_table, seq_lens, max_pages_per_seq, page_size,
+                      num_pages), stream);
+        if (c != ATTN_OK)
+            return c;
+    }
     attn::SeqArgs a{};
     a.q = static_cast<const uint16_t *>(q);
     a.kc = static_cast<const uint16_t *>(k_cache);
@@ -353,6 +448,13 @@ attn_status_t attn_prefill_varlen_backward(attn_dtype_t dtype, const void *q, co
     if (need && (!workspace || workspace_bytes < need))
         return fail(ATTN_ERR_WORKSPACE, "attn_prefill_varlen_backward: workspace %zu bytes, need %zu", workspace_bytes,
                     need);
+    {
+        const attn_status_t c = device_check(
+            "attn_prefill_varlen_backward", cu_spec(B, cu_seqlens_q, max_seqlen_q, -1, cu_seqlens_k, max_seqlen_k),
+            stream);
+        if (c != ATTN_OK)
+            return c;
+    }
     attn::BwdArgs a{};
     a.q = q;
     a.k = k;
@@ -437,6 +539,26 @@ attn_status_t attn_decode_paged_multi(const void *q, const int32_t *cu_seqlens_q
         return fail(ATTN_ERR_INVALID, "attn_decode_paged_multi: a required pointer is NULL");
     const int G = Hq / Hkv;
     const bool skip = skip_threshold > 0.f || skip_map;
+    if (!skip && (int64_t)max_seqlen_q * G <= kMultiSplitRows) {
+        // the split-K schedule: its grid limit and workspace are checked before the device check
+        const int S0 = num_splits == 0 ? kDefaultSplits : num_splits;
+        const int ncb0 = std::max(1, (max_seqlen_q * G + 15) / 16);
+        if ((int64_t)B * ncb0 > kMaxGridYZ)
+            return fail(ATTN_ERR_UNSUPPORTED, "attn_decode_paged_multi: B * ceil(max_seqlen_q * Hq / Hkv / 16) = %lld "
+                                              "above %d (a grid dimension)", (long long)B * ncb0, (int)kMaxGridYZ);
+        const size_t need0 = attn_decode_paged_multi_workspace_size(total_q, max_seqlen_q, Hq, Hkv, D, S0);
+        if (!workspace || workspace_bytes < need0)
+            return fail(ATTN_ERR_WORKSPACE, "attn_decode_paged_multi: workspace %zu bytes, need %zu", workspace_bytes,
+                        need0);
+    }
+    {
+        const attn_status_t c = device_check(
+            "attn_decode_paged_multi",
+            page_spec(cu_spec(B, cu_seqlens_q, max_seqlen_q, total_q, nullptr, 0), block_table, seq_lens,
+                      max_pages_per_seq, page_size, num_pages), stream);
+        if (c != ATTN_OK)
+            return c;
+    }
     if (skip || (int64_t)max_seqlen_q * G > kMultiSplitRows) {
         // long query chunks, or skip-softmax: the prefill kernel with K / V tiles gathered page by page
         attn::PrefillArgs a{};
@@ -511,6 +633,12 @@ attn_status_t attn_smallseq_cross(const void *q, const void *k, const void *v, c
         return ok();
     if (!q || !k || !v || !cu_seqlens_kv || !o)
         return fail(ATTN_ERR_INVALID, "attn_smallseq_cross: a required pointer is NULL");
+    {
+        const attn_status_t c =
+            device_check("attn_smallseq_cross", cu_spec(B, cu_seqlens_kv, max_seqlen_kv, -1, nullptr, 0), stream);
+        if (c != ATTN_OK)
+            return c;
+    }
     attn::SmallArgs a{};
     a.q = static_cast<const uint16_t *>(q);
     a.k = static_cast<const uint16_t *>(k);
@@ -546,6 +674,12 @@ attn_status_t attn_smallseq_cross_backward(const void *q, const void *k, const v
         return ok();
     if (!q || !k || !v || !dout || !cu_seqlens_kv || !dq || !dk || !dv || (max_seqlen_kv > 0 && !attn_weights))
         return fail(ATTN_ERR_INVALID, "attn_smallseq_cross_backward: a required pointer is NULL");
+    {
+        const attn_status_t c = device_check("attn_smallseq_cross_backward",
+                                             cu_spec(B, cu_seqlens_kv, max_seqlen_kv, -1, nullptr, 0), stream);
+        if (c != ATTN_OK)
+            return c;
+    }
     attn::SmallBwdArgs a{};
     a.q = static_cast<const uint16_t *>(q);
     a.k = static_cast<const uint16_t *>(k);
@@ -598,6 +732,12 @@ attn_status_t attn_prefill_varlen(attn_dtype_t dtype, const void *q, const void 
         return ok();
     if (!q || !k || !v || !cu_seqlens_q || !cu_seqlens_k || !o)
         return fail(ATTN_ERR_INVALID, "attn_prefill_varlen: a required pointer is NULL");
+    {
+        const attn_status_t c = device_check(
+            "attn_prefill_varlen", cu_spec(B, cu_seqlens_q, max_seqlen_q, -1, cu_seqlens_k, max_seqlen_k), stream);
+        if (c != ATTN_OK)
+            return c;
+    }
     attn::PrefillArgs a{};
     a.q = q;
     a.k = k;

@@ -214,15 +214,37 @@ __device__ __forceinline__ uint4 qdq_v8(uint4 v, Nvfp4 f)
     return make_uint4(o[0], o[1], o[2], o[3]);
 }
 
-// Folds one chunk into the state.  keep == false (per lane, i.e. per head) leaves that head's state
-// untouched: p = 0 and no rescale.  cmax_l2: chunk max in log2 units.  Keys at or past tend have their
-// V zeroed in LDS so that 0 * NaN never reaches the accumulator.  vt: this wave's LDS tile.
-// QDQ: fake-quantize P (blocks of the 16 keys of a page, per head; the row sum takes the unquantized P)
-// and V (per key, blocks of 16 along D) as qq says.
+// Stages one chunk's V in the wave's LDS tile vt (keys at or past tend cleared, so that 0 * NaN never
+// reaches the accumulator), fake-quantized per key in blocks of 16 along D when qq.v_on (QDQ).
 template <bool QDQ = false>
-__device__ __forceinline__ void chunk_update(WaveState &st, const f32x4 sc[2], float cmax_l2, bool keep,
-                                             const uint4 vr[2][4], int tok0, int tend, float scale_log2,
-                                             uint16_t *vt, int lane, const Qdq &qq = Qdq{})
+__device__ __forceinline__ void stage_v(const uint4 vr[2][4], int tok0, int tend, uint16_t *vt, int lane,
+                                        const Qdq &qq = Qdq{})
+{
+    // keys past tend: V cleared by an AND mask (no per-lane branch) under one wave-uniform branch
+    const bool partial = tok0 + 2 * kPage > tend;
+#pragma unroll
+    for (int pg = 0; pg < 2; ++pg)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int key = (lane >> 4) + 4 * r;
+            uint4 v = vr[pg][r];
+            if (QDQ && qq.v_on)
+                v = qdq_v8(v, qq.v);
+            if (partial) {
+                const uint32_t keep = tok0 + kPage * pg + key < tend ? ~0u : 0u;
+                v = make_uint4(v.x & keep, v.y & keep, v.z & keep, v.w & keep);
+            }
+            st16(vt + (pg * kPage + key) * kVPitch + 8 * (lane & 15), v);
+        }
+}
+
+// Folds one chunk, whose V is already staged in vt, into the state.  keep == false (per lane, i.e. per
+// head) leaves that head's state untouched: p = 0 and no rescale.  cmax_l2: chunk max in log2 units.
+// QDQ: fake-quantize P (blocks of the 16 keys of a page, per head; the row sum takes the unquantized P).
+template <bool QDQ = false>
+__device__ __forceinline__ void chunk_update_staged(WaveState &st, const f32x4 sc[2], float cmax_l2, bool keep,
+                                                    float scale_log2, const uint16_t *vt, int lane,
+                                                    const Qdq &qq = Qdq{})
 {
     const int n = lane & 15, j = lane >> 4;
     const float m_new = keep ? fmaxf(st.m, cmax_l2) : st.m;
@@ -254,19 +276,6 @@ __device__ __forceinline__ void chunk_update(WaveState &st, const f32x4 sc[2], f
     for (int db = 0; db < kD / 16; ++db)
         st.acc[db] *= alpha;
 
-    const bool partial = tok0 + 2 * kPage > tend;
-#pragma unroll
-    for (int pg = 0; pg < 2; ++pg)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int key = (lane >> 4) + 4 * r;
-            uint4 v = vr[pg][r];
-            if (QDQ && qq.v_on)
-                v = qdq_v8(v, qq.v);
-            if (partial && tok0 + kPage * pg + key >= tend)
-                v = make_uint4(0, 0, 0, 0);
-            st16(vt + (pg * kPage + key) * kVPitch + 8 * (lane & 15), v);
-        }
     __builtin_amdgcn_wave_barrier();
     const bf16x8 pop = as_bf16x8(make_uint4(pack_bf16x2(p[0][0], p[0][1]), pack_bf16x2(p[0][2], p[0][3]),
                                             pack_bf16x2(p[1][0], p[1][1]), pack_bf16x2(p[1][2], p[1][3])));
@@ -281,6 +290,16 @@ __device__ __forceinline__ void chunk_update(WaveState &st, const f32x4 sc[2], f
         st.acc[db] = mfma16(as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y)), pop, st.acc[db]);
     }
     __builtin_amdgcn_wave_barrier();
+}
+
+// stage_v, then chunk_update_staged: V (read only when some head keeps the chunk) staged after the scores.
+template <bool QDQ = false>
+__device__ __forceinline__ void chunk_update(WaveState &st, const f32x4 sc[2], float cmax_l2, bool keep,
+                                             const uint4 vr[2][4], int tok0, int tend, float scale_log2,
+                                             uint16_t *vt, int lane, const Qdq &qq = Qdq{})
+{
+    stage_v<QDQ>(vr, tok0, tend, vt, lane, qq);
+    chunk_update_staged<QDQ>(st, sc, cmax_l2, keep, scale_log2, vt, lane, qq);
 }
 
 // Merges the W wave states of the workgroup (through LDS at `smem`, which must hold
@@ -330,9 +349,38 @@ __device__ __forceinline__ void merge_waves(WaveState &st, void *smem, int G, Ou
     }
 }
 
+// Runs compute(tok, kr, vr) over a wave's chunks tok = first, first + step, ... < end, with the K and V
+// of the next chunk loaded (load(tok, kr, vr)) while the current one is computed.  The exit test comes
+// before each prefetch, so no branch joins right after the loads (at such a join the compiler waits for
+// every load in flight, the prefetch included), and the two buffer sets alternate by name (a register
+// copy of a load in flight would wait for it).
+template <typename Load, typename Compute>
+__device__ __forceinline__ void chunk_pipeline(int first, int end, int step, Load load, Compute compute)
+{
+    uint4 ka[2][4], va[2][4], kb[2][4], vb[2][4];
+    load(first, ka, va);
+    for (int tok = first;;) {
+        if (tok + step >= end) {
+            compute(tok, ka, va);
+            break;
+        }
+        load(tok + step, kb, vb);
+        compute(tok, ka, va);
+        tok += step;
+        if (tok + step >= end) {
+            compute(tok, kb, vb);
+            break;
+        }
+        load(tok + step, ka, va);
+        compute(tok, kb, vb);
+        tok += step;
+    }
+}
+
 // ------------------------------------------------------------------ split-K
 
-__global__ __launch_bounds__(64 * kSplitWaves) void decode_split_kernel(SplitArgs a)
+__global__ __launch_bounds__(64 * kSplitWaves) __attribute__((amdgpu_waves_per_eu(2, 2))) void
+decode_split_kernel(SplitArgs a)
 {
     const int g = blockIdx.x, sp = blockIdx.y, b = blockIdx.z;
     const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -353,46 +401,25 @@ __global__ __launch_bounds__(64 * kSplitWaves) void decode_split_kernel(SplitArg
     state_init(st);
     const int32_t *btr = a.bt + (size_t)b * a.max_pages;
     const size_t slab = (size_t)kPage * kD;
-    // software pipeline: the K and V of the wave's next chunk are loaded before the current chunk is
-    // computed; a chunk past the split's end borrows the split's first chunk (never used)
-    auto chunk_off = [&](int tok0, size_t &o0, size_t &o1) {
-        const int tt = tok0 < t1 ? tok0 : t0;
-        const int p0 = btr[tt / kPage];
-        const int p1 = tt + kPage < t1 ? btr[tt / kPage + 1] : p0;
-        o0 = ((size_t)p0 * a.Hkv + g) * slab;
-        o1 = ((size_t)p1 * a.Hkv + g) * slab;
-    };
     const int step = 2 * kPage * kSplitWaves;
-    int tok0 = t0 + 2 * kPage * w;
-    if (tok0 < t1) {
-        size_t o0, o1;
-        chunk_off(tok0, o0, o1);
-        uint4 kr[2][4], vr[2][4];
-        load_k_chunk(a.kc + o0, a.kc + o1, lane, kr);
-        load_v_chunk(a.vc + o0, a.vc + o1, lane, vr);
-        for (; tok0 < t1; tok0 += step) {
-            size_t n0, n1;
-            chunk_off(tok0 + step, n0, n1);
-            uint4 kn[2][4], vn[2][4];
-            const bool more = tok0 + step < t1;
-            if (more) {
-                load_k_chunk(a.kc + n0, a.kc + n1, lane, kn);
-                load_v_chunk(a.vc + n0, a.vc + n1, lane, vn);
-            }
-            f32x4 sc[2];
-            const float cmax = chunk_scores(kr, qop, tok0, t1, lane, sc);
-            chunk_update(st, sc, cmax * a.scale_log2, true, vr, tok0, t1, a.scale_log2, vt, lane);
-            if (more) {
-#pragma unroll
-                for (int pg = 0; pg < 2; ++pg)
-#pragma unroll
-                    for (int s4 = 0; s4 < 4; ++s4) {
-                        kr[pg][s4] = kn[pg][s4];
-                        vr[pg][s4] = vn[pg][s4];
-                    }
-            }
-        }
-    }
+    const int first = t0 + 2 * kPage * w;
+    if (first < t1)
+        chunk_pipeline(
+            first, t1, step,
+            [&](int tok0, uint4 (&kr)[2][4], uint4 (&vr)[2][4]) {
+                const int p0 = btr[tok0 / kPage];
+                const int p1 = tok0 + kPage < t1 ? btr[tok0 / kPage + 1] : p0;
+                const size_t o0 = ((size_t)p0 * a.Hkv + g) * slab, o1 = ((size_t)p1 * a.Hkv + g) * slab;
+                load_k_chunk(a.kc + o0, a.kc + o1, lane, kr);
+                load_v_chunk(a.vc + o0, a.vc + o1, lane, vr);
+            },
+            [&](int tok0, const uint4 (&kr)[2][4], const uint4 (&vr)[2][4]) {
+                // V goes to LDS first, so its registers are free before the scores are computed
+                stage_v(vr, tok0, t1, vt, lane);
+                f32x4 sc[2];
+                const float cmax = chunk_scores(kr, qop, tok0, t1, lane, sc);
+                chunk_update_staged(st, sc, cmax * a.scale_log2, true, a.scale_log2, vt, lane);
+            });
     const size_t row0 = (size_t)b * a.Hq + (size_t)g * a.G;
     merge_waves<kSplitWaves>(st, smem, a.G, [&](int h, int d, float o, float lse) {
         a.ws_o[((row0 + h) * S + sp) * kD + d] = o;
@@ -462,12 +489,12 @@ __global__ __launch_bounds__(256) void decode_merge_multi_kernel(MergeArgs a) { 
 
 hipError_t launch_decode_split(const SplitArgs &a, int B, uint16_t *o, float *lse, hipStream_t stream)
 {
-    hipLaunchKernelGGL(decode_split_kernel, dim3(a.Hkv, a.num_splits, B), dim3(64 * kSplitWaves), 0, stream, a);
+    ATTN_LAUNCH(decode_split_kernel, dim3(a.Hkv, a.num_splits, B), dim3(64 * kSplitWaves), 0, stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return e;
     MergeArgs m{a.ws_o, a.ws_lse, B * a.Hq, a.num_splits, o, lse};
-    hipLaunchKernelGGL(decode_merge_kernel, dim3((B * a.Hq + 3) / 4), dim3(256), 0, stream, m);
+    ATTN_LAUNCH(decode_merge_kernel, dim3((B * a.Hq + 3) / 4), dim3(256), 0, stream, m);
     return hipGetLastError();
 }
 
@@ -505,7 +532,8 @@ __device__ __forceinline__ float chunk_scores_lim(const uint4 kr[2][4], const bf
 // token (16 cb + n) / G, head g G + (16 cb + n) % G), so one read of the cache serves up to 16 rows;
 // otherwise the same split-K schedule, chunk pipeline and partials as decode_split_kernel, over the
 // keys the block's last token sees.
-__global__ __launch_bounds__(64 * kSplitWaves) void decode_multi_kernel(MultiArgs a)
+__global__ __launch_bounds__(64 * kSplitWaves) __attribute__((amdgpu_waves_per_eu(2, 2))) void
+decode_multi_kernel(MultiArgs a)
 {
     const int g = blockIdx.x, sp = blockIdx.y, b = blockIdx.z / a.ncb, cb = blockIdx.z % a.ncb;
     const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -548,44 +576,24 @@ __global__ __launch_bounds__(64 * kSplitWaves) void decode_multi_kernel(MultiArg
     state_init(st);
     const int32_t *btr = a.bt + (size_t)b * a.max_pages;
     const size_t slab = (size_t)kPage * kD;
-    auto chunk_off = [&](int tok0, size_t &o0, size_t &o1) {
-        const int tt = tok0 < t1 ? tok0 : t0;
-        const int p0 = btr[tt / kPage];
-        const int p1 = tt + kPage < t1 ? btr[tt / kPage + 1] : p0;
-        o0 = ((size_t)p0 * a.Hkv + g) * slab;
-        o1 = ((size_t)p1 * a.Hkv + g) * slab;
-    };
     const int step = 2 * kPage * kSplitWaves;
-    int tok0 = t0 + 2 * kPage * w;
-    if (tok0 < t1) {
-        size_t o0, o1;
-        chunk_off(tok0, o0, o1);
-        uint4 kr[2][4], vr[2][4];
-        load_k_chunk(a.kc + o0, a.kc + o1, lane, kr);
-        load_v_chunk(a.vc + o0, a.vc + o1, lane, vr);
-        for (; tok0 < t1; tok0 += step) {
-            size_t n0, n1;
-            chunk_off(tok0 + step, n0, n1);
-            uint4 kn[2][4], vn[2][4];
-            const bool more = tok0 + step < t1;
-            if (more) {
-                load_k_chunk(a.kc + n0, a.kc + n1, lane, kn);
-                load_v_chunk(a.vc + n0, a.vc + n1, lane, vn);
-            }
-            f32x4 sc[2];
-            const float cmax = chunk_scores_lim(kr, qop, tok0, lim, lim_min, lane, sc);
-            chunk_update(st, sc, cmax * a.scale_log2, true, vr, tok0, t1, a.scale_log2, vt, lane);
-            if (more) {
-#pragma unroll
-                for (int pg = 0; pg < 2; ++pg)
-#pragma unroll
-                    for (int s4 = 0; s4 < 4; ++s4) {
-                        kr[pg][s4] = kn[pg][s4];
-                        vr[pg][s4] = vn[pg][s4];
-                    }
-            }
-        }
-    }
+    const int first = t0 + 2 * kPage * w;
+    if (first < t1)
+        chunk_pipeline(
+            first, t1, step,
+            [&](int tok0, uint4 (&kr)[2][4], uint4 (&vr)[2][4]) {
+                const int p0 = btr[tok0 / kPage];
+                const int p1 = tok0 + kPage < t1 ? btr[tok0 / kPage + 1] : p0;
+                const size_t o0 = ((size_t)p0 * a.Hkv + g) * slab, o1 = ((size_t)p1 * a.Hkv + g) * slab;
+                load_k_chunk(a.kc + o0, a.kc + o1, lane, kr);
+                load_v_chunk(a.vc + o0, a.vc + o1, lane, vr);
+            },
+            [&](int tok0, const uint4 (&kr)[2][4], const uint4 (&vr)[2][4]) {
+                stage_v(vr, tok0, t1, vt, lane);
+                f32x4 sc[2];
+                const float cmax = chunk_scores_lim(kr, qop, tok0, lim, lim_min, lane, sc);
+                chunk_update_staged(st, sc, cmax * a.scale_log2, true, a.scale_log2, vt, lane);
+            });
     merge_waves<kSplitWaves>(st, smem, nc, [&](int h, int d, float o, float lse) {
         const size_t row = (size_t)(q0 + (r0 + h) / a.G) * a.Hq + (size_t)g * a.G + (r0 + h) % a.G;
         a.ws_o[(row * S + sp) * kD + d] = o;
@@ -596,13 +604,13 @@ __global__ __launch_bounds__(64 * kSplitWaves) void decode_multi_kernel(MultiArg
 
 hipError_t launch_decode_multi(const MultiArgs &a, int B, int total_q, uint16_t *o, float *lse, hipStream_t stream)
 {
-    hipLaunchKernelGGL(decode_multi_kernel, dim3(a.Hkv, a.num_splits, B * a.ncb), dim3(64 * kSplitWaves), 0, stream,
+    ATTN_LAUNCH(decode_multi_kernel, dim3(a.Hkv, a.num_splits, B * a.ncb), dim3(64 * kSplitWaves), 0, stream,
                        a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return e;
     MergeArgs m{a.ws_o, a.ws_lse, total_q * a.Hq, a.num_splits, o, lse};
-    hipLaunchKernelGGL(decode_merge_multi_kernel, dim3((total_q * a.Hq + 3) / 4), dim3(256), 0, stream, m);
+    ATTN_LAUNCH(decode_merge_multi_kernel, dim3((total_q * a.Hq + 3) / 4), dim3(256), 0, stream, m);
     return hipGetLastError();
 }
 
@@ -776,9 +784,9 @@ __global__ __launch_bounds__(64 * kSeqWaves) void decode_seq_qdq_kernel(SeqArgs 
 hipError_t launch_decode_seq(const SeqArgs &a, int B, hipStream_t stream)
 {
     if (a.p_qdq || a.v_qdq)
-        hipLaunchKernelGGL(decode_seq_qdq_kernel, dim3(a.Hkv, B), dim3(64 * kSeqWaves), 0, stream, a);
+        ATTN_LAUNCH(decode_seq_qdq_kernel, dim3(a.Hkv, B), dim3(64 * kSeqWaves), 0, stream, a);
     else
-        hipLaunchKernelGGL(decode_seq_kernel, dim3(a.Hkv, B), dim3(64 * kSeqWaves), 0, stream, a);
+        ATTN_LAUNCH(decode_seq_kernel, dim3(a.Hkv, B), dim3(64 * kSeqWaves), 0, stream, a);
     return hipGetLastError();
 }
 

@@ -100,6 +100,44 @@ struct BwdArgs {
     void *dq, *dk, *dv;        // bf16, like q, k, v
 };
 
+// ATTN_CHECK=1: device-side validation of a call's index arrays before its kernels (check.hip).  cu_a
+// (nullable): [B + 1] prefix sums, each difference at most max_a, cu_a[B] == total_a when total_a >= 0;
+// cu_b likewise with max_b; bt / seq_lens (nullable): a [B, max_pages] block table over num_pages pages
+// of `page` keys and the row lengths it covers.
+struct CheckSpec {
+    int B;
+    const int32_t *cu_a;
+    int max_a, total_a;
+    const int32_t *cu_b;
+    int max_b;
+    const int32_t *bt, *seq_lens;
+    int max_pages, page, num_pages;
+};
+enum CheckCode {
+    kCheckCuA = 1,   // +0 cu_a[0] != 0, +1 decreasing, +2 a length above max_a, +3 cu_a[B] != total_a
+    kCheckCuB = 5,   // the same for cu_b
+    kCheckSeqLen = 9, // seq_lens[b] outside [0, max_pages * page]
+    kCheckPage = 10,  // a visible block-table entry outside [0, num_pages)
+};
+struct CheckResult {
+    int code, row; // code 0: every check passed
+};
+// Queues the checks on `stream`, waits for them and reports the verdict.
+hipError_t check_indices(const CheckSpec &s, hipStream_t stream, CheckResult *out);
+
+// ATTN_LOG=1: every kernel launch (name, grid, block) and every rejected call (its message) is printed
+// to stderr.  Both variables are read on every call.
+bool log_enabled();
+void log_launch(const char *kernel, dim3 grid, dim3 block);
+
+// hipLaunchKernelGGL plus the ATTN_LOG line.
+#define ATTN_LAUNCH(kernel, grid, block, lds, stream, ...)                                                        \
+    do {                                                                                                          \
+        if (::attn::log_enabled())                                                                                \
+            ::attn::log_launch(#kernel, dim3(grid), dim3(block));                                                 \
+        hipLaunchKernelGGL(kernel, grid, block, lds, stream, __VA_ARGS__);                                        \
+    } while (0)
+
 hipError_t launch_decode_split(const SplitArgs &a, int B, uint16_t *o, float *lse, hipStream_t stream);
 hipError_t launch_decode_seq(const SeqArgs &a, int B, hipStream_t stream);
 hipError_t launch_decode_multi(const MultiArgs &a, int B, int total_q, uint16_t *o, float *lse, hipStream_t stream);

@@ -391,9 +391,9 @@ hipError_t launch_prefill(const PrefillArgs &a, bool bf16, int D, hipStream_t st
             return launch_prefill_d128(a, stream);
         } else if (D == 64) {
             if (skip)
-                hipLaunchKernelGGL((prefill_bf16_kernel<64, true>), grid, block, 0, stream, a);
+                ATTN_LAUNCH((prefill_bf16_kernel<64, true>), grid, block, 0, stream, a);
             else
-                hipLaunchKernelGGL((prefill_bf16_kernel<64, false>), grid, block, 0, stream, a);
+                ATTN_LAUNCH((prefill_bf16_kernel<64, false>), grid, block, 0, stream, a);
         } else {
             return hipErrorInvalidValue;
         }
@@ -402,7 +402,7 @@ hipError_t launch_prefill(const PrefillArgs &a, bool bf16, int D, hipStream_t st
     if (D != 64)
         return hipErrorNotSupported;
     dim3 grid(a.Hq, a.B, (a.max_q + 63) / 64);
-    hipLaunchKernelGGL((prefill_f32_kernel<64>), grid, dim3(64), 0, stream, a);
+    ATTN_LAUNCH((prefill_f32_kernel<64>), grid, dim3(64), 0, stream, a);
     return hipGetLastError();
 }
 

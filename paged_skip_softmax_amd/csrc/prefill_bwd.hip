@@ -7,12 +7,14 @@
 //
 // Three kernels, no atomics:
 //  * bwd_prep: Dsum and lse * log2(e) per (token, query head), fp32, into the caller's workspace.
-//  * bwd_dkdv: a workgroup of 4 waves owns 64 keys of one (sequence, KV head), 16 keys per wave, whose
-//    K and V stay in registers as MFMA B operands; it walks every query tile of 32 rows that sees any
-//    of its keys, for every query head of the group.  The workgroup stages each Q and dO tile in LDS
-//    once for its 4 waves (XOR-swizzled 16-byte chunks); per tile a wave computes, with 16x16x32 MFMAs,
-//      S = Q K^T, dP = dO V^T           [32 rows x 16 keys]   (A operands: 16-byte LDS reads)
-//      dV^T += dO^T P, dK^T += Q^T dS   [128 dims x 16 keys]  (A operands: transposed LDS reads)
+//  * bwd_dkdv: a workgroup of 4 waves owns 128 keys of one (sequence, KV head), 32 keys per wave, whose
+//    K and V stay in registers as MFMA B operands; it walks every 64-row query tile that sees any of its
+//    keys, for every query head of the group, from the sequence's last tile backwards (so that the key
+//    blocks of a sequence, dispatched together, share each tile through L2).  Q and dO tiles go to LDS
+//    by direct-to-LDS loads (XOR-swizzled 16-byte chunks) once for the 4 waves; per 32-row block a wave
+//    computes, with 32x32x16 MFMAs,
+//      S = Q K^T, dP = dO V^T           [32 rows x 32 keys]   (A operands: 16-byte LDS reads)
+//      dV^T += dO^T P, dK^T += Q^T dS   [128 dims x 32 keys]  (A operands: transposed LDS reads)
 //    so the key order inside the row contraction follows the S register layout and P, dS feed the
 //    MFMA B operand straight from registers.
 //  * bwd_dq: the forward's work split (4 waves, one query head and 32 rows each, the heads of a group
@@ -284,8 +286,8 @@ __device__ __forceinline__ void kv_step(const KvLane &L, const bf16x8 kop[8], co
 
 // dK, dV of 128 keys of one (sequence, KV head): wave w owns keys kb0 + 32 w .. +31, whose K and V stay in
 // registers as the B operands of S = Q K^T and dP = dO V^T.  The loop runs over the query heads of the
-// group and, per head, over the 64-row query tiles that see any of the keys, staged in a three-stage
-// direct-to-LDS ring.  A wave works in 32-row blocks through a three-deep software pipeline: while the
+// group and, per head, over the 64-row query tiles that see any of the keys, last tile first, staged in a
+// three-stage direct-to-LDS ring.  A wave works in 32-row blocks through a three-deep software pipeline: while the
 // MFMAs of S and dP [32 rows x 32 keys] of block j run (A operands: 16-B LDS reads of Q and dO rows),
 // so do those of dV^T += dO^T P and dK^T += Q^T dS [128 dims x 32 keys] of block j-2 (A operands:
 // transposed LDS reads), and P and dS of block j-1 are computed between them.  P and dS feed the B
@@ -293,16 +295,17 @@ __device__ __forceinline__ void kv_step(const KvLane &L, const bf16x8 kop[8], co
 __global__ __launch_bounds__(kKvThreads) void bwd_dkdv_kernel(BwdArgs a, int nkt, int nunits)
 {
     // XCD-aware order: block i runs on XCD i % 8, which takes a contiguous run of units ordered (KV
-    // head, key block, sequence): each XCD serves whole KV heads of every sequence (even load), and
-    // starts with the key blocks that see the most query rows (the first ones, under the causal mask);
-    // the key blocks of one sequence that run at the same time stream the same Q and dO tiles through
-    // the XCD's L2
+    // head, sequence, key block): each XCD serves whole KV heads of every sequence (even load), and the
+    // key blocks of one (sequence, KV head) are dispatched together.  Every key block walks its query
+    // tiles from the sequence's last one backwards (all key blocks see the last rows, under the causal
+    // mask too), so the key blocks running together read the same Q and dO tiles at about the same
+    // time and all but the first read of each come from the XCD's L2.
     const int per = gridDim.x / kXcds;
     const int unit = (blockIdx.x % kXcds) * per + blockIdx.x / kXcds;
     if (unit >= nunits)
         return;
     const int g = unit / (nkt * a.B), rem = unit % (nkt * a.B);
-    const int kt = rem / a.B, b = rem % a.B;
+    const int b = rem / nkt, kt = rem % nkt;
     const int q0 = a.cu_q[b], Lq = a.cu_q[b + 1] - q0;
     const int k0 = a.cu_k[b], Lk = a.cu_k[b + 1] - k0;
     const int kb0 = kt * kKeysPerWg;
@@ -381,16 +384,17 @@ __global__ __launch_bounds__(kKvThreads) void bwd_dkdv_kernel(BwdArgs a, int nkt
     const int qt_first = (a.causal ? max(0, kb0 - diag) : 0) / kQRows;
     const int nq = (Lq + kQRows - 1) / kQRows - qt_first;
     const int ntiles = nq > 0 ? a.G * nq : 0;
-    // a tile's place: ring stage, first row, query head (advanced one tile at a time)
+    // a tile's place: ring stage, first row, query head (advanced one tile at a time: per head, from
+    // the last tile down to the first)
     struct Tile {
         int st, row0, h;
     };
-    const int row_first = qt_first * kQRows, row_end = (qt_first + nq) * kQRows;
+    const int row_first = qt_first * kQRows, row_last = (qt_first + nq - 1) * kQRows;
     auto advance = [&](Tile t) {
         t.st = t.st == kQStages - 1 ? 0 : t.st + 1;
-        t.row0 += kQRows;
-        if (t.row0 == row_end) {
-            t.row0 = row_first;
+        t.row0 -= kQRows;
+        if (t.row0 < row_first) {
+            t.row0 = row_last;
             ++t.h;
         }
         return t;
@@ -420,7 +424,7 @@ __global__ __launch_bounds__(kKvThreads) void bwd_dkdv_kernel(BwdArgs a, int nkt
     if (ntiles > 0) {
         f32x16 sc, dp, scp, dpp;
         uint32_t pka[8], ska[8], pkb[8], skb[8];
-        Tile prev{0, row_first, g * a.G};
+        Tile prev{0, row_last, g * a.G};
         ld.issue(prev.st, prev.row0, prev.h);
         // steps 0 and 1: S of blocks 0, 1; P of block 0
         next_tile(prev, 0);
@@ -758,7 +762,7 @@ hipError_t launch_prefill_bwd(const BwdArgs &a, hipStream_t stream)
     if (slots > 0x7fffffffL)
         return hipErrorInvalidValue;
     if (slots > 0)
-        hipLaunchKernelGGL(bwd_prep_kernel, dim3((unsigned)((slots + 15) / 16)), dim3(256), 0, stream, a);
+        ATTN_LAUNCH(bwd_prep_kernel, dim3((unsigned)((slots + 15) / 16)), dim3(256), 0, stream, a);
     const int nkt = (a.max_k + kKeysPerWg - 1) / kKeysPerWg;
     const long units_kv = (long)a.Hkv * a.B * nkt;
     const long blocks_kv = (units_kv + kXcds - 1) / kXcds * kXcds;
@@ -769,10 +773,10 @@ hipError_t launch_prefill_bwd(const BwdArgs &a, hipStream_t stream)
     if (blocks_kv > 0x7fffffff || blocks_q > 0x7fffffff)
         return hipErrorInvalidValue;
     if (units_kv > 0)
-        hipLaunchKernelGGL(bwd_dkdv_kernel, dim3((unsigned)blocks_kv), dim3(kKvThreads), 0, stream, a, nkt,
+        ATTN_LAUNCH(bwd_dkdv_kernel, dim3((unsigned)blocks_kv), dim3(kKvThreads), 0, stream, a, nkt,
                            (int)units_kv);
     if (units_q > 0)
-        hipLaunchKernelGGL(bwd_dq_kernel, dim3((unsigned)blocks_q), dim3(kDqThreads), 0, stream, a, NH, RB, nqt,
+        ATTN_LAUNCH(bwd_dq_kernel, dim3((unsigned)blocks_q), dim3(kDqThreads), 0, stream, a, NH, RB, nqt,
                            (int)units_q);
     return hipGetLastError();
 }

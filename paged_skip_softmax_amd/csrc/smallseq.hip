@@ -207,13 +207,13 @@ __global__ __launch_bounds__(256) void smallseq_bwd_kernel(SmallBwdArgs a)
 
 hipError_t launch_smallseq_bwd(const SmallBwdArgs &a, hipStream_t stream)
 {
-    hipLaunchKernelGGL(smallseq_bwd_kernel, dim3(a.B, (a.H + 15) / 16), dim3(256), 0, stream, a);
+    ATTN_LAUNCH(smallseq_bwd_kernel, dim3(a.B, (a.H + 15) / 16), dim3(256), 0, stream, a);
     return hipGetLastError();
 }
 
 hipError_t launch_smallseq(const SmallArgs &a, hipStream_t stream)
 {
-    hipLaunchKernelGGL(smallseq_kernel, dim3(a.B, (a.H + 15) / 16), dim3(256), 0, stream, a);
+    ATTN_LAUNCH(smallseq_kernel, dim3(a.B, (a.H + 15) / 16), dim3(256), 0, stream, a);
     return hipGetLastError();
 }
 

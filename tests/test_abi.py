@@ -305,3 +305,31 @@ def test_decode_noalloc_validation(lib):
     assert call(B=128, Hq=32, Hkv=8) == WORKSPACE
     assert b"scratch" in lib.attn_last_error_message()
     assert call(B=64, Hq=32, Hkv=8, splits=64) == WORKSPACE
+
+
+def test_attn_log_prints_rejections(lib, capfd, monkeypatch):
+    """ATTN_LOG=1 prints every rejected call's reason to stderr (and every launch, on a GPU); unset, the
+    library prints nothing.  The variable is read on every call."""
+    monkeypatch.delenv("ATTN_LOG", raising=False)
+    assert _decode(lib, B=-1) == INVALID
+    assert capfd.readouterr().err == ""
+    monkeypatch.setenv("ATTN_LOG", "1")
+    assert _decode(lib, D=64) == UNSUPPORTED
+    assert _prefill(lib, thr=2.0) == INVALID
+    err = capfd.readouterr().err
+    assert "[attn] rejected (status 2): attn_decode_paged: D = 64" in err
+    assert "[attn] rejected (status 1): attn_prefill_varlen: skip_threshold" in err
+    monkeypatch.setenv("ATTN_LOG", "0")
+    assert _decode(lib, B=-1) == INVALID
+    assert capfd.readouterr().err == ""
+
+
+def test_attn_check_runs_after_the_host_checks(lib, monkeypatch):
+    """With ATTN_CHECK=1 the host-side validation still comes first: a call it rejects returns its
+    status without touching the device (so this runs without a GPU)."""
+    monkeypatch.setenv("ATTN_CHECK", "1")
+    assert _decode(lib, B=-1) == INVALID
+    assert _decode(lib, wsb=100) == WORKSPACE
+    assert _prefill(lib, D=96) == UNSUPPORTED
+    assert _small(lib, ms=17) == INVALID
+    assert _decode(lib, B=0) == _lib.ATTN_OK
