@@ -568,7 +568,19 @@ def _achievable(torch, dev):
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / 10
     res["copy_1GiB_GBps"] = 2.0 * (1 << 30) / (ms * 1e-3) / 1e9
-    del src, dst
+    # a plain read: torch's sum over 1 GiB of int32 (reads the bytes once, writes one scalar)
+    x32 = src.view(torch.int32)
+    for _ in range(3):
+        x32.sum()
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(10):
+        x32.sum()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / 10
+    res["read_1GiB_sum_GBps"] = float(1 << 30) / (ms * 1e-3) / 1e9
+    del src, dst, x32
     n = 8192
     a = torch.randn(n, n, device=dev, dtype=torch.bfloat16)
     b = torch.randn(n, n, device=dev, dtype=torch.bfloat16)

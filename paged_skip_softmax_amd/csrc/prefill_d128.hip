@@ -238,8 +238,7 @@ __device__ __forceinline__ bool needs_mask(int t, const IterCtx &c)
 //       MFMA-and-exponential phase goes first, the other fills the gaps);
 //   (c) mask tile t+1 where it crosses the diagonal or the sequence end;
 //   (d) P.V of tile t, with the row max of tile t+1 placed between its MFMAs.
-// On the last tile the dense kernel runs (b) as exponentials alone; the skip kernel computes scores from
-// a stale K stage there, which are never used.
+// On the last tile, (b)-(d) compute scores from a stale K stage that are never used.
 template <int ST, bool SKIP, bool PAGED>
 __device__ __forceinline__ void iteration(int t, const IterCtx &c, const Loader<PAGED> &ld, Wave &wv, f32x16 sc[2],
                                           float &t0, float &t1, SkipState &ss)
@@ -323,41 +322,23 @@ __device__ __forceinline__ void iteration(int t, const IterCtx &c, const Loader<
             k1 = k2;
         }
     };
-    // dense: the last tile has no tile t+1 to score, so its exponentials run alone, without the QK^T MFMAs
-    auto exps_only = [&]() {
+    if constexpr (!SKIP) {
 #pragma unroll
         for (int step = 0; step < 16; ++step) {
+            const uint4 k2 = step + 2 < 16 ? kop(step + 2) : k0;
+            nx[step & 1] = mfma32(as_bf16x8(k0), wv.qop[step >> 1], nx[step & 1]);
             const int kk = step >> 3, i = 2 * (step & 7);
-            const float mk = kk ? mk1 : mk0;
-            const float p0 = exp2_fast(fmaf(sc[kk][i], sl, -mk));
-            const float p1 = exp2_fast(fmaf(sc[kk][i + 1], sl, -mk));
+            const float p0 = exp2_fast(fmaf(sc[kk][i], sl, -m_use));
+            const float p1 = exp2_fast(fmaf(sc[kk][i + 1], sl, -m_use));
             wv.l += p0 + p1;
+            anchor(wv.l);
             pk[kk][i >> 1] = pack_bf16x2(p0, p1);
-        }
-    };
-    const bool last = t + 1 >= c.niter;
-    if constexpr (!SKIP) {
-        if (last) {
-            exps_only();
-        } else {
-#pragma unroll
-            for (int step = 0; step < 16; ++step) {
-                const uint4 k2 = step + 2 < 16 ? kop(step + 2) : k0;
-                nx[step & 1] = mfma32(as_bf16x8(k0), wv.qop[step >> 1], nx[step & 1]);
-                const int kk = step >> 3, i = 2 * (step & 7);
-                const float p0 = exp2_fast(fmaf(sc[kk][i], sl, -m_use));
-                const float p1 = exp2_fast(fmaf(sc[kk][i + 1], sl, -m_use));
-                wv.l += p0 + p1;
-                anchor(wv.l);
-                pk[kk][i >> 1] = pack_bf16x2(p0, p1);
-                anchor(pk[kk][i >> 1]);
-                sched_fence();
-                k0 = k1;
-                k1 = k2;
-            }
+            anchor(pk[kk][i >> 1]);
+            sched_fence();
+            k0 = k1;
+            k1 = k2;
         }
     } else if (__any(ss.keep[0] || ss.keep[1])) {
-        // (the skip variant keeps the stale scoring of the last tile: a separate path there spills)
         steps_b(std::true_type{});
     } else {
         steps_b(std::false_type{});
