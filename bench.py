@@ -228,7 +228,7 @@ def main():
     # previous call left in the L2s (4 MB per XCD) and the 256 MB last-level cache, so every call starts
     # cold.  A read, not a write: written lines would stay dirty in the caches and their write-back would
     # land inside the next timed call (measured: +5 to +14 % on the HBM-bound kernels).
-    flush_buf = torch.ones(FLUSH_BYTES // 4, dtype=torch.int32, device=dev)
+    flush_buf = torch.ones(FLUSH_BYTES // 4, dtype=torch.float32, device=dev)
 
     def flush():
         flush_buf.sum()
@@ -568,8 +568,8 @@ def _achievable(torch, dev):
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / 10
     res["copy_1GiB_GBps"] = 2.0 * (1 << 30) / (ms * 1e-3) / 1e9
-    # a plain read: torch's sum over 1 GiB of int32 (reads the bytes once, writes one scalar)
-    x32 = src.view(torch.int32)
+    # a plain read: torch's sum over 1 GiB of float32 (reads the bytes once, writes one scalar)
+    x32 = src.view(torch.float32)
     for _ in range(3):
         x32.sum()
     torch.cuda.synchronize()
@@ -579,7 +579,7 @@ def _achievable(torch, dev):
     e1.record()
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / 10
-    res["read_1GiB_sum_GBps"] = float(1 << 30) / (ms * 1e-3) / 1e9
+    res["read_1GiB_fp32_sum_GBps"] = float(1 << 30) / (ms * 1e-3) / 1e9
     del src, dst, x32
     n = 8192
     a = torch.randn(n, n, device=dev, dtype=torch.bfloat16)
