@@ -15,9 +15,9 @@
 //    rounds, publish their tile maxima in LDS, and each decides exactly from the prefix max -- the
 //    decisions of one sequential pass, taken in parallel.  V of a tile is read only when at least one
 //    query row of the group keeps it.  The K rows run two rounds ahead (requested after a round's V,
-//    so that waiting for that V leaves them in flight), and the batch rows are dispatched longest
-//    first, so that the longest sequences (the critical path of a one-split-per-sequence schedule)
-//    start at once and the short ones fill in behind them.
+//    so that waiting for that V leaves them in flight), and batches of up to 128 rows are dispatched
+//    longest first, so that the longest sequences (the critical path of a one-split-per-sequence
+//    schedule) start at once and the short ones fill in behind them.
 //
 // Cache layout: [num_pages, Hkv, 16, D] bf16, so one (page, KV head) is a contiguous 4 KB slab.
 //
@@ -616,27 +616,41 @@ hipError_t launch_decode_multi(const MultiArgs &a, int B, int total_q, uint16_t 
 
 // ------------------------------------------------------------------ sequential with skip-softmax
 
-// Sequences of up to this batch size are scheduled longest first.
-constexpr int kLptMaxBatch = 1024;
+// Sequences of up to this batch size are scheduled longest first.  Beyond it the batch spans enough
+// rounds of workgroups that the dispatch order matters little, while every workgroup ranking all B
+// rows (O(B^2)) costs more than it saves.  Measured (Hq 32, Hkv 8, lengths 256..4096 unless noted),
+// ranked against index order: B = 64 with lengths 1k..32k 0.705 / 0.848 ms, B = 128 0.225 / 0.234 ms,
+// B = 256 0.471 / 0.444 ms; the earlier per-workgroup ranking over global memory at B = 1024 took
+// 4.56 ms against 1.60 in index order.
+constexpr int kLptMaxBatch = 128;
 
 // Batch row of the workgroup at dispatch position `pos`: with B <= kLptMaxBatch the rows are taken
 // in order of decreasing length (ties by index), so that the longest sequences start first and the
-// short ones fill in behind them; otherwise in index order.
-__device__ __forceinline__ int lpt_row(const int32_t *seq_lens, int B, int pos, int *slot)
+// short ones fill in behind them; otherwise in index order.  The lengths are staged in `lens` (LDS,
+// 16-byte aligned, >= kLptMaxBatch ints, free again when this returns) and read four at a time.
+__device__ __forceinline__ int lpt_row(const int32_t *seq_lens, int B, int pos, int *slot, int32_t *lens)
 {
     if (B > kLptMaxBatch)
         return pos;
+    const int Bp = (B + 3) & ~3;
+    for (int i = threadIdx.x; i < Bp; i += blockDim.x)
+        lens[i] = i < B ? seq_lens[i] : -1; // padding: below every length, so it never outranks a row
     if (threadIdx.x == 0)
         *slot = pos;
     __syncthreads();
+    const int4 *l4 = reinterpret_cast<const int4 *>(lens);
     for (int i = threadIdx.x; i < B; i += blockDim.x) {
-        const int Li = seq_lens[i];
-        int rank = 0;
-        for (int jj = 0; jj < B; ++jj) {
-            const int Lj = seq_lens[jj];
-            rank += (Lj > Li) || (Lj == Li && jj < i);
+        const int Li = lens[i];
+        int r0 = 0, r1 = 0, r2 = 0, r3 = 0;
+        for (int q = 0; q < Bp / 4; ++q) {
+            const int4 v = l4[q];
+            const int j = 4 * q;
+            r0 += (v.x > Li) || (v.x == Li && j < i);
+            r1 += (v.y > Li) || (v.y == Li && j + 1 < i);
+            r2 += (v.z > Li) || (v.z == Li && j + 2 < i);
+            r3 += (v.w > Li) || (v.w == Li && j + 3 < i);
         }
-        if (rank == pos)
+        if (r0 + r1 + r2 + r3 == pos)
             *slot = i;
     }
     __syncthreads();
@@ -650,14 +664,17 @@ template <bool QDQ>
 __device__ __forceinline__ void decode_seq(const SeqArgs &a)
 {
     __shared__ int row_slot;
-    const int g = blockIdx.x, b = lpt_row(a.seq_lens, gridDim.y, blockIdx.y, &row_slot);
+    __shared__ __attribute__((aligned(16))) uint16_t smem[kSeqWaves * kVTile];
+    // the batch lengths for the dispatch order go to the V staging area, unused until the main loop
+    const int g = blockIdx.x,
+              b = lpt_row(a.seq_lens, gridDim.y, blockIdx.y, &row_slot, reinterpret_cast<int32_t *>(smem));
     const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int n = lane & 15, j = lane >> 4;
     const int L = a.seq_lens[b];
     const int ntiles = (L + kSkipTile - 1) / kSkipTile;
 
-    __shared__ __attribute__((aligned(16))) uint16_t smem[kSeqWaves * kVTile];
     static_assert(sizeof(smem) >= kSeqWaves * 16 * (kD + 2) * sizeof(float), "merge buffer");
+    static_assert(sizeof(smem) >= kLptMaxBatch * sizeof(int32_t), "batch lengths");
     __shared__ float tmax_buf[2][kSeqWaves][16];
     uint16_t *vt = smem + w * kVTile;
     const size_t row0 = (size_t)b * a.Hq + (size_t)g * a.G;
