@@ -87,10 +87,11 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdArgs a)
 // ------------------------------------------------------------------ dK, dV
 
 constexpr int kXcds = 8;
-constexpr int kKvWaves = 4;
+constexpr int kKvPairs = 4;                         // wave pairs per workgroup
+constexpr int kKvWaves = 2 * kKvPairs;              // two waves per SIMD
 constexpr int kKvThreads = 64 * kKvWaves;
-constexpr int kKeysPerWave = 32;
-constexpr int kKeysPerWg = kKvWaves * kKeysPerWave; // 128
+constexpr int kKeysPerPair = 32;
+constexpr int kKeysPerWg = kKvPairs * kKeysPerPair; // 128
 constexpr int kQRows = 64;                          // query rows per staged tile
 constexpr int kQTileBytes = kQRows * kRowBytes;     // 16 KB
 constexpr int kQLoads = kQTileBytes / 1024 / kKvWaves; // 1-KB direct-to-LDS loads per wave per tile
@@ -104,6 +105,32 @@ struct alignas(1024) QStage {
     float dsum[kQRows];
 };
 __shared__ QStage q_ring[kQStages];
+
+// P of a 32-row block, passed from a pair's P wave to its dS wave: the 8 packed registers of each lane,
+// as two 1-KB halves of 16 B per lane.  Two tiles in flight (the dS wave runs one tile behind), two
+// blocks per tile.
+constexpr int kXchgBlock = 2048;
+__shared__ __attribute__((aligned(1024))) char p_xchg[2][kKvPairs][2 * kXchgBlock];
+
+__device__ __forceinline__ void xchg_store(char *blk, int lane, const uint32_t pk[8])
+{
+    st16(blk + 16 * lane, make_uint4(pk[0], pk[1], pk[2], pk[3]));
+    st16(blk + 1024 + 16 * lane, make_uint4(pk[4], pk[5], pk[6], pk[7]));
+}
+__device__ __forceinline__ void xchg_load(const char *blk, int lane, uint32_t pk[8])
+{
+    const uint4 lo = ld16(blk + 16 * lane), hi = ld16(blk + 1024 + 16 * lane);
+    pk[0] = lo.x, pk[1] = lo.y, pk[2] = lo.z, pk[3] = lo.w;
+    pk[4] = hi.x, pk[5] = hi.y, pk[6] = hi.z, pk[7] = hi.w;
+}
+
+// s_waitcnt lgkmcnt(0): this wave's LDS writes are done (before a barrier that publishes them).
+__device__ __forceinline__ void wait_lds()
+{
+    compiler_fence();
+    __builtin_amdgcn_s_waitcnt(0xc07f); // vmcnt 63, expcnt 7, lgkmcnt 0
+    compiler_fence();
+}
 
 // What one lane needs to issue the direct-to-LDS loads of a Q / dO tile.
 struct QLoader {
@@ -137,7 +164,7 @@ struct Blk {
     const char *q, *g;
     const float *lse, *dsum;
     int row0;
-    bool full; // every row of the block sees every key of the wave
+    bool full; // every row of the block sees every key of the pair
 };
 
 // A operand of S / dP, k-step s: 16 B of row n of the block, dims 16 s + 8 J.
@@ -161,7 +188,7 @@ __device__ __forceinline__ bf16x8 half_op(const uint32_t x[8], int u)
     return as_bf16x8(make_uint4(x[4 * u], x[4 * u + 1], x[4 * u + 2], x[4 * u + 3]));
 }
 
-// Per-lane constants of the dK / dV wave.
+// Per-lane constants of a dK / dV wave.
 struct KvLane {
     uint32_t rowA;    // A-operand read offset (row n, chunk J)
     uint32_t trA[2];  // transposed-read offsets (16-row halves' lower and upper 8 rows)
@@ -170,128 +197,137 @@ struct KvLane {
     float sl;         // scale * log2(e)
 };
 
-// One pipeline step of a wave over 32-row blocks: with C, dV^T += dO^T P and dK^T += Q^T dS of an
-// older block (bc; its packed P and dS in pkc, skc); with S, S = Q K^T and dP = dO V^T of a new block
-// (bs) into sc, dp; with P, P = exp(scale S - lse) and dS = P (dP - Dsum) of the block in between (bp;
-// its scores scp, dpp) into pkn, skn, zero where the row does not see the key.  The 8 k-steps issue up to 4 MFMAs each, operands read two
-// k-steps ahead, and two of the 16 P / dS elements are placed between the MFMAs of each k-step.
-// Register i of a score block <-> row 8 (i/4) + 4 J + i%4 of the block; pk[j] packs registers 2j, 2j+1.
-template <bool C, bool S, bool P>
-__device__ __forceinline__ void kv_step(const KvLane &L, const bf16x8 kop[8], const bf16x8 vop[8], f32x16 dk[4],
-                                        f32x16 dv[4], const Blk &bc, const uint32_t pkc[8], const uint32_t skc[8],
-                                        const Blk &bs, f32x16 &sc, f32x16 &dp, const Blk &bp, const f32x16 &scp,
-                                        const f32x16 &dpp, uint32_t pkn[8], uint32_t skn[8])
+// One k-loop of a pair wave (8 k-steps, operands read two k-steps ahead).  With X: x = rows * bop, the
+// first product of a new block (S = Q K^T for the P wave, dP = dO V^T for the dS wave).  With Y:
+// acc += cols * yop, the second product of an older block (dV^T += dO^T P, dK^T += Q^T dS).  With F:
+// two elements per k-step of a block whose first product is done (fin): the P wave forms
+// P = exp2(scale log2(e) S - lse2), zeroed where the row does not see the key; the dS wave forms
+// dS = P (dP - Dsum) from that P (pin).  Register i of a block <-> row 8 (i/4) + 4 J + i%4 of the block
+// and the lane's key; fout[j] packs registers 2j, 2j+1.
+template <bool PW, bool X, bool Y, bool F>
+__device__ __forceinline__ void pair_phase(const KvLane &L, const bf16x8 bop[8], f32x16 acc[4], const char *xrows,
+                                           f32x16 &x, const char *ycols, const uint32_t yop[8], const Blk &bf,
+                                           const f32x16 &fin, const uint32_t pin[8], uint32_t fout[8])
 {
-    if (S) {
+    if (X) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            sc[i] = 0.f;
-            dp[i] = 0.f;
-        }
+        for (int i = 0; i < 16; ++i)
+            x[i] = 0.f;
     }
-    bf16x8 cg0, cq0, cg1, cq1, aq0, ag0, aq1, ag1;
-    if (C) {
-        cg0 = rd_cols(bc.g, L.trA, 0, 0);
-        cq0 = rd_cols(bc.q, L.trA, 0, 0);
-        cg1 = rd_cols(bc.g, L.trA, 0, 1);
-        cq1 = rd_cols(bc.q, L.trA, 0, 1);
+    bf16x8 x0, x1, y0, y1;
+    if (X) {
+        x0 = rd_rows(xrows, L.rowA, 0);
+        x1 = rd_rows(xrows, L.rowA, 1);
     }
-    if (S) {
-        aq0 = rd_rows(bs.q, L.rowA, 0);
-        ag0 = rd_rows(bs.g, L.rowA, 0);
-        aq1 = rd_rows(bs.q, L.rowA, 1);
-        ag1 = rd_rows(bs.g, L.rowA, 1);
+    if (Y) {
+        y0 = rd_cols(ycols, L.trA, 0, 0);
+        y1 = rd_cols(ycols, L.trA, 0, 1);
     }
-    float4 l4, d4;
-    if (P) {
-        l4 = *reinterpret_cast<const float4 *>(bp.lse + 4 * L.J);
-        d4 = *reinterpret_cast<const float4 *>(bp.dsum + 4 * L.J);
-    }
+    const float *fv = PW ? bf.lse : bf.dsum;
+    float4 v4;
+    if (F)
+        v4 = *reinterpret_cast<const float4 *>(fv + 4 * L.J);
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
         const int u = k >> 2, db = k & 3;
-        bf16x8 cg2 = cg0, cq2 = cq0, aq2 = aq0, ag2 = ag0;
+        bf16x8 x2 = x0, y2 = y0;
         if (k + 2 < 8) {
-            if (C) {
-                cg2 = rd_cols(bc.g, L.trA, (k + 2) >> 2, (k + 2) & 3);
-                cq2 = rd_cols(bc.q, L.trA, (k + 2) >> 2, (k + 2) & 3);
-            }
-            if (S) {
-                aq2 = rd_rows(bs.q, L.rowA, k + 2);
-                ag2 = rd_rows(bs.g, L.rowA, k + 2);
-            }
+            if (X)
+                x2 = rd_rows(xrows, L.rowA, k + 2);
+            if (Y)
+                y2 = rd_cols(ycols, L.trA, (k + 2) >> 2, (k + 2) & 3);
         }
-        float4 l4n = l4, d4n = d4;
-        if (P && (k & 1) && k < 7) {
-            const int i4 = (k + 1) >> 1;
-            l4n = *reinterpret_cast<const float4 *>(bp.lse + 8 * i4 + 4 * L.J);
-            d4n = *reinterpret_cast<const float4 *>(bp.dsum + 8 * i4 + 4 * L.J);
-        }
-        if (C)
-            dv[db] = mfma32(cg0, half_op(pkc, u), dv[db]);
-        if (S)
-            sc = mfma32(aq0, kop[k], sc);
-        if (P) {
+        float4 v4n = v4;
+        if (F && (k & 1) && k < 7)
+            v4n = *reinterpret_cast<const float4 *>(fv + 8 * ((k + 1) >> 1) + 4 * L.J);
+        if (X)
+            x = mfma32(x0, bop[k], x);
+        if (F) {
             // registers 2k, 2k+1: rows 8 (k/2) + 4 J + 2 (k%2) + {0, 1}
-            const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dsv[4] = {d4.x, d4.y, d4.z, d4.w};
-            float p[2], ds[2];
+            const float vv[4] = {v4.x, v4.y, v4.z, v4.w};
+            float o[2];
 #pragma unroll
             for (int e = 0; e < 2; ++e) {
                 const int i = 2 * k + e, r = i & 3;
-                p[e] = exp2_fast(fmaf(scp[i], L.sl, -lv[r]));
-                ds[e] = p[e] * (dpp[i] - dsv[r]);
+                if (PW)
+                    o[e] = exp2_fast(fmaf(fin[i], L.sl, -vv[r]));
+                else
+                    o[e] = (e ? bf16_hi(pin[k]) : bf16_lo(pin[k])) * (fin[i] - vv[r]);
             }
-            pkn[k] = pack_bf16x2(p[0], p[1]);
-            skn[k] = pack_bf16x2(ds[0], ds[1]);
-            anchor(pkn[k]);
-            anchor(skn[k]);
+            fout[k] = pack_bf16x2(o[0], o[1]);
+            anchor(fout[k]);
         }
-        if (C)
-            dk[db] = mfma32(cq0, half_op(skc, u), dk[db]);
-        if (S)
-            dp = mfma32(ag0, vop[k], dp);
+        if (Y)
+            acc[db] = mfma32(y0, half_op(yop, u), acc[db]);
         sched_fence();
-        cg0 = cg1;
-        cq0 = cq1;
-        cg1 = cg2;
-        cq1 = cq2;
-        aq0 = aq1;
-        ag0 = ag1;
-        aq1 = aq2;
-        ag1 = ag2;
-        if (k & 1) {
-            l4 = l4n;
-            d4 = d4n;
-        }
+        x0 = x1;
+        x1 = x2;
+        y0 = y1;
+        y1 = y2;
+        if (k & 1)
+            v4 = v4n;
     }
-    // Blocks that cross the causal diagonal or an end of the sequence: zero the entries whose row does
-    // not see the lane's key (their values above may be anything, infinities and NaN included, since
-    // rows past the sequence and keys past the diagonal were not kept out of the exponentials).
-    if (P && !bp.full) {
+    // The P wave, on blocks that cross the causal diagonal or an end of the sequence: zero the entries
+    // whose row does not see the lane's key (their values above may be anything, infinities and NaN
+    // included, since rows past the sequence and keys past the diagonal were not kept out of the
+    // exponentials).  The dS wave needs no mask: its P is zero there and dP - Dsum is finite (rows past
+    // the sequence and keys past it load as zero).
+    if (F && PW && !bf.full) {
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
             uint32_t m = 0;
 #pragma unroll
             for (int e = 0; e < 2; ++e) {
                 const int i = 2 * k + e;
-                const int row = bp.row0 + 8 * (i >> 2) + 4 * L.J + (i & 3);
+                const int row = bf.row0 + 8 * (i >> 2) + 4 * L.J + (i & 3);
                 if ((uint32_t)(row - L.lo_row) < (uint32_t)L.span)
                     m |= 0xffffu << (16 * e);
             }
-            pkn[k] &= m;
-            skn[k] &= m;
+            fout[k] &= m;
         }
     }
 }
 
-// dK, dV of 128 keys of one (sequence, KV head): wave w owns keys kb0 + 32 w .. +31, whose K and V stay in
-// registers as the B operands of S = Q K^T and dP = dO V^T.  The loop runs over the query heads of the
-// group and, per head, over the 64-row query tiles that see any of the keys, last tile first, staged in a
-// three-stage direct-to-LDS ring.  A wave works in 32-row blocks through a three-deep software pipeline: while the
-// MFMAs of S and dP [32 rows x 32 keys] of block j run (A operands: 16-B LDS reads of Q and dO rows),
-// so do those of dV^T += dO^T P and dK^T += Q^T dS [128 dims x 32 keys] of block j-2 (A operands:
-// transposed LDS reads), and P and dS of block j-1 are computed between them.  P and dS feed the B
-// operand from registers in the S register order.
+// The P wave's work on one staged tile (blocks b0, b1): S of b0; S of b1 with P of b0; dV^T += dO^T P
+// of b0 with P of b1; dV^T of b1.  Each block's P goes to the exchange (xb) as soon as it is formed.
+__device__ __forceinline__ void p_wave_tile(const KvLane &L, const bf16x8 kop[8], f32x16 dv[4], const Blk &b0,
+                                            const Blk &b1, char *xb, int lane)
+{
+    f32x16 s0, s1;
+    uint32_t p0[8], p1[8];
+    pair_phase<true, true, false, false>(L, kop, dv, b0.q, s0, nullptr, p0, b0, s0, p0, p0);
+    pair_phase<true, true, false, true>(L, kop, dv, b1.q, s1, nullptr, p0, b0, s0, p0, p0);
+    xchg_store(xb, lane, p0);
+    pair_phase<true, false, true, true>(L, kop, dv, nullptr, s1, b0.g, p0, b1, s1, p1, p1);
+    xchg_store(xb + kXchgBlock, lane, p1);
+    pair_phase<true, false, true, false>(L, kop, dv, nullptr, s1, b1.g, p1, b1, s1, p1, p1);
+}
+
+// The dS wave's work on one staged tile, one tile behind its P wave (P of the tile in xb): dP of b0;
+// dP of b1 with dS of b0; dK^T += Q^T dS of b0 with dS of b1; dK^T of b1.
+__device__ __forceinline__ void ds_wave_tile(const KvLane &L, const bf16x8 vop[8], f32x16 dk[4], const Blk &b0,
+                                             const Blk &b1, const char *xb, int lane)
+{
+    f32x16 d0, d1;
+    uint32_t p0[8], p1[8], t0[8], t1[8];
+    xchg_load(xb, lane, p0);
+    xchg_load(xb + kXchgBlock, lane, p1);
+    pair_phase<false, true, false, false>(L, vop, dk, b0.g, d0, nullptr, t0, b0, d0, p0, t0);
+    pair_phase<false, true, false, true>(L, vop, dk, b1.g, d1, nullptr, t0, b0, d0, p0, t0);
+    pair_phase<false, false, true, true>(L, vop, dk, nullptr, d1, b0.q, t0, b1, d1, p1, t1);
+    pair_phase<false, false, true, false>(L, vop, dk, nullptr, d1, b1.q, t1, b1, d1, p1, t1);
+}
+
+// dK, dV of 128 keys of one (sequence, KV head), two waves per SIMD: 4 pairs of waves, pair p owning keys
+// kb0 + 32 p .. +31.  The pair's P wave keeps K of its keys in registers (the B operand of S = Q K^T),
+// forms P and accumulates dV^T = sum dO^T P; its dS wave keeps V (the B operand of dP = dO V^T), takes P
+// from the P wave through LDS, forms dS and accumulates dK^T = sum Q^T dS.  The loop runs over the query
+// heads of the group and, per head, over the 64-row query tiles that see any of the keys, last tile
+// first, staged in a three-stage direct-to-LDS ring; the dS waves run one tile behind the P waves, so
+// one barrier per tile publishes both the tile and the P of the tile before it.  Both waves of a pair
+// work through a tile's two 32-row blocks in the same four phases (first product of block 0; of block 1
+// with the elementwise step of block 0; second product of block 0 with the elementwise step of block 1;
+// second product of block 1); the other wave of the SIMD fills the gaps.
 __global__ __launch_bounds__(kKvThreads) void bwd_dkdv_kernel(BwdArgs a, int nkt, int nunits)
 {
     // XCD-aware order: block i runs on XCD i % 8, which takes a contiguous run of units ordered (KV
@@ -313,9 +349,11 @@ __global__ __launch_bounds__(kKvThreads) void bwd_dkdv_kernel(BwdArgs a, int nkt
         return;
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int pair = w % kKvPairs;
+    const bool pwave = w < kKvPairs; // waves p and p + 4 form pair p
     const int n = lane & 31, J = lane >> 5;
-    const int kw = kb0 + kKeysPerWave * w; // the wave's first key
-    const int key = kw + n;                // the lane's key (MFMA column)
+    const int kw = kb0 + kKeysPerPair * pair; // the pair's first key
+    const int key = kw + n;                   // the lane's key (MFMA column)
     const int diag = Lk - Lq;
 
     KvLane L;
@@ -336,30 +374,26 @@ __global__ __launch_bounds__(kKvThreads) void bwd_dkdv_kernel(BwdArgs a, int nkt
         }
     }
 
-    // K and V as B operands: lane (key n, J) holds dims 16 s + 8 J .. +8
-    bf16x8 kop[8], vop[8];
+    // K (P wave) or V (dS wave) as the B operand: lane (key n, J) holds dims 16 s + 8 J .. +8
+    bf16x8 bop[8];
     {
-        const uint16_t *kg = static_cast<const uint16_t *>(a.k), *vg = static_cast<const uint16_t *>(a.v);
+        const uint16_t *src = static_cast<const uint16_t *>(pwave ? a.k : a.v);
 #pragma unroll
         for (int s = 0; s < 8; ++s) {
-            uint4 kv = make_uint4(0, 0, 0, 0), vv = make_uint4(0, 0, 0, 0);
-            if (key < Lk) {
-                const size_t off = ((size_t)(k0 + key) * a.Hkv + g) * D + 16 * s + 8 * J;
-                kv = ld16(kg + off);
-                vv = ld16(vg + off);
-            }
-            kop[s] = as_bf16x8(kv);
-            vop[s] = as_bf16x8(vv);
+            uint4 v = make_uint4(0, 0, 0, 0);
+            if (key < Lk)
+                v = ld16(src + ((size_t)(k0 + key) * a.Hkv + g) * D + 16 * s + 8 * J);
+            bop[s] = as_bf16x8(v);
         }
     }
-    f32x16 dk[4], dv[4]; // [128 dims x 32 keys] in blocks db of 32 dims: register i <-> dim 32 db + 8 (i/4) + 4 J + i%4
+    // dV^T (P wave) or dK^T (dS wave) [128 dims x 32 keys] in blocks db of 32 dims: register i <-> dim
+    // 32 db + 8 (i/4) + 4 J + i%4
+    f32x16 acc[4];
 #pragma unroll
     for (int db = 0; db < 4; ++db)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            dk[db][i] = 0.f;
-            dv[db][i] = 0.f;
-        }
+        for (int i = 0; i < 16; ++i)
+            acc[db][i] = 0.f;
 
     QLoader ld;
     {
@@ -406,66 +440,59 @@ __global__ __launch_bounds__(kKvThreads) void bwd_dkdv_kernel(BwdArgs a, int nkt
         x.lse = q_ring[t.st].lse + 32 * rb;
         x.dsum = q_ring[t.st].dsum + 32 * rb;
         x.row0 = t.row0 + 32 * rb;
-        x.full = x.row0 + 32 <= Lq && kw + kKeysPerWave <= Lk &&
-                 (!a.causal || kw + kKeysPerWave - 1 - diag <= x.row0);
+        x.full = x.row0 + 32 <= Lq && kw + kKeysPerPair <= Lk &&
+                 (!a.causal || kw + kKeysPerPair - 1 - diag <= x.row0);
         return x;
-    };
-    // tile t (in `cur`) was loaded one tile ahead; its stage is read until the step that finishes its
-    // blocks, two tiles later
-    auto next_tile = [&](const Tile &cur, int t) {
-        wait_vmcnt<0>();
-        barrier(); // tile t is in LDS for every wave; every wave is done with tile t - 2
-        if (t + 1 < ntiles) {
-            const Tile nx = advance(cur);
-            ld.issue(nx.st, nx.row0, nx.h);
-        }
     };
 
     if (ntiles > 0) {
-        f32x16 sc, dp, scp, dpp;
-        uint32_t pka[8], ska[8], pkb[8], skb[8];
-        Tile prev{0, row_last, g * a.G};
-        ld.issue(prev.st, prev.row0, prev.h);
-        // steps 0 and 1: S of blocks 0, 1; P of block 0
-        next_tile(prev, 0);
-        {
-            const Blk b0 = blk(prev, 0), b1 = blk(prev, 1);
-            kv_step<false, true, false>(L, kop, vop, dk, dv, b0, pka, ska, b0, scp, dpp, b0, sc, dp, pkb, skb);
-            kv_step<false, true, true>(L, kop, vop, dk, dv, b0, pka, ska, b1, sc, dp, b0, scp, dpp, pkb, skb);
-        }
-        // tile t: step 2t runs C of block 2t-2, S of block 2t, P of block 2t-1; step 2t+1 one block later.
-        // At its start pkb/skb hold P, dS of block 2t-2 and sc, dp the scores of block 2t-1.
-        for (int t = 1; t < ntiles; ++t) {
-            const Tile cur = advance(prev);
-            next_tile(cur, t);
-            const Blk bm2 = blk(prev, 0), bm1 = blk(prev, 1), bj = blk(cur, 0), bj1 = blk(cur, 1);
-            kv_step<true, true, true>(L, kop, vop, dk, dv, bm2, pkb, skb, bj, scp, dpp, bm1, sc, dp, pka, ska);
-            kv_step<true, true, true>(L, kop, vop, dk, dv, bm1, pka, ska, bj1, sc, dp, bj, scp, dpp, pkb, skb);
-            prev = cur;
-        }
-        // the last two steps: C of the last two blocks; P of the last block
-        {
-            const Blk bm2 = blk(prev, 0), bm1 = blk(prev, 1);
-            kv_step<true, false, true>(L, kop, vop, dk, dv, bm2, pkb, skb, bm2, scp, dpp, bm1, sc, dp, pka, ska);
-            kv_step<true, false, false>(L, kop, vop, dk, dv, bm1, pka, ska, bm1, scp, dpp, bm1, sc, dp, pkb, skb);
+        // step s: the P waves work on tile s, the dS waves on tile s - 1.  At its barrier tile s is in LDS
+        // and so is the P of tile s - 1, and every wave is done with tile s - 2 (stage and exchange).  Each
+        // role runs its own loop (one set of registers for its accumulators); both pass ntiles + 1
+        // barriers.
+        Tile cur{0, row_last, g * a.G};
+        ld.issue(cur.st, cur.row0, cur.h);
+        auto sync = [&](int s, Tile &c) {
+            wait_vmcnt<0>();
+            wait_lds();
+            barrier();
+            if (s + 1 < ntiles) {
+                c = advance(c);
+                ld.issue(c.st, c.row0, c.h);
+            }
+        };
+        if (pwave) {
+            for (int s = 0; s < ntiles; ++s) {
+                const Tile t = cur; // tile s
+                sync(s, cur);
+                p_wave_tile(L, bop, acc, blk(t, 0), blk(t, 1), p_xchg[s & 1][pair], lane);
+            }
+            sync(ntiles, cur);
+        } else {
+            Tile prev = cur;
+            sync(0, cur);
+            for (int s = 1; s <= ntiles; ++s) {
+                const Tile t = prev; // tile s - 1
+                prev = cur;
+                sync(s, cur);
+                ds_wave_tile(L, bop, acc, blk(t, 0), blk(t, 1), p_xchg[(s - 1) & 1][pair], lane);
+            }
         }
     }
 
     if (key >= Lk)
         return;
-    uint16_t *dkg = static_cast<uint16_t *>(a.dk) + ((size_t)(k0 + key) * a.Hkv + g) * D + 4 * J;
-    uint16_t *dvg = static_cast<uint16_t *>(a.dv) + ((size_t)(k0 + key) * a.Hkv + g) * D + 4 * J;
+    // the P wave writes dV, the dS wave dK = scale dS^T Q
+    const float f = pwave ? 1.f : a.scale;
+    uint16_t *dst = static_cast<uint16_t *>(pwave ? a.dv : a.dk) + ((size_t)(k0 + key) * a.Hkv + g) * D + 4 * J;
 #pragma unroll
     for (int db = 0; db < 4; ++db)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            uint2 pk, pv;
-            pk.x = pack_bf16x2(dk[db][4 * r] * a.scale, dk[db][4 * r + 1] * a.scale);
-            pk.y = pack_bf16x2(dk[db][4 * r + 2] * a.scale, dk[db][4 * r + 3] * a.scale);
-            pv.x = pack_bf16x2(dv[db][4 * r], dv[db][4 * r + 1]);
-            pv.y = pack_bf16x2(dv[db][4 * r + 2], dv[db][4 * r + 3]);
-            *reinterpret_cast<uint2 *>(dkg + 32 * db + 8 * r) = pk;
-            *reinterpret_cast<uint2 *>(dvg + 32 * db + 8 * r) = pv;
+            uint2 pk;
+            pk.x = pack_bf16x2(acc[db][4 * r] * f, acc[db][4 * r + 1] * f);
+            pk.y = pack_bf16x2(acc[db][4 * r + 2] * f, acc[db][4 * r + 3] * f);
+            *reinterpret_cast<uint2 *>(dst + 32 * db + 8 * r) = pk;
         }
 }
 
