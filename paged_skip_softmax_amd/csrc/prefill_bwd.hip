@@ -112,16 +112,22 @@ __shared__ QStage q_ring[kQStages];
 constexpr int kXchgBlock = 2048;
 __shared__ __attribute__((aligned(1024))) char p_xchg[2][kKvPairs][2 * kXchgBlock];
 
-__device__ __forceinline__ void xchg_store(char *blk, int lane, const uint32_t pk[8])
+// A block's packed P or dS: word j of half u packs registers 8u + 2j, 8u + 2j + 1 (one 16-row half of the
+// MFMA B operand per half).
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+struct Packed {
+    u32x4 h[2];
+};
+
+__device__ __forceinline__ void xchg_store(char *blk, int lane, const Packed &pk)
 {
-    st16(blk + 16 * lane, make_uint4(pk[0], pk[1], pk[2], pk[3]));
-    st16(blk + 1024 + 16 * lane, make_uint4(pk[4], pk[5], pk[6], pk[7]));
+    *reinterpret_cast<u32x4 *>(blk + 16 * lane) = pk.h[0];
+    *reinterpret_cast<u32x4 *>(blk + 1024 + 16 * lane) = pk.h[1];
 }
-__device__ __forceinline__ void xchg_load(const char *blk, int lane, uint32_t pk[8])
+__device__ __forceinline__ void xchg_load(const char *blk, int lane, Packed &pk)
 {
-    const uint4 lo = ld16(blk + 16 * lane), hi = ld16(blk + 1024 + 16 * lane);
-    pk[0] = lo.x, pk[1] = lo.y, pk[2] = lo.z, pk[3] = lo.w;
-    pk[4] = hi.x, pk[5] = hi.y, pk[6] = hi.z, pk[7] = hi.w;
+    pk.h[0] = *reinterpret_cast<const u32x4 *>(blk + 16 * lane);
+    pk.h[1] = *reinterpret_cast<const u32x4 *>(blk + 1024 + 16 * lane);
 }
 
 // s_waitcnt lgkmcnt(0): this wave's LDS writes are done (before a barrier that publishes them).
@@ -183,10 +189,6 @@ __device__ __forceinline__ bf16x8 rd_cols(const char *rows, const uint32_t trA[2
     return as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
 }
 
-__device__ __forceinline__ bf16x8 half_op(const uint32_t x[8], int u)
-{
-    return as_bf16x8(make_uint4(x[4 * u], x[4 * u + 1], x[4 * u + 2], x[4 * u + 3]));
-}
 
 // Per-lane constants of a dK / dV wave.
 struct KvLane {
@@ -204,24 +206,26 @@ struct KvLane {
 // P = exp2(scale log2(e) S - lse2), zeroed where the row does not see the key; the dS wave forms
 // dS = P (dP - Dsum) from that P (pin).  Register i of a block <-> row 8 (i/4) + 4 J + i%4 of the block
 // and the lane's key; fout[j] packs registers 2j, 2j+1.
+constexpr int kPairAhead = 2; // k-steps of LDS operands in flight in a pair wave
+
 template <bool PW, bool X, bool Y, bool F>
 __device__ __forceinline__ void pair_phase(const KvLane &L, const bf16x8 bop[8], f32x16 acc[4], const char *xrows,
-                                           f32x16 &x, const char *ycols, const uint32_t yop[8], const Blk &bf,
-                                           const f32x16 &fin, const uint32_t pin[8], uint32_t fout[8])
+                                           f32x16 &x, const char *ycols, const Packed &yop, const Blk &bf,
+                                           const f32x16 &fin, const Packed &pin, Packed &fout)
 {
     if (X) {
 #pragma unroll
         for (int i = 0; i < 16; ++i)
             x[i] = 0.f;
     }
-    bf16x8 x0, x1, y0, y1;
-    if (X) {
-        x0 = rd_rows(xrows, L.rowA, 0);
-        x1 = rd_rows(xrows, L.rowA, 1);
-    }
-    if (Y) {
-        y0 = rd_cols(ycols, L.trA, 0, 0);
-        y1 = rd_cols(ycols, L.trA, 0, 1);
+    // operands of k-steps k .. k + kPairAhead - 1 in flight (xq[j], yq[j] hold k-step k + j)
+    bf16x8 xq[kPairAhead + 1], yq[kPairAhead + 1];
+#pragma unroll
+    for (int j = 0; j < kPairAhead; ++j) {
+        if (X)
+            xq[j] = rd_rows(xrows, L.rowA, j);
+        if (Y)
+            yq[j] = rd_cols(ycols, L.trA, j >> 2, j & 3);
     }
     const float *fv = PW ? bf.lse : bf.dsum;
     float4 v4;
@@ -230,18 +234,17 @@ __device__ __forceinline__ void pair_phase(const KvLane &L, const bf16x8 bop[8],
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
         const int u = k >> 2, db = k & 3;
-        bf16x8 x2 = x0, y2 = y0;
-        if (k + 2 < 8) {
+        if (k + kPairAhead < 8) {
             if (X)
-                x2 = rd_rows(xrows, L.rowA, k + 2);
+                xq[kPairAhead] = rd_rows(xrows, L.rowA, k + kPairAhead);
             if (Y)
-                y2 = rd_cols(ycols, L.trA, (k + 2) >> 2, (k + 2) & 3);
+                yq[kPairAhead] = rd_cols(ycols, L.trA, (k + kPairAhead) >> 2, (k + kPairAhead) & 3);
         }
         float4 v4n = v4;
         if (F && (k & 1) && k < 7)
             v4n = *reinterpret_cast<const float4 *>(fv + 8 * ((k + 1) >> 1) + 4 * L.J);
         if (X)
-            x = mfma32(x0, bop[k], x);
+            x = mfma32(xq[0], bop[k], x);
         if (F) {
             // registers 2k, 2k+1: rows 8 (k/2) + 4 J + 2 (k%2) + {0, 1}
             const float vv[4] = {v4.x, v4.y, v4.z, v4.w};
@@ -252,18 +255,19 @@ __device__ __forceinline__ void pair_phase(const KvLane &L, const bf16x8 bop[8],
                 if (PW)
                     o[e] = exp2_fast(fmaf(fin[i], L.sl, -vv[r]));
                 else
-                    o[e] = (e ? bf16_hi(pin[k]) : bf16_lo(pin[k])) * (fin[i] - vv[r]);
+                    o[e] = (e ? bf16_hi(pin.h[u][k & 3]) : bf16_lo(pin.h[u][k & 3])) * (fin[i] - vv[r]);
             }
-            fout[k] = pack_bf16x2(o[0], o[1]);
-            anchor(fout[k]);
+            fout.h[u][k & 3] = pack_bf16x2(o[0], o[1]);
+            anchor(fout.h[u][k & 3]);
         }
         if (Y)
-            acc[db] = mfma32(y0, half_op(yop, u), acc[db]);
+            acc[db] = mfma32(yq[0], __builtin_bit_cast(bf16x8, yop.h[u]), acc[db]);
         sched_fence();
-        x0 = x1;
-        x1 = x2;
-        y0 = y1;
-        y1 = y2;
+#pragma unroll
+        for (int j = 0; j < kPairAhead; ++j) {
+            xq[j] = xq[j + 1];
+            yq[j] = yq[j + 1];
+        }
         if (k & 1)
             v4 = v4n;
     }
@@ -283,39 +287,74 @@ __device__ __forceinline__ void pair_phase(const KvLane &L, const bf16x8 bop[8],
                 if ((uint32_t)(row - L.lo_row) < (uint32_t)L.span)
                     m |= 0xffffu << (16 * e);
             }
-            fout[k] &= m;
+            fout.h[k >> 2][k & 3] &= m;
         }
     }
 }
 
-// The P wave's work on one staged tile (blocks b0, b1): S of b0; S of b1 with P of b0; dV^T += dO^T P
-// of b0 with P of b1; dV^T of b1.  Each block's P goes to the exchange (xb) as soon as it is formed.
+// The P wave's work on one staged tile (blocks b0, b1): S of b0, with dV^T += dO^T P of the previous
+// tile's second block when there is one (First false; its P in pl, its dO rows in gl); S of b1 with P of
+// b0; dV^T of b0 with P of b1 (into pl, for the next tile).  Each block's P goes to the exchange (xb) as
+// soon as it is formed.  The previous tile's stage is still in LDS: it is overwritten two tiles later.
+template <bool First>
 __device__ __forceinline__ void p_wave_tile(const KvLane &L, const bf16x8 kop[8], f32x16 dv[4], const Blk &b0,
-                                            const Blk &b1, char *xb, int lane)
+                                            const Blk &b1, const char *gl, Packed &pl, char *xb, int lane)
 {
     f32x16 s0, s1;
-    uint32_t p0[8], p1[8];
-    pair_phase<true, true, false, false>(L, kop, dv, b0.q, s0, nullptr, p0, b0, s0, p0, p0);
+    Packed p0;
+    pair_phase<true, true, !First, false>(L, kop, dv, b0.q, s0, gl, pl, b0, s0, pl, pl);
     pair_phase<true, true, false, true>(L, kop, dv, b1.q, s1, nullptr, p0, b0, s0, p0, p0);
     xchg_store(xb, lane, p0);
-    pair_phase<true, false, true, true>(L, kop, dv, nullptr, s1, b0.g, p0, b1, s1, p1, p1);
-    xchg_store(xb + kXchgBlock, lane, p1);
-    pair_phase<true, false, true, false>(L, kop, dv, nullptr, s1, b1.g, p1, b1, s1, p1, p1);
+    pair_phase<true, false, true, true>(L, kop, dv, nullptr, s1, b0.g, p0, b1, s1, pl, pl);
+    xchg_store(xb + kXchgBlock, lane, pl);
 }
 
-// The dS wave's work on one staged tile, one tile behind its P wave (P of the tile in xb): dP of b0;
-// dP of b1 with dS of b0; dK^T += Q^T dS of b0 with dS of b1; dK^T of b1.
+// The dS wave's work on one staged tile T, one tile behind its P wave (P of T in xb), whose first
+// block's dP (dn) was formed during the step before: dP of b1 with dS of b0; dK^T += Q^T dS of b0 with dS
+// of b1; dK^T of b1 with dP of the next tile's first block nb into dn (nb is already in LDS: it is the P
+// wave's tile of this step; after the last tile nb is any resident block and dn goes unused).
 __device__ __forceinline__ void ds_wave_tile(const KvLane &L, const bf16x8 vop[8], f32x16 dk[4], const Blk &b0,
-                                             const Blk &b1, const char *xb, int lane)
+                                             const Blk &b1, const Blk &nb, f32x16 &dn, const char *xb, int lane)
 {
-    f32x16 d0, d1;
-    uint32_t p0[8], p1[8], t0[8], t1[8];
+    f32x16 d1;
+    Packed p0, p1, t0, t1;
     xchg_load(xb, lane, p0);
     xchg_load(xb + kXchgBlock, lane, p1);
-    pair_phase<false, true, false, false>(L, vop, dk, b0.g, d0, nullptr, t0, b0, d0, p0, t0);
-    pair_phase<false, true, false, true>(L, vop, dk, b1.g, d1, nullptr, t0, b0, d0, p0, t0);
+    pair_phase<false, true, false, true>(L, vop, dk, b1.g, d1, nullptr, t0, b0, dn, p0, t0);
     pair_phase<false, false, true, true>(L, vop, dk, nullptr, d1, b0.q, t0, b1, d1, p1, t1);
-    pair_phase<false, false, true, false>(L, vop, dk, nullptr, d1, b1.q, t1, b1, d1, p1, t1);
+    pair_phase<false, true, true, false>(L, vop, dk, nb.g, dn, b1.q, t1, nb, d1, p1, t1);
+}
+
+// Sequences are taken in decreasing order of work (Lq * Lk; ties by index) when there are at most
+// kRankMaxBatch of them: each workgroup finds the sequence of rank r itself, from the lengths staged in
+// LDS.  The largest units then start first and the last ones to run are short, which shortens the tail of
+// the launch (each unit of a long sequence walks many query tiles).  Larger batches keep index order.
+constexpr int kRankMaxBatch = 128;
+__shared__ long long seq_work[kRankMaxBatch];
+__shared__ int seq_pick;
+
+__device__ __forceinline__ int seq_by_work(const int32_t *cu_q, const int32_t *cu_k, int B, int r)
+{
+    if (B > kRankMaxBatch)
+        return r;
+    for (int i = threadIdx.x; i < B; i += blockDim.x)
+        seq_work[i] = (long long)(cu_q[i + 1] - cu_q[i]) * (cu_k[i + 1] - cu_k[i]);
+    if (threadIdx.x == 0)
+        seq_pick = r;
+    __syncthreads();
+    // the ranks are a permutation of 0 .. B-1, so exactly one sequence has rank r
+    for (int i = threadIdx.x; i < B; i += blockDim.x) {
+        const long long wi = seq_work[i];
+        int rank = 0;
+        for (int j = 0; j < B; ++j) {
+            const long long wj = seq_work[j];
+            rank += (wj > wi) || (wj == wi && j < i);
+        }
+        if (rank == r)
+            seq_pick = i;
+    }
+    __syncthreads();
+    return seq_pick;
 }
 
 // dK, dV of 128 keys of one (sequence, KV head), two waves per SIMD: 4 pairs of waves, pair p owning keys
@@ -331,8 +370,8 @@ __device__ __forceinline__ void ds_wave_tile(const KvLane &L, const bf16x8 vop[8
 __global__ __launch_bounds__(kKvThreads) void bwd_dkdv_kernel(BwdArgs a, int nkt, int nunits)
 {
     // XCD-aware order: block i runs on XCD i % 8, which takes a contiguous run of units ordered (KV
-    // head, sequence, key block): each XCD serves whole KV heads of every sequence (even load), and the
-    // key blocks of one (sequence, KV head) are dispatched together.  Every key block walks its query
+    // head, sequence by decreasing work, key block): each XCD serves whole KV heads of every sequence
+    // (even load), and the key blocks of one (sequence, KV head) are dispatched together.  Every key block walks its query
     // tiles from the sequence's last one backwards (all key blocks see the last rows, under the causal
     // mask too), so the key blocks running together read the same Q and dO tiles at about the same
     // time and all but the first read of each come from the XCD's L2.
@@ -341,7 +380,7 @@ __global__ __launch_bounds__(kKvThreads) void bwd_dkdv_kernel(BwdArgs a, int nkt
     if (unit >= nunits)
         return;
     const int g = unit / (nkt * a.B), rem = unit % (nkt * a.B);
-    const int b = rem / nkt, kt = rem % nkt;
+    const int b = seq_by_work(a.cu_q, a.cu_k, a.B, rem / nkt), kt = rem % nkt;
     const int q0 = a.cu_q[b], Lq = a.cu_q[b + 1] - q0;
     const int k0 = a.cu_k[b], Lk = a.cu_k[b + 1] - k0;
     const int kb0 = kt * kKeysPerWg;
@@ -462,20 +501,39 @@ __global__ __launch_bounds__(kKvThreads) void bwd_dkdv_kernel(BwdArgs a, int nkt
             }
         };
         if (pwave) {
-            for (int s = 0; s < ntiles; ++s) {
+            Packed pl; // P of the last tile's second block, whose dV^T product runs with the next tile
+            const char *gl;
+            {
+                const Tile t = cur; // tile 0
+                sync(0, cur);
+                const Blk b0 = blk(t, 0), b1 = blk(t, 1);
+                p_wave_tile<true>(L, bop, acc, b0, b1, nullptr, pl, p_xchg[0][pair], lane);
+                gl = b1.g;
+            }
+            for (int s = 1; s < ntiles; ++s) {
                 const Tile t = cur; // tile s
                 sync(s, cur);
-                p_wave_tile(L, bop, acc, blk(t, 0), blk(t, 1), p_xchg[s & 1][pair], lane);
+                const Blk b0 = blk(t, 0), b1 = blk(t, 1);
+                p_wave_tile<false>(L, bop, acc, b0, b1, gl, pl, p_xchg[s & 1][pair], lane);
+                gl = b1.g;
             }
             sync(ntiles, cur);
+            f32x16 unused;
+            pair_phase<true, false, true, false>(L, bop, acc, nullptr, unused, gl, pl, blk(cur, 0), unused, pl, pl);
         } else {
             Tile prev = cur;
+            f32x16 dn; // dP of the first block of the next tile
             sync(0, cur);
+            {
+                Packed none;
+                pair_phase<false, true, false, false>(L, bop, acc, blk(prev, 0).g, dn, nullptr, none, blk(prev, 0),
+                                                      dn, none, none);
+            }
             for (int s = 1; s <= ntiles; ++s) {
                 const Tile t = prev; // tile s - 1
-                prev = cur;
+                prev = cur;          // tile s (when s < ntiles)
                 sync(s, cur);
-                ds_wave_tile(L, bop, acc, blk(t, 0), blk(t, 1), p_xchg[(s - 1) & 1][pair], lane);
+                ds_wave_tile(L, bop, acc, blk(t, 0), blk(t, 1), blk(prev, 0), dn, p_xchg[(s - 1) & 1][pair], lane);
             }
         }
     }
@@ -497,6 +555,12 @@ __global__ __launch_bounds__(kKvThreads) void bwd_dkdv_kernel(BwdArgs a, int nkt
 }
 
 // ------------------------------------------------------------------ dQ
+
+// Registers 8u .. 8u+7 of a packed block (x[j] packs registers 2j, 2j+1) as an MFMA operand.
+__device__ __forceinline__ bf16x8 half_op(const uint32_t x[8], int u)
+{
+    return as_bf16x8(make_uint4(x[4 * u], x[4 * u + 1], x[4 * u + 2], x[4 * u + 3]));
+}
 
 constexpr int kDqWaves = 4;
 constexpr int kDqThreads = 64 * kDqWaves;
