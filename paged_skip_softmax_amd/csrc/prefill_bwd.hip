@@ -556,13 +556,8 @@ __global__ __launch_bounds__(kKvThreads) void bwd_dkdv_kernel(BwdArgs a, int nkt
 
 // ------------------------------------------------------------------ dQ
 
-// Registers 8u .. 8u+7 of a packed block (x[j] packs registers 2j, 2j+1) as an MFMA operand.
-__device__ __forceinline__ bf16x8 half_op(const uint32_t x[8], int u)
-{
-    return as_bf16x8(make_uint4(x[4 * u], x[4 * u + 1], x[4 * u + 2], x[4 * u + 3]));
-}
-
-constexpr int kDqWaves = 4;
+constexpr int kDqPairs = 4;             // wave pairs per workgroup
+constexpr int kDqWaves = 2 * kDqPairs;  // two waves per SIMD
 constexpr int kDqThreads = 64 * kDqWaves;
 constexpr int kKTile = 64;                            // keys per staged tile
 constexpr int kKTileBytes = kKTile * kRowBytes;       // 16 KB
@@ -575,6 +570,9 @@ struct alignas(1024) KStage {
     char v[kKTileBytes];
 };
 __shared__ KStage k_ring[kKStages];
+
+// P^T of a 32-key block, from a pair's P wave to its dS wave (the layout of p_xchg).
+__shared__ __attribute__((aligned(1024))) char pt_xchg[2][kDqPairs][2 * kXchgBlock];
 
 struct KLoader {
     i32x4 krs, vrs;          // buffer resources of K, V (the sequence's rows of one KV head)
@@ -600,10 +598,10 @@ struct KLoader {
 struct KBlk {
     const char *k, *v;
     int kb;
-    bool full; // every row of the wave sees every key of the block
+    bool full; // every row of the pair sees every key of the block
 };
 
-// Per-lane constants of the dQ wave.
+// Per-lane constants of a dQ wave (lane: query row n of the pair's 32, MFMA column).
 struct QLane {
     uint32_t rowA, trA[2];
     int J;
@@ -611,92 +609,90 @@ struct QLane {
     float sl, lse2, dsum;
 };
 
-// One pipeline step of a dQ wave over 32-key blocks: with C, dQ^T += K^T dS^T of an older block (bc;
-// its packed dS^T in skc); with S, S^T = K Q^T and dP^T = V dO^T of a new block (bs) into sc, dp; with
-// P, dS^T = P (dP - Dsum), P = exp(scale S - lse), of the block in between (bp; its scores scp, dpp) into
-// skn, zero where the row does not see the key.  Register i of a score block <-> key
-// 8 (i/4) + 4 J + i%4 of the block; skn[j] packs registers 2j, 2j+1.
-template <bool C, bool S, bool P>
-__device__ __forceinline__ void q_step(const QLane &L, const bf16x8 qop[8], const bf16x8 gop[8], f32x16 dq[4],
-                                       const KBlk &bc, const uint32_t skc[8], const KBlk &bs, f32x16 &sc, f32x16 &dp,
-                                       const KBlk &bp, const f32x16 &scp, const f32x16 &dpp, uint32_t skn[8])
+// One k-loop of a dQ pair wave (8 k-steps, operands read two k-steps ahead).  With X: x = rows * bop, the
+// first product of a new block (S^T = K Q^T for the P wave, dP^T = V dO^T for the dS wave).  With Y:
+// acc += cols * yop, dQ^T += K^T dS^T of an older block (dS wave).  With F: two elements per k-step of
+// a block whose first product is done (fin): the P wave forms P^T = exp2(scale log2(e) S^T - lse2), zeroed
+// where the row does not see the key; the dS wave forms dS^T = P^T (dP^T - Dsum) from that P^T (pin).
+// Register i of a block <-> key 8 (i/4) + 4 J + i%4 of the block and the lane's row.
+template <bool PW, bool X, bool Y, bool F>
+__device__ __forceinline__ void dq_phase(const QLane &L, const bf16x8 bop[8], f32x16 acc[4], const char *xrows,
+                                         f32x16 &x, const char *ycols, const Packed &yop, const KBlk &bf,
+                                         const f32x16 &fin, const Packed &pin, Packed &fout)
 {
-    if (S) {
+    if (X) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            sc[i] = 0.f;
-            dp[i] = 0.f;
-        }
+        for (int i = 0; i < 16; ++i)
+            x[i] = 0.f;
     }
-    bf16x8 ck0, ck1, ak0, av0, ak1, av1;
-    if (C) {
-        ck0 = rd_cols(bc.k, L.trA, 0, 0);
-        ck1 = rd_cols(bc.k, L.trA, 0, 1);
-    }
-    if (S) {
-        ak0 = rd_rows(bs.k, L.rowA, 0);
-        av0 = rd_rows(bs.v, L.rowA, 0);
-        ak1 = rd_rows(bs.k, L.rowA, 1);
-        av1 = rd_rows(bs.v, L.rowA, 1);
+    bf16x8 xq[3], yq[3]; // operands of k-steps k, k + 1, k + 2
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        if (X)
+            xq[j] = rd_rows(xrows, L.rowA, j);
+        if (Y)
+            yq[j] = rd_cols(ycols, L.trA, 0, j);
     }
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
         const int u = k >> 2, db = k & 3;
-        bf16x8 ck2 = ck0, ak2 = ak0, av2 = av0;
         if (k + 2 < 8) {
-            if (C)
-                ck2 = rd_cols(bc.k, L.trA, (k + 2) >> 2, (k + 2) & 3);
-            if (S) {
-                ak2 = rd_rows(bs.k, L.rowA, k + 2);
-                av2 = rd_rows(bs.v, L.rowA, k + 2);
-            }
+            if (X)
+                xq[2] = rd_rows(xrows, L.rowA, k + 2);
+            if (Y)
+                yq[2] = rd_cols(ycols, L.trA, (k + 2) >> 2, (k + 2) & 3);
         }
-        if (S)
-            sc = mfma32(ak0, qop[k], sc);
-        if (P) {
-            float d[2];
+        if (X)
+            x = mfma32(xq[0], bop[k], x);
+        if (F) {
+            float o[2];
 #pragma unroll
             for (int e = 0; e < 2; ++e) {
                 const int i = 2 * k + e;
-                const float p = exp2_fast(fmaf(scp[i], L.sl, -L.lse2));
-                d[e] = p * (dpp[i] - L.dsum);
+                if (PW)
+                    o[e] = exp2_fast(fmaf(fin[i], L.sl, -L.lse2));
+                else
+                    o[e] = (e ? bf16_hi(pin.h[u][k & 3]) : bf16_lo(pin.h[u][k & 3])) * (fin[i] - L.dsum);
             }
-            skn[k] = pack_bf16x2(d[0], d[1]);
-            anchor(skn[k]);
+            fout.h[u][k & 3] = pack_bf16x2(o[0], o[1]);
+            anchor(fout.h[u][k & 3]);
         }
-        if (C)
-            dq[db] = mfma32(ck0, half_op(skc, u), dq[db]);
-        if (S)
-            dp = mfma32(av0, gop[k], dp);
+        if (Y)
+            acc[db] = mfma32(yq[0], __builtin_bit_cast(bf16x8, yop.h[u]), acc[db]);
         sched_fence();
-        ck0 = ck1;
-        ck1 = ck2;
-        ak0 = ak1;
-        av0 = av1;
-        ak1 = ak2;
-        av1 = av2;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            xq[j] = xq[j + 1];
+            yq[j] = yq[j + 1];
+        }
     }
-    if (P && !bp.full) {
+    // The P wave, on blocks that cross the causal diagonal or an end of the sequence: zero the entries
+    // whose row does not see the key (their exponentials may be anything).  The dS wave needs no mask:
+    // its P^T is zero there and dP^T - Dsum is finite (keys and rows past the sequence load as zero).
+    if (F && PW && !bf.full) {
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
             uint32_t m = 0;
 #pragma unroll
             for (int e = 0; e < 2; ++e) {
                 const int i = 2 * k + e;
-                if (bp.kb + 8 * (i >> 2) + 4 * L.J + (i & 3) < L.kend_row)
+                if (bf.kb + 8 * (i >> 2) + 4 * L.J + (i & 3) < L.kend_row)
                     m |= 0xffffu << (16 * e);
             }
-            skn[k] &= m;
+            fout.h[k >> 2][k & 3] &= m;
         }
     }
 }
 
-// dQ of 32 query rows per wave: the forward's work split (4 waves, NH query heads of one KV head's group
-// times 4 / NH blocks of 32 rows; the group's heads share each K / V tile in LDS) and XCD-aware order.
-// Q^T and dO^T of the wave's rows stay in registers as the B operands; K and V tiles of 64 keys stream
-// through a three-stage direct-to-LDS ring.  Per 32-key block a wave computes S^T = K Q^T and
-// dP^T = V dO^T (A operands: 16-B LDS reads of K and V rows), dS^T, and dQ^T += K^T dS^T (A operand:
-// transposed LDS reads of K), in the three-deep block pipeline of the dK / dV kernel.
+// dQ, two waves per SIMD: the forward's work split over 4 wave pairs (NH query heads of one KV head's
+// group times 4 / NH blocks of 32 rows; the group's heads share each K / V tile in LDS), XCD-aware order.
+// A pair's P wave keeps Q^T of its 32 rows in registers (the B operand of S^T = K Q^T) and forms P^T; its
+// dS wave keeps dO^T (the B operand of dP^T = V dO^T), takes P^T through LDS, forms dS^T and accumulates
+// dQ^T += K^T dS^T (K^T by transposed LDS reads).  K and V tiles of 64 keys stream through a three-stage
+// direct-to-LDS ring; the dS waves run one tile behind the P waves, one barrier per tile.  Per tile the P
+// wave forms S^T of its two 32-key blocks and their P^T; the dS wave forms dS^T of block 0 (whose dP^T it
+// computed during the step before) with dP^T of block 1, dQ^T of block 0 with dS^T of block 1, and dQ^T
+// of block 1 with dP^T of the next tile's block 0.
 __global__ __launch_bounds__(kDqThreads) void bwd_dq_kernel(BwdArgs a, int NH, int RB, int nqt, int nunits)
 {
     const int per = gridDim.x / kXcds;
@@ -715,10 +711,12 @@ __global__ __launch_bounds__(kDqThreads) void bwd_dq_kernel(BwdArgs a, int NH, i
         return;
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int pair = w % kDqPairs;
+    const bool pwave = w < kDqPairs; // waves p and p + 4 form pair p
     const int n = lane & 31, J = lane >> 5;
-    const int h = g * a.G + hc * NH + (w % NH);
-    const int row_w = m0 + 32 * (w / NH); // the wave's first row
-    const int qi = row_w + n;             // the lane's row (MFMA column)
+    const int h = g * a.G + hc * NH + (pair % NH);
+    const int row_w = m0 + 32 * (pair / NH); // the pair's first row
+    const int qi = row_w + n;                // the lane's row (MFMA column)
     const bool row_ok = qi < Lq;
     const int diag = Lk - Lq;
     const int last_row = min(m0 + rows_wg, Lq) - 1;
@@ -741,23 +739,19 @@ __global__ __launch_bounds__(kDqThreads) void bwd_dq_kernel(BwdArgs a, int NH, i
         }
     }
 
-    // Q^T and dO^T as B operands: lane (row n, J) holds dims 16 s + 8 J .. +8
-    bf16x8 qop[8], gop[8];
+    // Q^T (P wave) or dO^T (dS wave) as the B operand: lane (row n, J) holds dims 16 s + 8 J .. +8
+    bf16x8 bop[8];
     {
-        const uint16_t *qg = static_cast<const uint16_t *>(a.q), *dog = static_cast<const uint16_t *>(a.dout);
+        const uint16_t *src = static_cast<const uint16_t *>(pwave ? a.q : a.dout);
 #pragma unroll
         for (int s = 0; s < 8; ++s) {
-            uint4 qv = make_uint4(0, 0, 0, 0), gv = make_uint4(0, 0, 0, 0);
-            if (row_ok) {
-                const size_t off = ((size_t)(q0 + qi) * a.Hq + h) * D + 16 * s + 8 * J;
-                qv = ld16(qg + off);
-                gv = ld16(dog + off);
-            }
-            qop[s] = as_bf16x8(qv);
-            gop[s] = as_bf16x8(gv);
+            uint4 v = make_uint4(0, 0, 0, 0);
+            if (row_ok)
+                v = ld16(src + ((size_t)(q0 + qi) * a.Hq + h) * D + 16 * s + 8 * J);
+            bop[s] = as_bf16x8(v);
         }
     }
-    f32x16 dq[4]; // dQ^T [128 dims x 32 rows]: block db, register i <-> dim 32 db + 8 (i/4) + 4 J + i%4
+    f32x16 dq[4]; // dQ^T [128 dims x 32 rows] (dS wave): block db, register i <-> dim 32 db + 8 (i/4) + 4 J + i%4
 #pragma unroll
     for (int db = 0; db < 4; ++db)
 #pragma unroll
@@ -782,7 +776,8 @@ __global__ __launch_bounds__(kDqThreads) void bwd_dq_kernel(BwdArgs a, int NH, i
     }
 
     const int ntiles = (kend + kKTile - 1) / kKTile;
-    auto blk = [&](int st, int t, int kk) {
+    auto blk = [&](int t, int kk) {
+        const int st = t % kKStages;
         KBlk x;
         x.k = k_ring[st].k + kk * 32 * kRowBytes;
         x.v = k_ring[st].v + kk * 32 * kRowBytes;
@@ -790,40 +785,58 @@ __global__ __launch_bounds__(kDqThreads) void bwd_dq_kernel(BwdArgs a, int NH, i
         x.full = row_w + 32 <= Lq && x.kb + 32 <= Lk && (!a.causal || x.kb + 31 <= row_w + diag);
         return x;
     };
-    auto next_tile = [&](int st, int t) {
+    // step s: the P waves work on tile s, the dS waves on tile s - 1 (and on the first block of tile s).
+    // At its barrier tile s is in LDS and so is the P^T of tile s - 1, and every wave is done with tile
+    // s - 2 (stage and exchange).  Each role runs its own loop; both pass ntiles + 1 barriers.
+    auto sync = [&](int s) {
         wait_vmcnt<0>();
-        barrier(); // tile t is in LDS for every wave; every wave is done with tile t - 2
-        if (t + 1 < ntiles)
-            ld.issue(st == kKStages - 1 ? 0 : st + 1, t + 1);
+        wait_lds();
+        barrier();
+        if (s + 1 < ntiles)
+            ld.issue((s + 1) % kKStages, s + 1);
     };
 
     if (ntiles > 0) {
-        f32x16 sc, dp, scp, dpp;
-        uint32_t ska[8], skb[8];
         ld.issue(0, 0);
-        next_tile(0, 0);
-        {
-            const KBlk b0 = blk(0, 0, 0), b1 = blk(0, 0, 1);
-            q_step<false, true, false>(L, qop, gop, dq, b0, ska, b0, scp, dpp, b0, sc, dp, skb);
-            q_step<false, true, true>(L, qop, gop, dq, b0, ska, b1, sc, dp, b0, scp, dpp, skb);
-        }
-        int sp = 0; // stage of tile t - 1
-        for (int t = 1; t < ntiles; ++t) {
-            const int st = sp == kKStages - 1 ? 0 : sp + 1;
-            next_tile(st, t);
-            const KBlk bm2 = blk(sp, t - 1, 0), bm1 = blk(sp, t - 1, 1), bj = blk(st, t, 0), bj1 = blk(st, t, 1);
-            q_step<true, true, true>(L, qop, gop, dq, bm2, skb, bj, scp, dpp, bm1, sc, dp, ska);
-            q_step<true, true, true>(L, qop, gop, dq, bm1, ska, bj1, sc, dp, bj, scp, dpp, skb);
-            sp = st;
-        }
-        {
-            const KBlk bm2 = blk(sp, ntiles - 1, 0), bm1 = blk(sp, ntiles - 1, 1);
-            q_step<true, false, true>(L, qop, gop, dq, bm2, skb, bm2, scp, dpp, bm1, sc, dp, ska);
-            q_step<true, false, false>(L, qop, gop, dq, bm1, ska, bm1, scp, dpp, bm1, sc, dp, skb);
+        if (pwave) {
+            for (int s = 0; s < ntiles; ++s) {
+                sync(s);
+                const KBlk b0 = blk(s, 0), b1 = blk(s, 1);
+                char *xb = pt_xchg[s & 1][pair];
+                f32x16 s0, s1;
+                Packed p0, p1;
+                dq_phase<true, true, false, false>(L, bop, dq, b0.k, s0, nullptr, p0, b0, s0, p0, p0);
+                dq_phase<true, true, false, true>(L, bop, dq, b1.k, s1, nullptr, p0, b0, s0, p0, p0);
+                xchg_store(xb, lane, p0);
+                dq_phase<true, false, false, true>(L, bop, dq, nullptr, s1, nullptr, p0, b1, s1, p1, p1);
+                xchg_store(xb + kXchgBlock, lane, p1);
+            }
+            sync(ntiles);
+        } else {
+            f32x16 dn; // dP^T of the first block of the next tile
+            sync(0);
+            {
+                Packed none;
+                const KBlk b0 = blk(0, 0);
+                dq_phase<false, true, false, false>(L, bop, dq, b0.v, dn, nullptr, none, b0, dn, none, none);
+            }
+            for (int s = 1; s <= ntiles; ++s) {
+                sync(s);
+                // tile s - 1; the next tile's first block (after the last tile: a resident block, dn unused)
+                const KBlk b0 = blk(s - 1, 0), b1 = blk(s - 1, 1), nb = blk(s < ntiles ? s : s - 1, 0);
+                const char *xb = pt_xchg[(s - 1) & 1][pair];
+                f32x16 d1;
+                Packed p0, p1, t0, t1;
+                xchg_load(xb, lane, p0);
+                xchg_load(xb + kXchgBlock, lane, p1);
+                dq_phase<false, true, false, true>(L, bop, dq, b1.v, d1, nullptr, t0, b0, dn, p0, t0);
+                dq_phase<false, false, true, true>(L, bop, dq, nullptr, d1, b0.k, t0, b1, d1, p1, t1);
+                dq_phase<false, true, true, false>(L, bop, dq, nb.v, dn, b1.k, t1, nb, d1, p1, t1);
+            }
         }
     }
 
-    if (!row_ok)
+    if (pwave || !row_ok)
         return;
     uint16_t *dqg = static_cast<uint16_t *>(a.dq) + ((size_t)(q0 + qi) * a.Hq + h) * D;
 #pragma unroll
@@ -842,7 +855,7 @@ __global__ __launch_bounds__(kDqThreads) void bwd_dq_kernel(BwdArgs a, int NH, i
 static int heads_per_wg_bwd(int G)
 {
     int nh = 1;
-    while (nh < kDqWaves && G % (2 * nh) == 0)
+    while (nh < kDqPairs && G % (2 * nh) == 0)
         nh *= 2;
     return nh;
 }
@@ -857,7 +870,7 @@ hipError_t launch_prefill_bwd(const BwdArgs &a, hipStream_t stream)
     const int nkt = (a.max_k + kKeysPerWg - 1) / kKeysPerWg;
     const long units_kv = (long)a.Hkv * a.B * nkt;
     const long blocks_kv = (units_kv + kXcds - 1) / kXcds * kXcds;
-    const int NH = heads_per_wg_bwd(a.G), RB = kDqWaves / NH;
+    const int NH = heads_per_wg_bwd(a.G), RB = kDqPairs / NH;
     const int nqt = (a.max_q + 32 * RB - 1) / (32 * RB);
     const long units_q = (long)a.Hkv * (a.G / NH) * a.B * nqt;
     const long blocks_q = (units_q + kXcds - 1) / kXcds * kXcds;
