@@ -128,8 +128,10 @@ def main():
     torch.cuda.synchronize()
     print(f"# inputs generated in {time.time() - t_gen:.1f} s", file=sys.stderr, flush=True)
 
-    # rows past the hot path (timed after it, outside the step): the prefill backward
+    # rows past the hot path (timed after it, outside the step, each call in a loop of its own): the prefill
+    # backward, ...; `last` runs after all of them
     nxt = {}
+    last = {}
     if "prefill_bwd" in only:
         xb = work.get("prefill") or W.varlen_prefill(seed=1001 + args.seed, device=dev)
         work["prefill_bwd"] = xb
@@ -173,11 +175,14 @@ def main():
 
     calls = {}  # name -> zero-arg launcher
     if "tiny" in only:
+        # the tiny fp32 workload, each call in a loop of its own after every other call: short calls changed
+        # the clocks the calls after them ran at (measured: the hot-key skip-softmax prefill calls took 7-10 %
+        # longer in kernel time with the tiny calls in the step)
         xt = work["tiny"]
         o_t = torch.empty_like(xt.q)
         for causal in (True, False):
             for thr in (0.0, 0.1):
-                calls[f"tiny_{'causal' if causal else 'noncausal'}_{thr}"] = (
+                last[f"tiny_{'causal' if causal else 'noncausal'}_{thr}"] = (
                     lambda causal=causal, thr=thr: attn.attn_prefill_varlen(
                         xt.q, xt.k, xt.v, xt.cu_q, xt.cu_k, xt.max_q, xt.max_k, scale=xt.scale, causal=causal,
                         skip_threshold=thr, out=o_t))
@@ -189,10 +194,13 @@ def main():
     if "prefill_skip" in only:
         xh = work["prefill_skip"]
         o_ph = torch.empty_like(xh.q)
+        # the speedup curve of skip-softmax prefill over dense on the same input (hot keys here, a coherent sink
+        # below), each call timed in a loop of its own after the step: in the step, the calls' times depended on
+        # the calls before them (the clocks the GPU ran at), by more than the differences being measured
         for thr in (0.0, 0.01, 0.1):
-            calls[f"prefill_skip_{thr}"] = (lambda thr=thr: attn.attn_prefill_varlen(
+            nxt[f"prefill_skip_{thr}"] = (lambda thr=thr: attn.attn_prefill_varlen(
                 xh.q, xh.k, xh.v, xh.cu_q, xh.cu_k, xh.max_q, xh.max_k, causal=True, skip_threshold=thr, out=o_ph))
-        # the coherent-sink input: timed after the step, for the speedup-vs-skipped-fraction curve
+        # the coherent-sink input
         xs = work["prefill_sink"]
         for thr in (0.0, 0.01, 0.1):
             nxt[f"prefill_sink_{thr}"] = (lambda thr=thr: attn.attn_prefill_varlen(
@@ -221,6 +229,7 @@ def main():
         calls["smallseq"] = lambda: attn.attn_smallseq_cross(c.q, c.k, c.v, c.cu_kv, c.max_s, out=o_ss)
 
     calls = {k: _logged(k, f) for k, f in calls.items()}
+    nxt.update(last)
     nxt = {k: _logged(k, f) for k, f in nxt.items()}
     names = list(calls)
     stream = torch.cuda.current_stream()
@@ -501,18 +510,18 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": "varlen causal prefill bf16: 16 seqs, L~U[256,4096] THD, Hq=32, Hkv=8, D=128",
-                   "step_also_runs": ["tiny fp32 B=2 Hq=4 Hkv=2 D=64 S=128, {causal, non-causal} x thr {0, 0.1}",
-                                      "the same prefill shapes with hot keys, skip-softmax thr {0,0.01,0.1}",
-                                      "paged decode split-K B=64 L~U[1024,32768] page 16, 32x128-key splits",
+                   "step_also_runs": ["paged decode split-K B=64 L~U[1024,32768] page 16, 32x128-key splits",
                                       "sequential skip decode thr {0,0.01,0.1} on hot keys",
                                       "small-seq cross B=30720 s_kv in {2..16} H=16 D=128"],
-                   "timed_after_the_step": ["skip-softmax prefill thr {0,0.01,0.1} on the coherent-sink input",
+                   "timed_after_the_step": ["skip-softmax prefill thr {0,0.01,0.1} on the prefill shapes with hot "
+                                            "keys and on the coherent-sink input",
                                             "the prefill backward (dq, dk, dv) on the prefill shapes",
                                             "the small-seq backward from the stored weights on the small-seq shapes",
                                             "multi-token paged decode: the paged-decode cache with 1..4 new tokens "
                                             "per sequence, 32 splits",
                                             "chunked prefill over the paged-decode cache: 256 new tokens per "
-                                            "sequence"],
+                                            "sequence",
+                                            "tiny fp32 B=2 Hq=4 Hkv=2 D=64 S=128, {causal, non-causal} x thr {0, 0.1}"],
                    "seed": args.seed},
         "roofline": roofline,
         "cpu_baseline": cpu,
@@ -568,19 +577,20 @@ def _achievable(torch, dev):
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / 10
     res["copy_1GiB_GBps"] = 2.0 * (1 << 30) / (ms * 1e-3) / 1e9
-    # a plain read: torch's sum over 1 GiB of float32 (reads the bytes once, writes one scalar)
-    x32 = src.view(torch.float32)
+    # a plain read: torch's sum over 1 GiB viewed as int64 (reads the bytes once, writes one scalar; of the
+    # library reductions tried it reads fastest here: float32 sum and amax reach about 4 TB/s)
+    x64 = src.view(torch.int64)
     for _ in range(3):
-        x32.sum()
+        x64.sum()
     torch.cuda.synchronize()
     e0.record()
     for _ in range(10):
-        x32.sum()
+        x64.sum()
     e1.record()
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / 10
-    res["read_1GiB_fp32_sum_GBps"] = float(1 << 30) / (ms * 1e-3) / 1e9
-    del src, dst, x32
+    res["read_1GiB_int64_sum_GBps"] = float(1 << 30) / (ms * 1e-3) / 1e9
+    del src, dst, x64
     n = 8192
     a = torch.randn(n, n, device=dev, dtype=torch.bfloat16)
     b = torch.randn(n, n, device=dev, dtype=torch.bfloat16)
