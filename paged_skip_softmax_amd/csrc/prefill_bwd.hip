@@ -325,38 +325,6 @@ __device__ __forceinline__ void ds_wave_tile(const KvLane &L, const bf16x8 vop[8
     pair_phase<false, true, true, false>(L, vop, dk, nb.g, dn, b1.q, t1, nb, d1, p1, t1);
 }
 
-// Sequences are taken in decreasing order of work (Lq * Lk; ties by index) when there are at most
-// kRankMaxBatch of them: each workgroup finds the sequence of rank r itself, from the lengths staged in
-// LDS.  The largest units then start first and the last ones to run are short, which shortens the tail of
-// the launch (each unit of a long sequence walks many query tiles).  Larger batches keep index order.
-constexpr int kRankMaxBatch = 128;
-__shared__ long long seq_work[kRankMaxBatch];
-__shared__ int seq_pick;
-
-__device__ __forceinline__ int seq_by_work(const int32_t *cu_q, const int32_t *cu_k, int B, int r)
-{
-    if (B > kRankMaxBatch)
-        return r;
-    for (int i = threadIdx.x; i < B; i += blockDim.x)
-        seq_work[i] = (long long)(cu_q[i + 1] - cu_q[i]) * (cu_k[i + 1] - cu_k[i]);
-    if (threadIdx.x == 0)
-        seq_pick = r;
-    __syncthreads();
-    // the ranks are a permutation of 0 .. B-1, so exactly one sequence has rank r
-    for (int i = threadIdx.x; i < B; i += blockDim.x) {
-        const long long wi = seq_work[i];
-        int rank = 0;
-        for (int j = 0; j < B; ++j) {
-            const long long wj = seq_work[j];
-            rank += (wj > wi) || (wj == wi && j < i);
-        }
-        if (rank == r)
-            seq_pick = i;
-    }
-    __syncthreads();
-    return seq_pick;
-}
-
 // dK, dV of 128 keys of one (sequence, KV head), two waves per SIMD: 4 pairs of waves, pair p owning keys
 // kb0 + 32 p .. +31.  The pair's P wave keeps K of its keys in registers (the B operand of S = Q K^T),
 // forms P and accumulates dV^T = sum dO^T P; its dS wave keeps V (the B operand of dP = dO V^T), takes P
@@ -370,8 +338,8 @@ __device__ __forceinline__ int seq_by_work(const int32_t *cu_q, const int32_t *c
 __global__ __launch_bounds__(kKvThreads) void bwd_dkdv_kernel(BwdArgs a, int nkt, int nunits)
 {
     // XCD-aware order: block i runs on XCD i % 8, which takes a contiguous run of units ordered (KV
-    // head, sequence by decreasing work, key block): each XCD serves whole KV heads of every sequence
-    // (even load), and the key blocks of one (sequence, KV head) are dispatched together.  Every key block walks its query
+    // head, sequence, key block): each XCD serves whole KV heads of every sequence (even load), and the
+    // key blocks of one (sequence, KV head) are dispatched together.  Every key block walks its query
     // tiles from the sequence's last one backwards (all key blocks see the last rows, under the causal
     // mask too), so the key blocks running together read the same Q and dO tiles at about the same
     // time and all but the first read of each come from the XCD's L2.
@@ -380,7 +348,7 @@ __global__ __launch_bounds__(kKvThreads) void bwd_dkdv_kernel(BwdArgs a, int nkt
     if (unit >= nunits)
         return;
     const int g = unit / (nkt * a.B), rem = unit % (nkt * a.B);
-    const int b = seq_by_work(a.cu_q, a.cu_k, a.B, rem / nkt), kt = rem % nkt;
+    const int b = rem / nkt, kt = rem % nkt;
     const int q0 = a.cu_q[b], Lq = a.cu_q[b + 1] - q0;
     const int k0 = a.cu_k[b], Lk = a.cu_k[b + 1] - k0;
     const int kb0 = kt * kKeysPerWg;

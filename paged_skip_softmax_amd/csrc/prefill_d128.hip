@@ -372,9 +372,15 @@ __device__ __forceinline__ void iteration(int t, const IterCtx &c, const Loader<
                 const bf16x8 pop = __builtin_bit_cast(bf16x8, make_uint4(pk[kk][4 * u], pk[kk][4 * u + 1],
                                                                           pk[kk][4 * u + 2], pk[kk][4 * u + 3]));
                 wv.acc[step & 3] = mfma32(as_bf16x8(v0), pop, wv.acc[step & 3]);
-                if (step < 15) {
-                    t0 = fmaxf(t0, nx[0][step + 1]);
-                    t1 = fmaxf(t1, nx[1][step + 1]);
+                // two new elements per three-input max (v_max3_f32) on even steps, the last one alone
+                if ((step & 1) == 0 && step < 14) {
+                    t0 = fmaxf(t0, fmaxf(nx[0][step + 1], nx[0][step + 2]));
+                    t1 = fmaxf(t1, fmaxf(nx[1][step + 1], nx[1][step + 2]));
+                    anchor(t0);
+                    anchor(t1);
+                } else if (step == 14) {
+                    t0 = fmaxf(t0, nx[0][15]);
+                    t1 = fmaxf(t1, nx[1][15]);
                     anchor(t0);
                     anchor(t1);
                 }
