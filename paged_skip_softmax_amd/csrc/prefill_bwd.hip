@@ -7,20 +7,20 @@
 //
 // Three kernels, no atomics:
 //  * bwd_prep: Dsum and lse * log2(e) per (token, query head), fp32, into the caller's workspace.
-//  * bwd_dkdv: a workgroup of 4 waves owns 128 keys of one (sequence, KV head), 32 keys per wave, whose
-//    K and V stay in registers as MFMA B operands; it walks every 64-row query tile that sees any of its
-//    keys, for every query head of the group, from the sequence's last tile backwards (so that the key
-//    blocks of a sequence, dispatched together, share each tile through L2).  Q and dO tiles go to LDS
-//    by direct-to-LDS loads (XOR-swizzled 16-byte chunks) once for the 4 waves; per 32-row block a wave
-//    computes, with 32x32x16 MFMAs,
-//      S = Q K^T, dP = dO V^T           [32 rows x 32 keys]   (A operands: 16-byte LDS reads)
-//      dV^T += dO^T P, dK^T += Q^T dS   [128 dims x 32 keys]  (A operands: transposed LDS reads)
-//    so the key order inside the row contraction follows the S register layout and P, dS feed the
-//    MFMA B operand straight from registers.
-//  * bwd_dq: the forward's work split (4 waves, one query head and 32 rows each, the heads of a group
-//    sharing K/V tiles in LDS); Q^T and dO^T stay in registers as B operands; per 32-key tile
-//      S^T = K Q^T, dP^T = V dO^T   (32x32x16 MFMAs)
-//      dQ^T += K^T dS^T             (K^T by transposed LDS reads)
+//  * bwd_dkdv: a workgroup of 8 waves (two per SIMD) owns 128 keys of one (sequence, KV head) as 4 wave
+//    pairs of 32 keys.  It walks every 64-row query tile that sees any of its keys, for every query
+//    head of the group, from the sequence's last tile backwards (so that the key blocks of a sequence,
+//    dispatched together, share each tile through L2); Q and dO tiles go to LDS by direct-to-LDS loads
+//    (XOR-swizzled 16-byte chunks).  With 32x32x16 MFMAs, per 32-row block, a pair's
+//      P wave  (K in registers):  S = Q K^T, P = exp2(S scale log2(e) - lse2), dV^T += dO^T P
+//      dS wave (V in registers):  dP = dO V^T, dS = P (dP - Dsum), dK^T += Q^T dS
+//    with P passed through LDS; the dS wave runs one tile behind, so one barrier per tile serves both.
+//    The key order inside the row contraction follows the S register layout, so P and dS feed the
+//    MFMA B operand straight from registers (A operands: 16-byte and transposed LDS reads).
+//  * bwd_dq: the forward's work split over 4 wave pairs (one query head and 32 rows each, the heads of
+//    a group sharing K/V tiles in LDS); per 32-key block
+//      P wave  (Q^T in registers):   S^T = K Q^T, P^T
+//      dS wave (dO^T in registers):  dP^T = V dO^T, dS^T, dQ^T += K^T dS^T (K^T by transposed reads)
 #include "kcommon.h"
 #include "launch.h"
 #include "lds_dma.h"

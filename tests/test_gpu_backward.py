@@ -6,8 +6,9 @@ the oracle then forms dS from the same row dots dO.o as the GPU.  One test chain
 the GPU backward, as a training step does (see its comment for what it checks).
 
 Tolerance, derived from the arithmetic: each gradient element is a sum over rows (dk, dv) or keys (dq)
-of products whose factors the kernels round to bf16 (P and dS, relative 2^-9 each) before fp32
-accumulation, and the result is rounded to bf16 once more.  The rounding error of such a sum grows like
+of products whose factors the kernels round to bf16 (P and dS, relative 2^-9 each; dS is formed from
+the rounded P, which adds one more 2^-9 to it) before fp32 accumulation, and the result is rounded to
+bf16 once more.  The rounding error of such a sum grows like
 the root of the summed squared terms, which is shared by the whole (token, head) row of D elements (the
 row's rms), not like the element itself, which cancellation can make small.  So every element must
 satisfy
