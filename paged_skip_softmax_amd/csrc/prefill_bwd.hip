@@ -17,10 +17,12 @@
 //    with P passed through LDS; the dS wave runs one tile behind, so one barrier per tile serves both.
 //    The key order inside the row contraction follows the S register layout, so P and dS feed the
 //    MFMA B operand straight from registers (A operands: 16-byte and transposed LDS reads).
-//  * bwd_dq: the forward's work split over 4 wave pairs (one query head and 32 rows each, the heads of
-//    a group sharing K/V tiles in LDS); per 32-key block
-//      P wave  (Q^T in registers):   S^T = K Q^T, P^T
-//      dS wave (dO^T in registers):  dP^T = V dO^T, dS^T, dQ^T += K^T dS^T (K^T by transposed reads)
+//  * bwd_dq: the forward's work split over 4 groups (one query head and 32 rows each, the heads of a
+//    group sharing K/V tiles in LDS), three waves per group on one SIMD; per 32-key tile
+//      S wave (Q^T in registers):   S^T = K Q^T, P^T
+//      D wave (dO^T in registers):  dP^T = V dO^T, dS^T = P^T (dP^T - Dsum)
+//      Q wave:                      dQ^T += K^T dS^T (K^T by transposed reads)
+//    with P^T and dS^T passed through LDS, each wave one tile behind the one before it.
 #include "kcommon.h"
 #include "launch.h"
 #include "lds_dma.h"
@@ -524,13 +526,14 @@ __global__ __launch_bounds__(kKvThreads) void bwd_dkdv_kernel(BwdArgs a, int nkt
 
 // ------------------------------------------------------------------ dQ
 
-constexpr int kDqPairs = 4;             // wave pairs per workgroup
-constexpr int kDqWaves = 2 * kDqPairs;  // two waves per SIMD
+constexpr int kDqGroups = 4;             // 32-row groups per workgroup
+constexpr int kDqWaves = 3 * kDqGroups;  // three waves per SIMD: an S, a D and a Q wave per group
 constexpr int kDqThreads = 64 * kDqWaves;
-constexpr int kKTile = 64;                            // keys per staged tile
-constexpr int kKTileBytes = kKTile * kRowBytes;       // 16 KB
-constexpr int kKLoads = kKTileBytes / 1024 / kDqWaves; // 1-KB direct-to-LDS loads per wave per tile
-constexpr int kKStages = 3;
+constexpr int kKTile = 32;                      // keys per staged tile
+constexpr int kKTileBytes = kKTile * kRowBytes; // 8 KB
+constexpr int kKLoaders = 8;                    // waves that issue a tile's loads: one 1-KB chunk of K and of V each
+constexpr int kKStages = 4;
+static_assert(kKTileBytes == kKLoaders * 1024, "one K and one V chunk per loading wave");
 
 // One stage of the K / V ring (swizzled rows).
 struct alignas(1024) KStage {
@@ -539,37 +542,36 @@ struct alignas(1024) KStage {
 };
 __shared__ KStage k_ring[kKStages];
 
-// P^T of a 32-key block, from a pair's P wave to its dS wave (the layout of p_xchg).
-__shared__ __attribute__((aligned(1024))) char pt_xchg[2][kDqPairs][2 * kXchgBlock];
+// P^T (S wave -> D wave) and dS^T (D wave -> Q wave) of a group's 32-key tile, in the layout of p_xchg;
+// two tiles in flight each.
+__shared__ __attribute__((aligned(1024))) char pt_xchg[2][kDqGroups][kXchgBlock];
+__shared__ __attribute__((aligned(1024))) char dst_xchg[2][kDqGroups][kXchgBlock];
 
 struct KLoader {
-    i32x4 krs, vrs;          // buffer resources of K, V (the sequence's rows of one KV head)
-    uint32_t voff[kKLoads];  // lane's byte offsets inside a tile of rows (4-row blocks of the wave)
-    uint32_t tile_bytes;     // global bytes between consecutive tiles
+    i32x4 krs, vrs;      // buffer resources of K, V (the sequence's rows of one KV head)
+    uint32_t voff;       // lane's byte offset inside a tile of rows (the wave's 4-row block)
+    uint32_t tile_bytes; // global bytes between consecutive tiles
     int w;
 
-    // keys [64 t, 64 t + 64) into stage st (keys past the sequence read as zero)
+    // keys [32 t, 32 t + 32) into stage st (keys past the sequence read as zero); waves 0 .. 7
     __device__ __forceinline__ void issue(int st, int t) const
     {
+        if (w >= kKLoaders)
+            return;
         const uint32_t soff = (uint32_t)t * tile_bytes;
-        const uint32_t wk = lds_addr(k_ring[st].k) + w * (kKLoads * 1024);
-        const uint32_t wv = lds_addr(k_ring[st].v) + w * (kKLoads * 1024);
-#pragma unroll
-        for (int p = 0; p < kKLoads; ++p) {
-            dma16(wk + p * 1024, voff[p], krs, soff);
-            dma16(wv + p * 1024, voff[p], vrs, soff);
-        }
+        dma16(lds_addr(k_ring[st].k) + w * 1024, voff, krs, soff);
+        dma16(lds_addr(k_ring[st].v) + w * 1024, voff, vrs, soff);
     }
 };
 
-// A 32-key block of a staged tile: its K and V rows and its first key.
+// A 32-key tile: its K and V rows and its first key.
 struct KBlk {
     const char *k, *v;
     int kb;
-    bool full; // every row of the pair sees every key of the block
+    bool full; // every row of the group sees every key of the tile
 };
 
-// Per-lane constants of a dQ wave (lane: query row n of the pair's 32, MFMA column).
+// Per-lane constants of a dQ wave (lane: query row n of the group's 32, MFMA column).
 struct QLane {
     uint32_t rowA, trA[2];
     int J;
@@ -577,12 +579,12 @@ struct QLane {
     float sl, lse2, dsum;
 };
 
-// One k-loop of a dQ pair wave (8 k-steps, operands read two k-steps ahead).  With X: x = rows * bop, the
-// first product of a new block (S^T = K Q^T for the P wave, dP^T = V dO^T for the dS wave).  With Y:
-// acc += cols * yop, dQ^T += K^T dS^T of an older block (dS wave).  With F: two elements per k-step of
-// a block whose first product is done (fin): the P wave forms P^T = exp2(scale log2(e) S^T - lse2), zeroed
-// where the row does not see the key; the dS wave forms dS^T = P^T (dP^T - Dsum) from that P^T (pin).
-// Register i of a block <-> key 8 (i/4) + 4 J + i%4 of the block and the lane's row.
+// One k-loop of a dQ wave (8 k-steps, operands read two k-steps ahead).  With X: x = rows * bop, the first
+// product of a tile (S^T = K Q^T for the S wave, dP^T = V dO^T for the D wave).  With Y: acc += cols * yop,
+// dQ^T += K^T dS^T (Q wave).  With F: the element-wise step on a tile whose first product is done (fin):
+// the S wave forms P^T = exp2(scale log2(e) S^T - lse2), zeroed where the row does not see the key; the
+// D wave forms dS^T = P^T (dP^T - Dsum) from that P^T (pin).  Register i of a tile <-> key 8 (i/4) + 4 J
+// + i%4 of the tile and the lane's row.
 template <bool PW, bool X, bool Y, bool F>
 __device__ __forceinline__ void dq_phase(const QLane &L, const bf16x8 bop[8], f32x16 acc[4], const char *xrows,
                                          f32x16 &x, const char *ycols, const Packed &yop, const KBlk &bf,
@@ -634,9 +636,9 @@ __device__ __forceinline__ void dq_phase(const QLane &L, const bf16x8 bop[8], f3
             yq[j] = yq[j + 1];
         }
     }
-    // The P wave, on blocks that cross the causal diagonal or an end of the sequence: zero the entries
-    // whose row does not see the key (their exponentials may be anything).  The dS wave needs no mask:
-    // its P^T is zero there and dP^T - Dsum is finite (keys and rows past the sequence load as zero).
+    // The S wave, on tiles that cross the causal diagonal or an end of the sequence: zero the entries
+    // whose row does not see the key (their exponentials may be anything).  The D wave needs no mask: its
+    // P^T is zero there and dP^T - Dsum is finite (keys and rows past the sequence load as zero).
     if (F && PW && !bf.full) {
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
@@ -652,15 +654,15 @@ __device__ __forceinline__ void dq_phase(const QLane &L, const bf16x8 bop[8], f3
     }
 }
 
-// dQ, two waves per SIMD: the forward's work split over 4 wave pairs (NH query heads of one KV head's
-// group times 4 / NH blocks of 32 rows; the group's heads share each K / V tile in LDS), XCD-aware order.
-// A pair's P wave keeps Q^T of its 32 rows in registers (the B operand of S^T = K Q^T) and forms P^T; its
-// dS wave keeps dO^T (the B operand of dP^T = V dO^T), takes P^T through LDS, forms dS^T and accumulates
-// dQ^T += K^T dS^T (K^T by transposed LDS reads).  K and V tiles of 64 keys stream through a three-stage
-// direct-to-LDS ring; the dS waves run one tile behind the P waves, one barrier per tile.  Per tile the P
-// wave forms S^T of its two 32-key blocks and their P^T; the dS wave forms dS^T of block 0 (whose dP^T it
-// computed during the step before) with dP^T of block 1, dQ^T of block 0 with dS^T of block 1, and dQ^T
-// of block 1 with dP^T of the next tile's block 0.
+// dQ, three waves per SIMD: the forward's work split over 4 groups of 32 rows (NH query heads of one KV
+// head's group times 4 / NH blocks of 32 rows; the group's heads share each K / V tile in LDS), XCD-aware
+// order.  Each group has three waves, on one SIMD: the S wave keeps Q^T of the rows in registers (the B
+// operand of S^T = K Q^T) and forms P^T; the D wave keeps dO^T (the B operand of dP^T = V dO^T), takes
+// P^T through LDS and forms dS^T; the Q wave takes dS^T through LDS and accumulates dQ^T += K^T dS^T (K^T
+// by transposed LDS reads).  Each issues 8 MFMAs per 32-key tile.  K and V tiles stream through a
+// four-stage direct-to-LDS ring; at step s the S waves work on tile s, the D waves on tile s - 1 and the
+// Q waves on tile s - 2, so one barrier per tile publishes the tile, the P^T of the tile before it and the
+// dS^T of the one before that.
 __global__ __launch_bounds__(kDqThreads) void bwd_dq_kernel(BwdArgs a, int NH, int RB, int nqt, int nunits)
 {
     const int per = gridDim.x / kXcds;
@@ -679,12 +681,12 @@ __global__ __launch_bounds__(kDqThreads) void bwd_dq_kernel(BwdArgs a, int NH, i
         return;
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int pair = w % kDqPairs;
-    const bool pwave = w < kDqPairs; // waves p and p + 4 form pair p
+    const int grp = w % kDqGroups;
+    const int role = w / kDqGroups; // 0: S wave, 1: D wave, 2: Q wave
     const int n = lane & 31, J = lane >> 5;
-    const int h = g * a.G + hc * NH + (pair % NH);
-    const int row_w = m0 + 32 * (pair / NH); // the pair's first row
-    const int qi = row_w + n;                // the lane's row (MFMA column)
+    const int h = g * a.G + hc * NH + (grp % NH);
+    const int row_w = m0 + 32 * (grp / NH); // the group's first row
+    const int qi = row_w + n;               // the lane's row (MFMA column)
     const bool row_ok = qi < Lq;
     const int diag = Lk - Lq;
     const int last_row = min(m0 + rows_wg, Lq) - 1;
@@ -707,10 +709,10 @@ __global__ __launch_bounds__(kDqThreads) void bwd_dq_kernel(BwdArgs a, int NH, i
         }
     }
 
-    // Q^T (P wave) or dO^T (dS wave) as the B operand: lane (row n, J) holds dims 16 s + 8 J .. +8
+    // Q^T (S wave) or dO^T (D wave) as the B operand: lane (row n, J) holds dims 16 s + 8 J .. +8
     bf16x8 bop[8];
-    {
-        const uint16_t *src = static_cast<const uint16_t *>(pwave ? a.q : a.dout);
+    if (role < 2) {
+        const uint16_t *src = static_cast<const uint16_t *>(role == 0 ? a.q : a.dout);
 #pragma unroll
         for (int s = 0; s < 8; ++s) {
             uint4 v = make_uint4(0, 0, 0, 0);
@@ -719,7 +721,7 @@ __global__ __launch_bounds__(kDqThreads) void bwd_dq_kernel(BwdArgs a, int NH, i
             bop[s] = as_bf16x8(v);
         }
     }
-    f32x16 dq[4]; // dQ^T [128 dims x 32 rows] (dS wave): block db, register i <-> dim 32 db + 8 (i/4) + 4 J + i%4
+    f32x16 dq[4]; // dQ^T [128 dims x 32 rows] (Q wave): block db, register i <-> dim 32 db + 8 (i/4) + 4 J + i%4
 #pragma unroll
     for (int db = 0; db < 4; ++db)
 #pragma unroll
@@ -736,26 +738,24 @@ __global__ __launch_bounds__(kDqThreads) void bwd_dq_kernel(BwdArgs a, int NH, i
         ld.vrs = make_rsrc(vg + head0, seq_bytes);
         ld.tile_bytes = kKTile * row_bytes;
         ld.w = w;
-#pragma unroll
-        for (int p = 0; p < kKLoads; ++p) {
-            const int row = 4 * (kKLoads * w + p) + (lane >> 4);
-            ld.voff[p] = (uint32_t)row * row_bytes + 16 * ((lane & 15) ^ swz(row & 15));
-        }
+        const int row = 4 * w + (lane >> 4); // waves 0 .. 7: rows 4 w .. 4 w + 3 of the tile
+        ld.voff = (uint32_t)row * row_bytes + 16 * ((lane & 15) ^ swz(row & 15));
     }
 
     const int ntiles = (kend + kKTile - 1) / kKTile;
-    auto blk = [&](int t, int kk) {
+    auto blk = [&](int t) {
         const int st = t % kKStages;
         KBlk x;
-        x.k = k_ring[st].k + kk * 32 * kRowBytes;
-        x.v = k_ring[st].v + kk * 32 * kRowBytes;
-        x.kb = t * kKTile + 32 * kk;
+        x.k = k_ring[st].k;
+        x.v = k_ring[st].v;
+        x.kb = t * kKTile;
         x.full = row_w + 32 <= Lq && x.kb + 32 <= Lk && (!a.causal || x.kb + 31 <= row_w + diag);
         return x;
     };
-    // step s: the P waves work on tile s, the dS waves on tile s - 1 (and on the first block of tile s).
-    // At its barrier tile s is in LDS and so is the P^T of tile s - 1, and every wave is done with tile
-    // s - 2 (stage and exchange).  Each role runs its own loop; both pass ntiles + 1 barriers.
+    // step s: S waves on tile s, D waves on tile s - 1, Q waves on tile s - 2.  At its barrier tile s is in
+    // LDS, so are the P^T of tile s - 1 and the dS^T of tile s - 2, and every wave is done with tile s - 3
+    // (stage) and with the exchange buffers of two tiles back.  Each role runs its own loop; all pass
+    // ntiles + 2 barriers.
     auto sync = [&](int s) {
         wait_vmcnt<0>();
         wait_lds();
@@ -766,45 +766,47 @@ __global__ __launch_bounds__(kDqThreads) void bwd_dq_kernel(BwdArgs a, int NH, i
 
     if (ntiles > 0) {
         ld.issue(0, 0);
-        if (pwave) {
+        Packed none;
+        f32x16 fnone;
+        if (role == 0) {
             for (int s = 0; s < ntiles; ++s) {
                 sync(s);
-                const KBlk b0 = blk(s, 0), b1 = blk(s, 1);
-                char *xb = pt_xchg[s & 1][pair];
-                f32x16 s0, s1;
-                Packed p0, p1;
-                dq_phase<true, true, false, false>(L, bop, dq, b0.k, s0, nullptr, p0, b0, s0, p0, p0);
-                dq_phase<true, true, false, true>(L, bop, dq, b1.k, s1, nullptr, p0, b0, s0, p0, p0);
-                xchg_store(xb, lane, p0);
-                dq_phase<true, false, false, true>(L, bop, dq, nullptr, s1, nullptr, p0, b1, s1, p1, p1);
-                xchg_store(xb + kXchgBlock, lane, p1);
+                const KBlk bt = blk(s);
+                f32x16 st;
+                Packed p;
+                dq_phase<true, true, false, false>(L, bop, dq, bt.k, st, nullptr, none, bt, st, none, none);
+                dq_phase<true, false, false, true>(L, bop, dq, nullptr, fnone, nullptr, none, bt, st, none, p);
+                xchg_store(pt_xchg[s & 1][grp], lane, p);
             }
             sync(ntiles);
-        } else {
-            f32x16 dn; // dP^T of the first block of the next tile
+            sync(ntiles + 1);
+        } else if (role == 1) {
             sync(0);
-            {
-                Packed none;
-                const KBlk b0 = blk(0, 0);
-                dq_phase<false, true, false, false>(L, bop, dq, b0.v, dn, nullptr, none, b0, dn, none, none);
-            }
             for (int s = 1; s <= ntiles; ++s) {
                 sync(s);
-                // tile s - 1; the next tile's first block (after the last tile: a resident block, dn unused)
-                const KBlk b0 = blk(s - 1, 0), b1 = blk(s - 1, 1), nb = blk(s < ntiles ? s : s - 1, 0);
-                const char *xb = pt_xchg[(s - 1) & 1][pair];
-                f32x16 d1;
-                Packed p0, p1, t0, t1;
-                xchg_load(xb, lane, p0);
-                xchg_load(xb + kXchgBlock, lane, p1);
-                dq_phase<false, true, false, true>(L, bop, dq, b1.v, d1, nullptr, t0, b0, dn, p0, t0);
-                dq_phase<false, false, true, true>(L, bop, dq, nullptr, d1, b0.k, t0, b1, d1, p1, t1);
-                dq_phase<false, true, true, false>(L, bop, dq, nb.v, dn, b1.k, t1, nb, d1, p1, t1);
+                const KBlk bt = blk(s - 1);
+                f32x16 dp;
+                Packed p, ds;
+                xchg_load(pt_xchg[(s - 1) & 1][grp], lane, p);
+                dq_phase<false, true, false, false>(L, bop, dq, bt.v, dp, nullptr, none, bt, dp, none, none);
+                dq_phase<false, false, false, true>(L, bop, dq, nullptr, fnone, nullptr, none, bt, dp, p, ds);
+                xchg_store(dst_xchg[(s - 1) & 1][grp], lane, ds);
+            }
+            sync(ntiles + 1);
+        } else {
+            sync(0);
+            sync(1);
+            for (int s = 2; s <= ntiles + 1; ++s) {
+                sync(s);
+                const KBlk bt = blk(s - 2);
+                Packed ds;
+                xchg_load(dst_xchg[(s - 2) & 1][grp], lane, ds);
+                dq_phase<false, false, true, false>(L, bop, dq, nullptr, fnone, bt.k, ds, bt, fnone, none, none);
             }
         }
     }
 
-    if (pwave || !row_ok)
+    if (role != 2 || !row_ok)
         return;
     uint16_t *dqg = static_cast<uint16_t *>(a.dq) + ((size_t)(q0 + qi) * a.Hq + h) * D;
 #pragma unroll
@@ -823,7 +825,7 @@ __global__ __launch_bounds__(kDqThreads) void bwd_dq_kernel(BwdArgs a, int NH, i
 static int heads_per_wg_bwd(int G)
 {
     int nh = 1;
-    while (nh < kDqPairs && G % (2 * nh) == 0)
+    while (nh < kDqGroups && G % (2 * nh) == 0)
         nh *= 2;
     return nh;
 }
@@ -838,7 +840,7 @@ hipError_t launch_prefill_bwd(const BwdArgs &a, hipStream_t stream)
     const int nkt = (a.max_k + kKeysPerWg - 1) / kKeysPerWg;
     const long units_kv = (long)a.Hkv * a.B * nkt;
     const long blocks_kv = (units_kv + kXcds - 1) / kXcds * kXcds;
-    const int NH = heads_per_wg_bwd(a.G), RB = kDqPairs / NH;
+    const int NH = heads_per_wg_bwd(a.G), RB = kDqGroups / NH;
     const int nqt = (a.max_q + 32 * RB - 1) / (32 * RB);
     const long units_q = (long)a.Hkv * (a.G / NH) * a.B * nqt;
     const long blocks_q = (units_q + kXcds - 1) / kXcds * kXcds;
