@@ -81,6 +81,26 @@ def test_prefill_bf16_varlen_ragged(D, causal):
     assert np.max(np.abs(_np(lse) - ld)) <= 1e-3
 
 
+@pytest.mark.parametrize("B", [256, 300])
+@pytest.mark.parametrize("causal", [True, False])
+def test_prefill_bf16_batch_schedules(B, causal):
+    # large batches of short ragged sequences (most units of the grid past their sequence's end), with
+    # empty and one-row sequences, against the oracle
+    rng = np.random.default_rng(71 + B)
+    lens = rng.integers(0, 160, size=B)
+    lens[::37] = 0
+    lens[5::41] = 1
+    x = W.varlen_prefill(seed=37, device=DEV, lengths=lens.tolist(), Hq=8, Hkv=2, D=128)
+    o, lse, _ = attn.attn_prefill_varlen(x.q, x.k, x.v, x.cu_q, x.cu_k, x.max_q, x.max_k, causal=causal,
+                                         return_lse=True)
+    torch.cuda.synchronize()
+    od, ld, _ = oracle.prefill(x.q.cpu(), x.k.cpu(), x.v.cpu(), x.cu_q.cpu(), x.cu_k.cpu(), 8, 2, x.scale, causal)
+    assert np.max(np.abs(_np(o) - od)) <= BF16_TOL
+    ok = np.isfinite(ld)
+    assert np.max(np.abs(_np(lse)[ok] - ld[ok])) <= 1e-3
+    assert np.all(np.isneginf(_np(lse)[~ok]))
+
+
 @pytest.mark.parametrize("Hq,Hkv", [(8, 8), (16, 2), (32, 2), (12, 3), (6, 2)])
 @pytest.mark.parametrize("thr", [0.0, 0.1])
 def test_prefill_bf16_gqa_groupings(Hq, Hkv, thr):
