@@ -813,6 +813,9 @@ PROFILE_COMMANDS = {
              "--launch-log {out}/prof_write/launch_log.json",
     "mfma": "rocprofv3 --pmc MfmaUtil SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_BUSY_CYCLES -f csv -d {out}/prof_mfma -o run -- "
             "python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline --launch-log {out}/prof_mfma/launch_log.json",
+    "sq": "rocprofv3 --pmc MfmaUtil VALUBusy LdsUtil LdsBankConflict SQ_VALU_MFMA_BUSY_CYCLES SQ_VALU_MFMA_COEXEC_CYCLES "
+          "SQ_WAIT_INST_LDS SQ_WAVE_CYCLES -f csv -d {out}/prof_sq -o run -- "
+          "python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline --launch-log {out}/prof_sq/launch_log.json",
     "summary": "python3 bench.py --summarize-profiles {out}",
 }
 
@@ -949,6 +952,8 @@ def _summarize_profiles(base):
     print("wrote profiles/traffic.json")
     if os.path.isdir(os.path.join(base, "prof_mfma")):
         _summarize_mfma(base, durs)
+    if os.path.isdir(os.path.join(base, "prof_sq")):
+        _summarize_sq(base)
 
 
 # kernels whose matrix-core use the MFMA-busy summary reports (the contraction-bound ones)
@@ -993,6 +998,60 @@ def _summarize_mfma(base, durs):
     with open(path, "w") as f:
         f.write("\n".join(lines) + "\n")
     print("wrote profiles/mfma_busy.bench_workloads.txt")
+
+
+def _summarize_sq(base):
+    """Where the contraction-bound kernels spend their cycles, from rocprofv3's derived counters (MfmaUtil,
+    VALUBusy, LdsUtil, LdsBankConflict) and three SQ counters: the share of MFMA-busy cycles in which a
+    VALU instruction issued too (SQ_VALU_MFMA_COEXEC_CYCLES / SQ_VALU_MFMA_BUSY_CYCLES), and the share of
+    wave cycles spent waiting for LDS instructions (SQ_WAIT_INST_LDS / SQ_WAVE_CYCLES); per kernel and
+    bench call, into profiles/sq_counters.bench_workloads.txt."""
+    import numpy as np
+    rows = _csv(os.path.join(base, "prof_sq"), "counter_collection.csv")
+    mean = dict(reduce=np.mean)
+    cols = {"MfmaUtil": _per_dispatch_counter(rows, "MfmaUtil", **mean),
+            "VALUBusy": _per_dispatch_counter(rows, "VALUBusy", **mean),
+            "LdsUtil": _per_dispatch_counter(rows, "LdsUtil", **mean),
+            "LdsBankConflict": _per_dispatch_counter(rows, "LdsBankConflict", **mean)}
+    coexec = _per_dispatch_counter(rows, "SQ_VALU_MFMA_COEXEC_CYCLES")
+    mbusy = _per_dispatch_counter(rows, "SQ_VALU_MFMA_BUSY_CYCLES")
+    wlds = _per_dispatch_counter(rows, "SQ_WAIT_INST_LDS")
+    wcyc = _per_dispatch_counter(rows, "SQ_WAVE_CYCLES")
+    lines = ["# SQ counters per kernel, rocprofv3 (one dispatch = one launch), bench workloads as in the kernel",
+             "# summaries of this folder",
+             "# commands (repository root, TMPDIR=/tmp; the summary step runs on any host):",
+             "\n".join(f"#   {k}: {v.format(out=base)}" for k, v in PROFILE_COMMANDS.items()),
+             "# MfmaUtil, VALUBusy, LdsUtil (%) and LdsBankConflict (conflict cycles per LDS access) as rocprofv3",
+             "# derives them; coexec = SQ_VALU_MFMA_COEXEC_CYCLES / SQ_VALU_MFMA_BUSY_CYCLES (the share of",
+             "# MFMA-busy cycles in which a VALU instruction also issued); LDS wait = SQ_WAIT_INST_LDS /",
+             "# SQ_WAVE_CYCLES (the share of wave cycles spent waiting to issue an LDS instruction)", ""]
+    for k in MFMA_KERNELS:
+        if k not in cols["MfmaUtil"]:
+            continue
+        n = len(cols["MfmaUtil"][k])
+        roles = _roles(base, "prof_sq", k, n) or ["all"] * n
+
+        def part(vals, r):
+            return [v for v, x in zip(vals, roles) if x == r] if len(vals) == n else []
+
+        lines.append(f"{k}: {n} dispatches")
+        for r in dict.fromkeys(roles):
+            f = []
+            for name, c in cols.items():
+                v = part(c.get(k, []), r)
+                if v:
+                    f.append(f"{name} {np.mean(v):.3g}" + (" %" if name != "LdsBankConflict" else ""))
+            ce, mb = part(coexec.get(k, []), r), part(mbusy.get(k, []), r)
+            if ce and mb and sum(mb) > 0:
+                f.append(f"coexec {sum(ce) / sum(mb):.2f}")
+            wl, wc = part(wlds.get(k, []), r), part(wcyc.get(k, []), r)
+            if wl and wc and sum(wc) > 0:
+                f.append(f"LDS wait {100 * sum(wl) / sum(wc):.1f} %")
+            lines.append(f"    {r}: " + ", ".join(f))
+    path = os.path.join(ROOT, "profiles", "sq_counters.bench_workloads.txt")
+    with open(path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("wrote profiles/sq_counters.bench_workloads.txt")
 
 
 if __name__ == "__main__":
