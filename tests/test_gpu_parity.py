@@ -331,6 +331,32 @@ def test_decode_zero_length_and_block_table_permutation():
     assert torch.equal(o1, o2)
 
 
+@pytest.mark.parametrize("B", [100, 200])
+@pytest.mark.parametrize("thr", [0.0, 0.1])
+def test_decode_sequential_batch_order(B, thr):
+    # the sequential decode takes up to 128 batch rows longest first (each workgroup ranks the lengths in
+    # LDS) and larger batches in index order: both against the oracle, with empty and one-token rows and
+    # ties among the lengths
+    rng = np.random.default_rng(81 + B)
+    lengths = rng.integers(0, 700, size=B)
+    lengths[::23] = 0
+    lengths[1::29] = 1
+    lengths[2::31] = 256
+    x = W.paged_decode(seed=57, device=DEV, B=B, Hq=8, Hkv=2, D=128, page=16, pool=64 * B, lengths=lengths.tolist(),
+                       lmax=720, hot=True)
+    o, lse, smap = attn.attn_decode_paged(x.q, x.k_cache, x.v_cache, x.block_table, x.seq_lens, num_splits=1,
+                                          skip_threshold=thr, return_lse=True, return_skip_map=True)
+    torch.cuda.synchronize()
+    _, _, om = _decode_oracle(x, mode="skip", thr=thr, tile=32, stride=smap.shape[-1])
+    g, _ = _check_map(smap, om)
+    orp, lrp, _ = _decode_oracle(x, mode="skip", tile=32, replay=np.where(g == 2, 0, g).reshape(-1, g.shape[-1]),
+                                 stride=g.shape[-1])
+    assert np.max(np.abs(_np(o) - orp)) <= BF16_TOL
+    ok = np.isfinite(lrp)
+    assert np.max(np.abs(_np(lse)[ok] - lrp[ok])) <= 1e-3
+    assert np.all(np.isneginf(_np(lse)[~ok]))
+
+
 @pytest.mark.parametrize("thr", [0.0, 0.01, 0.1, 0.5])
 def test_decode_sequential_skip(thr):
     x = _small_decode(hot=True)
