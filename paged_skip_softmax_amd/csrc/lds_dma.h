@@ -82,6 +82,16 @@ __device__ __forceinline__ void dma16(uint32_t lds, uint32_t voff, i32x4 rsrc, u
                  : "s"(lds), "v"(voff), "s"(rsrc), "s"(soff)
                  : "memory");
 }
+// dma16 to lds + OFF: the offset is added while m0 is set (an immediate), so a caller issuing several
+// chunks from one base keeps one scalar register for them instead of one per chunk.
+template <uint32_t OFF>
+__device__ __forceinline__ void dma16_at(uint32_t lds, uint32_t voff, i32x4 rsrc, uint32_t soff)
+{
+    asm volatile("s_add_u32 m0, %0, %4\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+                 :
+                 : "s"(lds), "v"(voff), "s"(rsrc), "s"(soff), "n"(OFF)
+                 : "memory", "scc");
+}
 __device__ __forceinline__ void dma4(uint32_t lds, uint32_t voff, i32x4 rsrc, uint32_t soff)
 {
     asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, %3 offen lds"

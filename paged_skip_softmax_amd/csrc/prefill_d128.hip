@@ -107,11 +107,13 @@ struct Loader {
         return i32x4{__builtin_amdgcn_readfirstlane(r[0]), __builtin_amdgcn_readfirstlane(r[1]),
                      __builtin_amdgcn_readfirstlane(r[2]), r[3]};
     }
+    template <int P = 0>
     __device__ __forceinline__ void issue(const i32x4 &rs, uint32_t m0, uint32_t soff) const
     {
-#pragma unroll
-        for (int p = 0; p < kLoadsPerWave; ++p)
-            dma16(m0 + p * 1024, voff[p], rs, soff);
+        if constexpr (P < kLoadsPerWave) {
+            dma16_at<P * 1024>(m0, voff[P], rs, soff);
+            issue<P + 1>(rs, m0, soff);
+        }
     }
     template <int ST> __device__ __forceinline__ void issue_k(int t, int page) const
     {
