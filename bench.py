@@ -1017,6 +1017,18 @@ def _summarize_sq(base):
     mbusy = _per_dispatch_counter(rows, "SQ_VALU_MFMA_BUSY_CYCLES")
     wlds = _per_dispatch_counter(rows, "SQ_WAIT_INST_LDS")
     wcyc = _per_dispatch_counter(rows, "SQ_WAVE_CYCLES")
+    # dispatch duration (ns) from the rows' timestamps, for the shader clock: GRBM_GUI_ACTIVE cycles,
+    # recovered from MfmaUtil = 100 * MFMA-busy cycles / (GRBM_GUI_ACTIVE * SIMDs), over the duration
+    span = {}
+    for r in rows:
+        if r["Counter_Name"] == "MfmaUtil":
+            span[int(r["Dispatch_Id"])] = (_match(r["Kernel_Name"]),
+                                           int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+    durs = {}
+    for d in sorted(span):
+        if span[d][0]:
+            durs.setdefault(span[d][0], []).append(span[d][1])
+    simds = 4 * 256
     lines = ["# SQ counters per kernel, rocprofv3 (one dispatch = one launch), bench workloads as in the kernel",
              "# summaries of this folder",
              "# commands (repository root, TMPDIR=/tmp; the summary step runs on any host):",
@@ -1024,7 +1036,10 @@ def _summarize_sq(base):
              "# MfmaUtil, VALUBusy, LdsUtil (%) and LdsBankConflict (conflict cycles per LDS access) as rocprofv3",
              "# derives them; coexec = SQ_VALU_MFMA_COEXEC_CYCLES / SQ_VALU_MFMA_BUSY_CYCLES (the share of",
              "# MFMA-busy cycles in which a VALU instruction also issued); LDS wait = SQ_WAIT_INST_LDS /",
-             "# SQ_WAVE_CYCLES (the share of wave cycles spent waiting to issue an LDS instruction)", ""]
+             "# SQ_WAVE_CYCLES (the share of wave cycles spent waiting to issue an LDS instruction); clock =",
+             "# GRBM_GUI_ACTIVE cycles (100 * MFMA-busy cycles / (MfmaUtil * 1024 SIMDs)) over the dispatch's",
+             "# duration under counter collection: the shader clock the kernel ran at (published maximum",
+             "# 2.4 GHz)", ""]
     for k in MFMA_KERNELS:
         if k not in cols["MfmaUtil"]:
             continue
@@ -1047,6 +1062,11 @@ def _summarize_sq(base):
             wl, wc = part(wlds.get(k, []), r), part(wcyc.get(k, []), r)
             if wl and wc and sum(wc) > 0:
                 f.append(f"LDS wait {100 * sum(wl) / sum(wc):.1f} %")
+            mu, du = part(cols["MfmaUtil"].get(k, []), r), part(durs.get(k, []), r)
+            if mb and mu and du and len(mb) == len(mu) == len(du):
+                ghz = [100 * b / (u * simds) / t for b, u, t in zip(mb, mu, du) if u > 0 and t > 0]
+                if ghz:
+                    f.append(f"clock {np.mean(ghz):.2f} GHz")
             lines.append(f"    {r}: " + ", ".join(f))
     path = os.path.join(ROOT, "profiles", "sq_counters.bench_workloads.txt")
     with open(path, "w") as f:
