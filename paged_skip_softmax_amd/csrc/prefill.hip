@@ -287,98 +287,146 @@ void prefill_bf16_kernel(PrefillArgs a)
 
 // ------------------------------------------------------------------ fp32
 
-constexpr int kF32Tile = 32; // keys per LDS tile = skip tile
+constexpr int kF32Tile = 32;                  // keys per LDS tile = skip tile
+constexpr int kF32Rows = 64;                  // query rows per workgroup
+constexpr int kF32Parts = 4;                  // lanes per row (a lane quad), each with D / 4 dims
+constexpr int kF32Threads = kF32Rows * kF32Parts;
 
+// fp32 on the VALU: a lane quad per query row, each lane holding a quarter of the dims of q and of the
+// output; a score is the quad's four partial dot products summed across the quad.  K and V tiles of 32
+// keys are double-buffered in LDS, the next one loaded into registers while the current one is used.
 template <int D>
-__global__ __launch_bounds__(64) void prefill_f32_kernel(PrefillArgs a)
+__global__ __launch_bounds__(kF32Threads) void prefill_f32_kernel(PrefillArgs a)
 {
-    __shared__ float ks[kF32Tile][D];
-    __shared__ float vs[kF32Tile][D];
+    constexpr int DP = D / kF32Parts;                   // dims per lane
+    constexpr int kLd = kF32Tile * D / 4 / kF32Threads; // float4 loads per lane per tile, K and V each
+    static_assert(kLd >= 1 && kF32Tile * D == kLd * 4 * kF32Threads, "whole float4 loads per lane");
+    __shared__ float4 ks[2][kF32Tile][D / 4];
+    __shared__ float4 vs[2][kF32Tile][D / 4];
     const int h = blockIdx.x, b = blockIdx.y;
     const int qt = gridDim.z - 1 - blockIdx.z;
     const int q0 = a.cu_q[b], Lq = a.cu_q[b + 1] - q0;
     const int k0 = a.cu_k[b], Lk = a.cu_k[b + 1] - k0;
-    const int m0 = qt * 64;
+    const int m0 = qt * kF32Rows;
     if (m0 >= Lq)
         return;
-    const int g = h / a.G, lane = threadIdx.x;
-    const int qi = m0 + lane;
+    const int g = h / a.G, tid = threadIdx.x;
+    const int row = tid / kF32Parts, part = tid % kF32Parts;
+    const int qi = m0 + row;
     const bool row_ok = qi < Lq;
     const int diag = Lk - Lq;
-    const int last_row = min(m0 + 64, Lq) - 1;
+    const int last_row = min(m0 + kF32Rows, Lq) - 1;
     const int kend = a.causal ? max(0, min(Lk, last_row + 1 + diag)) : Lk;
     const int kend_row = !row_ok ? 0 : (a.causal ? max(0, min(Lk, qi + 1 + diag)) : Lk);
     const float *qg = static_cast<const float *>(a.q);
-    const float *kg = static_cast<const float *>(a.k);
-    const float *vg = static_cast<const float *>(a.v);
+    const float4 *kg = static_cast<const float4 *>(a.k);
+    const float4 *vg = static_cast<const float4 *>(a.v);
 
-    float q[D], acc[D];
+    float q[DP], acc[DP];
 #pragma unroll
-    for (int d = 0; d < D; ++d) {
-        q[d] = row_ok ? qg[((size_t)(q0 + qi) * a.Hq + h) * D + d] : 0.f;
+    for (int d = 0; d < DP; ++d) {
+        q[d] = row_ok ? qg[((size_t)(q0 + qi) * a.Hq + h) * D + DP * part + d] : 0.f;
         acc[d] = 0.f;
     }
     float m = kNegInf, l = 0.f;
-    uint8_t *maprow = (a.skip_map && row_ok) ? a.skip_map + ((size_t)(q0 + qi) * a.Hq + h) * a.map_stride : nullptr;
+    uint8_t *maprow = (a.skip_map && row_ok && part == 0)
+                          ? a.skip_map + ((size_t)(q0 + qi) * a.Hq + h) * a.map_stride : nullptr;
     if (maprow)
         for (int t = (kend_row + kF32Tile - 1) / kF32Tile; t < a.map_stride; ++t)
             maprow[t] = 2;
 
-    for (int kb = 0; kb < kend; kb += kF32Tile) {
-        __syncthreads();
-        for (int idx = lane; idx < kF32Tile * D; idx += 64) {
-            const int key = idx / D, d = idx % D;
+    // tile loads: float4 index e = tid + kF32Threads * i of the tile, key e / (D / 4), dims 4 (e % (D / 4))
+    float4 kr[kLd], vr[kLd];
+    auto load = [&](int kb) {
+#pragma unroll
+        for (int i = 0; i < kLd; ++i) {
+            const int e = tid + kF32Threads * i, key = e / (D / 4), c = e % (D / 4);
             const bool in = kb + key < Lk;
-            const size_t off = ((size_t)(k0 + kb + key) * a.Hkv + g) * D + d;
-            ks[key][d] = in ? kg[off] : 0.f;
-            vs[key][d] = in ? vg[off] : 0.f;
+            const size_t off = ((size_t)(k0 + kb + key) * a.Hkv + g) * (D / 4) + c;
+            kr[i] = in ? kg[off] : make_float4(0.f, 0.f, 0.f, 0.f);
+            vr[i] = in ? vg[off] : make_float4(0.f, 0.f, 0.f, 0.f);
         }
-        __syncthreads();
-        if (kb >= kend_row)
-            continue;
-        const int nk = min(kF32Tile, kend_row - kb);
-        float s[kF32Tile];
-        float tmax = kNegInf;
+    };
+    auto store = [&](int buf) {
 #pragma unroll
-        for (int j = 0; j < kF32Tile; ++j) {
-            float t = 0.f;
-#pragma unroll
-            for (int d = 0; d < D; ++d)
-                t = fmaf(q[d], ks[j][d], t);
-            s[j] = j < nk ? t * a.scale_log2 : kNegInf;
-            tmax = fmaxf(tmax, s[j]);
+        for (int i = 0; i < kLd; ++i) {
+            const int e = tid + kF32Threads * i, key = e / (D / 4), c = e % (D / 4);
+            ks[buf][key][c] = kr[i];
+            vs[buf][key][c] = vr[i];
         }
-        const bool skip = m != kNegInf && tmax - m < a.log2_thr;
-        if (maprow)
-            maprow[kb / kF32Tile] = skip ? 1 : 0;
-        if (skip)
-            continue;
-        const float m_new = fmaxf(m, tmax);
-        const float alpha = exp2_fast(m - m_new);
-        l *= alpha;
+    };
+    const int ntiles = (kend + kF32Tile - 1) / kF32Tile;
+    if (ntiles > 0) {
+        load(0);
+        store(0);
+    }
+    __syncthreads();
+    for (int t = 0; t < ntiles; ++t) {
+        const int kb = t * kF32Tile, buf = t & 1;
+        if (t + 1 < ntiles)
+            load(kb + kF32Tile);
+        if (kb < kend_row) {
+            const int nk = min(kF32Tile, kend_row - kb);
+            float s[kF32Tile];
+            float tmax = kNegInf;
 #pragma unroll
-        for (int d = 0; d < D; ++d)
-            acc[d] *= alpha;
+            for (int j = 0; j < kF32Tile; ++j) {
+                float x = 0.f;
 #pragma unroll
-        for (int j = 0; j < kF32Tile; ++j) {
-            if (j < nk) {
-                const float p = exp2_fast(s[j] - m_new);
-                l += p;
+                for (int c = 0; c < DP / 4; ++c) {
+                    const float4 kv = ks[buf][j][DP / 4 * part + c];
+                    x = fmaf(q[4 * c], kv.x, x);
+                    x = fmaf(q[4 * c + 1], kv.y, x);
+                    x = fmaf(q[4 * c + 2], kv.z, x);
+                    x = fmaf(q[4 * c + 3], kv.w, x);
+                }
+                x += __shfl_xor(x, 1);
+                x += __shfl_xor(x, 2);
+                s[j] = j < nk ? x * a.scale_log2 : kNegInf;
+                tmax = fmaxf(tmax, s[j]);
+            }
+            const bool skip = m != kNegInf && tmax - m < a.log2_thr;
+            if (maprow)
+                maprow[kb / kF32Tile] = skip ? 1 : 0;
+            if (!skip) {
+                const float m_new = fmaxf(m, tmax);
+                const float alpha = exp2_fast(m - m_new);
+                l *= alpha;
 #pragma unroll
-                for (int d = 0; d < D; ++d)
-                    acc[d] = fmaf(p, vs[j][d], acc[d]);
+                for (int d = 0; d < DP; ++d)
+                    acc[d] *= alpha;
+#pragma unroll
+                for (int j = 0; j < kF32Tile; ++j) {
+                    if (j < nk) {
+                        const float p = exp2_fast(s[j] - m_new);
+                        l += p;
+#pragma unroll
+                        for (int c = 0; c < DP / 4; ++c) {
+                            const float4 vv = vs[buf][j][DP / 4 * part + c];
+                            acc[4 * c] = fmaf(p, vv.x, acc[4 * c]);
+                            acc[4 * c + 1] = fmaf(p, vv.y, acc[4 * c + 1]);
+                            acc[4 * c + 2] = fmaf(p, vv.z, acc[4 * c + 2]);
+                            acc[4 * c + 3] = fmaf(p, vv.w, acc[4 * c + 3]);
+                        }
+                    }
+                }
+                m = m_new;
             }
         }
-        m = m_new;
+        // the other buffer was last read during tile t - 1, which every lane finished before the barrier
+        // that ended it
+        if (t + 1 < ntiles)
+            store(buf ^ 1);
+        __syncthreads();
     }
     if (!row_ok)
         return;
     const float inv = l > 0.f ? 1.f / l : 0.f;
-    float *og = static_cast<float *>(a.o) + ((size_t)(q0 + qi) * a.Hq + h) * D;
+    float *og = static_cast<float *>(a.o) + ((size_t)(q0 + qi) * a.Hq + h) * D + DP * part;
 #pragma unroll
-    for (int d = 0; d < D; ++d)
+    for (int d = 0; d < DP; ++d)
         og[d] = acc[d] * inv;
-    if (a.lse)
+    if (a.lse && part == 0)
         a.lse[(size_t)(q0 + qi) * a.Hq + h] = l > 0.f ? (m + __log2f(l)) * kLn2 : kNegInf;
 }
 
@@ -401,8 +449,8 @@ hipError_t launch_prefill(const PrefillArgs &a, bool bf16, int D, hipStream_t st
     }
     if (D != 64)
         return hipErrorNotSupported;
-    dim3 grid(a.Hq, a.B, (a.max_q + 63) / 64);
-    ATTN_LAUNCH((prefill_f32_kernel<64>), grid, dim3(64), 0, stream, a);
+    dim3 grid(a.Hq, a.B, (a.max_q + kF32Rows - 1) / kF32Rows);
+    ATTN_LAUNCH((prefill_f32_kernel<64>), grid, dim3(kF32Threads), 0, stream, a);
     return hipGetLastError();
 }
 

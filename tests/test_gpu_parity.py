@@ -68,6 +68,36 @@ def test_tiny_dense_fp32(causal, thr):
     assert np.max(np.abs(_np(lse) - lrp)) <= F32_TOL
 
 
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("thr", [0.0, 0.1])
+def test_fp32_varlen_ragged_cross(causal, thr):
+    # fp32 over several 64-row blocks and 32-key tiles: ragged lengths, an empty sequence, and queries
+    # fewer than keys (bottom-right causal) or more (rows that see no key)
+    lk = [1, 17, 128, 0, 129, 300, 64, 255, 40]
+    lq = [1, 5, 128, 0, 70, 300, 1, 200, 100]
+    kv = W.tiny_dense(seed=1010, device=DEV, lengths=lk)
+    qq = W.tiny_dense(seed=1011, device=DEV, lengths=lq)
+    o, lse, smap = attn.attn_prefill_varlen(qq.q, kv.k, kv.v, qq.cu_q, kv.cu_k, qq.max_q, kv.max_k,
+                                            scale=kv.scale, causal=causal, skip_threshold=thr, return_lse=True,
+                                            return_skip_map=True)
+    torch.cuda.synchronize()
+    args = (qq.q.cpu(), kv.k.cpu(), kv.v.cpu(), qq.cu_q.cpu(), kv.cu_k.cpu(), kv.Hq, kv.Hkv, kv.scale, causal)
+    _, _, om = oracle.prefill(*args, mode="skip", thr=thr, tile=32, stride=smap.shape[-1])
+    g, _ = _check_map(smap, om)
+    if thr == 0:
+        od, ld, _ = oracle.prefill(*args)
+        assert np.max(np.abs(_np(o) - od)) <= F32_TOL
+        fin = np.isfinite(ld)
+        assert np.array_equal(fin, np.isfinite(_np(lse)))
+        assert np.max(np.abs(_np(lse)[fin] - ld[fin])) <= F32_TOL
+    orp, lrp, _ = oracle.prefill(*args, mode="skip", tile=32, replay=np.where(g == 2, 0, g).reshape(-1, g.shape[-1]),
+                                 stride=g.shape[-1])
+    assert np.max(np.abs(_np(o) - orp)) <= F32_TOL
+    fin = np.isfinite(lrp)
+    assert np.array_equal(fin, np.isfinite(_np(lse)))
+    assert np.max(np.abs(_np(lse)[fin] - lrp[fin])) <= F32_TOL
+
+
 @pytest.mark.parametrize("D", [128, 64])
 @pytest.mark.parametrize("causal", [True, False])
 def test_prefill_bf16_varlen_ragged(D, causal):
