@@ -52,38 +52,49 @@ __device__ __forceinline__ void stage_rows(char *tile, const uint16_t *src, size
 
 // ------------------------------------------------------------------ Dsum and lse in log2 units
 
+constexpr int kPrepUnroll = 4; // rows a 16-lane group has in flight together
+
+// The (token, query head) rows are contiguous in O, dO and the LSE ([T, Hq, ...]); a grid-stride loop
+// over the T * Hq rows (T = cu_seqlens_q[B], read on the device), 16 lanes per row with 8 dims each and
+// kPrepUnroll rows per group in flight.
 __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdArgs a)
 {
-    // 16 lanes per (sequence, row, query head) slot of the padded [B, max_q, Hq] grid, 8 dims each
-    const int slot = blockIdx.x * 16 + (threadIdx.x >> 4), c = threadIdx.x & 15;
-    const int per_seq = a.max_q * a.Hq;
-    const int b = slot / per_seq, i = (slot % per_seq) / a.Hq, h = slot % a.Hq;
-    bool live = b < a.B;
-    size_t row = 0;
-    if (live) {
-        const int q0 = a.cu_q[b];
-        live = i < a.cu_q[b + 1] - q0;
-        row = (size_t)(q0 + i) * a.Hq + h;
-    }
-    float s = 0.f;
-    if (live) {
-        const uint16_t *o = static_cast<const uint16_t *>(a.o), *dout = static_cast<const uint16_t *>(a.dout);
-        const uint4 x = ld16(o + row * D + 8 * c), g = ld16(dout + row * D + 8 * c);
-        const uint32_t xw[4] = {x.x, x.y, x.z, x.w}, gw[4] = {g.x, g.y, g.z, g.w};
+    // valid cu_seqlens give T <= B * max_q, the rows the workspace holds; the bound keeps the writes in it
+    const long rows = min((long)a.cu_q[a.B], (long)a.B * a.max_q) * a.Hq;
+    const int c = threadIdx.x & 15;
+    const long group = (long)blockIdx.x * 16 + (threadIdx.x >> 4), groups = (long)gridDim.x * 16;
+    const uint16_t *o = static_cast<const uint16_t *>(a.o), *dout = static_cast<const uint16_t *>(a.dout);
+    for (long r0 = group; r0 < rows; r0 += groups * kPrepUnroll) {
+        uint4 x[kPrepUnroll], g[kPrepUnroll];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            s = fmaf(bf16_lo(xw[e]), bf16_lo(gw[e]), s);
-            s = fmaf(bf16_hi(xw[e]), bf16_hi(gw[e]), s);
+        for (int u = 0; u < kPrepUnroll; ++u) {
+            const long row = r0 + u * groups;
+            x[u] = g[u] = make_uint4(0, 0, 0, 0);
+            if (row < rows) {
+                x[u] = ld16(o + row * D + 8 * c);
+                g[u] = ld16(dout + row * D + 8 * c);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < kPrepUnroll; ++u) {
+            const long row = r0 + u * groups;
+            const uint32_t xw[4] = {x[u].x, x[u].y, x[u].z, x[u].w}, gw[4] = {g[u].x, g[u].y, g[u].z, g[u].w};
+            float s = 0.f;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                s = fmaf(bf16_lo(xw[e]), bf16_lo(gw[e]), s);
+                s = fmaf(bf16_hi(xw[e]), bf16_hi(gw[e]), s);
+            }
+            s += __shfl_xor(s, 8);
+            s += __shfl_xor(s, 4);
+            s += __shfl_xor(s, 2);
+            s += __shfl_xor(s, 1);
+            if (row < rows && c == 0)
+                a.dsum[row] = s;
+            if (row < rows && c == 1)
+                a.lse2[row] = a.lse[row] * kLog2e;
         }
     }
-    s += __shfl_xor(s, 8);
-    s += __shfl_xor(s, 4);
-    s += __shfl_xor(s, 2);
-    s += __shfl_xor(s, 1);
-    if (live && c == 0)
-        a.dsum[row] = s;
-    if (live && c == 1)
-        a.lse2[row] = a.lse[row] * kLog2e;
 }
 
 // ------------------------------------------------------------------ dK, dV
@@ -832,11 +843,12 @@ static int heads_per_wg_bwd(int G)
 
 hipError_t launch_prefill_bwd(const BwdArgs &a, hipStream_t stream)
 {
-    const long slots = (long)a.B * a.max_q * a.Hq;
+    const long slots = (long)a.B * a.max_q * a.Hq; // an upper bound of the T * Hq rows
     if (slots > 0x7fffffffL)
         return hipErrorInvalidValue;
     if (slots > 0)
-        ATTN_LAUNCH(bwd_prep_kernel, dim3((unsigned)((slots + 15) / 16)), dim3(256), 0, stream, a);
+        ATTN_LAUNCH(bwd_prep_kernel, dim3((unsigned)std::min<long>((slots + 15) / 16, 4096)), dim3(256), 0, stream,
+                    a);
     const int nkt = (a.max_k + kKeysPerWg - 1) / kKeysPerWg;
     const long units_kv = (long)a.Hkv * a.B * nkt;
     const long blocks_kv = (units_kv + kXcds - 1) / kXcds * kXcds;
