@@ -19,9 +19,14 @@
  * Conventions shared by every entry point
  *   - Every data pointer is a DEVICE pointer, owned by the caller, to a dense row-major array.  The
  *     library never allocates device memory, never synchronizes the stream, keeps no state besides a
- *     thread-local error message, and is reentrant.
+ *     thread-local error message, the allocation-free decode's scratch and the prefill backward's side
+ *     stream (below), and is reentrant.
  *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).  Work is enqueued on it
- *     and the call returns before the GPU finishes.
+ *     and the call returns before the GPU finishes.  The prefill backward forks part of its work onto
+ *     a side stream of the device and joins it back before returning (events recorded on `stream` and
+ *     on the side stream), so its work is ordered with `stream` like the rest; the side stream (default
+ *     priority) and two events are created on the first such call for a device that is not under
+ *     stream capture, and kept until the process ends.
  *   - Arguments are validated on the host before any HIP runtime call; a rejected call launches
  *     nothing and returns ATTN_ERR_INVALID / _UNSUPPORTED / _WORKSPACE.  Device-side contents
  *     (monotone cu_seqlens, in-range block_table entries, seq_lens within the table) are

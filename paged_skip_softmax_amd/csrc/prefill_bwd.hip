@@ -23,6 +23,8 @@
 //      D wave (dO^T in registers):  dP^T = V dO^T, dS^T = P^T (dP^T - Dsum)
 //      Q wave:                      dQ^T += K^T dS^T (K^T by transposed reads)
 //    with P^T and dS^T passed through LDS, each wave one tile behind the one before it.
+#include <mutex>
+
 #include "kcommon.h"
 #include "launch.h"
 #include "lds_dma.h"
@@ -32,23 +34,6 @@ namespace {
 
 constexpr int D = 128;
 constexpr int kRowBytes = D * 2; // one bf16 row of 128 dims
-
-// Byte offset of 16-byte chunk c of row r in a swizzled tile.
-__device__ __forceinline__ uint32_t chunk_off(int r, int c) { return (uint32_t)(r * kRowBytes + 16 * (c ^ swz(r & 15))); }
-
-// Copies rows [r0, r0 + nrows) of a [tokens, H, D] bf16 tensor (head h, rows past `valid` zero) into a
-// swizzled LDS tile, cooperatively over the workgroup's threads.
-__device__ __forceinline__ void stage_rows(char *tile, const uint16_t *src, size_t token0, int H, int h, int nrows,
-                                           int valid, int tid, int nthreads)
-{
-    for (int idx = tid; idx < nrows * 16; idx += nthreads) {
-        const int r = idx >> 4, c = idx & 15;
-        uint4 v = make_uint4(0, 0, 0, 0);
-        if (r < valid)
-            v = ld16(src + ((token0 + r) * H + h) * D + 8 * c);
-        st16(tile + chunk_off(r, c), v);
-    }
-}
 
 // ------------------------------------------------------------------ Dsum and lse in log2 units
 
@@ -841,6 +826,54 @@ static int heads_per_wg_bwd(int G)
     return nh;
 }
 
+// The backward's side stream of one device (default priority, non-blocking) and its fork / join events,
+// created on the first call for that device that is not under stream capture and kept until the
+// process ends.
+struct SideStream {
+    std::mutex mu;
+    hipStream_t s = nullptr;
+    hipEvent_t fork = nullptr, join = nullptr;
+};
+constexpr int kMaxSideDevices = 64;
+
+// The side stream of the device `stream` runs on, or null (then the kernels run on `stream` alone): when
+// the device is not the calling thread's current one, when `stream` is being captured before the side
+// stream exists, or when creating it fails.
+static SideStream *side_stream(hipStream_t stream)
+{
+    static SideStream side[kMaxSideDevices];
+    static std::mutex create_mu;
+    int cur = -1;
+    hipDevice_t dev = -1;
+    if (hipGetDevice(&cur) != hipSuccess || hipStreamGetDevice(stream, &dev) != hipSuccess || dev != cur ||
+        dev < 0 || dev >= kMaxSideDevices)
+        return nullptr;
+    SideStream &ss = side[dev];
+    std::lock_guard<std::mutex> lock(create_mu);
+    if (!ss.s) {
+        hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+        if (hipStreamIsCapturing(stream, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone)
+            return nullptr;
+        hipStream_t s = nullptr;
+        hipEvent_t f = nullptr, j = nullptr;
+        if (hipStreamCreateWithFlags(&s, hipStreamNonBlocking) != hipSuccess ||
+            hipEventCreateWithFlags(&f, hipEventDisableTiming) != hipSuccess ||
+            hipEventCreateWithFlags(&j, hipEventDisableTiming) != hipSuccess) {
+            if (j)
+                (void)hipEventDestroy(j);
+            if (f)
+                (void)hipEventDestroy(f);
+            if (s)
+                (void)hipStreamDestroy(s);
+            return nullptr;
+        }
+        ss.fork = f;
+        ss.join = j;
+        ss.s = s;
+    }
+    return &ss;
+}
+
 hipError_t launch_prefill_bwd(const BwdArgs &a, hipStream_t stream)
 {
     const long slots = (long)a.B * a.max_q * a.Hq; // an upper bound of the T * Hq rows
@@ -858,6 +891,27 @@ hipError_t launch_prefill_bwd(const BwdArgs &a, hipStream_t stream)
     const long blocks_q = (units_q + kXcds - 1) / kXcds * kXcds;
     if (blocks_kv > 0x7fffffff || blocks_q > 0x7fffffff)
         return hipErrorInvalidValue;
+    // dK/dV and dQ are independent once the prep kernel is done: dQ runs on a side stream of the device,
+    // forked from `stream` after the prep kernel and joined back after it, so each kernel's last
+    // workgroups share the GPU with the other's (same-process A/B on the prefill shapes: 3.25 -> 3.15 ms)
+    SideStream *ss = units_kv > 0 && units_q > 0 ? side_stream(stream) : nullptr;
+    if (ss) {
+        std::lock_guard<std::mutex> lock(ss->mu); // the fork / join events are shared by the device's callers
+        hipError_t e = hipEventRecord(ss->fork, stream);
+        if (e == hipSuccess)
+            e = hipStreamWaitEvent(ss->s, ss->fork, 0);
+        if (e != hipSuccess)
+            return e;
+        ATTN_LAUNCH(bwd_dq_kernel, dim3((unsigned)blocks_q), dim3(kDqThreads), 0, ss->s, a, NH, RB, nqt,
+                    (int)units_q);
+        ATTN_LAUNCH(bwd_dkdv_kernel, dim3((unsigned)blocks_kv), dim3(kKvThreads), 0, stream, a, nkt, (int)units_kv);
+        e = hipEventRecord(ss->join, ss->s);
+        if (e == hipSuccess)
+            e = hipStreamWaitEvent(stream, ss->join, 0);
+        if (e != hipSuccess)
+            return e;
+        return hipGetLastError();
+    }
     if (units_kv > 0)
         ATTN_LAUNCH(bwd_dkdv_kernel, dim3((unsigned)blocks_kv), dim3(kKvThreads), 0, stream, a, nkt,
                            (int)units_kv);

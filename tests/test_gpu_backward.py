@@ -144,6 +144,28 @@ def test_backward_deterministic():
         assert torch.equal(s, t)
 
 
+def test_backward_stream_ordered_with_two_callers():
+    # part of the backward runs on a side stream that the call forks from and joins back to its stream:
+    # copies taken on the caller's stream right after the call (no host synchronization in between) hold
+    # the finished gradients, also with two callers' streams (default priority) working at once
+    x = W.varlen_prefill(seed=53, device=DEV, lengths=[300, 65, 129, 700], Hq=8, Hkv=2)
+    do = W.grad_output(x, seed=54, device=DEV)
+    o, lse, _ = attn.attn_prefill_varlen(x.q, x.k, x.v, x.cu_q, x.cu_k, x.max_q, x.max_k, return_lse=True)
+    ref = attn.attn_prefill_varlen_backward(x.q, x.k, x.v, o, do, lse, x.cu_q, x.cu_k, x.max_q, x.max_k)
+    torch.cuda.synchronize()
+    streams = (torch.cuda.Stream(), torch.cuda.Stream())
+    outs = []
+    for st in streams:
+        st.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(st):
+            g = attn.attn_prefill_varlen_backward(x.q, x.k, x.v, o, do, lse, x.cu_q, x.cu_k, x.max_q, x.max_k)
+            outs.append([t.clone() for t in g])
+    torch.cuda.synchronize()
+    for got in outs:
+        for s_, t in zip(got, ref):
+            assert torch.equal(s_, t)
+
+
 def test_backward_full_size_sampled_sequences():
     # the full prefill workload (16 sequences of 935..4083 tokens, Hq 32, Hkv 8) in one backward call.  The
     # stored state is the GPU forward's, except for three whole sequences (the shortest, a middle and the
