@@ -893,11 +893,18 @@ def _summarize_profiles(base):
     c_fetch, c_write = max(fetch["copy"]), max(write["copy"])
     f_fetch = kib / c_fetch
     f_write = kib / c_write
-    durs = {}
+    durs, spans = {}, {}
     for r in sorted(trace, key=lambda r: int(r["Start_Timestamp"])):
         k = _match(r["Kernel_Name"])
         if k and k != "copy":
             durs.setdefault(k, []).append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+            spans.setdefault(k, []).append((int(r["Start_Timestamp"]), int(r["End_Timestamp"])))
+    # dK/dV and dQ of one backward call run at the same time (dQ on a side stream): the i-th dispatches of
+    # the two belong to the i-th call; the pair's span runs from the earlier start to the later end
+    pair = None
+    kv, dq = spans.get("bwd_dkdv_kernel", []), spans.get("bwd_dq_kernel", [])
+    if kv and len(kv) == len(dq):
+        pair = np.array([max(a[1], b[1]) - min(a[0], b[0]) for a, b in zip(kv, dq)], dtype=np.float64) / 1e3
     outdir = os.path.join(ROOT, "profiles")
     os.makedirs(outdir, exist_ok=True)
     traffic = {}
@@ -914,6 +921,11 @@ def _summarize_profiles(base):
                          f"{float(r['Percentage']):.2f}% of GPU kernel time")
         d = np.array(durs[k], dtype=np.float64) / 1e3
         lines.append(f"kernel_trace.csv: {len(d)} dispatches, mean {d.mean():.2f} us, median {np.median(d):.2f} us")
+        if k in ("bwd_dkdv_kernel", "bwd_dq_kernel") and pair is not None:
+            lines.append("  dK/dV and dQ run at the same time (dQ on a side stream forked after the prep kernel), "
+                         "so each one's duration")
+            lines.append(f"  spans time shared with the other; the two together: mean {pair.mean():.2f} us, "
+                         f"median {np.median(pair):.2f} us per call (earlier start to later end)")
         roles = _roles(base, "prof_trace", k, len(d))
         if roles:
             lines.append("  per bench call (from the run's launch log):")
