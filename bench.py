@@ -266,6 +266,8 @@ def main():
     t1 = time.perf_counter()
     ms = {nm: float(np.mean([a.elapsed_time(b) for a, b in rec[nm]])) for nm in names}
     ms_min = {nm: float(np.min([a.elapsed_time(b) for a, b in rec[nm]])) for nm in names}
+    ms_med = {nm: float(np.median([a.elapsed_time(b) for a, b in rec[nm]])) for nm in names}
+    ms_max = {nm: float(np.max([a.elapsed_time(b) for a, b in rec[nm]])) for nm in names}
     ms_per_step = (t1 - t0) * 1e3 / max(1, args.steps)
     for nm, fn in nxt.items():
         for _ in range(args.warmup):
@@ -284,7 +286,13 @@ def main():
         torch.cuda.synchronize()
         ms[nm] = float(np.mean([a.elapsed_time(b) for a, b in evs]))
         ms_min[nm] = float(np.min([a.elapsed_time(b) for a, b in evs]))
+        ms_med[nm] = float(np.median([a.elapsed_time(b) for a, b in evs]))
+        ms_max[nm] = float(np.max([a.elapsed_time(b) for a, b in evs]))
     del flush_buf
+
+    def spread(nm):
+        return {"ms_min": ms_min[nm], "ms_median": ms_med[nm], "ms_max": ms_max[nm]}
+
     print(f"# kernel ms (mean over {args.steps} steps): " + ", ".join(f"{k}={v:.4f}" for k, v in ms.items()),
           file=sys.stderr, flush=True)
 
@@ -309,7 +317,7 @@ def main():
             fl = _tiny_flops(xt, causal)
             for thr in (0.0, 0.1):
                 nm = f"tiny_{'causal' if causal else 'noncausal'}_{thr}"
-                res[nm[5:]] = {"ms": ms[nm], "ms_min": ms_min[nm], "flop_dense_equiv": fl,
+                res[nm[5:]] = {"ms": ms[nm], **spread(nm), "flop_dense_equiv": fl,
                                "gflops_dense_equiv": fl / (ms[nm] * 1e-3) / 1e9}
         res["note"] = ("fp32, B=2, Hq=4, Hkv=2, D=64, S=128, 32-key skip tiles; latency-bound (a few hundred "
                        "workgroups), reported for completeness")
@@ -318,8 +326,10 @@ def main():
         L = work["prefill"].lens.double()
         flops = 4.0 * 128 * 32 * float((L * (L + 1) / 2).sum())
         tflops = flops / (ms["prefill"] * 1e-3) / 1e12
-        out["prefill"] = {"ms": ms["prefill"], "ms_min": ms_min["prefill"], "flop": flops, "tflops": tflops,
+        out["prefill"] = {"ms": ms["prefill"], **spread("prefill"), "flop": flops, "tflops": tflops,
                           "frac_peak": tflops / PEAK_BF16_TFLOPS}
+        if achievable.get("mfma_bf16_loop_TFLOPs"):
+            out["prefill"]["frac_of_mfma_loop"] = tflops / achievable["mfma_bf16_loop_TFLOPs"]
         rooflines.append({"kernel": PF, "bound": "mfma", "achieved": tflops,
                           "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": tflops / PEAK_BF16_TFLOPS,
                           "traffic": _traffic_from_profiles(PF), "ms": ms["prefill"]})
@@ -333,7 +343,7 @@ def main():
             sub = {}
             for thr in (0.0, 0.01, 0.1):
                 t = ms[f"{key}_{thr}"]
-                ent = {"ms": t, "ms_min": ms_min[f"{key}_{thr}"], "dense_equiv_tflops": flops / (t * 1e-3) / 1e12}
+                ent = {"ms": t, **spread(f"{key}_{thr}"), "dense_equiv_tflops": flops / (t * 1e-3) / 1e12}
                 if thr > 0:
                     LAUNCH_LOG.append(f"map_{key}_{thr}")
                     _, _, smap = attn.attn_prefill_varlen(xh.q, xh.k, xh.v, xh.cu_q, xh.cu_k, xh.max_q, xh.max_k,
@@ -358,9 +368,11 @@ def main():
         kv = 4.0 * d.Hkv * d.D * float(d.lens.sum())
         gbps = kv / (ms["decode"] * 1e-3) / 1e9
         part = d.B * d.Hq * 32 * (d.D + 1) * 4 * 2
-        out["decode"] = {"ms": ms["decode"], "ms_min": ms_min["decode"], "kv_bytes": kv, "kv_GBps": gbps,
+        out["decode"] = {"ms": ms["decode"], **spread("decode"), "kv_bytes": kv, "kv_GBps": gbps,
                          "frac_peak": gbps / PEAK_HBM_GBPS, "split_partial_bytes": part,
                          "note": "time covers the split kernel and the merge kernel"}
+        if achievable.get("read_1GiB_int64_sum_GBps"):
+            out["decode"]["frac_of_plain_read"] = gbps / achievable["read_1GiB_int64_sum_GBps"]
         rooflines.append({"kernel": "decode_split_kernel+decode_merge_kernel", "bound": "hbm", "achieved": gbps,
                           "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": gbps / PEAK_HBM_GBPS,
                           "traffic": _traffic_from_profiles("decode_split_kernel"), "ms": ms["decode"]})
@@ -383,7 +395,7 @@ def main():
             kept_tiles_v = float((vis & ~vskip).sum())
             vbytes_kept = kbytes * (kept_tiles_v / float(vis.sum()))
             t = ms[f"skip_{thr}"]
-            res[str(thr)] = {"ms": t, "ms_min": ms_min[f"skip_{thr}"], "row_tile_skip_frac": f_r,
+            res[str(thr)] = {"ms": t, **spread(f"skip_{thr}"), "row_tile_skip_frac": f_r,
                              "group_v_tile_skip_frac": f_v, "bytes_read_alg": kbytes + vbytes_kept,
                              "GBps_alg": (kbytes + vbytes_kept) / (t * 1e-3) / 1e9,
                              "dense_equiv_GBps": 2 * kbytes / (t * 1e-3) / 1e9,
@@ -395,7 +407,7 @@ def main():
         for thr in ("0.0", "0.1"):
             t = ms[f"qdq_{thr}"]
             by = res[thr]["bytes_read_alg"]
-            res[thr]["nvfp4_qdq"] = {"ms": t, "ms_min": ms_min[f"qdq_{thr}"], "GBps_alg": by / (t * 1e-3) / 1e9,
+            res[thr]["nvfp4_qdq"] = {"ms": t, **spread(f"qdq_{thr}"), "GBps_alg": by / (t * 1e-3) / 1e9,
                                      "time_over_unquantized": t / res[thr]["ms"]}
         out["skip"] = res
         gq = res["0.0"]["nvfp4_qdq"]["GBps_alg"]
@@ -412,7 +424,7 @@ def main():
         kv = 4.0 * c.H * c.D * float(c.lens.sum())
         tot = kv + 2.0 * 2 * c.B * c.H * c.D + 2.0 * c.B * c.H * c.max_s
         gbps = kv / (ms["smallseq"] * 1e-3) / 1e9
-        out["smallseq"] = {"ms": ms["smallseq"], "ms_min": ms_min["smallseq"], "kv_bytes": kv, "kv_GBps": gbps,
+        out["smallseq"] = {"ms": ms["smallseq"], **spread("smallseq"), "kv_bytes": kv, "kv_GBps": gbps,
                            "all_bytes": tot, "all_GBps": tot / (ms["smallseq"] * 1e-3) / 1e9,
                            "frac_peak": gbps / PEAK_HBM_GBPS}
         rooflines.append({"kernel": "smallseq_kernel", "bound": "hbm", "achieved": gbps, "peak": PEAK_HBM_GBPS,
@@ -426,7 +438,7 @@ def main():
         # algorithmic: the five products S (recomputed), dP, dV, dK, dQ = 2.5x the forward's two; the dQ
         # kernel recomputes S and dP once more (executed: 3.5x)
         tf = 2.5 * fwd_flops / (t * 1e-3) / 1e12
-        out["prefill_bwd"] = {"ms": t, "ms_min": ms_min["prefill_bwd"], "flop_alg": 2.5 * fwd_flops, "tflops_alg": tf,
+        out["prefill_bwd"] = {"ms": t, **spread("prefill_bwd"), "flop_alg": 2.5 * fwd_flops, "tflops_alg": tf,
                               "tflops_executed": 3.5 * fwd_flops / (t * 1e-3) / 1e12,
                               "frac_peak": tf / PEAK_BF16_TFLOPS,
                               "note": "one call: bwd_prep + bwd_dkdv + bwd_dq; timed outside the step"}
@@ -440,7 +452,7 @@ def main():
         byts = 4.0 * c.H * c.D * 2 * nk + 3.0 * c.B * c.H * c.D * 2 + 2.0 * c.H * nk
         t = ms["smallseq_bwd"]
         gb = byts / (t * 1e-3) / 1e9
-        out["smallseq_bwd"] = {"ms": t, "ms_min": ms_min["smallseq_bwd"], "bytes_alg": byts, "GBps": gb,
+        out["smallseq_bwd"] = {"ms": t, **spread("smallseq_bwd"), "bytes_alg": byts, "GBps": gb,
                                "frac_peak": gb / PEAK_HBM_GBPS, "note": "one launch; timed outside the step"}
 
     if "decode_multi" in only:
@@ -449,7 +461,7 @@ def main():
         kv = 4.0 * dm.Hkv * dm.D * float(dm.lens.sum())
         t = ms["decode_multi"]
         gb = kv / (t * 1e-3) / 1e9
-        out["decode_multi"] = {"ms": t, "ms_min": ms_min["decode_multi"], "kv_bytes": kv, "kv_GBps": gb,
+        out["decode_multi"] = {"ms": t, **spread("decode_multi"), "kv_bytes": kv, "kv_GBps": gb,
                                "frac_peak": gb / PEAK_HBM_GBPS, "tokens": int(dm.q.shape[0]),
                                "note": "split kernel + merge; timed outside the step"}
         if "decode" in out:
@@ -464,7 +476,7 @@ def main():
         flops = 4.0 * pp.D * pp.Hq * pairs
         t = ms["prefill_paged"]
         tf = flops / (t * 1e-3) / 1e12
-        out["prefill_paged"] = {"ms": t, "ms_min": ms_min["prefill_paged"], "flop": flops, "tflops": tf,
+        out["prefill_paged"] = {"ms": t, **spread("prefill_paged"), "flop": flops, "tflops": tf,
                                 "frac_peak": tf / PEAK_BF16_TFLOPS, "tokens": int(pp.q.shape[0]),
                                 "note": "the prefill kernel with page-gathered K/V; timed outside the step"}
         if "prefill" in out:
@@ -605,6 +617,31 @@ def _achievable(torch, dev):
     ms = e0.elapsed_time(e1) / 10
     res["gemm_bf16_8192_TFLOPs"] = 2.0 * n ** 3 / (ms * 1e-3) / 1e12
     del a, b, c
+    # a plain 32x32x16 bf16 MFMA loop on every CU (two waves per SIMD, operands of ordinary magnitude): the
+    # matrix-core rate this chip sustains, clock drop included (measurement-only library, built beside
+    # libattn.so)
+    probe = os.path.join(ROOT, "paged_skip_softmax_amd", "libattn_probe.so")
+    if os.path.exists(probe):
+        import ctypes
+        lib = ctypes.CDLL(probe)
+        lib.attn_probe_mfma_bf16.restype = ctypes.c_int
+        lib.attn_probe_mfma_bf16.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+        lib.attn_probe_mfma_bf16_flop.restype = ctypes.c_double
+        lib.attn_probe_mfma_bf16_flop.argtypes = [ctypes.c_int, ctypes.c_int]
+        blocks, iters = 1024, 10000
+        out = torch.empty(blocks * 256, dtype=torch.float32, device=dev)
+        st = torch.cuda.current_stream().cuda_stream
+        for _ in range(2):
+            assert lib.attn_probe_mfma_bf16(out.data_ptr(), blocks, iters, st) == 0
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(5):
+            assert lib.attn_probe_mfma_bf16(out.data_ptr(), blocks, iters, st) == 0
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / 5
+        res["mfma_bf16_loop_TFLOPs"] = lib.attn_probe_mfma_bf16_flop(blocks, iters) / (ms * 1e-3) / 1e12
+        del out
     torch.cuda.empty_cache()
     return res
 

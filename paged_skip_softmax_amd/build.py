@@ -43,10 +43,24 @@ def _compile(src: str) -> str:
     return out
 
 
+# Measurement only, outside the library's ABI: the matrix-core loop the bench reports as the achievable
+# bf16 MFMA rate.
+PROBE_SRC = "probe.hip"
+PROBE_LIB = os.path.join(HERE, "libattn_probe.so")
+
+
 def build(verbose: bool = True) -> str:
     os.makedirs(OBJ, exist_ok=True)
-    with cf.ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
+    with cf.ThreadPoolExecutor(max_workers=len(SOURCES) + 1) as ex:
+        fut_probe = ex.submit(_compile, PROBE_SRC)
         objs = list(ex.map(_compile, SOURCES))
+        probe_obj = fut_probe.result()
+    tmp = PROBE_LIB + ".tmp%d" % os.getpid()
+    r = subprocess.run(["hipcc", f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, probe_obj],
+                       capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"probe link failed:\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp, PROBE_LIB)
     tmp = LIB + ".tmp%d" % os.getpid()
     r = subprocess.run(["hipcc", f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs],
                        capture_output=True, text=True)
