@@ -241,9 +241,8 @@ __device__ __forceinline__ bool needs_mask(int t, const IterCtx &c)
 //   (c) mask tile t+1 where it crosses the diagonal or the sequence end;
 //   (d) P.V of tile t, with the row max of tile t+1 placed between its MFMAs.
 // On the last tile, (b)-(d) compute scores from a stale K stage that are never used.
-// sc: the scores of tile t; the scores of tile t+1 go to nxo (dense: the loop's two unrolled iterations
-// pass two arrays in alternating roles, so no copy is needed between tiles) or, in the skip variant
-// (which has no registers for two arrays), to a local array copied back into sc.
+// sc: the scores of tile t; the scores of tile t+1 go to nxo (the loop's two unrolled iterations pass two
+// arrays in alternating roles, so no copy is needed between tiles).
 template <int ST, bool SKIP, bool PAGED>
 __device__ __forceinline__ void iteration(int t, const IterCtx &c, const Loader<PAGED> &ld, Wave &wv,
                                           f32x16 (&sc)[2], f32x16 (&nxo)[2], float &t0, float &t1,
@@ -291,8 +290,7 @@ __device__ __forceinline__ void iteration(int t, const IterCtx &c, const Loader<
     __builtin_amdgcn_s_setprio(1);
     sched_fence();
     // (b) 16 MFMA steps, alternating the two 32-key blocks of tile t+1; K operands read two steps ahead
-    f32x16 nxl[2];
-    f32x16(&nx)[2] = SKIP ? nxl : nxo;
+    f32x16(&nx)[2] = nxo;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
         nx[0][i] = 0.f;
@@ -419,10 +417,6 @@ __device__ __forceinline__ void iteration(int t, const IterCtx &c, const Loader<
                 }
             }
         }
-    }
-    if constexpr (SKIP) {
-        sc[0] = nx[0];
-        sc[1] = nx[1];
     }
 }
 
@@ -578,7 +572,7 @@ void prefill_d128_kernel(PrefillArgs a, int NH, int RB, int nqt, int nunits)
     for (int t = 0; t < niter; t += kStages) {
         iteration<0, SKIP, PAGED>(t, c, ld, wv, sc, sc2, t0, t1, ss);
         if (t + 1 < niter)
-            iteration<1, SKIP, PAGED>(t + 1, c, ld, wv, SKIP ? sc : sc2, SKIP ? sc2 : sc, t0, t1, ss);
+            iteration<1, SKIP, PAGED>(t + 1, c, ld, wv, sc2, sc, t0, t1, ss);
     }
 
     wv.l = sum_halves(wv.l);
