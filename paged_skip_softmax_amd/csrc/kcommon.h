@@ -51,18 +51,6 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c)
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-// Reductions across the four 16-lane groups that share lane%16.
-__device__ __forceinline__ float max_across_groups16(float v)
-{
-    v = fmaxf(v, __shfl_xor(v, 16));
-    return fmaxf(v, __shfl_xor(v, 32));
-}
-__device__ __forceinline__ float sum_across_groups16(float v)
-{
-    v += __shfl_xor(v, 16);
-    return v + __shfl_xor(v, 32);
-}
-
 // Max / sum of v over lanes l and l ^ 32, by v_permlane32_swap (a VALU op; no LDS round trip).  The
 // swap exchanges the upper half of its first operand with the lower half of its second: with both set
 // to v, lane l ends up holding {own, other} (l < 32) or {other, own} (l >= 32).
@@ -76,6 +64,23 @@ __device__ __forceinline__ float sum_halves(float v)
     const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
+
+// The same over lanes l and l ^ 16 by v_permlane16_swap, which exchanges the odd 16-lane rows of its
+// first operand with the even rows of its second.
+__device__ __forceinline__ float max_rows16(float v)
+{
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_rows16(float v)
+{
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Reductions across the four 16-lane groups that share lane%16 (VALU lane swaps, no LDS round trip).
+__device__ __forceinline__ float max_across_groups16(float v) { return max_halves(max_rows16(v)); }
+__device__ __forceinline__ float sum_across_groups16(float v) { return sum_halves(sum_rows16(v)); }
 
 // Full-wave reductions.
 __device__ __forceinline__ float wave_max(float v)
