@@ -5,7 +5,8 @@
 //   P = exp(scale Q K^T - lse),  dP = dO V^T,  Dsum = rowsum(dO * O),  dS = P * (dP - Dsum)
 //   dV = P^T dO,  dK = scale dS^T Q,  dQ = scale dS K         (dK, dV summed over a KV head's group)
 //
-// Three kernels, no atomics:
+// Three kernels, no atomics (dK/dV and dQ run at the same time, dQ on a side stream of the device that the
+// call forks from its stream after the prep kernel and joins back to it):
 //  * bwd_prep: Dsum and lse * log2(e) per (token, query head), fp32, into the caller's workspace.
 //  * bwd_dkdv: a workgroup of 8 waves (two per SIMD) owns 128 keys of one (sequence, KV head) as 4 wave
 //    pairs of 32 keys.  It walks every 64-row query tile that sees any of its keys, for every query
